@@ -1,0 +1,269 @@
+"""CPU oracle for submanifold sparse 3x3x3 convolution.
+
+TEST INFRASTRUCTURE. Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg import this module. The GPU library never calls
+it, never links it, and shares no code, table or helper with it.
+
+Sources (the pages this follows):
+
+* [P1] "[Kernel] Add submanifold sparse 3D convolution (bf16 implicit GEMM,
+  gfx950)", FlyDSL pull request #942 -- sections Summary, Design, Test plan,
+  and its commit messages.
+* [P5] "Sparse convolution in FP32", DriveRT project page -- sections
+  "The starting point", "Neighbour masks and sorted rows".
+
+What is computed ([P5] "The starting point"; [P1] Summary): for every
+active voxel p of the set S (the output set is S itself),
+
+    Y[p, co] = sum over the 27 offsets d with p + d in S of
+               sum over ci of X[p + d, ci] * W[k(d), ci, co]
+
+Readings fixed here where the pages are silent:
+
+* offset order: k(d) = 9 (dx + 1) + 3 (dy + 1) + (dz + 1), x slowest; the
+  centre is k = 13. The same k indexes the mask bit and W's first axis.
+* sign: output p reads input p + d (cross-correlation).
+* W layout: [27, C_in, C_out].
+* coordinates: rows (b, x, y, z) for [N, 4]; (x, y, z) with b = 0 for [N, 3];
+  neighbours never cross batches.
+* duplicate coordinates are a caller error (raised here).
+* mask sort: ascending plain mask value, ties by ascending row.
+* pair lists: tap-major, and within a tap in mask-sorted row order.
+* rounding to bf16: round to nearest, ties to even.
+
+Accumulation is float64 by default (the products of two bf16 values are
+exact in float64, so the only error is the float64 summation, far below the
+float32 accumulator the GPU uses); ``acc_dtype=np.float32`` gives the
+float32 per-offset accumulation the pages describe.
+
+Pins for every function live in tests/test_oracle_pins.py (brute-force
+neighbour enumeration, closed-form pair counts on full boxes, masked dense
+convolution via numpy shifted slices and via torch.nn.functional.conv3d,
+integer-exact and one-hot cases, hand-derived worked examples, and bf16
+rounding against torch's conversion). No function here is unpinned.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+TAPS = 27
+CENTRE = 13
+
+
+class DuplicateCoordinate(ValueError):
+    pass
+
+
+def tap_offsets() -> list:
+    """The 27 offsets d in tap order k = 9(dx+1) + 3(dy+1) + (dz+1)."""
+    offs = []
+    for dx in (-1, 0, 1):
+        for dy in (-1, 0, 1):
+            for dz in (-1, 0, 1):
+                offs.append((dx, dy, dz))
+    return offs
+
+
+# --------------------------------------------------------------------------
+# bf16 helpers (the pages fix bf16 storage, [P1] Design: "dtype is bf16")
+# --------------------------------------------------------------------------
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Decode bf16 bit patterns: a bf16 is the top half of a float32."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round real values to the nearest bf16 value, ties to even.
+
+    bf16 keeps 8 significant bits. Write x = m * 2**e with 0.5 <= |m| < 1;
+    the bf16 grid spacing around x is 2**(e - 8), never finer than the
+    subnormal spacing 2**-133. Dividing by the spacing is exact, and
+    numpy's round() rounds halves to even, which is the rule wanted.
+    Values are returned as float64 (every bf16 is exact there).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)
+    spacing = np.ldexp(1.0, np.maximum(e - 8, -133))
+    r = np.round(x / spacing) * spacing
+    big = np.abs(r) > 3.3895313892515355e38     # above the largest bf16
+    r = np.where(big, np.copysign(np.inf, x), r)
+    return np.where(np.isfinite(x), r, x)
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns of ``round_to_bf16(x)``."""
+    r = round_to_bf16(x).astype(np.float32)     # exact: bf16 values fit float32
+    return (r.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+# --------------------------------------------------------------------------
+# kernel map ([P5] "Neighbour masks and sorted rows"; [P1] Summary, Design)
+# --------------------------------------------------------------------------
+
+def _rows_bxyz(coords: np.ndarray) -> np.ndarray:
+    c = np.asarray(coords)
+    if c.ndim != 2 or c.shape[1] not in (3, 4):
+        raise ValueError("coords must be [N, 3] or [N, 4]")
+    if c.shape[1] == 3:
+        c = np.concatenate([np.zeros((c.shape[0], 1), c.dtype), c], axis=1)
+    return c.astype(np.int64)
+
+
+def build_kernel_map(coords: np.ndarray):
+    """Neighbour table and 27-bit neighbour masks from a hash map.
+
+    A dictionary maps each (b, x, y, z) to its row. For row i and tap k,
+    nbr[i, k] is the row at c_i + d_k, or -1 when that cell is inactive, and
+    bit k of mask[i] is set exactly when the neighbour exists. This is the
+    table plus mask that the map builder of [P5] "Neighbour masks and sorted
+    rows" emits; the centre column is always the row itself.
+
+    Returns (nbr int32 [N, 27], mask uint32 [N]).
+    """
+    c = _rows_bxyz(coords)
+    n = c.shape[0]
+    table = {}
+    for i in range(n):
+        key = tuple(c[i].tolist())
+        if key in table:
+            raise DuplicateCoordinate(f"rows {table[key]} and {i} share {key}")
+        table[key] = i
+    offs = tap_offsets()
+    nbr = np.full((n, TAPS), -1, dtype=np.int32)
+    mask = np.zeros(n, dtype=np.uint32)
+    for i in range(n):
+        b, x, y, z = c[i].tolist()
+        m = 0
+        for k, (dx, dy, dz) in enumerate(offs):
+            j = table.get((b, x + dx, y + dy, z + dz))
+            if j is not None:
+                nbr[i, k] = j
+                m |= 1 << k
+        mask[i] = m
+    return nbr, mask
+
+
+def mask_sort(mask: np.ndarray) -> np.ndarray:
+    """Rows ordered by neighbour mask ([P5] "Neighbour masks and sorted rows").
+
+    The page sorts rows by mask so that rows with equal masks sit together;
+    ties are broken by ascending row here so that the order is unique.
+    Returns perm int32 [N]: perm[s] is the row at sorted position s.
+    """
+    m = [int(v) for v in np.asarray(mask).tolist()]
+    order = sorted(range(len(m)), key=lambda r: (m[r], r))
+    return np.asarray(order, dtype=np.int32)
+
+
+def compact_pairs(nbr: np.ndarray, mask: np.ndarray, perm: np.ndarray):
+    """Per-tap pair lists holding only the neighbours that exist.
+
+    [P1] Design ("Compaction"): only valid (input, output) pairs are listed,
+    grouped by tap so that a run of pairs shares one weight slab; the centre
+    tap is listed like the others ([P1] commit d4161ef, "The centre tap is
+    compacted along with the rest"). Within a tap, pairs follow the
+    mask-sorted row order.
+
+    Returns (pair_in int32 [P], pair_out int32 [P], tap_off int64 [28]); the
+    pairs of tap k are [tap_off[k], tap_off[k+1]).
+    """
+    nbr = np.asarray(nbr)
+    mask = np.asarray(mask, dtype=np.uint32)
+    perm = np.asarray(perm, dtype=np.int64)
+    ins, outs, off = [], [], [0]
+    for k in range(TAPS):
+        rows = perm[((mask[perm] >> np.uint32(k)) & np.uint32(1)) == 1]
+        ins.append(nbr[rows, k].astype(np.int32))
+        outs.append(rows.astype(np.int32))
+        off.append(off[-1] + rows.size)
+    return (np.concatenate(ins) if ins else np.zeros(0, np.int32),
+            np.concatenate(outs) if outs else np.zeros(0, np.int32),
+            np.asarray(off, dtype=np.int64))
+
+
+# --------------------------------------------------------------------------
+# compute ([P5] "The starting point"; [P1] Design, "GEMM")
+# --------------------------------------------------------------------------
+
+def conv_accumulate(x: np.ndarray, w: np.ndarray, pair_in, pair_out, tap_off,
+                    n_out: int, acc_dtype=np.float64) -> np.ndarray:
+    """Per-offset gather -> matmul -> scatter-add into an accumulator.
+
+    For each tap k, the gathered input rows X[pair_in] times W[k] are added
+    to rows pair_out of the accumulator. An output row appears at most once
+    per tap, so the indexed add never collides. x: [N_in, C_in] values,
+    w: [27, C_in, C_out] values (both real-valued arrays).
+    """
+    x = np.asarray(x, dtype=acc_dtype)
+    w = np.asarray(w, dtype=acc_dtype)
+    acc = np.zeros((n_out, w.shape[2]), dtype=acc_dtype)
+    for k in range(TAPS):
+        a, b = int(tap_off[k]), int(tap_off[k + 1])
+        if a == b:
+            continue
+        acc[pair_out[a:b]] += x[pair_in[a:b]] @ w[k]
+    return acc
+
+
+def conv_rows(x: np.ndarray, w: np.ndarray, nbr: np.ndarray, rows) -> np.ndarray:
+    """The defining sum, evaluated row by row for the listed output rows.
+
+    Y[i] = sum over taps k with nbr[i, k] >= 0 of X[nbr[i, k]] @ W[k],
+    in float64. Used to check single rows of large problems.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    out = np.zeros((len(rows), w.shape[2]), dtype=np.float64)
+    for t, i in enumerate(rows):
+        for k in range(TAPS):
+            j = int(nbr[i, k])
+            if j >= 0:
+                out[t] += x[j] @ w[k]
+    return out
+
+
+def subm_conv(coords, x_bits, w_bits, relu: bool = False, acc_dtype=np.float64):
+    """One submanifold 3x3x3 layer from raw inputs.
+
+    coords int [N, 3|4]; x_bits, w_bits bf16 bit patterns. Returns a dict
+    with the map (nbr, mask, perm, pair lists), the accumulator and the
+    output as bf16 bits (ReLU after rounding when ``relu``).
+    """
+    nbr, mask = build_kernel_map(coords)
+    perm = mask_sort(mask)
+    pin, pout, toff = compact_pairs(nbr, mask, perm)
+    x = bf16_bits_to_f64(x_bits)
+    w = bf16_bits_to_f64(w_bits)
+    acc = conv_accumulate(x, w, pin, pout, toff, x.shape[0], acc_dtype)
+    y = round_to_bf16(acc)
+    if relu:
+        y = np.maximum(y, 0.0)
+    return dict(nbr=nbr, mask=mask, perm=perm, pair_in=pin, pair_out=pout,
+                tap_off=toff, acc=acc, y=y, y_bits=bf16_bits(y))
+
+
+def stage(coords, x_bits, w_bits_list, acc_dtype=np.float64):
+    """Consecutive layers sharing one kernel map, ReLU between layers.
+
+    The map is built once and reused by every layer ([P1] Performance,
+    the 6-layer stage sharing one map). The ReLU is applied to the bf16
+    output of every layer but the last, to every row ([P5] "Offset-group
+    partitioning": the rectification must span every row).
+    Returns the list of per-layer outputs (float64 bf16 values).
+    """
+    nbr, mask = build_kernel_map(coords)
+    perm = mask_sort(mask)
+    pin, pout, toff = compact_pairs(nbr, mask, perm)
+    h = bf16_bits_to_f64(x_bits)
+    outs = []
+    for li, wb in enumerate(w_bits_list):
+        acc = conv_accumulate(h, bf16_bits_to_f64(wb), pin, pout, toff,
+                              h.shape[0], acc_dtype)
+        y = round_to_bf16(acc)
+        if li + 1 < len(w_bits_list):
+            y = np.maximum(y, 0.0)
+        outs.append(y)
+        h = y
+    return outs

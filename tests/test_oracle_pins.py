@@ -1,0 +1,467 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+Each check is a function that raises AssertionError on a mismatch, so the
+planted-mistake tests at the bottom can run the same checks against broken
+copies of the oracle and require them to fail.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import smconv_oracle as so
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_examples.json")
+
+
+# --------------------------------------------------------------------------
+# independent references
+# --------------------------------------------------------------------------
+
+def brute_force_triples(coords):
+    """All (tap, in_row, out_row) adjacencies by O(N^2) enumeration.
+
+    The tap of an offset is found by position in a 3x3x3 array indexed
+    [dx+1, dy+1, dz+1] and flattened in C order, not by a formula.
+    """
+    c = so._rows_bxyz(coords)
+    tap_of = np.arange(27).reshape(3, 3, 3)
+    diff = c[None, :, 1:] - c[:, None, 1:]            # diff[i, j] = c_j - c_i
+    same_b = c[None, :, 0] == c[:, None, 0]
+    adj = same_b & (np.abs(diff) <= 1).all(axis=2)
+    out_rows, in_rows = np.nonzero(adj)
+    d = diff[out_rows, in_rows] + 1
+    taps = tap_of[d[:, 0], d[:, 1], d[:, 2]]
+    return set(zip(taps.tolist(), in_rows.tolist(), out_rows.tolist()))
+
+
+def dense_grid(coords, vals, shape):
+    g = np.zeros(tuple(shape) + (vals.shape[1],), dtype=np.float64)
+    g[coords[:, 1], coords[:, 2], coords[:, 3]] = vals
+    return g
+
+
+def masked_dense_conv_numpy(coords, x, w, shape):
+    """Dense 3x3x3 correlation on a zero-padded grid via shifted slices."""
+    X, Y, Z = shape
+    g = np.pad(dense_grid(coords, x, shape), ((1, 1), (1, 1), (1, 1), (0, 0)))
+    w5 = w.reshape(3, 3, 3, w.shape[1], w.shape[2])   # [dx+1, dy+1, dz+1, ci, co]
+    out = np.zeros((X, Y, Z, w.shape[2]))
+    for a in range(3):
+        for b in range(3):
+            for c in range(3):
+                out += g[a:a + X, b:b + Y, c:c + Z] @ w5[a, b, c]
+    return out[coords[:, 1], coords[:, 2], coords[:, 3]]
+
+
+def masked_dense_conv_torch(coords, x, w, shape):
+    """torch.nn.functional.conv3d (a cross-correlation) in float64."""
+    g = torch.from_numpy(dense_grid(coords, x, shape)).permute(3, 0, 1, 2)[None]
+    w5 = torch.from_numpy(w.reshape(3, 3, 3, w.shape[1], w.shape[2]))
+    wt = w5.permute(4, 3, 0, 1, 2).contiguous()         # [co, ci, kx, ky, kz]
+    out = torch.nn.functional.conv3d(g, wt, padding=1)[0].permute(1, 2, 3, 0)
+    return out.numpy()[coords[:, 1], coords[:, 2], coords[:, 3]]
+
+
+# --------------------------------------------------------------------------
+# checks (raise AssertionError)
+# --------------------------------------------------------------------------
+
+def check_map_vs_bruteforce(coords):
+    nbr, mask = so.build_kernel_map(coords)
+    got = set()
+    for i, k in zip(*np.nonzero(nbr >= 0)):
+        got.add((int(k), int(nbr[i, k]), int(i)))
+    assert got == brute_force_triples(coords), "neighbour table differs from brute force"
+    pop = np.array([bin(int(m)).count("1") for m in mask])
+    assert (pop == (nbr >= 0).sum(1)).all(), "mask popcount != neighbour count"
+    for i, k in zip(*np.nonzero(nbr >= 0)):
+        assert (int(mask[i]) >> int(k)) & 1
+
+
+def check_full_box(a, b, c):
+    coords = synth.box_coords(a, b, c, origin=(3, 5, 7), seed=a * 100 + b * 10 + c)
+    nbr, mask = so.build_kernel_map(coords)
+    perm = so.mask_sort(mask)
+    _, _, toff = so.compact_pairs(nbr, mask, perm)
+    counts = np.diff(toff)
+    for k, (dx, dy, dz) in enumerate(np.ndindex(3, 3, 3)):
+        want = max(a - abs(dx - 1), 0) * max(b - abs(dy - 1), 0) * max(c - abs(dz - 1), 0)
+        assert counts[k] == want, f"box {a}x{b}x{c} tap {k}: {counts[k]} != {want}"
+    assert toff[-1] == (3 * a - 2) * (3 * b - 2) * (3 * c - 2)
+
+
+def check_perm(mask, perm):
+    n = len(mask)
+    assert sorted(perm.tolist()) == list(range(n)), "perm is not a permutation"
+    m = mask[perm].astype(np.int64)
+    assert (np.diff(m) >= 0).all(), "masks not ascending"
+    same = np.diff(m) == 0
+    assert (np.diff(perm.astype(np.int64))[same] > 0).all(), "ties not by row"
+
+
+def check_pairs(coords):
+    nbr, mask = so.build_kernel_map(coords)
+    perm = so.mask_sort(mask)
+    check_perm(mask, perm)
+    pin, pout, toff = so.compact_pairs(nbr, mask, perm)
+    got = set()
+    pos = np.empty(len(perm), np.int64)
+    pos[perm] = np.arange(len(perm))
+    for k in range(27):
+        a, b = toff[k], toff[k + 1]
+        for i, o in zip(pin[a:b].tolist(), pout[a:b].tolist()):
+            got.add((k, i, o))
+        assert (np.diff(pos[pout[a:b]]) > 0).all(), f"tap {k} not in mask-sorted order"
+    assert got == brute_force_triples(coords), "pair lists differ from brute force"
+    bits = ((mask[:, None] >> np.arange(27, dtype=np.uint32)) & 1).sum(0)
+    assert (np.diff(toff) == bits).all(), "per-tap counts != mask column sums"
+
+
+def check_conv_vs_dense(coords, xb, wb, shape, exact=False):
+    x = so.bf16_bits_to_f64(xb)
+    w = so.bf16_bits_to_f64(wb)
+    r = so.subm_conv(coords, xb, wb)
+    ref_np = masked_dense_conv_numpy(coords, x, w, shape)
+    ref_t = masked_dense_conv_torch(coords, x, w, shape)
+    if exact:
+        assert np.array_equal(r["acc"], ref_np), "accumulator != numpy dense conv"
+        assert np.array_equal(r["acc"], ref_t), "accumulator != torch conv3d"
+    else:
+        scale = 1 + np.abs(ref_np)
+        assert np.max(np.abs(r["acc"] - ref_np) / scale) < 1e-12, "acc vs numpy dense conv"
+        assert np.max(np.abs(r["acc"] - ref_t) / scale) < 1e-12, "acc vs torch conv3d"
+
+
+def check_one_hot(coords, k):
+    c = 8
+    n = len(coords)
+    xb = synth.features(n, c, seed=11)
+    w = np.zeros((27, c, c), np.float32)
+    w[k] = np.eye(c, dtype=np.float32)
+    wb = synth.bf16_bits_from_f32(w)
+    r = so.subm_conv(coords, xb, wb)
+    nbr, _ = so.build_kernel_map(coords)
+    x = so.bf16_bits_to_f64(xb)
+    want = np.where((nbr[:, k] >= 0)[:, None], x[np.maximum(nbr[:, k], 0)], 0.0)
+    assert np.array_equal(r["y"], want), f"one-hot tap {k} is not a shifted copy"
+
+
+def check_hand_examples():
+    ex = json.load(open(GOLDEN))["examples"]
+    for e in ex:
+        coords = np.asarray(e["coords"], np.int32)
+        n = len(coords)
+        x = np.asarray(e["x"], np.float32)
+        ci, co = e["c_in"], e["c_out"]
+        w = np.zeros((27, ci, co), np.float32)
+        if e["name"] in ("two_voxels_along_z", "diagonal_and_x_neighbours"):
+            for k in range(27):
+                w[k] = k + 1
+        elif e["name"] == "batches_do_not_mix":
+            w[:] = 100.0
+            w[13] = 1.0
+        elif e["name"] == "round_half_to_even":
+            w[13] = 1.0078125
+            w[14] = 1.0
+        r = so.subm_conv(coords, synth.bf16_bits_from_f32(x), synth.bf16_bits_from_f32(w))
+        nb = {str(i): {str(k): int(r["nbr"][i, k]) for k in range(27) if r["nbr"][i, k] >= 0}
+              for i in range(n)}
+        assert nb == e["nbr_nonneg"], e["name"] + ": nbr"
+        assert r["mask"].tolist() == e["mask"], e["name"] + ": mask"
+        assert r["perm"].tolist() == e["perm"], e["name"] + ": perm"
+        assert r["pair_in"].tolist() == e["pair_in"], e["name"] + ": pair_in"
+        assert r["pair_out"].tolist() == e["pair_out"], e["name"] + ": pair_out"
+        assert r["tap_off"].tolist() == e["tap_off"], e["name"] + ": tap_off"
+        if "acc" in e:
+            assert np.array_equal(r["acc"], np.asarray(e["acc"])), e["name"] + ": acc"
+        assert np.array_equal(r["y"], np.asarray(e["y"])), e["name"] + ": y"
+
+
+def check_bf16_vs_torch(vals):
+    vals = np.asarray(vals, np.float32)
+    want = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = so.bf16_bits(vals.astype(np.float64))
+    assert np.array_equal(got, want), "bf16 rounding differs from torch"
+
+
+def bf16_test_values():
+    rng = np.random.default_rng(7)
+    a = rng.standard_normal(20000).astype(np.float32) * np.float32(3.0)
+    b = (rng.standard_normal(2000) * 1e-39).astype(np.float32)      # subnormals
+    # exact halfway cases: a bf16 value plus half an ulp
+    base = rng.integers(0x3F00, 0x4200, size=4000).astype(np.uint32) << np.uint32(16)
+    ties = (base | np.uint32(0x8000)).view(np.float32)
+    near = (base | np.uint32(0x7FFF)).view(np.float32)
+    return np.concatenate([a, b, ties, -ties, near, [0.0, -0.0, 1.0, 65504.0]]).astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# tests
+# --------------------------------------------------------------------------
+
+def test_hand_worked_examples():
+    check_hand_examples()
+
+
+def test_bf16_rounding_matches_torch():
+    check_bf16_vs_torch(bf16_test_values())
+
+
+def test_bf16_ties_to_even_by_hand():
+    # 1 + 2^-8 lies halfway between 1 (even) and 1 + 2^-7 (odd): goes to 1.
+    # 1 + 3*2^-8 lies halfway between 1 + 2^-7 (odd) and 1 + 2^-6 (even).
+    r = so.round_to_bf16(np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8)]))
+    assert r.tolist() == [1.0, 1 + 2 ** -6, -1.0]
+
+
+def test_bf16_decode():
+    assert so.bf16_bits_to_f64(np.array([0x3F80, 0xC000, 0x0000, 0x3F81], np.uint16)).tolist() \
+        == [1.0, -2.0, 0.0, 1.0078125]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_map_vs_bruteforce_uniform(seed):
+    coords = synth.tiny_coords(seed=seed, n=300, side=8)
+    check_map_vs_bruteforce(coords)
+
+
+def test_map_vs_bruteforce_two_batches():
+    a = synth.tiny_coords(seed=5, n=150, side=6)
+    b = synth.tiny_coords(seed=6, n=150, side=6)
+    b[:, 0] = 1
+    check_map_vs_bruteforce(np.concatenate([a, b]))
+
+
+def test_map_vs_bruteforce_ground_box():
+    coords = synth.ground_box_coords(600, (40, 40, 12), seed=9, n_boxes=6)
+    check_map_vs_bruteforce(coords)
+
+
+@pytest.mark.parametrize("abc", [(1, 1, 1), (3, 3, 3), (5, 4, 3), (1, 1, 7), (2, 6, 1), (4, 4, 4)])
+def test_full_box_closed_form(abc):
+    check_full_box(*abc)
+
+
+def test_full_cube_343():
+    coords = synth.box_coords(3, 3, 3)
+    r = so.subm_conv(coords, synth.features(27, 4, 1), synth.weights(4, 4, 1))
+    assert r["tap_off"][-1] == 343
+    assert r["mask"][13] == (1 << 27) - 1        # the centre cell sees all 27
+
+
+def test_isolated_voxels():
+    coords = synth.isolated_coords(200, spacing=2, seed=3)
+    nbr, mask = so.build_kernel_map(coords)
+    assert (mask == (1 << 13)).all()
+    assert (nbr[:, 13] == np.arange(200)).all()
+    assert ((nbr >= 0).sum() == 200)
+
+
+def test_symmetry_and_centre():
+    coords = synth.tiny_coords(seed=1)
+    nbr, mask = so.build_kernel_map(coords)
+    assert (nbr[:, 13] == np.arange(len(coords))).all()
+    for k in range(27):
+        j = nbr[:, k]
+        i = np.nonzero(j >= 0)[0]
+        assert (nbr[j[i], 26 - k] == i).all()
+    perm = so.mask_sort(mask)
+    _, _, toff = so.compact_pairs(nbr, mask, perm)
+    c = np.diff(toff)
+    assert (c == c[::-1]).all()
+
+
+def test_duplicates_raise():
+    coords = np.array([[0, 1, 2, 3], [0, 4, 4, 4], [0, 1, 2, 3]], np.int32)
+    with pytest.raises(so.DuplicateCoordinate):
+        so.build_kernel_map(coords)
+
+
+def test_three_column_coords_equal_batch_zero():
+    c4 = synth.tiny_coords(seed=3, n=200, side=7)
+    n3, m3 = so.build_kernel_map(c4[:, 1:])
+    n4, m4 = so.build_kernel_map(c4)
+    assert np.array_equal(n3, n4) and np.array_equal(m3, m4)
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_pairs_vs_bruteforce(seed):
+    check_pairs(synth.tiny_coords(seed=seed, n=400, side=9))
+
+
+def test_pairs_empty_and_single():
+    nbr, mask = so.build_kernel_map(np.zeros((0, 4), np.int32))
+    perm = so.mask_sort(mask)
+    pin, pout, toff = so.compact_pairs(nbr, mask, perm)
+    assert pin.size == 0 and toff.tolist() == [0] * 28
+    nbr, mask = so.build_kernel_map(np.array([[0, 5, 5, 5]], np.int32))
+    pin, pout, toff = so.compact_pairs(nbr, mask, so.mask_sort(mask))
+    assert pin.tolist() == [0] and pout.tolist() == [0] and toff[13] == 0 and toff[14] == 1
+
+
+def test_conv_vs_dense_random():
+    coords = synth.tiny_coords(seed=1, n=500, side=10)
+    check_conv_vs_dense(coords, synth.features(500, 6, 1), synth.weights(6, 5, 1), (10, 10, 10))
+
+
+def test_conv_vs_dense_tiny_config():
+    w = synth.workload("tiny")
+    coords = synth.make_coords(w)
+    check_conv_vs_dense(coords, synth.features(w.n, 16, w.seed), synth.weights(16, 16, w.seed),
+                        w.grid)
+
+
+def test_conv_integer_exact():
+    coords = synth.tiny_coords(seed=4, n=700, side=10)
+    xb = synth.int_features(700, 12, 4)
+    wb = synth.int_weights(12, 10, 4)
+    check_conv_vs_dense(coords, xb, wb, (10, 10, 10), exact=True)
+    r32 = so.subm_conv(coords, xb, wb, acc_dtype=np.float32)
+    r64 = so.subm_conv(coords, xb, wb)
+    assert np.array_equal(r32["acc"].astype(np.float64), r64["acc"])
+
+
+@pytest.mark.parametrize("k", [0, 4, 13, 14, 22, 26])
+def test_one_hot_taps(k):
+    check_one_hot(synth.tiny_coords(seed=2, n=300, side=8), k)
+
+
+def test_fp32_and_fp64_accumulation_agree():
+    coords = synth.tiny_coords(seed=8, n=500, side=9)
+    xb, wb = synth.features(500, 32, 8), synth.weights(32, 32, 8)
+    a32 = so.subm_conv(coords, xb, wb, acc_dtype=np.float32)["acc"]
+    a64 = so.subm_conv(coords, xb, wb)["acc"]
+    # 27*32 products per output; float32 summation error bound ~ n*u*sum|terms|
+    x = np.abs(so.bf16_bits_to_f64(xb))
+    w = np.abs(so.bf16_bits_to_f64(wb))
+    nbr, mask = so.build_kernel_map(coords)
+    bound = so.conv_rows(x, w, nbr, range(500)) * (27 * 32) * 2 ** -24
+    assert (np.abs(a32 - a64) <= bound + 1e-30).all()
+
+
+def test_conv_rows_equals_accumulate():
+    coords = synth.tiny_coords(seed=3, n=400, side=8)
+    xb, wb = synth.features(400, 8, 3), synth.weights(8, 8, 3)
+    r = so.subm_conv(coords, xb, wb)
+    rows = [0, 17, 399, 123]
+    got = so.conv_rows(so.bf16_bits_to_f64(xb), so.bf16_bits_to_f64(wb), r["nbr"], rows)
+    assert np.max(np.abs(got - r["acc"][rows])) < 1e-12
+
+
+def test_stage_relu_between_layers():
+    coords = synth.tiny_coords(seed=5, n=300, side=8)
+    xb, w1 = synth.features(300, 8, 5), synth.weights(8, 8, 5)
+    ident = np.zeros((27, 8, 8), np.float32)
+    ident[13] = np.eye(8, dtype=np.float32)
+    outs = so.stage(coords, xb, [w1, synth.bf16_bits_from_f32(ident)])
+    one = so.subm_conv(coords, xb, w1)["y"]
+    assert np.array_equal(outs[0], np.maximum(one, 0))         # ReLU after layer 1
+    assert np.array_equal(outs[1], np.maximum(one, 0))         # identity layer, no ReLU after
+    assert (outs[0] >= 0).all() and (one < 0).any()
+
+
+def test_generators_are_seeded_and_distinct():
+    for name in ("tiny", "deep"):
+        w = synth.workload(name)
+        a, b = synth.make_coords(w), synth.make_coords(w)
+        assert np.array_equal(a, b)
+        lin = (a[:, 1].astype(np.int64) * w.grid[1] + a[:, 2]) * w.grid[2] + a[:, 3]
+        assert np.unique(lin).size == w.n
+        assert (a[:, 1:] >= 0).all() and (a[:, 1:] < np.array(w.grid)).all()
+
+
+# --------------------------------------------------------------------------
+# planted mistakes: every pin above must be able to fail
+# --------------------------------------------------------------------------
+
+def _fails(fn, *a):
+    try:
+        fn(*a)
+    except AssertionError:
+        return True
+    return False
+
+
+def test_planted_flipped_offset_sign(monkeypatch):
+    orig = so.tap_offsets
+    monkeypatch.setattr(so, "tap_offsets", lambda: [(-a, -b, -c) for a, b, c in orig()])
+    coords = synth.tiny_coords(seed=0, n=300, side=8)
+    assert _fails(check_map_vs_bruteforce, coords)
+    assert _fails(check_conv_vs_dense, coords, synth.features(300, 4, 0),
+                  synth.weights(4, 4, 0), (8, 8, 8))
+    assert _fails(check_hand_examples)
+
+
+def test_planted_z_slowest_tap_order(monkeypatch):
+    orig = so.tap_offsets
+    monkeypatch.setattr(so, "tap_offsets", lambda: [(c, b, a) for a, b, c in orig()])
+    coords = synth.tiny_coords(seed=0, n=300, side=8)
+    assert _fails(check_map_vs_bruteforce, coords)
+    assert _fails(check_hand_examples)
+
+
+def test_planted_transposed_weights(monkeypatch):
+    orig = so.conv_accumulate
+    monkeypatch.setattr(so, "conv_accumulate",
+                        lambda x, w, *a, **k: orig(x, np.swapaxes(np.asarray(w), 1, 2), *a, **k))
+    coords = synth.tiny_coords(seed=0, n=300, side=8)
+    assert _fails(check_conv_vs_dense, coords, synth.features(300, 4, 0),
+                  synth.weights(4, 4, 0), (8, 8, 8))
+
+
+def test_planted_dropped_centre_tap(monkeypatch):
+    orig = so.compact_pairs
+
+    def broken(nbr, mask, perm):
+        return orig(nbr, np.asarray(mask) & np.uint32(~(1 << 13) & 0xFFFFFFFF), perm)
+    monkeypatch.setattr(so, "compact_pairs", broken)
+    assert _fails(check_full_box, 3, 3, 3)
+    assert _fails(check_hand_examples)
+
+
+def test_planted_dropped_pair(monkeypatch):
+    orig = so.compact_pairs
+
+    def broken(nbr, mask, perm):
+        pin, pout, toff = orig(nbr, mask, perm)
+        keep = np.ones(pin.size, bool)
+        keep[int(toff[13])] = False
+        toff = toff.copy()
+        toff[14:] -= 1
+        return pin[keep], pout[keep], toff
+    monkeypatch.setattr(so, "compact_pairs", broken)
+    assert _fails(check_pairs, synth.tiny_coords(seed=1, n=400, side=9))
+    assert _fails(check_full_box, 3, 3, 3)
+
+
+def test_planted_unstable_mask_sort(monkeypatch):
+    monkeypatch.setattr(so, "mask_sort",
+                        lambda m: np.asarray(sorted(range(len(m)), key=lambda r: (int(m[r]), -r)),
+                                             np.int32))
+    coords = synth.tiny_coords(seed=1, n=400, side=20)      # sparse: many equal masks
+    nbr, mask = so.build_kernel_map(coords)
+    assert len(np.unique(mask)) < len(mask) // 2
+    assert _fails(check_perm, mask, so.mask_sort(mask))
+
+
+def test_planted_truncating_bf16(monkeypatch):
+    monkeypatch.setattr(so, "round_to_bf16",
+                        lambda x: np.trunc(np.asarray(x, np.float64) * 128) / 128)
+    assert _fails(check_bf16_vs_torch, bf16_test_values())
+    assert _fails(check_hand_examples)
+
+
+def test_planted_batch_mixing(monkeypatch):
+    orig = so._rows_bxyz
+
+    def no_batch(c):
+        r = orig(c).copy()
+        r[:, 0] = 0
+        return r
+    monkeypatch.setattr(so, "_rows_bxyz", no_batch)
+    assert _fails(check_hand_examples)
