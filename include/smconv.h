@@ -1,0 +1,210 @@
+/*
+ * smconv.h -- C ABI of the submanifold sparse 3x3x3 convolution library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes ("Sparse convolution in FP32", DriveRT, section
+ * "The starting point"; "[Kernel] Add submanifold sparse 3D convolution
+ * (bf16 implicit GEMM, gfx950)", FlyDSL PR #942, Summary): for each active
+ * voxel p of the input set S, whose output set is S itself,
+ *
+ *     Y[p, co] = sum over offsets d in {-1,0,1}^3 with p + d in S of
+ *                sum over ci of X[p + d, ci] * W[k(d), ci, co],
+ *
+ * with k(d) = 9 (dx+1) + 3 (dy+1) + (dz+1) (x slowest; the centre is 13).
+ * Raw int32 voxel coordinates go in, the kernel map is built internally and
+ * can be reused by every layer that shares the coordinates (PR #942,
+ * commit "derive the rulebook cache key from the coords tensor"; here the
+ * reuse is an explicit handle), features and weights are bf16 and the
+ * accumulation is float32 (PR #942, Design: "dtype is bf16").
+ *
+ * Conventions for every call:
+ *  - Every call returns an int status (smc_status); 0 is success. No C++
+ *    exception crosses this interface. smc_last_error() gives a message for
+ *    the last failing call of the calling thread.
+ *  - "device pointer" means memory the HIP runtime can read from the GPU
+ *    the library was first used on (e.g. a torch CUDA tensor's data_ptr);
+ *    "host pointer" means ordinary CPU memory.
+ *  - "stream" is a hipStream_t passed as void* (NULL = the null stream).
+ *    All GPU work is enqueued on that stream; the caller keeps every input
+ *    alive and unmodified until the stream has run the work.
+ *  - The caller owns every buffer it passes. The library keeps no caller
+ *    pointer after a call returns (except in work already enqueued).
+ *  - A map handle owns its own device buffers, allocated with hipMalloc
+ *    when a build needs more room than it has (grow-only), and freed by
+ *    smc_map_destroy. A handle is not thread-safe; all builds and forwards
+ *    that use one handle must be issued on one stream, or the caller must
+ *    order them.
+ *  - bf16 tensors are passed as uint16_t bit patterns.
+ */
+#ifndef SMCONV_H
+#define SMCONV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct smc_map smc_map;
+
+typedef enum smc_status {
+    SMC_OK = 0,
+    SMC_ERR_ARG = 1,          /* a bad argument (null pointer, n < 0, C < 1, ...) */
+    SMC_ERR_DUPLICATE = 2,    /* two rows share one (b, x, y, z): a caller error */
+    SMC_ERR_RANGE = 3,        /* a coordinate outside [0, spatial_shape) or b outside [0, batch) */
+    SMC_ERR_KEY_OVERFLOW = 4, /* the packed sorted-route key needs more than 64 bits */
+    SMC_ERR_ALLOC = 5,        /* hipMalloc / hipHostMalloc failed */
+    SMC_ERR_HIP = 6,          /* a HIP runtime call or a kernel launch failed */
+    SMC_ERR_STATE = 7,        /* the map is not built, or was built with an error */
+    SMC_ERR_UNSUPPORTED = 8,  /* a valid request this version does not implement (kernel_size != 3) */
+    SMC_ERR_GRID = 9          /* the dense route was forced on a grid of 2^31 cells or more */
+} smc_status;
+
+/* Map routes ("[Kernel] Add submanifold sparse 3D convolution", Design:
+ * two mappers chosen by bounding-box volume). */
+enum {
+    SMC_ROUTE_AUTO = 0,   /* dense presence grid when it has < 2^31 cells and fits the
+                             dense-grid budget, sorted packed keys otherwise */
+    SMC_ROUTE_DENSE = 1,  /* force the dense presence grid */
+    SMC_ROUTE_SORTED = 2  /* force the sorted packed-key mapper */
+};
+
+/* smc_map_build flags */
+enum {
+    SMC_BUILD_ASYNC = 1   /* do not wait for the device-side checks; call smc_map_sync() later */
+};
+
+/* smc_conv_forward flags */
+enum {
+    SMC_FWD_RELU = 1,     /* apply max(y, 0) to the (rounded) output */
+    SMC_FWD_OUT_F32 = 2   /* write the float32 accumulator itself: y is float [n, c_out] */
+};
+
+typedef struct smc_map_info_s {
+    int64_t n;              /* active voxels (rows) */
+    int32_t route;          /* SMC_ROUTE_DENSE or SMC_ROUTE_SORTED */
+    int32_t key_bits;       /* sorted route: bits of the packed coordinate key; dense: 0 */
+    int32_t origin[3];      /* grid origin (x, y, z) the coordinates are taken relative to */
+    int32_t extent[3];      /* grid extent (X, Y, Z) */
+    int32_t batch;          /* number of batches B */
+    int32_t tile_m;         /* pairs per GEMM tile; every tap's pair run is padded to a multiple */
+    int64_t grid_cells;     /* dense route: cells of the padded presence grid; sorted: 0 */
+    int64_t pairs;          /* P: valid (input, output) pairs including the centre tap */
+    int64_t pairs_padded;   /* P after padding every tap to a multiple of tile_m */
+    int64_t n_tiles;        /* pairs_padded / tile_m */
+    int64_t tap_count[27];  /* pairs per tap */
+    int32_t status;         /* smc_status of the build's device-side checks */
+} smc_map_info_t;
+
+/* Create an empty map handle. *out receives it. No device memory is taken yet. */
+int smc_map_create(smc_map** out);
+
+/* Free the handle and every device buffer it owns. Waits for the handle's
+ * outstanding work first. NULL is accepted and ignored. */
+int smc_map_destroy(smc_map* map);
+
+/*
+ * Build the kernel map of a voxel set: neighbour table, 27-bit neighbour
+ * masks, mask-sorted row order and per-tap pair lists.
+ *
+ * Steps (all on the GPU): bounding box -> route by grid volume ("[Kernel]
+ * Add submanifold sparse 3D convolution", Design, the mapper table) ->
+ *   dense route:  presence grid scatter, 27 lookups per row;
+ *   sorted route: packed keys with packed(q + d) = packed(q) + packed(d),
+ *                 radix sort, 9 binary searches per row ("Z-Delta", Design);
+ * -> neighbour table + masks ("Sparse convolution in FP32", "Neighbour masks
+ * and sorted rows") -> radix sort of rows by mask -> per-tap counts, scan,
+ * pair write with each tap padded to a multiple of tile_m ("[Kernel] ...",
+ * Design "Compaction"; commits "move pair compaction from torch onto three fx
+ * kernels" and "scan the pair counts on the device").
+ *
+ * coords        device pointer, int32 [n, ncols], row-major. ncols = 4: rows
+ *               (b, x, y, z); ncols = 3: rows (x, y, z) with b = 0.
+ * n             rows, n >= 0 (n = 0 builds an empty map).
+ * spatial_shape host pointer to int32 [3] (X, Y, Z), or NULL. Given: every
+ *               coordinate must satisfy 0 <= c < shape (else SMC_ERR_RANGE) and the
+ *               grid is [0, shape). NULL: the grid is the coordinates' bounding
+ *               box, which costs one device->host read inside this call.
+ * batch_size    number of batches B (b in [0, B)); <= 0 derives it (one read).
+ * kernel_size   must be 3 (else SMC_ERR_UNSUPPORTED).
+ * route         SMC_ROUTE_*.
+ * flags         SMC_BUILD_ASYNC or 0. Without it the call waits for the
+ *               device-side checks and returns SMC_ERR_DUPLICATE / SMC_ERR_RANGE
+ *               when they fail. With it the call returns after enqueueing; the
+ *               check result comes from smc_map_sync(). A map whose checks failed
+ *               is in-bounds but meaningless and is refused by smc_conv_forward.
+ * The dense route keeps its presence grid (4 bytes per padded cell) in the
+ * handle between builds and leaves it cleared, so only the first build on
+ * a handle pays for filling it.
+ */
+int smc_map_build(smc_map* map, const int32_t* coords, int64_t n, int ncols,
+                  const int32_t* spatial_shape, int batch_size, int kernel_size,
+                  int route, unsigned flags, void* stream);
+
+/* Wait for the map's last build and return the status of its device-side
+ * checks (SMC_OK, SMC_ERR_DUPLICATE, SMC_ERR_RANGE). */
+int smc_map_sync(smc_map* map);
+
+/* Wait for the last build and describe the map. info: host pointer. */
+int smc_map_info(smc_map* map, smc_map_info_t* info);
+
+/*
+ * Copy the map to host memory for inspection (parity tests). Each pointer is
+ * a host pointer or NULL (skipped):
+ *   nbr      int32 [n, 27]  row of c_i + d_k, or -1
+ *   mask     uint32 [n]     bit k set iff nbr[i, k] >= 0
+ *   perm     int32 [n]      rows in ascending (mask, row) order
+ *   pair_in  int32 [pairs]  unpadded, tap-major, mask-sorted order within a tap
+ *   pair_out int32 [pairs]
+ *   tap_off  int64 [28]     pairs of tap k are [tap_off[k], tap_off[k+1])
+ * Waits for the map's stream.
+ */
+int smc_map_export(smc_map* map, int32_t* nbr, uint32_t* mask, int32_t* perm,
+                   int32_t* pair_in, int32_t* pair_out, int64_t* tap_off);
+
+/* Bytes of the packed weight buffer for c_in x c_out (both >= 1). */
+size_t smc_weight_packed_bytes(int c_in, int c_out);
+
+/*
+ * Pack weights for the GEMM ("[Kernel] Add submanifold sparse 3D
+ * convolution", Design: weights packed so that a wave reads fully used
+ * cache lines). w: device pointer, bf16 [27, c_in, c_out] row-major
+ * (W[k][ci][co]). out: device pointer of smc_weight_packed_bytes() bytes,
+ * 16-byte aligned. Channels are zero-padded internally, so any c >= 1 works.
+ * Pack once per weight tensor and reuse the result for every forward.
+ */
+int smc_weight_pack(const uint16_t* w, int c_in, int c_out, void* out, void* stream);
+
+/*
+ * One submanifold convolution layer over a built map ("[Kernel] ...",
+ * Design "GEMM": gather -> mfma_f32_16x16x32_bf16 with float32 accumulate
+ * -> scatter-add, the centre tap compacted with the rest).
+ * x       device pointer, bf16 [n, c_in] row-major (rows in coordinate order).
+ * wpacked device pointer from smc_weight_pack(c_in, c_out).
+ * y       device pointer, bf16 [n, c_out] (float [n, c_out] with SMC_FWD_OUT_F32);
+ *         every row is written.
+ * flags   SMC_FWD_RELU | SMC_FWD_OUT_F32, or 0. Without SMC_FWD_OUT_F32 the output
+ *         is the float32 accumulator rounded to bf16 (to nearest, ties to even).
+ * The float32 accumulator lives in the handle (grow-only, 4 n c_out bytes).
+ * Needs no host read of the map's pair counts: the GEMM reads them on the
+ * device. Refuses (SMC_ERR_STATE) a map whose synchronous build failed or
+ * a map that was never built.
+ */
+int smc_conv_forward(smc_map* map, const uint16_t* x, int c_in, const void* wpacked,
+                     int c_out, void* y, unsigned flags, void* stream);
+
+/* Static text for a status code. */
+const char* smc_status_string(int status);
+
+/* Message for the calling thread's last failing call ("" if none). */
+const char* smc_last_error(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int smc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SMCONV_H */

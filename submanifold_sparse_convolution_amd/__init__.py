@@ -1,0 +1,233 @@
+"""Submanifold sparse 3x3x3 convolution on MI355X: Python binding.
+
+A thin ctypes layer over libsmconv.so (C ABI in include/smconv.h). It only
+marshals arguments: torch tensors supply device memory and the current HIP
+stream, every step of the computation runs in the library's HIP kernels.
+There is no fallback: if the library is not built, every call raises.
+
+    m = KernelMap()
+    m.build(coords, spatial_shape=(1440, 1440, 41))     # int32 [N, 4] on the GPU
+    wp = pack_weights(w)                                 # bf16 [27, C_in, C_out]
+    y = m.forward(x, wp, relu=True)                      # bf16 [N, C_in] -> [N, C_out]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["KernelMap", "PackedWeights", "pack_weights", "subm_conv3d", "lib", "library_path",
+           "SmconvError", "ROUTES", "EXPORTED_SYMBOLS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libsmconv.so")
+
+ROUTES = {"auto": 0, "dense": 1, "sorted": 2}
+_ROUTE_NAMES = {v: k for k, v in ROUTES.items()}
+SMC_BUILD_ASYNC = 1
+SMC_FWD_RELU = 1
+SMC_FWD_OUT_F32 = 2
+
+EXPORTED_SYMBOLS = [
+    "smc_map_create", "smc_map_destroy", "smc_map_build", "smc_map_sync", "smc_map_info",
+    "smc_map_export", "smc_weight_packed_bytes", "smc_weight_pack", "smc_conv_forward",
+    "smc_status_string", "smc_last_error", "smc_version",
+]
+
+
+class SmconvError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+class MapInfo(ctypes.Structure):
+    _fields_ = [
+        ("n", ctypes.c_int64), ("route", ctypes.c_int32), ("key_bits", ctypes.c_int32),
+        ("origin", ctypes.c_int32 * 3), ("extent", ctypes.c_int32 * 3),
+        ("batch", ctypes.c_int32), ("tile_m", ctypes.c_int32), ("grid_cells", ctypes.c_int64),
+        ("pairs", ctypes.c_int64), ("pairs_padded", ctypes.c_int64), ("n_tiles", ctypes.c_int64),
+        ("tap_count", ctypes.c_int64 * 27), ("status", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """Load libsmconv.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is not built; run `python __graft_entry__.py build` "
+                           "(hipcc --offload-arch=gfx950) first")
+    L = ctypes.CDLL(_LIB_PATH)
+    vp, i32, i64, u32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint
+    L.smc_map_create.argtypes = [ctypes.POINTER(vp)]
+    L.smc_map_destroy.argtypes = [vp]
+    L.smc_map_build.argtypes = [vp, vp, i64, i32, vp, i32, i32, i32, u32, vp]
+    L.smc_map_sync.argtypes = [vp]
+    L.smc_map_info.argtypes = [vp, ctypes.POINTER(MapInfo)]
+    L.smc_map_export.argtypes = [vp, vp, vp, vp, vp, vp, vp]
+    L.smc_weight_packed_bytes.argtypes = [i32, i32]
+    L.smc_weight_packed_bytes.restype = ctypes.c_size_t
+    L.smc_weight_pack.argtypes = [vp, i32, i32, vp, vp]
+    L.smc_conv_forward.argtypes = [vp, vp, i32, vp, i32, vp, u32, vp]
+    L.smc_status_string.argtypes = [i32]
+    L.smc_status_string.restype = ctypes.c_char_p
+    L.smc_last_error.argtypes = []
+    L.smc_last_error.restype = ctypes.c_char_p
+    L.smc_version.restype = i32
+    for name in ("smc_map_create", "smc_map_destroy", "smc_map_build", "smc_map_sync",
+                 "smc_map_info", "smc_map_export", "smc_weight_pack", "smc_conv_forward"):
+        getattr(L, name).restype = i32
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != 0:
+        L = lib()
+        raise SmconvError(status, f"{L.smc_status_string(status).decode()}: "
+                                  f"{L.smc_last_error().decode()}")
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, dtype, name, ndim=None):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+class PackedWeights:
+    """Weights packed for the GEMM; holds the device buffer."""
+
+    def __init__(self, buf, c_in: int, c_out: int):
+        self.buf, self.c_in, self.c_out = buf, c_in, c_out
+
+
+def pack_weights(w, stream=None) -> PackedWeights:
+    """bf16 [27, C_in, C_out] CUDA tensor -> PackedWeights."""
+    import torch
+    _need(w, torch.bfloat16, "w", 3)
+    if w.shape[0] != 27:
+        raise ValueError("w must be [27, C_in, C_out]")
+    c_in, c_out = int(w.shape[1]), int(w.shape[2])
+    L = lib()
+    nbytes = L.smc_weight_packed_bytes(c_in, c_out)
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
+    _check(L.smc_weight_pack(ctypes.c_void_p(w.data_ptr()), c_in, c_out,
+                             ctypes.c_void_p(buf.data_ptr()), _stream(stream)))
+    return PackedWeights(buf, c_in, c_out)
+
+
+class KernelMap:
+    """A kernel map handle: built from coordinates, reused by every layer."""
+
+    def __init__(self):
+        self._h = ctypes.c_void_p()
+        _check(lib().smc_map_create(ctypes.byref(self._h)))
+        self.n = 0
+        self._coords = None
+
+    def close(self):
+        if self._h:
+            lib().smc_map_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def build(self, coords, spatial_shape=None, batch_size: int = 0, route: str = "auto",
+              sync: bool = True, stream=None) -> "KernelMap":
+        """coords: int32 [N, 4] (b, x, y, z) or [N, 3] (x, y, z) CUDA tensor."""
+        import torch
+        _need(coords, torch.int32, "coords", 2)
+        n, ncols = int(coords.shape[0]), int(coords.shape[1])
+        shape = None
+        if spatial_shape is not None:
+            shape = (ctypes.c_int32 * 3)(*[int(v) for v in spatial_shape])
+        flags = 0 if sync else SMC_BUILD_ASYNC
+        self._coords = coords          # keep alive while the stream reads it
+        self.n = n
+        _check(lib().smc_map_build(self._h, ctypes.c_void_p(coords.data_ptr() if n else 0), n,
+                                   ncols, shape, int(batch_size), 3, ROUTES[route], flags,
+                                   _stream(stream)))
+        return self
+
+    def sync(self):
+        _check(lib().smc_map_sync(self._h))
+
+    def info(self) -> dict:
+        inf = MapInfo()
+        _check(lib().smc_map_info(self._h, ctypes.byref(inf)))
+        return dict(n=inf.n, route=_ROUTE_NAMES.get(inf.route, inf.route), key_bits=inf.key_bits,
+                    origin=tuple(inf.origin), extent=tuple(inf.extent), batch=inf.batch,
+                    tile_m=inf.tile_m, grid_cells=inf.grid_cells, pairs=inf.pairs,
+                    pairs_padded=inf.pairs_padded, n_tiles=inf.n_tiles,
+                    tap_count=list(inf.tap_count), status=inf.status)
+
+    def export(self) -> dict:
+        """Copy nbr, mask, perm, pair lists and tap offsets to numpy (host)."""
+        import numpy as np
+        info = self.info()
+        n, p = info["n"], info["pairs"]
+        out = dict(nbr=np.empty((n, 27), np.int32), mask=np.empty(n, np.uint32),
+                   perm=np.empty(n, np.int32), pair_in=np.empty(p, np.int32),
+                   pair_out=np.empty(p, np.int32), tap_off=np.empty(28, np.int64))
+
+        def ptr(a):
+            return ctypes.c_void_p(a.ctypes.data) if a.size else None
+        _check(lib().smc_map_export(self._h, ptr(out["nbr"]), ptr(out["mask"]), ptr(out["perm"]),
+                                    ptr(out["pair_in"]), ptr(out["pair_out"]),
+                                    ptr(out["tap_off"])))
+        return out
+
+    def forward(self, x, w: PackedWeights, relu: bool = False, out=None, out_f32: bool = False,
+                stream=None):
+        """x: bf16 [N, C_in] CUDA tensor -> bf16 [N, C_out] (float32 with out_f32)."""
+        import torch
+        _need(x, torch.bfloat16, "x", 2)
+        if x.shape[0] != self.n:
+            raise ValueError(f"x has {x.shape[0]} rows, the map has {self.n}")
+        if x.shape[1] != w.c_in:
+            raise ValueError(f"x has {x.shape[1]} channels, weights expect {w.c_in}")
+        odt = torch.float32 if out_f32 else torch.bfloat16
+        if out is None:
+            out = torch.empty((self.n, w.c_out), dtype=odt, device=x.device)
+        else:
+            _need(out, odt, "out", 2)
+            if tuple(out.shape) != (self.n, w.c_out):
+                raise ValueError("out has the wrong shape")
+        _check(lib().smc_conv_forward(self._h, ctypes.c_void_p(x.data_ptr()), w.c_in,
+                                      ctypes.c_void_p(w.buf.data_ptr()), w.c_out,
+                                      ctypes.c_void_p(out.data_ptr()),
+                                      (SMC_FWD_RELU if relu else 0)
+                                      | (SMC_FWD_OUT_F32 if out_f32 else 0), _stream(stream)))
+        return out
+
+
+def subm_conv3d(coords, x, w, spatial_shape=None, relu: bool = False, route: str = "auto"):
+    """One layer from raw inputs: builds a map, packs w, runs the layer."""
+    m = KernelMap().build(coords, spatial_shape=spatial_shape, route=route)
+    y = m.forward(x, pack_weights(w), relu=relu)
+    return y

@@ -1,0 +1,298 @@
+// Kernel-map construction: bounding box, the dense presence-grid route and
+// the sorted packed-key route. Both routes emit the same neighbour table
+// nbr[n][27] (row of c_i + d_k, or -1) and 27-bit masks (bit k set iff the
+// neighbour exists), as described in "Sparse convolution in FP32" (DriveRT),
+// "Neighbour masks and sorted rows". The two routes and their trade-off
+// (O(volume) grid vs. one sort plus binary searches, flat in volume) follow
+// "[Kernel] Add submanifold sparse 3D convolution (bf16 implicit GEMM,
+// gfx950)", Design, the mapper table.
+#include "smc_internal.h"
+
+#include <climits>
+
+namespace smc {
+namespace {
+
+__device__ inline bool load_rel(const int32_t* __restrict__ coords, int64_t i, const Geom& g,
+                                int& b, int& x, int& y, int& z) {
+    const int32_t* c = coords + i * g.ncols;
+    if (g.ncols == 4) {
+        b = c[0];
+        c += 1;
+    } else {
+        b = 0;
+    }
+    x = c[0] - g.origin[0];
+    y = c[1] - g.origin[1];
+    z = c[2] - g.origin[2];
+    return (unsigned)b < (unsigned)g.batch && (unsigned)x < (unsigned)g.ext[0] &&
+           (unsigned)y < (unsigned)g.ext[1] && (unsigned)z < (unsigned)g.ext[2];
+}
+
+// cell of a voxel in the grid padded by one cell on every side
+__device__ inline int64_t dense_cell(const Geom& g, int b, int x, int y, int z) {
+    return b * g.sz_b + (int64_t)(x + 1) * g.sz_x + (int64_t)(y + 1) * g.sz_y + (z + 1);
+}
+
+__global__ void k_state_init(MapState* st) {
+    int t = threadIdx.x;
+    if (t == 0) st->status = 0;
+    if (t < 3) st->bbox[t] = INT_MAX;
+    else if (t < 6) st->bbox[t] = INT_MIN;
+    else if (t == 6) st->bbox[6] = INT_MAX;
+    else if (t == 7) st->bbox[7] = INT_MIN;
+    if (t < 4) st->totals[t] = 0;
+    if (t < 28) st->tap_off[t] = 0;
+    if (t < 27) st->tap_count[t] = 0;
+}
+
+__device__ inline int wave_min(int v) {
+    for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
+    return v;
+}
+__device__ inline int wave_max(int v) {
+    for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+    return v;
+}
+
+__global__ __launch_bounds__(kBlock) void k_bbox(const int32_t* __restrict__ coords, int64_t n,
+                                                 int ncols, MapState* st) {
+    int lo[4] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};
+    int hi[4] = {INT_MIN, INT_MIN, INT_MIN, INT_MIN};
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int32_t* c = coords + i * ncols;
+        int b = ncols == 4 ? c[0] : 0;
+        const int32_t* p = c + (ncols == 4 ? 1 : 0);
+        for (int d = 0; d < 3; ++d) {
+            lo[d] = min(lo[d], p[d]);
+            hi[d] = max(hi[d], p[d]);
+        }
+        lo[3] = min(lo[3], b);
+        hi[3] = max(hi[3], b);
+    }
+    for (int d = 0; d < 4; ++d) {
+        lo[d] = wave_min(lo[d]);
+        hi[d] = wave_max(hi[d]);
+    }
+    if ((threadIdx.x & 63) == 0) {
+        for (int d = 0; d < 3; ++d) {
+            atomicMin(&st->bbox[d], lo[d]);
+            atomicMax(&st->bbox[3 + d], hi[d]);
+        }
+        atomicMin(&st->bbox[6], lo[3]);
+        atomicMax(&st->bbox[7], hi[3]);
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void k_fill_i32(int32_t* p, int64_t n, int32_t v) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = v;
+}
+
+// One thread per row: claim the row's grid cell. A second claimant of a cell
+// means two rows share coordinates.
+__global__ __launch_bounds__(kBlock) void k_dense_scatter(const int32_t* __restrict__ coords,
+                                                          int64_t n, Geom g,
+                                                          int32_t* __restrict__ grid,
+                                                          MapState* st) {
+    int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    int b, x, y, z;
+    if (!load_rel(coords, i, g, b, x, y, z)) {
+        atomicOr(&st->status, kStRange);
+        return;
+    }
+    int old = atomicCAS(&grid[dense_cell(g, b, x, y, z)], -1, (int)i);
+    if (old != -1) atomicOr(&st->status, kStDuplicate);
+}
+
+// 32 lanes per row (27 active): lane k reads the cell at offset d_k. The
+// wave's ballot of hits gives both rows' masks directly.
+__global__ __launch_bounds__(kBlock) void k_dense_lookup(const int32_t* __restrict__ coords,
+                                                         int64_t n, Geom g,
+                                                         const int32_t* __restrict__ grid,
+                                                         int32_t* __restrict__ nbr,
+                                                         uint32_t* __restrict__ mask) {
+    int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    int64_t row = t >> 5;
+    int k = (int)(t & 31);
+    bool live = row < n && k < kTaps;
+    int v = -1;
+    if (live) {
+        int b, x, y, z;
+        if (load_rel(coords, row, g, b, x, y, z)) {
+            int dx = k / 9 - 1, dy = (k / 3) % 3 - 1, dz = k % 3 - 1;
+            v = grid[dense_cell(g, b, x, y, z) + dx * g.sz_x + dy * g.sz_y + dz];
+        }
+        nbr[row * kTaps + k] = v;
+    }
+    uint64_t hits = __ballot(v >= 0);
+    if (row < n && k == 0) mask[row] = (uint32_t)(hits >> (threadIdx.x & 32));
+}
+
+// Restore the grid's all-empty state: only the cells this build claimed.
+__global__ __launch_bounds__(kBlock) void k_dense_clear(const int32_t* __restrict__ coords,
+                                                        int64_t n, Geom g,
+                                                        int32_t* __restrict__ grid) {
+    int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    int b, x, y, z;
+    if (load_rel(coords, i, g, b, x, y, z)) grid[dense_cell(g, b, x, y, z)] = -1;
+}
+
+// Packed key of a voxel, fields (b | x+1 | y+1 | z+1) from high to low. The
+// one-cell padding keeps every neighbour query inside its field, so the key
+// of q + d is key(q) + packed(d) with no carry between fields (the
+// packed(q+d) = packed(q) + packed(d) property of the Z-Delta mapper).
+template <typename K>
+__global__ __launch_bounds__(kBlock) void k_make_keys(const int32_t* __restrict__ coords,
+                                                      int64_t n, Geom g, K* __restrict__ keys,
+                                                      MapState* st) {
+    int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    int b, x, y, z;
+    K key;
+    if (load_rel(coords, i, g, b, x, y, z)) {
+        key = (K)b;
+        key = (key << g.wx) | (K)(x + 1);
+        key = (key << g.wy) | (K)(y + 1);
+        key = (key << g.wz) | (K)(z + 1);
+    } else {
+        atomicOr(&st->status, kStRange);
+        key = ~(K)0;
+    }
+    keys[i] = key;
+}
+
+template <typename K>
+__device__ inline int64_t lower_bound(const K* __restrict__ keys, int64_t n, K t) {
+    int64_t lo = 0, len = n;
+    while (len > 0) {
+        int64_t half = len >> 1;
+        if (keys[lo + half] < t) {
+            lo += half + 1;
+            len -= half + 1;
+        } else {
+            len = half;
+        }
+    }
+    return lo;
+}
+
+// 16 lanes per sorted key (9 active), one per (dx, dy) column. The three
+// taps of a column (dz = -1, 0, +1) have consecutive keys, and so sit at
+// consecutive sorted positions when present: one binary search for the
+// column's lowest key, then up to three compares walking forward. The
+// centre column needs no search: its keys are at s - 1, s, s + 1.
+template <typename K>
+__global__ __launch_bounds__(kBlock) void k_sorted_lookup(const K* __restrict__ keys,
+                                                          const uint32_t* __restrict__ vals,
+                                                          int64_t n, Geom g,
+                                                          int32_t* __restrict__ nbr,
+                                                          uint32_t* __restrict__ mask,
+                                                          MapState* st) {
+    int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    int64_t s = t >> 4;
+    int c = (int)(t & 15);
+    uint32_t bits = 0;
+    if (s < n && c < 9) {
+        K q = keys[s];
+        int row = (int)vals[s];
+        int dx = c / 3 - 1, dy = c % 3 - 1;
+        K delta = (K)((int64_t)dx * ((int64_t)1 << (g.wy + g.wz))) +
+                  (K)((int64_t)dy * ((int64_t)1 << g.wz));
+        K first = q + delta - (K)1;
+        int64_t j;
+        if (c == 4) {
+            j = (s > 0 && keys[s - 1] == first) ? s - 1 : s;
+            if (s + 1 < n && keys[s + 1] == q) atomicOr(&st->status, kStDuplicate);
+        } else {
+            j = lower_bound(keys, n, first);
+        }
+#pragma unroll
+        for (int dz = 0; dz < 3; ++dz) {
+            int hit = -1;
+            if (j < n && keys[j] == first + (K)dz) {
+                hit = (int)vals[j];
+                ++j;
+            }
+            nbr[(int64_t)row * kTaps + 3 * c + dz] = hit;
+            if (hit >= 0) bits |= 1u << (3 * c + dz);
+        }
+    }
+    bits |= __shfl_xor(bits, 8, 16);
+    bits |= __shfl_xor(bits, 4, 16);
+    bits |= __shfl_xor(bits, 2, 16);
+    bits |= __shfl_xor(bits, 1, 16);
+    if (s < n && c == 0) mask[vals[s]] = bits;
+}
+
+inline unsigned blocks_for(int64_t threads) {
+    int64_t b = (threads + kBlock - 1) / kBlock;
+    return (unsigned)(b < 1 ? 1 : b);
+}
+
+}  // namespace
+
+hipError_t launch_state_init(MapState* st, hipStream_t s) {
+    k_state_init<<<1, 64, 0, s>>>(st);
+    return hipGetLastError();
+}
+
+hipError_t launch_bbox(const int32_t* coords, int64_t n, int ncols, MapState* st, hipStream_t s) {
+    unsigned blocks = blocks_for(n);
+    if (blocks > 1024) blocks = 1024;
+    k_bbox<<<blocks, kBlock, 0, s>>>(coords, n, ncols, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    unsigned blocks = blocks_for(n);
+    if (blocks > 65536) blocks = 65536;
+    k_fill_i32<<<blocks, kBlock, 0, s>>>(p, n, v);
+    return hipGetLastError();
+}
+
+hipError_t launch_dense_scatter(const int32_t* coords, int64_t n, const Geom& g, int32_t* grid,
+                                MapState* st, hipStream_t s) {
+    k_dense_scatter<<<blocks_for(n), kBlock, 0, s>>>(coords, n, g, grid, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_dense_lookup(const int32_t* coords, int64_t n, const Geom& g, const int32_t* grid,
+                               int32_t* nbr, uint32_t* mask, hipStream_t s) {
+    k_dense_lookup<<<blocks_for(n * 32), kBlock, 0, s>>>(coords, n, g, grid, nbr, mask);
+    return hipGetLastError();
+}
+
+hipError_t launch_dense_clear(const int32_t* coords, int64_t n, const Geom& g, int32_t* grid,
+                              hipStream_t s) {
+    k_dense_clear<<<blocks_for(n), kBlock, 0, s>>>(coords, n, g, grid);
+    return hipGetLastError();
+}
+
+hipError_t launch_make_keys(const int32_t* coords, int64_t n, const Geom& g, bool wide, void* keys,
+                            MapState* st, hipStream_t s) {
+    if (wide)
+        k_make_keys<uint64_t><<<blocks_for(n), kBlock, 0, s>>>(coords, n, g, (uint64_t*)keys, st);
+    else
+        k_make_keys<uint32_t><<<blocks_for(n), kBlock, 0, s>>>(coords, n, g, (uint32_t*)keys, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_sorted_lookup(const void* keys, const uint32_t* vals, int64_t n, const Geom& g,
+                                bool wide, int32_t* nbr, uint32_t* mask, MapState* st,
+                                hipStream_t s) {
+    if (wide)
+        k_sorted_lookup<uint64_t><<<blocks_for(n * 16), kBlock, 0, s>>>(
+            (const uint64_t*)keys, vals, n, g, nbr, mask, st);
+    else
+        k_sorted_lookup<uint32_t><<<blocks_for(n * 16), kBlock, 0, s>>>(
+            (const uint32_t*)keys, vals, n, g, nbr, mask, st);
+    return hipGetLastError();
+}
+
+}  // namespace smc

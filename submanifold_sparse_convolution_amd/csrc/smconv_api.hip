@@ -1,0 +1,499 @@
+// C ABI: map handles, the map build pipeline, weight packing and the
+// forward layer. See include/smconv.h for the contract of each call.
+#include "../../include/smconv.h"
+#include "smc_internal.h"
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+using namespace smc;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+#define SMC_HIP(call)                                                                          \
+    do {                                                                                       \
+        hipError_t e_ = (call);                                                                \
+        if (e_ != hipSuccess)                                                                  \
+            return fail(SMC_ERR_HIP, "%s failed: %s (%s:%d)", #call, hipGetErrorString(e_),    \
+                        __FILE__, __LINE__);                                                   \
+    } while (0)
+
+// Grow-only device buffer.
+struct DevBuf {
+    void* p = nullptr;
+    size_t bytes = 0;
+    int ensure(size_t want) {
+        if (want <= bytes) return SMC_OK;
+        if (p) {
+            (void)hipFree(p);
+            p = nullptr;
+            bytes = 0;
+        }
+        size_t alloc = want < 256 ? 256 : want;
+        if (hipMalloc(&p, alloc) != hipSuccess) {
+            (void)hipGetLastError();
+            p = nullptr;
+            return fail(SMC_ERR_ALLOC, "hipMalloc(%zu) failed", alloc);
+        }
+        bytes = alloc;
+        return SMC_OK;
+    }
+    void release() {
+        if (p) (void)hipFree(p);
+        p = nullptr;
+        bytes = 0;
+    }
+    template <typename T> T* as() const { return static_cast<T*>(p); }
+};
+
+constexpr int64_t kMaxRows = (int64_t)1 << 26;                 // keeps 27 n + pads < 2^31
+constexpr int64_t kDenseBudgetBytes = (int64_t)4 << 30;        // auto route: grid <= 4 GiB
+
+int bit_len(int64_t v) {   // bits needed to hold 0..v
+    int b = 0;
+    while (v > 0) {
+        ++b;
+        v >>= 1;
+    }
+    return b;
+}
+
+}  // namespace
+
+struct smc_map {
+    int device = -1;
+    int n_cu = 0;
+    hipEvent_t done = nullptr;
+    MapState* host_state = nullptr;   // pinned
+    bool built = false;
+    bool pending = false;             // a build whose device checks are not read yet
+    int build_status = SMC_OK;
+    int64_t n = 0;
+    int route = 0;
+    int key_bits = 0;
+    bool wide = false;
+    Geom geom{};
+    int64_t grid_cells = 0;
+    // device buffers
+    DevBuf state;                     // MapState
+    DevBuf grid;                      // int32 presence grid (dense route), kept all -1
+    int64_t grid_clean_cells = 0;     // prefix of grid known to be -1
+    DevBuf keys0, keys1, keys2;       // packed keys (u32 or u64)
+    DevBuf vals0, vals1;              // u32
+    DevBuf radix_counts;
+    DevBuf nbr, mask, mkey0, mkey1, mval0, mval1;
+    const uint32_t* perm = nullptr;   // points into mval0 or mval1
+    DevBuf chunk_counts;
+    DevBuf pair_in, pair_out, tile_tap;
+    int64_t pair_cap = 0;
+    DevBuf acc;                       // float32 accumulator, kept all zero between forwards
+    size_t acc_clean_bytes = 0;
+};
+
+namespace {
+
+int ensure_device(smc_map* m) {
+    int dev = 0;
+    SMC_HIP(hipGetDevice(&dev));
+    if (m->device < 0) {
+        m->device = dev;
+        SMC_HIP(hipDeviceGetAttribute(&m->n_cu, hipDeviceAttributeMultiprocessorCount, dev));
+        SMC_HIP(hipEventCreateWithFlags(&m->done, hipEventDisableTiming));
+        if (hipHostMalloc((void**)&m->host_state, sizeof(MapState), hipHostMallocDefault) !=
+            hipSuccess) {
+            (void)hipGetLastError();
+            m->host_state = nullptr;
+            return fail(SMC_ERR_ALLOC, "hipHostMalloc of the readback record failed");
+        }
+        int rc = m->state.ensure(sizeof(MapState));
+        if (rc) return rc;
+    } else if (dev != m->device) {
+        return fail(SMC_ERR_STATE, "map was created on device %d, current device is %d",
+                    m->device, dev);
+    }
+    return SMC_OK;
+}
+
+int wait_build(smc_map* m) {
+    if (!m->pending) return SMC_OK;
+    SMC_HIP(hipEventSynchronize(m->done));
+    m->pending = false;
+    uint32_t st = m->host_state->status;
+    if (st & kStDuplicate) {
+        m->build_status = SMC_ERR_DUPLICATE;
+        return fail(SMC_ERR_DUPLICATE, "two rows share the same (b, x, y, z)");
+    }
+    if (st & kStRange) {
+        m->build_status = SMC_ERR_RANGE;
+        return fail(SMC_ERR_RANGE, "a coordinate lies outside the spatial shape or batch range");
+    }
+    m->build_status = SMC_OK;
+    return SMC_OK;
+}
+
+int ensure_grid(smc_map* m, int64_t cells, hipStream_t s) {
+    size_t bytes = (size_t)cells * 4;
+    if (bytes > m->grid.bytes) {
+        int rc = m->grid.ensure(bytes);
+        if (rc) return rc;
+        m->grid_clean_cells = 0;
+    }
+    if (m->grid_clean_cells < cells) {
+        // fill the whole allocation once; later builds only clear what they used
+        int64_t all = (int64_t)(m->grid.bytes / 4);
+        SMC_HIP(launch_fill_i32(m->grid.as<int32_t>(), all, -1, s));
+        m->grid_clean_cells = all;
+    }
+    return SMC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int smc_version(void) { return 100; }
+
+const char* smc_status_string(int status) {
+    switch (status) {
+        case SMC_OK: return "ok";
+        case SMC_ERR_ARG: return "invalid argument";
+        case SMC_ERR_DUPLICATE: return "duplicate coordinates";
+        case SMC_ERR_RANGE: return "coordinate out of range";
+        case SMC_ERR_KEY_OVERFLOW: return "packed key needs more than 64 bits";
+        case SMC_ERR_ALLOC: return "allocation failed";
+        case SMC_ERR_HIP: return "HIP runtime error";
+        case SMC_ERR_STATE: return "map not built or built with an error";
+        case SMC_ERR_UNSUPPORTED: return "unsupported";
+        case SMC_ERR_GRID: return "dense grid too large";
+        default: return "unknown status";
+    }
+}
+
+const char* smc_last_error(void) { return g_last_error.c_str(); }
+
+int smc_map_create(smc_map** out) {
+    if (!out) return fail(SMC_ERR_ARG, "out is NULL");
+    smc_map* m = new (std::nothrow) smc_map();
+    if (!m) return fail(SMC_ERR_ALLOC, "out of host memory");
+    *out = m;
+    return SMC_OK;
+}
+
+int smc_map_destroy(smc_map* m) {
+    if (!m) return SMC_OK;
+    if (m->device >= 0) {
+        int cur = 0;
+        (void)hipGetDevice(&cur);
+        (void)hipSetDevice(m->device);
+        (void)hipDeviceSynchronize();
+        DevBuf* bufs[] = {&m->state, &m->grid, &m->keys0, &m->keys1, &m->keys2,
+                          &m->vals0, &m->vals1, &m->radix_counts, &m->nbr, &m->mask,
+                          &m->mkey0, &m->mkey1, &m->mval0, &m->mval1, &m->chunk_counts,
+                          &m->pair_in, &m->pair_out, &m->tile_tap, &m->acc};
+        for (DevBuf* b : bufs) b->release();
+        if (m->host_state) (void)hipHostFree(m->host_state);
+        if (m->done) (void)hipEventDestroy(m->done);
+        (void)hipSetDevice(cur);
+    }
+    delete m;
+    return SMC_OK;
+}
+
+int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
+                  const int32_t* spatial_shape, int batch_size, int kernel_size, int route,
+                  unsigned flags, void* stream) {
+    if (!m) return fail(SMC_ERR_ARG, "map is NULL");
+    if (kernel_size != 3) return fail(SMC_ERR_UNSUPPORTED, "kernel_size %d (only 3)", kernel_size);
+    if (ncols != 3 && ncols != 4) return fail(SMC_ERR_ARG, "ncols must be 3 or 4, got %d", ncols);
+    if (n < 0 || n > kMaxRows) return fail(SMC_ERR_ARG, "n = %lld out of [0, 2^26]", (long long)n);
+    if (n > 0 && !coords) return fail(SMC_ERR_ARG, "coords is NULL");
+    if (route < SMC_ROUTE_AUTO || route > SMC_ROUTE_SORTED)
+        return fail(SMC_ERR_ARG, "bad route %d", route);
+    if (spatial_shape)
+        for (int d = 0; d < 3; ++d)
+            if (spatial_shape[d] < 1)
+                return fail(SMC_ERR_ARG, "spatial_shape[%d] = %d", d, spatial_shape[d]);
+    int rc = ensure_device(m);
+    if (rc) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    // a previous async build must not be overwritten while still unread
+    if (m->pending) SMC_HIP(hipEventSynchronize(m->done));
+    m->pending = false;
+    m->built = false;
+    m->perm = nullptr;
+    MapState* st = m->state.as<MapState>();
+    SMC_HIP(launch_state_init(st, s));
+
+    // ---- geometry: explicit shape, or the bounding box (one read) ----
+    Geom g{};
+    g.ncols = ncols;
+    const bool need_bbox = n > 0 && (!spatial_shape || (ncols == 4 && batch_size <= 0));
+    int32_t bbox[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (need_bbox) {
+        SMC_HIP(launch_bbox(coords, n, ncols, st, s));
+        SMC_HIP(hipMemcpyAsync(m->host_state, st, sizeof(MapState), hipMemcpyDeviceToHost, s));
+        SMC_HIP(hipStreamSynchronize(s));
+        memcpy(bbox, m->host_state->bbox, sizeof(bbox));
+    }
+    if (spatial_shape) {
+        for (int d = 0; d < 3; ++d) {
+            g.origin[d] = 0;
+            g.ext[d] = spatial_shape[d];
+        }
+    } else if (n > 0) {
+        for (int d = 0; d < 3; ++d) {
+            g.origin[d] = bbox[d];
+            int64_t e = (int64_t)bbox[3 + d] - bbox[d] + 1;
+            if (e > ((int64_t)1 << 30)) return fail(SMC_ERR_RANGE, "extent %lld too large", (long long)e);
+            g.ext[d] = (int32_t)e;
+        }
+    } else {
+        for (int d = 0; d < 3; ++d) g.ext[d] = 1;
+    }
+    if (ncols == 3) {
+        g.batch = 1;
+    } else if (batch_size > 0) {
+        g.batch = batch_size;
+    } else if (n > 0) {
+        if (bbox[6] < 0) return fail(SMC_ERR_RANGE, "negative batch index %d", bbox[6]);
+        g.batch = bbox[7] + 1;
+    } else {
+        g.batch = 1;
+    }
+
+    // ---- route by grid volume ----
+    const double cells_d = (double)g.batch * (g.ext[0] + 2.0) * (g.ext[1] + 2.0) * (g.ext[2] + 2.0);
+    const bool dense_addressable = cells_d < 2147483648.0;
+    int chosen;
+    if (route == SMC_ROUTE_DENSE) {
+        if (!dense_addressable)
+            return fail(SMC_ERR_GRID, "dense grid of %.3g cells exceeds 2^31", cells_d);
+        chosen = SMC_ROUTE_DENSE;
+    } else if (route == SMC_ROUTE_SORTED) {
+        chosen = SMC_ROUTE_SORTED;
+    } else {
+        chosen = (dense_addressable && cells_d * 4.0 <= (double)kDenseBudgetBytes)
+                     ? SMC_ROUTE_DENSE : SMC_ROUTE_SORTED;
+    }
+    g.sz_y = g.ext[2] + 2;
+    g.sz_x = (int64_t)(g.ext[1] + 2) * g.sz_y;
+    g.sz_b = (int64_t)(g.ext[0] + 2) * g.sz_x;
+    int key_bits = 0;
+    if (chosen == SMC_ROUTE_SORTED) {
+        g.wz = bit_len((int64_t)g.ext[2] + 1);
+        g.wy = bit_len((int64_t)g.ext[1] + 1);
+        g.wx = bit_len((int64_t)g.ext[0] + 1);
+        g.wb = bit_len((int64_t)g.batch - 1);
+        key_bits = g.wz + g.wy + g.wx + g.wb;
+        if (key_bits > 64)
+            return fail(SMC_ERR_KEY_OVERFLOW, "packed key needs %d bits", key_bits);
+    }
+    m->geom = g;
+    m->route = chosen;
+    m->key_bits = key_bits;
+    m->wide = key_bits > 32;
+    m->grid_cells = chosen == SMC_ROUTE_DENSE ? (int64_t)cells_d : 0;
+    m->n = n;
+
+    // ---- buffers ----
+    const int64_t nn = n > 0 ? n : 1;
+    const int64_t n_chunks = (nn + kChunk - 1) / kChunk;
+    const int64_t pair_cap = 27 * nn + 27 * (int64_t)kTileM;
+    if ((rc = m->nbr.ensure((size_t)nn * kTaps * 4)) || (rc = m->mask.ensure((size_t)nn * 4)) ||
+        (rc = m->mkey0.ensure((size_t)nn * 4)) || (rc = m->mkey1.ensure((size_t)nn * 4)) ||
+        (rc = m->mval0.ensure((size_t)nn * 4)) || (rc = m->mval1.ensure((size_t)nn * 4)) ||
+        (rc = m->radix_counts.ensure(radix_counts_elems(nn) * 4)) ||
+        (rc = m->chunk_counts.ensure((size_t)n_chunks * kTaps * 4)) ||
+        (rc = m->pair_in.ensure((size_t)pair_cap * 4)) ||
+        (rc = m->pair_out.ensure((size_t)pair_cap * 4)) ||
+        (rc = m->tile_tap.ensure((size_t)(pair_cap / kTileM + 1) * 4)))
+        return rc;
+    m->pair_cap = pair_cap;
+
+    if (n > 0) {
+        int32_t* nbr = m->nbr.as<int32_t>();
+        uint32_t* mask = m->mask.as<uint32_t>();
+        if (chosen == SMC_ROUTE_DENSE) {
+            if ((rc = ensure_grid(m, m->grid_cells, s))) return rc;
+            int32_t* grid = m->grid.as<int32_t>();
+            SMC_HIP(launch_dense_scatter(coords, n, g, grid, st, s));
+            SMC_HIP(launch_dense_lookup(coords, n, g, grid, nbr, mask, s));
+            SMC_HIP(launch_dense_clear(coords, n, g, grid, s));
+        } else {
+            const size_t kb = (size_t)nn * (m->wide ? 8 : 4);
+            if ((rc = m->keys0.ensure(kb)) || (rc = m->keys1.ensure(kb)) ||
+                (rc = m->keys2.ensure(kb)) || (rc = m->vals0.ensure((size_t)nn * 4)) ||
+                (rc = m->vals1.ensure((size_t)nn * 4)))
+                return rc;
+            SMC_HIP(launch_make_keys(coords, n, g, m->wide, m->keys0.p, st, s));
+            const void* skeys;
+            const uint32_t* svals;
+            if (m->wide) {
+                SMC_HIP(radix_sort_u64(m->keys0.as<uint64_t>(), nullptr, n, key_bits,
+                                       m->keys1.as<uint64_t>(), m->keys2.as<uint64_t>(),
+                                       m->vals0.as<uint32_t>(), m->vals1.as<uint32_t>(),
+                                       m->radix_counts.as<uint32_t>(),
+                                       (const uint64_t**)&skeys, &svals, s));
+            } else {
+                SMC_HIP(radix_sort_u32(m->keys0.as<uint32_t>(), nullptr, n, key_bits,
+                                       m->keys1.as<uint32_t>(), m->keys2.as<uint32_t>(),
+                                       m->vals0.as<uint32_t>(), m->vals1.as<uint32_t>(),
+                                       m->radix_counts.as<uint32_t>(),
+                                       (const uint32_t**)&skeys, &svals, s));
+            }
+            SMC_HIP(launch_sorted_lookup(skeys, svals, n, g, m->wide, nbr, mask, st, s));
+        }
+        // rows ordered by (mask, row)
+        const uint32_t* sorted_masks;
+        SMC_HIP(radix_sort_u32(mask, nullptr, n, kTaps, m->mkey0.as<uint32_t>(),
+                               m->mkey1.as<uint32_t>(), m->mval0.as<uint32_t>(),
+                               m->mval1.as<uint32_t>(), m->radix_counts.as<uint32_t>(),
+                               &sorted_masks, &m->perm, s));
+        int32_t* counts = m->chunk_counts.as<int32_t>();
+        SMC_HIP(launch_pair_count(m->perm, mask, n, counts, s));
+        SMC_HIP(launch_pair_scan(counts, n, kTileM, st, m->pair_in.as<int32_t>(),
+                                 m->pair_out.as<int32_t>(), m->tile_tap.as<int32_t>(), s));
+        SMC_HIP(launch_pair_write(m->perm, mask, nbr, n, counts, m->pair_in.as<int32_t>(),
+                                  m->pair_out.as<int32_t>(), s));
+    }
+    SMC_HIP(hipMemcpyAsync(m->host_state, st, sizeof(MapState), hipMemcpyDeviceToHost, s));
+    SMC_HIP(hipEventRecord(m->done, s));
+    m->pending = true;
+    m->built = true;
+    m->build_status = SMC_OK;
+    if (flags & SMC_BUILD_ASYNC) return SMC_OK;
+    return wait_build(m);
+}
+
+int smc_map_sync(smc_map* m) {
+    if (!m) return fail(SMC_ERR_ARG, "map is NULL");
+    if (!m->built) return fail(SMC_ERR_STATE, "map was never built");
+    int rc = wait_build(m);
+    if (rc) return rc;
+    return m->build_status;
+}
+
+int smc_map_info(smc_map* m, smc_map_info_t* info) {
+    if (!m || !info) return fail(SMC_ERR_ARG, "NULL argument");
+    if (!m->built) return fail(SMC_ERR_STATE, "map was never built");
+    int rc = wait_build(m);
+    memset(info, 0, sizeof(*info));
+    info->n = m->n;
+    info->route = m->route;
+    info->key_bits = m->key_bits;
+    for (int d = 0; d < 3; ++d) {
+        info->origin[d] = m->geom.origin[d];
+        info->extent[d] = m->geom.ext[d];
+    }
+    info->batch = m->geom.batch;
+    info->tile_m = kTileM;
+    info->grid_cells = m->grid_cells;
+    const MapState& hs = *m->host_state;
+    info->pairs = hs.totals[0];
+    info->pairs_padded = hs.totals[1];
+    info->n_tiles = hs.totals[2];
+    for (int k = 0; k < kTaps; ++k) info->tap_count[k] = hs.tap_count[k];
+    info->status = rc ? rc : m->build_status;
+    return SMC_OK;
+}
+
+int smc_map_export(smc_map* m, int32_t* nbr, uint32_t* mask, int32_t* perm, int32_t* pair_in,
+                   int32_t* pair_out, int64_t* tap_off) {
+    if (!m) return fail(SMC_ERR_ARG, "map is NULL");
+    if (!m->built) return fail(SMC_ERR_STATE, "map was never built");
+    SMC_HIP(hipSetDevice(m->device));
+    (void)wait_build(m);
+    SMC_HIP(hipDeviceSynchronize());
+    const int64_t n = m->n;
+    const MapState& hs = *m->host_state;
+    if (n > 0) {
+        if (nbr) SMC_HIP(hipMemcpy(nbr, m->nbr.p, (size_t)n * kTaps * 4, hipMemcpyDeviceToHost));
+        if (mask) SMC_HIP(hipMemcpy(mask, m->mask.p, (size_t)n * 4, hipMemcpyDeviceToHost));
+        if (perm) SMC_HIP(hipMemcpy(perm, m->perm, (size_t)n * 4, hipMemcpyDeviceToHost));
+    }
+    if (tap_off) {
+        tap_off[0] = 0;
+        for (int k = 0; k < kTaps; ++k) tap_off[k + 1] = tap_off[k] + hs.tap_count[k];
+    }
+    if ((pair_in || pair_out) && n > 0) {
+        const int64_t padded = hs.totals[1];
+        std::vector<int32_t> tmp((size_t)std::max<int64_t>(padded, 1));
+        for (int which = 0; which < 2; ++which) {
+            int32_t* dst = which == 0 ? pair_in : pair_out;
+            if (!dst) continue;
+            const DevBuf& src = which == 0 ? m->pair_in : m->pair_out;
+            SMC_HIP(hipMemcpy(tmp.data(), src.p, (size_t)padded * 4, hipMemcpyDeviceToHost));
+            int64_t o = 0;
+            for (int k = 0; k < kTaps; ++k) {
+                memcpy(dst + o, tmp.data() + hs.tap_off[k], (size_t)hs.tap_count[k] * 4);
+                o += hs.tap_count[k];
+            }
+        }
+    }
+    return SMC_OK;
+}
+
+size_t smc_weight_packed_bytes(int c_in, int c_out) {
+    if (c_in < 1 || c_out < 1) return 0;
+    return packed_weight_bytes(c_in, c_out);
+}
+
+int smc_weight_pack(const uint16_t* w, int c_in, int c_out, void* out, void* stream) {
+    if (!w || !out) return fail(SMC_ERR_ARG, "NULL pointer");
+    if (c_in < 1 || c_out < 1) return fail(SMC_ERR_ARG, "c_in = %d, c_out = %d", c_in, c_out);
+    if (((uintptr_t)out & 15) != 0) return fail(SMC_ERR_ARG, "packed buffer not 16-byte aligned");
+    SMC_HIP(launch_weight_pack(w, c_in, c_out, out, (hipStream_t)stream));
+    return SMC_OK;
+}
+
+int smc_conv_forward(smc_map* m, const uint16_t* x, int c_in, const void* wpacked, int c_out,
+                     void* y, unsigned flags, void* stream) {
+    if (!m) return fail(SMC_ERR_ARG, "map is NULL");
+    if (!m->built) return fail(SMC_ERR_STATE, "map was never built");
+    if (!m->pending && m->build_status != SMC_OK)
+        return fail(SMC_ERR_STATE, "map build failed: %s", smc_status_string(m->build_status));
+    if (c_in < 1 || c_out < 1) return fail(SMC_ERR_ARG, "c_in = %d, c_out = %d", c_in, c_out);
+    if (c_in > 4096 || c_out > 4096) return fail(SMC_ERR_UNSUPPORTED, "channels above 4096");
+    if (m->n == 0) return SMC_OK;
+    if (!x || !wpacked || !y) return fail(SMC_ERR_ARG, "NULL pointer");
+    if (((uintptr_t)wpacked & 15) != 0) return fail(SMC_ERR_ARG, "packed weights not 16-byte aligned");
+    if ((c_in & 7) == 0 && ((uintptr_t)x & 15) != 0)
+        return fail(SMC_ERR_ARG, "x must be 16-byte aligned when c_in is a multiple of 8");
+    int dev = 0;
+    SMC_HIP(hipGetDevice(&dev));
+    if (dev != m->device) return fail(SMC_ERR_STATE, "map lives on device %d", m->device);
+    hipStream_t s = (hipStream_t)stream;
+    const size_t acc_bytes = (size_t)m->n * c_out * 4;
+    int rc = m->acc.ensure(acc_bytes);
+    if (rc) return rc;
+    if (m->acc_clean_bytes < m->acc.bytes) {
+        SMC_HIP(launch_fill_f32(m->acc.as<float>(), (int64_t)(m->acc.bytes / 4), s));
+        m->acc_clean_bytes = m->acc.bytes;
+    }
+    const int64_t max_tiles = m->pair_cap / kTileM;
+    SMC_HIP(launch_gemm(x, c_in, wpacked, c_out, m->pair_in.as<int32_t>(),
+                        m->pair_out.as<int32_t>(), m->tile_tap.as<int32_t>(),
+                        m->state.as<MapState>(), max_tiles, m->n_cu, m->acc.as<float>(), s));
+    SMC_HIP(launch_finalize(m->acc.as<float>(), y, (flags & SMC_FWD_OUT_F32) != 0,
+                            m->n * (int64_t)c_out, (flags & SMC_FWD_RELU) != 0, s));
+    return SMC_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+"""The C-ABI library loads and exports every symbol its header declares.
+
+Runs without a GPU: the calls made here only validate arguments or report
+static information, none launches a kernel.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "smconv.h")
+
+smc = pytest.importorskip("submanifold_sparse_convolution_amd")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(smc_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(smc.library_path()):
+        pytest.fail("libsmconv.so is not built (run __graft_entry__.build())")
+    return smc.lib()
+
+
+def test_header_declares_the_binding_symbols():
+    assert declared_functions() == sorted(smc.EXPORTED_SYMBOLS)
+
+
+def test_every_declared_symbol_is_exported(L):
+    nm = subprocess.run(["nm", "-D", "--defined-only", smc.library_path()],
+                        capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\b[Tt]\s+(smc_[a-z0-9_]+)$", nm, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(L, name) is not None
+
+
+def test_static_calls(L):
+    assert L.smc_version() >= 100
+    assert L.smc_status_string(0) == b"ok"
+    assert L.smc_status_string(2) == b"duplicate coordinates"
+    assert L.smc_status_string(999) == b"unknown status"
+    # packed weights: 27 taps x ceil(co/16) x ceil(ci/32) x 64 lanes x 16 bytes
+    assert L.smc_weight_packed_bytes(128, 128) == 27 * 8 * 4 * 64 * 16
+    assert L.smc_weight_packed_bytes(1, 1) == 27 * 1 * 1 * 64 * 16
+    assert L.smc_weight_packed_bytes(0, 5) == 0
+
+
+def test_argument_errors_without_gpu(L):
+    h = ctypes.c_void_p()
+    assert L.smc_map_create(ctypes.byref(h)) == 0
+    # kernel_size 5 -> unsupported; ncols 2 -> arg; n < 0 -> arg; no GPU work happens
+    assert L.smc_map_build(h, None, 0, 4, None, 0, 5, 0, 0, None) == 8
+    assert L.smc_map_build(h, None, 0, 2, None, 0, 3, 0, 0, None) == 1
+    assert L.smc_map_build(h, None, -1, 4, None, 0, 3, 0, 0, None) == 1
+    assert L.smc_map_build(h, None, 0, 4, None, 0, 3, 7, 0, None) == 1
+    assert b"route" in L.smc_last_error()
+    assert L.smc_map_build(None, None, 0, 4, None, 0, 3, 0, 0, None) == 1
+    info = smc.MapInfo()
+    assert L.smc_map_info(h, ctypes.byref(info)) == 7          # never built
+    assert L.smc_map_sync(h) == 7
+    assert L.smc_conv_forward(h, None, 16, None, 16, None, 0, None) == 7
+    assert L.smc_weight_pack(None, 16, 16, None, None) == 1
+    assert L.smc_map_destroy(h) == 0
+    assert L.smc_map_destroy(None) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    import importlib
+    mod = importlib.import_module("submanifold_sparse_convolution_amd")
+    monkeypatch.setattr(mod, "_LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(mod, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        mod.lib()

@@ -1,0 +1,158 @@
+"""GPU layer output vs the CPU oracle.
+
+bf16 output: |y - bf16(ref)| <= 2e-2 (1 + |ref|) elementwise (and at most one
+bf16 ulp from the oracle's own rounding); float32 accumulator: within
+1e-3 (1 + |ref|) elementwise and 1e-3 in relative L2. Integer-valued and
+one-hot inputs are exact in any summation order, so there the comparison
+is bit-exact.
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import smconv_oracle as so
+from _util import (bf16_bits_of, check_bf16_output, check_f32_acc, config, oracle_map,
+                   oracle_map_of, to_dev_bf16, to_dev_i32)
+
+pytestmark = pytest.mark.gpu
+
+smc = pytest.importorskip("submanifold_sparse_convolution_amd")
+
+
+def oracle_acc(om, xb, wb):
+    x = so.bf16_bits_to_f64(xb)
+    w = so.bf16_bits_to_f64(wb)
+    return so.conv_accumulate(x, w, om["pair_in"], om["pair_out"], om["tap_off"], x.shape[0])
+
+
+def run_gpu(coords, xb, wb, spatial_shape=None, route="auto", relu=False, out_f32=False):
+    m = smc.KernelMap().build(to_dev_i32(coords), spatial_shape=spatial_shape, route=route)
+    wp = smc.pack_weights(to_dev_bf16(wb))
+    y = m.forward(to_dev_bf16(xb), wp, relu=relu, out_f32=out_f32)
+    out = y.cpu().numpy() if out_f32 else bf16_bits_of(y)
+    m.close()
+    return out
+
+
+@pytest.mark.parametrize("name", ["tiny", "lidar", "deep", "wide"])
+def test_workload_layer(name):
+    w, coords = config(name)
+    c = w.channels
+    xb = synth.features(w.n, c, w.seed)
+    wb = synth.weights(c, c, w.seed)
+    print(f"conv parity {name} n={w.n} c={c}", flush=True)
+    ref = oracle_acc(oracle_map(name), xb, wb)
+    y = run_gpu(coords, xb, wb, spatial_shape=w.grid)
+    check_bf16_output(y, ref, name)
+    acc = run_gpu(coords, xb, wb, spatial_shape=w.grid, out_f32=True)
+    check_f32_acc(acc, ref, name)
+
+
+@pytest.mark.parametrize("route", ["dense", "sorted"])
+def test_integer_inputs_exact(route):
+    coords = synth.tiny_coords(seed=3, n=3000, side=20)
+    xb = synth.int_features(3000, 64, 3)
+    wb = synth.int_weights(64, 48, 3)
+    ref = oracle_acc(oracle_map_of(coords), xb, wb)
+    acc = run_gpu(coords, xb, wb, route=route, out_f32=True)
+    assert np.array_equal(acc.astype(np.float64), ref)
+    y = run_gpu(coords, xb, wb, route=route)
+    assert np.array_equal(so.bf16_bits_to_f64(y), so.round_to_bf16(ref))
+
+
+def test_integer_inputs_exact_c512():
+    w, coords = config("deep")
+    xb = synth.int_features(w.n, 512, 3)
+    wb = synth.int_weights(512, 512, 3)
+    ref = oracle_acc(oracle_map("deep"), xb, wb)
+    acc = run_gpu(coords, xb, wb, spatial_shape=w.grid, out_f32=True)
+    assert np.array_equal(acc.astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("k", [0, 4, 12, 13, 14, 22, 26])
+def test_one_hot_tap_is_shifted_copy(k):
+    coords = synth.tiny_coords(seed=9, n=2500, side=18)
+    c = 32
+    xb = synth.features(2500, c, 9)
+    w = np.zeros((27, c, c), np.float32)
+    w[k] = np.eye(c, dtype=np.float32)
+    y = run_gpu(coords, xb, synth.bf16_bits_from_f32(w))
+    om = oracle_map_of(coords)
+    j = om["nbr"][:, k]
+    want = np.where((j >= 0)[:, None], xb[np.maximum(j, 0)], 0).astype(np.uint16)
+    assert np.array_equal(y, want)
+
+
+@pytest.mark.parametrize("cin,cout", [(1, 1), (3, 5), (8, 8), (16, 16), (20, 36), (32, 32),
+                                      (40, 24), (64, 128), (128, 64), (96, 160), (256, 256)])
+def test_channel_shapes(cin, cout):
+    coords = synth.tiny_coords(seed=cin * 7 + cout, n=1500, side=16)
+    xb = synth.features(1500, cin, cin)
+    wb = synth.weights(cin, cout, cout)
+    ref = oracle_acc(oracle_map_of(coords), xb, wb)
+    check_bf16_output(run_gpu(coords, xb, wb), ref, f"{cin}x{cout}")
+    check_f32_acc(run_gpu(coords, xb, wb, out_f32=True), ref, f"{cin}x{cout}")
+
+
+def test_relu_flag():
+    w, coords = config("tiny")
+    xb = synth.features(w.n, 16, 1)
+    wb = synth.weights(16, 16, 1)
+    ref = oracle_acc(oracle_map("tiny"), xb, wb)
+    y = so.bf16_bits_to_f64(run_gpu(coords, xb, wb, relu=True))
+    assert (y >= 0).all()
+    assert np.array_equal(y, np.maximum(so.bf16_bits_to_f64(run_gpu(coords, xb, wb)), 0))
+    check_bf16_output(so.bf16_bits(np.maximum(so.round_to_bf16(ref), 0)),
+                      np.maximum(ref, 0), "relu-ref")
+
+
+def test_full_cube_and_single_voxel():
+    for coords in (synth.box_coords(3, 3, 3), np.array([[0, 5, 6, 7]], np.int32)):
+        n = len(coords)
+        xb = synth.features(n, 16, 2)
+        wb = synth.weights(16, 16, 2)
+        ref = oracle_acc(oracle_map_of(coords), xb, wb)
+        check_bf16_output(run_gpu(coords, xb, wb), ref, f"n={n}")
+
+
+def test_layers_share_one_map_and_accumulator_resets():
+    """Several forwards on one map: each equals a fresh single-layer run."""
+    w, coords = config("tiny")
+    m = smc.KernelMap().build(to_dev_i32(coords), spatial_shape=w.grid)
+    om = oracle_map("tiny")
+    for layer in range(4):
+        c_out = 16 if layer % 2 == 0 else 48
+        xb = synth.features(w.n, 16, 10 + layer)
+        wb = synth.weights(16, c_out, 1, layer)
+        y = bf16_bits_of(m.forward(to_dev_bf16(xb), smc.pack_weights(to_dev_bf16(wb))))
+        check_bf16_output(y, oracle_acc(om, xb, wb), f"layer {layer}")
+    m.close()
+
+
+def test_stage_six_layers():
+    """Six layers on one map with ReLU between them (the stage workload)."""
+    w, coords = config("stage")
+    c = w.channels
+    om = oracle_map("stage")
+    m = smc.KernelMap().build(to_dev_i32(coords), spatial_shape=w.grid)
+    hb = synth.features(w.n, c, w.seed)
+    h_dev = to_dev_bf16(hb)
+    ref_h = so.bf16_bits_to_f64(hb)
+    for layer in range(6):
+        wb = synth.weights(c, c, w.seed, layer)
+        relu = layer < 5
+        # teacher-forced: the oracle gets the GPU's own bf16 input of this layer
+        gpu_in = bf16_bits_of(h_dev)
+        ref = oracle_acc(om, gpu_in, wb)
+        h_dev = m.forward(h_dev, smc.pack_weights(to_dev_bf16(wb)), relu=relu)
+        got = bf16_bits_of(h_dev)
+        want = np.maximum(ref, 0) if relu else ref
+        check_bf16_output(got, want, f"stage layer {layer}")
+        # end to end: the oracle's own chain
+        ref_h = so.round_to_bf16(so.conv_accumulate(ref_h, so.bf16_bits_to_f64(wb), om["pair_in"],
+                                                    om["pair_out"], om["tap_off"], w.n))
+        if relu:
+            ref_h = np.maximum(ref_h, 0)
+    got = so.bf16_bits_to_f64(bf16_bits_of(h_dev))
+    assert (np.abs(got - ref_h) <= 2e-2 * (1 + np.abs(ref_h))).all()
+    m.close()

@@ -1,0 +1,131 @@
+"""GPU kernel map vs the CPU oracle: bit-exact neighbour table, masks, mask
+order, pair lists and per-tap offsets, on every workload and on edge sets."""
+import numpy as np
+import pytest
+
+import synth
+from _util import assert_map_equal, config, oracle_map, oracle_map_of, to_dev_i32
+
+pytestmark = pytest.mark.gpu
+
+smc = pytest.importorskip("submanifold_sparse_convolution_amd")
+
+
+def gpu_map(coords, route="auto", spatial_shape=None, batch_size=0, ncols=4):
+    c = coords if ncols == 4 else coords[:, 1:]
+    m = smc.KernelMap().build(to_dev_i32(c), spatial_shape=spatial_shape, batch_size=batch_size,
+                              route=route)
+    out = m.export()
+    out["info"] = m.info()
+    m.close()
+    return out
+
+
+@pytest.mark.parametrize("name", ["tiny", "lidar", "deep", "wide", "stage"])
+def test_workload_map_bit_exact(name):
+    w, coords = config(name)
+    print(f"map parity {name} n={len(coords)}", flush=True)
+    got = gpu_map(coords, spatial_shape=w.grid)
+    assert_map_equal(got, oracle_map(name), name)
+    info = got["info"]
+    assert info["pairs"] == len(oracle_map(name)["pair_in"])
+    assert info["route"] == ("sorted" if name == "wide" else "dense")
+    assert info["pairs_padded"] % info["tile_m"] == 0
+
+
+@pytest.mark.parametrize("name", ["tiny", "lidar", "deep"])
+def test_dense_equals_sorted(name):
+    w, coords = config(name)
+    a = gpu_map(coords, route="dense", spatial_shape=w.grid)
+    b = gpu_map(coords, route="sorted", spatial_shape=w.grid)
+    assert a["info"]["route"] == "dense" and b["info"]["route"] == "sorted"
+    assert b["info"]["key_bits"] <= 32          # 32-bit key path
+    assert_map_equal(a, b, name)
+
+
+def test_sorted_64bit_keys_and_derived_shape():
+    _, coords = config("wide")
+    got = gpu_map(coords)                      # bounding box derived on the device
+    assert got["info"]["key_bits"] > 32
+    assert_map_equal(got, oracle_map("wide"), "wide/derived")
+
+
+def test_derived_shape_dense():
+    _, coords = config("deep")
+    got = gpu_map(coords, route="dense")
+    assert_map_equal(got, oracle_map("deep"), "deep/derived")
+
+
+@pytest.mark.parametrize("n", [1, 7, 16, 17, 63, 64, 65, 255, 256, 257, 4097])
+@pytest.mark.parametrize("route", ["dense", "sorted"])
+def test_small_and_ragged(n, route):
+    coords = synth.tiny_coords(seed=n, n=n, side=max(3, int(round((4 * n) ** (1 / 3)))))
+    got = gpu_map(coords, route=route, spatial_shape=None)
+    assert_map_equal(got, oracle_map_of(coords), f"n={n} {route}")
+
+
+@pytest.mark.parametrize("route", ["dense", "sorted"])
+def test_full_boxes(route):
+    for abc in [(3, 3, 3), (1, 1, 1), (5, 4, 3), (1, 1, 40), (17, 9, 5)]:
+        coords = synth.box_coords(*abc, origin=(2, 3, 4), seed=sum(abc))
+        got = gpu_map(coords, route=route, spatial_shape=(30, 30, 50))
+        want = oracle_map_of(coords)
+        assert_map_equal(got, want, f"box {abc} {route}")
+        a, b, c = abc
+        assert got["info"]["pairs"] == (3 * a - 2) * (3 * b - 2) * (3 * c - 2)
+
+
+@pytest.mark.parametrize("route", ["dense", "sorted"])
+def test_isolated_voxels(route):
+    coords = synth.isolated_coords(3000, spacing=2, seed=4)
+    got = gpu_map(coords, route=route)
+    assert (got["mask"] == (1 << 13)).all()
+    assert_map_equal(got, oracle_map_of(coords), "isolated")
+
+
+@pytest.mark.parametrize("route", ["dense", "sorted"])
+def test_two_batches(route):
+    a = synth.tiny_coords(seed=5, n=900, side=12)
+    b = synth.tiny_coords(seed=6, n=700, side=12)
+    b[:, 0] = 1
+    coords = np.concatenate([a, b])
+    coords = coords[np.random.default_rng(0).permutation(len(coords))]
+    want = oracle_map_of(coords)
+    assert_map_equal(gpu_map(coords, route=route, spatial_shape=(12, 12, 12), batch_size=2),
+                     want, "batches explicit")
+    assert_map_equal(gpu_map(coords, route=route), want, "batches derived")
+
+
+def test_three_column_coords():
+    _, coords = config("tiny")
+    got = gpu_map(coords, ncols=3, spatial_shape=(24, 24, 24))
+    assert_map_equal(got, oracle_map("tiny"), "ncols=3")
+
+
+def test_empty_map():
+    import torch
+    m = smc.KernelMap().build(torch.zeros((0, 4), dtype=torch.int32, device="cuda"),
+                              spatial_shape=(4, 4, 4))
+    info = m.info()
+    assert info["n"] == 0 and info["pairs"] == 0
+    x = torch.zeros((0, 16), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((27, 16, 16), dtype=torch.bfloat16, device="cuda")
+    y = m.forward(x, smc.pack_weights(w))
+    assert tuple(y.shape) == (0, 16)
+
+
+def test_rebuild_reuses_handle_and_keeps_grid_clean():
+    """One handle, several builds of different sets: each must match."""
+    m = smc.KernelMap()
+    for seed in (1, 2, 3):
+        coords = synth.ground_box_coords(3000, (200, 200, 12), seed=seed, n_boxes=20)
+        m.build(to_dev_i32(coords), spatial_shape=(200, 200, 12))
+        assert_map_equal(m.export(), oracle_map_of(coords), f"rebuild {seed}")
+    m.close()
+
+
+def test_map_is_deterministic():
+    _, coords = config("stage")
+    a = gpu_map(coords, spatial_shape=(1440, 1440, 41))
+    b = gpu_map(coords, spatial_shape=(1440, 1440, 41))
+    assert_map_equal(a, b, "determinism")
