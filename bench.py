@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Benchmark: microseconds per submanifold 3x3x3 layer including the kernel
+map, effective TFLOP/s on useful MACs, and the roofline of the GEMM kernel.
+
+One step = one pass of the whole hot path over one seeded synthetic voxel
+set already resident in HBM: build the kernel map from raw coordinates
+(bounding box / route, neighbour search with masks, mask sort, pair
+compaction) and run the layer (gather -> MFMA -> scatter GEMM, bf16
+finalize). Weights are packed once before the timed region (a packed
+weight is cached per weight tensor) and the packing time is reported on
+its own.
+
+Prints ONE JSON line. --gpus above 1 exits: this build measures one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "µs per subm-conv layer incl. map + effective TFLOP/s (useful MACs) vs peak"
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+
+
+def dev_bf16(bits):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def gemm_algorithmic_bytes(n, c_in, c_out, pairs):
+    """Compulsory HBM bytes of one GEMM launch: each input row once (bf16),
+    the weights once, both pair lists, and the float32 accumulator once."""
+    return 2 * n * c_in + 2 * 27 * c_in * c_out + 8 * pairs + 4 * n * c_out
+
+
+def layer_algorithmic_bytes(n, c_in, c_out, pairs):
+    """Compulsory bytes of a whole layer: coordinates in, features in, weights,
+    pair lists, bf16 output."""
+    return 16 * n + 2 * n * c_in + 2 * 27 * c_in * c_out + 8 * pairs + 2 * n * c_out
+
+
+def run_workload(name, steps, warmup, sync_build=False):
+    import numpy as np
+    import torch
+
+    import submanifold_sparse_convolution_amd as smc
+    import synth
+
+    w = synth.workload(name)
+    coords = synth.make_coords(w)
+    c = w.channels
+    coords_d = torch.from_numpy(coords).cuda()
+    x_d = dev_bf16(synth.features(w.n, c, w.seed))
+    w_ds = [dev_bf16(synth.weights(c, c, w.seed, layer)) for layer in range(w.layers)]
+    m = smc.KernelMap()
+    # weight packing, once per weight (timed on its own)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    packed = [smc.pack_weights(wd) for wd in w_ds]
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(10):
+        for wd, p in zip(w_ds, packed):
+            smc.pack_weights(wd, out=p)
+    ev1.record()
+    torch.cuda.synchronize()
+    pack_us = ev0.elapsed_time(ev1) * 1e3 / (10 * w.layers)
+
+    ys = [torch.empty((w.n, c), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+
+    def step():
+        m.build(coords_d, spatial_shape=w.grid, batch_size=1, sync=sync_build)
+        h = x_d
+        for layer in range(w.layers):
+            h = m.forward(h, packed[layer], relu=layer + 1 < w.layers, out=ys[layer & 1])
+        return h
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    m.sync()
+    # timed region: K steps between device synchronisations
+    ev0.record()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    m.sync()                                  # the builds' device-side checks passed
+    wall_ms = (t1 - t0) * 1e3 / steps
+    gpu_ms = ev0.elapsed_time(ev1) / steps
+
+    # second pass with per-stage HIP event timers (stream-ordered)
+    m.timing(True)
+    for _ in range(steps):
+        step()
+    stages = m.timing_read(reset=True)
+    m.timing(False)
+    info = m.info()
+    m.close()
+
+    pairs = info["pairs"]
+    per_layer_us = wall_ms * 1e3 / w.layers
+    flops_layer = 2.0 * pairs * c * c
+    stage_us = {k: (v[0] * 1e3 / v[1] if v[1] else 0.0) for k, v in stages.items()}
+    gemm_us = stage_us["gemm"]
+    return dict(
+        workload=w, coords=coords, info=info, pairs=pairs, ms_per_step=wall_ms,
+        gpu_ms_per_step=gpu_ms, per_layer_us=per_layer_us, pack_us=pack_us,
+        tflops_effective=flops_layer * w.layers / (wall_ms * 1e-3) / 1e12,
+        stage_us=stage_us, gemm_us=gemm_us,
+        gemm_tflops=flops_layer / (gemm_us * 1e-6) / 1e12 if gemm_us else 0.0,
+        gemm_bytes=gemm_algorithmic_bytes(w.n, c, c, pairs),
+        layer_bytes=layer_algorithmic_bytes(w.n, c, c, pairs),
+    )
+
+
+def cpu_baseline(name, budget_s=12.0):
+    """The CPU oracle (untouched) on the same workload, repeated for ~budget_s."""
+    import numpy as np
+
+    import synth
+    from oracle import smconv_oracle as so
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        cores = max(blas) if blas else 1
+    except Exception:
+        cores = os.cpu_count() or 1
+    w = synth.workload(name)
+    coords = synth.make_coords(w)
+    xb = synth.features(w.n, w.channels, w.seed)
+    wb = synth.weights(w.channels, w.channels, w.seed)
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        so.subm_conv(coords, xb, wb)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > budget_s or len(times) >= 20:
+            break
+    med = statistics.median(times)
+    return {"value": med * 1e6, "unit": "us/layer", "cores": cores, "kind": "oracle",
+            "sample": f"{len(times)} full {name} layers (map from a dict, float64 per-tap matmuls),"
+                      f" median; the map part is single-threaded Python, the matmuls use "
+                      f"{cores} BLAS threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="lidar",
+                    choices=["tiny", "lidar", "deep", "wide", "stage"])
+    ap.add_argument("--sync-build", action="store_true",
+                    help="wait for the map's device-side checks inside every step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--report", default="",
+                    help="also run every workload and write their figures to this JSON file")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+              "(no multi-GPU path: every box here has one GPU)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+
+    r = run_workload(args.workload, args.steps, args.warmup, args.sync_build)
+    w, info = r["workload"], r["info"]
+    c = w.channels
+    gemm_gbs = r["gemm_bytes"] / (r["gemm_us"] * 1e-6) / 1e9 if r["gemm_us"] else 0.0
+    line = {
+        "metric": METRIC,
+        "value": round(r["per_layer_us"], 2),
+        "unit": "us/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: {w.n} voxels, grid {w.grid[0]}x{w.grid[1]}x{w.grid[2]}, "
+                        f"C_in=C_out={c}, {w.layers} layer(s), seed {w.seed}",
+            "n": w.n, "pairs": r["pairs"], "pairs_per_voxel": round(r["pairs"] / w.n, 4),
+            "route": info["route"], "c_in": c, "c_out": c, "layers": w.layers,
+            "map_built_every_step": True, "build_mode": "sync" if args.sync_build else "async",
+        },
+        "tflops_effective": round(r["tflops_effective"], 3),
+        "frac_bf16_peak": round(r["tflops_effective"] / PEAK_BF16_TFLOPS, 5),
+        "gpu_ms_per_step_events": round(r["gpu_ms_per_step"], 4),
+        "stage_us": {k: round(v, 2) for k, v in r["stage_us"].items()},
+        "weight_pack_us": round(r["pack_us"], 2),
+        "roofline": {
+            "kernel": "k_gemm (gather -> mfma_f32_16x16x32_bf16 -> atomic scatter)",
+            "bound": "hbm",
+            "achieved": round(gemm_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(gemm_gbs / PEAK_HBM_GBS, 4),
+            "traffic": None,
+            "avg_us": round(r["gemm_us"], 3),
+            "algorithmic_bytes": r["gemm_bytes"],
+            "mfma_tflops_useful": round(r["gemm_tflops"], 2),
+            "mfma_frac_useful": round(r["gemm_tflops"] / PEAK_BF16_TFLOPS, 5),
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.workload)
+    if args.report:
+        rep = {}
+        for name in ("tiny", "lidar", "deep", "wide", "stage"):
+            rr = run_workload(name, max(20, args.steps // 2), args.warmup)
+            rep[name] = {k: rr[k] for k in ("pairs", "ms_per_step", "per_layer_us", "pack_us",
+                                            "tflops_effective", "stage_us", "gemm_us",
+                                            "gemm_tflops", "gemm_bytes", "layer_bytes")}
+            rep[name]["route"] = rr["info"]["route"]
+            rep[name]["n"] = rr["workload"].n
+        with open(args.report, "w") as f:
+            json.dump(rep, f, indent=1)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -182,8 +182,8 @@ int smc_weight_pack(const uint16_t* w, int c_in, int c_out, void* out, void* str
  * -> scatter-add, the centre tap compacted with the rest).
  * x       device pointer, bf16 [n, c_in] row-major (rows in coordinate order).
  * wpacked device pointer from smc_weight_pack(c_in, c_out).
- * y       device pointer, bf16 [n, c_out] (float [n, c_out] with SMC_FWD_OUT_F32);
- *         every row is written.
+ * y       device pointer, 16-byte aligned, bf16 [n, c_out] (float [n, c_out] with
+ *         SMC_FWD_OUT_F32); every row is written.
  * flags   SMC_FWD_RELU | SMC_FWD_OUT_F32, or 0. Without SMC_FWD_OUT_F32 the output
  *         is the float32 accumulator rounded to bf16 (to nearest, ties to even).
  * The float32 accumulator lives in the handle (grow-only, 4 n c_out bytes).
@@ -193,6 +193,32 @@ int smc_weight_pack(const uint16_t* w, int c_in, int c_out, void* out, void* str
  */
 int smc_conv_forward(smc_map* map, const uint16_t* x, int c_in, const void* wpacked,
                      int c_out, void* y, unsigned flags, void* stream);
+
+/* Stage timers. Stages of a build and of a forward, for measurement. */
+enum {
+    SMC_STAGE_MAP = 0,         /* the whole smc_map_build enqueue (all steps below it) */
+    SMC_STAGE_NEIGHBOURS = 1,  /* route-specific neighbour search: table + masks */
+    SMC_STAGE_MASK_SORT = 2,   /* radix sort of rows by mask */
+    SMC_STAGE_COMPACT = 3,     /* pair count, scan and write */
+    SMC_STAGE_GEMM = 4,        /* GEMM over the pair lists of every tap but the centre */
+    SMC_STAGE_CENTRE = 5,      /* centre-tap GEMM fused with the output write */
+    SMC_STAGE_COUNT = 6
+};
+
+/*
+ * Turn per-stage timing on or off for one handle. While on, every build and
+ * forward records a pair of HIP events around each stage on the stream it
+ * runs on (the events add no kernels). Off by default.
+ */
+int smc_timing_enable(smc_map* map, int on);
+
+/*
+ * Wait for the timed work and add up its stage times. ms and calls are host
+ * arrays of SMC_STAGE_COUNT entries (either may be NULL): milliseconds of GPU
+ * time and number of timed executions per stage since the last reset.
+ * reset != 0 clears the totals after reading.
+ */
+int smc_timing_read(smc_map* map, double* ms, int64_t* calls, int reset);
 
 /* Static text for a status code. */
 const char* smc_status_string(int status);

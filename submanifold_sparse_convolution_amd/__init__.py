@@ -30,8 +30,9 @@ SMC_FWD_OUT_F32 = 2
 EXPORTED_SYMBOLS = [
     "smc_map_create", "smc_map_destroy", "smc_map_build", "smc_map_sync", "smc_map_info",
     "smc_map_export", "smc_weight_packed_bytes", "smc_weight_pack", "smc_conv_forward",
-    "smc_status_string", "smc_last_error", "smc_version",
+    "smc_status_string", "smc_last_error", "smc_version", "smc_timing_enable", "smc_timing_read",
 ]
+STAGES = ["map", "neighbours", "mask_sort", "compact", "gemm", "centre"]
 
 
 class SmconvError(RuntimeError):
@@ -82,8 +83,11 @@ def lib():
     L.smc_last_error.argtypes = []
     L.smc_last_error.restype = ctypes.c_char_p
     L.smc_version.restype = i32
+    L.smc_timing_enable.argtypes = [vp, i32]
+    L.smc_timing_read.argtypes = [vp, vp, vp, i32]
     for name in ("smc_map_create", "smc_map_destroy", "smc_map_build", "smc_map_sync",
-                 "smc_map_info", "smc_map_export", "smc_weight_pack", "smc_conv_forward"):
+                 "smc_map_info", "smc_map_export", "smc_weight_pack", "smc_conv_forward",
+                 "smc_timing_enable", "smc_timing_read"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -122,8 +126,8 @@ class PackedWeights:
         self.buf, self.c_in, self.c_out = buf, c_in, c_out
 
 
-def pack_weights(w, stream=None) -> PackedWeights:
-    """bf16 [27, C_in, C_out] CUDA tensor -> PackedWeights."""
+def pack_weights(w, out: PackedWeights = None, stream=None) -> PackedWeights:
+    """bf16 [27, C_in, C_out] CUDA tensor -> PackedWeights (into ``out`` if given)."""
     import torch
     _need(w, torch.bfloat16, "w", 3)
     if w.shape[0] != 27:
@@ -131,7 +135,12 @@ def pack_weights(w, stream=None) -> PackedWeights:
     c_in, c_out = int(w.shape[1]), int(w.shape[2])
     L = lib()
     nbytes = L.smc_weight_packed_bytes(c_in, c_out)
-    buf = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
+    if out is not None:
+        if (out.c_in, out.c_out) != (c_in, c_out):
+            raise ValueError("out was packed for other channel counts")
+        buf = out.buf
+    else:
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
     _check(L.smc_weight_pack(ctypes.c_void_p(w.data_ptr()), c_in, c_out,
                              ctypes.c_void_p(buf.data_ptr()), _stream(stream)))
     return PackedWeights(buf, c_in, c_out)
@@ -176,6 +185,17 @@ class KernelMap:
 
     def sync(self):
         _check(lib().smc_map_sync(self._h))
+
+    def timing(self, on: bool = True):
+        """Record HIP events around each stage of later builds and forwards."""
+        _check(lib().smc_timing_enable(self._h, 1 if on else 0))
+
+    def timing_read(self, reset: bool = True) -> dict:
+        """{stage: (total_ms, calls)} of the timed work (waits for it)."""
+        ms = (ctypes.c_double * len(STAGES))()
+        calls = (ctypes.c_int64 * len(STAGES))()
+        _check(lib().smc_timing_read(self._h, ms, calls, 1 if reset else 0))
+        return {name: (ms[i], calls[i]) for i, name in enumerate(STAGES)}
 
     def info(self) -> dict:
         inf = MapInfo()

@@ -34,7 +34,11 @@ __device__ inline int64_t dense_cell(const Geom& g, int b, int x, int y, int z) 
     return b * g.sz_b + (int64_t)(x + 1) * g.sz_x + (int64_t)(y + 1) * g.sz_y + (z + 1);
 }
 
-__global__ void k_state_init(MapState* st) {
+// Clears the build's device record and the sort histograms it accumulates.
+__global__ __launch_bounds__(kBlock) void k_state_init(MapState* st, uint32_t* hist, int hist_ints) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < hist_ints; i += gridDim.x * blockDim.x)
+        hist[i] = 0;
+    if (blockIdx.x != 0) return;
     int t = threadIdx.x;
     if (t == 0) st->status = 0;
     if (t < 3) st->bbox[t] = INT_MAX;
@@ -44,6 +48,7 @@ __global__ void k_state_init(MapState* st) {
     if (t < 4) st->totals[t] = 0;
     if (t < 28) st->tap_off[t] = 0;
     if (t < 27) st->tap_count[t] = 0;
+    if (t < 27) st->tap_tot[t] = 0;
 }
 
 __device__ inline int wave_min(int v) {
@@ -71,17 +76,26 @@ __global__ __launch_bounds__(kBlock) void k_bbox(const int32_t* __restrict__ coo
         lo[3] = min(lo[3], b);
         hi[3] = max(hi[3], b);
     }
+    __shared__ int s_lo[kBlock / 64][4], s_hi[kBlock / 64][4];
+    const int w = threadIdx.x >> 6;
     for (int d = 0; d < 4; ++d) {
         lo[d] = wave_min(lo[d]);
         hi[d] = wave_max(hi[d]);
-    }
-    if ((threadIdx.x & 63) == 0) {
-        for (int d = 0; d < 3; ++d) {
-            atomicMin(&st->bbox[d], lo[d]);
-            atomicMax(&st->bbox[3 + d], hi[d]);
+        if ((threadIdx.x & 63) == 0) {
+            s_lo[w][d] = lo[d];
+            s_hi[w][d] = hi[d];
         }
-        atomicMin(&st->bbox[6], lo[3]);
-        atomicMax(&st->bbox[7], hi[3]);
+    }
+    __syncthreads();
+    if (threadIdx.x < 4) {
+        const int d = threadIdx.x;
+        int a = s_lo[0][d], b = s_hi[0][d];
+        for (int v = 1; v < kBlock / 64; ++v) {
+            a = min(a, s_lo[v][d]);
+            b = max(b, s_hi[v][d]);
+        }
+        atomicMin(&st->bbox[d == 3 ? 6 : d], a);
+        atomicMax(&st->bbox[d == 3 ? 7 : 3 + d], b);
     }
 }
 
@@ -130,16 +144,6 @@ __global__ __launch_bounds__(kBlock) void k_dense_lookup(const int32_t* __restri
     }
     uint64_t hits = __ballot(v >= 0);
     if (row < n && k == 0) mask[row] = (uint32_t)(hits >> (threadIdx.x & 32));
-}
-
-// Restore the grid's all-empty state: only the cells this build claimed.
-__global__ __launch_bounds__(kBlock) void k_dense_clear(const int32_t* __restrict__ coords,
-                                                        int64_t n, Geom g,
-                                                        int32_t* __restrict__ grid) {
-    int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-    if (i >= n) return;
-    int b, x, y, z;
-    if (load_rel(coords, i, g, b, x, y, z)) grid[dense_cell(g, b, x, y, z)] = -1;
 }
 
 // Packed key of a voxel, fields (b | x+1 | y+1 | z+1) from high to low. The
@@ -199,7 +203,8 @@ __global__ __launch_bounds__(kBlock) void k_sorted_lookup(const K* __restrict__ 
     uint32_t bits = 0;
     if (s < n && c < 9) {
         K q = keys[s];
-        int row = (int)vals[s];
+        // vals is a permutation of [0, n); the clamps only matter if a sort wait stalled
+        int row = (int)min(vals[s], (uint32_t)(n - 1));
         int dx = c / 3 - 1, dy = c % 3 - 1;
         K delta = (K)((int64_t)dx * ((int64_t)1 << (g.wy + g.wz))) +
                   (K)((int64_t)dy * ((int64_t)1 << g.wz));
@@ -215,7 +220,7 @@ __global__ __launch_bounds__(kBlock) void k_sorted_lookup(const K* __restrict__ 
         for (int dz = 0; dz < 3; ++dz) {
             int hit = -1;
             if (j < n && keys[j] == first + (K)dz) {
-                hit = (int)vals[j];
+                hit = (int)min(vals[j], (uint32_t)(n - 1));
                 ++j;
             }
             nbr[(int64_t)row * kTaps + 3 * c + dz] = hit;
@@ -226,7 +231,7 @@ __global__ __launch_bounds__(kBlock) void k_sorted_lookup(const K* __restrict__ 
     bits |= __shfl_xor(bits, 4, 16);
     bits |= __shfl_xor(bits, 2, 16);
     bits |= __shfl_xor(bits, 1, 16);
-    if (s < n && c == 0) mask[vals[s]] = bits;
+    if (s < n && c == 0) mask[min(vals[s], (uint32_t)(n - 1))] = bits;
 }
 
 inline unsigned blocks_for(int64_t threads) {
@@ -236,14 +241,18 @@ inline unsigned blocks_for(int64_t threads) {
 
 }  // namespace
 
-hipError_t launch_state_init(MapState* st, hipStream_t s) {
-    k_state_init<<<1, 64, 0, s>>>(st);
+hipError_t launch_state_init(MapState* st, uint32_t* hist, int hist_ints, hipStream_t s) {
+    unsigned blocks = (unsigned)((hist_ints + kBlock - 1) / kBlock);
+    if (blocks < 1) blocks = 1;
+    if (blocks > 32) blocks = 32;
+    k_state_init<<<blocks, kBlock, 0, s>>>(st, hist, hist_ints);
     return hipGetLastError();
 }
 
 hipError_t launch_bbox(const int32_t* coords, int64_t n, int ncols, MapState* st, hipStream_t s) {
-    unsigned blocks = blocks_for(n);
-    if (blocks > 1024) blocks = 1024;
+    unsigned blocks = (unsigned)((n + 8 * kBlock - 1) / (8 * kBlock));
+    if (blocks < 1) blocks = 1;
+    if (blocks > 256) blocks = 256;
     k_bbox<<<blocks, kBlock, 0, s>>>(coords, n, ncols, st);
     return hipGetLastError();
 }
@@ -265,12 +274,6 @@ hipError_t launch_dense_scatter(const int32_t* coords, int64_t n, const Geom& g,
 hipError_t launch_dense_lookup(const int32_t* coords, int64_t n, const Geom& g, const int32_t* grid,
                                int32_t* nbr, uint32_t* mask, hipStream_t s) {
     k_dense_lookup<<<blocks_for(n * 32), kBlock, 0, s>>>(coords, n, g, grid, nbr, mask);
-    return hipGetLastError();
-}
-
-hipError_t launch_dense_clear(const int32_t* coords, int64_t n, const Geom& g, int32_t* grid,
-                              hipStream_t s) {
-    k_dense_clear<<<blocks_for(n), kBlock, 0, s>>>(coords, n, g, grid);
     return hipGetLastError();
 }
 

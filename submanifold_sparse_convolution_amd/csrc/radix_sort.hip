@@ -1,4 +1,4 @@
-// Stable LSD radix sort of (key, value) pairs, 8 bits per pass.
+// Stable LSD radix sort of (key, value) pairs: one kernel per digit pass.
 //
 // Used twice in the map build: on packed voxel keys in the sorted route
 // (the sort the Z-Delta mapper needs; "[Kernel] Add submanifold sparse 3D
@@ -6,176 +6,306 @@
 // to group rows with equal masks ("Sparse convolution in FP32", "Neighbour
 // masks and sorted rows": a GPU radix sort orders the rows by mask).
 //
-// Each pass is reduce-then-scan with no global atomics (the pull request's
-// Open questions record an atomic-counter compaction that serialised):
-//   count   per tile of 4096 keys, a 256-bin histogram, stored digit-major
-//   scan    one block turns the digit-major table into exclusive offsets
-//   scatter per tile, a stable rank inside the tile from wave ballots, then
-//           offset + rank
+// Design for small inputs (10^4 - 10^5 keys), where each kernel launch is a
+// large share of the cost:
+//  * the global digit histograms of every pass are counted in one read of
+//    the keys, by the kernel that produces them (mask lookup, key packing)
+//    or by k_key_hist;
+//  * each pass is a single kernel: a block ranks its tile stably (each wave
+//    owns a contiguous quarter of the tile and keeps per-digit running
+//    counts in LDS, so no block barrier per item), then finds how many keys
+//    of each digit precede its tile by decoupled look-back over the blocks
+//    before it, then scatters.
+// Look-back safety: block indices are taken from a ticket counter in launch
+// order, so a block only ever waits for blocks that already hold a ticket,
+// i.e. are running. Each wait is also bounded; a wait that runs out flags
+// the status word and the block carries on with in-bounds (wrong) output.
+// Look-back entries carry an epoch, so stale entries from earlier passes are
+// never taken for ready ones and the table needs no clearing.
 #include "smc_internal.h"
 
 namespace smc {
 namespace {
 
-constexpr int kRadixBits = 8;
-constexpr int kBins = 1 << kRadixBits;
-constexpr int kSortBlock = 256;
-constexpr int kItems = 16;
-constexpr int kTile = kSortBlock * kItems;
-constexpr int kScanBlock = 1024;
+constexpr int kOsThreads = 256;
+constexpr int kOsWaves = kOsThreads / 64;
+constexpr int kOsItems = 8;                     // keys per thread
+constexpr int kOsTile = kOsThreads * kOsItems;  // 2048 keys per block
+constexpr uint32_t kSpinLimit = 1u << 22;
 
-template <typename K>
-__global__ __launch_bounds__(kSortBlock) void k_radix_count(const K* __restrict__ keys, int64_t n,
-                                                            int shift, int n_tiles,
-                                                            uint32_t* __restrict__ counts) {
-    __shared__ uint32_t hist[kBins];
-    hist[threadIdx.x] = 0;
-    __syncthreads();
-    int64_t base = (int64_t)blockIdx.x * kTile;
-#pragma unroll 4
-    for (int i = 0; i < kItems; ++i) {
-        int64_t idx = base + i * kSortBlock + threadIdx.x;
-        if (idx < n) atomicAdd(&hist[(uint32_t)(keys[idx] >> shift) & (kBins - 1)], 1u);
-    }
-    __syncthreads();
-    counts[(int64_t)threadIdx.x * n_tiles + blockIdx.x] = hist[threadIdx.x];
+// look-back entry: epoch (30 bits) | state (2 bits) | count (32 bits)
+constexpr uint64_t kAgg = 1, kIncl = 2;
+__device__ inline uint64_t lb_pack(uint32_t epoch, uint64_t state, uint32_t count) {
+    return ((uint64_t)epoch << 34) | (state << 32) | count;
 }
 
-// Exclusive scan in place over m entries, one block.
-__global__ __launch_bounds__(kScanBlock) void k_exclusive_scan(uint32_t* __restrict__ v,
-                                                               int64_t m) {
-    __shared__ uint32_t wave_tot[kScanBlock / 64];
-    __shared__ uint32_t carry_s;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    if (tid == 0) carry_s = 0;
-    __syncthreads();
-    for (int64_t seg = 0; seg < m; seg += (int64_t)kScanBlock * 4) {
-        uint32_t x[4];
-        uint32_t sum = 0;
-        int64_t i0 = seg + (int64_t)tid * 4;
+__device__ inline uint64_t ld_acquire(const uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void st_release(uint64_t* p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Sum of the counts of entry column d over blocks pb, pb-1, ... back to the
+// first block that has published its inclusive prefix (or block 0). Entries
+// are read 8 at a time so a walk over many blocks costs few round trips.
+__device__ inline uint32_t lookback8(uint64_t* look, int stride, int d, int64_t pb,
+                                     uint32_t epoch, uint32_t* status) {
+    const uint32_t ep = epoch & 0x3FFFFFFFu;
+    uint32_t prefix = 0;
+    uint32_t spins = 0;
+    while (pb >= 0) {
+        uint64_t e[8];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            x[j] = (i0 + j < m) ? v[i0 + j] : 0u;
-            sum += x[j];
+        for (int j = 0; j < 8; ++j) e[j] = pb - j >= 0 ? ld_acquire(&look[(pb - j) * stride + d]) : 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (pb - j < 0) return prefix;
+            while ((uint32_t)(e[j] >> 34) != ep) {
+                if (++spins > kSpinLimit) {
+                    atomicOr(status, kStSortStall);
+                    return prefix;
+                }
+                __builtin_amdgcn_s_sleep(1);
+                e[j] = ld_acquire(&look[(pb - j) * stride + d]);
+            }
+            prefix += (uint32_t)e[j];
+            if (((e[j] >> 32) & 3u) == kIncl) return prefix;
         }
-        // inclusive wave scan of the per-thread sums
-        uint32_t inc = sum;
+        pb -= 8;
+    }
+    return prefix;
+}
+
+template <typename K, int BITS>
+__global__ __launch_bounds__(kOsThreads) void k_os_pass(
+    const K* __restrict__ kin, const uint32_t* __restrict__ vin, K* __restrict__ kout,
+    uint32_t* __restrict__ vout, int64_t n, int shift, const uint32_t* __restrict__ hist,
+    uint64_t* __restrict__ look, uint32_t* ticket, uint32_t epoch, uint32_t* status) {
+    constexpr int BINS = 1 << BITS;
+    constexpr int DPT = BINS / kOsThreads;      // digits per thread
+    __shared__ uint32_t s_bid;
+    __shared__ uint32_t s_wcnt[kOsWaves][BINS]; // per-wave counts, then per-wave offsets
+    __shared__ uint32_t s_base[BINS];           // global start of this tile's run of each digit
+    __shared__ uint32_t s_part[kOsThreads];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+
+    if (tid == 0) s_bid = atomicAdd(ticket, 1u);
+#pragma unroll
+    for (int j = 0; j < DPT; ++j)
+#pragma unroll
+        for (int v = 0; v < kOsWaves; ++v) s_wcnt[v][tid * DPT + j] = 0;
+    __syncthreads();
+    const uint32_t bid = s_bid;
+    const int64_t base = (int64_t)bid * kOsTile + (int64_t)w * (kOsTile / kOsWaves);
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+    // stable rank within the wave's contiguous run
+    K key[kOsItems];
+    uint32_t val[kOsItems], rank[kOsItems], dig[kOsItems];
+#pragma unroll
+    for (int i = 0; i < kOsItems; ++i) {               // all loads in flight together
+        int64_t idx = base + i * 64 + lane;
+        const int64_t ic = idx < n ? idx : n - 1;          // clamped: loads never branch
+        key[i] = kin[ic];
+        val[i] = vin ? vin[ic] : (uint32_t)idx;
+    }
+#pragma unroll
+    for (int i = 0; i < kOsItems; ++i) {
+        int64_t idx = base + i * 64 + lane;
+        bool valid = idx < n;
+        uint32_t d = (uint32_t)(key[i] >> shift) & (BINS - 1);
+        dig[i] = valid ? d : 0xFFFFFFFFu;
+        uint64_t peers = __ballot(valid);
+#pragma unroll
+        for (int b = 0; b < BITS; ++b) {
+            uint64_t bb = __ballot((d >> b) & 1u);
+            peers &= ((d >> b) & 1u) ? bb : ~bb;
+        }
+        uint32_t before = valid ? s_wcnt[w][d] : 0u;
+        rank[i] = before + (uint32_t)__popcll(peers & below);
+        if (valid && (peers & below) == 0) s_wcnt[w][d] = before + (uint32_t)__popcll(peers);
+        __builtin_amdgcn_wave_barrier();
+    }
+    __syncthreads();
+
+    // per digit: wave offsets inside the tile, tile count
+    uint32_t tile_cnt[DPT];
+#pragma unroll
+    for (int j = 0; j < DPT; ++j) {
+        int d = tid * DPT + j;
+        uint32_t run = 0;
+#pragma unroll
+        for (int v = 0; v < kOsWaves; ++v) {
+            uint32_t c = s_wcnt[v][d];
+            s_wcnt[v][d] = run;
+            run += c;
+        }
+        tile_cnt[j] = run;
+        st_release(&look[(int64_t)bid * BINS + d], lb_pack(epoch, bid == 0 ? kIncl : kAgg, run));
+    }
+
+    // global start of each digit: exclusive scan of the pass histogram
+    uint32_t hsum = 0, hv[DPT];
+#pragma unroll
+    for (int j = 0; j < DPT; ++j) {
+        hv[j] = hist[tid * DPT + j];
+        hsum += hv[j];
+    }
+    {
+        uint32_t inc = hsum;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
             uint32_t y = __shfl_up(inc, o);
             if (lane >= o) inc += y;
         }
-        if (lane == 63) wave_tot[w] = inc;
+        if (lane == 63) s_part[w] = inc;
         __syncthreads();
-        uint32_t before = carry_s;
-        for (int j = 0; j < w; ++j) before += wave_tot[j];
-        uint32_t run = before + inc - sum;
+        uint32_t off = inc - hsum;
+        for (int v = 0; v < w; ++v) off += s_part[v];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (i0 + j < m) v[i0 + j] = run;
-            run += x[j];
+        for (int j = 0; j < DPT; ++j) {
+            s_base[tid * DPT + j] = off;
+            off += hv[j];
         }
-        __syncthreads();
-        if (tid == kScanBlock - 1) carry_s = run;
-        __syncthreads();
     }
-}
 
-template <typename K>
-__global__ __launch_bounds__(kSortBlock) void k_radix_scatter(
-    const K* __restrict__ kin, const uint32_t* __restrict__ vin, K* __restrict__ kout,
-    uint32_t* __restrict__ vout, int64_t n, int shift, int n_tiles,
-    const uint32_t* __restrict__ offsets) {
-    __shared__ uint32_t next[kBins];                     // next free slot per digit
-    __shared__ uint32_t wave_cnt[kSortBlock / 64][kBins];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    next[tid] = offsets[(int64_t)tid * n_tiles + blockIdx.x];
+    // decoupled look-back over the blocks before this one, 8 entries per round trip
 #pragma unroll
-    for (int j = 0; j < kSortBlock / 64; ++j) wave_cnt[j][tid] = 0;
+    for (int j = 0; j < DPT; ++j) {
+        int d = tid * DPT + j;
+        uint32_t prefix = 0;
+        if (bid > 0) {
+            prefix = lookback8(look, BINS, d, (int64_t)bid - 1, epoch, status);
+            st_release(&look[(int64_t)bid * BINS + d], lb_pack(epoch, kIncl, prefix + tile_cnt[j]));
+        }
+        s_base[d] += prefix;
+    }
     __syncthreads();
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    int64_t base = (int64_t)blockIdx.x * kTile;
-    for (int i = 0; i < kItems; ++i) {
-        // processing order (i, wave, lane) is the input order: keeps the sort stable
-        int64_t idx = base + i * kSortBlock + tid;
-        bool valid = idx < n;
-        K key = valid ? kin[idx] : (K)0;
-        uint32_t val = valid ? (vin ? vin[idx] : (uint32_t)idx) : 0u;
-        uint32_t d = (uint32_t)(key >> shift) & (kBins - 1);
-        uint64_t peers = __ballot(valid);
+
+    // scatter
 #pragma unroll
-        for (int b = 0; b < kRadixBits; ++b) {
-            uint64_t bb = __ballot((d >> b) & 1u);
-            peers &= ((d >> b) & 1u) ? bb : ~bb;
-        }
-        uint32_t rank = (uint32_t)__popcll(peers & below);
-        if (valid && rank == 0) wave_cnt[w][d] = (uint32_t)__popcll(peers);
-        __syncthreads();
-        if (valid) {
-            uint32_t pos = next[d] + rank;
-            for (int j = 0; j < w; ++j) pos += wave_cnt[j][d];
-            kout[pos] = key;
-            vout[pos] = val;
-        }
-        __syncthreads();
-        uint32_t add = 0;
-#pragma unroll
-        for (int j = 0; j < kSortBlock / 64; ++j) {
-            add += wave_cnt[j][tid];
-            wave_cnt[j][tid] = 0;
-        }
-        next[tid] += add;
-        __syncthreads();
+    for (int i = 0; i < kOsItems; ++i) {
+        uint32_t d = dig[i];
+        if (d == 0xFFFFFFFFu) continue;
+        int64_t pos = (int64_t)s_base[d] + s_wcnt[w][d] + rank[i];
+        if (pos >= n) pos = n - 1;               // only reachable after a stalled wait
+        kout[pos] = key[i];
+        vout[pos] = val[i];
     }
+    if (bid == gridDim.x - 1 && tid == 0) atomicExch(ticket, 0u);   // every block holds its ticket
+}
+
+// Global digit histograms of every pass in one read of the keys.
+template <typename K>
+__global__ __launch_bounds__(kOsThreads) void k_key_hist(const K* __restrict__ keys, int64_t n,
+                                                         int bits, int passes,
+                                                         uint32_t* __restrict__ hist) {
+    extern __shared__ uint32_t s_h[];            // passes << bits counters
+    const int bins = 1 << bits;
+    for (int i = threadIdx.x; i < passes * bins; i += kOsThreads) s_h[i] = 0;
+    __syncthreads();
+    int64_t base = (int64_t)blockIdx.x * kOsTile;
+    for (int i = 0; i < kOsItems; ++i) {
+        int64_t idx = base + i * kOsThreads + threadIdx.x;
+        if (idx < n) {
+            K k = keys[idx];
+            for (int p = 0; p < passes; ++p)
+                atomicAdd(&s_h[p * bins + ((uint32_t)(k >> (p * bits)) & (bins - 1))], 1u);
+        }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < passes * bins; i += kOsThreads)
+        if (s_h[i]) atomicAdd(&hist[i], s_h[i]);
+}
+
+template <typename K, int BITS>
+hipError_t launch_pass(const K* kin, const uint32_t* vin, K* kout, uint32_t* vout, int64_t n,
+                       int shift, const uint32_t* hist, uint64_t* look, uint32_t* ticket,
+                       uint32_t epoch, uint32_t* status, hipStream_t s) {
+    unsigned blocks = (unsigned)((n + kOsTile - 1) / kOsTile);
+    k_os_pass<K, BITS><<<blocks, kOsThreads, 0, s>>>(kin, vin, kout, vout, n, shift, hist, look,
+                                                     ticket, epoch, status);
+    return hipGetLastError();
 }
 
 template <typename K>
-hipError_t radix_sort_impl(const K* keys_in, const uint32_t* vals_in, int64_t n, int key_bits,
-                           K* kbuf0, K* kbuf1, uint32_t* vbuf0, uint32_t* vbuf1, uint32_t* counts,
-                           const K** keys_out, const uint32_t** vals_out, hipStream_t s) {
-    const int n_tiles = (int)((n + kTile - 1) / kTile);
+hipError_t sort_impl(const K* keys_in, const uint32_t* vals_in, int64_t n, const SortPlan& plan,
+                     const uint32_t* hist, K* kbuf0, K* kbuf1, uint32_t* vbuf0, uint32_t* vbuf1,
+                     SortWork& ws, uint32_t* status, const K** keys_out,
+                     const uint32_t** vals_out, hipStream_t s) {
     const K* kcur = keys_in;
     const uint32_t* vcur = vals_in;
     K* kdst[2] = {kbuf0, kbuf1};
     uint32_t* vdst[2] = {vbuf0, vbuf1};
-    int passes = (key_bits + kRadixBits - 1) / kRadixBits;
-    if (passes < 1) passes = 1;   // still produce the value permutation
-    for (int p = 0; p < passes; ++p) {
-        int shift = p * kRadixBits;
-        k_radix_count<K><<<n_tiles, kSortBlock, 0, s>>>(kcur, n, shift, n_tiles, counts);
-        k_exclusive_scan<<<1, kScanBlock, 0, s>>>(counts, (int64_t)kBins * n_tiles);
-        k_radix_scatter<K><<<n_tiles, kSortBlock, 0, s>>>(kcur, vcur, kdst[p & 1], vdst[p & 1], n,
-                                                          shift, n_tiles, counts);
+    const int bins = 1 << plan.bits;
+    for (int p = 0; p < plan.passes; ++p) {
+        uint32_t epoch = ++ws.epoch & 0x3FFFFFFFu;
+        if (epoch == 0) epoch = ++ws.epoch & 0x3FFFFFFFu;
+        const uint32_t* h = hist + (size_t)p * bins;
+        hipError_t e;
+        switch (plan.bits) {
+            case 8: e = launch_pass<K, 8>(kcur, vcur, kdst[p & 1], vdst[p & 1], n, p * 8, h, ws.look, ws.ticket, epoch, status, s); break;
+            case 9: e = launch_pass<K, 9>(kcur, vcur, kdst[p & 1], vdst[p & 1], n, p * 9, h, ws.look, ws.ticket, epoch, status, s); break;
+            case 10: e = launch_pass<K, 10>(kcur, vcur, kdst[p & 1], vdst[p & 1], n, p * 10, h, ws.look, ws.ticket, epoch, status, s); break;
+            default: e = launch_pass<K, 11>(kcur, vcur, kdst[p & 1], vdst[p & 1], n, p * 11, h, ws.look, ws.ticket, epoch, status, s); break;
+        }
+        if (e != hipSuccess) return e;
         kcur = kdst[p & 1];
         vcur = vdst[p & 1];
     }
     *keys_out = kcur;
     *vals_out = vcur;
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 }  // namespace
 
-size_t radix_counts_elems(int64_t n) {
-    int64_t tiles = (n + kTile - 1) / kTile;
-    if (tiles < 1) tiles = 1;
-    return (size_t)tiles * kBins;
+SortPlan sort_plan(int key_bits) {
+    SortPlan p;
+    if (key_bits < 1) key_bits = 1;
+    p.passes = (key_bits + 10) / 11;
+    int b = (key_bits + p.passes - 1) / p.passes;
+    p.bits = b < 8 ? 8 : b;
+    return p;
 }
 
-hipError_t radix_sort_u32(const uint32_t* keys_in, const uint32_t* vals_in, int64_t n, int key_bits,
-                          uint32_t* kbuf0, uint32_t* kbuf1, uint32_t* vbuf0, uint32_t* vbuf1,
-                          uint32_t* counts, const uint32_t** keys_out, const uint32_t** vals_out,
-                          hipStream_t s) {
-    return radix_sort_impl<uint32_t>(keys_in, vals_in, n, key_bits, kbuf0, kbuf1, vbuf0, vbuf1,
-                                     counts, keys_out, vals_out, s);
+int64_t sort_tiles(int64_t n) { return (n + kOsTile - 1) / kOsTile; }
+
+size_t sort_look_bytes(int64_t n) {
+    int64_t t = sort_tiles(n);
+    return (size_t)(t < 1 ? 1 : t) * 2048 * sizeof(uint64_t);
 }
 
-hipError_t radix_sort_u64(const uint64_t* keys_in, const uint32_t* vals_in, int64_t n, int key_bits,
-                          uint64_t* kbuf0, uint64_t* kbuf1, uint32_t* vbuf0, uint32_t* vbuf1,
-                          uint32_t* counts, const uint64_t** keys_out, const uint32_t** vals_out,
+hipError_t launch_key_hist(const void* keys, bool wide, int64_t n, const SortPlan& plan,
+                           uint32_t* hist, hipStream_t s) {
+    unsigned blocks = (unsigned)((n + kOsTile - 1) / kOsTile);
+    size_t lds = (size_t)plan.passes * (1u << plan.bits) * 4;
+    if (wide)
+        k_key_hist<uint64_t><<<blocks, kOsThreads, lds, s>>>((const uint64_t*)keys, n, plan.bits,
+                                                             plan.passes, hist);
+    else
+        k_key_hist<uint32_t><<<blocks, kOsThreads, lds, s>>>((const uint32_t*)keys, n, plan.bits,
+                                                             plan.passes, hist);
+    return hipGetLastError();
+}
+
+hipError_t radix_sort_u32(const uint32_t* keys_in, const uint32_t* vals_in, int64_t n,
+                          const SortPlan& plan, const uint32_t* hist, uint32_t* kbuf0,
+                          uint32_t* kbuf1, uint32_t* vbuf0, uint32_t* vbuf1, SortWork& ws,
+                          uint32_t* status, const uint32_t** keys_out, const uint32_t** vals_out,
                           hipStream_t s) {
-    return radix_sort_impl<uint64_t>(keys_in, vals_in, n, key_bits, kbuf0, kbuf1, vbuf0, vbuf1,
-                                     counts, keys_out, vals_out, s);
+    return sort_impl<uint32_t>(keys_in, vals_in, n, plan, hist, kbuf0, kbuf1, vbuf0, vbuf1, ws,
+                               status, keys_out, vals_out, s);
+}
+
+hipError_t radix_sort_u64(const uint64_t* keys_in, const uint32_t* vals_in, int64_t n,
+                          const SortPlan& plan, const uint32_t* hist, uint64_t* kbuf0,
+                          uint64_t* kbuf1, uint32_t* vbuf0, uint32_t* vbuf1, SortWork& ws,
+                          uint32_t* status, const uint64_t** keys_out, const uint32_t** vals_out,
+                          hipStream_t s) {
+    return sort_impl<uint64_t>(keys_in, vals_in, n, plan, hist, kbuf0, kbuf1, vbuf0, vbuf1, ws,
+                               status, keys_out, vals_out, s);
 }
 
 }  // namespace smc

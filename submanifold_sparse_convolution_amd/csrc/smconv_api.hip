@@ -1,6 +1,6 @@
 // C ABI: map handles, the map build pipeline, weight packing and the
 // forward layer. See include/smconv.h for the contract of each call.
-#include "../../include/smconv.h"
+#include "smconv.h"
 #include "smc_internal.h"
 
 #include <algorithm>
@@ -97,14 +97,22 @@ struct smc_map {
     int64_t grid_clean_cells = 0;     // prefix of grid known to be -1
     DevBuf keys0, keys1, keys2;       // packed keys (u32 or u64)
     DevBuf vals0, vals1;              // u32
-    DevBuf radix_counts;
+    DevBuf hist;                      // digit histograms: mask sort, then key sort
+    DevBuf look, ticket;              // look-back table and block ticket (zeroed when allocated)
+    SortWork ws;
+    bool state_copied = false;        // host_state already holds the last build's record
     DevBuf nbr, mask, mkey0, mkey1, mval0, mval1;
     const uint32_t* perm = nullptr;   // points into mval0 or mval1
-    DevBuf chunk_counts;
     DevBuf pair_in, pair_out, tile_tap;
     int64_t pair_cap = 0;
     DevBuf acc;                       // float32 accumulator, kept all zero between forwards
     size_t acc_clean_bytes = 0;
+    // stage timers
+    bool timing = false;
+    std::vector<hipEvent_t> ev_pool;
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> ev_open[SMC_STAGE_COUNT];
+    double stage_ms[SMC_STAGE_COUNT] = {};
+    int64_t stage_calls[SMC_STAGE_COUNT] = {};
 };
 
 namespace {
@@ -124,6 +132,11 @@ int ensure_device(smc_map* m) {
         }
         int rc = m->state.ensure(sizeof(MapState));
         if (rc) return rc;
+        if ((rc = m->ticket.ensure(256)) || (rc = m->hist.ensure((kHistMaskInts + kHistKeyInts) * 4)))
+            return rc;
+        SMC_HIP(launch_fill_i32(m->ticket.as<int32_t>(), 64, 0, nullptr));
+        SMC_HIP(hipDeviceSynchronize());
+        m->ws.ticket = m->ticket.as<uint32_t>();
     } else if (dev != m->device) {
         return fail(SMC_ERR_STATE, "map was created on device %d, current device is %d",
                     m->device, dev);
@@ -134,8 +147,16 @@ int ensure_device(smc_map* m) {
 int wait_build(smc_map* m) {
     if (!m->pending) return SMC_OK;
     SMC_HIP(hipEventSynchronize(m->done));
+    if (!m->state_copied) {
+        SMC_HIP(hipMemcpy(m->host_state, m->state.p, sizeof(MapState), hipMemcpyDeviceToHost));
+        m->state_copied = true;
+    }
     m->pending = false;
     uint32_t st = m->host_state->status;
+    if (st & kStSortStall) {
+        m->build_status = SMC_ERR_HIP;
+        return fail(SMC_ERR_HIP, "a look-back wait of the map build ran out (results invalid)");
+    }
     if (st & kStDuplicate) {
         m->build_status = SMC_ERR_DUPLICATE;
         return fail(SMC_ERR_DUPLICATE, "two rows share the same (b, x, y, z)");
@@ -163,6 +184,47 @@ int ensure_grid(smc_map* m, int64_t cells, hipStream_t s) {
     }
     return SMC_OK;
 }
+
+// Records the start event of a stage on construction and the end event on
+// finish(); does nothing while timing is off.
+struct StageTimer {
+    smc_map* m;
+    int stage;
+    hipStream_t s;
+    hipEvent_t a = nullptr;
+    static hipEvent_t take(smc_map* m) {
+        if (!m->ev_pool.empty()) {
+            hipEvent_t e = m->ev_pool.back();
+            m->ev_pool.pop_back();
+            return e;
+        }
+        hipEvent_t e = nullptr;
+        if (hipEventCreate(&e) != hipSuccess) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        return e;
+    }
+    StageTimer(smc_map* m_, int stage_, hipStream_t s_) : m(m_), stage(stage_), s(s_) {
+        if (!m->timing) return;
+        a = take(m);
+        if (a) (void)hipEventRecord(a, s);
+    }
+    ~StageTimer() {
+        if (a) m->ev_pool.push_back(a);
+    }
+    void finish() {
+        if (!a) return;
+        hipEvent_t b = take(m);
+        if (b) {
+            (void)hipEventRecord(b, s);
+            m->ev_open[stage].push_back({a, b});
+        } else {
+            m->ev_pool.push_back(a);
+        }
+        a = nullptr;
+    }
+};
 
 }  // namespace
 
@@ -204,10 +266,16 @@ int smc_map_destroy(smc_map* m) {
         (void)hipSetDevice(m->device);
         (void)hipDeviceSynchronize();
         DevBuf* bufs[] = {&m->state, &m->grid, &m->keys0, &m->keys1, &m->keys2,
-                          &m->vals0, &m->vals1, &m->radix_counts, &m->nbr, &m->mask,
-                          &m->mkey0, &m->mkey1, &m->mval0, &m->mval1, &m->chunk_counts,
+                          &m->vals0, &m->vals1, &m->hist, &m->look, &m->ticket, &m->nbr,
+                          &m->mask, &m->mkey0, &m->mkey1, &m->mval0, &m->mval1,
                           &m->pair_in, &m->pair_out, &m->tile_tap, &m->acc};
         for (DevBuf* b : bufs) b->release();
+        for (auto& v : m->ev_open)
+            for (auto& pr : v) {
+                m->ev_pool.push_back(pr.first);
+                m->ev_pool.push_back(pr.second);
+            }
+        for (hipEvent_t e : m->ev_pool) (void)hipEventDestroy(e);
         if (m->host_state) (void)hipHostFree(m->host_state);
         if (m->done) (void)hipEventDestroy(m->done);
         (void)hipSetDevice(cur);
@@ -239,7 +307,8 @@ int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     m->built = false;
     m->perm = nullptr;
     MapState* st = m->state.as<MapState>();
-    SMC_HIP(launch_state_init(st, s));
+    StageTimer t_map(m, SMC_STAGE_MAP, s);
+    SMC_HIP(launch_state_init(st, m->hist.as<uint32_t>(), kHistMaskInts + kHistKeyInts, s));
 
     // ---- geometry: explicit shape, or the bounding box (one read) ----
     Geom g{};
@@ -314,28 +383,37 @@ int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
 
     // ---- buffers ----
     const int64_t nn = n > 0 ? n : 1;
-    const int64_t n_chunks = (nn + kChunk - 1) / kChunk;
     const int64_t pair_cap = 27 * nn + 27 * (int64_t)kTileM;
+    size_t look_bytes = sort_look_bytes(nn);
+    size_t look_c = (size_t)compact_chunks(nn) * kTaps * 8;
+    if (look_c > look_bytes) look_bytes = look_c;
+    const size_t look_before = m->look.bytes;
     if ((rc = m->nbr.ensure((size_t)nn * kTaps * 4)) || (rc = m->mask.ensure((size_t)nn * 4)) ||
         (rc = m->mkey0.ensure((size_t)nn * 4)) || (rc = m->mkey1.ensure((size_t)nn * 4)) ||
         (rc = m->mval0.ensure((size_t)nn * 4)) || (rc = m->mval1.ensure((size_t)nn * 4)) ||
-        (rc = m->radix_counts.ensure(radix_counts_elems(nn) * 4)) ||
-        (rc = m->chunk_counts.ensure((size_t)n_chunks * kTaps * 4)) ||
+        (rc = m->look.ensure(look_bytes)) ||
         (rc = m->pair_in.ensure((size_t)pair_cap * 4)) ||
         (rc = m->pair_out.ensure((size_t)pair_cap * 4)) ||
         (rc = m->tile_tap.ensure((size_t)(pair_cap / kTileM + 1) * 4)))
         return rc;
+    if (m->look.bytes != look_before || look_before == 0)   // new table: epoch 0 everywhere
+        SMC_HIP(launch_fill_i32(m->look.as<int32_t>(), (int64_t)(m->look.bytes / 4), 0, s));
+    m->ws.look = m->look.as<uint64_t>();
     m->pair_cap = pair_cap;
+    uint32_t* status = &st->status;
+    uint32_t* hist_mask = m->hist.as<uint32_t>();
+    uint32_t* hist_key = hist_mask + kHistMaskInts;
 
     if (n > 0) {
         int32_t* nbr = m->nbr.as<int32_t>();
         uint32_t* mask = m->mask.as<uint32_t>();
+        int32_t* grid = nullptr;
+        StageTimer t_nb(m, SMC_STAGE_NEIGHBOURS, s);
         if (chosen == SMC_ROUTE_DENSE) {
             if ((rc = ensure_grid(m, m->grid_cells, s))) return rc;
-            int32_t* grid = m->grid.as<int32_t>();
+            grid = m->grid.as<int32_t>();
             SMC_HIP(launch_dense_scatter(coords, n, g, grid, st, s));
             SMC_HIP(launch_dense_lookup(coords, n, g, grid, nbr, mask, s));
-            SMC_HIP(launch_dense_clear(coords, n, g, grid, s));
         } else {
             const size_t kb = (size_t)nn * (m->wide ? 8 : 4);
             if ((rc = m->keys0.ensure(kb)) || (rc = m->keys1.ensure(kb)) ||
@@ -343,42 +421,50 @@ int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
                 (rc = m->vals1.ensure((size_t)nn * 4)))
                 return rc;
             SMC_HIP(launch_make_keys(coords, n, g, m->wide, m->keys0.p, st, s));
+            const SortPlan kp = sort_plan(key_bits);
+            SMC_HIP(launch_key_hist(m->keys0.p, m->wide, n, kp, hist_key, s));
             const void* skeys;
             const uint32_t* svals;
             if (m->wide) {
-                SMC_HIP(radix_sort_u64(m->keys0.as<uint64_t>(), nullptr, n, key_bits,
+                SMC_HIP(radix_sort_u64(m->keys0.as<uint64_t>(), nullptr, n, kp, hist_key,
                                        m->keys1.as<uint64_t>(), m->keys2.as<uint64_t>(),
-                                       m->vals0.as<uint32_t>(), m->vals1.as<uint32_t>(),
-                                       m->radix_counts.as<uint32_t>(),
-                                       (const uint64_t**)&skeys, &svals, s));
+                                       m->vals0.as<uint32_t>(), m->vals1.as<uint32_t>(), m->ws,
+                                       status, (const uint64_t**)&skeys, &svals, s));
             } else {
-                SMC_HIP(radix_sort_u32(m->keys0.as<uint32_t>(), nullptr, n, key_bits,
+                SMC_HIP(radix_sort_u32(m->keys0.as<uint32_t>(), nullptr, n, kp, hist_key,
                                        m->keys1.as<uint32_t>(), m->keys2.as<uint32_t>(),
-                                       m->vals0.as<uint32_t>(), m->vals1.as<uint32_t>(),
-                                       m->radix_counts.as<uint32_t>(),
-                                       (const uint32_t**)&skeys, &svals, s));
+                                       m->vals0.as<uint32_t>(), m->vals1.as<uint32_t>(), m->ws,
+                                       status, (const uint32_t**)&skeys, &svals, s));
             }
             SMC_HIP(launch_sorted_lookup(skeys, svals, n, g, m->wide, nbr, mask, st, s));
         }
-        // rows ordered by (mask, row)
+        t_nb.finish();
+        // rows ordered by (mask, row): histograms (+ per-tap totals, grid cleanup), then passes
+        StageTimer t_ms(m, SMC_STAGE_MASK_SORT, s);
+        const SortPlan mp = sort_plan(kMaskBits);
+        SMC_HIP(launch_mask_hist(mask, n, mp, hist_mask, st->tap_tot, coords, g, grid, s));
         const uint32_t* sorted_masks;
-        SMC_HIP(radix_sort_u32(mask, nullptr, n, kTaps, m->mkey0.as<uint32_t>(),
+        SMC_HIP(radix_sort_u32(mask, nullptr, n, mp, hist_mask, m->mkey0.as<uint32_t>(),
                                m->mkey1.as<uint32_t>(), m->mval0.as<uint32_t>(),
-                               m->mval1.as<uint32_t>(), m->radix_counts.as<uint32_t>(),
-                               &sorted_masks, &m->perm, s));
-        int32_t* counts = m->chunk_counts.as<int32_t>();
-        SMC_HIP(launch_pair_count(m->perm, mask, n, counts, s));
-        SMC_HIP(launch_pair_scan(counts, n, kTileM, st, m->pair_in.as<int32_t>(),
-                                 m->pair_out.as<int32_t>(), m->tile_tap.as<int32_t>(), s));
-        SMC_HIP(launch_pair_write(m->perm, mask, nbr, n, counts, m->pair_in.as<int32_t>(),
-                                  m->pair_out.as<int32_t>(), s));
+                               m->mval1.as<uint32_t>(), m->ws, status, &sorted_masks, &m->perm,
+                               s));
+        t_ms.finish();
+        StageTimer t_cp(m, SMC_STAGE_COMPACT, s);
+        SMC_HIP(launch_compact(m->perm, mask, nbr, n, st->tap_tot, kTileM, st,
+                               m->pair_in.as<int32_t>(), m->pair_out.as<int32_t>(),
+                               m->tile_tap.as<int32_t>(), m->ws, status, s));
+        t_cp.finish();
     }
-    SMC_HIP(hipMemcpyAsync(m->host_state, st, sizeof(MapState), hipMemcpyDeviceToHost, s));
+    t_map.finish();
+    const bool async = (flags & SMC_BUILD_ASYNC) != 0;
+    if (!async)
+        SMC_HIP(hipMemcpyAsync(m->host_state, st, sizeof(MapState), hipMemcpyDeviceToHost, s));
+    m->state_copied = !async;
     SMC_HIP(hipEventRecord(m->done, s));
     m->pending = true;
     m->built = true;
     m->build_status = SMC_OK;
-    if (flags & SMC_BUILD_ASYNC) return SMC_OK;
+    if (async) return SMC_OK;
     return wait_build(m);
 }
 
@@ -476,6 +562,7 @@ int smc_conv_forward(smc_map* m, const uint16_t* x, int c_in, const void* wpacke
     if (((uintptr_t)wpacked & 15) != 0) return fail(SMC_ERR_ARG, "packed weights not 16-byte aligned");
     if ((c_in & 7) == 0 && ((uintptr_t)x & 15) != 0)
         return fail(SMC_ERR_ARG, "x must be 16-byte aligned when c_in is a multiple of 8");
+    if (((uintptr_t)y & 15) != 0) return fail(SMC_ERR_ARG, "y must be 16-byte aligned");
     int dev = 0;
     SMC_HIP(hipGetDevice(&dev));
     if (dev != m->device) return fail(SMC_ERR_STATE, "map lives on device %d", m->device);
@@ -488,11 +575,46 @@ int smc_conv_forward(smc_map* m, const uint16_t* x, int c_in, const void* wpacke
         m->acc_clean_bytes = m->acc.bytes;
     }
     const int64_t max_tiles = m->pair_cap / kTileM;
-    SMC_HIP(launch_gemm(x, c_in, wpacked, c_out, m->pair_in.as<int32_t>(),
-                        m->pair_out.as<int32_t>(), m->tile_tap.as<int32_t>(),
-                        m->state.as<MapState>(), max_tiles, m->n_cu, m->acc.as<float>(), s));
-    SMC_HIP(launch_finalize(m->acc.as<float>(), y, (flags & SMC_FWD_OUT_F32) != 0,
-                            m->n * (int64_t)c_out, (flags & SMC_FWD_RELU) != 0, s));
+    StageTimer t_g(m, SMC_STAGE_GEMM, s);
+    SMC_HIP(launch_gemm_nc(x, c_in, wpacked, c_out, m->pair_in.as<int32_t>(),
+                           m->pair_out.as<int32_t>(), m->tile_tap.as<int32_t>(),
+                           m->state.as<MapState>(), m->n, max_tiles, m->n_cu,
+                           m->acc.as<float>(), s));
+    t_g.finish();
+    StageTimer t_f(m, SMC_STAGE_CENTRE, s);
+    SMC_HIP(launch_gemm_centre(x, c_in, wpacked, c_out, m->mask.as<uint32_t>(), m->n,
+                               m->acc.as<float>(), y, (flags & SMC_FWD_OUT_F32) != 0,
+                               (flags & SMC_FWD_RELU) != 0, m->n_cu, s));
+    t_f.finish();
+    return SMC_OK;
+}
+
+int smc_timing_enable(smc_map* m, int on) {
+    if (!m) return fail(SMC_ERR_ARG, "map is NULL");
+    m->timing = on != 0;
+    return SMC_OK;
+}
+
+int smc_timing_read(smc_map* m, double* ms, int64_t* calls, int reset) {
+    if (!m) return fail(SMC_ERR_ARG, "map is NULL");
+    for (int st = 0; st < SMC_STAGE_COUNT; ++st) {
+        for (auto& pr : m->ev_open[st]) {
+            SMC_HIP(hipEventSynchronize(pr.second));
+            float e = 0.f;
+            SMC_HIP(hipEventElapsedTime(&e, pr.first, pr.second));
+            m->stage_ms[st] += e;
+            m->stage_calls[st] += 1;
+            m->ev_pool.push_back(pr.first);
+            m->ev_pool.push_back(pr.second);
+        }
+        m->ev_open[st].clear();
+        if (ms) ms[st] = m->stage_ms[st];
+        if (calls) calls[st] = m->stage_calls[st];
+        if (reset) {
+            m->stage_ms[st] = 0;
+            m->stage_calls[st] = 0;
+        }
+    }
     return SMC_OK;
 }
 

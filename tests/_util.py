@@ -52,13 +52,24 @@ def assert_map_equal(got, want, label=""):
                                  f"got {g[first]} want {w[first]}")
 
 
-def check_bf16_output(y_bits, acc_ref, label="", max_ulp=1):
-    """GPU bf16 output vs the oracle accumulator.
+def fp32_sum_bound(abs_ref, n_terms):
+    """Rigorous bound on |float32 sum - exact| for sums of n_terms products.
 
-    Required: |y - bf16(ref)| <= 2e-2 (1 + |bf16(ref)|) elementwise. Also
-    checked: at most ``max_ulp`` bf16 ulps from the oracle's rounding, which
-    is what a float32 accumulator differing from the float64 one only by
-    summation order can produce.
+    Any summation order: |fl(sum) - sum| <= gamma_n * sum|terms|, gamma_n =
+    n u / (1 - n u), u = 2^-24; abs_ref is sum|x||w| per output.
+    """
+    u = 2.0 ** -24
+    g = n_terms * u / (1 - n_terms * u)
+    return g * abs_ref
+
+
+def check_bf16_output(y_bits, acc_ref, label="", abs_ref=None, n_terms=None):
+    """GPU bf16 output vs the oracle accumulator (float64, exact products).
+
+    Required: |y - bf16(ref)| <= 2e-2 (1 + |bf16(ref)|) elementwise.
+    With abs_ref (sum |x||w| per output) also a tight, rigorous check: the
+    output is a float32 sum of n_terms products rounded to bf16, so
+    |y - exact| <= gamma_n abs_ref + 2^-8 max(|y|, |exact|) + 2^-133.
     """
     ref = so.round_to_bf16(acc_ref)
     got = so.bf16_bits_to_f64(y_bits)
@@ -66,22 +77,32 @@ def check_bf16_output(y_bits, acc_ref, label="", max_ulp=1):
     err = np.abs(got - ref)
     bound = 2e-2 * (1 + np.abs(ref))
     worst = np.argmax(err - bound)
-    assert (err <= bound).all(), (f"{label}: bf16 tolerance exceeded at {np.unravel_index(worst, err.shape)}:"
-                                  f" got {got.flat[worst]} ref {ref.flat[worst]}")
-    rb = so.bf16_bits(ref).astype(np.int32)
-    gb = np.asarray(y_bits, np.uint16).astype(np.int32)
-    # ordered integer view of bf16 bit patterns: distance in ulps
-    def ordered(b):
-        return np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
-    ulp = np.abs(ordered(gb) - ordered(rb))
-    assert ulp.max() <= max_ulp, f"{label}: {ulp.max()} bf16 ulps from the oracle (max {max_ulp})"
+    assert (err <= bound).all(), (f"{label}: bf16 tolerance exceeded at "
+                                  f"{np.unravel_index(worst, err.shape)}: got {got.flat[worst]} "
+                                  f"ref {ref.flat[worst]}")
+    if abs_ref is not None:
+        tight = (fp32_sum_bound(abs_ref, n_terms) + 2.0 ** -8 * np.maximum(np.abs(got), np.abs(acc_ref))
+                 + 2.0 ** -133)
+        e = np.abs(got - acc_ref)
+        worst = np.argmax(e - tight)
+        assert (e <= tight).all(), (f"{label}: outside the float32+bf16 rounding bound at "
+                                    f"{np.unravel_index(worst, e.shape)}: got {got.flat[worst]} "
+                                    f"exact {acc_ref.flat[worst]} bound {tight.flat[worst]}")
 
 
-def check_f32_acc(acc_gpu, acc_ref, label=""):
-    """|acc_gpu - acc_ref| <= 1e-3 (1 + |acc_ref|) elementwise, and relative L2 <= 1e-3."""
+def check_f32_acc(acc_gpu, acc_ref, label="", abs_ref=None, n_terms=None):
+    """|acc_gpu - acc_ref| <= 1e-3 (1 + |acc_ref|) elementwise, and relative L2 <= 1e-3.
+
+    With abs_ref, also the rigorous float32 summation bound gamma_n sum|x||w|.
+    """
     acc_gpu = np.asarray(acc_gpu, np.float64)
     d = np.abs(acc_gpu - acc_ref)
     assert (d <= 1e-3 * (1 + np.abs(acc_ref))).all(), f"{label}: fp32 accumulator tolerance"
+    if abs_ref is not None:
+        b = fp32_sum_bound(abs_ref, n_terms) + 2.0 ** -126
+        worst = np.argmax(d - b)
+        assert (d <= b).all(), (f"{label}: outside the float32 summation bound at "
+                                f"{np.unravel_index(worst, d.shape)}: {d.flat[worst]} > {b.flat[worst]}")
     nr = np.linalg.norm(acc_ref)
     if nr > 0:
         assert np.linalg.norm(acc_gpu - acc_ref) / nr <= 1e-3, f"{label}: relative L2"
