@@ -48,7 +48,7 @@ def layer_algorithmic_bytes(n, c_in, c_out, pairs):
     return 16 * n + 2 * n * c_in + 2 * 27 * c_in * c_out + 8 * pairs + 2 * n * c_out
 
 
-def run_workload(name, steps, warmup, sync_build=False):
+def run_workload(name, steps, warmup, sync_build=False, algo="pairs"):
     import numpy as np
     import torch
 
@@ -77,10 +77,12 @@ def run_workload(name, steps, warmup, sync_build=False):
     ys = [torch.empty((w.n, c), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
 
     def step():
-        m.build(coords_d, spatial_shape=w.grid, batch_size=1, sync=sync_build)
+        m.build(coords_d, spatial_shape=w.grid, batch_size=1, sync=sync_build,
+                pairs=(algo == "pairs"))
         h = x_d
         for layer in range(w.layers):
-            h = m.forward(h, packed[layer], relu=layer + 1 < w.layers, out=ys[layer & 1])
+            h = m.forward(h, packed[layer], relu=layer + 1 < w.layers, out=ys[layer & 1],
+                          algo=algo)
         return h
 
     for _ in range(warmup):
@@ -162,6 +164,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="lidar",
                     choices=["tiny", "lidar", "deep", "wide", "stage"])
+    ap.add_argument("--algo", default="pairs", choices=["pairs", "mask_tiles"],
+                    help="forward algorithm of the headline line (the other is reported too)")
     ap.add_argument("--sync-build", action="store_true",
                     help="wait for the map's device-side checks inside every step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -180,7 +184,9 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
 
-    r = run_workload(args.workload, args.steps, args.warmup, args.sync_build)
+    r = run_workload(args.workload, args.steps, args.warmup, args.sync_build, args.algo)
+    other = "mask_tiles" if args.algo == "pairs" else "pairs"
+    r2 = run_workload(args.workload, args.steps, args.warmup, args.sync_build, other)
     w, info = r["workload"], r["info"]
     c = w.channels
     gemm_gbs = r["gemm_bytes"] / (r["gemm_us"] * 1e-6) / 1e9 if r["gemm_us"] else 0.0
@@ -203,6 +209,7 @@ def main():
             "n": w.n, "pairs": r["pairs"], "pairs_per_voxel": round(r["pairs"] / w.n, 4),
             "route": info["route"], "c_in": c, "c_out": c, "layers": w.layers,
             "map_built_every_step": True, "build_mode": "sync" if args.sync_build else "async",
+            "algo": args.algo,
         },
         "tflops_effective": round(r["tflops_effective"], 3),
         "frac_bf16_peak": round(r["tflops_effective"] / PEAK_BF16_TFLOPS, 5),
@@ -223,17 +230,24 @@ def main():
             "mfma_frac_useful": round(r["gemm_tflops"] / PEAK_BF16_TFLOPS, 5),
         },
     }
+    line["other_algo"] = {
+        "algo": other, "us_per_layer": round(r2["per_layer_us"], 2),
+        "tflops_effective": round(r2["tflops_effective"], 3),
+        "stage_us": {k: round(v, 2) for k, v in r2["stage_us"].items()},
+    }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.workload)
     if args.report:
         rep = {}
         for name in ("tiny", "lidar", "deep", "wide", "stage"):
-            rr = run_workload(name, max(20, args.steps // 2), args.warmup)
-            rep[name] = {k: rr[k] for k in ("pairs", "ms_per_step", "per_layer_us", "pack_us",
-                                            "tflops_effective", "stage_us", "gemm_us",
-                                            "gemm_tflops", "gemm_bytes", "layer_bytes")}
-            rep[name]["route"] = rr["info"]["route"]
-            rep[name]["n"] = rr["workload"].n
+            for algo in ("pairs", "mask_tiles"):
+                rr = run_workload(name, max(20, args.steps // 2), args.warmup, algo=algo)
+                key = f"{name}/{algo}"
+                rep[key] = {k: rr[k] for k in ("pairs", "ms_per_step", "per_layer_us", "pack_us",
+                                               "tflops_effective", "stage_us", "gemm_us",
+                                               "gemm_tflops", "gemm_bytes", "layer_bytes")}
+                rep[key]["route"] = rr["info"]["route"]
+                rep[key]["n"] = rr["workload"].n
         with open(args.report, "w") as f:
             json.dump(rep, f, indent=1)
     print(json.dumps(line), flush=True)

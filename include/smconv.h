@@ -72,13 +72,16 @@ enum {
 
 /* smc_map_build flags */
 enum {
-    SMC_BUILD_ASYNC = 1   /* do not wait for the device-side checks; call smc_map_sync() later */
+    SMC_BUILD_ASYNC = 1,  /* do not wait for the device-side checks; call smc_map_sync() later */
+    SMC_BUILD_NO_PAIRS = 2 /* skip the per-tap pair lists (only SMC_FWD_MASK_TILES forwards
+                              and the table, mask and order exports are then available) */
 };
 
 /* smc_conv_forward flags */
 enum {
-    SMC_FWD_RELU = 1,     /* apply max(y, 0) to the (rounded) output */
-    SMC_FWD_OUT_F32 = 2   /* write the float32 accumulator itself: y is float [n, c_out] */
+    SMC_FWD_RELU = 1,       /* apply max(y, 0) to the (rounded) output */
+    SMC_FWD_OUT_F32 = 2,    /* write the float32 accumulator itself: y is float [n, c_out] */
+    SMC_FWD_MASK_TILES = 4  /* output-stationary mask-tile algorithm (see smc_conv_forward) */
 };
 
 typedef struct smc_map_info_s {
@@ -177,16 +180,24 @@ size_t smc_weight_packed_bytes(int c_in, int c_out);
 int smc_weight_pack(const uint16_t* w, int c_in, int c_out, void* out, void* stream);
 
 /*
- * One submanifold convolution layer over a built map ("[Kernel] ...",
- * Design "GEMM": gather -> mfma_f32_16x16x32_bf16 with float32 accumulate
- * -> scatter-add, the centre tap compacted with the rest).
+ * One submanifold convolution layer over a built map. Two algorithms:
+ *  - default, per-tap pair lists ("[Kernel] Add submanifold sparse 3D
+ *    convolution", Design "GEMM": gather -> mfma_f32_16x16x32_bf16 with
+ *    float32 accumulate -> scatter-add): the non-centre taps scatter-add into
+ *    a float32 accumulator, then the centre tap (every row with itself) runs
+ *    as a dense tile fused with the output write;
+ *  - SMC_FWD_MASK_TILES ("Sparse convolution in FP32", "Neighbour masks and
+ *    sorted rows"): tiles of mask-sorted rows run the union of their masks'
+ *    taps and keep every tap's sum in registers; one kernel, no atomics, no
+ *    accumulator in memory. Works on maps built with or without pair lists.
  * x       device pointer, bf16 [n, c_in] row-major (rows in coordinate order).
  * wpacked device pointer from smc_weight_pack(c_in, c_out).
  * y       device pointer, 16-byte aligned, bf16 [n, c_out] (float [n, c_out] with
  *         SMC_FWD_OUT_F32); every row is written.
  * flags   SMC_FWD_RELU | SMC_FWD_OUT_F32, or 0. Without SMC_FWD_OUT_F32 the output
  *         is the float32 accumulator rounded to bf16 (to nearest, ties to even).
- * The float32 accumulator lives in the handle (grow-only, 4 n c_out bytes).
+ * The pair-list algorithm's float32 accumulator lives in the handle (grow-only,
+ * 4 n c_out bytes); it needs a map built without SMC_BUILD_NO_PAIRS.
  * Needs no host read of the map's pair counts: the GEMM reads them on the
  * device. Refuses (SMC_ERR_STATE) a map whose synchronous build failed or
  * a map that was never built.

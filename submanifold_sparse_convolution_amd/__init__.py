@@ -26,6 +26,9 @@ _ROUTE_NAMES = {v: k for k, v in ROUTES.items()}
 SMC_BUILD_ASYNC = 1
 SMC_FWD_RELU = 1
 SMC_FWD_OUT_F32 = 2
+SMC_FWD_MASK_TILES = 4
+SMC_BUILD_NO_PAIRS = 2
+ALGOS = ("pairs", "mask_tiles")
 
 EXPORTED_SYMBOLS = [
     "smc_map_create", "smc_map_destroy", "smc_map_build", "smc_map_sync", "smc_map_info",
@@ -167,15 +170,17 @@ class KernelMap:
             pass
 
     def build(self, coords, spatial_shape=None, batch_size: int = 0, route: str = "auto",
-              sync: bool = True, stream=None) -> "KernelMap":
-        """coords: int32 [N, 4] (b, x, y, z) or [N, 3] (x, y, z) CUDA tensor."""
+              sync: bool = True, pairs: bool = True, stream=None) -> "KernelMap":
+        """coords: int32 [N, 4] (b, x, y, z) or [N, 3] (x, y, z) CUDA tensor.
+
+        pairs=False skips the per-tap pair lists (enough for algo="mask_tiles")."""
         import torch
         _need(coords, torch.int32, "coords", 2)
         n, ncols = int(coords.shape[0]), int(coords.shape[1])
         shape = None
         if spatial_shape is not None:
             shape = (ctypes.c_int32 * 3)(*[int(v) for v in spatial_shape])
-        flags = 0 if sync else SMC_BUILD_ASYNC
+        flags = (0 if sync else SMC_BUILD_ASYNC) | (0 if pairs else SMC_BUILD_NO_PAIRS)
         self._coords = coords          # keep alive while the stream reads it
         self.n = n
         _check(lib().smc_map_build(self._h, ctypes.c_void_p(coords.data_ptr() if n else 0), n,
@@ -206,25 +211,32 @@ class KernelMap:
                     pairs_padded=inf.pairs_padded, n_tiles=inf.n_tiles,
                     tap_count=list(inf.tap_count), status=inf.status)
 
-    def export(self) -> dict:
-        """Copy nbr, mask, perm, pair lists and tap offsets to numpy (host)."""
+    def export(self, pairs: bool = True) -> dict:
+        """Copy nbr, mask, perm, tap offsets (and the pair lists) to numpy (host)."""
         import numpy as np
         info = self.info()
         n, p = info["n"], info["pairs"]
         out = dict(nbr=np.empty((n, 27), np.int32), mask=np.empty(n, np.uint32),
-                   perm=np.empty(n, np.int32), pair_in=np.empty(p, np.int32),
-                   pair_out=np.empty(p, np.int32), tap_off=np.empty(28, np.int64))
+                   perm=np.empty(n, np.int32), tap_off=np.empty(28, np.int64))
+        if pairs:
+            out["pair_in"] = np.empty(p, np.int32)
+            out["pair_out"] = np.empty(p, np.int32)
 
-        def ptr(a):
-            return ctypes.c_void_p(a.ctypes.data) if a.size else None
-        _check(lib().smc_map_export(self._h, ptr(out["nbr"]), ptr(out["mask"]), ptr(out["perm"]),
-                                    ptr(out["pair_in"]), ptr(out["pair_out"]),
-                                    ptr(out["tap_off"])))
+        def ptr(key):
+            a = out.get(key)
+            return ctypes.c_void_p(a.ctypes.data) if a is not None and a.size else None
+        _check(lib().smc_map_export(self._h, ptr("nbr"), ptr("mask"), ptr("perm"),
+                                    ptr("pair_in"), ptr("pair_out"), ptr("tap_off")))
         return out
 
     def forward(self, x, w: PackedWeights, relu: bool = False, out=None, out_f32: bool = False,
-                stream=None):
-        """x: bf16 [N, C_in] CUDA tensor -> bf16 [N, C_out] (float32 with out_f32)."""
+                algo: str = "pairs", stream=None):
+        """x: bf16 [N, C_in] CUDA tensor -> bf16 [N, C_out] (float32 with out_f32).
+
+        algo: "pairs" (per-tap pair lists, scatter-add) or "mask_tiles"
+        (output-stationary tiles of mask-sorted rows)."""
+        if algo not in ALGOS:
+            raise ValueError(f"algo must be one of {ALGOS}")
         import torch
         _need(x, torch.bfloat16, "x", 2)
         if x.shape[0] != self.n:
@@ -242,7 +254,9 @@ class KernelMap:
                                       ctypes.c_void_p(w.buf.data_ptr()), w.c_out,
                                       ctypes.c_void_p(out.data_ptr()),
                                       (SMC_FWD_RELU if relu else 0)
-                                      | (SMC_FWD_OUT_F32 if out_f32 else 0), _stream(stream)))
+                                      | (SMC_FWD_OUT_F32 if out_f32 else 0)
+                                      | (SMC_FWD_MASK_TILES if algo == "mask_tiles" else 0),
+                                      _stream(stream)))
         return out
 
 

@@ -33,22 +33,10 @@
 // for output column c NBW + nb, so each lane ends up holding NBW
 // consecutive output columns of its rows (one vector store per row). The
 // packed weights follow both orderings.
-#include "smc_internal.h"
+#include "gemm_common.h"
 
 namespace smc {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kGemmThreads = 256;   // 4 waves, 16 rows each: kTileM = 64 rows per tile
-
-__device__ inline bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-inline int nbw_for(int c_out) {
-    int nb = (c_out + 15) / 16;
-    return nb >= 8 ? 8 : nb >= 4 ? (nb == 4 ? 4 : 8) : nb >= 2 ? (nb == 2 ? 2 : 4) : 1;
-}
 
 // Packed weights: [tap][wave tile][k-step][nb][lane][8] bf16; one MFMA's B
 // fragment is 1 KiB contiguous and a k-step's NBW fragments are adjacent.
@@ -86,22 +74,6 @@ __global__ __launch_bounds__(kBlock) void k_fill_f32_zero(float* p, int64_t n) {
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
          i += (int64_t)gridDim.x * blockDim.x)
         p[i] = 0.0f;
-}
-
-// 8 input channels k0..k0+7 of a gathered row. Reads that fall outside the
-// data are redirected, never masked: channels past c_in read the row's own
-// first channels (the packed weights are zero there, and those values are
-// finite whenever the row's output is), and absent rows (pad pairs, rows past
-// n) read row 0 (their output row is discarded). Only the address is
-// selected, so a batch of these loads issues back to back.
-template <bool VEC>
-__device__ __forceinline__ uint4 load_a(const uint16_t* __restrict__ xrow, int k0, int c_in) {
-    if (VEC) return *reinterpret_cast<const uint4*>(xrow + (k0 < c_in ? k0 : 0));
-    uint32_t h[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) h[j] = xrow[k0 + j < c_in ? k0 + j : 0];
-    return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                      h[6] | (h[7] << 16));
 }
 
 // Copy n16 16-byte words of packed weights into LDS with 8 loads in flight
@@ -219,13 +191,6 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_nc(
             }
         }
     }
-}
-
-__device__ inline uint32_t bf16_rne_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;   // NaN stays NaN
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
 }
 
 // Centre tap + output. Blocks stride over tiles of 64 MW consecutive rows;

@@ -116,4 +116,10 @@ hipError_t launch_gemm_centre(const uint16_t* x, int c_in, const void* wpacked, 
                               const uint32_t* mask, int64_t n, float* acc, void* y, bool out_f32,
                               bool relu, int n_cu, hipStream_t s);
 
+// ---- mask-tile GEMM (masktile_kernels.hip) ----
+hipError_t launch_conv_masktile(const uint16_t* x, int c_in, const void* wpacked, int c_out,
+                                const int32_t* nbr, const uint32_t* mask, const uint32_t* perm,
+                                int64_t n, const uint16_t* zrow, void* y, bool out_f32, bool relu,
+                                hipStream_t s);
+
 }  // namespace smc

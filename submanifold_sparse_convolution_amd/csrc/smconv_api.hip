@@ -63,7 +63,9 @@ struct DevBuf {
     template <typename T> T* as() const { return static_cast<T*>(p); }
 };
 
-constexpr int64_t kMaxRows = (int64_t)1 << 26;                 // keeps 27 n + pads < 2^31
+constexpr int64_t kMaxRows = (int64_t)1 << 26;
+constexpr int kMaxChannels = 4096;
+constexpr int kZeroRowBytes = kMaxChannels * 2;                 // keeps 27 n + pads < 2^31
 constexpr int64_t kDenseBudgetBytes = (int64_t)4 << 30;        // auto route: grid <= 4 GiB
 
 int bit_len(int64_t v) {   // bits needed to hold 0..v
@@ -106,6 +108,8 @@ struct smc_map {
     DevBuf pair_in, pair_out, tile_tap;
     int64_t pair_cap = 0;
     DevBuf acc;                       // float32 accumulator, kept all zero between forwards
+    DevBuf zrow;                      // zero row read for absent neighbours (mask-tile GEMM)
+    bool has_pairs = false;
     size_t acc_clean_bytes = 0;
     // stage timers
     bool timing = false;
@@ -132,9 +136,11 @@ int ensure_device(smc_map* m) {
         }
         int rc = m->state.ensure(sizeof(MapState));
         if (rc) return rc;
-        if ((rc = m->ticket.ensure(256)) || (rc = m->hist.ensure((kHistMaskInts + kHistKeyInts) * 4)))
+        if ((rc = m->ticket.ensure(256)) || (rc = m->hist.ensure((kHistMaskInts + kHistKeyInts) * 4)) ||
+            (rc = m->zrow.ensure(kZeroRowBytes)))
             return rc;
         SMC_HIP(launch_fill_i32(m->ticket.as<int32_t>(), 64, 0, nullptr));
+        SMC_HIP(launch_fill_i32(m->zrow.as<int32_t>(), kZeroRowBytes / 4, 0, nullptr));
         SMC_HIP(hipDeviceSynchronize());
         m->ws.ticket = m->ticket.as<uint32_t>();
     } else if (dev != m->device) {
@@ -268,7 +274,7 @@ int smc_map_destroy(smc_map* m) {
         DevBuf* bufs[] = {&m->state, &m->grid, &m->keys0, &m->keys1, &m->keys2,
                           &m->vals0, &m->vals1, &m->hist, &m->look, &m->ticket, &m->nbr,
                           &m->mask, &m->mkey0, &m->mkey1, &m->mval0, &m->mval1,
-                          &m->pair_in, &m->pair_out, &m->tile_tap, &m->acc};
+                          &m->pair_in, &m->pair_out, &m->tile_tap, &m->acc, &m->zrow};
         for (DevBuf* b : bufs) b->release();
         for (auto& v : m->ev_open)
             for (auto& pr : v) {
@@ -449,12 +455,15 @@ int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
                                m->mval1.as<uint32_t>(), m->ws, status, &sorted_masks, &m->perm,
                                s));
         t_ms.finish();
-        StageTimer t_cp(m, SMC_STAGE_COMPACT, s);
-        SMC_HIP(launch_compact(m->perm, mask, nbr, n, st->tap_tot, kTileM, st,
-                               m->pair_in.as<int32_t>(), m->pair_out.as<int32_t>(),
-                               m->tile_tap.as<int32_t>(), m->ws, status, s));
-        t_cp.finish();
+        if (!(flags & SMC_BUILD_NO_PAIRS)) {
+            StageTimer t_cp(m, SMC_STAGE_COMPACT, s);
+            SMC_HIP(launch_compact(m->perm, mask, nbr, n, st->tap_tot, kTileM, st,
+                                   m->pair_in.as<int32_t>(), m->pair_out.as<int32_t>(),
+                                   m->tile_tap.as<int32_t>(), m->ws, status, s));
+            t_cp.finish();
+        }
     }
+    m->has_pairs = !(flags & SMC_BUILD_NO_PAIRS);
     t_map.finish();
     const bool async = (flags & SMC_BUILD_ASYNC) != 0;
     if (!async)
@@ -492,10 +501,17 @@ int smc_map_info(smc_map* m, smc_map_info_t* info) {
     info->tile_m = kTileM;
     info->grid_cells = m->grid_cells;
     const MapState& hs = *m->host_state;
-    info->pairs = hs.totals[0];
-    info->pairs_padded = hs.totals[1];
-    info->n_tiles = hs.totals[2];
-    for (int k = 0; k < kTaps; ++k) info->tap_count[k] = hs.tap_count[k];
+    if (m->has_pairs) {
+        info->pairs = hs.totals[0];
+        info->pairs_padded = hs.totals[1];
+        info->n_tiles = hs.totals[2];
+        for (int k = 0; k < kTaps; ++k) info->tap_count[k] = hs.tap_count[k];
+    } else {                           // counts from the mask histogram; no lists were written
+        for (int k = 0; k < kTaps; ++k) {
+            info->tap_count[k] = hs.tap_tot[k];
+            info->pairs += hs.tap_tot[k];
+        }
+    }
     info->status = rc ? rc : m->build_status;
     return SMC_OK;
 }
@@ -504,6 +520,8 @@ int smc_map_export(smc_map* m, int32_t* nbr, uint32_t* mask, int32_t* perm, int3
                    int32_t* pair_out, int64_t* tap_off) {
     if (!m) return fail(SMC_ERR_ARG, "map is NULL");
     if (!m->built) return fail(SMC_ERR_STATE, "map was never built");
+    if ((pair_in || pair_out) && !m->has_pairs)
+        return fail(SMC_ERR_STATE, "map was built without pair lists (SMC_BUILD_NO_PAIRS)");
     SMC_HIP(hipSetDevice(m->device));
     (void)wait_build(m);
     SMC_HIP(hipDeviceSynchronize());
@@ -516,7 +534,8 @@ int smc_map_export(smc_map* m, int32_t* nbr, uint32_t* mask, int32_t* perm, int3
     }
     if (tap_off) {
         tap_off[0] = 0;
-        for (int k = 0; k < kTaps; ++k) tap_off[k + 1] = tap_off[k] + hs.tap_count[k];
+        for (int k = 0; k < kTaps; ++k)
+            tap_off[k + 1] = tap_off[k] + (m->has_pairs ? hs.tap_count[k] : hs.tap_tot[k]);
     }
     if ((pair_in || pair_out) && n > 0) {
         const int64_t padded = hs.totals[1];
@@ -556,7 +575,11 @@ int smc_conv_forward(smc_map* m, const uint16_t* x, int c_in, const void* wpacke
     if (!m->pending && m->build_status != SMC_OK)
         return fail(SMC_ERR_STATE, "map build failed: %s", smc_status_string(m->build_status));
     if (c_in < 1 || c_out < 1) return fail(SMC_ERR_ARG, "c_in = %d, c_out = %d", c_in, c_out);
-    if (c_in > 4096 || c_out > 4096) return fail(SMC_ERR_UNSUPPORTED, "channels above 4096");
+    if (c_in > kMaxChannels || c_out > kMaxChannels)
+        return fail(SMC_ERR_UNSUPPORTED, "channels above 4096");
+    const bool mask_tiles = (flags & SMC_FWD_MASK_TILES) != 0;
+    if (!mask_tiles && !m->has_pairs)
+        return fail(SMC_ERR_STATE, "map was built without pair lists (SMC_BUILD_NO_PAIRS)");
     if (m->n == 0) return SMC_OK;
     if (!x || !wpacked || !y) return fail(SMC_ERR_ARG, "NULL pointer");
     if (((uintptr_t)wpacked & 15) != 0) return fail(SMC_ERR_ARG, "packed weights not 16-byte aligned");
@@ -567,6 +590,15 @@ int smc_conv_forward(smc_map* m, const uint16_t* x, int c_in, const void* wpacke
     SMC_HIP(hipGetDevice(&dev));
     if (dev != m->device) return fail(SMC_ERR_STATE, "map lives on device %d", m->device);
     hipStream_t s = (hipStream_t)stream;
+    if (mask_tiles) {
+        StageTimer t_mt(m, SMC_STAGE_GEMM, s);
+        SMC_HIP(launch_conv_masktile(x, c_in, wpacked, c_out, m->nbr.as<int32_t>(),
+                                     m->mask.as<uint32_t>(), m->perm, m->n,
+                                     m->zrow.as<uint16_t>(), y, (flags & SMC_FWD_OUT_F32) != 0,
+                                     (flags & SMC_FWD_RELU) != 0, s));
+        t_mt.finish();
+        return SMC_OK;
+    }
     const size_t acc_bytes = (size_t)m->n * c_out * 4;
     int rc = m->acc.ensure(acc_bytes);
     if (rc) return rc;
