@@ -78,7 +78,7 @@ def run_workload(name, steps, warmup, sync_build=False, algo="pairs"):
 
     def step():
         m.build(coords_d, spatial_shape=w.grid, batch_size=1, sync=sync_build,
-                pairs=(algo == "pairs"))
+                pairs=(algo == "pairs"), sort=(algo == "mask_tiles"))
         h = x_d
         for layer in range(w.layers):
             h = m.forward(h, packed[layer], relu=layer + 1 < w.layers, out=ys[layer & 1],

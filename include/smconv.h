@@ -72,9 +72,11 @@ enum {
 
 /* smc_map_build flags */
 enum {
-    SMC_BUILD_ASYNC = 1,  /* do not wait for the device-side checks; call smc_map_sync() later */
-    SMC_BUILD_NO_PAIRS = 2 /* skip the per-tap pair lists (only SMC_FWD_MASK_TILES forwards
-                              and the table, mask and order exports are then available) */
+    SMC_BUILD_ASYNC = 1,    /* do not wait for the device-side checks; call smc_map_sync() later */
+    SMC_BUILD_NO_PAIRS = 2, /* skip the per-tap pair lists: the pair-list forward and the
+                               pair exports are then refused */
+    SMC_BUILD_NO_SORT = 4   /* skip the mask-sorted row order: SMC_FWD_MASK_TILES forwards
+                               and the perm export are then refused */
 };
 
 /* smc_conv_forward flags */
@@ -91,11 +93,11 @@ typedef struct smc_map_info_s {
     int32_t origin[3];      /* grid origin (x, y, z) the coordinates are taken relative to */
     int32_t extent[3];      /* grid extent (X, Y, Z) */
     int32_t batch;          /* number of batches B */
-    int32_t tile_m;         /* pairs per GEMM tile; every tap's pair run is padded to a multiple */
+    int32_t tile_m;         /* pairs per GEMM tile */
     int64_t grid_cells;     /* dense route: cells of the padded presence grid; sorted: 0 */
     int64_t pairs;          /* P: valid (input, output) pairs including the centre tap */
-    int64_t pairs_padded;   /* P after padding every tap to a multiple of tile_m */
-    int64_t n_tiles;        /* pairs_padded / tile_m */
+    int64_t pairs_padded;   /* sum over taps of tap_count rounded up to tile_m (0 without pairs) */
+    int64_t n_tiles;        /* pairs_padded / tile_m: GEMM tiles of all taps (0 without pairs) */
     int64_t tap_count[27];  /* pairs per tap */
     int32_t status;         /* smc_status of the build's device-side checks */
 } smc_map_info_t;
@@ -109,7 +111,8 @@ int smc_map_destroy(smc_map* map);
 
 /*
  * Build the kernel map of a voxel set: neighbour table, 27-bit neighbour
- * masks, mask-sorted row order and per-tap pair lists.
+ * masks, mask-sorted row order (unless SMC_BUILD_NO_SORT) and per-tap pair
+ * lists (unless SMC_BUILD_NO_PAIRS).
  *
  * Steps (all on the GPU): bounding box -> route by grid volume ("[Kernel]
  * Add submanifold sparse 3D convolution", Design, the mapper table) ->
@@ -117,10 +120,11 @@ int smc_map_destroy(smc_map* map);
  *   sorted route: packed keys with packed(q + d) = packed(q) + packed(d),
  *                 radix sort, 9 binary searches per row ("Z-Delta", Design);
  * -> neighbour table + masks ("Sparse convolution in FP32", "Neighbour masks
- * and sorted rows") -> radix sort of rows by mask -> per-tap counts, scan,
- * pair write with each tap padded to a multiple of tile_m ("[Kernel] ...",
- * Design "Compaction"; commits "move pair compaction from torch onto three fx
- * kernels" and "scan the pair counts on the device").
+ * and sorted rows") -> radix sort of rows by mask -> per-tap counts, scan
+ * and pair write, ascending output row within a tap ("[Kernel] ...", Design
+ * "Compaction"; commits "move pair compaction from torch onto three fx
+ * kernels" and "scan the pair counts on the device"), which also numbers
+ * every row's off-centre pairs for the pair-list forward.
  *
  * coords        device pointer, int32 [n, ncols], row-major. ncols = 4: rows
  *               (b, x, y, z); ncols = 3: rows (x, y, z) with b = 0.
@@ -132,7 +136,7 @@ int smc_map_destroy(smc_map* map);
  * batch_size    number of batches B (b in [0, B)); <= 0 derives it (one read).
  * kernel_size   must be 3 (else SMC_ERR_UNSUPPORTED).
  * route         SMC_ROUTE_*.
- * flags         SMC_BUILD_ASYNC or 0. Without it the call waits for the
+ * flags         SMC_BUILD_* bits or 0. Without SMC_BUILD_ASYNC the call waits for the
  *               device-side checks and returns SMC_ERR_DUPLICATE / SMC_ERR_RANGE
  *               when they fail. With it the call returns after enqueueing; the
  *               check result comes from smc_map_sync(). A map whose checks failed
@@ -157,11 +161,12 @@ int smc_map_info(smc_map* map, smc_map_info_t* info);
  * a host pointer or NULL (skipped):
  *   nbr      int32 [n, 27]  row of c_i + d_k, or -1
  *   mask     uint32 [n]     bit k set iff nbr[i, k] >= 0
- *   perm     int32 [n]      rows in ascending (mask, row) order
- *   pair_in  int32 [pairs]  unpadded, tap-major, mask-sorted order within a tap
+ *   perm     int32 [n]      rows in ascending (mask, row) order (needs a sorted map)
+ *   pair_in  int32 [pairs]  tap-major, ascending output row within a tap
  *   pair_out int32 [pairs]
  *   tap_off  int64 [28]     pairs of tap k are [tap_off[k], tap_off[k+1])
- * Waits for the map's stream.
+ * Waits for the device. SMC_ERR_STATE if perm is asked of a map built with
+ * SMC_BUILD_NO_SORT, or pair_in / pair_out of one built with SMC_BUILD_NO_PAIRS.
  */
 int smc_map_export(smc_map* map, int32_t* nbr, uint32_t* mask, int32_t* perm,
                    int32_t* pair_in, int32_t* pair_out, int64_t* tap_off);
@@ -183,24 +188,29 @@ int smc_weight_pack(const uint16_t* w, int c_in, int c_out, void* out, void* str
  * One submanifold convolution layer over a built map. Two algorithms:
  *  - default, per-tap pair lists ("[Kernel] Add submanifold sparse 3D
  *    convolution", Design "GEMM": gather -> mfma_f32_16x16x32_bf16 with
- *    float32 accumulate -> scatter-add): the non-centre taps scatter-add into
- *    a float32 accumulator, then the centre tap (every row with itself) runs
- *    as a dense tile fused with the output write;
+ *    float32 accumulate -> scatter): the non-centre taps store each pair's
+ *    float32 product row into a partial-product slab (one row per pair, a
+ *    row's pairs consecutive), then the centre tap (every row with itself)
+ *    runs as a dense GEMM whose epilogue adds the row's slab rows and writes
+ *    the output. Needs a map built without SMC_BUILD_NO_PAIRS;
  *  - SMC_FWD_MASK_TILES ("Sparse convolution in FP32", "Neighbour masks and
  *    sorted rows"): tiles of mask-sorted rows run the union of their masks'
- *    taps and keep every tap's sum in registers; one kernel, no atomics, no
- *    accumulator in memory. Works on maps built with or without pair lists.
+ *    taps and keep every tap's sum in registers; one kernel, nothing in
+ *    memory but the output. Needs a map built without SMC_BUILD_NO_SORT.
+ * Neither uses atomics: the output is the same on every run.
  * x       device pointer, bf16 [n, c_in] row-major (rows in coordinate order).
  * wpacked device pointer from smc_weight_pack(c_in, c_out).
  * y       device pointer, 16-byte aligned, bf16 [n, c_out] (float [n, c_out] with
  *         SMC_FWD_OUT_F32); every row is written.
  * flags   SMC_FWD_RELU | SMC_FWD_OUT_F32, or 0. Without SMC_FWD_OUT_F32 the output
  *         is the float32 accumulator rounded to bf16 (to nearest, ties to even).
- * The pair-list algorithm's float32 accumulator lives in the handle (grow-only,
- * 4 n c_out bytes); it needs a map built without SMC_BUILD_NO_PAIRS.
- * Needs no host read of the map's pair counts: the GEMM reads them on the
- * device. Refuses (SMC_ERR_STATE) a map whose synchronous build failed or
- * a map that was never built.
+ * The pair-list algorithm's slab lives in the handle (grow-only, 4 c_out bytes
+ * per off-centre pair). The host reads no pair count: the GEMM reads them on
+ * the device, and the slab is sized for 26 pairs per row when the build's
+ * counts have not been read (asynchronous builds) and that bound is under
+ * 4 GiB; otherwise the call waits for the build and sizes it exactly.
+ * Refuses (SMC_ERR_STATE) a map whose synchronous build failed or a map
+ * that was never built.
  */
 int smc_conv_forward(smc_map* map, const uint16_t* x, int c_in, const void* wpacked,
                      int c_out, void* y, unsigned flags, void* stream);
@@ -211,8 +221,8 @@ enum {
     SMC_STAGE_NEIGHBOURS = 1,  /* route-specific neighbour search: table + masks */
     SMC_STAGE_MASK_SORT = 2,   /* radix sort of rows by mask */
     SMC_STAGE_COMPACT = 3,     /* pair count, scan and write */
-    SMC_STAGE_GEMM = 4,        /* GEMM over the pair lists of every tap but the centre */
-    SMC_STAGE_CENTRE = 5,      /* centre-tap GEMM fused with the output write */
+    SMC_STAGE_GEMM = 4,        /* pair lists: GEMM of every tap but the centre; mask tiles: all */
+    SMC_STAGE_CENTRE = 5,      /* pair lists: centre-tap GEMM fused with the slab sum and output */
     SMC_STAGE_COUNT = 6
 };
 

@@ -28,7 +28,9 @@ Readings fixed here where the pages are silent:
   neighbours never cross batches.
 * duplicate coordinates are a caller error (raised here).
 * mask sort: ascending plain mask value, ties by ascending row.
-* pair lists: tap-major, and within a tap in mask-sorted row order.
+* pair lists: tap-major, and within a tap in ascending output row (the
+  order inside a tap does not change the sum; [P1]'s compaction lists each
+  tap's rows in the order it scans them).
 * rounding to bf16: round to nearest, ties to even.
 
 Accumulation is float64 by default (the products of two bf16 values are
@@ -157,24 +159,23 @@ def mask_sort(mask: np.ndarray) -> np.ndarray:
     return np.asarray(order, dtype=np.int32)
 
 
-def compact_pairs(nbr: np.ndarray, mask: np.ndarray, perm: np.ndarray):
+def compact_pairs(nbr: np.ndarray, mask: np.ndarray):
     """Per-tap pair lists holding only the neighbours that exist.
 
     [P1] Design ("Compaction"): only valid (input, output) pairs are listed,
     grouped by tap so that a run of pairs shares one weight slab; the centre
     tap is listed like the others ([P1] commit d4161ef, "The centre tap is
-    compacted along with the rest"). Within a tap, pairs follow the
-    mask-sorted row order.
+    compacted along with the rest"). Within a tap, pairs follow ascending
+    output row.
 
     Returns (pair_in int32 [P], pair_out int32 [P], tap_off int64 [28]); the
     pairs of tap k are [tap_off[k], tap_off[k+1]).
     """
     nbr = np.asarray(nbr)
     mask = np.asarray(mask, dtype=np.uint32)
-    perm = np.asarray(perm, dtype=np.int64)
     ins, outs, off = [], [], [0]
     for k in range(TAPS):
-        rows = perm[((mask[perm] >> np.uint32(k)) & np.uint32(1)) == 1]
+        rows = np.nonzero(((mask >> np.uint32(k)) & np.uint32(1)) == 1)[0]
         ins.append(nbr[rows, k].astype(np.int32))
         outs.append(rows.astype(np.int32))
         off.append(off[-1] + rows.size)
@@ -233,7 +234,7 @@ def subm_conv(coords, x_bits, w_bits, relu: bool = False, acc_dtype=np.float64):
     """
     nbr, mask = build_kernel_map(coords)
     perm = mask_sort(mask)
-    pin, pout, toff = compact_pairs(nbr, mask, perm)
+    pin, pout, toff = compact_pairs(nbr, mask)
     x = bf16_bits_to_f64(x_bits)
     w = bf16_bits_to_f64(w_bits)
     acc = conv_accumulate(x, w, pin, pout, toff, x.shape[0], acc_dtype)
@@ -255,7 +256,7 @@ def stage(coords, x_bits, w_bits_list, acc_dtype=np.float64):
     """
     nbr, mask = build_kernel_map(coords)
     perm = mask_sort(mask)
-    pin, pout, toff = compact_pairs(nbr, mask, perm)
+    pin, pout, toff = compact_pairs(nbr, mask)
     h = bf16_bits_to_f64(x_bits)
     outs = []
     for li, wb in enumerate(w_bits_list):

@@ -28,6 +28,7 @@ SMC_FWD_RELU = 1
 SMC_FWD_OUT_F32 = 2
 SMC_FWD_MASK_TILES = 4
 SMC_BUILD_NO_PAIRS = 2
+SMC_BUILD_NO_SORT = 4
 ALGOS = ("pairs", "mask_tiles")
 
 EXPORTED_SYMBOLS = [
@@ -170,17 +171,21 @@ class KernelMap:
             pass
 
     def build(self, coords, spatial_shape=None, batch_size: int = 0, route: str = "auto",
-              sync: bool = True, pairs: bool = True, stream=None) -> "KernelMap":
+              sync: bool = True, pairs: bool = True, sort: bool = True,
+              stream=None) -> "KernelMap":
         """coords: int32 [N, 4] (b, x, y, z) or [N, 3] (x, y, z) CUDA tensor.
 
-        pairs=False skips the per-tap pair lists (enough for algo="mask_tiles")."""
+        pairs=False skips the per-tap pair lists (algo="pairs" then refuses the
+        map); sort=False skips the mask-sorted row order (algo="mask_tiles"
+        then refuses it)."""
         import torch
         _need(coords, torch.int32, "coords", 2)
         n, ncols = int(coords.shape[0]), int(coords.shape[1])
         shape = None
         if spatial_shape is not None:
             shape = (ctypes.c_int32 * 3)(*[int(v) for v in spatial_shape])
-        flags = (0 if sync else SMC_BUILD_ASYNC) | (0 if pairs else SMC_BUILD_NO_PAIRS)
+        flags = ((0 if sync else SMC_BUILD_ASYNC) | (0 if pairs else SMC_BUILD_NO_PAIRS)
+                 | (0 if sort else SMC_BUILD_NO_SORT))
         self._coords = coords          # keep alive while the stream reads it
         self.n = n
         _check(lib().smc_map_build(self._h, ctypes.c_void_p(coords.data_ptr() if n else 0), n,
@@ -211,13 +216,15 @@ class KernelMap:
                     pairs_padded=inf.pairs_padded, n_tiles=inf.n_tiles,
                     tap_count=list(inf.tap_count), status=inf.status)
 
-    def export(self, pairs: bool = True) -> dict:
-        """Copy nbr, mask, perm, tap offsets (and the pair lists) to numpy (host)."""
+    def export(self, pairs: bool = True, perm: bool = True) -> dict:
+        """Copy nbr, mask, tap offsets (and the mask order, the pair lists) to numpy (host)."""
         import numpy as np
         info = self.info()
         n, p = info["n"], info["pairs"]
         out = dict(nbr=np.empty((n, 27), np.int32), mask=np.empty(n, np.uint32),
-                   perm=np.empty(n, np.int32), tap_off=np.empty(28, np.int64))
+                   tap_off=np.empty(28, np.int64))
+        if perm:
+            out["perm"] = np.empty(n, np.int32)
         if pairs:
             out["pair_in"] = np.empty(p, np.int32)
             out["pair_out"] = np.empty(p, np.int32)
@@ -233,8 +240,9 @@ class KernelMap:
                 algo: str = "pairs", stream=None):
         """x: bf16 [N, C_in] CUDA tensor -> bf16 [N, C_out] (float32 with out_f32).
 
-        algo: "pairs" (per-tap pair lists, scatter-add) or "mask_tiles"
-        (output-stationary tiles of mask-sorted rows)."""
+        algo: "pairs" (per-tap pair lists, partial-product slab summed by the
+        centre-tap GEMM) or "mask_tiles" (output-stationary tiles of
+        mask-sorted rows)."""
         if algo not in ALGOS:
             raise ValueError(f"algo must be one of {ALGOS}")
         import torch

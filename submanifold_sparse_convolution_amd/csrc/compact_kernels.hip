@@ -1,17 +1,23 @@
 // Compaction of the neighbour table into per-tap pair lists.
 //
 // Only existing (input, output) pairs are listed, grouped by tap so that a
-// GEMM tile shares one weight slab, and each tap's run is padded to a
-// multiple of the tile height ("[Kernel] Add submanifold sparse 3D
-// convolution (bf16 implicit GEMM, gfx950)", Design "Compaction"). Within a
-// tap, pairs follow the mask-sorted row order ("Sparse convolution in FP32",
-// "Neighbour masks and sorted rows"). That pull request counts per (tap,
-// tile), scans the small count table and then writes, keeping the totals on
-// the device (commits "move pair compaction from torch onto three fx
-// kernels", "scan the pair counts on the device"). Here the per-tap totals
-// come for free from the mask histogram pass, and the count/scan/write
-// become one kernel: each chunk of sorted rows finds the pairs of earlier
-// chunks by decoupled look-back (same ticket + epoch scheme as the sort).
+// GEMM tile shares one weight slab ("[Kernel] Add submanifold sparse 3D
+// convolution (bf16 implicit GEMM, gfx950)", Design "Compaction"); within a
+// tap the pairs follow ascending output row. That pull request counts per
+// (tap, tile), scans the small count table and then writes, keeping the
+// totals on the device (commits "move pair compaction from torch onto three
+// fx kernels", "scan the pair counts on the device"). Here count, scan and
+// write are one kernel: each chunk of rows finds the pairs of earlier chunks
+// by decoupled look-back (same ticket + epoch scheme as the sort), and every
+// tap owns a fixed run of the pair arrays (cap entries, cap = n rounded up
+// to the tile height), so no chunk needs the other taps' totals first.
+//
+// The same pass numbers the off-centre pairs of every output row
+// consecutively (row order, then tap order): pair_slot[p] is the row of a
+// float32 partial-product slab where the GEMM of the non-centre taps stores
+// the pair's product, and rowbase[i] is the first slab row of output row i.
+// The centre-tap GEMM then sums each row's slab rows in its epilogue: no
+// atomics and no accumulator to clear.
 #include "smc_internal.h"
 
 namespace smc {
@@ -66,8 +72,9 @@ __device__ inline uint32_t lookback8(uint64_t* look, int stride, int d, int64_t 
 }
 
 // One read of the masks: digit histograms of every mask-sort pass, pairs per
-// tap (mask column sums), and -- on the dense route -- the grid cells of the
-// rows put back to empty (the lookups that needed them have finished).
+// tap (mask column sums), and -- on the dense route, when no compaction
+// follows (grid not null) -- the grid cells of the rows put back to empty
+// (the lookups that needed them have finished).
 __global__ __launch_bounds__(kHThreads) void k_mask_hist(const uint32_t* __restrict__ mask,
                                                          int64_t n, int bits, int passes,
                                                          uint32_t* __restrict__ hist,
@@ -120,50 +127,38 @@ __global__ __launch_bounds__(kHThreads) void k_mask_hist(const uint32_t* __restr
     if (threadIdx.x < kTaps && s_tap[threadIdx.x]) atomicAdd(&tap_tot[threadIdx.x], (int32_t)s_tap[threadIdx.x]);
 }
 
-// Rows [bid*kCChunk, +kCChunk) of the mask-sorted order. Wave w owns a
-// contiguous quarter; for each tap the block counts its rows with that bit,
-// finds the count of earlier chunks by look-back, and writes its pairs.
+// Rows [bid*kCChunk, +kCChunk) in row order. Wave w owns a contiguous
+// quarter; for each tap (and for the slab rows, column kTaps) the block
+// counts its rows, finds the count of earlier chunks by look-back, and
+// writes its pairs. The last chunk publishes the totals.
 __global__ __launch_bounds__(kCThreads) void k_compact(
-    const uint32_t* __restrict__ perm, const uint32_t* __restrict__ mask,
-    const int32_t* __restrict__ nbr, int64_t n, const int32_t* __restrict__ tap_tot, int tile_m,
-    MapState* st, int32_t* __restrict__ pair_in, int32_t* __restrict__ pair_out,
-    int32_t* __restrict__ tile_tap, uint64_t* __restrict__ look, uint32_t* ticket,
-    uint32_t epoch, uint32_t* status) {
+    const uint32_t* __restrict__ mask, const int32_t* __restrict__ nbr, int64_t n, int64_t cap,
+    int tile_m, MapState* st, int32_t* __restrict__ pair_in, int32_t* __restrict__ pair_out,
+    int32_t* __restrict__ pair_slot, int32_t* __restrict__ rowbase, uint64_t* __restrict__ look,
+    uint32_t* ticket, uint32_t epoch, uint32_t* status, const int32_t* __restrict__ coords, Geom g,
+    int32_t* __restrict__ grid) {
+    constexpr int kCols = kTaps + 1;
     __shared__ uint32_t s_bid;
-    __shared__ int32_t s_off[kTaps + 1];          // padded tap starts
-    __shared__ int32_t s_tot[kTaps];
-    __shared__ uint32_t s_wc[kCWaves][kTaps];     // per-wave counts, then offsets in the chunk
-    __shared__ uint32_t s_pre[kTaps];             // pairs of this tap in earlier chunks
+    __shared__ uint32_t s_wc[kCWaves][kCols];     // per-wave counts, then offsets in the chunk
+    __shared__ uint32_t s_pre[kCols];             // counts of earlier chunks
+    __shared__ uint32_t s_tot[kCols];             // totals (last chunk only)
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    if (tid == 0) {
-        s_bid = atomicAdd(ticket, 1u);
-        int32_t off = 0;
-        for (int k = 0; k < kTaps; ++k) {
-            int32_t t = tap_tot[k];
-            s_tot[k] = t;
-            s_off[k] = off;
-            off += (t + tile_m - 1) / tile_m * tile_m;
-        }
-        s_off[kTaps] = off;
-    }
+    if (tid == 0) s_bid = atomicAdd(ticket, 1u);
     __syncthreads();
     const uint32_t bid = s_bid;
     const int64_t base = (int64_t)bid * kCChunk + (int64_t)w * (kCChunk / kCWaves);
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
-    uint32_t row[kCItems], m[kCItems];
+    uint32_t m[kCItems], deg[kCItems];
 #pragma unroll
     for (int i = 0; i < kCItems; ++i) {
-        int64_t s = base + i * 64 + lane;
-        row[i] = min(perm[s < n ? s : n - 1], (uint32_t)(n - 1));   // clamp: see the sort
+        const int64_t r = base + i * 64 + lane;
+        const uint32_t mv = mask[r < n ? r : n - 1];
+        m[i] = r < n ? mv : 0u;
     }
 #pragma unroll
-    for (int i = 0; i < kCItems; ++i) {
-        int64_t s = base + i * 64 + lane;
-        const uint32_t mv = mask[row[i]];
-        m[i] = s < n ? mv : 0u;
-    }
-    // per-wave count of each tap (lane k accumulates tap k)
+    for (int i = 0; i < kCItems; ++i) deg[i] = m[i] ? (uint32_t)__popc(m[i] & ~(1u << kCentre)) : 0u;
+    // per-wave count of each tap (lane k accumulates tap k) and of slab rows (lane kTaps)
     uint32_t cnt = 0;
 #pragma unroll
     for (int k = 0; k < kTaps; ++k) {
@@ -172,9 +167,26 @@ __global__ __launch_bounds__(kCThreads) void k_compact(
         for (int i = 0; i < kCItems; ++i) c += (uint32_t)__popcll(__ballot((m[i] >> k) & 1u));
         if (lane == k) cnt = c;
     }
+    // inclusive wave scans of the slab rows per item
+    uint32_t incl[kCItems], item_tot[kCItems];
+#pragma unroll
+    for (int i = 0; i < kCItems; ++i) {
+        uint32_t v = deg[i];
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t t = __shfl_up(v, o, 64);
+            if (lane >= o) v += t;
+        }
+        incl[i] = v;
+        item_tot[i] = __shfl(v, 63, 64);
+    }
+    uint32_t wave_slab = 0;
+#pragma unroll
+    for (int i = 0; i < kCItems; ++i) wave_slab += item_tot[i];
     if (lane < kTaps) s_wc[w][lane] = cnt;
+    if (lane == kTaps) s_wc[w][kTaps] = wave_slab;
     __syncthreads();
-    if (tid < kTaps) {
+    if (tid < kCols) {
         const int k = tid;
         uint32_t run = 0;
 #pragma unroll
@@ -183,18 +195,53 @@ __global__ __launch_bounds__(kCThreads) void k_compact(
             s_wc[v][k] = run;
             run += c;
         }
-        __hip_atomic_store(&look[(int64_t)bid * kTaps + k],
+        __hip_atomic_store(&look[(int64_t)bid * kCols + k],
                            lb_pack(epoch, bid == 0 ? kIncl : kAgg, run), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
         uint32_t prefix = 0;
         if (bid > 0) {
-            prefix = lookback8(look, kTaps, k, (int64_t)bid - 1, epoch, status);
-            __hip_atomic_store(&look[(int64_t)bid * kTaps + k], lb_pack(epoch, kIncl, prefix + run),
+            prefix = lookback8(look, kCols, k, (int64_t)bid - 1, epoch, status);
+            __hip_atomic_store(&look[(int64_t)bid * kCols + k], lb_pack(epoch, kIncl, prefix + run),
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         s_pre[k] = prefix;
+        if (bid == gridDim.x - 1) {
+            // the last chunk: prefix + run is the total of column k
+            const uint32_t tot = prefix + run;
+            s_tot[k] = tot;
+            if (k < kTaps) {
+                st->tap_count[k] = (int32_t)tot;
+                st->tap_off[k] = (int32_t)(k * cap);
+            } else {
+                st->totals[3] = (int32_t)tot;             // slab rows = off-centre pairs
+                st->tap_off[kTaps] = (int32_t)(kTaps * cap);
+            }
+        }
     }
     __syncthreads();
+    if (bid == gridDim.x - 1 && tid == 0) {
+        int32_t p = 0, padded = 0;
+        for (int k = 0; k < kTaps; ++k) {
+            const int32_t c = (int32_t)s_tot[k];
+            p += c;
+            padded += (c + tile_m - 1) / tile_m * tile_m;
+        }
+        st->totals[0] = p;
+        st->totals[1] = padded;
+        st->totals[2] = padded / tile_m;
+    }
+    // first slab row of every row
+    uint32_t rb[kCItems];
+    {
+        uint32_t off = s_pre[kTaps] + s_wc[w][kTaps];
+#pragma unroll
+        for (int i = 0; i < kCItems; ++i) {
+            rb[i] = off + incl[i] - deg[i];
+            off += item_tot[i];
+            const int64_t r = base + i * 64 + lane;
+            if (r < n) rowbase[r] = (int32_t)rb[i];
+        }
+    }
     // write pairs: neighbour ids of 9 taps x 4 rows loaded together, then stored
 #pragma unroll
     for (int k0 = 0; k0 < kTaps; k0 += 9) {
@@ -202,54 +249,48 @@ __global__ __launch_bounds__(kCThreads) void k_compact(
 #pragma unroll
         for (int kk = 0; kk < 9; ++kk)
 #pragma unroll
-            for (int i = 0; i < kCItems; ++i) nv[kk][i] = nbr[(int64_t)row[i] * kTaps + k0 + kk];
+            for (int i = 0; i < kCItems; ++i) {
+                const int64_t r = min(base + i * 64 + lane, n - 1);
+                nv[kk][i] = nbr[r * kTaps + k0 + kk];
+            }
 #pragma unroll
         for (int kk = 0; kk < 9; ++kk) {
             const int k = k0 + kk;
-            const int64_t start = (int64_t)s_off[k] + s_pre[k] + s_wc[w][k];
-            const int64_t lim = (int64_t)s_off[k] + s_tot[k];
+            const int64_t start = (int64_t)k * cap + s_pre[k] + s_wc[w][k];
+            const int64_t lim = (int64_t)k * cap + cap;
+            const uint32_t lower = (1u << k) - 1u;
             uint32_t run = 0;
 #pragma unroll
             for (int i = 0; i < kCItems; ++i) {
-                uint64_t b = __ballot((m[i] >> k) & 1u);
+                const uint64_t b = __ballot((m[i] >> k) & 1u);
                 if ((m[i] >> k) & 1u) {
-                    int64_t pos = start + run + (uint32_t)__popcll(b & below);
+                    const int64_t pos = start + run + (uint32_t)__popcll(b & below);
                     if (pos < lim) {               // false only after a stalled wait
                         pair_in[pos] = nv[kk][i];
-                        pair_out[pos] = (int32_t)row[i];
+                        pair_out[pos] = (int32_t)(base + i * 64 + lane);
+                        pair_slot[pos] = k == kCentre
+                                             ? -1
+                                             : (int32_t)(rb[i] + __popc(m[i] & lower & ~(1u << kCentre)));
                     }
                 }
                 run += (uint32_t)__popcll(b);
             }
         }
     }
-    // pads, totals, tile taps
-    const int32_t padded = s_off[kTaps];
-    const int32_t n_tiles = padded / tile_m;
-    if (bid == 0) {
-        for (int k = 0; k < kTaps; ++k)
-            for (int p = s_off[k] + s_tot[k] + tid; p < s_off[k + 1]; p += kCThreads) {
-                pair_in[p] = -1;
-                pair_out[p] = -1;
-            }
-        if (tid == 0) {
-            int32_t p = 0;
-            for (int k = 0; k < kTaps; ++k) p += s_tot[k];
-            st->totals[0] = p;
-            st->totals[1] = padded;
-            st->totals[2] = n_tiles;
+    // dense route: the grid cells of these rows go back to empty (every lookup has finished)
+    if (grid) {
+#pragma unroll
+        for (int i = 0; i < kCItems; ++i) {
+            const int64_t r = base + i * 64 + lane;
+            if (r >= n) continue;
+            const int32_t* c = coords + r * g.ncols;
+            const int b = g.ncols == 4 ? c[0] : 0;
+            const int32_t* q = c + (g.ncols == 4 ? 1 : 0);
+            const int x = q[0] - g.origin[0], y = q[1] - g.origin[1], z = q[2] - g.origin[2];
+            if ((unsigned)b < (unsigned)g.batch && (unsigned)x < (unsigned)g.ext[0] &&
+                (unsigned)y < (unsigned)g.ext[1] && (unsigned)z < (unsigned)g.ext[2])
+                grid[b * g.sz_b + (int64_t)(x + 1) * g.sz_x + (int64_t)(y + 1) * g.sz_y + (z + 1)] = -1;
         }
-        if (tid < kTaps) {
-            st->tap_count[tid] = s_tot[tid];
-            st->tap_off[tid] = s_off[tid];
-        }
-        if (tid == 0) st->tap_off[kTaps] = padded;
-    }
-    for (int64_t t = (int64_t)bid * kCThreads + tid; t < n_tiles; t += (int64_t)gridDim.x * kCThreads) {
-        const int32_t p = (int32_t)t * tile_m;
-        int k = 0;
-        while (k + 1 < kTaps && s_off[k + 1] <= p) ++k;
-        tile_tap[t] = k;
     }
     if (bid == gridDim.x - 1 && tid == 0) atomicExch(ticket, 0u);
 }
@@ -268,15 +309,18 @@ hipError_t launch_mask_hist(const uint32_t* mask, int64_t n, const SortPlan& pla
 
 int64_t compact_chunks(int64_t n) { return (n + kCChunk - 1) / kCChunk; }
 
-hipError_t launch_compact(const uint32_t* perm, const uint32_t* mask, const int32_t* nbr, int64_t n,
-                          const int32_t* tap_tot, int tile_m, MapState* st, int32_t* pair_in,
-                          int32_t* pair_out, int32_t* tile_tap, SortWork& ws, uint32_t* status,
-                          hipStream_t s) {
+size_t compact_look_bytes(int64_t n) { return (size_t)compact_chunks(n) * (kTaps + 1) * 8; }
+
+hipError_t launch_compact(const uint32_t* mask, const int32_t* nbr, int64_t n, int64_t cap,
+                          int tile_m, MapState* st, int32_t* pair_in, int32_t* pair_out,
+                          int32_t* pair_slot, int32_t* rowbase, SortWork& ws, uint32_t* status,
+                          const int32_t* coords, const Geom& g, int32_t* grid, hipStream_t s) {
     uint32_t epoch = ++ws.epoch & 0x3FFFFFFFu;
     if (epoch == 0) epoch = ++ws.epoch & 0x3FFFFFFFu;
     unsigned blocks = (unsigned)compact_chunks(n);
-    k_compact<<<blocks, kCThreads, 0, s>>>(perm, mask, nbr, n, tap_tot, tile_m, st, pair_in,
-                                           pair_out, tile_tap, ws.look, ws.ticket, epoch, status);
+    k_compact<<<blocks, kCThreads, 0, s>>>(mask, nbr, n, cap, tile_m, st, pair_in, pair_out,
+                                           pair_slot, rowbase, ws.look, ws.ticket, epoch, status,
+                                           coords, g, grid);
     return hipGetLastError();
 }
 

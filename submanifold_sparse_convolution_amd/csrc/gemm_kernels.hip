@@ -3,22 +3,22 @@
 // "[Kernel] Add submanifold sparse 3D convolution (bf16 implicit GEMM,
 // gfx950)", Design "GEMM" and commit d4161ef: mfma_f32_16x16x32_bf16 with
 // float32 accumulation; A is read through the pair list's input rows, the
-// result goes to the output rows through the pair list, nothing per pair is
-// materialised; weights are packed so a wave reads whole cache lines; the
-// loads of a k-step are issued ahead of its MFMAs.
+// result goes to the output rows through the pair list; weights are packed
+// so a wave reads whole cache lines; the loads of a k-step are issued ahead
+// of its MFMAs.
 //
 // Two kernels per layer, split by tap:
-//  * k_gemm_nc: every tap but the centre, tile by tile over the pair list,
-//    float32 atomic adds into a per-map accumulator;
-//  * k_gemm_centre: the centre tap pairs every row with itself, so its
-//    output rows are distinct and in row order: a dense, output-stationary
-//    tile over consecutive rows that also adds the accumulator (only for
-//    rows that have a non-centre neighbour, per their mask), applies the
-//    optional ReLU, rounds to bf16 (to nearest, ties to even), stores the
-//    output and clears the accumulator rows it read.
-// The centre tap is the largest tap by far on sparse scans (every row has
-// it), so most MACs avoid the atomic read-modify-write, and no separate
-// finalize pass or accumulator clear is needed.
+//  * k_gemm_nc: every tap but the centre, tile by tile over the pair lists.
+//    Each pair's product row is stored (float32, plain stores) into its own
+//    row of a partial-product slab, numbered by the compaction so that the
+//    rows of one output row are consecutive;
+//  * k_gemm_centre: the centre tap pairs every row with itself, so it is a
+//    dense, output-stationary GEMM over consecutive rows. Its epilogue adds
+//    the row's slab rows, applies the optional ReLU, rounds to bf16 (to
+//    nearest, ties to even) and stores the output.
+// No atomics: the pull request scatters with float32 atomic adds, which on
+// this GPU (device-scope atomics resolved past the per-die L2s) cost far
+// more than the slab's extra write and read.
 //
 // MFMA operand layout on gfx950 for v_mfma_f32_16x16x32_bf16 (lane l of the
 // 64-lane wave): A holds row (l % 16), k = 8 (l / 16) .. +7; B holds column
@@ -68,12 +68,6 @@ __global__ __launch_bounds__(kBlock) void k_weight_pack(const uint16_t* __restri
     o.z = v[4] | ((uint32_t)v[5] << 16);
     o.w = v[6] | ((uint32_t)v[7] << 16);
     out[t] = o;
-}
-
-__global__ __launch_bounds__(kBlock) void k_fill_f32_zero(float* p, int64_t n) {
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
-         i += (int64_t)gridDim.x * blockDim.x)
-        p[i] = 0.0f;
 }
 
 // Copy n16 16-byte words of packed weights into LDS with 8 loads in flight
@@ -137,34 +131,60 @@ __device__ __forceinline__ void wave_mma(const uint16_t* const (&xrow)[MW], int 
     }
 }
 
-// Non-centre taps: blocks stride over the pair-list tiles other than the
-// centre tap's (tile counts are read on the device). With LDS, the tile's
-// weight slab is staged once for the block's 4 waves.
+// Store NBW float values of one slab or output row (columns col0 ..).
+template <int NBW>
+__device__ __forceinline__ void store_f32(float* __restrict__ dst, int col0, int c_out,
+                                          const float (&v)[NBW]) {
+    if (NBW >= 4 && col0 + NBW <= c_out && (c_out & 3) == 0) {
+#pragma unroll
+        for (int q = 0; q < NBW; q += 4)
+            *reinterpret_cast<float4*>(dst + q) = make_float4(v[q], v[q + 1], v[q + 2], v[q + 3]);
+    } else {
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb)
+            if (col0 + nb < c_out) dst[nb] = v[nb];
+    }
+}
+
+// Non-centre taps: blocks stride over the tiles of the 26 pair lists (tap k
+// holds tap_count[k] pairs from k * cap on; the counts are read on the
+// device). With LDS, the tile's weight slab is staged once for the block's
+// 4 waves.
 template <int NBW, bool LDS, bool VEC>
 __global__ __launch_bounds__(kGemmThreads) void k_gemm_nc(
     const uint16_t* __restrict__ x, int c_in, int steps, const uint4* __restrict__ wp, int n_wt,
-    int c_out, const int32_t* __restrict__ pair_in, const int32_t* __restrict__ pair_out,
-    const int32_t* __restrict__ tile_tap, const MapState* __restrict__ st, int64_t n,
-    float* __restrict__ acc) {
+    int c_out, const int32_t* __restrict__ pair_in, const int32_t* __restrict__ pair_slot,
+    const MapState* __restrict__ st, int64_t cap, int64_t n, float* __restrict__ part) {
     extern __shared__ uint4 s_b[];
+    __shared__ int32_t s_first[kTaps + 1];      // first tile of each tap (centre: none)
+    __shared__ int32_t s_cnt[kTaps];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
-    const int n_tiles = st->totals[2];
-    const int c_lo = st->tap_off[kCentre] / kTileM;
-    const int c_n = st->tap_off[kCentre + 1] / kTileM - c_lo;
-    const int n_nc = n_tiles - c_n;
+    if (threadIdx.x == 0) {
+        int32_t t = 0;
+        for (int k = 0; k < kTaps; ++k) {
+            const int32_t c = k == kCentre ? 0 : st->tap_count[k];
+            s_cnt[k] = c;
+            s_first[k] = t;
+            t += (c + kTileM - 1) / kTileM;
+        }
+        s_first[kTaps] = t;
+    }
+    __syncthreads();
+    const int n_nc = s_first[kTaps];
     const int wt_i = blockIdx.y;
     const int col0 = wt_i * 16 * NBW + r * NBW;
     const int n16 = steps * NBW * 64;
-    const bool full = col0 + NBW <= c_out;
     for (int u = blockIdx.x; u < n_nc; u += gridDim.x) {
-        const int t = u < c_lo ? u : u + c_n;
-        const int tap = min(max(tile_tap[t], 0), kTaps - 1);
-        const int64_t base = (int64_t)t * kTileM + w * 16;
-        int in_row = pair_in[base + r];
-        const int4 po = *reinterpret_cast<const int4*>(pair_out + base + 4 * g);
-        if (in_row >= n) in_row = -1;           // never for a valid map
-        const uint16_t* xrow[1] = {x + (int64_t)(in_row < 0 ? 0 : in_row) * c_in};
+        int tap = 0;
+        while (tap + 1 < kTaps && s_first[tap + 1] <= u) ++tap;
+        const int j0 = (u - s_first[tap]) * kTileM + w * 16;   // this wave's first pair in the tap
+        const int cnt = s_cnt[tap];
+        const int64_t base = (int64_t)tap * cap + j0;
+        const int pi = pair_in[base + r];
+        const int4 ps = *reinterpret_cast<const int4*>(pair_slot + base + 4 * g);
+        const bool a_ok = j0 + r < cnt && pi >= 0 && pi < n;
+        const uint16_t* xrow[1] = {x + (int64_t)(a_ok ? pi : 0) * c_in};
         const uint4* src = wp + ((int64_t)tap * n_wt + wt_i) * n16;
         const uint4* b = src + lane;
         if (LDS) {
@@ -175,32 +195,30 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_nc(
         }
         f32x4 c[1][NBW];
         wave_mma<NBW, 1, VEC>(xrow, c_in, steps, b, lane, c);
-        const int orows[4] = {po.x, po.y, po.z, po.w};
+        if (col0 >= c_out) continue;
+        const int slots[4] = {ps.x, ps.y, ps.z, ps.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int orow = orows[j];
-            if (orow < 0 || orow >= n || col0 >= c_out) continue;
-            float* yrow = acc + (int64_t)orow * c_out + col0;
-            if (full) {
+            if (j0 + 4 * g + j >= cnt || slots[j] < 0) continue;
+            float v[NBW];
 #pragma unroll
-                for (int nb = 0; nb < NBW; ++nb) atomicAdd(yrow + nb, c[0][nb][j]);
-            } else {
-#pragma unroll
-                for (int nb = 0; nb < NBW; ++nb)
-                    if (col0 + nb < c_out) atomicAdd(yrow + nb, c[0][nb][j]);
-            }
+            for (int nb = 0; nb < NBW; ++nb) v[nb] = c[0][nb][j];
+            store_f32<NBW>(part + (int64_t)slots[j] * c_out + col0, col0, c_out, v);
         }
     }
 }
 
 // Centre tap + output. Blocks stride over tiles of 64 MW consecutive rows;
 // wave w takes rows +16 MW w .. +16 MW w + 16 MW - 1. With LDS the centre
-// weight slab is staged once per block.
+// weight slab is staged once per block. A lane's 4 output rows of a
+// fragment are consecutive, so their slab rows form one consecutive run
+// [rowbase[first], rowbase[last] + deg(last)); it is read 4 slab rows at a
+// time and each slab row is added to the output row it belongs to.
 template <int NBW, int MW, bool OUT_F32, bool LDS, bool VEC>
 __global__ __launch_bounds__(kGemmThreads) void k_gemm_centre(
     const uint16_t* __restrict__ x, int c_in, int steps, const uint4* __restrict__ wp, int n_wt,
-    int c_out, const uint32_t* __restrict__ mask, int64_t n, float* __restrict__ acc,
-    void* __restrict__ yv, int relu) {
+    int c_out, const uint32_t* __restrict__ mask, const int32_t* __restrict__ rowbase, int64_t n,
+    const float* __restrict__ part, void* __restrict__ yv, int relu) {
     extern __shared__ uint4 s_b[];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
@@ -214,8 +232,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_centre(
         __syncthreads();
         b = s_b + lane;
     }
-    const bool full = col0 + NBW <= c_out;
-    const bool vec_acc = full && (c_out & 3) == 0 && NBW >= 4;
+    const bool vec_part = col0 + NBW <= c_out && (c_out & 3) == 0 && NBW >= 4;
     const int64_t rows_per_tile = 64 * MW;
     const int64_t n_rt = (n + rows_per_tile - 1) / rows_per_tile;
     for (int64_t rt = blockIdx.x; rt < n_rt; rt += gridDim.x) {
@@ -226,92 +243,76 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_centre(
             const int64_t ir = row0 + m * 16 + r;
             xrow[m] = x + (ir < n ? ir : 0) * c_in;
         }
-        // masks of this lane's output rows, loaded before the MFMAs need them
-        uint32_t rmask[MW][4];
+        // slab runs of this lane's output rows, loaded before the MFMAs need them; rows
+        // past n get empty runs at the end of the last real row's run
+        int32_t rb[MW][4], re[MW];
 #pragma unroll
-        for (int m = 0; m < MW; ++m)
+        for (int m = 0; m < MW; ++m) {
+            int32_t en[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int64_t row = row0 + m * 16 + 4 * g + j;
-                rmask[m][j] = mask[row < n ? row : n - 1];
+                const int64_t rc = row < n ? row : n - 1;
+                rb[m][j] = rowbase[rc];
+                en[j] = rb[m][j] + (row < n ? __popc(mask[rc] & ~(1u << kCentre)) : 0);
             }
+            int32_t e = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (row0 + m * 16 + 4 * g + j < n) e = en[j];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (row0 + m * 16 + 4 * g + j >= n) rb[m][j] = e;
+            re[m] = e;
+        }
         f32x4 c[MW][NBW];
         wave_mma<NBW, MW, VEC>(xrow, c_in, steps, b, lane, c);
 #pragma unroll
         for (int m = 0; m < MW; ++m) {
-            // accumulator rows from the other taps: all loads first, then use
-            float av[4][NBW];
-            bool has[4];
+            float v[4][NBW];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t row = row0 + m * 16 + 4 * g + j;
-                has[j] = row < n && col0 < c_out && rmask[m][j] != (1u << kCentre);
-                const float* arow = acc + (has[j] ? row * c_out + col0 : 0);
-                if (vec_acc) {
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-                    for (int q = 0; q < NBW; q += 4) {
-                        const float4 a4 = *reinterpret_cast<const float4*>(arow + q);
-                        av[j][q] = a4.x;
-                        av[j][q + 1] = a4.y;
-                        av[j][q + 2] = a4.z;
-                        av[j][q + 3] = a4.w;
+                for (int nb = 0; nb < NBW; ++nb) v[j][nb] = c[m][nb][j];
+            // partial products: slab rows [rb[m][0], re[m]), 4 at a time
+            if (col0 < c_out) {
+                for (int s0 = rb[m][0]; s0 < re[m]; s0 += 4) {
+                    float pv[4][NBW];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const float* prow = part + (int64_t)min(s0 + u, re[m] - 1) * c_out + col0;
+                        if (vec_part) {
+#pragma unroll
+                            for (int q = 0; q < NBW; q += 4) {
+                                const float4 p4 = *reinterpret_cast<const float4*>(prow + q);
+                                pv[u][q] = p4.x;
+                                pv[u][q + 1] = p4.y;
+                                pv[u][q + 2] = p4.z;
+                                pv[u][q + 3] = p4.w;
+                            }
+                        } else {
+#pragma unroll
+                            for (int nb = 0; nb < NBW; ++nb) pv[u][nb] = prow[col0 + nb < c_out ? nb : 0];
+                        }
                     }
-                } else {
 #pragma unroll
-                    for (int nb = 0; nb < NBW; ++nb)
-                        av[j][nb] = arow[has[j] && col0 + nb < c_out ? nb : 0];
+                    for (int u = 0; u < 4; ++u) {
+                        const int sl = s0 + u;
+                        if (sl >= re[m]) break;
+                        const int jr = (sl >= rb[m][1]) + (sl >= rb[m][2]) + (sl >= rb[m][3]);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            if (j == jr)
+#pragma unroll
+                                for (int nb = 0; nb < NBW; ++nb) v[j][nb] += pv[u][nb];
+                    }
                 }
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int64_t row = row0 + m * 16 + 4 * g + j;
                 if (row >= n || col0 >= c_out) continue;
-                float v[NBW];
-#pragma unroll
-                for (int nb = 0; nb < NBW; ++nb) v[nb] = c[m][nb][j] + (has[j] ? av[j][nb] : 0.f);
-                if (has[j]) {
-                    float* arow = acc + row * c_out + col0;
-                    if (vec_acc) {
-#pragma unroll
-                        for (int q = 0; q < NBW; q += 4)
-                            *reinterpret_cast<float4*>(arow + q) = make_float4(0.f, 0.f, 0.f, 0.f);
-                    } else {
-#pragma unroll
-                        for (int nb = 0; nb < NBW; ++nb)
-                            if (col0 + nb < c_out) arow[nb] = 0.f;
-                    }
-                }
-                if (OUT_F32) {
-                    float* y = static_cast<float*>(yv) + row * c_out + col0;
-#pragma unroll
-                    for (int nb = 0; nb < NBW; ++nb)
-                        if (col0 + nb < c_out) y[nb] = (relu && v[nb] < 0.f) ? 0.f : v[nb];
-                } else {
-                    uint16_t* y = static_cast<uint16_t*>(yv) + row * c_out + col0;
-                    uint32_t bb[8];
-#pragma unroll
-                    for (int nb = 0; nb < 8; ++nb) {
-                        bb[nb] = nb < NBW ? bf16_rne_bits(v[nb < NBW ? nb : 0]) : 0u;
-                        if (relu && (bb[nb] & 0x8000u)) bb[nb] = 0;
-                    }
-                    if (NBW == 8 && full && (c_out & 7) == 0) {
-                        uint4 o;
-                        o.x = bb[0] | (bb[1] << 16);
-                        o.y = bb[2] | (bb[3] << 16);
-                        o.z = bb[4] | (bb[5] << 16);
-                        o.w = bb[6] | (bb[7] << 16);
-                        *reinterpret_cast<uint4*>(y) = o;
-                    } else if (NBW == 4 && full && (c_out & 3) == 0) {
-                        uint2 o;
-                        o.x = bb[0] | (bb[1] << 16);
-                        o.y = bb[2] | (bb[3] << 16);
-                        *reinterpret_cast<uint2*>(y) = o;
-                    } else {
-#pragma unroll
-                        for (int nb = 0; nb < NBW; ++nb)
-                            if (col0 + nb < c_out) y[nb] = (uint16_t)bb[nb];
-                    }
-                }
+                store_row<NBW, OUT_F32>(yv, row, c_out, col0, v[j], relu);
             }
         }
     }
@@ -334,51 +335,51 @@ bool allow_lds(F* fn, size_t bytes) {
 
 template <int NBW, bool VEC>
 void launch_nc_t(dim3 grid, hipStream_t s, const uint16_t* x, int c_in, int steps,
-                 const uint4* wp, int n_wt, int c_out, const int32_t* pi, const int32_t* po,
-                 const int32_t* tt, const MapState* st, int64_t n, float* acc) {
+                 const uint4* wp, int n_wt, int c_out, const int32_t* pi, const int32_t* ps,
+                 const MapState* st, int64_t cap, int64_t n, float* part) {
     const size_t lds = (size_t)steps * NBW * 1024;
     if (allow_lds(k_gemm_nc<NBW, true, VEC>, lds))
         k_gemm_nc<NBW, true, VEC><<<grid, kGemmThreads, lds, s>>>(x, c_in, steps, wp, n_wt, c_out,
-                                                                  pi, po, tt, st, n, acc);
+                                                                  pi, ps, st, cap, n, part);
     else
         k_gemm_nc<NBW, false, VEC><<<grid, kGemmThreads, 0, s>>>(x, c_in, steps, wp, n_wt, c_out,
-                                                                 pi, po, tt, st, n, acc);
+                                                                 pi, ps, st, cap, n, part);
 }
 
 template <int NBW>
 void launch_nc(dim3 grid, hipStream_t s, const uint16_t* x, int c_in, int steps, const uint4* wp,
-               int n_wt, int c_out, const int32_t* pi, const int32_t* po, const int32_t* tt,
-               const MapState* st, int64_t n, float* acc) {
+               int n_wt, int c_out, const int32_t* pi, const int32_t* ps, const MapState* st,
+               int64_t cap, int64_t n, float* part) {
     if ((c_in & 7) == 0)
-        launch_nc_t<NBW, true>(grid, s, x, c_in, steps, wp, n_wt, c_out, pi, po, tt, st, n, acc);
+        launch_nc_t<NBW, true>(grid, s, x, c_in, steps, wp, n_wt, c_out, pi, ps, st, cap, n, part);
     else
-        launch_nc_t<NBW, false>(grid, s, x, c_in, steps, wp, n_wt, c_out, pi, po, tt, st, n, acc);
+        launch_nc_t<NBW, false>(grid, s, x, c_in, steps, wp, n_wt, c_out, pi, ps, st, cap, n, part);
 }
 
 template <int NBW, int MW, bool OUT_F32, bool VEC>
 void launch_centre_t(dim3 grid, hipStream_t s, const uint16_t* x, int c_in, int steps,
-                     const uint4* wp, int n_wt, int c_out, const uint32_t* mask, int64_t n,
-                     float* acc, void* y, int relu) {
+                     const uint4* wp, int n_wt, int c_out, const uint32_t* mask,
+                     const int32_t* rowbase, int64_t n, const float* part, void* y, int relu) {
     const size_t lds = (size_t)steps * NBW * 1024;
     if (allow_lds(k_gemm_centre<NBW, MW, OUT_F32, true, VEC>, lds))
         k_gemm_centre<NBW, MW, OUT_F32, true, VEC><<<grid, kGemmThreads, lds, s>>>(
-            x, c_in, steps, wp, n_wt, c_out, mask, n, acc, y, relu);
+            x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, relu);
     else
         k_gemm_centre<NBW, MW, OUT_F32, false, VEC><<<grid, kGemmThreads, 0, s>>>(
-            x, c_in, steps, wp, n_wt, c_out, mask, n, acc, y, relu);
+            x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, relu);
 }
 
 template <int NBW>
 void launch_centre(dim3 grid, hipStream_t s, bool out_f32, const uint16_t* x, int c_in, int steps,
-                   const uint4* wp, int n_wt, int c_out, const uint32_t* mask, int64_t n,
-                   float* acc, void* y, int relu) {
+                   const uint4* wp, int n_wt, int c_out, const uint32_t* mask,
+                   const int32_t* rowbase, int64_t n, const float* part, void* y, int relu) {
     const bool vec = (c_in & 7) == 0;
     if (out_f32) {
-        if (vec) launch_centre_t<NBW, 2, true, true>(grid, s, x, c_in, steps, wp, n_wt, c_out, mask, n, acc, y, relu);
-        else launch_centre_t<NBW, 2, true, false>(grid, s, x, c_in, steps, wp, n_wt, c_out, mask, n, acc, y, relu);
+        if (vec) launch_centre_t<NBW, 2, true, true>(grid, s, x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, relu);
+        else launch_centre_t<NBW, 2, true, false>(grid, s, x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, relu);
     } else {
-        if (vec) launch_centre_t<NBW, 2, false, true>(grid, s, x, c_in, steps, wp, n_wt, c_out, mask, n, acc, y, relu);
-        else launch_centre_t<NBW, 2, false, false>(grid, s, x, c_in, steps, wp, n_wt, c_out, mask, n, acc, y, relu);
+        if (vec) launch_centre_t<NBW, 2, false, true>(grid, s, x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, relu);
+        else launch_centre_t<NBW, 2, false, false>(grid, s, x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, relu);
     }
 }
 
@@ -401,39 +402,30 @@ hipError_t launch_weight_pack(const uint16_t* w, int c_in, int c_out, void* out,
     return hipGetLastError();
 }
 
-hipError_t launch_fill_f32(float* p, int64_t n, hipStream_t s) {
-    if (n <= 0) return hipSuccess;
-    int64_t b = (n + kBlock - 1) / kBlock;
-    unsigned blocks = (unsigned)(b > 65536 ? 65536 : b);
-    k_fill_f32_zero<<<blocks, kBlock, 0, s>>>(p, n);
-    return hipGetLastError();
-}
-
 hipError_t launch_gemm_nc(const uint16_t* x, int c_in, const void* wpacked, int c_out,
-                          const int32_t* pair_in, const int32_t* pair_out, const int32_t* tile_tap,
-                          const MapState* st, int64_t n, int64_t max_tiles, int n_cu,
-                          float* acc, hipStream_t s) {
+                          const int32_t* pair_in, const int32_t* pair_slot, const MapState* st,
+                          int64_t cap, int64_t n, int n_cu, float* part, hipStream_t s) {
     const int steps = (c_in + 31) / 32;
     const int nbw = nbw_for(c_out);
     const int n_wt = (c_out + 16 * nbw - 1) / (16 * nbw);
-    int64_t gx = max_tiles;
-    int64_t cap = (int64_t)n_cu * 2;
-    if (gx > cap) gx = cap;
+    int64_t gx = (kTaps - 1) * (cap / kTileM);     // tiles if every tap were full
+    if (gx > (int64_t)n_cu * 2) gx = (int64_t)n_cu * 2;
     if (gx < 1) gx = 1;
     dim3 grid((unsigned)gx, (unsigned)n_wt);
     const uint4* wp = (const uint4*)wpacked;
     switch (nbw) {
-        case 1: launch_nc<1>(grid, s, x, c_in, steps, wp, n_wt, c_out, pair_in, pair_out, tile_tap, st, n, acc); break;
-        case 2: launch_nc<2>(grid, s, x, c_in, steps, wp, n_wt, c_out, pair_in, pair_out, tile_tap, st, n, acc); break;
-        case 4: launch_nc<4>(grid, s, x, c_in, steps, wp, n_wt, c_out, pair_in, pair_out, tile_tap, st, n, acc); break;
-        default: launch_nc<8>(grid, s, x, c_in, steps, wp, n_wt, c_out, pair_in, pair_out, tile_tap, st, n, acc); break;
+        case 1: launch_nc<1>(grid, s, x, c_in, steps, wp, n_wt, c_out, pair_in, pair_slot, st, cap, n, part); break;
+        case 2: launch_nc<2>(grid, s, x, c_in, steps, wp, n_wt, c_out, pair_in, pair_slot, st, cap, n, part); break;
+        case 4: launch_nc<4>(grid, s, x, c_in, steps, wp, n_wt, c_out, pair_in, pair_slot, st, cap, n, part); break;
+        default: launch_nc<8>(grid, s, x, c_in, steps, wp, n_wt, c_out, pair_in, pair_slot, st, cap, n, part); break;
     }
     return hipGetLastError();
 }
 
 hipError_t launch_gemm_centre(const uint16_t* x, int c_in, const void* wpacked, int c_out,
-                              const uint32_t* mask, int64_t n, float* acc, void* y, bool out_f32,
-                              bool relu, int n_cu, hipStream_t s) {
+                              const uint32_t* mask, const int32_t* rowbase, int64_t n,
+                              const float* part, void* y, bool out_f32, bool relu, int n_cu,
+                              hipStream_t s) {
     if (n <= 0) return hipSuccess;
     const int steps = (c_in + 31) / 32;
     const int nbw = nbw_for(c_out);
@@ -444,10 +436,10 @@ hipError_t launch_gemm_centre(const uint16_t* x, int c_in, const void* wpacked, 
     const uint4* wp = (const uint4*)wpacked;
     const int rl = relu ? 1 : 0;
     switch (nbw) {
-        case 1: launch_centre<1>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, mask, n, acc, y, rl); break;
-        case 2: launch_centre<2>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, mask, n, acc, y, rl); break;
-        case 4: launch_centre<4>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, mask, n, acc, y, rl); break;
-        default: launch_centre<8>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, mask, n, acc, y, rl); break;
+        case 1: launch_centre<1>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, rl); break;
+        case 2: launch_centre<2>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, rl); break;
+        case 4: launch_centre<4>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, rl); break;
+        default: launch_centre<8>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, rl); break;
     }
     return hipGetLastError();
 }

@@ -10,7 +10,6 @@ constexpr int kTaps = 27;
 constexpr int kCentre = 13;
 constexpr int kTileM = 64;          // pairs per GEMM tile (4 waves x 16 rows)
 constexpr int kBlock = 256;         // threads per block for the map kernels
-constexpr int kChunk = 256;         // sorted rows per compaction chunk
 
 // bits of the device status word
 enum : uint32_t { kStDuplicate = 1u, kStRange = 2u, kStSortStall = 4u };
@@ -19,9 +18,9 @@ enum : uint32_t { kStDuplicate = 1u, kStRange = 2u, kStSortStall = 4u };
 struct MapState {
     uint32_t status;        // kSt* bits
     int32_t bbox[8];        // min x, y, z, max x, y, z, min b, max b
-    int32_t totals[4];      // pairs, pairs_padded, n_tiles, unused
-    int32_t tap_off[28];    // padded start of each tap's pair run (tap_off[27] = pairs_padded)
-    int32_t tap_count[27];  // unpadded pairs per tap (written by the compaction)
+    int32_t totals[4];      // pairs, pairs padded per tap to the tile, tiles, slab rows
+    int32_t tap_off[28];    // start of each tap's pair run (k * cap; tap_off[27] = 27 cap)
+    int32_t tap_count[27];  // pairs per tap (written by the compaction)
     int32_t tap_tot[27];    // pairs per tap, accumulated by the mask histogram
 };
 
@@ -99,22 +98,26 @@ hipError_t launch_mask_hist(const uint32_t* mask, int64_t n, const SortPlan& pla
                             int32_t* tap_tot, const int32_t* coords, const Geom& g,
                             int32_t* grid, hipStream_t s);
 int64_t compact_chunks(int64_t n);
-hipError_t launch_compact(const uint32_t* perm, const uint32_t* mask, const int32_t* nbr, int64_t n,
-                          const int32_t* tap_tot, int tile_m, MapState* st, int32_t* pair_in,
-                          int32_t* pair_out, int32_t* tile_tap, SortWork& ws, uint32_t* status,
-                          hipStream_t s);
+size_t compact_look_bytes(int64_t n);
+// Pairs of tap k go to [k cap, k cap + tap_count[k]) in ascending output row;
+// pair_slot numbers the off-centre pairs row by row (rowbase[i] = first slab
+// row of output row i). grid (dense route) or null: cells of the rows are
+// reset to -1.
+hipError_t launch_compact(const uint32_t* mask, const int32_t* nbr, int64_t n, int64_t cap,
+                          int tile_m, MapState* st, int32_t* pair_in, int32_t* pair_out,
+                          int32_t* pair_slot, int32_t* rowbase, SortWork& ws, uint32_t* status,
+                          const int32_t* coords, const Geom& g, int32_t* grid, hipStream_t s);
 
 // ---- GEMM (gemm_kernels.hip) ----
 size_t packed_weight_bytes(int c_in, int c_out);
 hipError_t launch_weight_pack(const uint16_t* w, int c_in, int c_out, void* out, hipStream_t s);
-hipError_t launch_fill_f32(float* p, int64_t n, hipStream_t s);
 hipError_t launch_gemm_nc(const uint16_t* x, int c_in, const void* wpacked, int c_out,
-                          const int32_t* pair_in, const int32_t* pair_out, const int32_t* tile_tap,
-                          const MapState* st, int64_t n, int64_t max_tiles, int n_cu,
-                          float* acc, hipStream_t s);
+                          const int32_t* pair_in, const int32_t* pair_slot, const MapState* st,
+                          int64_t cap, int64_t n, int n_cu, float* part, hipStream_t s);
 hipError_t launch_gemm_centre(const uint16_t* x, int c_in, const void* wpacked, int c_out,
-                              const uint32_t* mask, int64_t n, float* acc, void* y, bool out_f32,
-                              bool relu, int n_cu, hipStream_t s);
+                              const uint32_t* mask, const int32_t* rowbase, int64_t n,
+                              const float* part, void* y, bool out_f32, bool relu, int n_cu,
+                              hipStream_t s);
 
 // ---- mask-tile GEMM (masktile_kernels.hip) ----
 hipError_t launch_conv_masktile(const uint16_t* x, int c_in, const void* wpacked, int c_out,

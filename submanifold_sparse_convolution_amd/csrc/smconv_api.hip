@@ -67,6 +67,7 @@ constexpr int64_t kMaxRows = (int64_t)1 << 26;
 constexpr int kMaxChannels = 4096;
 constexpr int kZeroRowBytes = kMaxChannels * 2;                 // keeps 27 n + pads < 2^31
 constexpr int64_t kDenseBudgetBytes = (int64_t)4 << 30;        // auto route: grid <= 4 GiB
+constexpr int64_t kSlabBoundBytes = (int64_t)4 << 30;          // unread counts: bound the slab
 
 int bit_len(int64_t v) {   // bits needed to hold 0..v
     int b = 0;
@@ -105,12 +106,12 @@ struct smc_map {
     bool state_copied = false;        // host_state already holds the last build's record
     DevBuf nbr, mask, mkey0, mkey1, mval0, mval1;
     const uint32_t* perm = nullptr;   // points into mval0 or mval1
-    DevBuf pair_in, pair_out, tile_tap;
-    int64_t pair_cap = 0;
-    DevBuf acc;                       // float32 accumulator, kept all zero between forwards
+    DevBuf pair_in, pair_out, pair_slot, rowbase;
+    int64_t cap = 0;                  // pairs per tap the pair arrays hold (n rounded up to a tile)
+    DevBuf part;                      // float32 partial-product slab of the pair-list forward
     DevBuf zrow;                      // zero row read for absent neighbours (mask-tile GEMM)
     bool has_pairs = false;
-    size_t acc_clean_bytes = 0;
+    bool has_sort = false;
     // stage timers
     bool timing = false;
     std::vector<hipEvent_t> ev_pool;
@@ -274,7 +275,8 @@ int smc_map_destroy(smc_map* m) {
         DevBuf* bufs[] = {&m->state, &m->grid, &m->keys0, &m->keys1, &m->keys2,
                           &m->vals0, &m->vals1, &m->hist, &m->look, &m->ticket, &m->nbr,
                           &m->mask, &m->mkey0, &m->mkey1, &m->mval0, &m->mval1,
-                          &m->pair_in, &m->pair_out, &m->tile_tap, &m->acc, &m->zrow};
+                          &m->pair_in, &m->pair_out, &m->pair_slot, &m->rowbase, &m->part,
+                          &m->zrow};
         for (DevBuf* b : bufs) b->release();
         for (auto& v : m->ev_open)
             for (auto& pr : v) {
@@ -388,24 +390,29 @@ int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     m->n = n;
 
     // ---- buffers ----
+    const bool want_pairs = !(flags & SMC_BUILD_NO_PAIRS);
+    const bool want_sort = !(flags & SMC_BUILD_NO_SORT);
     const int64_t nn = n > 0 ? n : 1;
-    const int64_t pair_cap = 27 * nn + 27 * (int64_t)kTileM;
+    const int64_t cap = (nn + kTileM - 1) / kTileM * kTileM;
     size_t look_bytes = sort_look_bytes(nn);
-    size_t look_c = (size_t)compact_chunks(nn) * kTaps * 8;
+    const size_t look_c = compact_look_bytes(nn);
     if (look_c > look_bytes) look_bytes = look_c;
     const size_t look_before = m->look.bytes;
     if ((rc = m->nbr.ensure((size_t)nn * kTaps * 4)) || (rc = m->mask.ensure((size_t)nn * 4)) ||
         (rc = m->mkey0.ensure((size_t)nn * 4)) || (rc = m->mkey1.ensure((size_t)nn * 4)) ||
         (rc = m->mval0.ensure((size_t)nn * 4)) || (rc = m->mval1.ensure((size_t)nn * 4)) ||
-        (rc = m->look.ensure(look_bytes)) ||
-        (rc = m->pair_in.ensure((size_t)pair_cap * 4)) ||
-        (rc = m->pair_out.ensure((size_t)pair_cap * 4)) ||
-        (rc = m->tile_tap.ensure((size_t)(pair_cap / kTileM + 1) * 4)))
+        (rc = m->look.ensure(look_bytes)))
+        return rc;
+    if (want_pairs &&
+        ((rc = m->pair_in.ensure((size_t)kTaps * cap * 4)) ||
+         (rc = m->pair_out.ensure((size_t)kTaps * cap * 4)) ||
+         (rc = m->pair_slot.ensure((size_t)kTaps * cap * 4)) ||
+         (rc = m->rowbase.ensure((size_t)nn * 4))))
         return rc;
     if (m->look.bytes != look_before || look_before == 0)   // new table: epoch 0 everywhere
         SMC_HIP(launch_fill_i32(m->look.as<int32_t>(), (int64_t)(m->look.bytes / 4), 0, s));
     m->ws.look = m->look.as<uint64_t>();
-    m->pair_cap = pair_cap;
+    m->cap = cap;
     uint32_t* status = &st->status;
     uint32_t* hist_mask = m->hist.as<uint32_t>();
     uint32_t* hist_key = hist_mask + kHistMaskInts;
@@ -445,25 +452,35 @@ int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
             SMC_HIP(launch_sorted_lookup(skeys, svals, n, g, m->wide, nbr, mask, st, s));
         }
         t_nb.finish();
-        // rows ordered by (mask, row): histograms (+ per-tap totals, grid cleanup), then passes
-        StageTimer t_ms(m, SMC_STAGE_MASK_SORT, s);
-        const SortPlan mp = sort_plan(kMaskBits);
-        SMC_HIP(launch_mask_hist(mask, n, mp, hist_mask, st->tap_tot, coords, g, grid, s));
-        const uint32_t* sorted_masks;
-        SMC_HIP(radix_sort_u32(mask, nullptr, n, mp, hist_mask, m->mkey0.as<uint32_t>(),
-                               m->mkey1.as<uint32_t>(), m->mval0.as<uint32_t>(),
-                               m->mval1.as<uint32_t>(), m->ws, status, &sorted_masks, &m->perm,
-                               s));
-        t_ms.finish();
-        if (!(flags & SMC_BUILD_NO_PAIRS)) {
+        // The grid cells go back to empty in the last pass over the rows: the compaction
+        // when pair lists are built, otherwise the mask histogram (which then also gives
+        // the per-tap counts).
+        if (want_sort || !want_pairs) {
+            // rows ordered by (mask, row): histograms (+ per-tap totals), then passes
+            StageTimer t_ms(m, SMC_STAGE_MASK_SORT, s);
+            SortPlan mp = sort_plan(kMaskBits);
+            if (!want_sort) mp.passes = 0;
+            SMC_HIP(launch_mask_hist(mask, n, mp, hist_mask, st->tap_tot, coords, g,
+                                     want_pairs ? nullptr : grid, s));
+            if (want_sort) {
+                const uint32_t* sorted_masks;
+                SMC_HIP(radix_sort_u32(mask, nullptr, n, mp, hist_mask, m->mkey0.as<uint32_t>(),
+                                       m->mkey1.as<uint32_t>(), m->mval0.as<uint32_t>(),
+                                       m->mval1.as<uint32_t>(), m->ws, status, &sorted_masks,
+                                       &m->perm, s));
+            }
+            t_ms.finish();
+        }
+        if (want_pairs) {
             StageTimer t_cp(m, SMC_STAGE_COMPACT, s);
-            SMC_HIP(launch_compact(m->perm, mask, nbr, n, st->tap_tot, kTileM, st,
-                                   m->pair_in.as<int32_t>(), m->pair_out.as<int32_t>(),
-                                   m->tile_tap.as<int32_t>(), m->ws, status, s));
+            SMC_HIP(launch_compact(mask, nbr, n, cap, kTileM, st, m->pair_in.as<int32_t>(),
+                                   m->pair_out.as<int32_t>(), m->pair_slot.as<int32_t>(),
+                                   m->rowbase.as<int32_t>(), m->ws, status, coords, g, grid, s));
             t_cp.finish();
         }
     }
-    m->has_pairs = !(flags & SMC_BUILD_NO_PAIRS);
+    m->has_pairs = want_pairs;
+    m->has_sort = want_sort;
     t_map.finish();
     const bool async = (flags & SMC_BUILD_ASYNC) != 0;
     if (!async)
@@ -501,7 +518,9 @@ int smc_map_info(smc_map* m, smc_map_info_t* info) {
     info->tile_m = kTileM;
     info->grid_cells = m->grid_cells;
     const MapState& hs = *m->host_state;
-    if (m->has_pairs) {
+    if (m->n == 0) {
+        // nothing was counted
+    } else if (m->has_pairs) {
         info->pairs = hs.totals[0];
         info->pairs_padded = hs.totals[1];
         info->n_tiles = hs.totals[2];
@@ -522,6 +541,8 @@ int smc_map_export(smc_map* m, int32_t* nbr, uint32_t* mask, int32_t* perm, int3
     if (!m->built) return fail(SMC_ERR_STATE, "map was never built");
     if ((pair_in || pair_out) && !m->has_pairs)
         return fail(SMC_ERR_STATE, "map was built without pair lists (SMC_BUILD_NO_PAIRS)");
+    if (perm && !m->has_sort)
+        return fail(SMC_ERR_STATE, "map was built without the mask order (SMC_BUILD_NO_SORT)");
     SMC_HIP(hipSetDevice(m->device));
     (void)wait_build(m);
     SMC_HIP(hipDeviceSynchronize());
@@ -535,20 +556,22 @@ int smc_map_export(smc_map* m, int32_t* nbr, uint32_t* mask, int32_t* perm, int3
     if (tap_off) {
         tap_off[0] = 0;
         for (int k = 0; k < kTaps; ++k)
-            tap_off[k + 1] = tap_off[k] + (m->has_pairs ? hs.tap_count[k] : hs.tap_tot[k]);
+            tap_off[k + 1] = tap_off[k] + (n == 0 ? 0 : m->has_pairs ? hs.tap_count[k] : hs.tap_tot[k]);
     }
     if ((pair_in || pair_out) && n > 0) {
-        const int64_t padded = hs.totals[1];
-        std::vector<int32_t> tmp((size_t)std::max<int64_t>(padded, 1));
+        // tap k's run starts at k * cap on the device
         for (int which = 0; which < 2; ++which) {
             int32_t* dst = which == 0 ? pair_in : pair_out;
             if (!dst) continue;
-            const DevBuf& src = which == 0 ? m->pair_in : m->pair_out;
-            SMC_HIP(hipMemcpy(tmp.data(), src.p, (size_t)padded * 4, hipMemcpyDeviceToHost));
+            const int32_t* src = (which == 0 ? m->pair_in : m->pair_out).as<int32_t>();
             int64_t o = 0;
             for (int k = 0; k < kTaps; ++k) {
-                memcpy(dst + o, tmp.data() + hs.tap_off[k], (size_t)hs.tap_count[k] * 4);
-                o += hs.tap_count[k];
+                const int64_t c = hs.tap_count[k];
+                if (c > m->cap) return fail(SMC_ERR_STATE, "tap %d holds %lld pairs", k, (long long)c);
+                if (c > 0)
+                    SMC_HIP(hipMemcpy(dst + o, src + (int64_t)k * m->cap, (size_t)c * 4,
+                                      hipMemcpyDeviceToHost));
+                o += c;
             }
         }
     }
@@ -580,6 +603,8 @@ int smc_conv_forward(smc_map* m, const uint16_t* x, int c_in, const void* wpacke
     const bool mask_tiles = (flags & SMC_FWD_MASK_TILES) != 0;
     if (!mask_tiles && !m->has_pairs)
         return fail(SMC_ERR_STATE, "map was built without pair lists (SMC_BUILD_NO_PAIRS)");
+    if (mask_tiles && !m->has_sort)
+        return fail(SMC_ERR_STATE, "map was built without the mask order (SMC_BUILD_NO_SORT)");
     if (m->n == 0) return SMC_OK;
     if (!x || !wpacked || !y) return fail(SMC_ERR_ARG, "NULL pointer");
     if (((uintptr_t)wpacked & 15) != 0) return fail(SMC_ERR_ARG, "packed weights not 16-byte aligned");
@@ -599,24 +624,26 @@ int smc_conv_forward(smc_map* m, const uint16_t* x, int c_in, const void* wpacke
         t_mt.finish();
         return SMC_OK;
     }
-    const size_t acc_bytes = (size_t)m->n * c_out * 4;
-    int rc = m->acc.ensure(acc_bytes);
-    if (rc) return rc;
-    if (m->acc_clean_bytes < m->acc.bytes) {
-        SMC_HIP(launch_fill_f32(m->acc.as<float>(), (int64_t)(m->acc.bytes / 4), s));
-        m->acc_clean_bytes = m->acc.bytes;
+    // slab: 4 c_out bytes per off-centre pair; without the build's counts, 26 pairs a row
+    double slab = (double)(kTaps - 1) * m->n * c_out * 4.0;
+    if (m->pending && slab > (double)kSlabBoundBytes) {
+        int rc = wait_build(m);
+        if (rc) return rc;
     }
-    const int64_t max_tiles = m->pair_cap / kTileM;
+    if (!m->pending) slab = (double)m->host_state->totals[3] * c_out * 4.0;
+    if (slab > (double)((size_t)1 << 46)) return fail(SMC_ERR_ALLOC, "slab of %.3g bytes", slab);
+    int rc = m->part.ensure(slab > 256.0 ? (size_t)slab : 256);
+    if (rc) return rc;
     StageTimer t_g(m, SMC_STAGE_GEMM, s);
     SMC_HIP(launch_gemm_nc(x, c_in, wpacked, c_out, m->pair_in.as<int32_t>(),
-                           m->pair_out.as<int32_t>(), m->tile_tap.as<int32_t>(),
-                           m->state.as<MapState>(), m->n, max_tiles, m->n_cu,
-                           m->acc.as<float>(), s));
+                           m->pair_slot.as<int32_t>(), m->state.as<MapState>(), m->cap, m->n,
+                           m->n_cu, m->part.as<float>(), s));
     t_g.finish();
     StageTimer t_f(m, SMC_STAGE_CENTRE, s);
-    SMC_HIP(launch_gemm_centre(x, c_in, wpacked, c_out, m->mask.as<uint32_t>(), m->n,
-                               m->acc.as<float>(), y, (flags & SMC_FWD_OUT_F32) != 0,
-                               (flags & SMC_FWD_RELU) != 0, m->n_cu, s));
+    SMC_HIP(launch_gemm_centre(x, c_in, wpacked, c_out, m->mask.as<uint32_t>(),
+                               m->rowbase.as<int32_t>(), m->n, m->part.as<float>(), y,
+                               (flags & SMC_FWD_OUT_F32) != 0, (flags & SMC_FWD_RELU) != 0,
+                               m->n_cu, s));
     t_f.finish();
     return SMC_OK;
 }

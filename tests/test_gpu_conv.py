@@ -4,9 +4,8 @@ bf16 output: |y - bf16(ref)| <= 2e-2 (1 + |ref|) elementwise, and inside the
 rigorous float32-summation + bf16-rounding bound; float32 accumulator:
 within 1e-3 (1 + |ref|) elementwise, 1e-3 in relative L2, and inside the
 float32 summation bound. Integer-valued and one-hot inputs are exact in any
-summation order, so there the comparison is bit-exact. (The GPU adds the
-non-centre taps with float atomics, so random-valued results may differ in
-the last bits from run to run; no test compares two such runs bit for bit.)
+summation order, so there the comparison is bit-exact. Neither algorithm
+uses atomics, so two runs of one layer are bit-identical.
 """
 import numpy as np
 import pytest
@@ -40,7 +39,7 @@ ALGOS = ["pairs", "mask_tiles"]
 def run_gpu(coords, xb, wb, spatial_shape=None, route="auto", relu=False, out_f32=False,
             algo="pairs"):
     m = smc.KernelMap().build(to_dev_i32(coords), spatial_shape=spatial_shape, route=route,
-                              pairs=(algo == "pairs"))
+                              pairs=(algo == "pairs"), sort=(algo == "mask_tiles"))
     wp = smc.pack_weights(to_dev_bf16(wb))
     y = m.forward(to_dev_bf16(xb), wp, relu=relu, out_f32=out_f32, algo=algo)
     out = y.cpu().numpy() if out_f32 else bf16_bits_of(y)
@@ -149,8 +148,9 @@ def test_full_cube_and_single_voxel(algo):
         check_bf16_output(run_gpu(coords, xb, wb, algo=algo), ref, f"n={n}")
 
 
-def test_layers_share_one_map_and_accumulator_resets():
-    """Several forwards on one map: each equals a fresh single-layer run."""
+def test_layers_share_one_map():
+    """Several forwards on one map (the slab grows with c_out): each equals a fresh
+    single-layer run."""
     w, coords = config("tiny")
     m = smc.KernelMap().build(to_dev_i32(coords), spatial_shape=w.grid)
     om = oracle_map("tiny")
@@ -169,7 +169,8 @@ def test_stage_six_layers(algo):
     w, coords = config("stage")
     c = w.channels
     om = oracle_map("stage")
-    m = smc.KernelMap().build(to_dev_i32(coords), spatial_shape=w.grid, pairs=(algo == "pairs"))
+    m = smc.KernelMap().build(to_dev_i32(coords), spatial_shape=w.grid, pairs=(algo == "pairs"),
+                              sort=(algo == "mask_tiles"))
     hb = synth.features(w.n, c, w.seed)
     h_dev = to_dev_bf16(hb)
     ref_h = so.bf16_bits_to_f64(hb)
@@ -209,3 +210,40 @@ def test_both_algorithms_agree_and_map_without_pairs():
     with pytest.raises(smc.SmconvError):
         m.forward(to_dev_bf16(xi), smc.pack_weights(to_dev_bf16(wi)), algo="pairs")
     m.close()
+    # a map without the mask order: pair lists exact, perm and mask tiles refused
+    m = smc.KernelMap().build(to_dev_i32(coords), spatial_shape=w.grid, sort=False)
+    ex = m.export(pairs=True, perm=False)
+    for key in ("nbr", "mask", "pair_in", "pair_out", "tap_off"):
+        assert np.array_equal(np.asarray(ex[key], np.int64), np.asarray(om[key], np.int64)), key
+    with pytest.raises(smc.SmconvError):
+        m.export(pairs=False, perm=True)
+    with pytest.raises(smc.SmconvError):
+        m.forward(to_dev_bf16(xi), smc.pack_weights(to_dev_bf16(wi)), algo="mask_tiles")
+    m.close()
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_async_build_then_forward(algo):
+    """Forward enqueued right behind an asynchronous build (no host read of the counts)."""
+    w, coords = config("lidar")
+    xb = synth.features(w.n, w.channels, w.seed)
+    wb = synth.weights(w.channels, w.channels, w.seed)
+    m = smc.KernelMap().build(to_dev_i32(coords), spatial_shape=w.grid, batch_size=1, sync=False,
+                              pairs=(algo == "pairs"), sort=(algo == "mask_tiles"))
+    y = m.forward(to_dev_bf16(xb), smc.pack_weights(to_dev_bf16(wb)), algo=algo)
+    m.sync()
+    om = oracle_map("lidar")
+    check_bf16_output(bf16_bits_of(y), oracle_acc(om, xb, wb), "async lidar",
+                      abs_ref=oracle_abs(om, xb, wb), n_terms=27 * w.channels)
+    m.close()
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_repeat_runs_bit_identical(algo):
+    """No atomics: the same layer twice gives the same bits (random values, deep)."""
+    w, coords = config("deep")
+    xb = synth.features(w.n, w.channels, w.seed)
+    wb = synth.weights(w.channels, w.channels, w.seed)
+    a = run_gpu(coords, xb, wb, spatial_shape=w.grid, algo=algo, out_f32=True)
+    b = run_gpu(coords, xb, wb, spatial_shape=w.grid, algo=algo, out_f32=True)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))

@@ -114,13 +114,19 @@ def test_empty_map():
     assert tuple(y.shape) == (0, 16)
 
 
-def test_rebuild_reuses_handle_and_keeps_grid_clean():
-    """One handle, several builds of different sets: each must match."""
+@pytest.mark.parametrize("pairs,sort", [(True, True), (True, False), (False, True), (False, False)])
+def test_rebuild_reuses_handle_and_keeps_grid_clean(pairs, sort):
+    """One handle, several builds of different sets: each must match. Whichever
+    pass ends the build (compaction, mask histogram) must leave the dense grid
+    empty for the next build."""
     m = smc.KernelMap()
     for seed in (1, 2, 3):
         coords = synth.ground_box_coords(3000, (200, 200, 12), seed=seed, n_boxes=20)
-        m.build(to_dev_i32(coords), spatial_shape=(200, 200, 12))
-        assert_map_equal(m.export(), oracle_map_of(coords), f"rebuild {seed}")
+        print(f"rebuild seed {seed} pairs={pairs} sort={sort}", flush=True)
+        m.build(to_dev_i32(coords), spatial_shape=(200, 200, 12), pairs=pairs, sort=sort)
+        got = m.export(pairs=pairs, perm=sort)
+        assert_map_equal(got, oracle_map_of(coords), f"rebuild {seed}")
+        assert m.info()["pairs"] == int(oracle_map_of(coords)["tap_off"][-1])
     m.close()
 
 

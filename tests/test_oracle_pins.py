@@ -86,8 +86,7 @@ def check_map_vs_bruteforce(coords):
 def check_full_box(a, b, c):
     coords = synth.box_coords(a, b, c, origin=(3, 5, 7), seed=a * 100 + b * 10 + c)
     nbr, mask = so.build_kernel_map(coords)
-    perm = so.mask_sort(mask)
-    _, _, toff = so.compact_pairs(nbr, mask, perm)
+    _, _, toff = so.compact_pairs(nbr, mask)
     counts = np.diff(toff)
     for k, (dx, dy, dz) in enumerate(np.ndindex(3, 3, 3)):
         want = max(a - abs(dx - 1), 0) * max(b - abs(dy - 1), 0) * max(c - abs(dz - 1), 0)
@@ -108,15 +107,13 @@ def check_pairs(coords):
     nbr, mask = so.build_kernel_map(coords)
     perm = so.mask_sort(mask)
     check_perm(mask, perm)
-    pin, pout, toff = so.compact_pairs(nbr, mask, perm)
+    pin, pout, toff = so.compact_pairs(nbr, mask)
     got = set()
-    pos = np.empty(len(perm), np.int64)
-    pos[perm] = np.arange(len(perm))
     for k in range(27):
         a, b = toff[k], toff[k + 1]
         for i, o in zip(pin[a:b].tolist(), pout[a:b].tolist()):
             got.add((k, i, o))
-        assert (np.diff(pos[pout[a:b]]) > 0).all(), f"tap {k} not in mask-sorted order"
+        assert (np.diff(pout[a:b].astype(np.int64)) > 0).all(), f"tap {k} not in row order"
     assert got == brute_force_triples(coords), "pair lists differ from brute force"
     bits = ((mask[:, None] >> np.arange(27, dtype=np.uint32)) & 1).sum(0)
     assert (np.diff(toff) == bits).all(), "per-tap counts != mask column sums"
@@ -270,8 +267,7 @@ def test_symmetry_and_centre():
         j = nbr[:, k]
         i = np.nonzero(j >= 0)[0]
         assert (nbr[j[i], 26 - k] == i).all()
-    perm = so.mask_sort(mask)
-    _, _, toff = so.compact_pairs(nbr, mask, perm)
+    _, _, toff = so.compact_pairs(nbr, mask)
     c = np.diff(toff)
     assert (c == c[::-1]).all()
 
@@ -296,11 +292,11 @@ def test_pairs_vs_bruteforce(seed):
 
 def test_pairs_empty_and_single():
     nbr, mask = so.build_kernel_map(np.zeros((0, 4), np.int32))
-    perm = so.mask_sort(mask)
-    pin, pout, toff = so.compact_pairs(nbr, mask, perm)
+    assert so.mask_sort(mask).size == 0
+    pin, pout, toff = so.compact_pairs(nbr, mask)
     assert pin.size == 0 and toff.tolist() == [0] * 28
     nbr, mask = so.build_kernel_map(np.array([[0, 5, 5, 5]], np.int32))
-    pin, pout, toff = so.compact_pairs(nbr, mask, so.mask_sort(mask))
+    pin, pout, toff = so.compact_pairs(nbr, mask)
     assert pin.tolist() == [0] and pout.tolist() == [0] and toff[13] == 0 and toff[14] == 1
 
 
@@ -417,8 +413,8 @@ def test_planted_transposed_weights(monkeypatch):
 def test_planted_dropped_centre_tap(monkeypatch):
     orig = so.compact_pairs
 
-    def broken(nbr, mask, perm):
-        return orig(nbr, np.asarray(mask) & np.uint32(~(1 << 13) & 0xFFFFFFFF), perm)
+    def broken(nbr, mask):
+        return orig(nbr, np.asarray(mask) & np.uint32(~(1 << 13) & 0xFFFFFFFF))
     monkeypatch.setattr(so, "compact_pairs", broken)
     assert _fails(check_full_box, 3, 3, 3)
     assert _fails(check_hand_examples)
@@ -427,8 +423,8 @@ def test_planted_dropped_centre_tap(monkeypatch):
 def test_planted_dropped_pair(monkeypatch):
     orig = so.compact_pairs
 
-    def broken(nbr, mask, perm):
-        pin, pout, toff = orig(nbr, mask, perm)
+    def broken(nbr, mask):
+        pin, pout, toff = orig(nbr, mask)
         keep = np.ones(pin.size, bool)
         keep[int(toff[13])] = False
         toff = toff.copy()
