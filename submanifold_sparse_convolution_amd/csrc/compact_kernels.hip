@@ -28,8 +28,10 @@ constexpr int kHItems = 4;
 constexpr int kHTile = kHThreads * kHItems;       // rows per histogram block
 constexpr int kCThreads = 256;
 constexpr int kCWaves = kCThreads / 64;
-constexpr int kCItems = 4;
-constexpr int kCChunk = kCThreads * kCItems;      // sorted rows per compaction block
+constexpr int kCItems = 2;
+constexpr int kCChunk = kCThreads * kCItems;      // rows per compaction block
+constexpr int kCNbrVec = kCChunk * kTaps / 4;     // 16-byte words of the chunk's neighbour rows
+constexpr int kCNbrPer = (kCNbrVec + kCThreads - 1) / kCThreads;
 constexpr uint32_t kSpinLimit = 1u << 22;
 constexpr uint64_t kAgg = 1, kIncl = 2;
 
@@ -130,7 +132,9 @@ __global__ __launch_bounds__(kHThreads) void k_mask_hist(const uint32_t* __restr
 // Rows [bid*kCChunk, +kCChunk) in row order. Wave w owns a contiguous
 // quarter; for each tap (and for the slab rows, column kTaps) the block
 // counts its rows, finds the count of earlier chunks by look-back, and
-// writes its pairs. The last chunk publishes the totals.
+// writes its pairs. The chunk's neighbour rows (contiguous in the table) are
+// read once, coalesced, into LDS at the start, so the pair writes read LDS
+// only. The last chunk publishes the totals.
 __global__ __launch_bounds__(kCThreads) void k_compact(
     const uint32_t* __restrict__ mask, const int32_t* __restrict__ nbr, int64_t n, int64_t cap,
     int tile_m, MapState* st, int32_t* __restrict__ pair_in, int32_t* __restrict__ pair_out,
@@ -142,19 +146,42 @@ __global__ __launch_bounds__(kCThreads) void k_compact(
     __shared__ uint32_t s_wc[kCWaves][kCols];     // per-wave counts, then offsets in the chunk
     __shared__ uint32_t s_pre[kCols];             // counts of earlier chunks
     __shared__ uint32_t s_tot[kCols];             // totals (last chunk only)
+    __shared__ int4 s_nb4[kCNbrVec];              // the chunk's neighbour rows [kCChunk][kTaps]
+    const int32_t* s_nb = reinterpret_cast<const int32_t*>(s_nb4);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     if (tid == 0) s_bid = atomicAdd(ticket, 1u);
     __syncthreads();
     const uint32_t bid = s_bid;
-    const int64_t base = (int64_t)bid * kCChunk + (int64_t)w * (kCChunk / kCWaves);
+    const int64_t base0 = (int64_t)bid * kCChunk;
+    const int64_t base = base0 + (int64_t)w * (kCChunk / kCWaves);
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
+    // loads: masks, neighbour rows (whole 16-byte words; the table is padded so the last
+    // word of the last row is readable), coordinates for the grid cleanup
     uint32_t m[kCItems], deg[kCItems];
 #pragma unroll
     for (int i = 0; i < kCItems; ++i) {
         const int64_t r = base + i * 64 + lane;
         const uint32_t mv = mask[r < n ? r : n - 1];
         m[i] = r < n ? mv : 0u;
+    }
+    int4 nv4[kCNbrPer];
+    {
+        const int4* src = reinterpret_cast<const int4*>(nbr + base0 * kTaps);
+        const int64_t q_last = (n * kTaps + 3) / 4 - 1 - base0 * kTaps / 4;   // last readable word
+#pragma unroll
+        for (int j = 0; j < kCNbrPer; ++j) {
+            const int64_t q = tid + j * kCThreads;
+            nv4[j] = src[q < q_last ? q : q_last];
+        }
+    }
+    int4 cq[kCItems];                             // (b, x, y, z) of the rows
+    if (grid) {
+#pragma unroll
+        for (int i = 0; i < kCItems; ++i) {
+            const int32_t* c = coords + min(base + i * 64 + lane, n - 1) * g.ncols;
+            cq[i] = g.ncols == 4 ? make_int4(c[0], c[1], c[2], c[3]) : make_int4(0, c[0], c[1], c[2]);
+        }
     }
 #pragma unroll
     for (int i = 0; i < kCItems; ++i) deg[i] = m[i] ? (uint32_t)__popc(m[i] & ~(1u << kCentre)) : 0u;
@@ -185,6 +212,11 @@ __global__ __launch_bounds__(kCThreads) void k_compact(
     for (int i = 0; i < kCItems; ++i) wave_slab += item_tot[i];
     if (lane < kTaps) s_wc[w][lane] = cnt;
     if (lane == kTaps) s_wc[w][kTaps] = wave_slab;
+#pragma unroll
+    for (int j = 0; j < kCNbrPer; ++j) {
+        const int q = tid + j * kCThreads;
+        if (q < kCNbrVec) s_nb4[q] = nv4[j];
+    }
     __syncthreads();
     if (tid < kCols) {
         const int k = tid;
@@ -242,39 +274,28 @@ __global__ __launch_bounds__(kCThreads) void k_compact(
             if (r < n) rowbase[r] = (int32_t)rb[i];
         }
     }
-    // write pairs: neighbour ids of 9 taps x 4 rows loaded together, then stored
+    // pairs, tap by tap (the centre's input row is the row itself)
 #pragma unroll
-    for (int k0 = 0; k0 < kTaps; k0 += 9) {
-        int32_t nv[9][kCItems];
+    for (int k = 0; k < kTaps; ++k) {
+        const int64_t start = (int64_t)k * cap + s_pre[k] + s_wc[w][k];
+        const int64_t lim = (int64_t)k * cap + cap;
+        const uint32_t lower = (1u << k) - 1u;
+        uint32_t run = 0;
 #pragma unroll
-        for (int kk = 0; kk < 9; ++kk)
-#pragma unroll
-            for (int i = 0; i < kCItems; ++i) {
-                const int64_t r = min(base + i * 64 + lane, n - 1);
-                nv[kk][i] = nbr[r * kTaps + k0 + kk];
-            }
-#pragma unroll
-        for (int kk = 0; kk < 9; ++kk) {
-            const int k = k0 + kk;
-            const int64_t start = (int64_t)k * cap + s_pre[k] + s_wc[w][k];
-            const int64_t lim = (int64_t)k * cap + cap;
-            const uint32_t lower = (1u << k) - 1u;
-            uint32_t run = 0;
-#pragma unroll
-            for (int i = 0; i < kCItems; ++i) {
-                const uint64_t b = __ballot((m[i] >> k) & 1u);
-                if ((m[i] >> k) & 1u) {
-                    const int64_t pos = start + run + (uint32_t)__popcll(b & below);
-                    if (pos < lim) {               // false only after a stalled wait
-                        pair_in[pos] = nv[kk][i];
-                        pair_out[pos] = (int32_t)(base + i * 64 + lane);
-                        pair_slot[pos] = k == kCentre
-                                             ? -1
-                                             : (int32_t)(rb[i] + __popc(m[i] & lower & ~(1u << kCentre)));
-                    }
+        for (int i = 0; i < kCItems; ++i) {
+            const uint64_t b = __ballot((m[i] >> k) & 1u);
+            const int lr = w * (kCChunk / kCWaves) + i * 64 + lane;   // row within the chunk
+            if ((m[i] >> k) & 1u) {
+                const int64_t pos = start + run + (uint32_t)__popcll(b & below);
+                if (pos < lim) {                   // false only after a stalled wait
+                    pair_in[pos] = k == kCentre ? (int32_t)(base0 + lr) : s_nb[lr * kTaps + k];
+                    pair_out[pos] = (int32_t)(base0 + lr);
+                    pair_slot[pos] = k == kCentre
+                                         ? -1
+                                         : (int32_t)(rb[i] + __popc(m[i] & lower & ~(1u << kCentre)));
                 }
-                run += (uint32_t)__popcll(b);
             }
+            run += (uint32_t)__popcll(b);
         }
     }
     // dense route: the grid cells of these rows go back to empty (every lookup has finished)
@@ -282,12 +303,9 @@ __global__ __launch_bounds__(kCThreads) void k_compact(
 #pragma unroll
         for (int i = 0; i < kCItems; ++i) {
             const int64_t r = base + i * 64 + lane;
-            if (r >= n) continue;
-            const int32_t* c = coords + r * g.ncols;
-            const int b = g.ncols == 4 ? c[0] : 0;
-            const int32_t* q = c + (g.ncols == 4 ? 1 : 0);
-            const int x = q[0] - g.origin[0], y = q[1] - g.origin[1], z = q[2] - g.origin[2];
-            if ((unsigned)b < (unsigned)g.batch && (unsigned)x < (unsigned)g.ext[0] &&
+            const int b = cq[i].x;
+            const int x = cq[i].y - g.origin[0], y = cq[i].z - g.origin[1], z = cq[i].w - g.origin[2];
+            if (r < n && (unsigned)b < (unsigned)g.batch && (unsigned)x < (unsigned)g.ext[0] &&
                 (unsigned)y < (unsigned)g.ext[1] && (unsigned)z < (unsigned)g.ext[2])
                 grid[b * g.sz_b + (int64_t)(x + 1) * g.sz_x + (int64_t)(y + 1) * g.sz_y + (z + 1)] = -1;
         }

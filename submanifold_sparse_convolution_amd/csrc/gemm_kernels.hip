@@ -84,50 +84,59 @@ __device__ inline void stage_b(uint4* __restrict__ dst, const uint4* __restrict_
     for (int i = full + threadIdx.x; i < n16; i += kGemmThreads) dst[i] = src[i];
 }
 
+// A fragments of k-steps s0 .. s0+3 for MW gathered rows (steps past the
+// last re-read the last one: valid addresses, results unused).
+template <int MW, bool VEC>
+__device__ __forceinline__ void load_group(const uint16_t* const (&xrow)[MW], int c_in, int steps,
+                                           int s0, int g, u32x4 (&a)[4][MW]) {
+    const int kq = steps * 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int st = min(s0 + i, steps - 1);
+#pragma unroll
+        for (int m = 0; m < MW; ++m) a[i][m] = load_a4<VEC>(xrow[m], g * kq + st * 8, c_in);
+    }
+}
+
+// c += A (k-steps s0 .. s0+3, those below steps) x B; b points at this lane's
+// word of the (tap, wave tile) fragments, in LDS or in global memory.
+template <int NBW, int MW>
+__device__ __forceinline__ void mma_group(const u32x4 (&a)[4][MW], const uint4* __restrict__ b,
+                                          int s0, int steps, f32x4 (&c)[MW][NBW]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (s0 + i >= steps) break;
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) {
+            const uint4 bv = b[((s0 + i) * NBW + nb) * 64];
+#pragma unroll
+            for (int m = 0; m < MW; ++m)
+                c[m][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[i][m]), as_bf16x8(bv),
+                                                                   c[m][nb], 0, 0, 0);
+        }
+    }
+}
+
 // One wave: MW fragments of 16 rows times 16 NBW columns, one tap's weights.
-// b points at this lane's word of the (tap, wave tile) fragments, in LDS or
-// in global memory. A loads of 4 k-steps are issued before their MFMAs.
+// a holds the first group of k-steps (loaded by the caller, ahead of
+// whatever it had to wait for); each later group is loaded while the
+// previous one is multiplied.
 template <int NBW, int MW, bool VEC>
 __device__ __forceinline__ void wave_mma(const uint16_t* const (&xrow)[MW], int c_in, int steps,
-                                         const uint4* __restrict__ b, int lane,
+                                         const uint4* __restrict__ b, int g, u32x4 (&a)[4][MW],
                                          f32x4 (&c)[MW][NBW]) {
-    const int g = lane >> 4;
-    const int kq = steps * 8;
 #pragma unroll
     for (int m = 0; m < MW; ++m)
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb) c[m][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    int s0 = 0;
-    for (; s0 + 4 <= steps; s0 += 4) {        // groups of 4 k-steps: A loads first
-        uint4 a[4][MW];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int m = 0; m < MW; ++m) a[i][m] = load_a<VEC>(xrow[m], g * kq + (s0 + i) * 8, c_in);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int nb = 0; nb < NBW; ++nb) {
-                const uint4 bv = b[((s0 + i) * NBW + nb) * 64];
-#pragma unroll
-                for (int m = 0; m < MW; ++m)
-                    c[m][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        as_bf16x8(a[i][m]), as_bf16x8(bv), c[m][nb], 0, 0, 0);
-            }
-    }
-    for (; s0 < steps; ++s0) {                 // remaining k-steps (fewer than 4)
-        uint4 a[MW];
-#pragma unroll
-        for (int m = 0; m < MW; ++m) a[m] = load_a<VEC>(xrow[m], g * kq + s0 * 8, c_in);
-#pragma unroll
-        for (int nb = 0; nb < NBW; ++nb) {
-            const uint4 bv = b[(s0 * NBW + nb) * 64];
-#pragma unroll
-            for (int m = 0; m < MW; ++m)
-                c[m][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[m]), as_bf16x8(bv),
-                                                                   c[m][nb], 0, 0, 0);
-        }
+    u32x4 an[4][MW];
+    for (int s0 = 0;; s0 += 8) {
+        if (s0 + 4 < steps) load_group<MW, VEC>(xrow, c_in, steps, s0 + 4, g, an);
+        mma_group<NBW, MW>(a, b, s0, steps, c);
+        if (s0 + 4 >= steps) break;
+        if (s0 + 8 < steps) load_group<MW, VEC>(xrow, c_in, steps, s0 + 8, g, a);
+        mma_group<NBW, MW>(an, b, s0 + 4, steps, c);
+        if (s0 + 8 >= steps) break;
     }
 }
 
@@ -185,6 +194,8 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_nc(
         const int4 ps = *reinterpret_cast<const int4*>(pair_slot + base + 4 * g);
         const bool a_ok = j0 + r < cnt && pi >= 0 && pi < n;
         const uint16_t* xrow[1] = {x + (int64_t)(a_ok ? pi : 0) * c_in};
+        u32x4 a[4][1];
+        load_group<1, VEC>(xrow, c_in, steps, 0, g, a);   // in flight while weights are staged
         const uint4* src = wp + ((int64_t)tap * n_wt + wt_i) * n16;
         const uint4* b = src + lane;
         if (LDS) {
@@ -194,7 +205,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_nc(
             b = s_b + lane;
         }
         f32x4 c[1][NBW];
-        wave_mma<NBW, 1, VEC>(xrow, c_in, steps, b, lane, c);
+        wave_mma<NBW, 1, VEC>(xrow, c_in, steps, b, g, a, c);
         if (col0 >= c_out) continue;
         const int slots[4] = {ps.x, ps.y, ps.z, ps.w};
 #pragma unroll
@@ -212,8 +223,80 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_nc(
 // wave w takes rows +16 MW w .. +16 MW w + 16 MW - 1. With LDS the centre
 // weight slab is staged once per block. A lane's 4 output rows of a
 // fragment are consecutive, so their slab rows form one consecutive run
-// [rowbase[first], rowbase[last] + deg(last)); it is read 4 slab rows at a
-// time and each slab row is added to the output row it belongs to.
+// [rowbase[first], rowbase[last] + deg(last)). Every load that does not
+// depend on another is issued first (gathered rows, run bounds, weights);
+// the first kSlabBatch slab rows of the lane's runs are in flight while the
+// MFMAs run, and longer runs take further batches afterwards.
+constexpr int kSlabBatch = 4;
+
+// Slab row of flat index t over a lane's MW runs [rb[m][0], rb[m][0] + len[m])
+// (past the end: row 0, read but unused).
+template <int MW>
+__device__ __forceinline__ int32_t slab_row(const int32_t (&rb)[MW][4], const int32_t (&len)[MW],
+                                            int tot, int t) {
+    int32_t sr = 0;
+    int before = 0;
+#pragma unroll
+    for (int m = 0; m < MW; ++m) {
+        if (t >= before && t < before + len[m]) sr = rb[m][0] + t - before;
+        before += len[m];
+    }
+    return t < tot ? sr : 0;
+}
+
+// kSlabBatch slab rows from flat index t0 on, NBW columns from col.
+template <int NBW, int MW>
+__device__ __forceinline__ void load_slab(const float* __restrict__ part, int c_out, int col,
+                                          bool vec, const int32_t (&rb)[MW][4],
+                                          const int32_t (&len)[MW], int tot, int t0,
+                                          float (&pv)[kSlabBatch][NBW]) {
+#pragma unroll
+    for (int u = 0; u < kSlabBatch; ++u) {
+        const float* prow = part + (int64_t)slab_row<MW>(rb, len, tot, t0 + u) * c_out + col;
+        if (vec) {
+#pragma unroll
+            for (int q = 0; q < NBW; q += 4) {
+                const float4 p4 = *reinterpret_cast<const float4*>(prow + q);
+                pv[u][q] = p4.x;
+                pv[u][q + 1] = p4.y;
+                pv[u][q + 2] = p4.z;
+                pv[u][q + 3] = p4.w;
+            }
+        } else {
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb) pv[u][nb] = prow[col + nb < c_out ? nb : 0];
+        }
+    }
+}
+
+// Add slab rows t0 .. t0 + kSlabBatch - 1 (those below tot) to the output rows
+// they belong to.
+template <int NBW, int MW>
+__device__ __forceinline__ void add_slab(const int32_t (&rb)[MW][4], const int32_t (&re)[MW],
+                                         const int32_t (&len)[MW], int tot, int t0,
+                                         const float (&pv)[kSlabBatch][NBW],
+                                         float (&v)[MW][4][NBW]) {
+#pragma unroll
+    for (int u = 0; u < kSlabBatch; ++u) {
+        const int t = t0 + u;
+        if (t >= tot) break;
+        const int32_t sl = slab_row<MW>(rb, len, tot, t);
+        // every element is written (a select, not a branch): a conditional update of
+        // v[m][jr] would become a dynamically indexed array in scratch memory
+#pragma unroll
+        for (int m = 0; m < MW; ++m) {
+            const bool in_m = sl >= rb[m][0] && sl < re[m];
+            const int jr = (sl >= rb[m][1]) + (sl >= rb[m][2]) + (sl >= rb[m][3]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bool hit = in_m && j == jr;
+#pragma unroll
+                for (int nb = 0; nb < NBW; ++nb) v[m][j][nb] = hit ? v[m][j][nb] + pv[u][nb] : v[m][j][nb];
+            }
+        }
+    }
+}
+
 template <int NBW, int MW, bool OUT_F32, bool LDS, bool VEC>
 __global__ __launch_bounds__(kGemmThreads) void k_gemm_centre(
     const uint16_t* __restrict__ x, int c_in, int steps, const uint4* __restrict__ wp, int n_wt,
@@ -224,97 +307,109 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_centre(
     const int r = lane & 15, g = lane >> 4;
     const int wt_i = blockIdx.y;
     const int col0 = wt_i * 16 * NBW + r * NBW;
+    const int colc = col0 < c_out ? col0 : 0;     // slab column read by lanes past c_out
     const int n16 = steps * NBW * 64;
-    const uint4* src = wp + ((int64_t)kCentre * n_wt + wt_i) * n16;
-    const uint4* b = src + lane;
-    if (LDS) {
-        stage_b(s_b, src, n16);
-        __syncthreads();
-        b = s_b + lane;
-    }
     const bool vec_part = col0 + NBW <= c_out && (c_out & 3) == 0 && NBW >= 4;
     const int64_t rows_per_tile = 64 * MW;
     const int64_t n_rt = (n + rows_per_tile - 1) / rows_per_tile;
-    for (int64_t rt = blockIdx.x; rt < n_rt; rt += gridDim.x) {
+    int64_t rt = blockIdx.x;
+    if (rt >= n_rt) return;
+    const uint4* src = wp + ((int64_t)kCentre * n_wt + wt_i) * n16;
+    const uint4* b = src + lane;
+    bool staged = false;
+
+    for (;;) {
         const int64_t row0 = rt * rows_per_tile + w * 16 * MW;
+        // gathered rows (first k-group) and raw run bounds
         const uint16_t* xrow[MW];
 #pragma unroll
         for (int m = 0; m < MW; ++m) {
             const int64_t ir = row0 + m * 16 + r;
             xrow[m] = x + (ir < n ? ir : 0) * c_in;
         }
-        // slab runs of this lane's output rows, loaded before the MFMAs need them; rows
-        // past n get empty runs at the end of the last real row's run
-        int32_t rb[MW][4], re[MW];
+        u32x4 a[4][MW];
+        load_group<MW, VEC>(xrow, c_in, steps, 0, g, a);
+        int32_t rb[MW][4];
+        uint32_t mk[MW][4];
 #pragma unroll
-        for (int m = 0; m < MW; ++m) {
-            int32_t en[4];
+        for (int m = 0; m < MW; ++m)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int64_t row = row0 + m * 16 + 4 * g + j;
                 const int64_t rc = row < n ? row : n - 1;
                 rb[m][j] = rowbase[rc];
-                en[j] = rb[m][j] + (row < n ? __popc(mask[rc] & ~(1u << kCentre)) : 0);
+                mk[m][j] = mask[rc];
             }
+        // weights: one round of 8 words per thread is loaded here, before any wait
+        u32x4 bw[8];
+        const bool one_round = LDS && !staged && n16 <= 8 * kGemmThreads;
+        if (one_round) {
+            const u32x4* src4 = reinterpret_cast<const u32x4*>(src);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int i = threadIdx.x + j * kGemmThreads;
+                bw[j] = src4[i < n16 ? i : n16 - 1];
+            }
+        }
+        // runs: rows past n get empty runs at the end of the last real row's run
+        int32_t re[MW], len[MW];
+#pragma unroll
+        for (int m = 0; m < MW; ++m) {
             int32_t e = 0;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (row0 + m * 16 + 4 * g + j < n) e = en[j];
+            for (int j = 0; j < 4; ++j) {
+                const int64_t row = row0 + m * 16 + 4 * g + j;
+                if (row < n) e = rb[m][j] + __popc(mk[m][j] & ~(1u << kCentre));
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 if (row0 + m * 16 + 4 * g + j >= n) rb[m][j] = e;
             re[m] = e;
+            len[m] = e - rb[m][0];
+        }
+        int tot = 0;
+#pragma unroll
+        for (int m = 0; m < MW; ++m) tot += len[m];
+        float pv[kSlabBatch][NBW];
+        load_slab<NBW, MW>(part, c_out, colc, vec_part, rb, len, tot, 0, pv);
+        if (LDS && !staged) {
+            if (one_round) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int i = threadIdx.x + j * kGemmThreads;
+                    if (i < n16) reinterpret_cast<u32x4*>(s_b)[i] = bw[j];
+                }
+            } else {
+                stage_b(s_b, src, n16);
+            }
+            __syncthreads();
+            b = s_b + lane;
+            staged = true;
         }
         f32x4 c[MW][NBW];
-        wave_mma<NBW, MW, VEC>(xrow, c_in, steps, b, lane, c);
+        wave_mma<NBW, MW, VEC>(xrow, c_in, steps, b, g, a, c);
+        float v[MW][4][NBW];
 #pragma unroll
-        for (int m = 0; m < MW; ++m) {
-            float v[4][NBW];
+        for (int m = 0; m < MW; ++m)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int nb = 0; nb < NBW; ++nb) v[j][nb] = c[m][nb][j];
-            // partial products: slab rows [rb[m][0], re[m]), 4 at a time
-            if (col0 < c_out) {
-                for (int s0 = rb[m][0]; s0 < re[m]; s0 += 4) {
-                    float pv[4][NBW];
+                for (int nb = 0; nb < NBW; ++nb) v[m][j][nb] = c[m][nb][j];
+        add_slab<NBW, MW>(rb, re, len, tot, 0, pv, v);
+        for (int t0 = kSlabBatch; t0 < tot; t0 += kSlabBatch) {
+            load_slab<NBW, MW>(part, c_out, colc, vec_part, rb, len, tot, t0, pv);
+            add_slab<NBW, MW>(rb, re, len, tot, t0, pv, v);
+        }
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const float* prow = part + (int64_t)min(s0 + u, re[m] - 1) * c_out + col0;
-                        if (vec_part) {
-#pragma unroll
-                            for (int q = 0; q < NBW; q += 4) {
-                                const float4 p4 = *reinterpret_cast<const float4*>(prow + q);
-                                pv[u][q] = p4.x;
-                                pv[u][q + 1] = p4.y;
-                                pv[u][q + 2] = p4.z;
-                                pv[u][q + 3] = p4.w;
-                            }
-                        } else {
-#pragma unroll
-                            for (int nb = 0; nb < NBW; ++nb) pv[u][nb] = prow[col0 + nb < c_out ? nb : 0];
-                        }
-                    }
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int sl = s0 + u;
-                        if (sl >= re[m]) break;
-                        const int jr = (sl >= rb[m][1]) + (sl >= rb[m][2]) + (sl >= rb[m][3]);
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            if (j == jr)
-#pragma unroll
-                                for (int nb = 0; nb < NBW; ++nb) v[j][nb] += pv[u][nb];
-                    }
-                }
-            }
+        for (int m = 0; m < MW; ++m)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int64_t row = row0 + m * 16 + 4 * g + j;
                 if (row >= n || col0 >= c_out) continue;
-                store_row<NBW, OUT_F32>(yv, row, c_out, col0, v[j], relu);
+                store_row<NBW, OUT_F32>(yv, row, c_out, col0, v[m][j], relu);
             }
-        }
+        rt += gridDim.x;
+        if (rt >= n_rt) break;
     }
 }
 

@@ -8,6 +8,8 @@
 // gfx950)", Design, the mapper table.
 #include "smc_internal.h"
 
+#include <cstddef>
+
 #include <climits>
 
 namespace smc {
@@ -34,21 +36,23 @@ __device__ inline int64_t dense_cell(const Geom& g, int b, int x, int y, int z) 
     return b * g.sz_b + (int64_t)(x + 1) * g.sz_x + (int64_t)(y + 1) * g.sz_y + (z + 1);
 }
 
-// Clears the build's device record and the sort histograms it accumulates.
+// Puts a build record in its starting state (bounding box empty, everything
+// else zero) and clears its sort histograms; grid-strided over all threads.
+__device__ inline void clear_record(MapState* st, uint32_t* hist, int hist_ints) {
+    const int64_t t0 = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    const int64_t nt = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = t0; i < hist_ints; i += nt) hist[i] = 0;
+    constexpr int kWords = (int)(sizeof(MapState) / 4);
+    constexpr int kBox = (int)(offsetof(MapState, bbox) / 4);
+    uint32_t* wv = reinterpret_cast<uint32_t*>(st);
+    for (int64_t i = t0; i < kWords; i += nt) {
+        const int b = (int)i - kBox;
+        wv[i] = (b >= 0 && b < 8) ? (uint32_t)((b < 3 || b == 6) ? INT_MAX : INT_MIN) : 0u;
+    }
+}
+
 __global__ __launch_bounds__(kBlock) void k_state_init(MapState* st, uint32_t* hist, int hist_ints) {
-    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < hist_ints; i += gridDim.x * blockDim.x)
-        hist[i] = 0;
-    if (blockIdx.x != 0) return;
-    int t = threadIdx.x;
-    if (t == 0) st->status = 0;
-    if (t < 3) st->bbox[t] = INT_MAX;
-    else if (t < 6) st->bbox[t] = INT_MIN;
-    else if (t == 6) st->bbox[6] = INT_MAX;
-    else if (t == 7) st->bbox[7] = INT_MIN;
-    if (t < 4) st->totals[t] = 0;
-    if (t < 28) st->tap_off[t] = 0;
-    if (t < 27) st->tap_count[t] = 0;
-    if (t < 27) st->tap_tot[t] = 0;
+    clear_record(st, hist, hist_ints);
 }
 
 __device__ inline int wave_min(int v) {
@@ -110,7 +114,8 @@ __global__ __launch_bounds__(kBlock) void k_fill_i32(int32_t* p, int64_t n, int3
 __global__ __launch_bounds__(kBlock) void k_dense_scatter(const int32_t* __restrict__ coords,
                                                           int64_t n, Geom g,
                                                           int32_t* __restrict__ grid,
-                                                          MapState* st) {
+                                                          MapState* st, NextRecord next) {
+    if (next.st) clear_record(next.st, next.hist, next.hist_ints);
     int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
     if (i >= n) return;
     int b, x, y, z;
@@ -153,7 +158,8 @@ __global__ __launch_bounds__(kBlock) void k_dense_lookup(const int32_t* __restri
 template <typename K>
 __global__ __launch_bounds__(kBlock) void k_make_keys(const int32_t* __restrict__ coords,
                                                       int64_t n, Geom g, K* __restrict__ keys,
-                                                      MapState* st) {
+                                                      MapState* st, NextRecord next) {
+    if (next.st) clear_record(next.st, next.hist, next.hist_ints);
     int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
     if (i >= n) return;
     int b, x, y, z;
@@ -244,7 +250,7 @@ inline unsigned blocks_for(int64_t threads) {
 hipError_t launch_state_init(MapState* st, uint32_t* hist, int hist_ints, hipStream_t s) {
     unsigned blocks = (unsigned)((hist_ints + kBlock - 1) / kBlock);
     if (blocks < 1) blocks = 1;
-    if (blocks > 32) blocks = 32;
+    if (blocks > 64) blocks = 64;
     k_state_init<<<blocks, kBlock, 0, s>>>(st, hist, hist_ints);
     return hipGetLastError();
 }
@@ -266,8 +272,8 @@ hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s) {
 }
 
 hipError_t launch_dense_scatter(const int32_t* coords, int64_t n, const Geom& g, int32_t* grid,
-                                MapState* st, hipStream_t s) {
-    k_dense_scatter<<<blocks_for(n), kBlock, 0, s>>>(coords, n, g, grid, st);
+                                MapState* st, const NextRecord& next, hipStream_t s) {
+    k_dense_scatter<<<blocks_for(n), kBlock, 0, s>>>(coords, n, g, grid, st, next);
     return hipGetLastError();
 }
 
@@ -278,11 +284,11 @@ hipError_t launch_dense_lookup(const int32_t* coords, int64_t n, const Geom& g, 
 }
 
 hipError_t launch_make_keys(const int32_t* coords, int64_t n, const Geom& g, bool wide, void* keys,
-                            MapState* st, hipStream_t s) {
+                            MapState* st, const NextRecord& next, hipStream_t s) {
     if (wide)
-        k_make_keys<uint64_t><<<blocks_for(n), kBlock, 0, s>>>(coords, n, g, (uint64_t*)keys, st);
+        k_make_keys<uint64_t><<<blocks_for(n), kBlock, 0, s>>>(coords, n, g, (uint64_t*)keys, st, next);
     else
-        k_make_keys<uint32_t><<<blocks_for(n), kBlock, 0, s>>>(coords, n, g, (uint32_t*)keys, st);
+        k_make_keys<uint32_t><<<blocks_for(n), kBlock, 0, s>>>(coords, n, g, (uint32_t*)keys, st, next);
     return hipGetLastError();
 }
 

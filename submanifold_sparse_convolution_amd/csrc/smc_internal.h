@@ -41,6 +41,7 @@ struct SortWork {
 constexpr int kMaskBits = 27;
 constexpr int kHistMaskInts = 3 * 512;        // mask sort: 3 passes x 9 bits
 constexpr int kHistKeyInts = 6 * 2048;        // key sort: up to 6 passes x 11 bits
+constexpr int kHistInts = kHistMaskInts + kHistKeyInts;
 
 // Where voxels live. Coordinates are taken relative to origin; a voxel is in
 // range when 0 <= rel < ext and 0 <= b < batch.
@@ -57,16 +58,25 @@ struct Geom {
     int32_t wz, wy, wx, wb;
 };
 
+// The record (and sort histograms) the next build will use: the first kernel
+// of a build clears it, so no build needs a clearing launch of its own.
+// st == nullptr: nothing to clear.
+struct NextRecord {
+    MapState* st = nullptr;
+    uint32_t* hist = nullptr;
+    int hist_ints = 0;
+};
+
 // ---- map kernels (map_kernels.hip) ----
 hipError_t launch_state_init(MapState* st, uint32_t* hist, int hist_ints, hipStream_t s);
 hipError_t launch_bbox(const int32_t* coords, int64_t n, int ncols, MapState* st, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 hipError_t launch_dense_scatter(const int32_t* coords, int64_t n, const Geom& g, int32_t* grid,
-                                MapState* st, hipStream_t s);
+                                MapState* st, const NextRecord& next, hipStream_t s);
 hipError_t launch_dense_lookup(const int32_t* coords, int64_t n, const Geom& g, const int32_t* grid,
                                int32_t* nbr, uint32_t* mask, hipStream_t s);
 hipError_t launch_make_keys(const int32_t* coords, int64_t n, const Geom& g, bool wide, void* keys,
-                            MapState* st, hipStream_t s);
+                            MapState* st, const NextRecord& next, hipStream_t s);
 hipError_t launch_sorted_lookup(const void* keys, const uint32_t* vals, int64_t n, const Geom& g,
                                 bool wide, int32_t* nbr, uint32_t* mask, MapState* st,
                                 hipStream_t s);

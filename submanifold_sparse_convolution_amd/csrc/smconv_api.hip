@@ -95,12 +95,14 @@ struct smc_map {
     Geom geom{};
     int64_t grid_cells = 0;
     // device buffers
-    DevBuf state;                     // MapState
+    DevBuf state;                     // two MapState records: builds alternate between them
+    int slot = 1;                     // record of the last build
+    bool slot_clean[2] = {true, true};  // record in its starting state
     DevBuf grid;                      // int32 presence grid (dense route), kept all -1
     int64_t grid_clean_cells = 0;     // prefix of grid known to be -1
     DevBuf keys0, keys1, keys2;       // packed keys (u32 or u64)
     DevBuf vals0, vals1;              // u32
-    DevBuf hist;                      // digit histograms: mask sort, then key sort
+    DevBuf hist;                      // per record: digit histograms, mask sort then key sort
     DevBuf look, ticket;              // look-back table and block ticket (zeroed when allocated)
     SortWork ws;
     bool state_copied = false;        // host_state already holds the last build's record
@@ -135,12 +137,15 @@ int ensure_device(smc_map* m) {
             m->host_state = nullptr;
             return fail(SMC_ERR_ALLOC, "hipHostMalloc of the readback record failed");
         }
-        int rc = m->state.ensure(sizeof(MapState));
+        int rc = m->state.ensure(2 * sizeof(MapState));
         if (rc) return rc;
-        if ((rc = m->ticket.ensure(256)) || (rc = m->hist.ensure((kHistMaskInts + kHistKeyInts) * 4)) ||
+        if ((rc = m->ticket.ensure(256)) || (rc = m->hist.ensure((size_t)2 * kHistInts * 4)) ||
             (rc = m->zrow.ensure(kZeroRowBytes)))
             return rc;
         SMC_HIP(launch_fill_i32(m->ticket.as<int32_t>(), 64, 0, nullptr));
+        for (int k = 0; k < 2; ++k)
+            SMC_HIP(launch_state_init(m->state.as<MapState>() + k, m->hist.as<uint32_t>() + k * kHistInts,
+                                      kHistInts, nullptr));
         SMC_HIP(launch_fill_i32(m->zrow.as<int32_t>(), kZeroRowBytes / 4, 0, nullptr));
         SMC_HIP(hipDeviceSynchronize());
         m->ws.ticket = m->ticket.as<uint32_t>();
@@ -155,7 +160,8 @@ int wait_build(smc_map* m) {
     if (!m->pending) return SMC_OK;
     SMC_HIP(hipEventSynchronize(m->done));
     if (!m->state_copied) {
-        SMC_HIP(hipMemcpy(m->host_state, m->state.p, sizeof(MapState), hipMemcpyDeviceToHost));
+        SMC_HIP(hipMemcpy(m->host_state, m->state.as<MapState>() + m->slot, sizeof(MapState),
+                          hipMemcpyDeviceToHost));
         m->state_copied = true;
     }
     m->pending = false;
@@ -314,9 +320,19 @@ int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     m->pending = false;
     m->built = false;
     m->perm = nullptr;
-    MapState* st = m->state.as<MapState>();
+    // this build's record and histograms; the other slot is cleared by its first kernel
+    const int slot = m->slot ^ 1;
+    m->slot = slot;
+    MapState* st = m->state.as<MapState>() + slot;
+    uint32_t* hist_mask = m->hist.as<uint32_t>() + slot * kHistInts;
+    uint32_t* hist_key = hist_mask + kHistMaskInts;
+    NextRecord next;
+    next.st = m->state.as<MapState>() + (slot ^ 1);
+    next.hist = m->hist.as<uint32_t>() + (slot ^ 1) * kHistInts;
+    next.hist_ints = kHistInts;
     StageTimer t_map(m, SMC_STAGE_MAP, s);
-    SMC_HIP(launch_state_init(st, m->hist.as<uint32_t>(), kHistMaskInts + kHistKeyInts, s));
+    if (!m->slot_clean[slot]) SMC_HIP(launch_state_init(st, hist_mask, kHistInts, s));
+    if (n > 0) m->slot_clean[slot] = false;
 
     // ---- geometry: explicit shape, or the bounding box (one read) ----
     Geom g{};
@@ -398,7 +414,8 @@ int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     const size_t look_c = compact_look_bytes(nn);
     if (look_c > look_bytes) look_bytes = look_c;
     const size_t look_before = m->look.bytes;
-    if ((rc = m->nbr.ensure((size_t)nn * kTaps * 4)) || (rc = m->mask.ensure((size_t)nn * 4)) ||
+    // (the neighbour table is read in whole 16-byte words: keep the last one readable)
+    if ((rc = m->nbr.ensure((size_t)nn * kTaps * 4 + 16)) || (rc = m->mask.ensure((size_t)nn * 4)) ||
         (rc = m->mkey0.ensure((size_t)nn * 4)) || (rc = m->mkey1.ensure((size_t)nn * 4)) ||
         (rc = m->mval0.ensure((size_t)nn * 4)) || (rc = m->mval1.ensure((size_t)nn * 4)) ||
         (rc = m->look.ensure(look_bytes)))
@@ -414,8 +431,6 @@ int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     m->ws.look = m->look.as<uint64_t>();
     m->cap = cap;
     uint32_t* status = &st->status;
-    uint32_t* hist_mask = m->hist.as<uint32_t>();
-    uint32_t* hist_key = hist_mask + kHistMaskInts;
 
     if (n > 0) {
         int32_t* nbr = m->nbr.as<int32_t>();
@@ -425,7 +440,8 @@ int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
         if (chosen == SMC_ROUTE_DENSE) {
             if ((rc = ensure_grid(m, m->grid_cells, s))) return rc;
             grid = m->grid.as<int32_t>();
-            SMC_HIP(launch_dense_scatter(coords, n, g, grid, st, s));
+            SMC_HIP(launch_dense_scatter(coords, n, g, grid, st, next, s));
+            m->slot_clean[slot ^ 1] = true;
             SMC_HIP(launch_dense_lookup(coords, n, g, grid, nbr, mask, s));
         } else {
             const size_t kb = (size_t)nn * (m->wide ? 8 : 4);
@@ -433,7 +449,8 @@ int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
                 (rc = m->keys2.ensure(kb)) || (rc = m->vals0.ensure((size_t)nn * 4)) ||
                 (rc = m->vals1.ensure((size_t)nn * 4)))
                 return rc;
-            SMC_HIP(launch_make_keys(coords, n, g, m->wide, m->keys0.p, st, s));
+            SMC_HIP(launch_make_keys(coords, n, g, m->wide, m->keys0.p, st, next, s));
+            m->slot_clean[slot ^ 1] = true;
             const SortPlan kp = sort_plan(key_bits);
             SMC_HIP(launch_key_hist(m->keys0.p, m->wide, n, kp, hist_key, s));
             const void* skeys;
@@ -632,11 +649,13 @@ int smc_conv_forward(smc_map* m, const uint16_t* x, int c_in, const void* wpacke
     }
     if (!m->pending) slab = (double)m->host_state->totals[3] * c_out * 4.0;
     if (slab > (double)((size_t)1 << 46)) return fail(SMC_ERR_ALLOC, "slab of %.3g bytes", slab);
-    int rc = m->part.ensure(slab > 256.0 ? (size_t)slab : 256);
+    // at least one row: lanes with nothing to add read row 0
+    if (slab < (double)c_out * 4.0) slab = (double)c_out * 4.0;
+    int rc = m->part.ensure((size_t)slab);
     if (rc) return rc;
     StageTimer t_g(m, SMC_STAGE_GEMM, s);
     SMC_HIP(launch_gemm_nc(x, c_in, wpacked, c_out, m->pair_in.as<int32_t>(),
-                           m->pair_slot.as<int32_t>(), m->state.as<MapState>(), m->cap, m->n,
+                           m->pair_slot.as<int32_t>(), m->state.as<MapState>() + m->slot, m->cap, m->n,
                            m->n_cu, m->part.as<float>(), s));
     t_g.finish();
     StageTimer t_f(m, SMC_STAGE_CENTRE, s);
