@@ -13,9 +13,9 @@
  * with k(d) = 9 (dx+1) + 3 (dy+1) + (dz+1) (x slowest; the centre is 13).
  * Raw int32 voxel coordinates go in, the kernel map is built internally and
  * can be reused by every layer that shares the coordinates (PR #942,
- * commit "derive the rulebook cache key from the coords tensor"; here the
+ * commit 706a0bf, which keys the map cache on the coordinates; here the
  * reuse is an explicit handle), features and weights are bf16 and the
- * accumulation is float32 (PR #942, Design: "dtype is bf16").
+ * accumulation is float32 (PR #942, section "Design, and the measurements behind it").
  *
  * Conventions for every call:
  *  - Every call returns an int status (smc_status); 0 is success. No C++
@@ -61,8 +61,9 @@ typedef enum smc_status {
     SMC_ERR_GRID = 9          /* the dense route was forced on a grid of 2^31 cells or more */
 } smc_status;
 
-/* Map routes ("[Kernel] Add submanifold sparse 3D convolution", Design:
- * two mappers chosen by bounding-box volume). */
+/* Map routes ("[Kernel] Add submanifold sparse 3D convolution", section
+ * "Design, and the measurements behind it": two mappers chosen by
+ * bounding-box volume). */
 enum {
     SMC_ROUTE_AUTO = 0,   /* dense presence grid when it has < 2^31 cells and fits the
                              dense-grid budget, sorted packed keys otherwise */
@@ -115,15 +116,15 @@ int smc_map_destroy(smc_map* map);
  * lists (unless SMC_BUILD_NO_PAIRS).
  *
  * Steps (all on the GPU): bounding box -> route by grid volume ("[Kernel]
- * Add submanifold sparse 3D convolution", Design, the mapper table) ->
+ * Add submanifold sparse 3D convolution", section "Design, and the measurements behind it",
+ * the mapper table) ->
  *   dense route:  presence grid scatter, 27 lookups per row;
  *   sorted route: packed keys with packed(q + d) = packed(q) + packed(d),
- *                 radix sort, 9 binary searches per row ("Z-Delta", Design);
+ *                 radix sort, 9 binary searches per row (the Z-Delta mapper, same section);
  * -> neighbour table + masks ("Sparse convolution in FP32", "Neighbour masks
  * and sorted rows") -> radix sort of rows by mask -> per-tap counts, scan
- * and pair write, ascending output row within a tap ("[Kernel] ...", Design
- * "Compaction"; commits "move pair compaction from torch onto three fx
- * kernels" and "scan the pair counts on the device"), which also numbers
+ * and pair write, ascending output row within a tap ("[Kernel] ...", same
+ * section; commits 6ee20cd and f9cb4f1), which also numbers
  * every row's off-centre pairs for the pair-list forward.
  *
  * coords        device pointer, int32 [n, ncols], row-major. ncols = 4: rows
@@ -176,8 +177,8 @@ size_t smc_weight_packed_bytes(int c_in, int c_out);
 
 /*
  * Pack weights for the GEMM ("[Kernel] Add submanifold sparse 3D
- * convolution", Design: weights packed so that a wave reads fully used
- * cache lines). w: device pointer, bf16 [27, c_in, c_out] row-major
+ * convolution", section "Design, and the measurements behind it": weights
+ * packed so that a wave reads fully used cache lines). w: device pointer, bf16 [27, c_in, c_out] row-major
  * (W[k][ci][co]). out: device pointer of smc_weight_packed_bytes() bytes,
  * 16-byte aligned. Channels are zero-padded internally, so any c >= 1 works.
  * Pack once per weight tensor and reuse the result for every forward.
@@ -187,8 +188,9 @@ int smc_weight_pack(const uint16_t* w, int c_in, int c_out, void* out, void* str
 /*
  * One submanifold convolution layer over a built map. Two algorithms:
  *  - default, per-tap pair lists ("[Kernel] Add submanifold sparse 3D
- *    convolution", Design "GEMM": gather -> mfma_f32_16x16x32_bf16 with
- *    float32 accumulate -> scatter): the non-centre taps store each pair's
+ *    convolution", section "Design, and the measurements behind it" and
+ *    commit d4161ef: gather -> mfma_f32_16x16x32_bf16 with float32
+ *    accumulate -> scatter): the non-centre taps store each pair's
  *    float32 product row into a partial-product slab (one row per pair, a
  *    row's pairs consecutive), then the centre tap (every row with itself)
  *    runs as a dense GEMM whose epilogue adds the row's slab rows and writes

@@ -7,7 +7,7 @@ it, never links it, and shares no code, table or helper with it.
 Sources (the pages this follows):
 
 * [P1] "[Kernel] Add submanifold sparse 3D convolution (bf16 implicit GEMM,
-  gfx950)", FlyDSL pull request #942 -- sections Summary, Design, Test plan,
+  gfx950)", FlyDSL pull request #942 -- sections "Summary", "Design, and the measurements behind it", "Test plan",
   and its commit messages.
 * [P5] "Sparse convolution in FP32", DriveRT project page -- sections
   "The starting point", "Neighbour masks and sorted rows".
@@ -67,7 +67,8 @@ def tap_offsets() -> list:
 
 
 # --------------------------------------------------------------------------
-# bf16 helpers (the pages fix bf16 storage, [P1] Design: "dtype is bf16")
+# bf16 helpers ([P1] "Design, and the measurements behind it": features and
+# weights are stored as bf16)
 # --------------------------------------------------------------------------
 
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
@@ -101,7 +102,7 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
-# kernel map ([P5] "Neighbour masks and sorted rows"; [P1] Summary, Design)
+# kernel map ([P5] "Neighbour masks and sorted rows"; [P1] "Summary", "Design, and the measurements behind it")
 # --------------------------------------------------------------------------
 
 def _rows_bxyz(coords: np.ndarray) -> np.ndarray:
@@ -162,7 +163,7 @@ def mask_sort(mask: np.ndarray) -> np.ndarray:
 def compact_pairs(nbr: np.ndarray, mask: np.ndarray):
     """Per-tap pair lists holding only the neighbours that exist.
 
-    [P1] Design ("Compaction"): only valid (input, output) pairs are listed,
+    [P1] "Design, and the measurements behind it" (compaction): only valid (input, output) pairs are listed,
     grouped by tap so that a run of pairs shares one weight slab; the centre
     tap is listed like the others ([P1] commit d4161ef, "The centre tap is
     compacted along with the rest"). Within a tap, pairs follow ascending
@@ -185,7 +186,7 @@ def compact_pairs(nbr: np.ndarray, mask: np.ndarray):
 
 
 # --------------------------------------------------------------------------
-# compute ([P5] "The starting point"; [P1] Design, "GEMM")
+# compute ([P5] "The starting point"; [P1] "Design, and the measurements behind it", commit d4161ef)
 # --------------------------------------------------------------------------
 
 def conv_accumulate(x: np.ndarray, w: np.ndarray, pair_in, pair_out, tap_off,

@@ -1,16 +1,14 @@
 // Compaction of the neighbour table into per-tap pair lists.
 //
-// Only existing (input, output) pairs are listed, grouped by tap so that a
-// GEMM tile shares one weight slab ("[Kernel] Add submanifold sparse 3D
-// convolution (bf16 implicit GEMM, gfx950)", Design "Compaction"); within a
-// tap the pairs follow ascending output row. That pull request counts per
-// (tap, tile), scans the small count table and then writes, keeping the
-// totals on the device (commits "move pair compaction from torch onto three
-// fx kernels", "scan the pair counts on the device"). Here count, scan and
-// write are one kernel: each chunk of rows finds the pairs of earlier chunks
-// by decoupled look-back (same ticket + epoch scheme as the sort), and every
-// tap owns a fixed run of the pair arrays (cap entries, cap = n rounded up
-// to the tile height), so no chunk needs the other taps' totals first.
+// Only existing (input, output) pairs are listed, grouped by tap so that a GEMM tile shares one
+// weight slab ("[Kernel] Add submanifold sparse 3D convolution (bf16 implicit GEMM, gfx950)",
+// section "Design, and the measurements behind it"); within a tap the pairs follow ascending
+// output row. That pull request counts per (tap, tile), scans the small count table and then
+// writes, keeping the totals on the device (commits 6ee20cd and f9cb4f1). Here count, scan and
+// write are one kernel: each chunk of rows finds the pairs of earlier chunks by decoupled
+// look-back (same ticket + epoch scheme as the sort), and every tap owns a fixed run of the
+// pair arrays (cap entries, cap = n rounded up to the tile height), so no chunk needs the other
+// taps' totals first.
 //
 // The same pass numbers the off-centre pairs of every output row
 // consecutively (row order, then tap order): pair_slot[p] is the row of a

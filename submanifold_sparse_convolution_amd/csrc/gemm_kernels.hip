@@ -1,11 +1,10 @@
 // Implicit GEMM over per-tap pair lists: gather -> MFMA -> scatter.
 //
-// "[Kernel] Add submanifold sparse 3D convolution (bf16 implicit GEMM,
-// gfx950)", Design "GEMM" and commit d4161ef: mfma_f32_16x16x32_bf16 with
-// float32 accumulation; A is read through the pair list's input rows, the
-// result goes to the output rows through the pair list; weights are packed
-// so a wave reads whole cache lines; the loads of a k-step are issued ahead
-// of its MFMAs.
+// "[Kernel] Add submanifold sparse 3D convolution (bf16 implicit GEMM, gfx950)", section
+// "Design, and the measurements behind it", and commit d4161ef: mfma_f32_16x16x32_bf16 with
+// float32 accumulation; A is read through the pair list's input rows, the result goes to the
+// output rows through the pair list; weights are packed so a wave reads whole cache lines; the
+// loads of a k-step are issued ahead of its MFMAs.
 //
 // Two kernels per layer, split by tap:
 //  * k_gemm_nc: every tap but the centre, tile by tile over the pair lists.

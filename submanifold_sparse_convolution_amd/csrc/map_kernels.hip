@@ -5,7 +5,7 @@
 // "Neighbour masks and sorted rows". The two routes and their trade-off
 // (O(volume) grid vs. one sort plus binary searches, flat in volume) follow
 // "[Kernel] Add submanifold sparse 3D convolution (bf16 implicit GEMM,
-// gfx950)", Design, the mapper table.
+// gfx950)", section "Design, and the measurements behind it", the mapper table.
 #include "smc_internal.h"
 
 #include <cstddef>

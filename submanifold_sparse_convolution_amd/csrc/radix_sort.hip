@@ -2,9 +2,10 @@
 //
 // Used twice in the map build: on packed voxel keys in the sorted route
 // (the sort the Z-Delta mapper needs; "[Kernel] Add submanifold sparse 3D
-// convolution (bf16 implicit GEMM, gfx950)", Design) and on neighbour masks
-// to group rows with equal masks ("Sparse convolution in FP32", "Neighbour
-// masks and sorted rows": a GPU radix sort orders the rows by mask).
+// convolution (bf16 implicit GEMM, gfx950)", section "Design, and the
+// measurements behind it") and on neighbour masks to group rows with equal
+// masks ("Sparse convolution in FP32", "Neighbour masks and sorted rows": a
+// GPU radix sort orders the rows by mask).
 //
 // Design for small inputs (10^4 - 10^5 keys), where each kernel launch is a
 // large share of the cost:
