@@ -1,20 +1,34 @@
 #!/usr/bin/env python3
 """Benchmark: microseconds per submanifold 3x3x3 layer including the kernel
-map, effective TFLOP/s on useful MACs, and the roofline of the GEMM kernel.
+map, effective TFLOP/s on useful MACs, and the roofline of the dominant
+kernel.
 
 One step = one pass of the whole hot path over one seeded synthetic voxel
 set already resident in HBM: build the kernel map from raw coordinates
-(bounding box / route, neighbour search with masks, mask sort, pair
-compaction) and run the layer (gather -> MFMA -> scatter GEMM, bf16
-finalize). Weights are packed once before the timed region (a packed
-weight is cached per weight tensor) and the packing time is reported on
-its own.
+(route, neighbour search with masks, compaction into per-tap pair lists --
+or the mask sort for the mask-tile algorithm) and run the layer(s) (gather
+-> MFMA -> slab -> centre-tap GEMM with the bf16 finalize). Weights are
+packed once before the timed region (a packed weight is reused for every
+forward) and the packing time is reported on its own.
 
 Prints ONE JSON line. --gpus above 1 exits: this build measures one GPU.
+
+Per-stage times come from a second pass with the library's stage timers:
+every kernel launched in a stage carries its own HIP start/stop events
+(stamped by the kernel's dispatch), so a single-kernel stage's average is
+that kernel's average duration, as rocprofv3's kernel trace reports it.
+
+  --summarize-pmc FETCH_DIR WRITE_DIR   turn two `rocprofv3 --pmc FETCH_SIZE`
+      / `--pmc WRITE_SIZE` runs of this script (with --copy-probe-mb) into
+      profiles/traffic_<workload>_<algo>.json, which later runs read for the
+      roofline's "traffic" (null when a kernel source changed since).
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import statistics
@@ -28,6 +42,25 @@ if ROOT not in sys.path:
 METRIC = "µs per subm-conv layer incl. map + effective TFLOP/s (useful MACs) vs peak"
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # flop per byte
+CSRC = os.path.join(ROOT, "submanifold_sparse_convolution_amd", "csrc")
+
+# stage -> the kernels it launches (dense route; the sorted route's neighbour
+# stage is k_make_keys + k_key_hist + k_os_pass + k_sorted_lookup)
+STAGE_KERNELS = {
+    "neighbours": ("k_dense_scatter", "k_dense_lookup"),
+    "mask_sort": ("k_mask_hist", "k_os_pass"),
+    "compact": ("k_compact",),
+    "gemm": ("k_gemm_nc",),
+    "centre": ("k_gemm_centre",),
+}
+MASK_TILE_GEMM = ("k_conv_masktile",)
+KERNEL_SOURCES = {
+    "k_compact": "compact_kernels.hip", "k_mask_hist": "compact_kernels.hip",
+    "k_gemm_nc": "gemm_kernels.hip", "k_gemm_centre": "gemm_kernels.hip",
+    "k_conv_masktile": "masktile_kernels.hip", "k_dense_scatter": "map_kernels.hip",
+    "k_dense_lookup": "map_kernels.hip", "k_os_pass": "radix_sort.hip",
+}
 
 
 def dev_bf16(bits):
@@ -36,20 +69,37 @@ def dev_bf16(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def gemm_algorithmic_bytes(n, c_in, c_out, pairs):
-    """Compulsory HBM bytes of one GEMM launch: each input row once (bf16),
-    the weights once, both pair lists, and the float32 accumulator once."""
-    return 2 * n * c_in + 2 * 27 * c_in * c_out + 8 * pairs + 4 * n * c_out
+def stage_model(stage, algo, route, n, p, c_in, c_out):
+    """Algorithmic (compulsory) bytes and useful flops of one stage execution.
+
+    Each input is counted once and each output once; reads of random grid cells
+    and gathered rows count their payload only.
+    """
+    p_nc = p - n
+    if stage == "neighbours":
+        if route == "dense":
+            # scatter: coords in, grid cell out; lookup: coords + 27 cells in, nbr + mask out
+            return 16 * n + 4 * n + (16 * n + 108 * n) + (108 * n + 4 * n), 0
+        # sorted: coords -> keys, key sort passes, 9 searches per row (8-byte keys)
+        return 16 * n + 8 * n + 5 * 2 * 12 * n + 9 * 8 * n + 112 * n, 0
+    if stage == "mask_sort":
+        return 4 * n + 3 * 2 * 8 * n, 0
+    if stage == "compact":
+        grid = 16 * n + 4 * n if route == "dense" else 0
+        return 4 * n + 108 * n + 12 * p + 4 * n + grid, 0
+    if stage == "gemm" and algo == "pairs":
+        return ((2 * c_in + 8 + 4 * c_out) * p_nc + 2 * 26 * c_in * c_out,
+                2.0 * p_nc * c_in * c_out)
+    if stage == "gemm":          # mask tiles: x once, all weights, nbr/mask/perm, y once
+        return (2 * c_in * n + 2 * 27 * c_in * c_out + 116 * n + 2 * c_out * n,
+                2.0 * p * c_in * c_out)
+    if stage == "centre":
+        return (2 * c_in * n + 2 * c_in * c_out + 8 * n + 4 * c_out * p_nc + 2 * c_out * n,
+                2.0 * n * c_in * c_out)
+    return 0, 0
 
 
-def layer_algorithmic_bytes(n, c_in, c_out, pairs):
-    """Compulsory bytes of a whole layer: coordinates in, features in, weights,
-    pair lists, bf16 output."""
-    return 16 * n + 2 * n * c_in + 2 * 27 * c_in * c_out + 8 * pairs + 2 * n * c_out
-
-
-def run_workload(name, steps, warmup, sync_build=False, algo="pairs"):
-    import numpy as np
+def run_workload(name, steps, warmup, sync_build=False, algo="pairs", copy_probe_mb=0):
     import torch
 
     import submanifold_sparse_convolution_amd as smc
@@ -62,14 +112,22 @@ def run_workload(name, steps, warmup, sync_build=False, algo="pairs"):
     x_d = dev_bf16(synth.features(w.n, c, w.seed))
     w_ds = [dev_bf16(synth.weights(c, c, w.seed, layer)) for layer in range(w.layers)]
     m = smc.KernelMap()
+    if copy_probe_mb:
+        # a plain device copy of known size: the reference for the PMC byte counters
+        a = torch.empty(copy_probe_mb << 20, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
     # weight packing, once per weight (timed on its own)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     packed = [smc.pack_weights(wd) for wd in w_ds]
     torch.cuda.synchronize()
     ev0.record()
     for _ in range(10):
-        for wd, p in zip(w_ds, packed):
-            smc.pack_weights(wd, out=p)
+        for wd, pk in zip(w_ds, packed):
+            smc.pack_weights(wd, out=pk)
     ev1.record()
     torch.cuda.synchronize()
     pack_us = ev0.elapsed_time(ev1) * 1e3 / (10 * w.layers)
@@ -101,7 +159,7 @@ def run_workload(name, steps, warmup, sync_build=False, algo="pairs"):
     wall_ms = (t1 - t0) * 1e3 / steps
     gpu_ms = ev0.elapsed_time(ev1) / steps
 
-    # second pass with per-stage HIP event timers (stream-ordered)
+    # second pass with per-kernel HIP events (stream-ordered, on the library's stream)
     m.timing(True)
     for _ in range(steps):
         step()
@@ -114,22 +172,75 @@ def run_workload(name, steps, warmup, sync_build=False, algo="pairs"):
     per_layer_us = wall_ms * 1e3 / w.layers
     flops_layer = 2.0 * pairs * c * c
     stage_us = {k: (v[0] * 1e3 / v[1] if v[1] else 0.0) for k, v in stages.items()}
-    gemm_us = stage_us["gemm"]
-    return dict(
-        workload=w, coords=coords, info=info, pairs=pairs, ms_per_step=wall_ms,
-        gpu_ms_per_step=gpu_ms, per_layer_us=per_layer_us, pack_us=pack_us,
-        tflops_effective=flops_layer * w.layers / (wall_ms * 1e-3) / 1e12,
-        stage_us=stage_us, gemm_us=gemm_us,
-        gemm_tflops=flops_layer / (gemm_us * 1e-6) / 1e12 if gemm_us else 0.0,
-        gemm_bytes=gemm_algorithmic_bytes(w.n, c, c, pairs),
-        layer_bytes=layer_algorithmic_bytes(w.n, c, c, pairs),
-    )
+    # per execution; forward stages run once per layer
+    model = {}
+    for st in ("neighbours", "mask_sort", "compact", "gemm", "centre"):
+        if stage_us.get(st, 0.0) <= 0.0:
+            continue
+        by, fl = stage_model(st, algo, info["route"], w.n, pairs, c, c)
+        us = stage_us[st]
+        model[st] = dict(us=us, bytes=by, flops=fl, gbs=by / (us * 1e-6) / 1e9,
+                         tflops=fl / (us * 1e-6) / 1e12 if fl else 0.0)
+    return dict(workload=w, coords=coords, info=info, pairs=pairs, ms_per_step=wall_ms,
+                gpu_ms_per_step=gpu_ms, per_layer_us=per_layer_us, pack_us=pack_us,
+                tflops_effective=flops_layer * w.layers / (wall_ms * 1e-3) / 1e12,
+                stage_us=stage_us, model=model, algo=algo)
+
+
+def source_digest(kernel):
+    f = KERNEL_SOURCES.get(kernel)
+    if f is None:
+        return None
+    h = hashlib.sha256()
+    for path in sorted([os.path.join(CSRC, f), os.path.join(CSRC, "gemm_common.h"),
+                        os.path.join(CSRC, "smc_internal.h")]):
+        if os.path.exists(path):
+            with open(path, "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(workload, algo, kernel):
+    """Calibrated HBM bytes per launch of `kernel`, from the committed PMC record,
+    or None (no record, or the kernel's source changed since it was taken)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_{algo}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    k = rec.get("kernels", {}).get(kernel)
+    if not k or k.get("source_digest") != source_digest(kernel):
+        return None
+    return round(k["bytes_per_launch"])
+
+
+def roofline(r):
+    """The dominant stage (largest kernel time) and its roofline."""
+    model = r["model"]
+    if not model:
+        return None
+    st = max(model, key=lambda s: model[s]["us"])
+    mo = model[st]
+    kernels = MASK_TILE_GEMM if (st == "gemm" and r["algo"] == "mask_tiles") else STAGE_KERNELS[st]
+    kernel = kernels[0] if len(kernels) == 1 else "+".join(kernels)
+    intensity = mo["flops"] / mo["bytes"] if mo["bytes"] else 0.0
+    mfma = intensity > RIDGE
+    out = {"kernel": kernel, "stage": st,
+           "bound": "mfma" if mfma else "hbm",
+           "achieved": round(mo["tflops"] if mfma else mo["gbs"], 3 if mfma else 1),
+           "peak": PEAK_BF16_TFLOPS if mfma else PEAK_HBM_GBS,
+           "unit": "TFLOP/s" if mfma else "GB/s"}
+    out["frac"] = round(out["achieved"] / out["peak"], 5)
+    out["traffic"] = traffic_for(r["workload"].name, r["algo"], kernel) if len(kernels) == 1 else None
+    out["avg_us"] = round(mo["us"], 3)
+    out["algorithmic_bytes"] = mo["bytes"]
+    out["flops_useful"] = mo["flops"]
+    out["mfma_frac_useful"] = round(mo["tflops"] / PEAK_BF16_TFLOPS, 5)
+    return out
 
 
 def cpu_baseline(name, budget_s=12.0):
     """The CPU oracle (untouched) on the same workload, repeated for ~budget_s."""
-    import numpy as np
-
     import synth
     from oracle import smconv_oracle as so
     try:
@@ -157,6 +268,69 @@ def cpu_baseline(name, budget_s=12.0):
                       f"{cores} BLAS threads"}
 
 
+def _pmc_rows(d, counter):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    rows = []
+    for fn in files:
+        with open(fn) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") == counter:
+                    rows.append((row["Kernel_Name"], float(row["Counter_Value"])))
+    return rows
+
+
+def summarize_pmc(fetch_dir, write_dir, workload, algo, copy_mb):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of every kernel, scaled by what the
+    same counters read for a plain device copy of copy_mb MiB."""
+    import re
+
+    def short(k):
+        k = k.replace("(anonymous namespace)::", "").replace("void ", "").replace("smc::", "")
+        return re.sub(r"\(.*", "", k).split("<")[0].strip()
+
+    out = {"workload": workload, "algo": algo, "copy_probe_mib": copy_mb, "kernels": {}}
+    per = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        vals = {}
+        for k, v in _pmc_rows(d, counter):
+            vals.setdefault(short(k), []).append(v)
+        per[counter] = vals
+    copy_names = [k for k in per["FETCH_SIZE"] if "copyBuffer" in k or "elementwise" in k.lower()]
+    if not copy_names:
+        raise SystemExit("no copy kernel found for the calibration")
+    cname = max(copy_names, key=lambda k: max(per["FETCH_SIZE"][k]))
+    kib = copy_mb * 1024.0
+    f_copy = max(per["FETCH_SIZE"][cname])
+    w_copy = max(per["WRITE_SIZE"].get(cname, [0.0]))
+    out["copy_kernel"] = cname
+    out["copy_fetch_kib"] = f_copy
+    out["copy_write_kib"] = w_copy
+    out["fetch_scale"] = kib / f_copy if f_copy else None
+    out["write_scale"] = kib / w_copy if w_copy else None
+    for k in sorted(set(per["FETCH_SIZE"]) | set(per["WRITE_SIZE"])):
+        if not k.startswith("k_"):
+            continue
+        fv = per["FETCH_SIZE"].get(k, [])
+        wv = per["WRITE_SIZE"].get(k, [])
+        f_avg = statistics.mean(fv) if fv else 0.0
+        w_avg = statistics.mean(wv) if wv else 0.0
+        fb = f_avg * 1024.0 * (out["fetch_scale"] or 1.0)
+        wb = w_avg * 1024.0 * (out["write_scale"] or 1.0)
+        out["kernels"][k] = {"dispatches": len(fv), "fetch_kib_raw": f_avg, "write_kib_raw": w_avg,
+                             "fetch_bytes": fb, "write_bytes": wb,
+                             "bytes_per_launch": fb + wb, "source_digest": source_digest(k)}
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_{algo}.json")
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(f"wrote {path}")
+    for k, v in out["kernels"].items():
+        print(f"  {k:22s} fetch {v['fetch_bytes'] / 1e6:9.3f} MB  write {v['write_bytes'] / 1e6:9.3f} MB"
+              f"  ({v['dispatches']} dispatches)")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -169,9 +343,18 @@ def main():
     ap.add_argument("--sync-build", action="store_true",
                     help="wait for the map's device-side checks inside every step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-algo", action="store_true")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (PMC calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--report", default="",
                     help="also run every workload and write their figures to this JSON file")
     args = ap.parse_args()
+
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.algo,
+                      args.copy_probe_mb or 256)
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
@@ -184,12 +367,10 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
 
-    r = run_workload(args.workload, args.steps, args.warmup, args.sync_build, args.algo)
-    other = "mask_tiles" if args.algo == "pairs" else "pairs"
-    r2 = run_workload(args.workload, args.steps, args.warmup, args.sync_build, other)
+    r = run_workload(args.workload, args.steps, args.warmup, args.sync_build, args.algo,
+                     args.copy_probe_mb)
     w, info = r["workload"], r["info"]
     c = w.channels
-    gemm_gbs = r["gemm_bytes"] / (r["gemm_us"] * 1e-6) / 1e9 if r["gemm_us"] else 0.0
     line = {
         "metric": METRIC,
         "value": round(r["per_layer_us"], 2),
@@ -215,26 +396,20 @@ def main():
         "frac_bf16_peak": round(r["tflops_effective"] / PEAK_BF16_TFLOPS, 5),
         "gpu_ms_per_step_events": round(r["gpu_ms_per_step"], 4),
         "stage_us": {k: round(v, 2) for k, v in r["stage_us"].items()},
+        "stages": {k: {"us": round(v["us"], 2), "GB/s": round(v["gbs"], 1),
+                       "hbm_frac": round(v["gbs"] / PEAK_HBM_GBS, 4),
+                       "TFLOP/s": round(v["tflops"], 2)} for k, v in r["model"].items()},
         "weight_pack_us": round(r["pack_us"], 2),
-        "roofline": {
-            "kernel": "k_gemm (gather -> mfma_f32_16x16x32_bf16 -> atomic scatter)",
-            "bound": "hbm",
-            "achieved": round(gemm_gbs, 1),
-            "peak": PEAK_HBM_GBS,
-            "unit": "GB/s",
-            "frac": round(gemm_gbs / PEAK_HBM_GBS, 4),
-            "traffic": None,
-            "avg_us": round(r["gemm_us"], 3),
-            "algorithmic_bytes": r["gemm_bytes"],
-            "mfma_tflops_useful": round(r["gemm_tflops"], 2),
-            "mfma_frac_useful": round(r["gemm_tflops"] / PEAK_BF16_TFLOPS, 5),
-        },
+        "roofline": roofline(r),
     }
-    line["other_algo"] = {
-        "algo": other, "us_per_layer": round(r2["per_layer_us"], 2),
-        "tflops_effective": round(r2["tflops_effective"], 3),
-        "stage_us": {k: round(v, 2) for k, v in r2["stage_us"].items()},
-    }
+    if not args.no_other_algo:
+        other = "mask_tiles" if args.algo == "pairs" else "pairs"
+        r2 = run_workload(args.workload, args.steps, args.warmup, args.sync_build, other)
+        line["other_algo"] = {
+            "algo": other, "us_per_layer": round(r2["per_layer_us"], 2),
+            "tflops_effective": round(r2["tflops_effective"], 3),
+            "stage_us": {k: round(v, 2) for k, v in r2["stage_us"].items()},
+        }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.workload)
     if args.report:
@@ -244,10 +419,10 @@ def main():
                 rr = run_workload(name, max(20, args.steps // 2), args.warmup, algo=algo)
                 key = f"{name}/{algo}"
                 rep[key] = {k: rr[k] for k in ("pairs", "ms_per_step", "per_layer_us", "pack_us",
-                                               "tflops_effective", "stage_us", "gemm_us",
-                                               "gemm_tflops", "gemm_bytes", "layer_bytes")}
+                                               "tflops_effective", "stage_us", "model")}
                 rep[key]["route"] = rr["info"]["route"]
                 rep[key]["n"] = rr["workload"].n
+                rep[key]["roofline"] = roofline(rr)
         with open(args.report, "w") as f:
             json.dump(rep, f, indent=1)
     print(json.dumps(line), flush=True)

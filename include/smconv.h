@@ -229,9 +229,11 @@ enum {
 };
 
 /*
- * Turn per-stage timing on or off for one handle. While on, every build and
- * forward records a pair of HIP events around each stage on the stream it
- * runs on (the events add no kernels). Off by default.
+ * Turn per-stage timing on or off for one handle. While on, every kernel a
+ * stage launches carries its own start/stop HIP events, stamped by the
+ * kernel's dispatch (hipExtLaunchKernel), so a stage's time is the sum of
+ * its kernels' durations; SMC_STAGE_MAP instead brackets the whole build
+ * with one event pair (gaps between kernels included). Off by default.
  */
 int smc_timing_enable(smc_map* map, int on);
 

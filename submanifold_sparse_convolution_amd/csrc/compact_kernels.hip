@@ -318,7 +318,7 @@ hipError_t launch_mask_hist(const uint32_t* mask, int64_t n, const SortPlan& pla
                             int32_t* grid, hipStream_t s) {
     unsigned blocks = (unsigned)((n + kHTile - 1) / kHTile);
     size_t lds = ((size_t)plan.passes * (1u << plan.bits) + kTaps) * 4;
-    k_mask_hist<<<blocks, kHThreads, lds, s>>>(mask, n, plan.bits, plan.passes, hist, tap_tot,
+    launch(k_mask_hist, blocks, kHThreads, lds, s, mask, n, plan.bits, plan.passes, hist, tap_tot,
                                                coords, g, grid);
     return hipGetLastError();
 }
@@ -334,7 +334,7 @@ hipError_t launch_compact(const uint32_t* mask, const int32_t* nbr, int64_t n, i
     uint32_t epoch = ++ws.epoch & 0x3FFFFFFFu;
     if (epoch == 0) epoch = ++ws.epoch & 0x3FFFFFFFu;
     unsigned blocks = (unsigned)compact_chunks(n);
-    k_compact<<<blocks, kCThreads, 0, s>>>(mask, nbr, n, cap, tile_m, st, pair_in, pair_out,
+    launch(k_compact, blocks, kCThreads, 0, s, mask, nbr, n, cap, tile_m, st, pair_in, pair_out,
                                            pair_slot, rowbase, ws.look, ws.ticket, epoch, status,
                                            coords, g, grid);
     return hipGetLastError();

@@ -433,10 +433,10 @@ void launch_nc_t(dim3 grid, hipStream_t s, const uint16_t* x, int c_in, int step
                  const MapState* st, int64_t cap, int64_t n, float* part) {
     const size_t lds = (size_t)steps * NBW * 1024;
     if (allow_lds(k_gemm_nc<NBW, true, VEC>, lds))
-        k_gemm_nc<NBW, true, VEC><<<grid, kGemmThreads, lds, s>>>(x, c_in, steps, wp, n_wt, c_out,
+        launch(k_gemm_nc<NBW, true, VEC>, grid, kGemmThreads, lds, s, x, c_in, steps, wp, n_wt, c_out,
                                                                   pi, ps, st, cap, n, part);
     else
-        k_gemm_nc<NBW, false, VEC><<<grid, kGemmThreads, 0, s>>>(x, c_in, steps, wp, n_wt, c_out,
+        launch(k_gemm_nc<NBW, false, VEC>, grid, kGemmThreads, 0, s, x, c_in, steps, wp, n_wt, c_out,
                                                                  pi, ps, st, cap, n, part);
 }
 
@@ -456,10 +456,10 @@ void launch_centre_t(dim3 grid, hipStream_t s, const uint16_t* x, int c_in, int 
                      const int32_t* rowbase, int64_t n, const float* part, void* y, int relu) {
     const size_t lds = (size_t)steps * NBW * 1024;
     if (allow_lds(k_gemm_centre<NBW, MW, OUT_F32, true, VEC>, lds))
-        k_gemm_centre<NBW, MW, OUT_F32, true, VEC><<<grid, kGemmThreads, lds, s>>>(
+        launch(k_gemm_centre<NBW, MW, OUT_F32, true, VEC>, grid, kGemmThreads, lds, s, 
             x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, relu);
     else
-        k_gemm_centre<NBW, MW, OUT_F32, false, VEC><<<grid, kGemmThreads, 0, s>>>(
+        launch(k_gemm_centre<NBW, MW, OUT_F32, false, VEC>, grid, kGemmThreads, 0, s, 
             x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, relu);
 }
 
@@ -492,7 +492,7 @@ hipError_t launch_weight_pack(const uint16_t* w, int c_in, int c_out, void* out,
     int n_wt = (c_out + 16 * nbw - 1) / (16 * nbw);
     int64_t total = (int64_t)kTaps * n_wt * steps * nbw * 64;
     unsigned blocks = (unsigned)((total + kBlock - 1) / kBlock);
-    k_weight_pack<<<blocks, kBlock, 0, s>>>(w, c_in, c_out, nbw, n_wt, steps, (uint4*)out);
+    launch(k_weight_pack, blocks, kBlock, 0, s, w, c_in, c_out, nbw, n_wt, steps, (uint4*)out);
     return hipGetLastError();
 }
 

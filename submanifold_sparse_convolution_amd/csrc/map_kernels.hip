@@ -251,7 +251,7 @@ hipError_t launch_state_init(MapState* st, uint32_t* hist, int hist_ints, hipStr
     unsigned blocks = (unsigned)((hist_ints + kBlock - 1) / kBlock);
     if (blocks < 1) blocks = 1;
     if (blocks > 64) blocks = 64;
-    k_state_init<<<blocks, kBlock, 0, s>>>(st, hist, hist_ints);
+    launch(k_state_init, blocks, kBlock, 0, s, st, hist, hist_ints);
     return hipGetLastError();
 }
 
@@ -259,7 +259,7 @@ hipError_t launch_bbox(const int32_t* coords, int64_t n, int ncols, MapState* st
     unsigned blocks = (unsigned)((n + 8 * kBlock - 1) / (8 * kBlock));
     if (blocks < 1) blocks = 1;
     if (blocks > 256) blocks = 256;
-    k_bbox<<<blocks, kBlock, 0, s>>>(coords, n, ncols, st);
+    launch(k_bbox, blocks, kBlock, 0, s, coords, n, ncols, st);
     return hipGetLastError();
 }
 
@@ -267,28 +267,28 @@ hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s) {
     if (n <= 0) return hipSuccess;
     unsigned blocks = blocks_for(n);
     if (blocks > 65536) blocks = 65536;
-    k_fill_i32<<<blocks, kBlock, 0, s>>>(p, n, v);
+    launch(k_fill_i32, blocks, kBlock, 0, s, p, n, v);
     return hipGetLastError();
 }
 
 hipError_t launch_dense_scatter(const int32_t* coords, int64_t n, const Geom& g, int32_t* grid,
                                 MapState* st, const NextRecord& next, hipStream_t s) {
-    k_dense_scatter<<<blocks_for(n), kBlock, 0, s>>>(coords, n, g, grid, st, next);
+    launch(k_dense_scatter, blocks_for(n), kBlock, 0, s, coords, n, g, grid, st, next);
     return hipGetLastError();
 }
 
 hipError_t launch_dense_lookup(const int32_t* coords, int64_t n, const Geom& g, const int32_t* grid,
                                int32_t* nbr, uint32_t* mask, hipStream_t s) {
-    k_dense_lookup<<<blocks_for(n * 32), kBlock, 0, s>>>(coords, n, g, grid, nbr, mask);
+    launch(k_dense_lookup, blocks_for(n * 32), kBlock, 0, s, coords, n, g, grid, nbr, mask);
     return hipGetLastError();
 }
 
 hipError_t launch_make_keys(const int32_t* coords, int64_t n, const Geom& g, bool wide, void* keys,
                             MapState* st, const NextRecord& next, hipStream_t s) {
     if (wide)
-        k_make_keys<uint64_t><<<blocks_for(n), kBlock, 0, s>>>(coords, n, g, (uint64_t*)keys, st, next);
+        launch(k_make_keys<uint64_t>, blocks_for(n), kBlock, 0, s, coords, n, g, (uint64_t*)keys, st, next);
     else
-        k_make_keys<uint32_t><<<blocks_for(n), kBlock, 0, s>>>(coords, n, g, (uint32_t*)keys, st, next);
+        launch(k_make_keys<uint32_t>, blocks_for(n), kBlock, 0, s, coords, n, g, (uint32_t*)keys, st, next);
     return hipGetLastError();
 }
 
@@ -296,10 +296,10 @@ hipError_t launch_sorted_lookup(const void* keys, const uint32_t* vals, int64_t 
                                 bool wide, int32_t* nbr, uint32_t* mask, MapState* st,
                                 hipStream_t s) {
     if (wide)
-        k_sorted_lookup<uint64_t><<<blocks_for(n * 16), kBlock, 0, s>>>(
+        launch(k_sorted_lookup<uint64_t>, blocks_for(n * 16), kBlock, 0, s, 
             (const uint64_t*)keys, vals, n, g, nbr, mask, st);
     else
-        k_sorted_lookup<uint32_t><<<blocks_for(n * 16), kBlock, 0, s>>>(
+        launch(k_sorted_lookup<uint32_t>, blocks_for(n * 16), kBlock, 0, s, 
             (const uint32_t*)keys, vals, n, g, nbr, mask, st);
     return hipGetLastError();
 }

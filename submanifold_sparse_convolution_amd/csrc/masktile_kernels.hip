@@ -376,7 +376,7 @@ hipError_t launch_mt(dim3 grid, hipStream_t s, const uint16_t* x, int c_in, int 
     }
     attr_ok = true;
     grid.z = NBW / nbh_for(NBW);
-    k_conv_masktile<NBW, OUT_F32, VEC><<<grid, kGemmThreads, lds, s>>>(
+    launch(k_conv_masktile<NBW, OUT_F32, VEC>, grid, kGemmThreads, lds, s, 
         x, c_in, steps, wp, n_wt, c_out, nbr, mask, perm, n, zrow, y, relu, kMaxLightItems);
     return hipGetLastError();
 }

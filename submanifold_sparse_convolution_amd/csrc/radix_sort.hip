@@ -225,7 +225,7 @@ hipError_t launch_pass(const K* kin, const uint32_t* vin, K* kout, uint32_t* vou
                        int shift, const uint32_t* hist, uint64_t* look, uint32_t* ticket,
                        uint32_t epoch, uint32_t* status, hipStream_t s) {
     unsigned blocks = (unsigned)((n + kOsTile - 1) / kOsTile);
-    k_os_pass<K, BITS><<<blocks, kOsThreads, 0, s>>>(kin, vin, kout, vout, n, shift, hist, look,
+    launch(k_os_pass<K, BITS>, blocks, kOsThreads, 0, s, kin, vin, kout, vout, n, shift, hist, look,
                                                      ticket, epoch, status);
     return hipGetLastError();
 }
@@ -283,10 +283,10 @@ hipError_t launch_key_hist(const void* keys, bool wide, int64_t n, const SortPla
     unsigned blocks = (unsigned)((n + kOsTile - 1) / kOsTile);
     size_t lds = (size_t)plan.passes * (1u << plan.bits) * 4;
     if (wide)
-        k_key_hist<uint64_t><<<blocks, kOsThreads, lds, s>>>((const uint64_t*)keys, n, plan.bits,
+        launch(k_key_hist<uint64_t>, blocks, kOsThreads, lds, s, (const uint64_t*)keys, n, plan.bits,
                                                              plan.passes, hist);
     else
-        k_key_hist<uint32_t><<<blocks, kOsThreads, lds, s>>>((const uint32_t*)keys, n, plan.bits,
+        launch(k_key_hist<uint32_t>, blocks, kOsThreads, lds, s, (const uint32_t*)keys, n, plan.bits,
                                                              plan.passes, hist);
     return hipGetLastError();
 }

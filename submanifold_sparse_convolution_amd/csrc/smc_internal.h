@@ -1,6 +1,7 @@
 // Internal declarations shared by the library's HIP sources (not installed).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -10,6 +11,26 @@ constexpr int kTaps = 27;
 constexpr int kCentre = 13;
 constexpr int kTileM = 64;          // pairs per GEMM tile (4 waves x 16 rows)
 constexpr int kBlock = 256;         // threads per block for the map kernels
+
+// Per-kernel timing. While a stage timer of the API is active, take() hands
+// out a start/stop event pair for every kernel launched, and the launch
+// carries them (hipExtLaunchKernel: the events are stamped by the kernel's
+// own dispatch, so they time the kernel and nothing around it).
+struct KernelTimer {
+    void* ctx = nullptr;
+    bool (*take)(void* ctx, hipEvent_t* start, hipEvent_t* stop) = nullptr;
+};
+extern thread_local KernelTimer g_ktimer;
+
+// Every kernel of the library is launched through here.
+template <typename... P, typename... A>
+inline void launch(void (*kern)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                   A... args) {
+    static_assert(sizeof...(P) == sizeof...(A), "argument count");
+    hipEvent_t a = nullptr, b = nullptr;
+    if (g_ktimer.take && !g_ktimer.take(g_ktimer.ctx, &a, &b)) a = b = nullptr;
+    hipExtLaunchKernelGGL(kern, grid, block, (uint32_t)lds, s, a, b, 0u, static_cast<P>(args)...);
+}
 
 // bits of the device status word
 enum : uint32_t { kStDuplicate = 1u, kStRange = 2u, kStSortStall = 4u };

@@ -12,6 +12,10 @@
 
 using namespace smc;
 
+namespace smc {
+thread_local KernelTimer g_ktimer;
+}
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -120,6 +124,7 @@ struct smc_map {
     std::vector<std::pair<hipEvent_t, hipEvent_t>> ev_open[SMC_STAGE_COUNT];
     double stage_ms[SMC_STAGE_COUNT] = {};
     int64_t stage_calls[SMC_STAGE_COUNT] = {};
+    int64_t stage_exec[SMC_STAGE_COUNT] = {};   // timed executions not yet read
 };
 
 namespace {
@@ -198,44 +203,76 @@ int ensure_grid(smc_map* m, int64_t cells, hipStream_t s) {
     return SMC_OK;
 }
 
-// Records the start event of a stage on construction and the end event on
-// finish(); does nothing while timing is off.
+hipEvent_t take_event(smc_map* m) {
+    if (!m->ev_pool.empty()) {
+        hipEvent_t e = m->ev_pool.back();
+        m->ev_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    return e;
+}
+
+// Stage timer (only while timing is on). Kernel mode: every kernel launched
+// while the timer is active carries its own start/stop events, and the
+// stage's time is the sum of its kernels' durations. Bracket mode (the whole
+// build): one event before and one after, gaps between kernels included.
 struct StageTimer {
     smc_map* m;
     int stage;
     hipStream_t s;
+    bool bracket;
+    bool active = false;
     hipEvent_t a = nullptr;
-    static hipEvent_t take(smc_map* m) {
-        if (!m->ev_pool.empty()) {
-            hipEvent_t e = m->ev_pool.back();
-            m->ev_pool.pop_back();
-            return e;
+    KernelTimer saved;
+    static bool take_pair(void* ctx, hipEvent_t* e0, hipEvent_t* e1) {
+        StageTimer* t = static_cast<StageTimer*>(ctx);
+        hipEvent_t x = take_event(t->m), y = take_event(t->m);
+        if (!x || !y) {
+            if (x) t->m->ev_pool.push_back(x);
+            if (y) t->m->ev_pool.push_back(y);
+            return false;
         }
-        hipEvent_t e = nullptr;
-        if (hipEventCreate(&e) != hipSuccess) {
-            (void)hipGetLastError();
-            return nullptr;
-        }
-        return e;
+        t->m->ev_open[t->stage].push_back({x, y});
+        *e0 = x;
+        *e1 = y;
+        return true;
     }
-    StageTimer(smc_map* m_, int stage_, hipStream_t s_) : m(m_), stage(stage_), s(s_) {
+    StageTimer(smc_map* m_, int stage_, hipStream_t s_, bool bracket_ = false)
+        : m(m_), stage(stage_), s(s_), bracket(bracket_) {
         if (!m->timing) return;
-        a = take(m);
-        if (a) (void)hipEventRecord(a, s);
-    }
-    ~StageTimer() {
-        if (a) m->ev_pool.push_back(a);
-    }
-    void finish() {
-        if (!a) return;
-        hipEvent_t b = take(m);
-        if (b) {
-            (void)hipEventRecord(b, s);
-            m->ev_open[stage].push_back({a, b});
+        active = true;
+        if (bracket) {
+            a = take_event(m);
+            if (a) (void)hipEventRecord(a, s);
         } else {
-            m->ev_pool.push_back(a);
+            saved = g_ktimer;
+            g_ktimer.ctx = this;
+            g_ktimer.take = &take_pair;
         }
-        a = nullptr;
+    }
+    ~StageTimer() { finish(); }
+    void finish() {
+        if (!active) return;
+        active = false;
+        if (bracket) {
+            if (!a) return;
+            hipEvent_t b = take_event(m);
+            if (b) {
+                (void)hipEventRecord(b, s);
+                m->ev_open[stage].push_back({a, b});
+            } else {
+                m->ev_pool.push_back(a);
+            }
+            a = nullptr;
+        } else {
+            g_ktimer = saved;
+        }
+        m->stage_exec[stage] += 1;
     }
 };
 
@@ -330,7 +367,7 @@ int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     next.st = m->state.as<MapState>() + (slot ^ 1);
     next.hist = m->hist.as<uint32_t>() + (slot ^ 1) * kHistInts;
     next.hist_ints = kHistInts;
-    StageTimer t_map(m, SMC_STAGE_MAP, s);
+    StageTimer t_map(m, SMC_STAGE_MAP, s, /*bracket=*/true);
     if (!m->slot_clean[slot]) SMC_HIP(launch_state_init(st, hist_mask, kHistInts, s));
     if (n > 0) m->slot_clean[slot] = false;
 
@@ -681,11 +718,12 @@ int smc_timing_read(smc_map* m, double* ms, int64_t* calls, int reset) {
             float e = 0.f;
             SMC_HIP(hipEventElapsedTime(&e, pr.first, pr.second));
             m->stage_ms[st] += e;
-            m->stage_calls[st] += 1;
             m->ev_pool.push_back(pr.first);
             m->ev_pool.push_back(pr.second);
         }
         m->ev_open[st].clear();
+        m->stage_calls[st] += m->stage_exec[st];
+        m->stage_exec[st] = 0;
         if (ms) ms[st] = m->stage_ms[st];
         if (calls) calls[st] = m->stage_calls[st];
         if (reset) {
