@@ -26,8 +26,7 @@ constexpr int kHItems = 4;
 constexpr int kHTile = kHThreads * kHItems;       // rows per histogram block
 constexpr int kCThreads = 256;
 constexpr int kCWaves = kCThreads / 64;
-constexpr int kCItems = 2;
-constexpr int kCChunk = kCThreads * kCItems;      // rows per compaction block
+constexpr int kCChunk = kCThreads;                // rows per compaction block (one per thread)
 constexpr int kCNbrVec = kCChunk * kTaps / 4;     // 16-byte words of the chunk's neighbour rows
 constexpr int kCNbrPer = (kCNbrVec + kCThreads - 1) / kCThreads;
 constexpr uint32_t kSpinLimit = 1u << 22;
@@ -38,21 +37,22 @@ __device__ inline uint64_t lb_pack(uint32_t epoch, uint64_t state, uint32_t coun
 }
 
 // Sum of column d of the look-back table over blocks pb, pb-1, ... back to
-// the first inclusive entry (8 loads per round trip).
-__device__ inline uint32_t lookback8(uint64_t* look, int stride, int d, int64_t pb,
-                                     uint32_t epoch, uint32_t* status) {
+// the first inclusive entry (W loads per round trip).
+template <int W>
+__device__ inline uint32_t lookback(uint64_t* look, int stride, int d, int64_t pb, uint32_t epoch,
+                                    uint32_t* status) {
     const uint32_t ep = epoch & 0x3FFFFFFFu;
     uint32_t prefix = 0;
     uint32_t spins = 0;
     while (pb >= 0) {
-        uint64_t e[8];
+        uint64_t e[W];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < W; ++j)
             e[j] = pb - j >= 0 ? __hip_atomic_load(&look[(pb - j) * stride + d], __ATOMIC_RELAXED,
                                                    __HIP_MEMORY_SCOPE_AGENT)
                                : 0;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < W; ++j) {
             if (pb - j < 0) return prefix;
             while ((uint32_t)(e[j] >> 34) != ep) {
                 if (++spins > kSpinLimit) {
@@ -66,9 +66,79 @@ __device__ inline uint32_t lookback8(uint64_t* look, int stride, int d, int64_t 
             prefix += (uint32_t)e[j];
             if (((e[j] >> 32) & 3u) == kIncl) return prefix;
         }
-        pb -= 8;
+        pb -= W;
     }
     return prefix;
+}
+
+// Prefix of column k (k < NC) over blocks pb, pb-1, ..., read by the whole
+// block: thread t < 9 NC covers column t % NC and every 9th predecessor
+// starting at pb - t / NC, W of them per round trip (72 predecessors per
+// column per round). A round finds, per column, the nearest entry that
+// holds an inclusive prefix (LDS minimum of the distance), and sums the
+// entries up to and including it; columns without one go on to the next
+// round. Every thread of the block must call this. The result is in
+// s_sum[k] on return.
+template <int NC, int W>
+__device__ void block_lookback(uint64_t* look, int64_t pb, uint32_t epoch, uint32_t* status,
+                               uint32_t* s_sum, uint32_t* s_near, uint32_t* s_done) {
+    constexpr int kLanes = 9;                     // threads per column
+    const int tid = threadIdx.x;
+    const int k = tid % NC, j0 = tid / NC;
+    const bool active = tid < kLanes * NC;
+    const uint32_t ep = epoch & 0x3FFFFFFFu;
+    if (tid < NC) {
+        s_sum[tid] = 0;
+        s_done[tid] = pb < 0 ? 1u : 0u;
+    }
+    __syncthreads();
+    uint32_t spins = 0;
+    for (int64_t top = pb; top >= 0; top -= kLanes * W) {
+        if (tid < NC) s_near[tid] = 0xFFFFFFFFu;
+        __syncthreads();
+        const bool go = active && !s_done[k];
+        uint64_t e[W];
+        uint32_t near = 0xFFFFFFFFu;
+#pragma unroll
+        for (int j = 0; j < W; ++j) {
+            const int64_t idx = top - j0 - (int64_t)j * kLanes;
+            e[j] = 0;
+            if (go && idx >= 0)
+                e[j] = __hip_atomic_load(&look[idx * NC + k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int j = 0; j < W; ++j) {
+            const int64_t idx = top - j0 - (int64_t)j * kLanes;
+            if (!go || idx < 0) continue;
+            while ((uint32_t)(e[j] >> 34) != ep) {
+                if (++spins > kSpinLimit) {
+                    atomicOr(status, kStSortStall);
+                    e[j] = 0;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+                e[j] = __hip_atomic_load(&look[idx * NC + k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            if (((e[j] >> 32) & 3u) == kIncl) near = min(near, (uint32_t)(top - idx));
+        }
+        if (go && near != 0xFFFFFFFFu) atomicMin(&s_near[k], near);
+        __syncthreads();
+        const uint32_t lim = go ? s_near[k] : 0u;
+        uint32_t part = 0;
+#pragma unroll
+        for (int j = 0; j < W; ++j) {
+            const int64_t idx = top - j0 - (int64_t)j * kLanes;
+            if (go && idx >= 0 && (uint32_t)(top - idx) <= lim) part += (uint32_t)e[j];
+        }
+        if (part) atomicAdd(&s_sum[k], part);
+        __syncthreads();
+        if (tid < NC && !s_done[tid] && (s_near[tid] != 0xFFFFFFFFu || top - kLanes * W < 0))
+            s_done[tid] = 1u;
+        __syncthreads();
+        bool all = true;
+        for (int q = 0; q < NC; ++q) all = all && s_done[q];
+        if (all) break;
+    }
 }
 
 // One read of the masks: digit histograms of every mask-sort pass, pairs per
@@ -127,12 +197,13 @@ __global__ __launch_bounds__(kHThreads) void k_mask_hist(const uint32_t* __restr
     if (threadIdx.x < kTaps && s_tap[threadIdx.x]) atomicAdd(&tap_tot[threadIdx.x], (int32_t)s_tap[threadIdx.x]);
 }
 
-// Rows [bid*kCChunk, +kCChunk) in row order. Wave w owns a contiguous
-// quarter; for each tap (and for the slab rows, column kTaps) the block
-// counts its rows, finds the count of earlier chunks by look-back, and
-// writes its pairs. The chunk's neighbour rows (contiguous in the table) are
-// read once, coalesced, into LDS at the start, so the pair writes read LDS
-// only. The last chunk publishes the totals.
+// Rows [bid*kCChunk, +kCChunk) in row order, one per thread. For each tap
+// (and for the slab rows, column kTaps) the block counts its rows, finds the
+// count of earlier chunks by look-back and writes its pairs. The chunk's
+// neighbour rows (contiguous in the table) are read once, coalesced, into
+// LDS at the start; the chunk's pairs are first listed in LDS as (row, tap)
+// entries in output order, then written out with consecutive threads on
+// consecutive pair positions. The last chunk publishes the totals.
 __global__ __launch_bounds__(kCThreads) void k_compact(
     const uint32_t* __restrict__ mask, const int32_t* __restrict__ nbr, int64_t n, int64_t cap,
     int tile_m, MapState* st, int32_t* __restrict__ pair_in, int32_t* __restrict__ pair_out,
@@ -143,26 +214,24 @@ __global__ __launch_bounds__(kCThreads) void k_compact(
     __shared__ uint32_t s_bid;
     __shared__ uint32_t s_wc[kCWaves][kCols];     // per-wave counts, then offsets in the chunk
     __shared__ uint32_t s_pre[kCols];             // counts of earlier chunks
-    __shared__ uint32_t s_tot[kCols];             // totals (last chunk only)
+    __shared__ uint32_t s_loc[kCols];             // chunk-local start of each tap's pairs
+    __shared__ uint32_t s_tot[kCols];             // the chunk's own counts
+    __shared__ uint32_t s_near[kCols], s_done[kCols];   // look-back scratch
     __shared__ int4 s_nb4[kCNbrVec];              // the chunk's neighbour rows [kCChunk][kTaps]
+    __shared__ uint16_t s_list[kCChunk * kTaps];  // (row | tap << 8) in output order
+    __shared__ uint32_t s_m[kCChunk], s_rb[kCChunk];
     const int32_t* s_nb = reinterpret_cast<const int32_t*>(s_nb4);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     if (tid == 0) s_bid = atomicAdd(ticket, 1u);
     __syncthreads();
     const uint32_t bid = s_bid;
     const int64_t base0 = (int64_t)bid * kCChunk;
-    const int64_t base = base0 + (int64_t)w * (kCChunk / kCWaves);
+    const int64_t row = base0 + tid;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
-    // loads: masks, neighbour rows (whole 16-byte words; the table is padded so the last
+    // loads: mask, neighbour rows (whole 16-byte words; the table is padded so the last
     // word of the last row is readable), coordinates for the grid cleanup
-    uint32_t m[kCItems], deg[kCItems];
-#pragma unroll
-    for (int i = 0; i < kCItems; ++i) {
-        const int64_t r = base + i * 64 + lane;
-        const uint32_t mv = mask[r < n ? r : n - 1];
-        m[i] = r < n ? mv : 0u;
-    }
+    const uint32_t mv = mask[row < n ? row : n - 1];
     int4 nv4[kCNbrPer];
     {
         const int4* src = reinterpret_cast<const int4*>(nbr + base0 * kTaps);
@@ -173,43 +242,30 @@ __global__ __launch_bounds__(kCThreads) void k_compact(
             nv4[j] = src[q < q_last ? q : q_last];
         }
     }
-    int4 cq[kCItems];                             // (b, x, y, z) of the rows
+    int4 cq = make_int4(0, 0, 0, 0);              // (b, x, y, z) of the row
     if (grid) {
-#pragma unroll
-        for (int i = 0; i < kCItems; ++i) {
-            const int32_t* c = coords + min(base + i * 64 + lane, n - 1) * g.ncols;
-            cq[i] = g.ncols == 4 ? make_int4(c[0], c[1], c[2], c[3]) : make_int4(0, c[0], c[1], c[2]);
-        }
+        const int32_t* c = coords + min(row, n - 1) * g.ncols;
+        cq = g.ncols == 4 ? make_int4(c[0], c[1], c[2], c[3]) : make_int4(0, c[0], c[1], c[2]);
     }
-#pragma unroll
-    for (int i = 0; i < kCItems; ++i) deg[i] = m[i] ? (uint32_t)__popc(m[i] & ~(1u << kCentre)) : 0u;
-    // per-wave count of each tap (lane k accumulates tap k) and of slab rows (lane kTaps)
+    const uint32_t m = row < n ? mv : 0u;
+    const uint32_t deg = m ? (uint32_t)__popc(m & ~(1u << kCentre)) : 0u;
+    // per-wave count of each tap (lane k keeps tap k) and of slab rows (lane kTaps)
     uint32_t cnt = 0;
 #pragma unroll
     for (int k = 0; k < kTaps; ++k) {
-        uint32_t c = 0;
-#pragma unroll
-        for (int i = 0; i < kCItems; ++i) c += (uint32_t)__popcll(__ballot((m[i] >> k) & 1u));
+        const uint32_t c = (uint32_t)__popcll(__ballot((m >> k) & 1u));
         if (lane == k) cnt = c;
     }
-    // inclusive wave scans of the slab rows per item
-    uint32_t incl[kCItems], item_tot[kCItems];
+    uint32_t incl = deg;                          // inclusive wave scan of the slab rows
 #pragma unroll
-    for (int i = 0; i < kCItems; ++i) {
-        uint32_t v = deg[i];
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t t = __shfl_up(v, o, 64);
-            if (lane >= o) v += t;
-        }
-        incl[i] = v;
-        item_tot[i] = __shfl(v, 63, 64);
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
     }
-    uint32_t wave_slab = 0;
-#pragma unroll
-    for (int i = 0; i < kCItems; ++i) wave_slab += item_tot[i];
+    const uint32_t wave_slab = __shfl(incl, 63, 64);
     if (lane < kTaps) s_wc[w][lane] = cnt;
     if (lane == kTaps) s_wc[w][kTaps] = wave_slab;
+    s_m[tid] = m;
 #pragma unroll
     for (int j = 0; j < kCNbrPer; ++j) {
         const int q = tid + j * kCThreads;
@@ -225,20 +281,22 @@ __global__ __launch_bounds__(kCThreads) void k_compact(
             s_wc[v][k] = run;
             run += c;
         }
+        s_tot[k] = run;                           // the chunk's own count, for now
         __hip_atomic_store(&look[(int64_t)bid * kCols + k],
                            lb_pack(epoch, bid == 0 ? kIncl : kAgg, run), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
-        uint32_t prefix = 0;
-        if (bid > 0) {
-            prefix = lookback8(look, kCols, k, (int64_t)bid - 1, epoch, status);
+    }
+    block_lookback<kCols, 8>(look, (int64_t)bid - 1, epoch, status, s_pre, s_near, s_done);
+    if (tid < kCols) {
+        const int k = tid;
+        const uint32_t run = s_tot[k];
+        const uint32_t prefix = s_pre[k];
+        if (bid > 0)
             __hip_atomic_store(&look[(int64_t)bid * kCols + k], lb_pack(epoch, kIncl, prefix + run),
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        s_pre[k] = prefix;
         if (bid == gridDim.x - 1) {
             // the last chunk: prefix + run is the total of column k
             const uint32_t tot = prefix + run;
-            s_tot[k] = tot;
             if (k < kTaps) {
                 st->tap_count[k] = (int32_t)tot;
                 st->tap_off[k] = (int32_t)(k * cap);
@@ -249,64 +307,58 @@ __global__ __launch_bounds__(kCThreads) void k_compact(
         }
     }
     __syncthreads();
-    if (bid == gridDim.x - 1 && tid == 0) {
+    if (tid == 0) {                               // chunk-local tap starts, totals
+        uint32_t loc = 0;
         int32_t p = 0, padded = 0;
         for (int k = 0; k < kTaps; ++k) {
-            const int32_t c = (int32_t)s_tot[k];
+            s_loc[k] = loc;
+            loc += s_tot[k];
+            const int32_t c = (int32_t)(s_pre[k] + s_tot[k]);
             p += c;
             padded += (c + tile_m - 1) / tile_m * tile_m;
         }
-        st->totals[0] = p;
-        st->totals[1] = padded;
-        st->totals[2] = padded / tile_m;
-    }
-    // first slab row of every row
-    uint32_t rb[kCItems];
-    {
-        uint32_t off = s_pre[kTaps] + s_wc[w][kTaps];
-#pragma unroll
-        for (int i = 0; i < kCItems; ++i) {
-            rb[i] = off + incl[i] - deg[i];
-            off += item_tot[i];
-            const int64_t r = base + i * 64 + lane;
-            if (r < n) rowbase[r] = (int32_t)rb[i];
+        s_loc[kTaps] = loc;
+        if (bid == gridDim.x - 1) {
+            st->totals[0] = p;
+            st->totals[1] = padded;
+            st->totals[2] = padded / tile_m;
         }
     }
-    // pairs, tap by tap (the centre's input row is the row itself)
+    // first slab row of the row
+    const uint32_t rb = s_pre[kTaps] + s_wc[w][kTaps] + incl - deg;
+    if (row < n) rowbase[row] = (int32_t)rb;
+    s_rb[tid] = rb;
+    __syncthreads();
+    // list the chunk's pairs in output order: tap-major, rows ascending
 #pragma unroll
     for (int k = 0; k < kTaps; ++k) {
-        const int64_t start = (int64_t)k * cap + s_pre[k] + s_wc[w][k];
-        const int64_t lim = (int64_t)k * cap + cap;
-        const uint32_t lower = (1u << k) - 1u;
-        uint32_t run = 0;
-#pragma unroll
-        for (int i = 0; i < kCItems; ++i) {
-            const uint64_t b = __ballot((m[i] >> k) & 1u);
-            const int lr = w * (kCChunk / kCWaves) + i * 64 + lane;   // row within the chunk
-            if ((m[i] >> k) & 1u) {
-                const int64_t pos = start + run + (uint32_t)__popcll(b & below);
-                if (pos < lim) {                   // false only after a stalled wait
-                    pair_in[pos] = k == kCentre ? (int32_t)(base0 + lr) : s_nb[lr * kTaps + k];
-                    pair_out[pos] = (int32_t)(base0 + lr);
-                    pair_slot[pos] = k == kCentre
-                                         ? -1
-                                         : (int32_t)(rb[i] + __popc(m[i] & lower & ~(1u << kCentre)));
-                }
-            }
-            run += (uint32_t)__popcll(b);
-        }
+        const uint64_t b = __ballot((m >> k) & 1u);
+        if ((m >> k) & 1u)
+            s_list[s_loc[k] + s_wc[w][k] + (uint32_t)__popcll(b & below)] =
+                (uint16_t)(tid | (k << 8));
     }
-    // dense route: the grid cells of these rows go back to empty (every lookup has finished)
+    __syncthreads();
+    // write them out: entry p of tap k goes to k cap + (pairs of k in earlier chunks) + its rank
+    const int total = (int)s_loc[kTaps];
+    for (int p = tid; p < total; p += kCThreads) {
+        const uint32_t e = s_list[p];
+        const int lr = (int)(e & 0xFFu), k = (int)(e >> 8);
+        const int64_t pos = (int64_t)k * cap + s_pre[k] + (p - (int)s_loc[k]);
+        if (pos >= (int64_t)k * cap + cap) continue;          // only after a stalled wait
+        const uint32_t mr = s_m[lr];
+        pair_in[pos] = k == kCentre ? (int32_t)(base0 + lr) : s_nb[lr * kTaps + k];
+        pair_out[pos] = (int32_t)(base0 + lr);
+        pair_slot[pos] = k == kCentre
+                             ? -1
+                             : (int32_t)(s_rb[lr] + __popc(mr & ((1u << k) - 1u) & ~(1u << kCentre)));
+    }
+    // dense route: the grid cell of this row goes back to empty (every lookup has finished)
     if (grid) {
-#pragma unroll
-        for (int i = 0; i < kCItems; ++i) {
-            const int64_t r = base + i * 64 + lane;
-            const int b = cq[i].x;
-            const int x = cq[i].y - g.origin[0], y = cq[i].z - g.origin[1], z = cq[i].w - g.origin[2];
-            if (r < n && (unsigned)b < (unsigned)g.batch && (unsigned)x < (unsigned)g.ext[0] &&
-                (unsigned)y < (unsigned)g.ext[1] && (unsigned)z < (unsigned)g.ext[2])
-                grid[b * g.sz_b + (int64_t)(x + 1) * g.sz_x + (int64_t)(y + 1) * g.sz_y + (z + 1)] = -1;
-        }
+        const int b = cq.x;
+        const int x = cq.y - g.origin[0], y = cq.z - g.origin[1], z = cq.w - g.origin[2];
+        if (row < n && (unsigned)b < (unsigned)g.batch && (unsigned)x < (unsigned)g.ext[0] &&
+            (unsigned)y < (unsigned)g.ext[1] && (unsigned)z < (unsigned)g.ext[2])
+            grid[b * g.sz_b + (int64_t)(x + 1) * g.sz_x + (int64_t)(y + 1) * g.sz_y + (z + 1)] = -1;
     }
     if (bid == gridDim.x - 1 && tid == 0) atomicExch(ticket, 0u);
 }

@@ -296,6 +296,57 @@ __device__ __forceinline__ void add_slab(const int32_t (&rb)[MW][4], const int32
     }
 }
 
+// Loads of one 64 MW-row tile: gathered rows (first k-group), raw run bounds
+// (rowbase and mask of this lane's output rows).
+template <int MW, bool VEC>
+__device__ __forceinline__ void centre_tile_loads(const uint16_t* __restrict__ x, int c_in, int steps,
+                                                  const uint32_t* __restrict__ mask,
+                                                  const int32_t* __restrict__ rowbase, int64_t n,
+                                                  int64_t row0, int r, int g,
+                                                  const uint16_t* (&xrow)[MW], u32x4 (&a)[4][MW],
+                                                  int32_t (&rb)[MW][4], uint32_t (&mk)[MW][4]) {
+#pragma unroll
+    for (int m = 0; m < MW; ++m) {
+        const int64_t ir = row0 + m * 16 + r;
+        xrow[m] = x + (ir < n ? ir : 0) * c_in;
+    }
+    load_group<MW, VEC>(xrow, c_in, steps, 0, g, a);
+#pragma unroll
+    for (int m = 0; m < MW; ++m)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t row = row0 + m * 16 + 4 * g + j;
+            const int64_t rc = row < n ? row : n - 1;
+            rb[m][j] = rowbase[rc];
+            mk[m][j] = mask[rc];
+        }
+}
+
+// Slab runs from the raw bounds: rows past n get empty runs at the end of the
+// last real row's run. Returns the lane's total slab rows.
+template <int MW>
+__device__ __forceinline__ int centre_runs(int64_t row0, int g, int64_t n, int32_t (&rb)[MW][4],
+                                           const uint32_t (&mk)[MW][4], int32_t (&re)[MW],
+                                           int32_t (&len)[MW]) {
+    int tot = 0;
+#pragma unroll
+    for (int m = 0; m < MW; ++m) {
+        int32_t e = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t row = row0 + m * 16 + 4 * g + j;
+            if (row < n) e = rb[m][j] + __popc(mk[m][j] & ~(1u << kCentre));
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (row0 + m * 16 + 4 * g + j >= n) rb[m][j] = e;
+        re[m] = e;
+        len[m] = e - rb[m][0];
+        tot += len[m];
+    }
+    return tot;
+}
+
 template <int NBW, int MW, bool OUT_F32, bool LDS, bool VEC>
 __global__ __launch_bounds__(kGemmThreads) void k_gemm_centre(
     const uint16_t* __restrict__ x, int c_in, int steps, const uint4* __restrict__ wp, int n_wt,
@@ -314,79 +365,43 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_centre(
     int64_t rt = blockIdx.x;
     if (rt >= n_rt) return;
     const uint4* src = wp + ((int64_t)kCentre * n_wt + wt_i) * n16;
-    const uint4* b = src + lane;
-    bool staged = false;
+    // the MFMAs read B from LDS (LDS) or from global memory: fixed at compile time
+    const uint4* bmma = LDS ? static_cast<const uint4*>(s_b) + lane : src + lane;
+
+    // first tile: every independent load is issued before any wait
+    const uint16_t* xrow[MW];
+    u32x4 a[4][MW];
+    int32_t rb[MW][4];
+    uint32_t mk[MW][4];
+    int64_t row0 = rt * rows_per_tile + w * 16 * MW;
+    centre_tile_loads<MW, VEC>(x, c_in, steps, mask, rowbase, n, row0, r, g, xrow, a, rb, mk);
+    u32x4 bw[8];
+    if (LDS) {                                    // first round of the weight slab
+        const u32x4* src4 = reinterpret_cast<const u32x4*>(src);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int i = threadIdx.x + j * kGemmThreads;
+            bw[j] = src4[i < n16 ? i : n16 - 1];
+        }
+    }
+    int32_t re[MW], len[MW];
+    int tot = centre_runs<MW>(row0, g, n, rb, mk, re, len);
+    float pv[kSlabBatch][NBW];
+    load_slab<NBW, MW>(part, c_out, colc, vec_part, rb, len, tot, 0, pv);
+    if (LDS) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int i = threadIdx.x + j * kGemmThreads;
+            if (i < n16) reinterpret_cast<u32x4*>(s_b)[i] = bw[j];
+        }
+        if (n16 > 8 * kGemmThreads)               // wide inputs: the remaining rounds
+            for (int i = 8 * kGemmThreads + threadIdx.x; i < n16; i += kGemmThreads) s_b[i] = src[i];
+        __syncthreads();
+    }
 
     for (;;) {
-        const int64_t row0 = rt * rows_per_tile + w * 16 * MW;
-        // gathered rows (first k-group) and raw run bounds
-        const uint16_t* xrow[MW];
-#pragma unroll
-        for (int m = 0; m < MW; ++m) {
-            const int64_t ir = row0 + m * 16 + r;
-            xrow[m] = x + (ir < n ? ir : 0) * c_in;
-        }
-        u32x4 a[4][MW];
-        load_group<MW, VEC>(xrow, c_in, steps, 0, g, a);
-        int32_t rb[MW][4];
-        uint32_t mk[MW][4];
-#pragma unroll
-        for (int m = 0; m < MW; ++m)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t row = row0 + m * 16 + 4 * g + j;
-                const int64_t rc = row < n ? row : n - 1;
-                rb[m][j] = rowbase[rc];
-                mk[m][j] = mask[rc];
-            }
-        // weights: one round of 8 words per thread is loaded here, before any wait
-        u32x4 bw[8];
-        const bool one_round = LDS && !staged && n16 <= 8 * kGemmThreads;
-        if (one_round) {
-            const u32x4* src4 = reinterpret_cast<const u32x4*>(src);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int i = threadIdx.x + j * kGemmThreads;
-                bw[j] = src4[i < n16 ? i : n16 - 1];
-            }
-        }
-        // runs: rows past n get empty runs at the end of the last real row's run
-        int32_t re[MW], len[MW];
-#pragma unroll
-        for (int m = 0; m < MW; ++m) {
-            int32_t e = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t row = row0 + m * 16 + 4 * g + j;
-                if (row < n) e = rb[m][j] + __popc(mk[m][j] & ~(1u << kCentre));
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (row0 + m * 16 + 4 * g + j >= n) rb[m][j] = e;
-            re[m] = e;
-            len[m] = e - rb[m][0];
-        }
-        int tot = 0;
-#pragma unroll
-        for (int m = 0; m < MW; ++m) tot += len[m];
-        float pv[kSlabBatch][NBW];
-        load_slab<NBW, MW>(part, c_out, colc, vec_part, rb, len, tot, 0, pv);
-        if (LDS && !staged) {
-            if (one_round) {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int i = threadIdx.x + j * kGemmThreads;
-                    if (i < n16) reinterpret_cast<u32x4*>(s_b)[i] = bw[j];
-                }
-            } else {
-                stage_b(s_b, src, n16);
-            }
-            __syncthreads();
-            b = s_b + lane;
-            staged = true;
-        }
         f32x4 c[MW][NBW];
-        wave_mma<NBW, MW, VEC>(xrow, c_in, steps, b, g, a, c);
+        wave_mma<NBW, MW, VEC>(xrow, c_in, steps, bmma, g, a, c);
         float v[MW][4][NBW];
 #pragma unroll
         for (int m = 0; m < MW; ++m)
@@ -409,6 +424,10 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_centre(
             }
         rt += gridDim.x;
         if (rt >= n_rt) break;
+        row0 = rt * rows_per_tile + w * 16 * MW;
+        centre_tile_loads<MW, VEC>(x, c_in, steps, mask, rowbase, n, row0, r, g, xrow, a, rb, mk);
+        tot = centre_runs<MW>(row0, g, n, rb, mk, re, len);
+        load_slab<NBW, MW>(part, c_out, colc, vec_part, rb, len, tot, 0, pv);
     }
 }
 
