@@ -54,9 +54,17 @@ STAGE_KERNELS = {
     "gemm": ("k_gemm_nc",),
     "centre": ("k_gemm_centre",),
 }
+# dense route with pair lists: the lookup is fused into the compaction kernel
+STAGE_KERNELS_FUSED = {
+    "neighbours": ("k_dense_scatter",),
+    "compact": ("k_lookup_compact",),
+    "gemm": ("k_gemm_nc",),
+    "centre": ("k_gemm_centre",),
+}
 MASK_TILE_GEMM = ("k_conv_masktile",)
 KERNEL_SOURCES = {
     "k_compact": "compact_kernels.hip", "k_mask_hist": "compact_kernels.hip",
+    "k_lookup_compact": "compact_kernels.hip",
     "k_gemm_nc": "gemm_kernels.hip", "k_gemm_centre": "gemm_kernels.hip",
     "k_conv_masktile": "masktile_kernels.hip", "k_dense_scatter": "map_kernels.hip",
     "k_dense_lookup": "map_kernels.hip", "k_os_pass": "radix_sort.hip",
@@ -76,17 +84,24 @@ def stage_model(stage, algo, route, n, p, c_in, c_out):
     and gathered rows count their payload only.
     """
     p_nc = p - n
+    fused = route == "dense" and algo == "pairs"   # lookup runs inside the compaction kernel
     if stage == "neighbours":
+        if fused:
+            # scatter: coords in, grid cell + the row's cell record out; the previous
+            # build's cells read and put back (same count, taken as n)
+            return 16 * n + 4 * n + 4 * n + 4 * n + 4 * n, 0
         if route == "dense":
-            # scatter: coords in, grid cell out; lookup: coords + 27 cells in, nbr + mask out
-            return 16 * n + 4 * n + (16 * n + 108 * n) + (108 * n + 4 * n), 0
+            # scatter as above; lookup: coords + 27 cells in, nbr + mask out
+            return 16 * n + 16 * n + (16 * n + 108 * n) + (108 * n + 4 * n), 0
         # sorted: coords -> keys, key sort passes, 9 searches per row (8-byte keys)
         return 16 * n + 8 * n + 5 * 2 * 12 * n + 9 * 8 * n + 112 * n, 0
     if stage == "mask_sort":
         return 4 * n + 3 * 2 * 8 * n, 0
     if stage == "compact":
-        grid = 16 * n + 4 * n if route == "dense" else 0
-        return 4 * n + 108 * n + 12 * p + 4 * n + grid, 0
+        if fused:
+            # coords + 27 cells in; nbr, mask, pair lists (in, out, slot), rowbase out
+            return 16 * n + 108 * n + 108 * n + 4 * n + 12 * p + 4 * n, 0
+        return 4 * n + 108 * n + 12 * p + 4 * n, 0
     if stage == "gemm" and algo == "pairs":
         return ((2 * c_in + 8 + 4 * c_out) * p_nc + 2 * 26 * c_in * c_out,
                 2.0 * p_nc * c_in * c_out)
@@ -221,7 +236,12 @@ def roofline(r):
         return None
     st = max(model, key=lambda s: model[s]["us"])
     mo = model[st]
-    kernels = MASK_TILE_GEMM if (st == "gemm" and r["algo"] == "mask_tiles") else STAGE_KERNELS[st]
+    if st == "gemm" and r["algo"] == "mask_tiles":
+        kernels = MASK_TILE_GEMM
+    elif r["info"]["route"] == "dense" and r["algo"] == "pairs" and st in STAGE_KERNELS_FUSED:
+        kernels = STAGE_KERNELS_FUSED[st]
+    else:
+        kernels = STAGE_KERNELS[st]
     kernel = kernels[0] if len(kernels) == 1 else "+".join(kernels)
     intensity = mo["flops"] / mo["bytes"] if mo["bytes"] else 0.0
     mfma = intensity > RIDGE

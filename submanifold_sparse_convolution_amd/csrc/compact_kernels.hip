@@ -141,16 +141,12 @@ __device__ void block_lookback(uint64_t* look, int64_t pb, uint32_t epoch, uint3
     }
 }
 
-// One read of the masks: digit histograms of every mask-sort pass, pairs per
-// tap (mask column sums), and -- on the dense route, when no compaction
-// follows (grid not null) -- the grid cells of the rows put back to empty
-// (the lookups that needed them have finished).
+// One read of the masks: digit histograms of every mask-sort pass and pairs
+// per tap (mask column sums).
 __global__ __launch_bounds__(kHThreads) void k_mask_hist(const uint32_t* __restrict__ mask,
                                                          int64_t n, int bits, int passes,
                                                          uint32_t* __restrict__ hist,
-                                                         int32_t* __restrict__ tap_tot,
-                                                         const int32_t* __restrict__ coords,
-                                                         Geom g, int32_t* __restrict__ grid) {
+                                                         int32_t* __restrict__ tap_tot) {
     extern __shared__ uint32_t s_h[];             // passes << bits, then 27 tap counters
     const int bins = 1 << bits;
     uint32_t* s_tap = s_h + passes * bins;
@@ -173,16 +169,6 @@ __global__ __launch_bounds__(kHThreads) void k_mask_hist(const uint32_t* __restr
         if (idx < n) {
             for (int p = 0; p < passes; ++p)
                 atomicAdd(&s_h[p * bins + ((m >> (p * bits)) & (bins - 1))], 1u);
-            if (grid) {
-                const int32_t* c = coords + idx * g.ncols;
-                int b = g.ncols == 4 ? c[0] : 0;
-                const int32_t* q = c + (g.ncols == 4 ? 1 : 0);
-                int x = q[0] - g.origin[0], y = q[1] - g.origin[1], z = q[2] - g.origin[2];
-                if ((unsigned)b < (unsigned)g.batch && (unsigned)x < (unsigned)g.ext[0] &&
-                    (unsigned)y < (unsigned)g.ext[1] && (unsigned)z < (unsigned)g.ext[2])
-                    grid[b * g.sz_b + (int64_t)(x + 1) * g.sz_x + (int64_t)(y + 1) * g.sz_y +
-                         (z + 1)] = -1;
-            }
         }
 #pragma unroll
         for (int k = 0; k < kTaps; ++k) {
@@ -197,57 +183,37 @@ __global__ __launch_bounds__(kHThreads) void k_mask_hist(const uint32_t* __restr
     if (threadIdx.x < kTaps && s_tap[threadIdx.x]) atomicAdd(&tap_tot[threadIdx.x], (int32_t)s_tap[threadIdx.x]);
 }
 
-// Rows [bid*kCChunk, +kCChunk) in row order, one per thread. For each tap
-// (and for the slab rows, column kTaps) the block counts its rows, finds the
-// count of earlier chunks by look-back and writes its pairs. The chunk's
-// neighbour rows (contiguous in the table) are read once, coalesced, into
-// LDS at the start; the chunk's pairs are first listed in LDS as (row, tap)
-// entries in output order, then written out with consecutive threads on
-// consecutive pair positions. The last chunk publishes the totals.
-__global__ __launch_bounds__(kCThreads) void k_compact(
-    const uint32_t* __restrict__ mask, const int32_t* __restrict__ nbr, int64_t n, int64_t cap,
-    int tile_m, MapState* st, int32_t* __restrict__ pair_in, int32_t* __restrict__ pair_out,
-    int32_t* __restrict__ pair_slot, int32_t* __restrict__ rowbase, uint64_t* __restrict__ look,
-    uint32_t* ticket, uint32_t epoch, uint32_t* status, const int32_t* __restrict__ coords, Geom g,
-    int32_t* __restrict__ grid) {
+// LDS of one compaction chunk.
+struct CompactLds {
+    uint32_t bid;
+    uint32_t wc[kCWaves][kTaps + 1];              // per-wave counts, then offsets in the chunk
+    uint32_t pre[kTaps + 1];                      // counts of earlier chunks
+    uint32_t loc[kTaps + 1];                      // chunk-local start of each tap's pairs
+    uint32_t tot[kTaps + 1];                      // the chunk's own counts
+    uint32_t near_[kTaps + 1], done[kTaps + 1];   // look-back scratch
+    int32_t nb[kCChunk * kTaps];                  // the chunk's neighbour rows
+    uint16_t list[kCChunk * kTaps];               // (row | tap << 8) in output order
+    uint32_t m[kCChunk], rb[kCChunk];
+};
+
+// Everything of a chunk after its masks are known (m: this thread's row;
+// L.nb filled): per-tap counts, look-back over earlier chunks, the chunk's
+// pairs listed in LDS as (row, tap) entries in output order, then written out
+// with consecutive threads on consecutive pair positions. The last chunk
+// publishes the totals. Starts and ends with all threads in step.
+__device__ __forceinline__ void compact_chunk(CompactLds& L, uint32_t m, uint32_t bid, int64_t n,
+                                              int64_t cap, int tile_m, MapState* st,
+                                              int32_t* __restrict__ pair_in,
+                                              int32_t* __restrict__ pair_out,
+                                              int32_t* __restrict__ pair_slot,
+                                              int32_t* __restrict__ rowbase,
+                                              uint64_t* __restrict__ look, uint32_t epoch,
+                                              uint32_t* status) {
     constexpr int kCols = kTaps + 1;
-    __shared__ uint32_t s_bid;
-    __shared__ uint32_t s_wc[kCWaves][kCols];     // per-wave counts, then offsets in the chunk
-    __shared__ uint32_t s_pre[kCols];             // counts of earlier chunks
-    __shared__ uint32_t s_loc[kCols];             // chunk-local start of each tap's pairs
-    __shared__ uint32_t s_tot[kCols];             // the chunk's own counts
-    __shared__ uint32_t s_near[kCols], s_done[kCols];   // look-back scratch
-    __shared__ int4 s_nb4[kCNbrVec];              // the chunk's neighbour rows [kCChunk][kTaps]
-    __shared__ uint16_t s_list[kCChunk * kTaps];  // (row | tap << 8) in output order
-    __shared__ uint32_t s_m[kCChunk], s_rb[kCChunk];
-    const int32_t* s_nb = reinterpret_cast<const int32_t*>(s_nb4);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    if (tid == 0) s_bid = atomicAdd(ticket, 1u);
-    __syncthreads();
-    const uint32_t bid = s_bid;
     const int64_t base0 = (int64_t)bid * kCChunk;
     const int64_t row = base0 + tid;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-
-    // loads: mask, neighbour rows (whole 16-byte words; the table is padded so the last
-    // word of the last row is readable), coordinates for the grid cleanup
-    const uint32_t mv = mask[row < n ? row : n - 1];
-    int4 nv4[kCNbrPer];
-    {
-        const int4* src = reinterpret_cast<const int4*>(nbr + base0 * kTaps);
-        const int64_t q_last = (n * kTaps + 3) / 4 - 1 - base0 * kTaps / 4;   // last readable word
-#pragma unroll
-        for (int j = 0; j < kCNbrPer; ++j) {
-            const int64_t q = tid + j * kCThreads;
-            nv4[j] = src[q < q_last ? q : q_last];
-        }
-    }
-    int4 cq = make_int4(0, 0, 0, 0);              // (b, x, y, z) of the row
-    if (grid) {
-        const int32_t* c = coords + min(row, n - 1) * g.ncols;
-        cq = g.ncols == 4 ? make_int4(c[0], c[1], c[2], c[3]) : make_int4(0, c[0], c[1], c[2]);
-    }
-    const uint32_t m = row < n ? mv : 0u;
     const uint32_t deg = m ? (uint32_t)__popc(m & ~(1u << kCentre)) : 0u;
     // per-wave count of each tap (lane k keeps tap k) and of slab rows (lane kTaps)
     uint32_t cnt = 0;
@@ -263,34 +229,29 @@ __global__ __launch_bounds__(kCThreads) void k_compact(
         if (lane >= o) incl += t;
     }
     const uint32_t wave_slab = __shfl(incl, 63, 64);
-    if (lane < kTaps) s_wc[w][lane] = cnt;
-    if (lane == kTaps) s_wc[w][kTaps] = wave_slab;
-    s_m[tid] = m;
-#pragma unroll
-    for (int j = 0; j < kCNbrPer; ++j) {
-        const int q = tid + j * kCThreads;
-        if (q < kCNbrVec) s_nb4[q] = nv4[j];
-    }
+    if (lane < kTaps) L.wc[w][lane] = cnt;
+    if (lane == kTaps) L.wc[w][kTaps] = wave_slab;
+    L.m[tid] = m;
     __syncthreads();
     if (tid < kCols) {
         const int k = tid;
         uint32_t run = 0;
 #pragma unroll
         for (int v = 0; v < kCWaves; ++v) {
-            uint32_t c = s_wc[v][k];
-            s_wc[v][k] = run;
+            uint32_t c = L.wc[v][k];
+            L.wc[v][k] = run;
             run += c;
         }
-        s_tot[k] = run;                           // the chunk's own count, for now
+        L.tot[k] = run;
         __hip_atomic_store(&look[(int64_t)bid * kCols + k],
                            lb_pack(epoch, bid == 0 ? kIncl : kAgg, run), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
-    block_lookback<kCols, 8>(look, (int64_t)bid - 1, epoch, status, s_pre, s_near, s_done);
+    block_lookback<kCols, 8>(look, (int64_t)bid - 1, epoch, status, L.pre, L.near_, L.done);
     if (tid < kCols) {
         const int k = tid;
-        const uint32_t run = s_tot[k];
-        const uint32_t prefix = s_pre[k];
+        const uint32_t run = L.tot[k];
+        const uint32_t prefix = L.pre[k];
         if (bid > 0)
             __hip_atomic_store(&look[(int64_t)bid * kCols + k], lb_pack(epoch, kIncl, prefix + run),
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -311,13 +272,13 @@ __global__ __launch_bounds__(kCThreads) void k_compact(
         uint32_t loc = 0;
         int32_t p = 0, padded = 0;
         for (int k = 0; k < kTaps; ++k) {
-            s_loc[k] = loc;
-            loc += s_tot[k];
-            const int32_t c = (int32_t)(s_pre[k] + s_tot[k]);
+            L.loc[k] = loc;
+            loc += L.tot[k];
+            const int32_t c = (int32_t)(L.pre[k] + L.tot[k]);
             p += c;
             padded += (c + tile_m - 1) / tile_m * tile_m;
         }
-        s_loc[kTaps] = loc;
+        L.loc[kTaps] = loc;
         if (bid == gridDim.x - 1) {
             st->totals[0] = p;
             st->totals[1] = padded;
@@ -325,53 +286,140 @@ __global__ __launch_bounds__(kCThreads) void k_compact(
         }
     }
     // first slab row of the row
-    const uint32_t rb = s_pre[kTaps] + s_wc[w][kTaps] + incl - deg;
+    const uint32_t rb = L.pre[kTaps] + L.wc[w][kTaps] + incl - deg;
     if (row < n) rowbase[row] = (int32_t)rb;
-    s_rb[tid] = rb;
+    L.rb[tid] = rb;
     __syncthreads();
     // list the chunk's pairs in output order: tap-major, rows ascending
 #pragma unroll
     for (int k = 0; k < kTaps; ++k) {
         const uint64_t b = __ballot((m >> k) & 1u);
         if ((m >> k) & 1u)
-            s_list[s_loc[k] + s_wc[w][k] + (uint32_t)__popcll(b & below)] =
-                (uint16_t)(tid | (k << 8));
+            L.list[L.loc[k] + L.wc[w][k] + (uint32_t)__popcll(b & below)] = (uint16_t)(tid | (k << 8));
     }
     __syncthreads();
     // write them out: entry p of tap k goes to k cap + (pairs of k in earlier chunks) + its rank
-    const int total = (int)s_loc[kTaps];
+    const int total = (int)L.loc[kTaps];
     for (int p = tid; p < total; p += kCThreads) {
-        const uint32_t e = s_list[p];
+        const uint32_t e = L.list[p];
         const int lr = (int)(e & 0xFFu), k = (int)(e >> 8);
-        const int64_t pos = (int64_t)k * cap + s_pre[k] + (p - (int)s_loc[k]);
+        const int64_t pos = (int64_t)k * cap + L.pre[k] + (p - (int)L.loc[k]);
         if (pos >= (int64_t)k * cap + cap) continue;          // only after a stalled wait
-        const uint32_t mr = s_m[lr];
-        pair_in[pos] = k == kCentre ? (int32_t)(base0 + lr) : s_nb[lr * kTaps + k];
+        const uint32_t mr = L.m[lr];
+        pair_in[pos] = k == kCentre ? (int32_t)(base0 + lr) : L.nb[lr * kTaps + k];
         pair_out[pos] = (int32_t)(base0 + lr);
         pair_slot[pos] = k == kCentre
                              ? -1
-                             : (int32_t)(s_rb[lr] + __popc(mr & ((1u << k) - 1u) & ~(1u << kCentre)));
+                             : (int32_t)(L.rb[lr] + __popc(mr & ((1u << k) - 1u) & ~(1u << kCentre)));
     }
-    // dense route: the grid cell of this row goes back to empty (every lookup has finished)
-    if (grid) {
-        const int b = cq.x;
-        const int x = cq.y - g.origin[0], y = cq.z - g.origin[1], z = cq.w - g.origin[2];
-        if (row < n && (unsigned)b < (unsigned)g.batch && (unsigned)x < (unsigned)g.ext[0] &&
-            (unsigned)y < (unsigned)g.ext[1] && (unsigned)z < (unsigned)g.ext[2])
-            grid[b * g.sz_b + (int64_t)(x + 1) * g.sz_x + (int64_t)(y + 1) * g.sz_y + (z + 1)] = -1;
+}
+
+// Compaction of a neighbour table in memory (sorted route): rows
+// [bid*kCChunk, +kCChunk) in row order, one per thread. The chunk's
+// neighbour rows (contiguous in the table) are read once, coalesced, into
+// LDS.
+__global__ __launch_bounds__(kCThreads) void k_compact(
+    const uint32_t* __restrict__ mask, const int32_t* __restrict__ nbr, int64_t n, int64_t cap,
+    int tile_m, MapState* st, int32_t* __restrict__ pair_in, int32_t* __restrict__ pair_out,
+    int32_t* __restrict__ pair_slot, int32_t* __restrict__ rowbase, uint64_t* __restrict__ look,
+    uint32_t* ticket, uint32_t epoch, uint32_t* status) {
+    __shared__ CompactLds L;
+    const int tid = threadIdx.x;
+    if (tid == 0) L.bid = atomicAdd(ticket, 1u);
+    __syncthreads();
+    const uint32_t bid = L.bid;
+    const int64_t base0 = (int64_t)bid * kCChunk;
+    const int64_t row = base0 + tid;
+    // mask, neighbour rows (whole 16-byte words; the table is padded so the last word
+    // of the last row is readable)
+    const uint32_t mv = mask[row < n ? row : n - 1];
+    int4 nv4[kCNbrPer];
+    {
+        const int4* src = reinterpret_cast<const int4*>(nbr + base0 * kTaps);
+        const int64_t q_last = (n * kTaps + 3) / 4 - 1 - base0 * kTaps / 4;   // last readable word
+#pragma unroll
+        for (int j = 0; j < kCNbrPer; ++j) {
+            const int64_t q = tid + j * kCThreads;
+            nv4[j] = src[q < q_last ? q : q_last];
+        }
     }
+    int4* nb4 = reinterpret_cast<int4*>(L.nb);
+#pragma unroll
+    for (int j = 0; j < kCNbrPer; ++j) {
+        const int q = tid + j * kCThreads;
+        if (q < kCNbrVec) nb4[q] = nv4[j];
+    }
+    compact_chunk(L, row < n ? mv : 0u, bid, n, cap, tile_m, st, pair_in, pair_out, pair_slot,
+                  rowbase, look, epoch, status);
+    if (bid == gridDim.x - 1 && tid == 0) atomicExch(ticket, 0u);
+}
+
+// Dense route: lookup and compaction in one kernel. Each thread looks up its
+// row's 27 cells as 9 (dx, dy) columns of 3 consecutive cells (z fastest),
+// writes the neighbour row to LDS and its mask; the chunk's neighbour rows go
+// to the table with coalesced stores, then the chunk is compacted.
+__global__ __launch_bounds__(kCThreads) void k_lookup_compact(
+    const int32_t* __restrict__ coords, int64_t n, Geom g, const int32_t* __restrict__ grid,
+    int32_t* __restrict__ nbr, uint32_t* __restrict__ mask, int64_t cap, int tile_m, MapState* st,
+    int32_t* __restrict__ pair_in, int32_t* __restrict__ pair_out, int32_t* __restrict__ pair_slot,
+    int32_t* __restrict__ rowbase, uint64_t* __restrict__ look, uint32_t* ticket, uint32_t epoch,
+    uint32_t* status) {
+    __shared__ CompactLds L;
+    const int tid = threadIdx.x;
+    if (tid == 0) L.bid = atomicAdd(ticket, 1u);
+    __syncthreads();
+    const uint32_t bid = L.bid;
+    const int64_t base0 = (int64_t)bid * kCChunk;
+    const int64_t row = base0 + tid;
+    const int64_t rc = row < n ? row : n - 1;
+    const int32_t* c = coords + rc * g.ncols;
+    const int b = g.ncols == 4 ? c[0] : 0;
+    const int32_t* q = c + (g.ncols == 4 ? 1 : 0);
+    const int x = q[0] - g.origin[0], y = q[1] - g.origin[1], z = q[2] - g.origin[2];
+    const bool ok = row < n && (unsigned)b < (unsigned)g.batch && (unsigned)x < (unsigned)g.ext[0] &&
+                    (unsigned)y < (unsigned)g.ext[1] && (unsigned)z < (unsigned)g.ext[2];
+    // cell (x, y, z - 1) of the padded grid, whose 3x3x3 neighbourhood starts at
+    // c0 - sz_x - sz_y. Rows out of range (and rows past n) read the neighbourhood of
+    // padded cell (1, 1, 0) instead, which lies inside the grid; their values are unused.
+    const int64_t c0 = ok ? b * g.sz_b + (int64_t)(x + 1) * g.sz_x + (int64_t)(y + 1) * g.sz_y + z
+                          : g.sz_x + g.sz_y;
+    int32_t v[kTaps];
+#pragma unroll
+    for (int dx = 0; dx < 3; ++dx)
+#pragma unroll
+        for (int dy = 0; dy < 3; ++dy) {
+            const int32_t* p3 = grid + c0 + (int64_t)(dx - 1) * g.sz_x + (int64_t)(dy - 1) * g.sz_y;
+#pragma unroll
+            for (int dz = 0; dz < 3; ++dz) v[9 * dx + 3 * dy + dz] = p3[dz];
+        }
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 0; k < kTaps; ++k) {
+        v[k] = ok ? v[k] : -1;
+        m |= (v[k] >= 0 ? 1u : 0u) << k;
+        L.nb[tid * kTaps + k] = v[k];
+    }
+    if (row < n) mask[row] = m;
+    __syncthreads();
+    {                                             // neighbour rows out, coalesced
+        const int4* nb4 = reinterpret_cast<const int4*>(L.nb);
+        int4* dst = reinterpret_cast<int4*>(nbr + base0 * kTaps);
+        const int64_t q_end = ((n - base0) * kTaps + 3) / 4;      // words holding rows < n
+        for (int j = tid; j < kCNbrVec; j += kCThreads)
+            if (j < q_end) dst[j] = nb4[j];
+    }
+    compact_chunk(L, m, bid, n, cap, tile_m, st, pair_in, pair_out, pair_slot, rowbase, look,
+                  epoch, status);
     if (bid == gridDim.x - 1 && tid == 0) atomicExch(ticket, 0u);
 }
 
 }  // namespace
 
 hipError_t launch_mask_hist(const uint32_t* mask, int64_t n, const SortPlan& plan, uint32_t* hist,
-                            int32_t* tap_tot, const int32_t* coords, const Geom& g,
-                            int32_t* grid, hipStream_t s) {
+                            int32_t* tap_tot, hipStream_t s) {
     unsigned blocks = (unsigned)((n + kHTile - 1) / kHTile);
     size_t lds = ((size_t)plan.passes * (1u << plan.bits) + kTaps) * 4;
-    launch(k_mask_hist, blocks, kHThreads, lds, s, mask, n, plan.bits, plan.passes, hist, tap_tot,
-                                               coords, g, grid);
+    launch(k_mask_hist, blocks, kHThreads, lds, s, mask, n, plan.bits, plan.passes, hist, tap_tot);
     return hipGetLastError();
 }
 
@@ -379,16 +427,31 @@ int64_t compact_chunks(int64_t n) { return (n + kCChunk - 1) / kCChunk; }
 
 size_t compact_look_bytes(int64_t n) { return (size_t)compact_chunks(n) * (kTaps + 1) * 8; }
 
+static uint32_t next_epoch(SortWork& ws) {
+    uint32_t epoch = ++ws.epoch & 0x3FFFFFFFu;
+    if (epoch == 0) epoch = ++ws.epoch & 0x3FFFFFFFu;
+    return epoch;
+}
+
 hipError_t launch_compact(const uint32_t* mask, const int32_t* nbr, int64_t n, int64_t cap,
                           int tile_m, MapState* st, int32_t* pair_in, int32_t* pair_out,
                           int32_t* pair_slot, int32_t* rowbase, SortWork& ws, uint32_t* status,
-                          const int32_t* coords, const Geom& g, int32_t* grid, hipStream_t s) {
-    uint32_t epoch = ++ws.epoch & 0x3FFFFFFFu;
-    if (epoch == 0) epoch = ++ws.epoch & 0x3FFFFFFFu;
-    unsigned blocks = (unsigned)compact_chunks(n);
-    launch(k_compact, blocks, kCThreads, 0, s, mask, nbr, n, cap, tile_m, st, pair_in, pair_out,
-                                           pair_slot, rowbase, ws.look, ws.ticket, epoch, status,
-                                           coords, g, grid);
+                          hipStream_t s) {
+    const uint32_t epoch = next_epoch(ws);
+    launch(k_compact, (unsigned)compact_chunks(n), kCThreads, 0, s, mask, nbr, n, cap, tile_m, st,
+           pair_in, pair_out, pair_slot, rowbase, ws.look, ws.ticket, epoch, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_lookup_compact(const int32_t* coords, int64_t n, const Geom& g,
+                                 const int32_t* grid, int32_t* nbr, uint32_t* mask, int64_t cap,
+                                 int tile_m, MapState* st, int32_t* pair_in, int32_t* pair_out,
+                                 int32_t* pair_slot, int32_t* rowbase, SortWork& ws,
+                                 uint32_t* status, hipStream_t s) {
+    const uint32_t epoch = next_epoch(ws);
+    launch(k_lookup_compact, (unsigned)compact_chunks(n), kCThreads, 0, s, coords, n, g, grid, nbr,
+           mask, cap, tile_m, st, pair_in, pair_out, pair_slot, rowbase, ws.look, ws.ticket, epoch,
+           status);
     return hipGetLastError();
 }
 

@@ -109,22 +109,42 @@ __global__ __launch_bounds__(kBlock) void k_fill_i32(int32_t* p, int64_t n, int3
         p[i] = v;
 }
 
-// One thread per row: claim the row's grid cell. A second claimant of a cell
-// means two rows share coordinates.
+// One thread per row: claim the row's grid cell and record it in cells. A
+// second claimant of a cell means two rows share coordinates. Thread i first
+// puts back to empty cell i of the previous dense build (other grid), so the
+// launch covers max(n, prev.n) threads.
 __global__ __launch_bounds__(kBlock) void k_dense_scatter(const int32_t* __restrict__ coords,
                                                           int64_t n, Geom g,
                                                           int32_t* __restrict__ grid,
-                                                          MapState* st, NextRecord next) {
+                                                          int32_t* __restrict__ cells,
+                                                          MapState* st, NextRecord next,
+                                                          PrevCells prev) {
     if (next.st) clear_record(next.st, next.hist, next.hist_ints);
-    int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (i < prev.n) {
+        const int32_t c = prev.cells[i];
+        if (c >= 0) prev.grid[c] = -1;
+    }
     if (i >= n) return;
     int b, x, y, z;
     if (!load_rel(coords, i, g, b, x, y, z)) {
         atomicOr(&st->status, kStRange);
+        cells[i] = -1;
         return;
     }
-    int old = atomicCAS(&grid[dense_cell(g, b, x, y, z)], -1, (int)i);
+    const int64_t cell = dense_cell(g, b, x, y, z);
+    cells[i] = (int32_t)cell;
+    int old = atomicCAS(&grid[cell], -1, (int)i);
     if (old != -1) atomicOr(&st->status, kStDuplicate);
+}
+
+// Only the cleanup part of k_dense_scatter (a build that writes no grid).
+__global__ __launch_bounds__(kBlock) void k_clear_cells(PrevCells prev) {
+    const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (i < prev.n) {
+        const int32_t c = prev.cells[i];
+        if (c >= 0) prev.grid[c] = -1;
+    }
 }
 
 // 32 lanes per row (27 active): lane k reads the cell at offset d_k. The
@@ -272,8 +292,16 @@ hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s) {
 }
 
 hipError_t launch_dense_scatter(const int32_t* coords, int64_t n, const Geom& g, int32_t* grid,
-                                MapState* st, const NextRecord& next, hipStream_t s) {
-    launch(k_dense_scatter, blocks_for(n), kBlock, 0, s, coords, n, g, grid, st, next);
+                                int32_t* cells, MapState* st, const NextRecord& next,
+                                const PrevCells& prev, hipStream_t s) {
+    launch(k_dense_scatter, blocks_for(n > prev.n ? n : prev.n), kBlock, 0, s, coords, n, g, grid,
+           cells, st, next, prev);
+    return hipGetLastError();
+}
+
+hipError_t launch_clear_cells(const PrevCells& prev, hipStream_t s) {
+    if (prev.n <= 0) return hipSuccess;
+    launch(k_clear_cells, blocks_for(prev.n), kBlock, 0, s, prev);
     return hipGetLastError();
 }
 

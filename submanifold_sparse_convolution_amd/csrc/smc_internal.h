@@ -88,12 +88,23 @@ struct NextRecord {
     int hist_ints = 0;
 };
 
+// Cells of the previous dense build, to put back to empty in the other grid
+// (dense grids are double-buffered: a build writes one grid while its first
+// kernel clears the cells the previous build set in the other one).
+struct PrevCells {
+    const int32_t* cells = nullptr;   // grid cell of each row of that build (-1: none)
+    int64_t n = 0;
+    int32_t* grid = nullptr;
+};
+
 // ---- map kernels (map_kernels.hip) ----
 hipError_t launch_state_init(MapState* st, uint32_t* hist, int hist_ints, hipStream_t s);
 hipError_t launch_bbox(const int32_t* coords, int64_t n, int ncols, MapState* st, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 hipError_t launch_dense_scatter(const int32_t* coords, int64_t n, const Geom& g, int32_t* grid,
-                                MapState* st, const NextRecord& next, hipStream_t s);
+                                int32_t* cells, MapState* st, const NextRecord& next,
+                                const PrevCells& prev, hipStream_t s);
+hipError_t launch_clear_cells(const PrevCells& prev, hipStream_t s);
 hipError_t launch_dense_lookup(const int32_t* coords, int64_t n, const Geom& g, const int32_t* grid,
                                int32_t* nbr, uint32_t* mask, hipStream_t s);
 hipError_t launch_make_keys(const int32_t* coords, int64_t n, const Geom& g, bool wide, void* keys,
@@ -126,18 +137,23 @@ hipError_t radix_sort_u64(const uint64_t* keys_in, const uint32_t* vals_in, int6
 
 // ---- compaction (compact_kernels.hip) ----
 hipError_t launch_mask_hist(const uint32_t* mask, int64_t n, const SortPlan& plan, uint32_t* hist,
-                            int32_t* tap_tot, const int32_t* coords, const Geom& g,
-                            int32_t* grid, hipStream_t s);
+                            int32_t* tap_tot, hipStream_t s);
 int64_t compact_chunks(int64_t n);
 size_t compact_look_bytes(int64_t n);
 // Pairs of tap k go to [k cap, k cap + tap_count[k]) in ascending output row;
 // pair_slot numbers the off-centre pairs row by row (rowbase[i] = first slab
-// row of output row i). grid (dense route) or null: cells of the rows are
-// reset to -1.
+// row of output row i).
 hipError_t launch_compact(const uint32_t* mask, const int32_t* nbr, int64_t n, int64_t cap,
                           int tile_m, MapState* st, int32_t* pair_in, int32_t* pair_out,
                           int32_t* pair_slot, int32_t* rowbase, SortWork& ws, uint32_t* status,
-                          const int32_t* coords, const Geom& g, int32_t* grid, hipStream_t s);
+                          hipStream_t s);
+// Dense route: neighbour lookup and compaction in one kernel (also writes nbr
+// and mask).
+hipError_t launch_lookup_compact(const int32_t* coords, int64_t n, const Geom& g,
+                                 const int32_t* grid, int32_t* nbr, uint32_t* mask, int64_t cap,
+                                 int tile_m, MapState* st, int32_t* pair_in, int32_t* pair_out,
+                                 int32_t* pair_slot, int32_t* rowbase, SortWork& ws,
+                                 uint32_t* status, hipStream_t s);
 
 // ---- GEMM (gemm_kernels.hip) ----
 size_t packed_weight_bytes(int c_in, int c_out);

@@ -102,8 +102,15 @@ struct smc_map {
     DevBuf state;                     // two MapState records: builds alternate between them
     int slot = 1;                     // record of the last build
     bool slot_clean[2] = {true, true};  // record in its starting state
-    DevBuf grid;                      // int32 presence grid (dense route), kept all -1
-    int64_t grid_clean_cells = 0;     // prefix of grid known to be -1
+    // Dense route: two int32 presence grids, used by alternate dense builds and kept
+    // all -1 between them. cells[i] records the cell of every row of the last build
+    // on grid i; the next dense build (on the other grid) or, before a sorted build,
+    // a small kernel puts those cells back to -1.
+    DevBuf grid[2];
+    int64_t grid_clean_cells[2] = {0, 0};   // prefix of each grid known to be -1
+    DevBuf cells[2];
+    int next_grid = 0;                       // grid of the next dense build
+    PrevCells stale;                         // cells not yet put back (stale.n = 0: none)
     DevBuf keys0, keys1, keys2;       // packed keys (u32 or u64)
     DevBuf vals0, vals1;              // u32
     DevBuf hist;                      // per record: digit histograms, mask sort then key sort
@@ -187,18 +194,20 @@ int wait_build(smc_map* m) {
     return SMC_OK;
 }
 
-int ensure_grid(smc_map* m, int64_t cells, hipStream_t s) {
+int ensure_grid(smc_map* m, int gi, int64_t cells, hipStream_t s) {
     size_t bytes = (size_t)cells * 4;
-    if (bytes > m->grid.bytes) {
-        int rc = m->grid.ensure(bytes);
+    DevBuf& grid = m->grid[gi];
+    if (bytes > grid.bytes) {
+        if (m->stale.n > 0 && m->stale.grid == grid.as<int32_t>()) m->stale = PrevCells();
+        int rc = grid.ensure(bytes);
         if (rc) return rc;
-        m->grid_clean_cells = 0;
+        m->grid_clean_cells[gi] = 0;
     }
-    if (m->grid_clean_cells < cells) {
+    if (m->grid_clean_cells[gi] < cells) {
         // fill the whole allocation once; later builds only clear what they used
-        int64_t all = (int64_t)(m->grid.bytes / 4);
-        SMC_HIP(launch_fill_i32(m->grid.as<int32_t>(), all, -1, s));
-        m->grid_clean_cells = all;
+        int64_t all = (int64_t)(grid.bytes / 4);
+        SMC_HIP(launch_fill_i32(grid.as<int32_t>(), all, -1, s));
+        m->grid_clean_cells[gi] = all;
     }
     return SMC_OK;
 }
@@ -315,7 +324,8 @@ int smc_map_destroy(smc_map* m) {
         (void)hipGetDevice(&cur);
         (void)hipSetDevice(m->device);
         (void)hipDeviceSynchronize();
-        DevBuf* bufs[] = {&m->state, &m->grid, &m->keys0, &m->keys1, &m->keys2,
+        DevBuf* bufs[] = {&m->state, &m->grid[0], &m->grid[1], &m->cells[0], &m->cells[1],
+                          &m->keys0, &m->keys1, &m->keys2,
                           &m->vals0, &m->vals1, &m->hist, &m->look, &m->ticket, &m->nbr,
                           &m->mask, &m->mkey0, &m->mkey1, &m->mval0, &m->mval1,
                           &m->pair_in, &m->pair_out, &m->pair_slot, &m->rowbase, &m->part,
@@ -472,15 +482,37 @@ int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     if (n > 0) {
         int32_t* nbr = m->nbr.as<int32_t>();
         uint32_t* mask = m->mask.as<uint32_t>();
-        int32_t* grid = nullptr;
+        const bool fused = chosen == SMC_ROUTE_DENSE && want_pairs;
         StageTimer t_nb(m, SMC_STAGE_NEIGHBOURS, s);
         if (chosen == SMC_ROUTE_DENSE) {
-            if ((rc = ensure_grid(m, m->grid_cells, s))) return rc;
-            grid = m->grid.as<int32_t>();
-            SMC_HIP(launch_dense_scatter(coords, n, g, grid, st, next, s));
+            const int gi = m->next_grid;
+            if ((rc = ensure_grid(m, gi, m->grid_cells, s)) ||
+                (rc = m->cells[gi].ensure((size_t)nn * 4)))
+                return rc;
+            int32_t* grid = m->grid[gi].as<int32_t>();
+            SMC_HIP(launch_dense_scatter(coords, n, g, grid, m->cells[gi].as<int32_t>(), st, next,
+                                         m->stale, s));
             m->slot_clean[slot ^ 1] = true;
-            SMC_HIP(launch_dense_lookup(coords, n, g, grid, nbr, mask, s));
+            m->stale.cells = m->cells[gi].as<int32_t>();
+            m->stale.n = n;
+            m->stale.grid = grid;
+            m->next_grid = gi ^ 1;
+            if (fused) {
+                t_nb.finish();
+                StageTimer t_cp(m, SMC_STAGE_COMPACT, s);
+                SMC_HIP(launch_lookup_compact(coords, n, g, grid, nbr, mask, cap, kTileM, st,
+                                              m->pair_in.as<int32_t>(), m->pair_out.as<int32_t>(),
+                                              m->pair_slot.as<int32_t>(),
+                                              m->rowbase.as<int32_t>(), m->ws, status, s));
+                t_cp.finish();
+            } else {
+                SMC_HIP(launch_dense_lookup(coords, n, g, grid, nbr, mask, s));
+            }
         } else {
+            if (m->stale.n > 0) {             // the last dense build's cells
+                SMC_HIP(launch_clear_cells(m->stale, s));
+                m->stale = PrevCells();
+            }
             const size_t kb = (size_t)nn * (m->wide ? 8 : 4);
             if ((rc = m->keys0.ensure(kb)) || (rc = m->keys1.ensure(kb)) ||
                 (rc = m->keys2.ensure(kb)) || (rc = m->vals0.ensure((size_t)nn * 4)) ||
@@ -506,16 +538,13 @@ int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
             SMC_HIP(launch_sorted_lookup(skeys, svals, n, g, m->wide, nbr, mask, st, s));
         }
         t_nb.finish();
-        // The grid cells go back to empty in the last pass over the rows: the compaction
-        // when pair lists are built, otherwise the mask histogram (which then also gives
-        // the per-tap counts).
+        // the mask histogram also gives the per-tap counts of a map without pair lists
         if (want_sort || !want_pairs) {
             // rows ordered by (mask, row): histograms (+ per-tap totals), then passes
             StageTimer t_ms(m, SMC_STAGE_MASK_SORT, s);
             SortPlan mp = sort_plan(kMaskBits);
             if (!want_sort) mp.passes = 0;
-            SMC_HIP(launch_mask_hist(mask, n, mp, hist_mask, st->tap_tot, coords, g,
-                                     want_pairs ? nullptr : grid, s));
+            SMC_HIP(launch_mask_hist(mask, n, mp, hist_mask, st->tap_tot, s));
             if (want_sort) {
                 const uint32_t* sorted_masks;
                 SMC_HIP(radix_sort_u32(mask, nullptr, n, mp, hist_mask, m->mkey0.as<uint32_t>(),
@@ -525,11 +554,11 @@ int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
             }
             t_ms.finish();
         }
-        if (want_pairs) {
+        if (want_pairs && !fused) {
             StageTimer t_cp(m, SMC_STAGE_COMPACT, s);
             SMC_HIP(launch_compact(mask, nbr, n, cap, kTileM, st, m->pair_in.as<int32_t>(),
                                    m->pair_out.as<int32_t>(), m->pair_slot.as<int32_t>(),
-                                   m->rowbase.as<int32_t>(), m->ws, status, coords, g, grid, s));
+                                   m->rowbase.as<int32_t>(), m->ws, status, s));
             t_cp.finish();
         }
     }

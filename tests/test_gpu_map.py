@@ -130,6 +130,25 @@ def test_rebuild_reuses_handle_and_keeps_grid_clean(pairs, sort):
     m.close()
 
 
+def test_route_switches_and_sizes_on_one_handle():
+    """Dense builds alternate between two presence grids and clear the previous
+    build's cells; a sorted build in between clears them too. Every build on one
+    handle must still match the oracle, whatever the order of routes and sizes."""
+    m = smc.KernelMap()
+    plan = [("dense", 3000, 1), ("dense", 500, 2), ("sorted", 2000, 3), ("dense", 4000, 4),
+            ("dense", 100, 5), ("dense", 4000, 4), ("sorted", 700, 6), ("sorted", 900, 7),
+            ("dense", 2500, 8)]
+    for route, n, seed in plan:
+        coords = synth.ground_box_coords(n, (200, 200, 12), seed=seed, n_boxes=20)
+        print(f"route {route} n {n} seed {seed}", flush=True)
+        for pairs, sort in ((True, False), (True, True), (False, True)):
+            m.build(to_dev_i32(coords), spatial_shape=(200, 200, 12), route=route, pairs=pairs,
+                    sort=sort)
+            assert_map_equal(m.export(pairs=pairs, perm=sort), oracle_map_of(coords),
+                             f"{route} n={n} pairs={pairs} sort={sort}")
+    m.close()
+
+
 def test_map_is_deterministic():
     _, coords = config("stage")
     a = gpu_map(coords, spatial_shape=(1440, 1440, 41))
