@@ -7,8 +7,8 @@
 // 4 (l / 16) .. +3.
 //
 // Packed weights ([tap][wave tile][k-step][nb][lane][8] bf16) assign input
-// channel g Kp/4 + 8 s .. +7 to lane group g = l / 16 at k-step s (a lane
-// walks one contiguous stretch of its gathered row), and output column
+// channels 32 s + 8 g .. +7 to lane group g = l / 16 at k-step s (so a load
+// instruction of A reads 64 contiguous bytes per row), and output column
 // c NBW + nb (plus the wave tile's base) to column block nb, lane column c
 // (each lane ends up holding NBW consecutive output columns).
 #pragma once

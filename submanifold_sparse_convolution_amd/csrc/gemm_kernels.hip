@@ -24,14 +24,15 @@
 // (l % 16), the same k; the 16x16 float result holds column (l % 16), rows
 // 4 (l / 16) .. +3.
 //
-// Free orderings used: (1) the input channels: lane group g = l / 16 is
-// given a contiguous quarter of the padded input channels, channel
-// g Kp/4 + 8 s .. +7 at k-step s, so a lane walks one contiguous stretch of
-// its gathered row; (2) the output columns: a wave covers WT = 16 NBW
-// columns with NBW MFMA column blocks, and block nb, lane column c stands
-// for output column c NBW + nb, so each lane ends up holding NBW
-// consecutive output columns of its rows (one vector store per row). The
-// packed weights follow both orderings.
+// Orderings used: (1) the input channels: k-step s covers channels
+// 32 s .. 32 s + 31 and lane group g = l / 16 takes 32 s + 8 g .. +7, so one
+// load instruction reads 64 contiguous bytes of each of its 16 rows (a
+// quarter-per-lane-group order instead spreads an instruction over 64 cache
+// lines and, at C = 512, thrashes L1 across k-steps); (2) the output
+// columns (a free choice): a wave covers WT = 16 NBW columns with NBW MFMA
+// column blocks, and block nb, lane column c stands for output column
+// c NBW + nb, so each lane ends up holding NBW consecutive output columns
+// of its rows (one vector store per row). The packed weights follow both.
 #include "gemm_common.h"
 
 namespace smc {
@@ -54,7 +55,7 @@ __global__ __launch_bounds__(kBlock) void k_weight_pack(const uint16_t* __restri
     int wt = (int)(r % n_wt);
     int tap = (int)(r / n_wt);
     int col = wt * 16 * nbw + (lane & 15) * nbw + nb;
-    int k0 = (lane >> 4) * (steps * 8) + s * 8;
+    int k0 = s * 32 + (lane >> 4) * 8;
     uint16_t v[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -69,45 +70,32 @@ __global__ __launch_bounds__(kBlock) void k_weight_pack(const uint16_t* __restri
     out[t] = o;
 }
 
-// Copy n16 16-byte words of packed weights into LDS with 8 loads in flight
-// per thread: whole rounds of 8 x 256 words without conditions, then the rest.
-__device__ inline void stage_b(uint4* __restrict__ dst, const uint4* __restrict__ src, int n16) {
-    const int full = n16 / (8 * kGemmThreads) * (8 * kGemmThreads);
-    for (int i0 = threadIdx.x; i0 < full; i0 += 8 * kGemmThreads) {
-        uint4 v[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = src[i0 + j * kGemmThreads];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) dst[i0 + j * kGemmThreads] = v[j];
-    }
-    for (int i = full + threadIdx.x; i < n16; i += kGemmThreads) dst[i] = src[i];
-}
-
 // A fragments of k-steps s0 .. s0+3 for MW gathered rows (steps past the
 // last re-read the last one: valid addresses, results unused).
 template <int MW, bool VEC>
 __device__ __forceinline__ void load_group(const uint16_t* const (&xrow)[MW], int c_in, int steps,
                                            int s0, int g, u32x4 (&a)[4][MW]) {
-    const int kq = steps * 8;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int st = min(s0 + i, steps - 1);
 #pragma unroll
-        for (int m = 0; m < MW; ++m) a[i][m] = load_a4<VEC>(xrow[m], g * kq + st * 8, c_in);
+        for (int m = 0; m < MW; ++m) a[i][m] = load_a4<VEC>(xrow[m], st * 32 + g * 8, c_in);
     }
 }
 
-// c += A (k-steps s0 .. s0+3, those below steps) x B; b points at this lane's
-// word of the (tap, wave tile) fragments, in LDS or in global memory.
+constexpr int kChunk = 4;    // k-steps per streamed weight chunk (the A group size too)
+
+// c += A (k-steps s0 .. s0+3, those below steps) x the weight chunk at b
+// (this lane's word of the chunk's first fragment, in LDS).
 template <int NBW, int MW>
-__device__ __forceinline__ void mma_group(const u32x4 (&a)[4][MW], const uint4* __restrict__ b,
-                                          int s0, int steps, f32x4 (&c)[MW][NBW]) {
+__device__ __forceinline__ void mma_chunk(const u32x4 (&a)[4][MW], const u32x4* b, int s0, int steps,
+                                          f32x4 (&c)[MW][NBW]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kChunk; ++i) {
         if (s0 + i >= steps) break;
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb) {
-            const uint4 bv = b[((s0 + i) * NBW + nb) * 64];
+            const u32x4 bv = b[(i * NBW + nb) * 64];
 #pragma unroll
             for (int m = 0; m < MW; ++m)
                 c[m][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[i][m]), as_bf16x8(bv),
@@ -116,27 +104,85 @@ __device__ __forceinline__ void mma_group(const u32x4 (&a)[4][MW], const uint4* 
     }
 }
 
-// One wave: MW fragments of 16 rows times 16 NBW columns, one tap's weights.
-// a holds the first group of k-steps (loaded by the caller, ahead of
-// whatever it had to wait for); each later group is loaded while the
-// previous one is multiplied.
-template <int NBW, int MW, bool VEC>
-__device__ __forceinline__ void wave_mma(const uint16_t* const (&xrow)[MW], int c_in, int steps,
-                                         const uint4* __restrict__ b, int g, u32x4 (&a)[4][MW],
-                                         f32x4 (&c)[MW][NBW]) {
+// Weight words of one streamed chunk per thread.
+template <int NBW>
+constexpr int bg_per() { return kChunk * NBW * 64 / kGemmThreads; }
+
+// First chunk of a weight slab into registers (issued early, before the
+// caller's other waits).
+template <int NBW>
+__device__ __forceinline__ void bg_fetch0(const u32x4* __restrict__ src, int steps,
+                                          u32x4 (&bw)[bg_per<NBW>()]) {
+    const int n_words = steps * NBW * 64;
+#pragma unroll
+    for (int j = 0; j < bg_per<NBW>(); ++j) {
+        const int i = threadIdx.x + j * kGemmThreads;
+        bw[j] = src[i < n_words ? i : n_words - 1];
+    }
+}
+
+// One block tile: every wave multiplies its MW row fragments (16 rows each)
+// by one (tap, wave tile) weight slab src ([k-step][nb][lane] words). The
+// slab streams through two LDS buffers kChunk k-steps at a time: chunk ch+1
+// (weights and this wave's gathered rows) is loaded while chunk ch is
+// multiplied, one barrier per chunk. The caller has loaded the first A
+// group into a and the first weight chunk into bw (bg_fetch0), and must
+// have finished every read of s_b from before -- unless resident: a slab of
+// one chunk already in buffer 0 from the previous tile, which is reused
+// as is. All threads of the block call this. Loads past the last chunk
+// re-read it (valid addresses, unused), so the loop has no conditional
+// loads.
+template <int NBW, int MW, bool VEC, bool STREAM>
+__device__ __forceinline__ void block_gemm(const uint16_t* const (&xrow)[MW], int c_in, int steps,
+                                           const u32x4* __restrict__ src, u32x4* s_b, int lane, int g,
+                                           u32x4 (&a)[4][MW], u32x4 (&bw)[bg_per<NBW>()],
+                                           bool resident, f32x4 (&c)[MW][NBW]) {
+    constexpr int kBufW = kChunk * NBW * 64;           // words per LDS buffer
+    constexpr int kPer = bg_per<NBW>();                // words per thread per chunk
+    const int tid = threadIdx.x;
+    const int n_words = steps * NBW * 64;
+    const int n_ch = (steps + kChunk - 1) / kChunk;
 #pragma unroll
     for (int m = 0; m < MW; ++m)
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb) c[m][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    u32x4 an[4][MW];
-    for (int s0 = 0;; s0 += 8) {
-        if (s0 + 4 < steps) load_group<MW, VEC>(xrow, c_in, steps, s0 + 4, g, an);
-        mma_group<NBW, MW>(a, b, s0, steps, c);
-        if (s0 + 4 >= steps) break;
-        if (s0 + 8 < steps) load_group<MW, VEC>(xrow, c_in, steps, s0 + 8, g, a);
-        mma_group<NBW, MW>(an, b, s0 + 4, steps, c);
-        if (s0 + 8 >= steps) break;
+    if (STREAM || !resident) {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int i = tid + j * kGemmThreads;
+            if (i < n_words) s_b[i] = bw[j];
+        }
+        __syncthreads();
     }
+    if (!STREAM) {                                // one chunk (steps <= kChunk): nothing to stream
+        mma_chunk<NBW, MW>(a, s_b + lane, 0, steps, c);
+        return;
+    }
+    u32x4 an[4][MW];
+// chunk CH (its weights in buffer CH & 1, rows in ACUR); prefetch chunk CH + 1 into ANEXT
+#define SMC_BG_STEP(ACUR, ANEXT)                                                                  \
+    {                                                                                             \
+        const int nx_ = min(ch + 1, n_ch - 1);                                                    \
+        _Pragma("unroll") for (int j = 0; j < kPer; ++j) {                                        \
+            const int i_ = nx_ * kBufW + tid + j * kGemmThreads;                                  \
+            bw[j] = src[i_ < n_words ? i_ : n_words - 1];                                         \
+        }                                                                                         \
+        load_group<MW, VEC>(xrow, c_in, steps, nx_ * kChunk, g, ANEXT);                           \
+        mma_chunk<NBW, MW>(ACUR, s_b + (ch & 1) * kBufW + lane, ch * kChunk, steps, c);           \
+        if (ch + 1 >= n_ch) break;                                                                \
+        _Pragma("unroll") for (int j = 0; j < kPer; ++j) {                                        \
+            const int i_ = tid + j * kGemmThreads;                                                \
+            if ((ch + 1) * kBufW + i_ < n_words) s_b[((ch + 1) & 1) * kBufW + i_] = bw[j];        \
+        }                                                                                         \
+        __syncthreads();                                                                          \
+        ++ch;                                                                                     \
+    }
+    int ch = 0;
+    while (true) {
+        SMC_BG_STEP(a, an)
+        SMC_BG_STEP(an, a)
+    }
+#undef SMC_BG_STEP
 }
 
 // Store NBW float values of one slab or output row (columns col0 ..).
@@ -154,17 +200,17 @@ __device__ __forceinline__ void store_f32(float* __restrict__ dst, int col0, int
     }
 }
 
-// Non-centre taps: blocks stride over the tiles of the 26 pair lists (tap k
-// holds tap_count[k] pairs from k * cap on; the counts are read on the
-// device). With LDS, the tile's weight slab is staged once for the block's
-// 4 waves.
-template <int NBW, bool LDS, bool VEC>
-__global__ __launch_bounds__(kGemmThreads) void k_gemm_nc(
-    const uint16_t* __restrict__ x, int c_in, int steps, const uint4* __restrict__ wp, int n_wt,
+// Non-centre taps: blocks stride over tiles of 64 MW pairs of one tap (tap k
+// holds tap_count[k] pairs from k * cap on, cap a multiple of 256; the counts
+// are read on the device). Each pair's product row goes to its slab row.
+template <int NBW, int MW, bool VEC, bool STREAM>
+__global__ __launch_bounds__(kGemmThreads, STREAM ? 1 : 2) void k_gemm_nc(
+    const uint16_t* __restrict__ x, int c_in, int steps, const u32x4* __restrict__ wp, int n_wt,
     int c_out, const int32_t* __restrict__ pair_in, const int32_t* __restrict__ pair_slot,
     const MapState* __restrict__ st, int64_t cap, int64_t n, float* __restrict__ part) {
-    extern __shared__ uint4 s_b[];
-    __shared__ int32_t s_first[kTaps + 1];      // first tile of each tap (centre: none)
+    constexpr int kRows = 64 * MW;                 // pairs per tile
+    extern __shared__ u32x4 s_b[];
+    __shared__ int32_t s_first[kTaps + 1];        // first tile of each tap (centre: none)
     __shared__ int32_t s_cnt[kTaps];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
@@ -174,7 +220,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_nc(
             const int32_t c = k == kCentre ? 0 : st->tap_count[k];
             s_cnt[k] = c;
             s_first[k] = t;
-            t += (c + kTileM - 1) / kTileM;
+            t += (c + kRows - 1) / kRows;
         }
         s_first[kTaps] = t;
     }
@@ -182,50 +228,56 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_nc(
     const int n_nc = s_first[kTaps];
     const int wt_i = blockIdx.y;
     const int col0 = wt_i * 16 * NBW + r * NBW;
-    const int n16 = steps * NBW * 64;
+    const int64_t n16 = (int64_t)steps * NBW * 64;
+    int last_tap = -1;                            // tap whose one-chunk slab is in LDS
     for (int u = blockIdx.x; u < n_nc; u += gridDim.x) {
         int tap = 0;
         while (tap + 1 < kTaps && s_first[tap + 1] <= u) ++tap;
-        const int j0 = (u - s_first[tap]) * kTileM + w * 16;   // this wave's first pair in the tap
+        const int j0 = (u - s_first[tap]) * kRows + w * 16 * MW;   // this wave's first pair
         const int cnt = s_cnt[tap];
         const int64_t base = (int64_t)tap * cap + j0;
-        const int pi = pair_in[base + r];
-        const int4 ps = *reinterpret_cast<const int4*>(pair_slot + base + 4 * g);
-        const bool a_ok = j0 + r < cnt && pi >= 0 && pi < n;
-        const uint16_t* xrow[1] = {x + (int64_t)(a_ok ? pi : 0) * c_in};
-        u32x4 a[4][1];
-        load_group<1, VEC>(xrow, c_in, steps, 0, g, a);   // in flight while weights are staged
-        const uint4* src = wp + ((int64_t)tap * n_wt + wt_i) * n16;
-        const uint4* b = src + lane;
-        if (LDS) {
-            __syncthreads();                    // the previous tile's reads of s_b are done
-            stage_b(s_b, src, n16);
-            __syncthreads();
-            b = s_b + lane;
+        const uint16_t* xrow[MW];
+        int4 ps[MW];
+#pragma unroll
+        for (int m = 0; m < MW; ++m) {
+            const int pi = pair_in[base + m * 16 + r];
+            ps[m] = *reinterpret_cast<const int4*>(pair_slot + base + m * 16 + 4 * g);
+            const bool ok = j0 + m * 16 + r < cnt && pi >= 0 && pi < n;
+            xrow[m] = x + (int64_t)(ok ? pi : 0) * c_in;
         }
-        f32x4 c[1][NBW];
-        wave_mma<NBW, 1, VEC>(xrow, c_in, steps, b, g, a, c);
+        const u32x4* src = wp + ((int64_t)tap * n_wt + wt_i) * n16;
+        const bool resident = !STREAM && tap == last_tap;     // a one-chunk slab stays in LDS
+        last_tap = tap;
+        u32x4 a[4][MW];
+        load_group<MW, VEC>(xrow, c_in, steps, 0, g, a);
+        u32x4 bw[bg_per<NBW>()];
+        bg_fetch0<NBW>(src, steps, bw);
+        if (!resident) __syncthreads();            // the previous tile's reads of s_b are done
+        f32x4 c[MW][NBW];
+        block_gemm<NBW, MW, VEC, STREAM>(xrow, c_in, steps, src, s_b, lane, g, a, bw, resident, c);
         if (col0 >= c_out) continue;
-        const int slots[4] = {ps.x, ps.y, ps.z, ps.w};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (j0 + 4 * g + j >= cnt || slots[j] < 0) continue;
-            float v[NBW];
+        for (int m = 0; m < MW; ++m) {
+            const int slots[4] = {ps[m].x, ps[m].y, ps[m].z, ps[m].w};
 #pragma unroll
-            for (int nb = 0; nb < NBW; ++nb) v[nb] = c[0][nb][j];
-            store_f32<NBW>(part + (int64_t)slots[j] * c_out + col0, col0, c_out, v);
+            for (int j = 0; j < 4; ++j) {
+                if (j0 + m * 16 + 4 * g + j >= cnt || slots[j] < 0) continue;
+                float v[NBW];
+#pragma unroll
+                for (int nb = 0; nb < NBW; ++nb) v[nb] = c[m][nb][j];
+                store_f32<NBW>(part + (int64_t)slots[j] * c_out + col0, col0, c_out, v);
+            }
         }
     }
 }
 
 // Centre tap + output. Blocks stride over tiles of 64 MW consecutive rows;
-// wave w takes rows +16 MW w .. +16 MW w + 16 MW - 1. With LDS the centre
-// weight slab is staged once per block. A lane's 4 output rows of a
-// fragment are consecutive, so their slab rows form one consecutive run
-// [rowbase[first], rowbase[last] + deg(last)). Every load that does not
-// depend on another is issued first (gathered rows, run bounds, weights);
-// the first kSlabBatch slab rows of the lane's runs are in flight while the
-// MFMAs run, and longer runs take further batches afterwards.
+// wave w takes rows +16 MW w .. +16 MW w + 16 MW - 1. A lane's 4 output rows
+// of a fragment are consecutive, so their slab rows form one consecutive run
+// [rowbase[first], rowbase[last] + deg(last)). The tile's independent loads
+// (gathered rows, run bounds) are issued first; the first kSlabBatch slab
+// rows of the lane's runs are in flight while the weights stream and the
+// MFMAs run; longer runs take further batches afterwards.
 constexpr int kSlabBatch = 4;
 
 // Slab row of flat index t over a lane's MW runs [rb[m][0], rb[m][0] + len[m])
@@ -347,61 +399,39 @@ __device__ __forceinline__ int centre_runs(int64_t row0, int g, int64_t n, int32
     return tot;
 }
 
-template <int NBW, int MW, bool OUT_F32, bool LDS, bool VEC>
-__global__ __launch_bounds__(kGemmThreads) void k_gemm_centre(
-    const uint16_t* __restrict__ x, int c_in, int steps, const uint4* __restrict__ wp, int n_wt,
+template <int NBW, int MW, bool OUT_F32, bool VEC, bool STREAM>
+__global__ __launch_bounds__(kGemmThreads, STREAM ? 1 : 2) void k_gemm_centre(
+    const uint16_t* __restrict__ x, int c_in, int steps, const u32x4* __restrict__ wp, int n_wt,
     int c_out, const uint32_t* __restrict__ mask, const int32_t* __restrict__ rowbase, int64_t n,
     const float* __restrict__ part, void* __restrict__ yv, int relu) {
-    extern __shared__ uint4 s_b[];
+    extern __shared__ u32x4 s_b[];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
     const int wt_i = blockIdx.y;
     const int col0 = wt_i * 16 * NBW + r * NBW;
     const int colc = col0 < c_out ? col0 : 0;     // slab column read by lanes past c_out
-    const int n16 = steps * NBW * 64;
+    const int64_t n16 = (int64_t)steps * NBW * 64;
     const bool vec_part = col0 + NBW <= c_out && (c_out & 3) == 0 && NBW >= 4;
     const int64_t rows_per_tile = 64 * MW;
     const int64_t n_rt = (n + rows_per_tile - 1) / rows_per_tile;
-    int64_t rt = blockIdx.x;
-    if (rt >= n_rt) return;
-    const uint4* src = wp + ((int64_t)kCentre * n_wt + wt_i) * n16;
-    // the MFMAs read B from LDS (LDS) or from global memory: fixed at compile time
-    const uint4* bmma = LDS ? static_cast<const uint4*>(s_b) + lane : src + lane;
-
-    // first tile: every independent load is issued before any wait
-    const uint16_t* xrow[MW];
-    u32x4 a[4][MW];
-    int32_t rb[MW][4];
-    uint32_t mk[MW][4];
-    int64_t row0 = rt * rows_per_tile + w * 16 * MW;
-    centre_tile_loads<MW, VEC>(x, c_in, steps, mask, rowbase, n, row0, r, g, xrow, a, rb, mk);
-    u32x4 bw[8];
-    if (LDS) {                                    // first round of the weight slab
-        const u32x4* src4 = reinterpret_cast<const u32x4*>(src);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int i = threadIdx.x + j * kGemmThreads;
-            bw[j] = src4[i < n16 ? i : n16 - 1];
-        }
-    }
-    int32_t re[MW], len[MW];
-    int tot = centre_runs<MW>(row0, g, n, rb, mk, re, len);
-    float pv[kSlabBatch][NBW];
-    load_slab<NBW, MW>(part, c_out, colc, vec_part, rb, len, tot, 0, pv);
-    if (LDS) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int i = threadIdx.x + j * kGemmThreads;
-            if (i < n16) reinterpret_cast<u32x4*>(s_b)[i] = bw[j];
-        }
-        if (n16 > 8 * kGemmThreads)               // wide inputs: the remaining rounds
-            for (int i = 8 * kGemmThreads + threadIdx.x; i < n16; i += kGemmThreads) s_b[i] = src[i];
-        __syncthreads();
-    }
-
-    for (;;) {
+    const u32x4* src = wp + ((int64_t)kCentre * n_wt + wt_i) * n16;
+    for (int64_t rt = blockIdx.x; rt < n_rt; rt += gridDim.x) {
+        const int64_t row0 = rt * rows_per_tile + w * 16 * MW;
+        const uint16_t* xrow[MW];
+        u32x4 a[4][MW];
+        int32_t rb[MW][4];
+        uint32_t mk[MW][4];
+        const bool resident = !STREAM && rt != blockIdx.x;    // the one-chunk slab stays in LDS
+        centre_tile_loads<MW, VEC>(x, c_in, steps, mask, rowbase, n, row0, r, g, xrow, a, rb, mk);
+        u32x4 bw[bg_per<NBW>()];
+        if (STREAM || !resident) bg_fetch0<NBW>(src, steps, bw);
+        int32_t re[MW], len[MW];
+        const int tot = centre_runs<MW>(row0, g, n, rb, mk, re, len);
+        float pv[kSlabBatch][NBW];
+        load_slab<NBW, MW>(part, c_out, colc, vec_part, rb, len, tot, 0, pv);
+        if (!resident) __syncthreads();            // the previous tile's reads of s_b are done
         f32x4 c[MW][NBW];
-        wave_mma<NBW, MW, VEC>(xrow, c_in, steps, bmma, g, a, c);
+        block_gemm<NBW, MW, VEC, STREAM>(xrow, c_in, steps, src, s_b, lane, g, a, bw, resident, c);
         float v[MW][4][NBW];
 #pragma unroll
         for (int m = 0; m < MW; ++m)
@@ -422,78 +452,89 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_centre(
                 if (row >= n || col0 >= c_out) continue;
                 store_row<NBW, OUT_F32>(yv, row, c_out, col0, v[m][j], relu);
             }
-        rt += gridDim.x;
-        if (rt >= n_rt) break;
-        row0 = rt * rows_per_tile + w * 16 * MW;
-        centre_tile_loads<MW, VEC>(x, c_in, steps, mask, rowbase, n, row0, r, g, xrow, a, rb, mk);
-        tot = centre_runs<MW>(row0, g, n, rb, mk, re, len);
-        load_slab<NBW, MW>(part, c_out, colc, vec_part, rb, len, tot, 0, pv);
     }
 }
 
-// Largest dynamic LDS a block of these kernels may ask for.
-constexpr size_t kLdsCap = 160 * 1024;
+// LDS of both kernels: two weight chunks when streaming, else one.
+template <int NBW, bool STREAM>
+constexpr size_t gemm_lds_bytes() { return (STREAM ? 2 : 1) * (size_t)kChunk * NBW * 64 * 16; }
 
-template <typename F>
-bool allow_lds(F* fn, size_t bytes) {
-    if (bytes <= 64 * 1024) return true;
-    if (bytes > kLdsCap) return false;
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) != hipSuccess) {
-        (void)hipGetLastError();
-        return false;
-    }
-    return true;
+// Row fragments per wave: wide inputs reuse each streamed weight chunk over
+// more rows (only with 16-byte row loads, which keep the register budget);
+// narrow ones keep more, smaller tiles in flight (the pair lists of a
+// sparse scan hold few pairs per tap).
+inline int mw_for(int c_in) { return c_in >= 256 && (c_in & 7) == 0 ? 4 : 2; }
+inline int mw_nc_for(int c_in) { return c_in >= 256 && (c_in & 7) == 0 ? 4 : 1; }
+
+// Lets a kernel take `bytes` of dynamic LDS (once per kernel; the default cap
+// is 64 KiB including the kernel's static LDS).
+template <typename K>
+bool lds_ok(K kernel, size_t bytes) {
+    if (bytes + 1024 <= 64 * 1024) return true;
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) == hipSuccess;
 }
 
-template <int NBW, bool VEC>
-void launch_nc_t(dim3 grid, hipStream_t s, const uint16_t* x, int c_in, int steps,
-                 const uint4* wp, int n_wt, int c_out, const int32_t* pi, const int32_t* ps,
-                 const MapState* st, int64_t cap, int64_t n, float* part) {
-    const size_t lds = (size_t)steps * NBW * 1024;
-    if (allow_lds(k_gemm_nc<NBW, true, VEC>, lds))
-        launch(k_gemm_nc<NBW, true, VEC>, grid, kGemmThreads, lds, s, x, c_in, steps, wp, n_wt, c_out,
-                                                                  pi, ps, st, cap, n, part);
-    else
-        launch(k_gemm_nc<NBW, false, VEC>, grid, kGemmThreads, 0, s, x, c_in, steps, wp, n_wt, c_out,
-                                                                 pi, ps, st, cap, n, part);
+template <int NBW, int MW, bool VEC, bool STREAM>
+void launch_nc_t(dim3 grid, hipStream_t s, const uint16_t* x, int c_in, int steps, const u32x4* wp,
+                 int n_wt, int c_out, const int32_t* pi, const int32_t* ps, const MapState* st,
+                 int64_t cap, int64_t n, float* part) {
+    constexpr size_t lds = gemm_lds_bytes<NBW, STREAM>();
+    static const bool ok = lds_ok(k_gemm_nc<NBW, MW, VEC, STREAM>, lds);
+    (void)ok;
+    launch(k_gemm_nc<NBW, MW, VEC, STREAM>, grid, kGemmThreads, lds, s, x, c_in, steps, wp, n_wt,
+           c_out, pi, ps, st, cap, n, part);
 }
 
 template <int NBW>
-void launch_nc(dim3 grid, hipStream_t s, const uint16_t* x, int c_in, int steps, const uint4* wp,
-               int n_wt, int c_out, const int32_t* pi, const int32_t* ps, const MapState* st,
-               int64_t cap, int64_t n, float* part) {
-    if ((c_in & 7) == 0)
-        launch_nc_t<NBW, true>(grid, s, x, c_in, steps, wp, n_wt, c_out, pi, ps, st, cap, n, part);
+void launch_nc(dim3 grid, hipStream_t s, int mw, const uint16_t* x, int c_in, int steps,
+               const u32x4* wp, int n_wt, int c_out, const int32_t* pi, const int32_t* ps,
+               const MapState* st, int64_t cap, int64_t n, float* part) {
+    const bool vec = (c_in & 7) == 0;
+    if (mw == 4)                                   // mw_nc_for: wide, 16-byte row loads
+        launch_nc_t<NBW, 4, true, true>(grid, s, x, c_in, steps, wp, n_wt, c_out, pi, ps, st, cap, n, part);
+    else if (steps > kChunk)
+        launch_nc_t<NBW, 1, false, true>(grid, s, x, c_in, steps, wp, n_wt, c_out, pi, ps, st, cap, n, part);
+    else if (vec)
+        launch_nc_t<NBW, 1, true, false>(grid, s, x, c_in, steps, wp, n_wt, c_out, pi, ps, st, cap, n, part);
     else
-        launch_nc_t<NBW, false>(grid, s, x, c_in, steps, wp, n_wt, c_out, pi, ps, st, cap, n, part);
+        launch_nc_t<NBW, 1, false, false>(grid, s, x, c_in, steps, wp, n_wt, c_out, pi, ps, st, cap, n, part);
 }
 
-template <int NBW, int MW, bool OUT_F32, bool VEC>
+template <int NBW, int MW, bool OUT_F32, bool VEC, bool STREAM>
 void launch_centre_t(dim3 grid, hipStream_t s, const uint16_t* x, int c_in, int steps,
-                     const uint4* wp, int n_wt, int c_out, const uint32_t* mask,
+                     const u32x4* wp, int n_wt, int c_out, const uint32_t* mask,
                      const int32_t* rowbase, int64_t n, const float* part, void* y, int relu) {
-    const size_t lds = (size_t)steps * NBW * 1024;
-    if (allow_lds(k_gemm_centre<NBW, MW, OUT_F32, true, VEC>, lds))
-        launch(k_gemm_centre<NBW, MW, OUT_F32, true, VEC>, grid, kGemmThreads, lds, s, 
-            x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, relu);
+    constexpr size_t lds = gemm_lds_bytes<NBW, STREAM>();
+    static const bool ok = lds_ok(k_gemm_centre<NBW, MW, OUT_F32, VEC, STREAM>, lds);
+    (void)ok;
+    launch(k_gemm_centre<NBW, MW, OUT_F32, VEC, STREAM>, grid, kGemmThreads, lds, s, x, c_in,
+           steps, wp, n_wt, c_out, mask, rowbase, n, part, y, relu);
+}
+
+template <int NBW, int MW, bool VEC, bool STREAM>
+void launch_centre_mw(dim3 grid, hipStream_t s, bool out_f32, const uint16_t* x, int c_in,
+                      int steps, const u32x4* wp, int n_wt, int c_out, const uint32_t* mask,
+                      const int32_t* rowbase, int64_t n, const float* part, void* y, int relu) {
+    if (out_f32)
+        launch_centre_t<NBW, MW, true, VEC, STREAM>(grid, s, x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, relu);
     else
-        launch(k_gemm_centre<NBW, MW, OUT_F32, false, VEC>, grid, kGemmThreads, 0, s, 
-            x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, relu);
+        launch_centre_t<NBW, MW, false, VEC, STREAM>(grid, s, x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, relu);
 }
 
 template <int NBW>
-void launch_centre(dim3 grid, hipStream_t s, bool out_f32, const uint16_t* x, int c_in, int steps,
-                   const uint4* wp, int n_wt, int c_out, const uint32_t* mask,
+void launch_centre(dim3 grid, hipStream_t s, int mw, bool out_f32, const uint16_t* x, int c_in,
+                   int steps, const u32x4* wp, int n_wt, int c_out, const uint32_t* mask,
                    const int32_t* rowbase, int64_t n, const float* part, void* y, int relu) {
     const bool vec = (c_in & 7) == 0;
-    if (out_f32) {
-        if (vec) launch_centre_t<NBW, 2, true, true>(grid, s, x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, relu);
-        else launch_centre_t<NBW, 2, true, false>(grid, s, x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, relu);
-    } else {
-        if (vec) launch_centre_t<NBW, 2, false, true>(grid, s, x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, relu);
-        else launch_centre_t<NBW, 2, false, false>(grid, s, x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, relu);
-    }
+    if (mw == 4)                                   // mw_for: wide, 16-byte row loads
+        launch_centre_mw<NBW, 4, true, true>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, relu);
+    else if (steps > kChunk)
+        launch_centre_mw<NBW, 2, false, true>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, relu);
+    else if (vec)
+        launch_centre_mw<NBW, 2, true, false>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, relu);
+    else
+        launch_centre_mw<NBW, 2, false, false>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, relu);
 }
 
 }  // namespace
@@ -521,16 +562,17 @@ hipError_t launch_gemm_nc(const uint16_t* x, int c_in, const void* wpacked, int 
     const int steps = (c_in + 31) / 32;
     const int nbw = nbw_for(c_out);
     const int n_wt = (c_out + 16 * nbw - 1) / (16 * nbw);
-    int64_t gx = (kTaps - 1) * (cap / kTileM);     // tiles if every tap were full
+    const int mw = mw_nc_for(c_in);
+    int64_t gx = (kTaps - 1) * (cap / (64 * mw));  // tiles if every tap were full
     if (gx > (int64_t)n_cu * 2) gx = (int64_t)n_cu * 2;
     if (gx < 1) gx = 1;
     dim3 grid((unsigned)gx, (unsigned)n_wt);
-    const uint4* wp = (const uint4*)wpacked;
+    const u32x4* wp = (const u32x4*)wpacked;
     switch (nbw) {
-        case 1: launch_nc<1>(grid, s, x, c_in, steps, wp, n_wt, c_out, pair_in, pair_slot, st, cap, n, part); break;
-        case 2: launch_nc<2>(grid, s, x, c_in, steps, wp, n_wt, c_out, pair_in, pair_slot, st, cap, n, part); break;
-        case 4: launch_nc<4>(grid, s, x, c_in, steps, wp, n_wt, c_out, pair_in, pair_slot, st, cap, n, part); break;
-        default: launch_nc<8>(grid, s, x, c_in, steps, wp, n_wt, c_out, pair_in, pair_slot, st, cap, n, part); break;
+        case 1: launch_nc<1>(grid, s, mw, x, c_in, steps, wp, n_wt, c_out, pair_in, pair_slot, st, cap, n, part); break;
+        case 2: launch_nc<2>(grid, s, mw, x, c_in, steps, wp, n_wt, c_out, pair_in, pair_slot, st, cap, n, part); break;
+        case 4: launch_nc<4>(grid, s, mw, x, c_in, steps, wp, n_wt, c_out, pair_in, pair_slot, st, cap, n, part); break;
+        default: launch_nc<8>(grid, s, mw, x, c_in, steps, wp, n_wt, c_out, pair_in, pair_slot, st, cap, n, part); break;
     }
     return hipGetLastError();
 }
@@ -543,16 +585,17 @@ hipError_t launch_gemm_centre(const uint16_t* x, int c_in, const void* wpacked, 
     const int steps = (c_in + 31) / 32;
     const int nbw = nbw_for(c_out);
     const int n_wt = (c_out + 16 * nbw - 1) / (16 * nbw);
-    int64_t row_tiles = (n + 2 * kTileM - 1) / (2 * kTileM);   // 128-row tiles (MW = 2)
-    int64_t gx = row_tiles < (int64_t)n_cu * 2 ? row_tiles : (int64_t)n_cu * 2;
+    const int mw = mw_for(c_in);
+    const int64_t row_tiles = (n + 64 * mw - 1) / (64 * mw);
+    const int64_t gx = row_tiles < (int64_t)n_cu * 2 ? row_tiles : (int64_t)n_cu * 2;
     dim3 grid((unsigned)gx, (unsigned)n_wt);
-    const uint4* wp = (const uint4*)wpacked;
+    const u32x4* wp = (const u32x4*)wpacked;
     const int rl = relu ? 1 : 0;
     switch (nbw) {
-        case 1: launch_centre<1>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, rl); break;
-        case 2: launch_centre<2>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, rl); break;
-        case 4: launch_centre<4>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, rl); break;
-        default: launch_centre<8>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, rl); break;
+        case 1: launch_centre<1>(grid, s, mw, out_f32, x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, rl); break;
+        case 2: launch_centre<2>(grid, s, mw, out_f32, x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, rl); break;
+        case 4: launch_centre<4>(grid, s, mw, out_f32, x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, rl); break;
+        default: launch_centre<8>(grid, s, mw, out_f32, x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, rl); break;
     }
     return hipGetLastError();
 }

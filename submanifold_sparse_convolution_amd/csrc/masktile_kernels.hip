@@ -87,7 +87,6 @@ __device__ __forceinline__ void heavy_tile(
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
     const int wt = blockIdx.y;
-    const int kq = steps * 8;
     const int64_t t0 = (int64_t)blockIdx.x * kMtRows;
     const int64_t n16 = (int64_t)steps * NBW * 64;
     const int n_taps = 1 + __builtin_popcount(rest);
@@ -128,7 +127,7 @@ __device__ __forceinline__ void heavy_tile(
         _Pragma("unroll") for (int f_ = 0; f_ < 4; ++f_) {                                        \
             const int id_ = tap_ == kCentre ? (int)rowf[f_] : s_nb[(f_ * 16 + r) * kTaps + tap_]; \
             const uint16_t* xr_ = id_ >= 0 && id_ < n ? x + (int64_t)id_ * c_in : zrow;          \
-            A[f_] = load_a4<VEC>(xr_, g * kq + st_ * 8, c_in);                                    \
+            A[f_] = load_a4<VEC>(xr_, st_ * 32 + g * 8, c_in);                                    \
         }                                                                                         \
     }
 #define SMC_HV_MMA(A, B)                                                                          \
@@ -204,7 +203,6 @@ __global__ __launch_bounds__(kGemmThreads) void k_conv_masktile(
     const int r = lane & 15, g = lane >> 4;
     const int wt = blockIdx.y;
     const int col0 = wt * 16 * NBW + r * NBW;
-    const int kq = steps * 8;
     const int n_chunks = (steps + kChunkSteps - 1) / kChunkSteps;
     const int64_t t0 = (int64_t)blockIdx.x * kMtRows;     // first sorted position of the tile
     const int64_t s0 = t0 + w * 16;
@@ -229,7 +227,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_conv_masktile(
         const uint16_t* xr_ = (XR);                                                               \
         _Pragma("unroll") for (int q_ = 0; q_ < kChunkSteps; ++q_) {                              \
             const int st_ = (C) * kChunkSteps + q_;                                               \
-            A[q_] = load_a4<VEC>(xr_, st_ < steps ? g * kq + st_ * 8 : c_in, c_in);               \
+            A[q_] = load_a4<VEC>(xr_, st_ < steps ? st_ * 32 + g * 8 : c_in, c_in);               \
         }                                                                                         \
     }
 

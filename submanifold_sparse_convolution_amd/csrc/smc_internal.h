@@ -9,7 +9,9 @@ namespace smc {
 
 constexpr int kTaps = 27;
 constexpr int kCentre = 13;
-constexpr int kTileM = 64;          // pairs per GEMM tile (4 waves x 16 rows)
+constexpr int kTileM = 64;          // granularity of the per-tap pair counts reported as padded
+constexpr int kCapAlign = 256;      // each tap's run of the pair arrays: n rounded up to this
+                                    // (a multiple of every GEMM tile height)
 constexpr int kBlock = 256;         // threads per block for the map kernels
 
 // Per-kernel timing. While a stage timer of the API is active, take() hands

@@ -456,7 +456,7 @@ int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     const bool want_pairs = !(flags & SMC_BUILD_NO_PAIRS);
     const bool want_sort = !(flags & SMC_BUILD_NO_SORT);
     const int64_t nn = n > 0 ? n : 1;
-    const int64_t cap = (nn + kTileM - 1) / kTileM * kTileM;
+    const int64_t cap = (nn + kCapAlign - 1) / kCapAlign * kCapAlign;
     size_t look_bytes = sort_look_bytes(nn);
     const size_t look_c = compact_look_bytes(nn);
     if (look_c > look_bytes) look_bytes = look_c;
