@@ -10,7 +10,8 @@ Sources (the pages this follows):
   gfx950)", FlyDSL pull request #942 -- sections "Summary", "Design, and the measurements behind it", "Test plan",
   and its commit messages.
 * [P5] "Sparse convolution in FP32", DriveRT project page -- sections
-  "The starting point", "Neighbour masks and sorted rows".
+  "The starting point", "Neighbour masks and sorted rows", "Calibrated bit
+  order", "Offset-group partitioning".
 
 What is computed ([P5] "The starting point"; [P1] Summary): for every
 active voxel p of the set S (the output set is S itself),
@@ -28,6 +29,9 @@ Readings fixed here where the pages are silent:
   neighbours never cross batches.
 * duplicate coordinates are a caller error (raised here).
 * mask sort: ascending plain mask value, ties by ascending row.
+* calibrated bit order and offset groups: see ``group_row_orders`` and
+  ``calibrate_order`` (a greedy search; the pages do not say how the order
+  or the groups are chosen).
 * pair lists: tap-major, and within a tap in ascending output row (the
   order inside a tap does not change the sum; [P1]'s compaction lists each
   tap's rows in the order it scans them).
@@ -158,6 +162,129 @@ def mask_sort(mask: np.ndarray) -> np.ndarray:
     m = [int(v) for v in np.asarray(mask).tolist()]
     order = sorted(range(len(m)), key=lambda r: (m[r], r))
     return np.asarray(order, dtype=np.int32)
+
+
+# --------------------------------------------------------------------------
+# mask-tile row orders ([P5] "Calibrated bit order", "Offset-group
+# partitioning"; "Neighbour masks and sorted rows")
+# --------------------------------------------------------------------------
+
+def _check_order(bit_order, group_of):
+    order = list(range(TAPS - 1, -1, -1)) if bit_order is None else [int(t) for t in bit_order]
+    if sorted(order) != list(range(TAPS)):
+        raise ValueError("bit_order must list each of the 27 taps once")
+    groups = [0] * TAPS if group_of is None else [int(g) for g in group_of]
+    if len(groups) != TAPS or min(groups) < 0:
+        raise ValueError("group_of must give a group index >= 0 for each tap")
+    n_groups = max(groups) + 1
+    if sorted(set(groups)) != list(range(n_groups)):
+        raise ValueError("group indices must be 0 .. G-1 with no gap")
+    if groups[CENTRE] != n_groups - 1:
+        raise ValueError("the centre tap must be in the last group")
+    return order, groups, n_groups
+
+
+def group_row_orders(mask: np.ndarray, bit_order=None, group_of=None):
+    """Row order of every offset group for the mask-tile GEMM.
+
+    [P5] "Calibrated bit order": rows are sorted by their mask with its bits
+    taken in a chosen order (``bit_order`` lists the taps from most to least
+    significant; None is the plain mask value, tap 26 first).
+    [P5] "Offset-group partitioning": the taps are split into groups
+    (``group_of[k]`` is tap k's group) and each group has its own row order,
+    under the mask restricted to the group's taps. Reading fixed here: group
+    g lists the rows with at least one tap in the group, by (restricted mask
+    in bit order, row); the rows with none follow, by row. The centre tap
+    must be in the last group, so the last group holds every row (the page's
+    last launch spans every row).
+
+    Returns (orders, counts): orders is int32 [G, N] (row ids), counts[g]
+    the number of rows of group g that have a tap in it.
+    """
+    order, groups, n_groups = _check_order(bit_order, group_of)
+    m = [int(v) for v in np.asarray(mask).tolist()]
+    n = len(m)
+    out = np.zeros((n_groups, n), dtype=np.int32)
+    counts = []
+    for g in range(n_groups):
+        taps = [t for t in order if groups[t] == g]          # most significant first
+        keys = []
+        for r in range(n):
+            bits = tuple((m[r] >> t) & 1 for t in taps)
+            keys.append((0 if any(bits) else 1, bits, r))
+        keys.sort()
+        out[g] = [k[2] for k in keys]
+        counts.append(sum(1 for k in keys if k[0] == 0))
+    return out, np.asarray(counts, dtype=np.int64)
+
+
+def tile_work(mask: np.ndarray, rows, count: int, taps=None, tile: int = 64) -> int:
+    """Tap-rows a mask-tile pass executes ([P5] "Neighbour masks and sorted
+    rows": a tile evaluates the union of its rows' offsets for every row).
+
+    The first ``count`` entries of ``rows`` are cut into consecutive tiles of
+    ``tile`` rows; each tile costs its row count times the number of taps
+    (of ``taps``, default all 27) present in at least one of its rows.
+    """
+    allowed = set(range(TAPS)) if taps is None else {int(t) for t in taps}
+    m = [int(v) for v in np.asarray(mask).tolist()]
+    work = 0
+    for s in range(0, int(count), tile):
+        part = [int(r) for r in rows[s:min(s + tile, int(count))]]
+        union = {t for r in part for t in allowed if (m[r] >> t) & 1}
+        work += len(part) * len(union)
+    return work
+
+
+def calibrate_order(mask: np.ndarray, n_groups: int = 1, tile: int = 64):
+    """A bit order and offset groups chosen on a calibration map.
+
+    The pages calibrate a permutation of the 27 bits offline ([P5]
+    "Calibrated bit order") and split the offsets into a few groups ([P5]
+    "Offset-group partitioning") without saying how either is chosen. The
+    reading fixed here is a greedy search on the executed work of the mask
+    tiles (``tile_work`` of the one-group order):
+
+    1. Start from the 26 off-centre taps by ascending count of rows that
+       have them (ties: lower tap first); the centre, present in every row,
+       is always least significant.
+    2. For each position from the most significant down, try every
+       remaining tap there, the others following in their current order,
+       and keep the one with the least work (ties: the earlier candidate).
+    3. Groups: the off-centre taps, in the chosen order, are cut into
+       ``n_groups`` consecutive runs, run g holding positions
+       floor(26 g / G) .. floor(26 (g+1) / G) - 1; the centre joins the last.
+
+    Returns (bit_order list[27], group_of list[27]).
+    """
+    if not 1 <= n_groups <= 26:
+        raise ValueError("n_groups must be in 1 .. 26")
+    m = np.asarray(mask, dtype=np.uint32)
+    counts = [int(((m >> np.uint32(t)) & 1).sum()) for t in range(TAPS)]
+    remaining = sorted((t for t in range(TAPS) if t != CENTRE), key=lambda t: (counts[t], t))
+    chosen: list = []
+    n = len(m)
+
+    def work_of(order):
+        orders, cnt = group_row_orders(m, order, None)
+        return tile_work(m, orders[0], cnt[0], None, tile)
+
+    while remaining:
+        best_t, best_w = None, None
+        for t in remaining:
+            cand = chosen + [t] + [r for r in remaining if r != t] + [CENTRE]
+            w = work_of(cand) if n else 0
+            if best_w is None or w < best_w:
+                best_t, best_w = t, w
+        chosen.append(best_t)
+        remaining.remove(best_t)
+    order = chosen + [CENTRE]
+    group_of = [0] * TAPS
+    for g in range(n_groups):
+        for pos in range((26 * g) // n_groups, (26 * (g + 1)) // n_groups):
+            group_of[chosen[pos]] = g
+    group_of[CENTRE] = n_groups - 1
+    return order, group_of
 
 
 def compact_pairs(nbr: np.ndarray, mask: np.ndarray):

@@ -179,6 +179,90 @@ def check_hand_examples():
         assert np.array_equal(r["y"], np.asarray(e["y"])), e["name"] + ": y"
 
 
+MASK_ORDERS = os.path.join(os.path.dirname(__file__), "golden", "mask_orders.json")
+
+
+def golden_bit_order(head):
+    return list(head) + [t for t in range(27) if t not in head and t != 13] + [13]
+
+
+def check_mask_order_examples():
+    e = json.load(open(MASK_ORDERS))
+    mask = np.asarray([sum(1 << t for t in taps) for taps in e["rows_taps"]], np.uint32)
+    order = golden_bit_order(e["bit_order_head"])
+    two = [0 if t in e["group0_taps"] else 1 for t in range(27)]
+    args = {"plain_one_group": (None, None), "ordered_one_group": (order, None),
+            "ordered_two_groups": (order, two)}
+    got = {}
+    for name, (bo, go) in args.items():
+        orders, counts = so.group_row_orders(mask, bo, go)
+        want = e["cases"][name]
+        assert orders.tolist() == want["orders"], name + ": orders"
+        assert counts.tolist() == want["counts"], name + ": counts"
+        got[name] = (orders, counts)
+    tw = e["tile_work_tile2"]
+    for name in ("plain_one_group", "ordered_one_group"):
+        o, c = got[name]
+        assert so.tile_work(mask, o[0], c[0], None, 2) == tw[name], name + ": tile work"
+    o, c = got["ordered_two_groups"]
+    g0 = e["group0_taps"]
+    g1 = [t for t in range(27) if t not in g0]
+    assert [so.tile_work(mask, o[0], c[0], g0, 2),
+            so.tile_work(mask, o[1], c[1], g1, 2)] == tw["ordered_two_groups"], "grouped tile work"
+    assert so.tile_work(mask, o[1], c[1], None, 1) == tw["useful"], "tile of one row = popcount"
+
+
+def check_group_orders(mask, bit_order, group_of):
+    """Each group's order, checked by comparing neighbours in the list.
+
+    Rows with a tap of the group come first; two consecutive ones must be
+    in order at the first tap of the group (in bit order) where their masks
+    differ, the earlier row lacking it, or, with equal restricted masks, be
+    in row order. The rows without a tap follow in row order.
+    """
+    orders, counts = so.group_row_orders(mask, bit_order, group_of)
+    order = list(range(26, -1, -1)) if bit_order is None else list(bit_order)
+    groups = [0] * 27 if group_of is None else list(group_of)
+    n = len(mask)
+    G = max(groups) + 1
+    assert orders.shape == (G, n)
+    for g in range(G):
+        taps = [t for t in order if groups[t] == g]
+        rows = orders[g].tolist()
+        assert sorted(rows) == list(range(n)), f"group {g}: not a permutation"
+        has = [any((int(mask[r]) >> t) & 1 for t in taps) for r in range(n)]
+        c = int(counts[g])
+        assert c == sum(has), f"group {g}: count"
+        if g == G - 1:
+            assert c == n, "last group must hold every row"
+        assert all(has[r] for r in rows[:c]) and not any(has[r] for r in rows[c:])
+        for a, b in zip(rows[:c], rows[1:c]):
+            diff = [t for t in taps if ((int(mask[a]) >> t) & 1) != ((int(mask[b]) >> t) & 1)]
+            if diff:
+                assert not (int(mask[a]) >> diff[0]) & 1, f"group {g}: rows {a}, {b} out of order"
+            else:
+                assert a < b, f"group {g}: equal masks not by row"
+        assert rows[c:] == sorted(rows[c:]), f"group {g}: rows without a tap not by row"
+
+
+def check_calibration(mask, n_groups, tile=64):
+    order, group_of = so.calibrate_order(mask, n_groups, tile)
+    assert sorted(order) == list(range(27)) and order[-1] == 13
+    assert group_of[13] == n_groups - 1
+    sizes = [sum(1 for t in range(27) if t != 13 and group_of[t] == g) for g in range(n_groups)]
+    assert sizes == [(26 * (g + 1)) // n_groups - (26 * g) // n_groups for g in range(n_groups)]
+    pos = {t: i for i, t in enumerate(order)}
+    assert all(group_of[a] <= group_of[b] for a in range(27) for b in range(27)
+               if a != 13 and b != 13 and pos[a] < pos[b]), "groups are not runs of the order"
+    # the search starts from the taps by ascending count and never gets worse
+    cnt = [int(((mask >> np.uint32(t)) & 1).sum()) for t in range(27)]
+    start = sorted((t for t in range(27) if t != 13), key=lambda t: (cnt[t], t)) + [13]
+    o1, c1 = so.group_row_orders(mask, order)
+    o0, c0 = so.group_row_orders(mask, start)
+    assert so.tile_work(mask, o1[0], c1[0], None, tile) <= so.tile_work(mask, o0[0], c0[0], None, tile)
+    return order, group_of
+
+
 def check_bf16_vs_torch(vals):
     vals = np.asarray(vals, np.float32)
     want = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
@@ -203,6 +287,69 @@ def bf16_test_values():
 
 def test_hand_worked_examples():
     check_hand_examples()
+
+
+def test_mask_order_hand_examples():
+    check_mask_order_examples()
+
+
+@pytest.mark.parametrize("groups", [None, "dx", "three_runs"])
+@pytest.mark.parametrize("order", [None, "reversed", "shuffled"])
+def test_group_orders_by_neighbour_comparison(order, groups):
+    coords = synth.tiny_coords(seed=4, n=600, side=12)
+    _, mask = so.build_kernel_map(coords)
+    bo = {None: None, "reversed": list(range(27)),
+          "shuffled": [int(t) for t in np.random.default_rng(3).permutation(27)]}[order]
+    go = {None: None,
+          "dx": [{0: 0, 2: 1, 1: 2}[k // 9] for k in range(27)],
+          "three_runs": [min(k // 9, 2) if k != 13 else 2 for k in range(27)]}[groups]
+    check_group_orders(mask, bo, go)
+
+
+def test_plain_single_group_is_mask_sort():
+    coords = synth.tiny_coords(seed=5, n=500, side=14)
+    _, mask = so.build_kernel_map(coords)
+    orders, counts = so.group_row_orders(mask)
+    check_perm(mask, orders[0])
+    assert counts.tolist() == [len(mask)]
+
+
+def test_single_bit_masks_sort_by_reverse_bit_order():
+    # row r has only tap order[r] (and no centre): least significant bit first
+    order = [int(t) for t in np.random.default_rng(9).permutation(27)]
+    order.remove(13)
+    order.append(13)
+    mask = np.asarray([1 << t for t in order], np.uint32)
+    orders, _ = so.group_row_orders(mask, order)
+    assert orders[0].tolist() == list(range(26, -1, -1))
+
+
+def test_tile_work_limits():
+    coords = synth.tiny_coords(seed=6, n=700, side=12)
+    _, mask = so.build_kernel_map(coords)
+    rows = np.arange(len(mask))
+    pop = sum(bin(int(v)).count("1") for v in mask)
+    assert so.tile_work(mask, rows, len(mask), None, 1) == pop
+    union = bin(int(np.bitwise_or.reduce(mask))).count("1")
+    assert so.tile_work(mask, rows, len(mask), None, len(mask)) == len(mask) * union
+    assert so.tile_work(mask, rows, 0) == 0
+
+
+@pytest.mark.parametrize("n_groups", [1, 3])
+def test_calibration_properties(n_groups):
+    coords = synth.tiny_coords(seed=7, n=500, side=13)
+    _, mask = so.build_kernel_map(coords)
+    check_calibration(mask, n_groups, tile=16)
+
+
+def test_order_argument_errors():
+    mask = np.zeros(3, np.uint32)
+    with pytest.raises(ValueError):
+        so.group_row_orders(mask, list(range(26)) + [0])
+    with pytest.raises(ValueError):
+        so.group_row_orders(mask, None, [0] * 13 + [0] + [1] * 13)     # centre not last
+    with pytest.raises(ValueError):
+        so.group_row_orders(mask, None, [0] * 13 + [2] + [2] * 13)     # gap in group ids
 
 
 def test_bf16_rounding_matches_torch():
@@ -461,3 +608,56 @@ def test_planted_batch_mixing(monkeypatch):
         return r
     monkeypatch.setattr(so, "_rows_bxyz", no_batch)
     assert _fails(check_hand_examples)
+
+
+def test_planted_descending_group_order(monkeypatch):
+    orig = so.group_row_orders
+
+    def broken(mask, bit_order=None, group_of=None):
+        o, c = orig(mask, bit_order, group_of)
+        o = o.copy()
+        for g in range(o.shape[0]):
+            o[g, :c[g]] = o[g, :c[g]][::-1]
+        return o, c
+    monkeypatch.setattr(so, "group_row_orders", broken)
+    coords = synth.tiny_coords(seed=4, n=300, side=10)
+    _, mask = so.build_kernel_map(coords)
+    assert _fails(check_group_orders, mask, None, None)
+    assert _fails(check_mask_order_examples)
+
+
+def test_planted_plain_order_ignored(monkeypatch):
+    orig = so.group_row_orders
+    monkeypatch.setattr(so, "group_row_orders", lambda m, b=None, g=None: orig(m, None, g))
+    coords = synth.tiny_coords(seed=4, n=300, side=10)
+    _, mask = so.build_kernel_map(coords)
+    assert _fails(check_group_orders, mask, list(range(27)), None)
+    assert _fails(check_mask_order_examples)
+
+
+def test_planted_group_without_empty_rows_last(monkeypatch):
+    orig = so.group_row_orders
+
+    def broken(mask, bit_order=None, group_of=None):
+        o, c = orig(mask, bit_order, group_of)
+        return o, np.full_like(c, len(mask))     # every row claimed by every group
+    monkeypatch.setattr(so, "group_row_orders", broken)
+    coords = synth.tiny_coords(seed=4, n=300, side=10)
+    _, mask = so.build_kernel_map(coords)
+    go = [min(k // 9, 2) if k != 13 else 2 for k in range(27)]
+    assert _fails(check_group_orders, mask, None, go)
+
+
+def test_planted_calibration_takes_worst(monkeypatch):
+    orig_tw = so.tile_work
+    monkeypatch.setattr(so, "tile_work", lambda *a, **k: -orig_tw(*a, **k))
+    coords = synth.tiny_coords(seed=7, n=300, side=11)
+    _, mask = so.build_kernel_map(coords)
+    # the search now maximises the work; the check measures with the true work
+    order, _ = so.calibrate_order(mask, 1, 16)
+    monkeypatch.setattr(so, "tile_work", orig_tw)
+    cnt = [int(((mask >> np.uint32(t)) & 1).sum()) for t in range(27)]
+    start = sorted((t for t in range(27) if t != 13), key=lambda t: (cnt[t], t)) + [13]
+    o1, c1 = so.group_row_orders(mask, order)
+    o0, c0 = so.group_row_orders(mask, start)
+    assert so.tile_work(mask, o1[0], c1[0], None, 16) > so.tile_work(mask, o0[0], c0[0], None, 16)
