@@ -101,6 +101,8 @@ typedef struct smc_map_info_s {
     int64_t n_tiles;        /* pairs_padded / tile_m: GEMM tiles of all taps (0 without pairs) */
     int64_t tap_count[27];  /* pairs per tap */
     int32_t status;         /* smc_status of the build's device-side checks */
+    int32_t n_groups;       /* offset groups of the mask-tile row orders (0: map not sorted) */
+    int64_t group_rows[4];  /* rows with a tap of each group (the last group: every row) */
 } smc_map_info_t;
 
 /* Create an empty map handle. *out receives it. No device memory is taken yet. */
@@ -162,7 +164,11 @@ int smc_map_info(smc_map* map, smc_map_info_t* info);
  * a host pointer or NULL (skipped):
  *   nbr      int32 [n, 27]  row of c_i + d_k, or -1
  *   mask     uint32 [n]     bit k set iff nbr[i, k] >= 0
- *   perm     int32 [n]      rows in ascending (mask, row) order (needs a sorted map)
+ *   perm     int32 [G, n]   G = info.n_groups row orders (needs a sorted map). With
+ *                           the plain order (G = 1): rows by ascending (mask, row).
+ *                           Otherwise group g lists its group_rows[g] rows that have
+ *                           a tap of the group, by (mask restricted to the group,
+ *                           bits in the set order, row), then the other rows by row.
  *   pair_in  int32 [pairs]  tap-major, ascending output row within a tap
  *   pair_out int32 [pairs]
  *   tap_off  int64 [28]     pairs of tap k are [tap_off[k], tap_off[k+1])
@@ -171,6 +177,41 @@ int smc_map_info(smc_map* map, smc_map_info_t* info);
  */
 int smc_map_export(smc_map* map, int32_t* nbr, uint32_t* mask, int32_t* perm,
                    int32_t* pair_in, int32_t* pair_out, int64_t* tap_off);
+
+/*
+ * Bit order and offset groups of the mask sort of later builds ("Sparse
+ * convolution in FP32" (DriveRT), sections "Calibrated bit order" and
+ * "Offset-group partitioning"). The order a tile meets its rows in decides
+ * how many taps its union holds: rows are sorted by their mask with the
+ * bits in the order given, and with several groups every group has its own
+ * row order under the mask restricted to the group's taps, and
+ * SMC_FWD_MASK_TILES runs one pass per group.
+ * bit_order  host int32 [27]: the taps from most to least significant, or
+ *            NULL for 26, 25, ..., 0 (the plain mask value).
+ * group_of   host int32 [27]: group 0..G-1 of each tap (G <= 4, no empty
+ *            group, the centre tap 13 in group G-1 so that the last pass
+ *            holds every row), or NULL for one group.
+ * Takes effect at the next smc_map_build (a built map keeps its order).
+ * SMC_ERR_ARG on an invalid order or grouping; the previous one then stays.
+ */
+int smc_map_set_order(smc_map* map, const int32_t* bit_order, const int32_t* group_of);
+
+/*
+ * Choose a bit order and n_groups offset groups (1..4) on a built map, as
+ * the calibration frame of the section "Calibrated bit order". The pages do
+ * not say how; here a greedy search minimises the tap-rows that 64-row mask
+ * tiles of the one-group order execute: from the off-centre taps by
+ * ascending count (ties: lower tap), each position from the most
+ * significant down takes the remaining tap with the least work (ties: the
+ * earlier one), the others following in their current order; the centre
+ * tap is always last. The off-centre taps, in that order, are then cut into
+ * n_groups runs (run g: positions floor(26 g / G) .. floor(26 (g+1) / G) - 1)
+ * and the centre joins the last. Host-side planning: it reads the masks
+ * back once and runs 351 sorts of n keys on the CPU (about a second at
+ * n = 100k); it is meant to run once per workload, not per layer.
+ * bit_order, group_of: host int32 [27] outputs, ready for smc_map_set_order.
+ */
+int smc_map_calibrate(smc_map* map, int n_groups, int32_t* bit_order, int32_t* group_of);
 
 /* Bytes of the packed weight buffer for c_in x c_out (both >= 1). */
 size_t smc_weight_packed_bytes(int c_in, int c_out);
@@ -197,8 +238,13 @@ int smc_weight_pack(const uint16_t* w, int c_in, int c_out, void* out, void* str
  *    the output. Needs a map built without SMC_BUILD_NO_PAIRS;
  *  - SMC_FWD_MASK_TILES ("Sparse convolution in FP32", "Neighbour masks and
  *    sorted rows"): tiles of mask-sorted rows run the union of their masks'
- *    taps and keep every tap's sum in registers; one kernel, nothing in
- *    memory but the output. Needs a map built without SMC_BUILD_NO_SORT.
+ *    taps and keep every tap's sum in registers; with one offset group, one
+ *    kernel and nothing in memory but the output. With G groups
+ *    (smc_map_set_order), one pass per group over that group's rows; the
+ *    first G-1 leave float32 partial sums in the handle (4 n c_out bytes,
+ *    grow-only) and the last, which holds every row, adds them and writes y
+ *    ("Offset-group partitioning"). Needs a map built without
+ *    SMC_BUILD_NO_SORT.
  * Neither uses atomics: the output is the same on every run.
  * x       device pointer, bf16 [n, c_in] row-major (rows in coordinate order).
  * wpacked device pointer from smc_weight_pack(c_in, c_out).

@@ -35,6 +35,7 @@ EXPORTED_SYMBOLS = [
     "smc_map_create", "smc_map_destroy", "smc_map_build", "smc_map_sync", "smc_map_info",
     "smc_map_export", "smc_weight_packed_bytes", "smc_weight_pack", "smc_conv_forward",
     "smc_status_string", "smc_last_error", "smc_version", "smc_timing_enable", "smc_timing_read",
+    "smc_map_set_order", "smc_map_calibrate",
 ]
 STAGES = ["map", "neighbours", "mask_sort", "compact", "gemm", "centre"]
 
@@ -52,6 +53,7 @@ class MapInfo(ctypes.Structure):
         ("batch", ctypes.c_int32), ("tile_m", ctypes.c_int32), ("grid_cells", ctypes.c_int64),
         ("pairs", ctypes.c_int64), ("pairs_padded", ctypes.c_int64), ("n_tiles", ctypes.c_int64),
         ("tap_count", ctypes.c_int64 * 27), ("status", ctypes.c_int32),
+        ("n_groups", ctypes.c_int32), ("group_rows", ctypes.c_int64 * 4),
     ]
 
 
@@ -70,6 +72,11 @@ def lib():
     if not os.path.exists(_LIB_PATH):
         raise RuntimeError(f"{_LIB_PATH} is not built; run `python __graft_entry__.py build` "
                            "(hipcc --offload-arch=gfx950) first")
+    # torch ships its own HIP runtime under the same soname (libamdhip64.so.7).
+    # Importing torch first makes the library bind to that runtime, the one
+    # that owns the tensors and streams handed over; loaded first, the library
+    # would pull in a second runtime that cannot use them.
+    import torch  # noqa: F401
     L = ctypes.CDLL(_LIB_PATH)
     vp, i32, i64, u32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint
     L.smc_map_create.argtypes = [ctypes.POINTER(vp)]
@@ -89,9 +96,12 @@ def lib():
     L.smc_version.restype = i32
     L.smc_timing_enable.argtypes = [vp, i32]
     L.smc_timing_read.argtypes = [vp, vp, vp, i32]
+    L.smc_map_set_order.argtypes = [vp, vp, vp]
+    L.smc_map_calibrate.argtypes = [vp, i32, vp, vp]
     for name in ("smc_map_create", "smc_map_destroy", "smc_map_build", "smc_map_sync",
                  "smc_map_info", "smc_map_export", "smc_weight_pack", "smc_conv_forward",
-                 "smc_timing_enable", "smc_timing_read"):
+                 "smc_timing_enable", "smc_timing_read", "smc_map_set_order",
+                 "smc_map_calibrate"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -196,6 +206,26 @@ class KernelMap:
     def sync(self):
         _check(lib().smc_map_sync(self._h))
 
+    def set_order(self, bit_order=None, group_of=None) -> "KernelMap":
+        """Bit order (27 taps, most significant first) and offset groups (group
+        of each tap) of the mask sort of later builds; None: plain / one group."""
+        arr = {}
+        for name, v in (("bit_order", bit_order), ("group_of", group_of)):
+            if v is not None:
+                v = [int(t) for t in v]
+                if len(v) != 27:
+                    raise ValueError(f"{name} must have 27 entries")
+                arr[name] = (ctypes.c_int32 * 27)(*v)
+        _check(lib().smc_map_set_order(self._h, arr.get("bit_order"), arr.get("group_of")))
+        return self
+
+    def calibrate(self, n_groups: int = 1):
+        """(bit_order, group_of) chosen on this built map (see smc_map_calibrate)."""
+        order = (ctypes.c_int32 * 27)()
+        groups = (ctypes.c_int32 * 27)()
+        _check(lib().smc_map_calibrate(self._h, int(n_groups), order, groups))
+        return list(order), list(groups)
+
     def timing(self, on: bool = True):
         """Record HIP events around each stage of later builds and forwards."""
         _check(lib().smc_timing_enable(self._h, 1 if on else 0))
@@ -214,17 +244,20 @@ class KernelMap:
                     origin=tuple(inf.origin), extent=tuple(inf.extent), batch=inf.batch,
                     tile_m=inf.tile_m, grid_cells=inf.grid_cells, pairs=inf.pairs,
                     pairs_padded=inf.pairs_padded, n_tiles=inf.n_tiles,
-                    tap_count=list(inf.tap_count), status=inf.status)
+                    tap_count=list(inf.tap_count), status=inf.status, n_groups=inf.n_groups,
+                    group_rows=list(inf.group_rows)[:inf.n_groups])
 
     def export(self, pairs: bool = True, perm: bool = True) -> dict:
-        """Copy nbr, mask, tap offsets (and the mask order, the pair lists) to numpy (host)."""
+        """Copy nbr, mask, tap offsets (and the mask-tile row orders [G, N], the
+        pair lists) to numpy (host)."""
         import numpy as np
         info = self.info()
         n, p = info["n"], info["pairs"]
         out = dict(nbr=np.empty((n, 27), np.int32), mask=np.empty(n, np.uint32),
                    tap_off=np.empty(28, np.int64))
         if perm:
-            out["perm"] = np.empty(n, np.int32)
+            out["perm"] = np.empty((max(info["n_groups"], 1), n), np.int32)
+            out["group_rows"] = np.asarray(info["group_rows"], np.int64)
         if pairs:
             out["pair_in"] = np.empty(p, np.int32)
             out["pair_out"] = np.empty(p, np.int32)

@@ -142,19 +142,31 @@ __device__ void block_lookback(uint64_t* look, int64_t pb, uint32_t epoch, uint3
 }
 
 // One read of the masks: digit histograms of every mask-sort pass and pairs
-// per tap (mask column sums).
+// per tap (mask column sums). With a calibrated order or offset groups
+// ("Sparse convolution in FP32" (DriveRT), sections "Calibrated bit order" and
+// "Offset-group partitioning") the sort keys are not the masks: each row gets
+// one key per group, its group taps moved to their bits in that group's key,
+// the group index above them and, for a row without a tap of the group, a
+// bit that sends it behind every row that has one. The keys are written out
+// here and histogrammed instead, and rows with a tap per group are counted.
 __global__ __launch_bounds__(kHThreads) void k_mask_hist(const uint32_t* __restrict__ mask,
                                                          int64_t n, int bits, int passes,
+                                                         MaskOrder ord, uint32_t* __restrict__ keys,
                                                          uint32_t* __restrict__ hist,
-                                                         int32_t* __restrict__ tap_tot) {
-    extern __shared__ uint32_t s_h[];             // passes << bits, then 27 tap counters
+                                                         int32_t* __restrict__ tap_tot,
+                                                         int32_t* __restrict__ group_rows) {
+    extern __shared__ uint32_t s_h[];             // passes << bits, 27 tap and 4 group counters
     const int bins = 1 << bits;
     uint32_t* s_tap = s_h + passes * bins;
-    for (int i = threadIdx.x; i < passes * bins + kTaps; i += kHThreads) s_h[i] = 0;
+    uint32_t* s_grp = s_tap + kTaps;
+    for (int i = threadIdx.x; i < passes * bins + kTaps + kMaxGroups; i += kHThreads) s_h[i] = 0;
     __syncthreads();
     const int lane = threadIdx.x & 63;
+    const int G = ord.n_groups, B = ord.group_bits;
+    const int gshift = G > 1 ? B + 1 : 0;
     int64_t base = (int64_t)blockIdx.x * kHTile;
     uint32_t tap_acc = 0;                          // lane k < 27 keeps tap k's wave count
+    uint32_t grp_acc = 0;                          // lane g < G keeps group g's wave count
     uint32_t mv[kHItems];
 #pragma unroll
     for (int i = 0; i < kHItems; ++i) {
@@ -166,9 +178,31 @@ __global__ __launch_bounds__(kHThreads) void k_mask_hist(const uint32_t* __restr
     for (int i = 0; i < kHItems; ++i) {
         int64_t idx = base + i * kHThreads + threadIdx.x;
         const uint32_t m = mv[i];
-        if (idx < n) {
-            for (int p = 0; p < passes; ++p)
-                atomicAdd(&s_h[p * bins + ((m >> (p * bits)) & (bins - 1))], 1u);
+        if (ord.plain) {
+            if (idx < n) {
+                for (int p = 0; p < passes; ++p)
+                    atomicAdd(&s_h[p * bins + ((m >> (p * bits)) & (bins - 1))], 1u);
+            }
+        } else {
+            uint32_t kg[kMaxGroups] = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int t = 0; t < kTaps; ++t) {
+                const uint32_t b = ((m >> t) & 1u) << ord.pos[t];
+#pragma unroll
+                for (int g = 0; g < kMaxGroups; ++g) kg[g] |= ord.grp[t] == g ? b : 0u;
+            }
+#pragma unroll
+            for (int g = 0; g < kMaxGroups; ++g) {
+                if (g >= G) break;
+                const uint32_t key = ((uint32_t)g << gshift) | (kg[g] ? kg[g] : 1u << B);
+                if (idx < n) {
+                    keys[g * n + idx] = key;
+                    for (int p = 0; p < passes; ++p)
+                        atomicAdd(&s_h[p * bins + ((key >> (p * bits)) & (bins - 1))], 1u);
+                }
+                const uint32_t c = (uint32_t)__popcll(__ballot(idx < n && kg[g] != 0u));
+                if (lane == g) grp_acc += c;
+            }
         }
 #pragma unroll
         for (int k = 0; k < kTaps; ++k) {
@@ -177,10 +211,13 @@ __global__ __launch_bounds__(kHThreads) void k_mask_hist(const uint32_t* __restr
         }
     }
     if (lane < kTaps && tap_acc) atomicAdd(&s_tap[lane], tap_acc);
+    if (lane < kMaxGroups && grp_acc) atomicAdd(&s_grp[lane], grp_acc);
     __syncthreads();
     for (int i = threadIdx.x; i < passes * bins; i += kHThreads)
         if (s_h[i]) atomicAdd(&hist[i], s_h[i]);
     if (threadIdx.x < kTaps && s_tap[threadIdx.x]) atomicAdd(&tap_tot[threadIdx.x], (int32_t)s_tap[threadIdx.x]);
+    if (threadIdx.x < kMaxGroups && s_grp[threadIdx.x])
+        atomicAdd(&group_rows[threadIdx.x], (int32_t)s_grp[threadIdx.x]);
 }
 
 // LDS of one compaction chunk.
@@ -415,11 +452,22 @@ __global__ __launch_bounds__(kCThreads) void k_lookup_compact(
 
 }  // namespace
 
-hipError_t launch_mask_hist(const uint32_t* mask, int64_t n, const SortPlan& plan, uint32_t* hist,
-                            int32_t* tap_tot, hipStream_t s) {
+int mask_sort_bits(const MaskOrder& ord) {
+    if (ord.plain) return kMaskBits;
+    if (ord.n_groups == 1) return ord.group_bits;
+    int gb = 0;
+    while ((1 << gb) < ord.n_groups) ++gb;
+    return ord.group_bits + 1 + gb;
+}
+
+hipError_t launch_mask_hist(const uint32_t* mask, int64_t n, const SortPlan& plan,
+                            const MaskOrder& ord, uint32_t* keys, uint32_t* hist, int32_t* tap_tot,
+                            int32_t* group_rows, hipStream_t s) {
+    if (!ord.plain && !keys) return hipErrorInvalidValue;
     unsigned blocks = (unsigned)((n + kHTile - 1) / kHTile);
-    size_t lds = ((size_t)plan.passes * (1u << plan.bits) + kTaps) * 4;
-    launch(k_mask_hist, blocks, kHThreads, lds, s, mask, n, plan.bits, plan.passes, hist, tap_tot);
+    size_t lds = ((size_t)plan.passes * (1u << plan.bits) + kTaps + kMaxGroups) * 4;
+    launch(k_mask_hist, blocks, kHThreads, lds, s, mask, n, plan.bits, plan.passes, ord, keys, hist,
+           tap_tot, group_rows);
     return hipGetLastError();
 }
 

@@ -45,6 +45,21 @@ struct MapState {
     int32_t tap_off[28];    // start of each tap's pair run (k * cap; tap_off[27] = 27 cap)
     int32_t tap_count[27];  // pairs per tap (written by the compaction)
     int32_t tap_tot[27];    // pairs per tap, accumulated by the mask histogram
+    int32_t group_rows[4];  // rows with a tap in each offset group (mask-tile row orders)
+};
+
+constexpr int kMaxGroups = 4;
+
+// Significance order of the mask bits and offset groups of the mask-tile row
+// orders. Tap t is bit pos[t] of group grp[t]'s key; group g of a row has key
+// = its group-g taps placed at those bits. plain: one group, pos[t] = t (the
+// key is the mask itself).
+struct MaskOrder {
+    int32_t n_groups = 1;
+    int32_t group_bits = 27;  // bits of a group key: the largest group's tap count
+    int32_t plain = 1;
+    uint8_t pos[27];
+    uint8_t grp[27];
 };
 
 // Digit plan of a radix sort: passes x bits (bits in 8..11).
@@ -62,7 +77,7 @@ struct SortWork {
 };
 
 constexpr int kMaskBits = 27;
-constexpr int kHistMaskInts = 3 * 512;        // mask sort: 3 passes x 9 bits
+constexpr int kHistMaskInts = 3 * 1024;       // mask sort: up to 3 passes x 10 bits
 constexpr int kHistKeyInts = 6 * 2048;        // key sort: up to 6 passes x 11 bits
 constexpr int kHistInts = kHistMaskInts + kHistKeyInts;
 
@@ -138,8 +153,16 @@ hipError_t radix_sort_u64(const uint64_t* keys_in, const uint32_t* vals_in, int6
                           hipStream_t s);
 
 // ---- compaction (compact_kernels.hip) ----
-hipError_t launch_mask_hist(const uint32_t* mask, int64_t n, const SortPlan& plan, uint32_t* hist,
-                            int32_t* tap_tot, hipStream_t s);
+// Digit histograms of the mask sort and pairs per tap, in one read of the
+// masks. A plain order sorts the masks themselves (keys == nullptr). Otherwise
+// every row gets one key per group, keys[g n + row] = (g << (B + 1)) | (the
+// group key, or 1 << B if the row has no tap of the group), which one sort
+// of G n items orders group by group (B = ord.group_bits); group_rows[g]
+// counts the rows with a tap of group g.
+int mask_sort_bits(const MaskOrder& ord);
+hipError_t launch_mask_hist(const uint32_t* mask, int64_t n, const SortPlan& plan,
+                            const MaskOrder& ord, uint32_t* keys, uint32_t* hist, int32_t* tap_tot,
+                            int32_t* group_rows, hipStream_t s);
 int64_t compact_chunks(int64_t n);
 size_t compact_look_bytes(int64_t n);
 // Pairs of tap k go to [k cap, k cap + tap_count[k]) in ascending output row;
@@ -169,8 +192,22 @@ hipError_t launch_gemm_centre(const uint16_t* x, int c_in, const void* wpacked, 
                               hipStream_t s);
 
 // ---- mask-tile GEMM (masktile_kernels.hip) ----
+// One pass over the rows of one offset group: taps gm of the rows listed at
+// perm (entries are item indices, row = entry - goff). rows: device count of
+// listed rows, or nullptr for all n. Rows with a tap in prev (earlier groups)
+// add their float32 partial sums; the last pass writes y, the others write
+// the float32 partial sums.
+struct GroupPass {
+    uint32_t gm = 0x7FFFFFFu;
+    uint32_t prev = 0;
+    bool last = true;
+    const uint32_t* perm = nullptr;
+    int64_t goff = 0;
+    const int32_t* rows = nullptr;
+    float* partial = nullptr;
+};
 hipError_t launch_conv_masktile(const uint16_t* x, int c_in, const void* wpacked, int c_out,
-                                const int32_t* nbr, const uint32_t* mask, const uint32_t* perm,
+                                const int32_t* nbr, const uint32_t* mask, const GroupPass& gp,
                                 int64_t n, const uint16_t* zrow, void* y, bool out_f32, bool relu,
                                 hipStream_t s);
 

@@ -118,7 +118,10 @@ struct smc_map {
     SortWork ws;
     bool state_copied = false;        // host_state already holds the last build's record
     DevBuf nbr, mask, mkey0, mkey1, mval0, mval1;
-    const uint32_t* perm = nullptr;   // points into mval0 or mval1
+    const uint32_t* perm = nullptr;   // points into mval0 or mval1: [groups][n] item indices
+    MaskOrder order;                  // bit order and offset groups of the next builds' mask sort
+    MaskOrder sorted_order;           // the order the last build's mask sort used
+    DevBuf okeys;                     // per-group sort keys ([groups][n])
     DevBuf pair_in, pair_out, pair_slot, rowbase;
     int64_t cap = 0;                  // pairs per tap the pair arrays hold (n rounded up to a tile)
     DevBuf part;                      // float32 partial-product slab of the pair-list forward
@@ -457,16 +460,19 @@ int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     const bool want_sort = !(flags & SMC_BUILD_NO_SORT);
     const int64_t nn = n > 0 ? n : 1;
     const int64_t cap = (nn + kCapAlign - 1) / kCapAlign * kCapAlign;
-    size_t look_bytes = sort_look_bytes(nn);
+    const MaskOrder ord = want_sort ? m->order : MaskOrder();
+    const int64_t items = nn * ord.n_groups;          // mask-sort items: one per (group, row)
+    size_t look_bytes = sort_look_bytes(items > nn ? items : nn);
     const size_t look_c = compact_look_bytes(nn);
     if (look_c > look_bytes) look_bytes = look_c;
     const size_t look_before = m->look.bytes;
     // (the neighbour table is read in whole 16-byte words: keep the last one readable)
     if ((rc = m->nbr.ensure((size_t)nn * kTaps * 4 + 16)) || (rc = m->mask.ensure((size_t)nn * 4)) ||
-        (rc = m->mkey0.ensure((size_t)nn * 4)) || (rc = m->mkey1.ensure((size_t)nn * 4)) ||
-        (rc = m->mval0.ensure((size_t)nn * 4)) || (rc = m->mval1.ensure((size_t)nn * 4)) ||
+        (rc = m->mkey0.ensure((size_t)items * 4)) || (rc = m->mkey1.ensure((size_t)items * 4)) ||
+        (rc = m->mval0.ensure((size_t)items * 4)) || (rc = m->mval1.ensure((size_t)items * 4)) ||
         (rc = m->look.ensure(look_bytes)))
         return rc;
+    if (!ord.plain && (rc = m->okeys.ensure((size_t)items * 4))) return rc;
     if (want_pairs &&
         ((rc = m->pair_in.ensure((size_t)kTaps * cap * 4)) ||
          (rc = m->pair_out.ensure((size_t)kTaps * cap * 4)) ||
@@ -542,14 +548,21 @@ int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
         if (want_sort || !want_pairs) {
             // rows ordered by (mask, row): histograms (+ per-tap totals), then passes
             StageTimer t_ms(m, SMC_STAGE_MASK_SORT, s);
-            SortPlan mp = sort_plan(kMaskBits);
+            // (with a calibrated order or offset groups: per-group keys, one sort of them all)
+            SortPlan mp = sort_plan(mask_sort_bits(ord));
             if (!want_sort) mp.passes = 0;
-            SMC_HIP(launch_mask_hist(mask, n, mp, hist_mask, st->tap_tot, s));
+            if (mp.passes * (1 << mp.bits) > kHistMaskInts)
+                return fail(SMC_ERR_UNSUPPORTED, "mask sort needs %d histogram bins",
+                            mp.passes * (1 << mp.bits));
+            uint32_t* okeys = ord.plain ? nullptr : m->okeys.as<uint32_t>();
+            SMC_HIP(launch_mask_hist(mask, n, mp, ord, okeys, hist_mask, st->tap_tot,
+                                     st->group_rows, s));
             if (want_sort) {
-                const uint32_t* sorted_masks;
-                SMC_HIP(radix_sort_u32(mask, nullptr, n, mp, hist_mask, m->mkey0.as<uint32_t>(),
+                const uint32_t* sorted_keys;
+                SMC_HIP(radix_sort_u32(ord.plain ? mask : okeys, nullptr, n * ord.n_groups, mp,
+                                       hist_mask, m->mkey0.as<uint32_t>(),
                                        m->mkey1.as<uint32_t>(), m->mval0.as<uint32_t>(),
-                                       m->mval1.as<uint32_t>(), m->ws, status, &sorted_masks,
+                                       m->mval1.as<uint32_t>(), m->ws, status, &sorted_keys,
                                        &m->perm, s));
             }
             t_ms.finish();
@@ -564,6 +577,7 @@ int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     }
     m->has_pairs = want_pairs;
     m->has_sort = want_sort;
+    m->sorted_order = ord;
     t_map.finish();
     const bool async = (flags & SMC_BUILD_ASYNC) != 0;
     if (!async)
@@ -615,6 +629,12 @@ int smc_map_info(smc_map* m, smc_map_info_t* info) {
         }
     }
     info->status = rc ? rc : m->build_status;
+    info->n_groups = m->has_sort ? m->sorted_order.n_groups : 0;
+    if (m->has_sort) {
+        for (int g = 0; g < info->n_groups; ++g)
+            info->group_rows[g] = m->sorted_order.plain || g == info->n_groups - 1 ? m->n
+                                                                                   : hs.group_rows[g];
+    }
     return SMC_OK;
 }
 
@@ -634,7 +654,13 @@ int smc_map_export(smc_map* m, int32_t* nbr, uint32_t* mask, int32_t* perm, int3
     if (n > 0) {
         if (nbr) SMC_HIP(hipMemcpy(nbr, m->nbr.p, (size_t)n * kTaps * 4, hipMemcpyDeviceToHost));
         if (mask) SMC_HIP(hipMemcpy(mask, m->mask.p, (size_t)n * 4, hipMemcpyDeviceToHost));
-        if (perm) SMC_HIP(hipMemcpy(perm, m->perm, (size_t)n * 4, hipMemcpyDeviceToHost));
+        if (perm) {
+            // item indices g n + row -> rows, group by group
+            const int G = m->sorted_order.n_groups;
+            SMC_HIP(hipMemcpy(perm, m->perm, (size_t)G * n * 4, hipMemcpyDeviceToHost));
+            for (int g = 1; g < G; ++g)
+                for (int64_t i = 0; i < n; ++i) perm[g * n + i] -= (int32_t)(g * n);
+        }
     }
     if (tap_off) {
         tap_off[0] = 0;
@@ -699,11 +725,32 @@ int smc_conv_forward(smc_map* m, const uint16_t* x, int c_in, const void* wpacke
     if (dev != m->device) return fail(SMC_ERR_STATE, "map lives on device %d", m->device);
     hipStream_t s = (hipStream_t)stream;
     if (mask_tiles) {
+        // one pass per offset group; the earlier ones leave float32 partial sums
+        const MaskOrder& o = m->sorted_order;
+        if (o.n_groups > 1) {
+            int rc = m->part.ensure((size_t)m->n * c_out * 4);
+            if (rc) return rc;
+        }
+        const MapState* dst = m->state.as<MapState>() + m->slot;
         StageTimer t_mt(m, SMC_STAGE_GEMM, s);
-        SMC_HIP(launch_conv_masktile(x, c_in, wpacked, c_out, m->nbr.as<int32_t>(),
-                                     m->mask.as<uint32_t>(), m->perm, m->n,
-                                     m->zrow.as<uint16_t>(), y, (flags & SMC_FWD_OUT_F32) != 0,
-                                     (flags & SMC_FWD_RELU) != 0, s));
+        uint32_t prev = 0;
+        for (int g = 0; g < o.n_groups; ++g) {
+            GroupPass gp;
+            gp.gm = 0;
+            for (int t = 0; t < kTaps; ++t)
+                if (o.grp[t] == g || o.plain) gp.gm |= 1u << t;
+            gp.prev = prev;
+            gp.last = g == o.n_groups - 1;
+            gp.perm = m->perm + (int64_t)g * m->n;
+            gp.goff = (int64_t)g * m->n;
+            gp.rows = gp.last ? nullptr : dst->group_rows + g;
+            gp.partial = o.n_groups > 1 ? m->part.as<float>() : nullptr;
+            SMC_HIP(launch_conv_masktile(x, c_in, wpacked, c_out, m->nbr.as<int32_t>(),
+                                         m->mask.as<uint32_t>(), gp, m->n,
+                                         m->zrow.as<uint16_t>(), y, (flags & SMC_FWD_OUT_F32) != 0,
+                                         (flags & SMC_FWD_RELU) != 0, s));
+            prev |= gp.gm;
+        }
         t_mt.finish();
         return SMC_OK;
     }
@@ -730,6 +777,146 @@ int smc_conv_forward(smc_map* m, const uint16_t* x, int c_in, const void* wpacke
                                (flags & SMC_FWD_OUT_F32) != 0, (flags & SMC_FWD_RELU) != 0,
                                m->n_cu, s));
     t_f.finish();
+    return SMC_OK;
+}
+
+int smc_map_set_order(smc_map* m, const int32_t* bit_order, const int32_t* group_of) {
+    if (!m) return fail(SMC_ERR_ARG, "map is NULL");
+    int order[kTaps], grp[kTaps];
+    for (int j = 0; j < kTaps; ++j) order[j] = bit_order ? bit_order[j] : kTaps - 1 - j;
+    for (int t = 0; t < kTaps; ++t) grp[t] = group_of ? group_of[t] : 0;
+    bool seen[kTaps] = {};
+    for (int j = 0; j < kTaps; ++j) {
+        if (order[j] < 0 || order[j] >= kTaps || seen[order[j]])
+            return fail(SMC_ERR_ARG, "bit_order must list each of the 27 taps once");
+        seen[order[j]] = true;
+    }
+    int n_groups = 0;
+    for (int t = 0; t < kTaps; ++t) {
+        if (grp[t] < 0 || grp[t] >= kMaxGroups)
+            return fail(SMC_ERR_ARG, "group_of[%d] = %d outside [0, %d)", t, grp[t], kMaxGroups);
+        if (grp[t] + 1 > n_groups) n_groups = grp[t] + 1;
+    }
+    int size[kMaxGroups] = {};
+    for (int t = 0; t < kTaps; ++t) ++size[grp[t]];
+    for (int g = 0; g < n_groups; ++g)
+        if (size[g] == 0) return fail(SMC_ERR_ARG, "group %d has no tap", g);
+    if (grp[kCentre] != n_groups - 1)
+        return fail(SMC_ERR_ARG, "the centre tap (13) must be in the last group");
+    MaskOrder o;
+    o.n_groups = n_groups;
+    o.group_bits = 0;
+    int left[kMaxGroups];
+    for (int g = 0; g < n_groups; ++g) {
+        left[g] = size[g];
+        if (size[g] > o.group_bits) o.group_bits = size[g];
+    }
+    // the first tap of a group in bit order takes its group key's highest bit
+    for (int j = 0; j < kTaps; ++j) {
+        const int t = order[j];
+        o.grp[t] = (uint8_t)grp[t];
+        o.pos[t] = (uint8_t)(--left[grp[t]]);
+    }
+    bool identity = n_groups == 1;
+    for (int t = 0; t < kTaps; ++t) identity = identity && o.pos[t] == t;
+    o.plain = identity ? 1 : 0;
+    if (o.plain) o.group_bits = kMaskBits;
+    m->order = o;
+    return SMC_OK;
+}
+
+namespace {
+
+// Executed tap-rows of the mask tiles when the rows are sorted by the key
+// that the bit order `order` gives (one group, kMtRows rows per tile): a
+// stable LSD radix sort of the keys, then per tile its rows times the
+// popcount of the OR of their masks.
+int64_t calib_work(const std::vector<uint32_t>& mask, const int* order, std::vector<uint32_t>& key,
+                   std::vector<uint32_t>& idx, std::vector<uint32_t>& tmp) {
+    const int64_t n = (int64_t)mask.size();
+    uint32_t tab[4][256];
+    for (int b = 0; b < 4; ++b)
+        for (int v = 0; v < 256; ++v) {
+            uint32_t k = 0;
+            for (int j = 0; j < kTaps; ++j) {
+                const int t = order[j];
+                if (t / 8 == b && ((v >> (t % 8)) & 1)) k |= 1u << (kTaps - 1 - j);
+            }
+            tab[b][v] = k;
+        }
+    for (int64_t i = 0; i < n; ++i) {
+        const uint32_t m = mask[i];
+        key[i] = tab[0][m & 255] | tab[1][(m >> 8) & 255] | tab[2][(m >> 16) & 255] |
+                 tab[3][(m >> 24) & 255];
+        idx[i] = (uint32_t)i;
+    }
+    for (int pass = 0; pass < 3; ++pass) {
+        const int sh = 9 * pass;
+        int64_t cnt[513] = {};
+        for (int64_t i = 0; i < n; ++i) ++cnt[((key[idx[i]] >> sh) & 511) + 1];
+        for (int d = 0; d < 512; ++d) cnt[d + 1] += cnt[d];
+        for (int64_t i = 0; i < n; ++i) tmp[cnt[(key[idx[i]] >> sh) & 511]++] = idx[i];
+        idx.swap(tmp);
+    }
+    int64_t work = 0;
+    for (int64_t s0 = 0; s0 < n; s0 += kTileM) {
+        const int64_t e = s0 + kTileM < n ? s0 + kTileM : n;
+        uint32_t u = 0;
+        for (int64_t i = s0; i < e; ++i) u |= mask[idx[i]];
+        work += (e - s0) * __builtin_popcount(u);
+    }
+    return work;
+}
+
+}  // namespace
+
+int smc_map_calibrate(smc_map* m, int n_groups, int32_t* bit_order, int32_t* group_of) {
+    if (!m || !bit_order || !group_of) return fail(SMC_ERR_ARG, "NULL argument");
+    if (!m->built) return fail(SMC_ERR_STATE, "map was never built");
+    if (n_groups < 1 || n_groups > kMaxGroups)
+        return fail(SMC_ERR_ARG, "n_groups = %d outside [1, %d]", n_groups, kMaxGroups);
+    SMC_HIP(hipSetDevice(m->device));
+    int rc = wait_build(m);
+    if (rc) return rc;
+    if (m->build_status != SMC_OK) return fail(SMC_ERR_STATE, "map build failed");
+    const int64_t n = m->n;
+    std::vector<uint32_t> mask((size_t)n), key((size_t)n), idx((size_t)n), tmp((size_t)n);
+    if (n > 0) SMC_HIP(hipMemcpy(mask.data(), m->mask.p, (size_t)n * 4, hipMemcpyDeviceToHost));
+    int64_t cnt[kTaps] = {};
+    for (int64_t i = 0; i < n; ++i)
+        for (int t = 0; t < kTaps; ++t) cnt[t] += (mask[i] >> t) & 1u;
+    // start: off-centre taps by ascending count (ties: lower tap); centre always last
+    std::vector<int> rem;
+    for (int t = 0; t < kTaps; ++t)
+        if (t != kCentre) rem.push_back(t);
+    std::stable_sort(rem.begin(), rem.end(), [&](int a, int b) { return cnt[a] < cnt[b]; });
+    std::vector<int> chosen;
+    int cand[kTaps];
+    while (!rem.empty()) {
+        int best = -1;
+        int64_t best_w = 0;
+        for (size_t c = 0; c < rem.size(); ++c) {
+            int q = 0;
+            for (int t : chosen) cand[q++] = t;
+            cand[q++] = rem[c];
+            for (size_t r = 0; r < rem.size(); ++r)
+                if (r != c) cand[q++] = rem[r];
+            cand[q++] = kCentre;
+            const int64_t w = n > 0 ? calib_work(mask, cand, key, idx, tmp) : 0;
+            if (best < 0 || w < best_w) {
+                best = (int)c;
+                best_w = w;
+            }
+        }
+        chosen.push_back(rem[best]);
+        rem.erase(rem.begin() + best);
+    }
+    for (int j = 0; j < kTaps - 1; ++j) bit_order[j] = chosen[j];
+    bit_order[kTaps - 1] = kCentre;
+    for (int g = 0; g < n_groups; ++g)
+        for (int p = (26 * g) / n_groups; p < (26 * (g + 1)) / n_groups; ++p)
+            group_of[chosen[p]] = g;
+    group_of[kCentre] = n_groups - 1;
     return SMC_OK;
 }
 

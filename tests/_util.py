@@ -21,9 +21,10 @@ def oracle_map(name):
 
 def oracle_map_of(coords):
     nbr, mask = so.build_kernel_map(coords)
-    perm = so.mask_sort(mask)
+    perm = so.mask_sort(mask)[None, :]          # one group, plain order: [1, N]
     pin, pout, toff = so.compact_pairs(nbr, mask)
-    return dict(nbr=nbr, mask=mask, perm=perm, pair_in=pin, pair_out=pout, tap_off=toff)
+    return dict(nbr=nbr, mask=mask, perm=perm, pair_in=pin, pair_out=pout, tap_off=toff,
+                group_rows=np.asarray([len(mask)], np.int64))
 
 
 def to_dev_bf16(bits):
@@ -44,8 +45,8 @@ def bf16_bits_of(t):
 def assert_map_equal(got, want, label=""):
     """Every part of the map present in got (nbr, mask, perm, pair lists, tap_off)
     equals want, bit for bit."""
-    for key in ("nbr", "mask", "perm", "pair_in", "pair_out", "tap_off"):
-        if key not in got:
+    for key in ("nbr", "mask", "perm", "group_rows", "pair_in", "pair_out", "tap_off"):
+        if key not in got or key not in want:
             continue
         g, w = np.asarray(got[key]), np.asarray(want[key])
         assert g.shape == w.shape, f"{label} {key}: shape {g.shape} != {w.shape}"
