@@ -114,7 +114,60 @@ def stage_model(stage, algo, route, n, p, c_in, c_out):
     return 0, 0
 
 
-def run_workload(name, steps, warmup, sync_build=False, algo="pairs", copy_probe_mb=0):
+ORDERS = {"plain": 0, "calibrated": 1, "grouped": 3}   # mask-tile row order -> offset groups
+CALIBRATION_SEED_OFFSET = 1000
+
+
+def calibrate(w, n_groups):
+    """Bit order and groups chosen on a held-out voxel set: the same generator
+    and sizes with another seed (the calibration frame), never the timed set."""
+    import dataclasses
+
+    import torch
+
+    import submanifold_sparse_convolution_amd as smc
+    import synth
+
+    wc = dataclasses.replace(w, seed=w.seed + CALIBRATION_SEED_OFFSET)
+    cal = smc.KernelMap().build(torch.from_numpy(synth.make_coords(wc)).cuda(),
+                                spatial_shape=wc.grid, batch_size=1, pairs=False)
+    t0 = time.perf_counter()
+    bo, go = cal.calibrate(n_groups)
+    secs = time.perf_counter() - t0
+    cal.close()
+    return bo, go, secs
+
+
+def tile_work_ratio(mask, perm, group_rows, group_masks):
+    """Executed tap-rows of the mask tiles / useful tap-rows (pairs), from an
+    exported map: per group, 64-row tiles of its order, each costing its rows
+    times the taps of the group present in any of them."""
+    import numpy as np
+
+    def popc(a):
+        a = a.astype(np.uint32)
+        c = np.zeros(a.shape, np.int64)
+        for b in range(27):
+            c += ((a >> np.uint32(b)) & np.uint32(1)).astype(np.int64)
+        return c
+    mask = mask.astype(np.uint32)
+    useful = int(popc(mask).sum())
+    executed = 0
+    for g, gm in enumerate(group_masks):
+        sub = mask[perm[g, :group_rows[g]]] & np.uint32(gm)
+        nt = (len(sub) + 63) // 64
+        if nt == 0:
+            continue
+        pad = np.zeros(nt * 64 - len(sub), np.uint32)
+        u = np.bitwise_or.reduce(np.concatenate([sub, pad]).reshape(nt, 64), axis=1)
+        r = np.full(nt, 64)
+        r[-1] = len(sub) - (nt - 1) * 64
+        executed += int((popc(u) * r).sum())
+    return executed / useful if useful else 1.0
+
+
+def run_workload(name, steps, warmup, sync_build=False, algo="pairs", copy_probe_mb=0,
+                 order="plain"):
     import torch
 
     import submanifold_sparse_convolution_amd as smc
@@ -127,6 +180,12 @@ def run_workload(name, steps, warmup, sync_build=False, algo="pairs", copy_probe
     x_d = dev_bf16(synth.features(w.n, c, w.seed))
     w_ds = [dev_bf16(synth.weights(c, c, w.seed, layer)) for layer in range(w.layers)]
     m = smc.KernelMap()
+    cal = None
+    if algo == "mask_tiles" and order != "plain":
+        bo, go, secs = calibrate(w, ORDERS[order])
+        m.set_order(bo, go)
+        cal = dict(bit_order=bo, group_of=go, seconds=round(secs, 3),
+                   seed=w.seed + CALIBRATION_SEED_OFFSET)
     if copy_probe_mb:
         # a plain device copy of known size: the reference for the PMC byte counters
         a = torch.empty(copy_probe_mb << 20, dtype=torch.uint8, device="cuda")
@@ -181,6 +240,12 @@ def run_workload(name, steps, warmup, sync_build=False, algo="pairs", copy_probe
     stages = m.timing_read(reset=True)
     m.timing(False)
     info = m.info()
+    work_ratio = None
+    if algo == "mask_tiles":
+        ex = m.export(pairs=False)
+        go = cal["group_of"] if cal else [0] * 27
+        gms = [sum(1 << t for t in range(27) if go[t] == g) for g in range(info["n_groups"])]
+        work_ratio = tile_work_ratio(ex["mask"], ex["perm"], ex["group_rows"], gms)
     m.close()
 
     pairs = info["pairs"]
@@ -193,13 +258,17 @@ def run_workload(name, steps, warmup, sync_build=False, algo="pairs", copy_probe
         if stage_us.get(st, 0.0) <= 0.0:
             continue
         by, fl = stage_model(st, algo, info["route"], w.n, pairs, c, c)
+        if st == "gemm" and algo == "mask_tiles" and info["n_groups"] > 1:
+            # float32 partial sums: written by each early pass and read once after
+            by += 8 * c * sum(info["group_rows"][:-1])
         us = stage_us[st]
         model[st] = dict(us=us, bytes=by, flops=fl, gbs=by / (us * 1e-6) / 1e9,
                          tflops=fl / (us * 1e-6) / 1e12 if fl else 0.0)
     return dict(workload=w, coords=coords, info=info, pairs=pairs, ms_per_step=wall_ms,
                 gpu_ms_per_step=gpu_ms, per_layer_us=per_layer_us, pack_us=pack_us,
                 tflops_effective=flops_layer * w.layers / (wall_ms * 1e-3) / 1e12,
-                stage_us=stage_us, model=model, algo=algo)
+                stage_us=stage_us, model=model, algo=algo, order=order, calibration=cal,
+                tile_work_ratio=work_ratio)
 
 
 def source_digest(kernel):
@@ -360,6 +429,9 @@ def main():
                     choices=["tiny", "lidar", "deep", "wide", "stage"])
     ap.add_argument("--algo", default="pairs", choices=["pairs", "mask_tiles"],
                     help="forward algorithm of the headline line (the other is reported too)")
+    ap.add_argument("--order", default="plain", choices=list(ORDERS),
+                    help="mask-tile row order: plain mask value, calibrated bit order, or "
+                         "calibrated order with 3 offset groups (calibrated on another seed)")
     ap.add_argument("--sync-build", action="store_true",
                     help="wait for the map's device-side checks inside every step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -388,7 +460,7 @@ def main():
     torch.cuda.set_device(0)
 
     r = run_workload(args.workload, args.steps, args.warmup, args.sync_build, args.algo,
-                     args.copy_probe_mb)
+                     args.copy_probe_mb, args.order)
     w, info = r["workload"], r["info"]
     c = w.channels
     line = {
@@ -411,6 +483,7 @@ def main():
             "route": info["route"], "c_in": c, "c_out": c, "layers": w.layers,
             "map_built_every_step": True, "build_mode": "sync" if args.sync_build else "async",
             "algo": args.algo,
+            **({"order": args.order} if args.algo == "mask_tiles" else {}),
         },
         "tflops_effective": round(r["tflops_effective"], 3),
         "frac_bf16_peak": round(r["tflops_effective"] / PEAK_BF16_TFLOPS, 5),
@@ -422,24 +495,36 @@ def main():
         "weight_pack_us": round(r["pack_us"], 2),
         "roofline": roofline(r),
     }
+    if r["tile_work_ratio"] is not None:
+        line["tile_work_ratio"] = round(r["tile_work_ratio"], 4)
     if not args.no_other_algo:
-        other = "mask_tiles" if args.algo == "pairs" else "pairs"
-        r2 = run_workload(args.workload, args.steps, args.warmup, args.sync_build, other)
-        line["other_algo"] = {
-            "algo": other, "us_per_layer": round(r2["per_layer_us"], 2),
-            "tflops_effective": round(r2["tflops_effective"], 3),
-            "stage_us": {k: round(v, 2) for k, v in r2["stage_us"].items()},
-        }
+        # the other forward algorithm, and the mask-tile row orders
+        variants = [("pairs", "plain")] if args.algo == "mask_tiles" else []
+        variants += [("mask_tiles", o) for o in ORDERS
+                     if not (args.algo == "mask_tiles" and o == args.order)]
+        line["other_algo"] = []
+        for algo2, order2 in variants:
+            r2 = run_workload(args.workload, args.steps, args.warmup, args.sync_build, algo2,
+                              order=order2)
+            e = {"algo": algo2, "us_per_layer": round(r2["per_layer_us"], 2),
+                 "tflops_effective": round(r2["tflops_effective"], 3),
+                 "stage_us": {k: round(v, 2) for k, v in r2["stage_us"].items()}}
+            if algo2 == "mask_tiles":
+                e["order"] = order2
+                e["tile_work_ratio"] = round(r2["tile_work_ratio"], 4)
+            line["other_algo"].append(e)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.workload)
     if args.report:
         rep = {}
         for name in ("tiny", "lidar", "deep", "wide", "stage"):
-            for algo in ("pairs", "mask_tiles"):
-                rr = run_workload(name, max(20, args.steps // 2), args.warmup, algo=algo)
-                key = f"{name}/{algo}"
+            for algo, order in [("pairs", "plain")] + [("mask_tiles", o) for o in ORDERS]:
+                rr = run_workload(name, max(20, args.steps // 2), args.warmup, algo=algo,
+                                  order=order)
+                key = f"{name}/{algo}" + ("" if order == "plain" else f"/{order}")
                 rep[key] = {k: rr[k] for k in ("pairs", "ms_per_step", "per_layer_us", "pack_us",
-                                               "tflops_effective", "stage_us", "model")}
+                                               "tflops_effective", "stage_us", "model",
+                                               "tile_work_ratio", "calibration")}
                 rep[key]["route"] = rr["info"]["route"]
                 rep[key]["n"] = rr["workload"].n
                 rep[key]["roofline"] = roofline(rr)
