@@ -19,12 +19,17 @@ active voxel p of the set S (the output set is S itself),
     Y[p, co] = sum over the 27 offsets d with p + d in S of
                sum over ci of X[p + d, ci] * W[k(d), ci, co]
 
+and the same with the 125 offsets of a 5 x 5 x 5 kernel ([P1] "Test plan"
+lists kernel sizes 3 and 5).
+
 Readings fixed here where the pages are silent:
 
 * offset order: k(d) = 9 (dx + 1) + 3 (dy + 1) + (dz + 1), x slowest; the
-  centre is k = 13. The same k indexes the mask bit and W's first axis.
+  centre is k = 13. The same k indexes the mask bit and W's first axis. For
+  K = 5 the same rule with offsets -2..2: k = 25 (dx + 2) + 5 (dy + 2) +
+  (dz + 2), centre 62; the 125-bit mask is kept as four 32-bit words.
 * sign: output p reads input p + d (cross-correlation).
-* W layout: [27, C_in, C_out].
+* W layout: [K^3, C_in, C_out].
 * coordinates: rows (b, x, y, z) for [N, 4]; (x, y, z) with b = 0 for [N, 3];
   neighbours never cross batches.
 * duplicate coordinates are a caller error (raised here).
@@ -54,18 +59,34 @@ import numpy as np
 
 TAPS = 27
 CENTRE = 13
+KERNEL_SIZES = (3, 5)
+
+
+def taps_of(kernel_size: int) -> int:
+    """Offsets of a K x K x K kernel (27 or 125)."""
+    if kernel_size not in KERNEL_SIZES:
+        raise ValueError("kernel_size must be 3 or 5")
+    return kernel_size ** 3
+
+
+def centre_of(kernel_size: int) -> int:
+    """Tap of the zero offset: the middle of the K^3 taps (13 or 62)."""
+    return (taps_of(kernel_size) - 1) // 2
 
 
 class DuplicateCoordinate(ValueError):
     pass
 
 
-def tap_offsets() -> list:
-    """The 27 offsets d in tap order k = 9(dx+1) + 3(dy+1) + (dz+1)."""
+def tap_offsets(kernel_size: int = 3) -> list:
+    """The K^3 offsets d in tap order k = K^2 (dx+r) + K (dy+r) + (dz+r),
+    r = (K-1)/2 (for K = 3: k = 9(dx+1) + 3(dy+1) + (dz+1))."""
+    taps_of(kernel_size)
+    r = (kernel_size - 1) // 2
     offs = []
-    for dx in (-1, 0, 1):
-        for dy in (-1, 0, 1):
-            for dz in (-1, 0, 1):
+    for dx in range(-r, r + 1):
+        for dy in range(-r, r + 1):
+            for dz in range(-r, r + 1):
                 offs.append((dx, dy, dz))
     return offs
 
@@ -118,17 +139,20 @@ def _rows_bxyz(coords: np.ndarray) -> np.ndarray:
     return c.astype(np.int64)
 
 
-def build_kernel_map(coords: np.ndarray):
-    """Neighbour table and 27-bit neighbour masks from a hash map.
+def build_kernel_map(coords: np.ndarray, kernel_size: int = 3):
+    """Neighbour table and neighbour masks from a hash map.
 
     A dictionary maps each (b, x, y, z) to its row. For row i and tap k,
     nbr[i, k] is the row at c_i + d_k, or -1 when that cell is inactive, and
-    bit k of mask[i] is set exactly when the neighbour exists. This is the
-    table plus mask that the map builder of [P5] "Neighbour masks and sorted
-    rows" emits; the centre column is always the row itself.
+    bit k of row i's mask is set exactly when the neighbour exists. This is
+    the table plus mask that the map builder of [P5] "Neighbour masks and
+    sorted rows" emits; the centre column is always the row itself. K = 5
+    ([P1] "Test plan": kernel sizes 3 and 5) gives 125 taps.
 
-    Returns (nbr int32 [N, 27], mask uint32 [N]).
+    Returns (nbr int32 [N, K^3], mask): mask is uint32 [N] for K = 3 (27
+    bits) and uint32 [N, 4] for K = 5 (bit k in word k // 32, bit k % 32).
     """
+    kv = taps_of(kernel_size)
     c = _rows_bxyz(coords)
     n = c.shape[0]
     table = {}
@@ -137,9 +161,10 @@ def build_kernel_map(coords: np.ndarray):
         if key in table:
             raise DuplicateCoordinate(f"rows {table[key]} and {i} share {key}")
         table[key] = i
-    offs = tap_offsets()
-    nbr = np.full((n, TAPS), -1, dtype=np.int32)
-    mask = np.zeros(n, dtype=np.uint32)
+    offs = tap_offsets(kernel_size)
+    nbr = np.full((n, kv), -1, dtype=np.int32)
+    words = (kv + 31) // 32
+    mask = np.zeros((n, words), dtype=np.uint32)
     for i in range(n):
         b, x, y, z = c[i].tolist()
         m = 0
@@ -148,8 +173,9 @@ def build_kernel_map(coords: np.ndarray):
             if j is not None:
                 nbr[i, k] = j
                 m |= 1 << k
-        mask[i] = m
-    return nbr, mask
+        for q in range(words):
+            mask[i, q] = (m >> (32 * q)) & 0xFFFFFFFF
+    return nbr, (mask[:, 0].copy() if kernel_size == 3 else mask)
 
 
 def mask_sort(mask: np.ndarray) -> np.ndarray:
@@ -287,6 +313,14 @@ def calibrate_order(mask: np.ndarray, n_groups: int = 1, tile: int = 64):
     return order, group_of
 
 
+def mask_bit(mask: np.ndarray, k: int) -> np.ndarray:
+    """Bit k of every row's mask (uint32 [N] or words [N, W]) as a bool array."""
+    m = np.asarray(mask, dtype=np.uint32)
+    if m.ndim == 1:
+        return ((m >> np.uint32(k)) & np.uint32(1)) == 1
+    return ((m[:, k // 32] >> np.uint32(k % 32)) & np.uint32(1)) == 1
+
+
 def compact_pairs(nbr: np.ndarray, mask: np.ndarray):
     """Per-tap pair lists holding only the neighbours that exist.
 
@@ -294,16 +328,15 @@ def compact_pairs(nbr: np.ndarray, mask: np.ndarray):
     grouped by tap so that a run of pairs shares one weight slab; the centre
     tap is listed like the others ([P1] commit d4161ef, "The centre tap is
     compacted along with the rest"). Within a tap, pairs follow ascending
-    output row.
+    output row. The tap count is nbr's width (27 or 125).
 
-    Returns (pair_in int32 [P], pair_out int32 [P], tap_off int64 [28]); the
-    pairs of tap k are [tap_off[k], tap_off[k+1]).
+    Returns (pair_in int32 [P], pair_out int32 [P], tap_off int64 [taps+1]);
+    the pairs of tap k are [tap_off[k], tap_off[k+1]).
     """
     nbr = np.asarray(nbr)
-    mask = np.asarray(mask, dtype=np.uint32)
     ins, outs, off = [], [], [0]
-    for k in range(TAPS):
-        rows = np.nonzero(((mask >> np.uint32(k)) & np.uint32(1)) == 1)[0]
+    for k in range(nbr.shape[1]):
+        rows = np.nonzero(mask_bit(mask, k))[0]
         ins.append(nbr[rows, k].astype(np.int32))
         outs.append(rows.astype(np.int32))
         off.append(off[-1] + rows.size)
@@ -323,12 +356,12 @@ def conv_accumulate(x: np.ndarray, w: np.ndarray, pair_in, pair_out, tap_off,
     For each tap k, the gathered input rows X[pair_in] times W[k] are added
     to rows pair_out of the accumulator. An output row appears at most once
     per tap, so the indexed add never collides. x: [N_in, C_in] values,
-    w: [27, C_in, C_out] values (both real-valued arrays).
+    w: [taps, C_in, C_out] values (both real-valued arrays).
     """
     x = np.asarray(x, dtype=acc_dtype)
     w = np.asarray(w, dtype=acc_dtype)
     acc = np.zeros((n_out, w.shape[2]), dtype=acc_dtype)
-    for k in range(TAPS):
+    for k in range(w.shape[0]):
         a, b = int(tap_off[k]), int(tap_off[k + 1])
         if a == b:
             continue
@@ -346,7 +379,7 @@ def conv_rows(x: np.ndarray, w: np.ndarray, nbr: np.ndarray, rows) -> np.ndarray
     w = np.asarray(w, dtype=np.float64)
     out = np.zeros((len(rows), w.shape[2]), dtype=np.float64)
     for t, i in enumerate(rows):
-        for k in range(TAPS):
+        for k in range(nbr.shape[1]):
             j = int(nbr[i, k])
             if j >= 0:
                 out[t] += x[j] @ w[k]
@@ -354,14 +387,16 @@ def conv_rows(x: np.ndarray, w: np.ndarray, nbr: np.ndarray, rows) -> np.ndarray
 
 
 def subm_conv(coords, x_bits, w_bits, relu: bool = False, acc_dtype=np.float64):
-    """One submanifold 3x3x3 layer from raw inputs.
+    """One submanifold K x K x K layer from raw inputs (K from w's first axis:
+    27 taps for K = 3, 125 for K = 5).
 
     coords int [N, 3|4]; x_bits, w_bits bf16 bit patterns. Returns a dict
-    with the map (nbr, mask, perm, pair lists), the accumulator and the
-    output as bf16 bits (ReLU after rounding when ``relu``).
+    with the map (nbr, mask, perm for K = 3, pair lists), the accumulator and
+    the output as bf16 bits (ReLU after rounding when ``relu``).
     """
-    nbr, mask = build_kernel_map(coords)
-    perm = mask_sort(mask)
+    k_size = {27: 3, 125: 5}[np.asarray(w_bits).shape[0]]
+    nbr, mask = build_kernel_map(coords, k_size)
+    perm = mask_sort(mask) if k_size == 3 else None
     pin, pout, toff = compact_pairs(nbr, mask)
     x = bf16_bits_to_f64(x_bits)
     w = bf16_bits_to_f64(w_bits)

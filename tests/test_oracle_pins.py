@@ -22,19 +22,20 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_examples.json")
 # independent references
 # --------------------------------------------------------------------------
 
-def brute_force_triples(coords):
+def brute_force_triples(coords, K=3):
     """All (tap, in_row, out_row) adjacencies by O(N^2) enumeration.
 
-    The tap of an offset is found by position in a 3x3x3 array indexed
-    [dx+1, dy+1, dz+1] and flattened in C order, not by a formula.
+    The tap of an offset is found by position in a K x K x K array indexed
+    [dx+r, dy+r, dz+r] and flattened in C order, not by a formula.
     """
+    r = (K - 1) // 2
     c = so._rows_bxyz(coords)
-    tap_of = np.arange(27).reshape(3, 3, 3)
+    tap_of = np.arange(K ** 3).reshape(K, K, K)
     diff = c[None, :, 1:] - c[:, None, 1:]            # diff[i, j] = c_j - c_i
     same_b = c[None, :, 0] == c[:, None, 0]
-    adj = same_b & (np.abs(diff) <= 1).all(axis=2)
+    adj = same_b & (np.abs(diff) <= r).all(axis=2)
     out_rows, in_rows = np.nonzero(adj)
-    d = diff[out_rows, in_rows] + 1
+    d = diff[out_rows, in_rows] + r
     taps = tap_of[d[:, 0], d[:, 1], d[:, 2]]
     return set(zip(taps.tolist(), in_rows.tolist(), out_rows.tolist()))
 
@@ -46,24 +47,28 @@ def dense_grid(coords, vals, shape):
 
 
 def masked_dense_conv_numpy(coords, x, w, shape):
-    """Dense 3x3x3 correlation on a zero-padded grid via shifted slices."""
+    """Dense K x K x K correlation on a zero-padded grid via shifted slices
+    (K from w's first axis)."""
     X, Y, Z = shape
-    g = np.pad(dense_grid(coords, x, shape), ((1, 1), (1, 1), (1, 1), (0, 0)))
-    w5 = w.reshape(3, 3, 3, w.shape[1], w.shape[2])   # [dx+1, dy+1, dz+1, ci, co]
+    K = round(w.shape[0] ** (1 / 3))
+    r = (K - 1) // 2
+    g = np.pad(dense_grid(coords, x, shape), ((r, r), (r, r), (r, r), (0, 0)))
+    w5 = w.reshape(K, K, K, w.shape[1], w.shape[2])   # [dx+r, dy+r, dz+r, ci, co]
     out = np.zeros((X, Y, Z, w.shape[2]))
-    for a in range(3):
-        for b in range(3):
-            for c in range(3):
+    for a in range(K):
+        for b in range(K):
+            for c in range(K):
                 out += g[a:a + X, b:b + Y, c:c + Z] @ w5[a, b, c]
     return out[coords[:, 1], coords[:, 2], coords[:, 3]]
 
 
 def masked_dense_conv_torch(coords, x, w, shape):
     """torch.nn.functional.conv3d (a cross-correlation) in float64."""
+    K = round(w.shape[0] ** (1 / 3))
     g = torch.from_numpy(dense_grid(coords, x, shape)).permute(3, 0, 1, 2)[None]
-    w5 = torch.from_numpy(w.reshape(3, 3, 3, w.shape[1], w.shape[2]))
+    w5 = torch.from_numpy(w.reshape(K, K, K, w.shape[1], w.shape[2]))
     wt = w5.permute(4, 3, 0, 1, 2).contiguous()         # [co, ci, kx, ky, kz]
-    out = torch.nn.functional.conv3d(g, wt, padding=1)[0].permute(1, 2, 3, 0)
+    out = torch.nn.functional.conv3d(g, wt, padding=(K - 1) // 2)[0].permute(1, 2, 3, 0)
     return out.numpy()[coords[:, 1], coords[:, 2], coords[:, 3]]
 
 
@@ -71,27 +76,41 @@ def masked_dense_conv_torch(coords, x, w, shape):
 # checks (raise AssertionError)
 # --------------------------------------------------------------------------
 
-def check_map_vs_bruteforce(coords):
-    nbr, mask = so.build_kernel_map(coords)
+def mask_ints(mask):
+    """Each row's mask as one Python int (from uint32 [N] or words [N, W])."""
+    m = np.asarray(mask)
+    if m.ndim == 1:
+        return [int(v) for v in m]
+    return [sum(int(w) << (32 * q) for q, w in enumerate(row)) for row in m]
+
+
+def check_map_vs_bruteforce(coords, K=3):
+    nbr, mask = so.build_kernel_map(coords, K)
+    assert nbr.shape[1] == K ** 3
     got = set()
     for i, k in zip(*np.nonzero(nbr >= 0)):
         got.add((int(k), int(nbr[i, k]), int(i)))
-    assert got == brute_force_triples(coords), "neighbour table differs from brute force"
-    pop = np.array([bin(int(m)).count("1") for m in mask])
+    assert got == brute_force_triples(coords, K), "neighbour table differs from brute force"
+    ms = mask_ints(mask)
+    pop = np.array([bin(m).count("1") for m in ms])
     assert (pop == (nbr >= 0).sum(1)).all(), "mask popcount != neighbour count"
     for i, k in zip(*np.nonzero(nbr >= 0)):
-        assert (int(mask[i]) >> int(k)) & 1
+        assert (ms[i] >> int(k)) & 1
 
 
-def check_full_box(a, b, c):
+def check_full_box(a, b, c, K=3):
+    r = (K - 1) // 2
     coords = synth.box_coords(a, b, c, origin=(3, 5, 7), seed=a * 100 + b * 10 + c)
-    nbr, mask = so.build_kernel_map(coords)
+    nbr, mask = so.build_kernel_map(coords, K)
     _, _, toff = so.compact_pairs(nbr, mask)
     counts = np.diff(toff)
-    for k, (dx, dy, dz) in enumerate(np.ndindex(3, 3, 3)):
-        want = max(a - abs(dx - 1), 0) * max(b - abs(dy - 1), 0) * max(c - abs(dz - 1), 0)
-        assert counts[k] == want, f"box {a}x{b}x{c} tap {k}: {counts[k]} != {want}"
-    assert toff[-1] == (3 * a - 2) * (3 * b - 2) * (3 * c - 2)
+    for k, (dx, dy, dz) in enumerate(np.ndindex(K, K, K)):
+        want = (max(a - abs(dx - r), 0) * max(b - abs(dy - r), 0) * max(c - abs(dz - r), 0))
+        assert counts[k] == want, f"K={K} box {a}x{b}x{c} tap {k}: {counts[k]} != {want}"
+    per_axis = [sum(max(e - abs(d), 0) for d in range(-r, r + 1)) for e in (a, b, c)]
+    assert toff[-1] == per_axis[0] * per_axis[1] * per_axis[2]
+    if K == 3:
+        assert toff[-1] == (3 * a - 2) * (3 * b - 2) * (3 * c - 2)
 
 
 def check_perm(mask, perm):
@@ -103,19 +122,20 @@ def check_perm(mask, perm):
     assert (np.diff(perm.astype(np.int64))[same] > 0).all(), "ties not by row"
 
 
-def check_pairs(coords):
-    nbr, mask = so.build_kernel_map(coords)
-    perm = so.mask_sort(mask)
-    check_perm(mask, perm)
+def check_pairs(coords, K=3):
+    nbr, mask = so.build_kernel_map(coords, K)
+    if K == 3:
+        check_perm(mask, so.mask_sort(mask))
     pin, pout, toff = so.compact_pairs(nbr, mask)
     got = set()
-    for k in range(27):
+    for k in range(K ** 3):
         a, b = toff[k], toff[k + 1]
         for i, o in zip(pin[a:b].tolist(), pout[a:b].tolist()):
             got.add((k, i, o))
         assert (np.diff(pout[a:b].astype(np.int64)) > 0).all(), f"tap {k} not in row order"
-    assert got == brute_force_triples(coords), "pair lists differ from brute force"
-    bits = ((mask[:, None] >> np.arange(27, dtype=np.uint32)) & 1).sum(0)
+    assert got == brute_force_triples(coords, K), "pair lists differ from brute force"
+    ms = mask_ints(mask)
+    bits = np.array([sum((m >> k) & 1 for m in ms) for k in range(K ** 3)])
     assert (np.diff(toff) == bits).all(), "per-tap counts != mask column sums"
 
 
@@ -134,15 +154,15 @@ def check_conv_vs_dense(coords, xb, wb, shape, exact=False):
         assert np.max(np.abs(r["acc"] - ref_t) / scale) < 1e-12, "acc vs torch conv3d"
 
 
-def check_one_hot(coords, k):
+def check_one_hot(coords, k, K=3):
     c = 8
     n = len(coords)
     xb = synth.features(n, c, seed=11)
-    w = np.zeros((27, c, c), np.float32)
+    w = np.zeros((K ** 3, c, c), np.float32)
     w[k] = np.eye(c, dtype=np.float32)
     wb = synth.bf16_bits_from_f32(w)
     r = so.subm_conv(coords, xb, wb)
-    nbr, _ = so.build_kernel_map(coords)
+    nbr, _ = so.build_kernel_map(coords, K)
     x = so.bf16_bits_to_f64(xb)
     want = np.where((nbr[:, k] >= 0)[:, None], x[np.maximum(nbr[:, k], 0)], 0.0)
     assert np.array_equal(r["y"], want), f"one-hot tap {k} is not a shifted copy"
@@ -352,6 +372,76 @@ def test_order_argument_errors():
         so.group_row_orders(mask, None, [0] * 13 + [2] + [2] * 13)     # gap in group ids
 
 
+# --- kernel size 5 ([P1] "Test plan": kernel sizes 3 and 5) ---------------
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_k5_map_vs_bruteforce(seed):
+    check_map_vs_bruteforce(synth.tiny_coords(seed=seed, n=250, side=9), K=5)
+
+
+def test_k5_map_two_batches_and_three_columns():
+    a = synth.tiny_coords(seed=2, n=150, side=7)
+    b = synth.tiny_coords(seed=3, n=150, side=7)
+    b[:, 0] = 1
+    coords = np.concatenate([a, b])
+    check_map_vs_bruteforce(coords, K=5)
+    n3, m3 = so.build_kernel_map(a[:, 1:], 5)
+    n4, m4 = so.build_kernel_map(a, 5)
+    assert np.array_equal(n3, n4) and np.array_equal(m3, m4)
+
+
+@pytest.mark.parametrize("abc", [(1, 1, 1), (2, 3, 4), (5, 5, 5), (7, 3, 6)])
+def test_k5_full_box_closed_form(abc):
+    check_full_box(*abc, K=5)
+
+
+def test_k5_symmetry_centre_and_mask_words():
+    coords = synth.tiny_coords(seed=5, n=300, side=9)
+    nbr, mask = so.build_kernel_map(coords, 5)
+    assert mask.shape == (300, 4) and mask.dtype == np.uint32
+    assert (mask[:, 3] >> np.uint32(29) == 0).all(), "bits above 124 must be clear"
+    assert (nbr[:, 62] == np.arange(300)).all()
+    for i, k in zip(*np.nonzero(nbr >= 0)):
+        assert nbr[nbr[i, k], 124 - k] == i
+
+
+def test_k5_pairs_vs_bruteforce():
+    check_pairs(synth.tiny_coords(seed=6, n=250, side=9), K=5)
+
+
+def test_k5_conv_vs_dense():
+    coords = synth.tiny_coords(seed=7, n=220, side=8)
+    x = synth.features(220, 5, 7)
+    w = synth.bf16_bits_from_f32(np.random.default_rng(8).standard_normal((125, 5, 4))
+                                 .astype(np.float32) * np.float32(0.1))
+    check_conv_vs_dense(coords, x, w, (8, 8, 8))
+
+
+def test_k5_conv_integer_exact_vs_dense():
+    coords = synth.tiny_coords(seed=9, n=200, side=8)
+    x = synth.int_features(200, 6, 9)
+    w = synth.bf16_bits_from_f32(np.random.default_rng(10).integers(-2, 3, (125, 6, 3))
+                                 .astype(np.float32))
+    check_conv_vs_dense(coords, x, w, (8, 8, 8), exact=True)
+
+
+@pytest.mark.parametrize("k", [0, 31, 32, 62, 100, 124])
+def test_k5_one_hot_taps(k):
+    check_one_hot(synth.tiny_coords(seed=11, n=200, side=8), k, K=5)
+
+
+def test_k5_isolated_and_k3_is_a_subset():
+    coords = synth.isolated_coords(200, spacing=3, seed=1)
+    nbr, _ = so.build_kernel_map(coords, 5)
+    assert (nbr >= 0).sum() == 200                       # pitch 3 > 2: only the centre
+    coords = synth.tiny_coords(seed=12, n=300, side=9)
+    n3, _ = so.build_kernel_map(coords, 3)
+    n5, _ = so.build_kernel_map(coords, 5)
+    off5 = {o: k for k, o in enumerate(so.tap_offsets(5))}
+    for k3, o in enumerate(so.tap_offsets(3)):
+        assert np.array_equal(n3[:, k3], n5[:, off5[o]]), o
+
+
 def test_bf16_rounding_matches_torch():
     check_bf16_vs_torch(bf16_test_values())
 
@@ -532,7 +622,7 @@ def _fails(fn, *a):
 
 def test_planted_flipped_offset_sign(monkeypatch):
     orig = so.tap_offsets
-    monkeypatch.setattr(so, "tap_offsets", lambda: [(-a, -b, -c) for a, b, c in orig()])
+    monkeypatch.setattr(so, "tap_offsets", lambda k=3: [(-a, -b, -c) for a, b, c in orig(k)])
     coords = synth.tiny_coords(seed=0, n=300, side=8)
     assert _fails(check_map_vs_bruteforce, coords)
     assert _fails(check_conv_vs_dense, coords, synth.features(300, 4, 0),
@@ -542,7 +632,7 @@ def test_planted_flipped_offset_sign(monkeypatch):
 
 def test_planted_z_slowest_tap_order(monkeypatch):
     orig = so.tap_offsets
-    monkeypatch.setattr(so, "tap_offsets", lambda: [(c, b, a) for a, b, c in orig()])
+    monkeypatch.setattr(so, "tap_offsets", lambda k=3: [(c, b, a) for a, b, c in orig(k)])
     coords = synth.tiny_coords(seed=0, n=300, side=8)
     assert _fails(check_map_vs_bruteforce, coords)
     assert _fails(check_hand_examples)
@@ -661,3 +751,12 @@ def test_planted_calibration_takes_worst(monkeypatch):
     o1, c1 = so.group_row_orders(mask, order)
     o0, c0 = so.group_row_orders(mask, start)
     assert so.tile_work(mask, o1[0], c1[0], None, 16) > so.tile_work(mask, o0[0], c0[0], None, 16)
+
+
+def test_planted_k5_offsets_clipped_to_one(monkeypatch):
+    orig = so.tap_offsets
+    monkeypatch.setattr(so, "tap_offsets",
+                        lambda k=3: [tuple(max(-1, min(1, v)) for v in o) for o in orig(k)])
+    coords = synth.tiny_coords(seed=0, n=200, side=8)
+    assert _fails(check_map_vs_bruteforce, coords, 5)
+    assert _fails(check_full_box, 3, 4, 5, 5)
