@@ -99,10 +99,12 @@ typedef struct smc_map_info_s {
     int64_t pairs;          /* P: valid (input, output) pairs including the centre tap */
     int64_t pairs_padded;   /* sum over taps of tap_count rounded up to tile_m (0 without pairs) */
     int64_t n_tiles;        /* pairs_padded / tile_m: GEMM tiles of all taps (0 without pairs) */
-    int64_t tap_count[27];  /* pairs per tap */
+    int64_t tap_count[125]; /* pairs per tap (the first `taps` entries) */
     int32_t status;         /* smc_status of the build's device-side checks */
     int32_t n_groups;       /* offset groups of the mask-tile row orders (0: map not sorted) */
     int64_t group_rows[4];  /* rows with a tap of each group (the last group: every row) */
+    int32_t kernel_size;    /* K: 3 or 5 */
+    int32_t taps;           /* K^3: 27 or 125 */
 } smc_map_info_t;
 
 /* Create an empty map handle. *out receives it. No device memory is taken yet. */
@@ -137,7 +139,12 @@ int smc_map_destroy(smc_map* map);
  *               grid is [0, shape). NULL: the grid is the coordinates' bounding
  *               box, which costs one device->host read inside this call.
  * batch_size    number of batches B (b in [0, B)); <= 0 derives it (one read).
- * kernel_size   must be 3 (else SMC_ERR_UNSUPPORTED).
+ * kernel_size   3 or 5 (else SMC_ERR_UNSUPPORTED): 27 or 125 taps, tap
+ *               k = K^2 (dx+r) + K (dy+r) + (dz+r) for offsets -r..r, r = (K-1)/2
+ *               ("[Kernel] Add submanifold sparse 3D convolution", "Test plan":
+ *               kernel sizes 3 and 5). A 5x5x5 map always has pair lists
+ *               (SMC_BUILD_NO_PAIRS is refused) and never a mask order (the
+ *               mask-tile algorithm is 3x3x3 only; SMC_BUILD_NO_SORT is implied).
  * route         SMC_ROUTE_*.
  * flags         SMC_BUILD_* bits or 0. Without SMC_BUILD_ASYNC the call waits for the
  *               device-side checks and returns SMC_ERR_DUPLICATE / SMC_ERR_RANGE
@@ -162,8 +169,9 @@ int smc_map_info(smc_map* map, smc_map_info_t* info);
 /*
  * Copy the map to host memory for inspection (parity tests). Each pointer is
  * a host pointer or NULL (skipped):
- *   nbr      int32 [n, 27]  row of c_i + d_k, or -1
- *   mask     uint32 [n]     bit k set iff nbr[i, k] >= 0
+ *   nbr      int32 [n, taps]  row of c_i + d_k, or -1
+ *   mask     uint32 [n] (K = 3) or [n, 4] (K = 5: bit k in word k / 32)
+ *                           bit k set iff nbr[i, k] >= 0
  *   perm     int32 [G, n]   G = info.n_groups row orders (needs a sorted map). With
  *                           the plain order (G = 1): rows by ascending (mask, row).
  *                           Otherwise group g lists its group_rows[g] rows that have
@@ -171,7 +179,7 @@ int smc_map_info(smc_map* map, smc_map_info_t* info);
  *                           bits in the set order, row), then the other rows by row.
  *   pair_in  int32 [pairs]  tap-major, ascending output row within a tap
  *   pair_out int32 [pairs]
- *   tap_off  int64 [28]     pairs of tap k are [tap_off[k], tap_off[k+1])
+ *   tap_off  int64 [taps+1] pairs of tap k are [tap_off[k], tap_off[k+1])
  * Waits for the device. SMC_ERR_STATE if perm is asked of a map built with
  * SMC_BUILD_NO_SORT, or pair_in / pair_out of one built with SMC_BUILD_NO_PAIRS.
  */
@@ -213,18 +221,22 @@ int smc_map_set_order(smc_map* map, const int32_t* bit_order, const int32_t* gro
  */
 int smc_map_calibrate(smc_map* map, int n_groups, int32_t* bit_order, int32_t* group_of);
 
-/* Bytes of the packed weight buffer for c_in x c_out (both >= 1). */
-size_t smc_weight_packed_bytes(int c_in, int c_out);
+/* Bytes of the packed weight buffer for a K x K x K kernel (K = 3 or 5) and
+ * c_in x c_out (both >= 1); 0 for an invalid request. */
+size_t smc_weight_packed_bytes(int kernel_size, int c_in, int c_out);
 
 /*
  * Pack weights for the GEMM ("[Kernel] Add submanifold sparse 3D
  * convolution", section "Design, and the measurements behind it": weights
- * packed so that a wave reads fully used cache lines). w: device pointer, bf16 [27, c_in, c_out] row-major
- * (W[k][ci][co]). out: device pointer of smc_weight_packed_bytes() bytes,
- * 16-byte aligned. Channels are zero-padded internally, so any c >= 1 works.
- * Pack once per weight tensor and reuse the result for every forward.
+ * packed so that a wave reads fully used cache lines). w: device pointer, bf16
+ * [K^3, c_in, c_out] row-major (W[k][ci][co]). out: device pointer of
+ * smc_weight_packed_bytes(K, c_in, c_out) bytes, 16-byte aligned. Channels are
+ * zero-padded internally, so any c >= 1 works. Pack once per weight tensor and
+ * reuse the result for every forward; the forward takes weights packed for
+ * the map's kernel size (the caller's duty: a raw pointer carries no size).
  */
-int smc_weight_pack(const uint16_t* w, int c_in, int c_out, void* out, void* stream);
+int smc_weight_pack(const uint16_t* w, int kernel_size, int c_in, int c_out, void* out,
+                    void* stream);
 
 /*
  * One submanifold convolution layer over a built map. Two algorithms:
@@ -247,7 +259,7 @@ int smc_weight_pack(const uint16_t* w, int c_in, int c_out, void* out, void* str
  *    SMC_BUILD_NO_SORT.
  * Neither uses atomics: the output is the same on every run.
  * x       device pointer, bf16 [n, c_in] row-major (rows in coordinate order).
- * wpacked device pointer from smc_weight_pack(c_in, c_out).
+ * wpacked device pointer from smc_weight_pack(map kernel size, c_in, c_out).
  * y       device pointer, 16-byte aligned, bf16 [n, c_out] (float [n, c_out] with
  *         SMC_FWD_OUT_F32); every row is written.
  * flags   SMC_FWD_RELU | SMC_FWD_OUT_F32, or 0. Without SMC_FWD_OUT_F32 the output

@@ -52,8 +52,9 @@ class MapInfo(ctypes.Structure):
         ("origin", ctypes.c_int32 * 3), ("extent", ctypes.c_int32 * 3),
         ("batch", ctypes.c_int32), ("tile_m", ctypes.c_int32), ("grid_cells", ctypes.c_int64),
         ("pairs", ctypes.c_int64), ("pairs_padded", ctypes.c_int64), ("n_tiles", ctypes.c_int64),
-        ("tap_count", ctypes.c_int64 * 27), ("status", ctypes.c_int32),
+        ("tap_count", ctypes.c_int64 * 125), ("status", ctypes.c_int32),
         ("n_groups", ctypes.c_int32), ("group_rows", ctypes.c_int64 * 4),
+        ("kernel_size", ctypes.c_int32), ("taps", ctypes.c_int32),
     ]
 
 
@@ -85,9 +86,9 @@ def lib():
     L.smc_map_sync.argtypes = [vp]
     L.smc_map_info.argtypes = [vp, ctypes.POINTER(MapInfo)]
     L.smc_map_export.argtypes = [vp, vp, vp, vp, vp, vp, vp]
-    L.smc_weight_packed_bytes.argtypes = [i32, i32]
+    L.smc_weight_packed_bytes.argtypes = [i32, i32, i32]
     L.smc_weight_packed_bytes.restype = ctypes.c_size_t
-    L.smc_weight_pack.argtypes = [vp, i32, i32, vp, vp]
+    L.smc_weight_pack.argtypes = [vp, i32, i32, i32, vp, vp]
     L.smc_conv_forward.argtypes = [vp, vp, i32, vp, i32, vp, u32, vp]
     L.smc_status_string.argtypes = [i32]
     L.smc_status_string.restype = ctypes.c_char_p
@@ -136,28 +137,33 @@ def _need(t, dtype, name, ndim=None):
 class PackedWeights:
     """Weights packed for the GEMM; holds the device buffer."""
 
-    def __init__(self, buf, c_in: int, c_out: int):
-        self.buf, self.c_in, self.c_out = buf, c_in, c_out
+    def __init__(self, buf, c_in: int, c_out: int, kernel_size: int = 3):
+        self.buf, self.c_in, self.c_out, self.kernel_size = buf, c_in, c_out, kernel_size
+
+
+_KSIZE_OF_TAPS = {27: 3, 125: 5}
 
 
 def pack_weights(w, out: PackedWeights = None, stream=None) -> PackedWeights:
-    """bf16 [27, C_in, C_out] CUDA tensor -> PackedWeights (into ``out`` if given)."""
+    """bf16 [K^3, C_in, C_out] CUDA tensor (K = 3 or 5) -> PackedWeights
+    (into ``out`` if given)."""
     import torch
     _need(w, torch.bfloat16, "w", 3)
-    if w.shape[0] != 27:
-        raise ValueError("w must be [27, C_in, C_out]")
+    if int(w.shape[0]) not in _KSIZE_OF_TAPS:
+        raise ValueError("w must be [27, C_in, C_out] or [125, C_in, C_out]")
+    k = _KSIZE_OF_TAPS[int(w.shape[0])]
     c_in, c_out = int(w.shape[1]), int(w.shape[2])
     L = lib()
-    nbytes = L.smc_weight_packed_bytes(c_in, c_out)
+    nbytes = L.smc_weight_packed_bytes(k, c_in, c_out)
     if out is not None:
-        if (out.c_in, out.c_out) != (c_in, c_out):
-            raise ValueError("out was packed for other channel counts")
+        if (out.c_in, out.c_out, out.kernel_size) != (c_in, c_out, k):
+            raise ValueError("out was packed for other channel counts or kernel size")
         buf = out.buf
     else:
         buf = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
-    _check(L.smc_weight_pack(ctypes.c_void_p(w.data_ptr()), c_in, c_out,
+    _check(L.smc_weight_pack(ctypes.c_void_p(w.data_ptr()), k, c_in, c_out,
                              ctypes.c_void_p(buf.data_ptr()), _stream(stream)))
-    return PackedWeights(buf, c_in, c_out)
+    return PackedWeights(buf, c_in, c_out, k)
 
 
 class KernelMap:
@@ -167,6 +173,7 @@ class KernelMap:
         self._h = ctypes.c_void_p()
         _check(lib().smc_map_create(ctypes.byref(self._h)))
         self.n = 0
+        self.kernel_size = 3
         self._coords = None
 
     def close(self):
@@ -182,12 +189,13 @@ class KernelMap:
 
     def build(self, coords, spatial_shape=None, batch_size: int = 0, route: str = "auto",
               sync: bool = True, pairs: bool = True, sort: bool = True,
-              stream=None) -> "KernelMap":
+              kernel_size: int = 3, stream=None) -> "KernelMap":
         """coords: int32 [N, 4] (b, x, y, z) or [N, 3] (x, y, z) CUDA tensor.
 
         pairs=False skips the per-tap pair lists (algo="pairs" then refuses the
         map); sort=False skips the mask-sorted row order (algo="mask_tiles"
-        then refuses it)."""
+        then refuses it). kernel_size 3 or 5 (a 5x5x5 map has pair lists and
+        no mask order)."""
         import torch
         _need(coords, torch.int32, "coords", 2)
         n, ncols = int(coords.shape[0]), int(coords.shape[1])
@@ -196,11 +204,14 @@ class KernelMap:
             shape = (ctypes.c_int32 * 3)(*[int(v) for v in spatial_shape])
         flags = ((0 if sync else SMC_BUILD_ASYNC) | (0 if pairs else SMC_BUILD_NO_PAIRS)
                  | (0 if sort else SMC_BUILD_NO_SORT))
+        if kernel_size == 5:
+            flags |= SMC_BUILD_NO_SORT
         self._coords = coords          # keep alive while the stream reads it
         self.n = n
         _check(lib().smc_map_build(self._h, ctypes.c_void_p(coords.data_ptr() if n else 0), n,
-                                   ncols, shape, int(batch_size), 3, ROUTES[route], flags,
-                                   _stream(stream)))
+                                   ncols, shape, int(batch_size), int(kernel_size), ROUTES[route],
+                                   flags, _stream(stream)))
+        self.kernel_size = int(kernel_size)
         return self
 
     def sync(self):
@@ -244,17 +255,19 @@ class KernelMap:
                     origin=tuple(inf.origin), extent=tuple(inf.extent), batch=inf.batch,
                     tile_m=inf.tile_m, grid_cells=inf.grid_cells, pairs=inf.pairs,
                     pairs_padded=inf.pairs_padded, n_tiles=inf.n_tiles,
-                    tap_count=list(inf.tap_count), status=inf.status, n_groups=inf.n_groups,
-                    group_rows=list(inf.group_rows)[:inf.n_groups])
+                    tap_count=list(inf.tap_count)[:inf.taps], status=inf.status,
+                    n_groups=inf.n_groups, group_rows=list(inf.group_rows)[:inf.n_groups],
+                    kernel_size=inf.kernel_size, taps=inf.taps)
 
     def export(self, pairs: bool = True, perm: bool = True) -> dict:
         """Copy nbr, mask, tap offsets (and the mask-tile row orders [G, N], the
         pair lists) to numpy (host)."""
         import numpy as np
         info = self.info()
-        n, p = info["n"], info["pairs"]
-        out = dict(nbr=np.empty((n, 27), np.int32), mask=np.empty(n, np.uint32),
-                   tap_off=np.empty(28, np.int64))
+        n, p, taps = info["n"], info["pairs"], info["taps"]
+        out = dict(nbr=np.empty((n, taps), np.int32),
+                   mask=np.empty(n if taps == 27 else (n, 4), np.uint32),
+                   tap_off=np.empty(taps + 1, np.int64))
         if perm:
             out["perm"] = np.empty((max(info["n_groups"], 1), n), np.int32)
             out["group_rows"] = np.asarray(info["group_rows"], np.int64)
@@ -284,6 +297,8 @@ class KernelMap:
             raise ValueError(f"x has {x.shape[0]} rows, the map has {self.n}")
         if x.shape[1] != w.c_in:
             raise ValueError(f"x has {x.shape[1]} channels, weights expect {w.c_in}")
+        if w.kernel_size != self.kernel_size:
+            raise ValueError(f"weights are {w.kernel_size}^3, the map is {self.kernel_size}^3")
         odt = torch.float32 if out_f32 else torch.bfloat16
         if out is None:
             out = torch.empty((self.n, w.c_out), dtype=odt, device=x.device)
@@ -302,7 +317,9 @@ class KernelMap:
 
 
 def subm_conv3d(coords, x, w, spatial_shape=None, relu: bool = False, route: str = "auto"):
-    """One layer from raw inputs: builds a map, packs w, runs the layer."""
-    m = KernelMap().build(coords, spatial_shape=spatial_shape, route=route)
-    y = m.forward(x, pack_weights(w), relu=relu)
-    return y
+    """One layer from raw inputs: builds a map (kernel size from w: 27 or 125
+    taps), packs w, runs the layer."""
+    wp = pack_weights(w)
+    m = KernelMap().build(coords, spatial_shape=spatial_shape, route=route,
+                          kernel_size=wp.kernel_size)
+    return m.forward(x, wp, relu=relu)

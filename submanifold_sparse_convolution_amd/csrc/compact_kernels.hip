@@ -72,17 +72,17 @@ __device__ inline uint32_t lookback(uint64_t* look, int stride, int d, int64_t p
 }
 
 // Prefix of column k (k < NC) over blocks pb, pb-1, ..., read by the whole
-// block: thread t < 9 NC covers column t % NC and every 9th predecessor
-// starting at pb - t / NC, W of them per round trip (72 predecessors per
-// column per round). A round finds, per column, the nearest entry that
+// block: thread t < kLanes NC covers column t % NC and every kLanes-th
+// predecessor starting at pb - t / NC, W of them per round trip (kLanes W
+// predecessors per column per round; 9 lanes for 28 columns, 2 for 126). A round finds, per column, the nearest entry that
 // holds an inclusive prefix (LDS minimum of the distance), and sums the
 // entries up to and including it; columns without one go on to the next
 // round. Every thread of the block must call this. The result is in
 // s_sum[k] on return.
-template <int NC, int W>
+template <int NC, int W, int kLanes = 9>
 __device__ void block_lookback(uint64_t* look, int64_t pb, uint32_t epoch, uint32_t* status,
                                uint32_t* s_sum, uint32_t* s_near, uint32_t* s_done) {
-    constexpr int kLanes = 9;                     // threads per column
+    static_assert(kLanes * NC <= 256, "one thread per (column, lane)");
     const int tid = threadIdx.x;
     const int k = tid % NC, j0 = tid / NC;
     const bool active = tid < kLanes * NC;
@@ -301,6 +301,7 @@ __device__ __forceinline__ void compact_chunk(CompactLds& L, uint32_t m, uint32_
             } else {
                 st->totals[3] = (int32_t)tot;             // slab rows = off-centre pairs
                 st->tap_off[kTaps] = (int32_t)(kTaps * cap);
+                rowbase[n] = (int32_t)tot;                // end of the last row's run
             }
         }
     }
@@ -450,6 +451,122 @@ __global__ __launch_bounds__(kCThreads) void k_lookup_compact(
     if (bid == gridDim.x - 1 && tid == 0) atomicExch(ticket, 0u);
 }
 
+// Compaction for the 5 x 5 x 5 kernel: 125 taps, masks of 4 words. One row
+// per thread, 256-row chunks in row order; per-tap counts per wave from
+// ballots, block look-back over 126 columns (125 taps + slab rows, 2 lanes
+// per column), then each row writes its own pairs (positions from the wave
+// offsets and its rank in the ballot), its neighbour rows read straight
+// from the table. Same outputs and layout as the 3 x 3 x 3 compaction.
+constexpr int kK5Taps = 125, kK5Centre = 62, kK5Cols = kK5Taps + 1;
+
+__global__ __launch_bounds__(kCThreads) void k_compact5(
+    const uint32_t* __restrict__ mask, const int32_t* __restrict__ nbr, int64_t n, int64_t cap,
+    int tile_m, MapState* st, int32_t* __restrict__ pair_in, int32_t* __restrict__ pair_out,
+    int32_t* __restrict__ pair_slot, int32_t* __restrict__ rowbase, uint64_t* __restrict__ look,
+    uint32_t* ticket, uint32_t epoch, uint32_t* status) {
+    __shared__ uint32_t s_bid;
+    __shared__ uint32_t s_wc[kCWaves][kK5Cols];   // per-wave counts, then offsets in the chunk
+    __shared__ uint32_t s_pre[kK5Cols], s_tot[kK5Cols], s_near[kK5Cols], s_done[kK5Cols];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    if (tid == 0) s_bid = atomicAdd(ticket, 1u);
+    __syncthreads();
+    const uint32_t bid = s_bid;
+    const int64_t row = (int64_t)bid * kCChunk + tid;
+    const bool valid = row < n;
+    const int64_t rc = valid ? row : n - 1;
+    uint32_t mw[kMaxMaskWords];
+#pragma unroll
+    for (int q = 0; q < kMaxMaskWords; ++q) mw[q] = valid ? mask[rc * kMaxMaskWords + q] : 0u;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    uint32_t pop = 0;
+#pragma unroll
+    for (int q = 0; q < kMaxMaskWords; ++q) pop += (uint32_t)__popc(mw[q]);
+    const uint32_t deg = pop ? pop - 1u : 0u;     // off-centre pairs of the row
+#pragma unroll
+    for (int k = 0; k < kK5Taps; ++k) {
+        const uint64_t b = __ballot((mw[k >> 5] >> (k & 31)) & 1u);
+        if (lane == 0) s_wc[w][k] = (uint32_t)__popcll(b);
+    }
+    uint32_t incl = deg;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
+    }
+    if (lane == 63) s_wc[w][kK5Taps] = incl;
+    __syncthreads();
+    if (tid < kK5Cols) {
+        uint32_t run = 0;
+#pragma unroll
+        for (int v = 0; v < kCWaves; ++v) {
+            const uint32_t c = s_wc[v][tid];
+            s_wc[v][tid] = run;
+            run += c;
+        }
+        s_tot[tid] = run;
+        __hip_atomic_store(&look[(int64_t)bid * kK5Cols + tid],
+                           lb_pack(epoch, bid == 0 ? kIncl : kAgg, run), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    block_lookback<kK5Cols, 8, 2>(look, (int64_t)bid - 1, epoch, status, s_pre, s_near, s_done);
+    if (tid < kK5Cols) {
+        const uint32_t run = s_tot[tid], prefix = s_pre[tid];
+        if (bid > 0)
+            __hip_atomic_store(&look[(int64_t)bid * kK5Cols + tid],
+                               lb_pack(epoch, kIncl, prefix + run), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        if (bid == gridDim.x - 1) {
+            const uint32_t tot = prefix + run;
+            if (tid < kK5Taps) {
+                st->tap_count[tid] = (int32_t)tot;
+                st->tap_off[tid] = (int32_t)(tid * cap);
+            } else {
+                st->totals[3] = (int32_t)tot;
+                st->tap_off[kK5Taps] = (int32_t)(kK5Taps * cap);
+                rowbase[n] = (int32_t)tot;
+            }
+        }
+    }
+    __syncthreads();
+    if (tid == 0 && bid == gridDim.x - 1) {
+        int32_t p = 0, padded = 0;
+        for (int k = 0; k < kK5Taps; ++k) {
+            const int32_t c = (int32_t)(s_pre[k] + s_tot[k]);
+            p += c;
+            padded += (c + tile_m - 1) / tile_m * tile_m;
+        }
+        st->totals[0] = p;
+        st->totals[1] = padded;
+        st->totals[2] = padded / tile_m;
+    }
+    const uint32_t rb = s_pre[kK5Taps] + s_wc[w][kK5Taps] + incl - deg;
+    if (valid) rowbase[row] = (int32_t)rb;
+    const int32_t* nrow = nbr + rc * kK5Taps;
+    uint32_t rank = 0;                            // off-centre pairs of the row so far
+#pragma unroll
+    for (int q = 0; q < kMaxMaskWords; ++q) {
+        const uint32_t word = mw[q];
+#pragma unroll 4
+        for (int bb = 0; bb < 32; ++bb) {
+            const int k = 32 * q + bb;
+            if (k >= kK5Taps) break;
+            const bool has = (word >> bb) & 1u;
+            const uint64_t b = __ballot(has);
+            if (has) {
+                const int64_t pos =
+                    (int64_t)k * cap + s_pre[k] + s_wc[w][k] + (uint32_t)__popcll(b & below);
+                if (pos < (int64_t)k * cap + cap) {       // (only false after a stalled wait)
+                    pair_in[pos] = k == kK5Centre ? (int32_t)row : nrow[k];
+                    pair_out[pos] = (int32_t)row;
+                    pair_slot[pos] = k == kK5Centre ? -1 : (int32_t)(rb + rank);
+                }
+                if (k != kK5Centre) ++rank;
+            }
+        }
+    }
+    if (bid == gridDim.x - 1 && tid == 0) atomicExch(ticket, 0u);
+}
+
 }  // namespace
 
 int mask_sort_bits(const MaskOrder& ord) {
@@ -475,19 +592,27 @@ int64_t compact_chunks(int64_t n) { return (n + kCChunk - 1) / kCChunk; }
 
 size_t compact_look_bytes(int64_t n) { return (size_t)compact_chunks(n) * (kTaps + 1) * 8; }
 
+size_t compact_look_bytes_k(int64_t n, int ksize) {
+    return (size_t)compact_chunks(n) * (ksize == 5 ? kK5Cols : kTaps + 1) * 8;
+}
+
 static uint32_t next_epoch(SortWork& ws) {
     uint32_t epoch = ++ws.epoch & 0x3FFFFFFFu;
     if (epoch == 0) epoch = ++ws.epoch & 0x3FFFFFFFu;
     return epoch;
 }
 
-hipError_t launch_compact(const uint32_t* mask, const int32_t* nbr, int64_t n, int64_t cap,
-                          int tile_m, MapState* st, int32_t* pair_in, int32_t* pair_out,
-                          int32_t* pair_slot, int32_t* rowbase, SortWork& ws, uint32_t* status,
-                          hipStream_t s) {
+hipError_t launch_compact(const uint32_t* mask, const int32_t* nbr, int64_t n, int ksize,
+                          int64_t cap, int tile_m, MapState* st, int32_t* pair_in,
+                          int32_t* pair_out, int32_t* pair_slot, int32_t* rowbase, SortWork& ws,
+                          uint32_t* status, hipStream_t s) {
     const uint32_t epoch = next_epoch(ws);
-    launch(k_compact, (unsigned)compact_chunks(n), kCThreads, 0, s, mask, nbr, n, cap, tile_m, st,
-           pair_in, pair_out, pair_slot, rowbase, ws.look, ws.ticket, epoch, status);
+    if (ksize == 5)
+        launch(k_compact5, (unsigned)compact_chunks(n), kCThreads, 0, s, mask, nbr, n, cap, tile_m,
+               st, pair_in, pair_out, pair_slot, rowbase, ws.look, ws.ticket, epoch, status);
+    else
+        launch(k_compact, (unsigned)compact_chunks(n), kCThreads, 0, s, mask, nbr, n, cap, tile_m,
+               st, pair_in, pair_out, pair_slot, rowbase, ws.look, ws.ticket, epoch, status);
     return hipGetLastError();
 }
 

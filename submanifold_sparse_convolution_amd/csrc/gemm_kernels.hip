@@ -40,11 +40,11 @@ namespace {
 
 // Packed weights: [tap][wave tile][k-step][nb][lane][8] bf16; one MFMA's B
 // fragment is 1 KiB contiguous and a k-step's NBW fragments are adjacent.
-__global__ __launch_bounds__(kBlock) void k_weight_pack(const uint16_t* __restrict__ w, int c_in,
-                                                        int c_out, int nbw, int n_wt, int steps,
-                                                        uint4* __restrict__ out) {
+__global__ __launch_bounds__(kBlock) void k_weight_pack(const uint16_t* __restrict__ w, int taps,
+                                                        int c_in, int c_out, int nbw, int n_wt,
+                                                        int steps, uint4* __restrict__ out) {
     int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-    int64_t total = (int64_t)kTaps * n_wt * steps * nbw * 64;
+    int64_t total = (int64_t)taps * n_wt * steps * nbw * 64;
     if (t >= total) return;
     int lane = (int)(t & 63);
     int64_t r = t >> 6;
@@ -206,33 +206,35 @@ __device__ __forceinline__ void store_f32(float* __restrict__ dst, int col0, int
 template <int NBW, int MW, bool VEC, bool STREAM>
 __global__ __launch_bounds__(kGemmThreads, STREAM ? 1 : 2) void k_gemm_nc(
     const uint16_t* __restrict__ x, int c_in, int steps, const u32x4* __restrict__ wp, int n_wt,
-    int c_out, const int32_t* __restrict__ pair_in, const int32_t* __restrict__ pair_slot,
-    const MapState* __restrict__ st, int64_t cap, int64_t n, float* __restrict__ part) {
+    int c_out, int taps, const int32_t* __restrict__ pair_in,
+    const int32_t* __restrict__ pair_slot, const MapState* __restrict__ st, int64_t cap, int64_t n,
+    float* __restrict__ part) {
     constexpr int kRows = 64 * MW;                 // pairs per tile
     extern __shared__ u32x4 s_b[];
-    __shared__ int32_t s_first[kTaps + 1];        // first tile of each tap (centre: none)
-    __shared__ int32_t s_cnt[kTaps];
+    __shared__ int32_t s_first[kMaxTaps + 1];     // first tile of each tap (centre: none)
+    __shared__ int32_t s_cnt[kMaxTaps];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
+    const int centre = taps / 2;
     if (threadIdx.x == 0) {
         int32_t t = 0;
-        for (int k = 0; k < kTaps; ++k) {
-            const int32_t c = k == kCentre ? 0 : st->tap_count[k];
+        for (int k = 0; k < taps; ++k) {
+            const int32_t c = k == centre ? 0 : st->tap_count[k];
             s_cnt[k] = c;
             s_first[k] = t;
             t += (c + kRows - 1) / kRows;
         }
-        s_first[kTaps] = t;
+        s_first[taps] = t;
     }
     __syncthreads();
-    const int n_nc = s_first[kTaps];
+    const int n_nc = s_first[taps];
     const int wt_i = blockIdx.y;
     const int col0 = wt_i * 16 * NBW + r * NBW;
     const int64_t n16 = (int64_t)steps * NBW * 64;
     int last_tap = -1;                            // tap whose one-chunk slab is in LDS
+    int tap = 0;                                  // u only grows: the tap search resumes
     for (int u = blockIdx.x; u < n_nc; u += gridDim.x) {
-        int tap = 0;
-        while (tap + 1 < kTaps && s_first[tap + 1] <= u) ++tap;
+        while (tap + 1 < taps && s_first[tap + 1] <= u) ++tap;
         const int j0 = (u - s_first[tap]) * kRows + w * 16 * MW;   // this wave's first pair
         const int cnt = s_cnt[tap];
         const int64_t base = (int64_t)tap * cap + j0;
@@ -349,14 +351,14 @@ __device__ __forceinline__ void add_slab(const int32_t (&rb)[MW][4], const int32
 }
 
 // Loads of one 64 MW-row tile: gathered rows (first k-group), raw run bounds
-// (rowbase and mask of this lane's output rows).
+// (rowbase of this lane's 4 output rows, and the end of the last one's run:
+// rowbase[row + 1], rowbase[n] being the slab's size).
 template <int MW, bool VEC>
 __device__ __forceinline__ void centre_tile_loads(const uint16_t* __restrict__ x, int c_in, int steps,
-                                                  const uint32_t* __restrict__ mask,
                                                   const int32_t* __restrict__ rowbase, int64_t n,
                                                   int64_t row0, int r, int g,
                                                   const uint16_t* (&xrow)[MW], u32x4 (&a)[4][MW],
-                                                  int32_t (&rb)[MW][4], uint32_t (&mk)[MW][4]) {
+                                                  int32_t (&rb)[MW][4], int32_t (&rend)[MW]) {
 #pragma unroll
     for (int m = 0; m < MW; ++m) {
         const int64_t ir = row0 + m * 16 + r;
@@ -370,25 +372,24 @@ __device__ __forceinline__ void centre_tile_loads(const uint16_t* __restrict__ x
             const int64_t row = row0 + m * 16 + 4 * g + j;
             const int64_t rc = row < n ? row : n - 1;
             rb[m][j] = rowbase[rc];
-            mk[m][j] = mask[rc];
         }
+#pragma unroll
+    for (int m = 0; m < MW; ++m) {
+        const int64_t e = row0 + m * 16 + 4 * g + 4;          // one past the lane's last row
+        rend[m] = rowbase[e < n ? e : n];
+    }
 }
 
 // Slab runs from the raw bounds: rows past n get empty runs at the end of the
 // last real row's run. Returns the lane's total slab rows.
 template <int MW>
 __device__ __forceinline__ int centre_runs(int64_t row0, int g, int64_t n, int32_t (&rb)[MW][4],
-                                           const uint32_t (&mk)[MW][4], int32_t (&re)[MW],
+                                           const int32_t (&rend)[MW], int32_t (&re)[MW],
                                            int32_t (&len)[MW]) {
     int tot = 0;
 #pragma unroll
     for (int m = 0; m < MW; ++m) {
-        int32_t e = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t row = row0 + m * 16 + 4 * g + j;
-            if (row < n) e = rb[m][j] + __popc(mk[m][j] & ~(1u << kCentre));
-        }
+        const int32_t e = rend[m];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             if (row0 + m * 16 + 4 * g + j >= n) rb[m][j] = e;
@@ -402,7 +403,7 @@ __device__ __forceinline__ int centre_runs(int64_t row0, int g, int64_t n, int32
 template <int NBW, int MW, bool OUT_F32, bool VEC, bool STREAM>
 __global__ __launch_bounds__(kGemmThreads, STREAM ? 1 : 2) void k_gemm_centre(
     const uint16_t* __restrict__ x, int c_in, int steps, const u32x4* __restrict__ wp, int n_wt,
-    int c_out, const uint32_t* __restrict__ mask, const int32_t* __restrict__ rowbase, int64_t n,
+    int c_out, int centre, const int32_t* __restrict__ rowbase, int64_t n,
     const float* __restrict__ part, void* __restrict__ yv, int relu) {
     extern __shared__ u32x4 s_b[];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -414,19 +415,19 @@ __global__ __launch_bounds__(kGemmThreads, STREAM ? 1 : 2) void k_gemm_centre(
     const bool vec_part = col0 + NBW <= c_out && (c_out & 3) == 0 && NBW >= 4;
     const int64_t rows_per_tile = 64 * MW;
     const int64_t n_rt = (n + rows_per_tile - 1) / rows_per_tile;
-    const u32x4* src = wp + ((int64_t)kCentre * n_wt + wt_i) * n16;
+    const u32x4* src = wp + ((int64_t)centre * n_wt + wt_i) * n16;
     for (int64_t rt = blockIdx.x; rt < n_rt; rt += gridDim.x) {
         const int64_t row0 = rt * rows_per_tile + w * 16 * MW;
         const uint16_t* xrow[MW];
         u32x4 a[4][MW];
         int32_t rb[MW][4];
-        uint32_t mk[MW][4];
+        int32_t rend[MW];
         const bool resident = !STREAM && rt != blockIdx.x;    // the one-chunk slab stays in LDS
-        centre_tile_loads<MW, VEC>(x, c_in, steps, mask, rowbase, n, row0, r, g, xrow, a, rb, mk);
+        centre_tile_loads<MW, VEC>(x, c_in, steps, rowbase, n, row0, r, g, xrow, a, rb, rend);
         u32x4 bw[bg_per<NBW>()];
         if (STREAM || !resident) bg_fetch0<NBW>(src, steps, bw);
         int32_t re[MW], len[MW];
-        const int tot = centre_runs<MW>(row0, g, n, rb, mk, re, len);
+        const int tot = centre_runs<MW>(row0, g, n, rb, rend, re, len);
         float pv[kSlabBatch][NBW];
         load_slab<NBW, MW>(part, c_out, colc, vec_part, rb, len, tot, 0, pv);
         if (!resident) __syncthreads();            // the previous tile's reads of s_b are done
@@ -477,110 +478,112 @@ bool lds_ok(K kernel, size_t bytes) {
 
 template <int NBW, int MW, bool VEC, bool STREAM>
 void launch_nc_t(dim3 grid, hipStream_t s, const uint16_t* x, int c_in, int steps, const u32x4* wp,
-                 int n_wt, int c_out, const int32_t* pi, const int32_t* ps, const MapState* st,
-                 int64_t cap, int64_t n, float* part) {
+                 int n_wt, int c_out, int taps, const int32_t* pi, const int32_t* ps,
+                 const MapState* st, int64_t cap, int64_t n, float* part) {
     constexpr size_t lds = gemm_lds_bytes<NBW, STREAM>();
     static const bool ok = lds_ok(k_gemm_nc<NBW, MW, VEC, STREAM>, lds);
     (void)ok;
     launch(k_gemm_nc<NBW, MW, VEC, STREAM>, grid, kGemmThreads, lds, s, x, c_in, steps, wp, n_wt,
-           c_out, pi, ps, st, cap, n, part);
+           c_out, taps, pi, ps, st, cap, n, part);
 }
 
 template <int NBW>
 void launch_nc(dim3 grid, hipStream_t s, int mw, const uint16_t* x, int c_in, int steps,
-               const u32x4* wp, int n_wt, int c_out, const int32_t* pi, const int32_t* ps,
-               const MapState* st, int64_t cap, int64_t n, float* part) {
+               const u32x4* wp, int n_wt, int c_out, int taps, const int32_t* pi,
+               const int32_t* ps, const MapState* st, int64_t cap, int64_t n, float* part) {
     const bool vec = (c_in & 7) == 0;
     if (mw == 4)                                   // mw_nc_for: wide, 16-byte row loads
-        launch_nc_t<NBW, 4, true, true>(grid, s, x, c_in, steps, wp, n_wt, c_out, pi, ps, st, cap, n, part);
+        launch_nc_t<NBW, 4, true, true>(grid, s, x, c_in, steps, wp, n_wt, c_out, taps, pi, ps, st, cap, n, part);
     else if (steps > kChunk)
-        launch_nc_t<NBW, 1, false, true>(grid, s, x, c_in, steps, wp, n_wt, c_out, pi, ps, st, cap, n, part);
+        launch_nc_t<NBW, 1, false, true>(grid, s, x, c_in, steps, wp, n_wt, c_out, taps, pi, ps, st, cap, n, part);
     else if (vec)
-        launch_nc_t<NBW, 1, true, false>(grid, s, x, c_in, steps, wp, n_wt, c_out, pi, ps, st, cap, n, part);
+        launch_nc_t<NBW, 1, true, false>(grid, s, x, c_in, steps, wp, n_wt, c_out, taps, pi, ps, st, cap, n, part);
     else
-        launch_nc_t<NBW, 1, false, false>(grid, s, x, c_in, steps, wp, n_wt, c_out, pi, ps, st, cap, n, part);
+        launch_nc_t<NBW, 1, false, false>(grid, s, x, c_in, steps, wp, n_wt, c_out, taps, pi, ps, st, cap, n, part);
 }
 
 template <int NBW, int MW, bool OUT_F32, bool VEC, bool STREAM>
 void launch_centre_t(dim3 grid, hipStream_t s, const uint16_t* x, int c_in, int steps,
-                     const u32x4* wp, int n_wt, int c_out, const uint32_t* mask,
+                     const u32x4* wp, int n_wt, int c_out, int centre,
                      const int32_t* rowbase, int64_t n, const float* part, void* y, int relu) {
     constexpr size_t lds = gemm_lds_bytes<NBW, STREAM>();
     static const bool ok = lds_ok(k_gemm_centre<NBW, MW, OUT_F32, VEC, STREAM>, lds);
     (void)ok;
     launch(k_gemm_centre<NBW, MW, OUT_F32, VEC, STREAM>, grid, kGemmThreads, lds, s, x, c_in,
-           steps, wp, n_wt, c_out, mask, rowbase, n, part, y, relu);
+           steps, wp, n_wt, c_out, centre, rowbase, n, part, y, relu);
 }
 
 template <int NBW, int MW, bool VEC, bool STREAM>
 void launch_centre_mw(dim3 grid, hipStream_t s, bool out_f32, const uint16_t* x, int c_in,
-                      int steps, const u32x4* wp, int n_wt, int c_out, const uint32_t* mask,
+                      int steps, const u32x4* wp, int n_wt, int c_out, int centre,
                       const int32_t* rowbase, int64_t n, const float* part, void* y, int relu) {
     if (out_f32)
-        launch_centre_t<NBW, MW, true, VEC, STREAM>(grid, s, x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, relu);
+        launch_centre_t<NBW, MW, true, VEC, STREAM>(grid, s, x, c_in, steps, wp, n_wt, c_out, centre, rowbase, n, part, y, relu);
     else
-        launch_centre_t<NBW, MW, false, VEC, STREAM>(grid, s, x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, relu);
+        launch_centre_t<NBW, MW, false, VEC, STREAM>(grid, s, x, c_in, steps, wp, n_wt, c_out, centre, rowbase, n, part, y, relu);
 }
 
 template <int NBW>
 void launch_centre(dim3 grid, hipStream_t s, int mw, bool out_f32, const uint16_t* x, int c_in,
-                   int steps, const u32x4* wp, int n_wt, int c_out, const uint32_t* mask,
+                   int steps, const u32x4* wp, int n_wt, int c_out, int centre,
                    const int32_t* rowbase, int64_t n, const float* part, void* y, int relu) {
     const bool vec = (c_in & 7) == 0;
     if (mw == 4)                                   // mw_for: wide, 16-byte row loads
-        launch_centre_mw<NBW, 4, true, true>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, relu);
+        launch_centre_mw<NBW, 4, true, true>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, centre, rowbase, n, part, y, relu);
     else if (steps > kChunk)
-        launch_centre_mw<NBW, 2, false, true>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, relu);
+        launch_centre_mw<NBW, 2, false, true>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, centre, rowbase, n, part, y, relu);
     else if (vec)
-        launch_centre_mw<NBW, 2, true, false>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, relu);
+        launch_centre_mw<NBW, 2, true, false>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, centre, rowbase, n, part, y, relu);
     else
-        launch_centre_mw<NBW, 2, false, false>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, relu);
+        launch_centre_mw<NBW, 2, false, false>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, centre, rowbase, n, part, y, relu);
 }
 
 }  // namespace
 
-size_t packed_weight_bytes(int c_in, int c_out) {
+size_t packed_weight_bytes(int taps, int c_in, int c_out) {
     int64_t steps = (c_in + 31) / 32;
     int nbw = nbw_for(c_out);
     int64_t n_wt = (c_out + 16 * nbw - 1) / (16 * nbw);
-    return (size_t)(kTaps * n_wt * steps * nbw * 64 * 16);
+    return (size_t)(taps * n_wt * steps * nbw * 64 * 16);
 }
 
-hipError_t launch_weight_pack(const uint16_t* w, int c_in, int c_out, void* out, hipStream_t s) {
+hipError_t launch_weight_pack(const uint16_t* w, int taps, int c_in, int c_out, void* out,
+                              hipStream_t s) {
     int steps = (c_in + 31) / 32;
     int nbw = nbw_for(c_out);
     int n_wt = (c_out + 16 * nbw - 1) / (16 * nbw);
-    int64_t total = (int64_t)kTaps * n_wt * steps * nbw * 64;
+    int64_t total = (int64_t)taps * n_wt * steps * nbw * 64;
     unsigned blocks = (unsigned)((total + kBlock - 1) / kBlock);
-    launch(k_weight_pack, blocks, kBlock, 0, s, w, c_in, c_out, nbw, n_wt, steps, (uint4*)out);
+    launch(k_weight_pack, blocks, kBlock, 0, s, w, taps, c_in, c_out, nbw, n_wt, steps,
+           (uint4*)out);
     return hipGetLastError();
 }
 
-hipError_t launch_gemm_nc(const uint16_t* x, int c_in, const void* wpacked, int c_out,
+hipError_t launch_gemm_nc(const uint16_t* x, int c_in, const void* wpacked, int c_out, int taps,
                           const int32_t* pair_in, const int32_t* pair_slot, const MapState* st,
                           int64_t cap, int64_t n, int n_cu, float* part, hipStream_t s) {
     const int steps = (c_in + 31) / 32;
     const int nbw = nbw_for(c_out);
     const int n_wt = (c_out + 16 * nbw - 1) / (16 * nbw);
     const int mw = mw_nc_for(c_in);
-    int64_t gx = (kTaps - 1) * (cap / (64 * mw));  // tiles if every tap were full
+    int64_t gx = (taps - 1) * (cap / (64 * mw));  // tiles if every tap were full
     if (gx > (int64_t)n_cu * 2) gx = (int64_t)n_cu * 2;
     if (gx < 1) gx = 1;
     dim3 grid((unsigned)gx, (unsigned)n_wt);
     const u32x4* wp = (const u32x4*)wpacked;
     switch (nbw) {
-        case 1: launch_nc<1>(grid, s, mw, x, c_in, steps, wp, n_wt, c_out, pair_in, pair_slot, st, cap, n, part); break;
-        case 2: launch_nc<2>(grid, s, mw, x, c_in, steps, wp, n_wt, c_out, pair_in, pair_slot, st, cap, n, part); break;
-        case 4: launch_nc<4>(grid, s, mw, x, c_in, steps, wp, n_wt, c_out, pair_in, pair_slot, st, cap, n, part); break;
-        default: launch_nc<8>(grid, s, mw, x, c_in, steps, wp, n_wt, c_out, pair_in, pair_slot, st, cap, n, part); break;
+        case 1: launch_nc<1>(grid, s, mw, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part); break;
+        case 2: launch_nc<2>(grid, s, mw, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part); break;
+        case 4: launch_nc<4>(grid, s, mw, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part); break;
+        default: launch_nc<8>(grid, s, mw, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part); break;
     }
     return hipGetLastError();
 }
 
 hipError_t launch_gemm_centre(const uint16_t* x, int c_in, const void* wpacked, int c_out,
-                              const uint32_t* mask, const int32_t* rowbase, int64_t n,
-                              const float* part, void* y, bool out_f32, bool relu, int n_cu,
-                              hipStream_t s) {
+                              int taps, const int32_t* rowbase, int64_t n, const float* part,
+                              void* y, bool out_f32, bool relu, int n_cu, hipStream_t s) {
+    const int centre = taps / 2;
     if (n <= 0) return hipSuccess;
     const int steps = (c_in + 31) / 32;
     const int nbw = nbw_for(c_out);
@@ -592,10 +595,10 @@ hipError_t launch_gemm_centre(const uint16_t* x, int c_in, const void* wpacked, 
     const u32x4* wp = (const u32x4*)wpacked;
     const int rl = relu ? 1 : 0;
     switch (nbw) {
-        case 1: launch_centre<1>(grid, s, mw, out_f32, x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, rl); break;
-        case 2: launch_centre<2>(grid, s, mw, out_f32, x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, rl); break;
-        case 4: launch_centre<4>(grid, s, mw, out_f32, x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, rl); break;
-        default: launch_centre<8>(grid, s, mw, out_f32, x, c_in, steps, wp, n_wt, c_out, mask, rowbase, n, part, y, rl); break;
+        case 1: launch_centre<1>(grid, s, mw, out_f32, x, c_in, steps, wp, n_wt, c_out, centre, rowbase, n, part, y, rl); break;
+        case 2: launch_centre<2>(grid, s, mw, out_f32, x, c_in, steps, wp, n_wt, c_out, centre, rowbase, n, part, y, rl); break;
+        case 4: launch_centre<4>(grid, s, mw, out_f32, x, c_in, steps, wp, n_wt, c_out, centre, rowbase, n, part, y, rl); break;
+        default: launch_centre<8>(grid, s, mw, out_f32, x, c_in, steps, wp, n_wt, c_out, centre, rowbase, n, part, y, rl); break;
     }
     return hipGetLastError();
 }

@@ -33,7 +33,7 @@ __device__ inline bool load_rel(const int32_t* __restrict__ coords, int64_t i, c
 
 // cell of a voxel in the grid padded by one cell on every side
 __device__ inline int64_t dense_cell(const Geom& g, int b, int x, int y, int z) {
-    return b * g.sz_b + (int64_t)(x + 1) * g.sz_x + (int64_t)(y + 1) * g.sz_y + (z + 1);
+    return b * g.sz_b + (int64_t)(x + g.pad) * g.sz_x + (int64_t)(y + g.pad) * g.sz_y + (z + g.pad);
 }
 
 // Puts a build record in its starting state (bounding box empty, everything
@@ -171,8 +171,38 @@ __global__ __launch_bounds__(kBlock) void k_dense_lookup(const int32_t* __restri
     if (row < n && k == 0) mask[row] = (uint32_t)(hits >> (threadIdx.x & 32));
 }
 
-// Packed key of a voxel, fields (b | x+1 | y+1 | z+1) from high to low. The
-// one-cell padding keeps every neighbour query inside its field, so the key
+// 5 x 5 x 5 kernel: 128 lanes per row (125 active), lane k reads the cell at
+// offset d_k. The two waves of a row hold taps 0..63 and 64..127; each
+// wave's ballot of hits is two words of the row's 4-word mask.
+__global__ __launch_bounds__(kBlock) void k_dense_lookup5(const int32_t* __restrict__ coords,
+                                                          int64_t n, Geom g,
+                                                          const int32_t* __restrict__ grid,
+                                                          int32_t* __restrict__ nbr,
+                                                          uint32_t* __restrict__ mask) {
+    constexpr int kT = 125;
+    const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    const int64_t row = t >> 7;
+    const int k = (int)(t & 127);
+    const bool live = row < n && k < kT;
+    int v = -1;
+    if (live) {
+        int b, x, y, z;
+        if (load_rel(coords, row, g, b, x, y, z)) {
+            const int dx = k / 25 - 2, dy = (k / 5) % 5 - 2, dz = k % 5 - 2;
+            v = grid[dense_cell(g, b, x, y, z) + dx * g.sz_x + dy * g.sz_y + dz];
+        }
+        nbr[row * kT + k] = v;
+    }
+    const uint64_t hits = __ballot(v >= 0);
+    if (row < n && (k & 63) == 0) {
+        const int h = k >> 6;
+        mask[row * kMaxMaskWords + 2 * h] = (uint32_t)hits;
+        mask[row * kMaxMaskWords + 2 * h + 1] = (uint32_t)(hits >> 32);
+    }
+}
+
+// Packed key of a voxel, fields (b | x+r | y+r | z+r) from high to low. The
+// r-cell padding keeps every neighbour query inside its field, so the key
 // of q + d is key(q) + packed(d) with no carry between fields (the
 // packed(q+d) = packed(q) + packed(d) property of the Z-Delta mapper).
 template <typename K>
@@ -186,9 +216,9 @@ __global__ __launch_bounds__(kBlock) void k_make_keys(const int32_t* __restrict_
     K key;
     if (load_rel(coords, i, g, b, x, y, z)) {
         key = (K)b;
-        key = (key << g.wx) | (K)(x + 1);
-        key = (key << g.wy) | (K)(y + 1);
-        key = (key << g.wz) | (K)(z + 1);
+        key = (key << g.wx) | (K)(x + g.pad);
+        key = (key << g.wy) | (K)(y + g.pad);
+        key = (key << g.wz) | (K)(z + g.pad);
     } else {
         atomicOr(&st->status, kStRange);
         key = ~(K)0;
@@ -211,53 +241,74 @@ __device__ inline int64_t lower_bound(const K* __restrict__ keys, int64_t n, K t
     return lo;
 }
 
-// 16 lanes per sorted key (9 active), one per (dx, dy) column. The three
-// taps of a column (dz = -1, 0, +1) have consecutive keys, and so sit at
-// consecutive sorted positions when present: one binary search for the
-// column's lowest key, then up to three compares walking forward. The
-// centre column needs no search: its keys are at s - 1, s, s + 1.
-template <typename K>
+// Lanes per sorted key: one per (dx, dy) column (9 for K = 3, 25 for K = 5),
+// rounded up to a power of two. The K taps of a column (dz = -r .. r) have
+// consecutive keys, and so sit at consecutive sorted positions when
+// present: one binary search for the column's lowest key, then up to K
+// compares walking forward. The centre column needs no search: its keys
+// are at s - r .. s + r, found by stepping back from s.
+template <typename K, int KS>
 __global__ __launch_bounds__(kBlock) void k_sorted_lookup(const K* __restrict__ keys,
                                                           const uint32_t* __restrict__ vals,
                                                           int64_t n, Geom g,
                                                           int32_t* __restrict__ nbr,
                                                           uint32_t* __restrict__ mask,
                                                           MapState* st) {
-    int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-    int64_t s = t >> 4;
-    int c = (int)(t & 15);
-    uint32_t bits = 0;
-    if (s < n && c < 9) {
-        K q = keys[s];
+    constexpr int R = (KS - 1) / 2, COLS = KS * KS, KV = KS * KS * KS;
+    constexpr int LANES = KS == 3 ? 16 : 32;
+    constexpr int MW = (KV + 31) / 32;
+    const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    const int64_t s = t / LANES;
+    const int c = (int)(t % LANES);
+    uint32_t bits[MW];
+#pragma unroll
+    for (int q = 0; q < MW; ++q) bits[q] = 0;
+    if (s < n && c < COLS) {
+        const K q = keys[s];
         // vals is a permutation of [0, n); the clamps only matter if a sort wait stalled
-        int row = (int)min(vals[s], (uint32_t)(n - 1));
-        int dx = c / 3 - 1, dy = c % 3 - 1;
-        K delta = (K)((int64_t)dx * ((int64_t)1 << (g.wy + g.wz))) +
-                  (K)((int64_t)dy * ((int64_t)1 << g.wz));
-        K first = q + delta - (K)1;
+        const int row = (int)min(vals[s], (uint32_t)(n - 1));
+        const int dx = c / KS - R, dy = c % KS - R;
+        const K delta = (K)((int64_t)dx * ((int64_t)1 << (g.wy + g.wz))) +
+                        (K)((int64_t)dy * ((int64_t)1 << g.wz));
+        const K first = q + delta - (K)R;
         int64_t j;
-        if (c == 4) {
-            j = (s > 0 && keys[s - 1] == first) ? s - 1 : s;
+        if (c == COLS / 2) {
+            j = s;
+#pragma unroll
+            for (int i = 0; i < R; ++i)
+                if (j > 0 && keys[j - 1] >= first) --j;
             if (s + 1 < n && keys[s + 1] == q) atomicOr(&st->status, kStDuplicate);
         } else {
             j = lower_bound(keys, n, first);
         }
 #pragma unroll
-        for (int dz = 0; dz < 3; ++dz) {
+        for (int dz = 0; dz < KS; ++dz) {
             int hit = -1;
             if (j < n && keys[j] == first + (K)dz) {
                 hit = (int)min(vals[j], (uint32_t)(n - 1));
                 ++j;
             }
-            nbr[(int64_t)row * kTaps + 3 * c + dz] = hit;
-            if (hit >= 0) bits |= 1u << (3 * c + dz);
+            const int kk = KS * c + dz;
+            nbr[(int64_t)row * KV + kk] = hit;
+            if (hit >= 0) {
+#pragma unroll
+                for (int w = 0; w < MW; ++w) bits[w] |= (kk >> 5) == w ? 1u << (kk & 31) : 0u;
+            }
         }
     }
-    bits |= __shfl_xor(bits, 8, 16);
-    bits |= __shfl_xor(bits, 4, 16);
-    bits |= __shfl_xor(bits, 2, 16);
-    bits |= __shfl_xor(bits, 1, 16);
-    if (s < n && c == 0) mask[min(vals[s], (uint32_t)(n - 1))] = bits;
+#pragma unroll
+    for (int w = 0; w < MW; ++w)
+#pragma unroll
+        for (int o = LANES / 2; o > 0; o >>= 1) bits[w] |= __shfl_xor(bits[w], o, LANES);
+    if (s < n && c == 0) {
+        const int64_t r = min(vals[s], (uint32_t)(n - 1));
+        if (KS == 3) {
+            mask[r] = bits[0];
+        } else {
+#pragma unroll
+            for (int w = 0; w < MW; ++w) mask[r * kMaxMaskWords + w] = bits[w];
+        }
+    }
 }
 
 inline unsigned blocks_for(int64_t threads) {
@@ -307,7 +358,10 @@ hipError_t launch_clear_cells(const PrevCells& prev, hipStream_t s) {
 
 hipError_t launch_dense_lookup(const int32_t* coords, int64_t n, const Geom& g, const int32_t* grid,
                                int32_t* nbr, uint32_t* mask, hipStream_t s) {
-    launch(k_dense_lookup, blocks_for(n * 32), kBlock, 0, s, coords, n, g, grid, nbr, mask);
+    if (g.ksize == 5)
+        launch(k_dense_lookup5, blocks_for(n * 128), kBlock, 0, s, coords, n, g, grid, nbr, mask);
+    else
+        launch(k_dense_lookup, blocks_for(n * 32), kBlock, 0, s, coords, n, g, grid, nbr, mask);
     return hipGetLastError();
 }
 
@@ -323,12 +377,20 @@ hipError_t launch_make_keys(const int32_t* coords, int64_t n, const Geom& g, boo
 hipError_t launch_sorted_lookup(const void* keys, const uint32_t* vals, int64_t n, const Geom& g,
                                 bool wide, int32_t* nbr, uint32_t* mask, MapState* st,
                                 hipStream_t s) {
-    if (wide)
-        launch(k_sorted_lookup<uint64_t>, blocks_for(n * 16), kBlock, 0, s, 
-            (const uint64_t*)keys, vals, n, g, nbr, mask, st);
-    else
-        launch(k_sorted_lookup<uint32_t>, blocks_for(n * 16), kBlock, 0, s, 
-            (const uint32_t*)keys, vals, n, g, nbr, mask, st);
+    if (g.ksize == 5) {
+        if (wide)
+            launch(k_sorted_lookup<uint64_t, 5>, blocks_for(n * 32), kBlock, 0, s,
+                   (const uint64_t*)keys, vals, n, g, nbr, mask, st);
+        else
+            launch(k_sorted_lookup<uint32_t, 5>, blocks_for(n * 32), kBlock, 0, s,
+                   (const uint32_t*)keys, vals, n, g, nbr, mask, st);
+    } else if (wide) {
+        launch(k_sorted_lookup<uint64_t, 3>, blocks_for(n * 16), kBlock, 0, s,
+               (const uint64_t*)keys, vals, n, g, nbr, mask, st);
+    } else {
+        launch(k_sorted_lookup<uint32_t, 3>, blocks_for(n * 16), kBlock, 0, s,
+               (const uint32_t*)keys, vals, n, g, nbr, mask, st);
+    }
     return hipGetLastError();
 }
 

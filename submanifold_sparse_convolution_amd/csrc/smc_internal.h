@@ -7,8 +7,10 @@
 
 namespace smc {
 
-constexpr int kTaps = 27;
+constexpr int kTaps = 27;           // 3 x 3 x 3 kernel (the mask-tile path, the fused lookup)
 constexpr int kCentre = 13;
+constexpr int kMaxTaps = 125;       // 5 x 5 x 5 kernel
+constexpr int kMaxMaskWords = 4;    // 32-bit words of a 125-bit mask
 constexpr int kTileM = 64;          // granularity of the per-tap pair counts reported as padded
 constexpr int kCapAlign = 256;      // each tap's run of the pair arrays: n rounded up to this
                                     // (a multiple of every GEMM tile height)
@@ -42,9 +44,9 @@ struct MapState {
     uint32_t status;        // kSt* bits
     int32_t bbox[8];        // min x, y, z, max x, y, z, min b, max b
     int32_t totals[4];      // pairs, pairs padded per tap to the tile, tiles, slab rows
-    int32_t tap_off[28];    // start of each tap's pair run (k * cap; tap_off[27] = 27 cap)
-    int32_t tap_count[27];  // pairs per tap (written by the compaction)
-    int32_t tap_tot[27];    // pairs per tap, accumulated by the mask histogram
+    int32_t tap_off[kMaxTaps + 1];  // start of each tap's pair run (k cap; tap_off[taps] = taps cap)
+    int32_t tap_count[kMaxTaps];    // pairs per tap (written by the compaction)
+    int32_t tap_tot[kTaps];         // pairs per tap, accumulated by the mask histogram (K = 3)
     int32_t group_rows[4];  // rows with a tap in each offset group (mask-tile row orders)
 };
 
@@ -88,10 +90,12 @@ struct Geom {
     int32_t ext[3];
     int32_t batch;
     int32_t ncols;
-    // dense route: strides of the grid padded by one cell on every side
-    int64_t sz_y;           // (Z + 2)
-    int64_t sz_x;           // (Y + 2) (Z + 2)
-    int64_t sz_b;           // (X + 2) (Y + 2) (Z + 2)
+    int32_t ksize;          // kernel size K (3 or 5)
+    int32_t pad;            // r = (K - 1) / 2: padding cells per side (grid) / key offset
+    // dense route: strides of the grid padded by r cells on every side
+    int64_t sz_y;           // (Z + 2r)
+    int64_t sz_x;           // (Y + 2r) (Z + 2r)
+    int64_t sz_b;           // (X + 2r) (Y + 2r) (Z + 2r)
     // sorted route: bit widths of the packed key fields (z lowest)
     int32_t wz, wy, wx, wb;
 };
@@ -122,6 +126,7 @@ hipError_t launch_dense_scatter(const int32_t* coords, int64_t n, const Geom& g,
                                 int32_t* cells, MapState* st, const NextRecord& next,
                                 const PrevCells& prev, hipStream_t s);
 hipError_t launch_clear_cells(const PrevCells& prev, hipStream_t s);
+// nbr [n, K^3]; mask [n] (K = 3) or [n, 4] words (K = 5): g.ksize decides.
 hipError_t launch_dense_lookup(const int32_t* coords, int64_t n, const Geom& g, const int32_t* grid,
                                int32_t* nbr, uint32_t* mask, hipStream_t s);
 hipError_t launch_make_keys(const int32_t* coords, int64_t n, const Geom& g, bool wide, void* keys,
@@ -165,13 +170,15 @@ hipError_t launch_mask_hist(const uint32_t* mask, int64_t n, const SortPlan& pla
                             int32_t* group_rows, hipStream_t s);
 int64_t compact_chunks(int64_t n);
 size_t compact_look_bytes(int64_t n);
+size_t compact_look_bytes_k(int64_t n, int ksize);
 // Pairs of tap k go to [k cap, k cap + tap_count[k]) in ascending output row;
 // pair_slot numbers the off-centre pairs row by row (rowbase[i] = first slab
-// row of output row i).
-hipError_t launch_compact(const uint32_t* mask, const int32_t* nbr, int64_t n, int64_t cap,
-                          int tile_m, MapState* st, int32_t* pair_in, int32_t* pair_out,
-                          int32_t* pair_slot, int32_t* rowbase, SortWork& ws, uint32_t* status,
-                          hipStream_t s);
+// row of output row i; rowbase[n] = all off-centre pairs). ksize 3 or 5
+// (mask words and tap count follow it).
+hipError_t launch_compact(const uint32_t* mask, const int32_t* nbr, int64_t n, int ksize,
+                          int64_t cap, int tile_m, MapState* st, int32_t* pair_in,
+                          int32_t* pair_out, int32_t* pair_slot, int32_t* rowbase, SortWork& ws,
+                          uint32_t* status, hipStream_t s);
 // Dense route: neighbour lookup and compaction in one kernel (also writes nbr
 // and mask).
 hipError_t launch_lookup_compact(const int32_t* coords, int64_t n, const Geom& g,
@@ -181,15 +188,17 @@ hipError_t launch_lookup_compact(const int32_t* coords, int64_t n, const Geom& g
                                  uint32_t* status, hipStream_t s);
 
 // ---- GEMM (gemm_kernels.hip) ----
-size_t packed_weight_bytes(int c_in, int c_out);
-hipError_t launch_weight_pack(const uint16_t* w, int c_in, int c_out, void* out, hipStream_t s);
-hipError_t launch_gemm_nc(const uint16_t* x, int c_in, const void* wpacked, int c_out,
+// taps: 27 or 125 (the packed weights hold that many taps).
+size_t packed_weight_bytes(int taps, int c_in, int c_out);
+hipError_t launch_weight_pack(const uint16_t* w, int taps, int c_in, int c_out, void* out,
+                              hipStream_t s);
+hipError_t launch_gemm_nc(const uint16_t* x, int c_in, const void* wpacked, int c_out, int taps,
                           const int32_t* pair_in, const int32_t* pair_slot, const MapState* st,
                           int64_t cap, int64_t n, int n_cu, float* part, hipStream_t s);
+// rowbase: [n + 1], row i's slab rows are rowbase[i] .. rowbase[i+1] - 1.
 hipError_t launch_gemm_centre(const uint16_t* x, int c_in, const void* wpacked, int c_out,
-                              const uint32_t* mask, const int32_t* rowbase, int64_t n,
-                              const float* part, void* y, bool out_f32, bool relu, int n_cu,
-                              hipStream_t s);
+                              int taps, const int32_t* rowbase, int64_t n, const float* part,
+                              void* y, bool out_f32, bool relu, int n_cu, hipStream_t s);
 
 // ---- mask-tile GEMM (masktile_kernels.hip) ----
 // One pass over the rows of one offset group: taps gm of the rows listed at

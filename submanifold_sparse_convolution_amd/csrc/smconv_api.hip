@@ -128,6 +128,7 @@ struct smc_map {
     DevBuf zrow;                      // zero row read for absent neighbours (mask-tile GEMM)
     bool has_pairs = false;
     bool has_sort = false;
+    int ksize = 3;                    // kernel size of the last build (taps = ksize^3)
     // stage timers
     bool timing = false;
     std::vector<hipEvent_t> ev_pool;
@@ -352,7 +353,10 @@ int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
                   const int32_t* spatial_shape, int batch_size, int kernel_size, int route,
                   unsigned flags, void* stream) {
     if (!m) return fail(SMC_ERR_ARG, "map is NULL");
-    if (kernel_size != 3) return fail(SMC_ERR_UNSUPPORTED, "kernel_size %d (only 3)", kernel_size);
+    if (kernel_size != 3 && kernel_size != 5)
+        return fail(SMC_ERR_UNSUPPORTED, "kernel_size %d (3 or 5)", kernel_size);
+    if (kernel_size == 5 && (flags & SMC_BUILD_NO_PAIRS))
+        return fail(SMC_ERR_UNSUPPORTED, "kernel_size 5 maps always carry pair lists");
     if (ncols != 3 && ncols != 4) return fail(SMC_ERR_ARG, "ncols must be 3 or 4, got %d", ncols);
     if (n < 0 || n > kMaxRows) return fail(SMC_ERR_ARG, "n = %lld out of [0, 2^26]", (long long)n);
     if (n > 0 && !coords) return fail(SMC_ERR_ARG, "coords is NULL");
@@ -387,6 +391,10 @@ int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     // ---- geometry: explicit shape, or the bounding box (one read) ----
     Geom g{};
     g.ncols = ncols;
+    g.ksize = kernel_size;
+    g.pad = (kernel_size - 1) / 2;
+    const int taps = kernel_size * kernel_size * kernel_size;
+    const int mwords = kernel_size == 3 ? 1 : kMaxMaskWords;
     const bool need_bbox = n > 0 && (!spatial_shape || (ncols == 4 && batch_size <= 0));
     int32_t bbox[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (need_bbox) {
@@ -422,7 +430,9 @@ int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     }
 
     // ---- route by grid volume ----
-    const double cells_d = (double)g.batch * (g.ext[0] + 2.0) * (g.ext[1] + 2.0) * (g.ext[2] + 2.0);
+    const double pad2 = 2.0 * g.pad;
+    const double cells_d =
+        (double)g.batch * (g.ext[0] + pad2) * (g.ext[1] + pad2) * (g.ext[2] + pad2);
     const bool dense_addressable = cells_d < 2147483648.0;
     int chosen;
     if (route == SMC_ROUTE_DENSE) {
@@ -435,14 +445,15 @@ int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
         chosen = (dense_addressable && cells_d * 4.0 <= (double)kDenseBudgetBytes)
                      ? SMC_ROUTE_DENSE : SMC_ROUTE_SORTED;
     }
-    g.sz_y = g.ext[2] + 2;
-    g.sz_x = (int64_t)(g.ext[1] + 2) * g.sz_y;
-    g.sz_b = (int64_t)(g.ext[0] + 2) * g.sz_x;
+    g.sz_y = g.ext[2] + 2 * g.pad;
+    g.sz_x = (int64_t)(g.ext[1] + 2 * g.pad) * g.sz_y;
+    g.sz_b = (int64_t)(g.ext[0] + 2 * g.pad) * g.sz_x;
     int key_bits = 0;
     if (chosen == SMC_ROUTE_SORTED) {
-        g.wz = bit_len((int64_t)g.ext[2] + 1);
-        g.wy = bit_len((int64_t)g.ext[1] + 1);
-        g.wx = bit_len((int64_t)g.ext[0] + 1);
+        // a field holds c + r + d for d in [-r, r]: 0 .. ext - 1 + 2r
+        g.wz = bit_len((int64_t)g.ext[2] - 1 + 2 * g.pad);
+        g.wy = bit_len((int64_t)g.ext[1] - 1 + 2 * g.pad);
+        g.wx = bit_len((int64_t)g.ext[0] - 1 + 2 * g.pad);
         g.wb = bit_len((int64_t)g.batch - 1);
         key_bits = g.wz + g.wy + g.wx + g.wb;
         if (key_bits > 64)
@@ -457,27 +468,28 @@ int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
 
     // ---- buffers ----
     const bool want_pairs = !(flags & SMC_BUILD_NO_PAIRS);
-    const bool want_sort = !(flags & SMC_BUILD_NO_SORT);
+    const bool want_sort = !(flags & SMC_BUILD_NO_SORT) && kernel_size == 3;   // mask tiles: 3^3
     const int64_t nn = n > 0 ? n : 1;
     const int64_t cap = (nn + kCapAlign - 1) / kCapAlign * kCapAlign;
     const MaskOrder ord = want_sort ? m->order : MaskOrder();
     const int64_t items = nn * ord.n_groups;          // mask-sort items: one per (group, row)
     size_t look_bytes = sort_look_bytes(items > nn ? items : nn);
-    const size_t look_c = compact_look_bytes(nn);
+    const size_t look_c = compact_look_bytes_k(nn, kernel_size);
     if (look_c > look_bytes) look_bytes = look_c;
     const size_t look_before = m->look.bytes;
     // (the neighbour table is read in whole 16-byte words: keep the last one readable)
-    if ((rc = m->nbr.ensure((size_t)nn * kTaps * 4 + 16)) || (rc = m->mask.ensure((size_t)nn * 4)) ||
+    if ((rc = m->nbr.ensure((size_t)nn * taps * 4 + 16)) ||
+        (rc = m->mask.ensure((size_t)nn * mwords * 4)) ||
         (rc = m->mkey0.ensure((size_t)items * 4)) || (rc = m->mkey1.ensure((size_t)items * 4)) ||
         (rc = m->mval0.ensure((size_t)items * 4)) || (rc = m->mval1.ensure((size_t)items * 4)) ||
         (rc = m->look.ensure(look_bytes)))
         return rc;
     if (!ord.plain && (rc = m->okeys.ensure((size_t)items * 4))) return rc;
     if (want_pairs &&
-        ((rc = m->pair_in.ensure((size_t)kTaps * cap * 4)) ||
-         (rc = m->pair_out.ensure((size_t)kTaps * cap * 4)) ||
-         (rc = m->pair_slot.ensure((size_t)kTaps * cap * 4)) ||
-         (rc = m->rowbase.ensure((size_t)nn * 4))))
+        ((rc = m->pair_in.ensure((size_t)taps * cap * 4)) ||
+         (rc = m->pair_out.ensure((size_t)taps * cap * 4)) ||
+         (rc = m->pair_slot.ensure((size_t)taps * cap * 4)) ||
+         (rc = m->rowbase.ensure((size_t)(nn + 1) * 4))))
         return rc;
     if (m->look.bytes != look_before || look_before == 0)   // new table: epoch 0 everywhere
         SMC_HIP(launch_fill_i32(m->look.as<int32_t>(), (int64_t)(m->look.bytes / 4), 0, s));
@@ -488,7 +500,7 @@ int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     if (n > 0) {
         int32_t* nbr = m->nbr.as<int32_t>();
         uint32_t* mask = m->mask.as<uint32_t>();
-        const bool fused = chosen == SMC_ROUTE_DENSE && want_pairs;
+        const bool fused = chosen == SMC_ROUTE_DENSE && want_pairs && kernel_size == 3;
         StageTimer t_nb(m, SMC_STAGE_NEIGHBOURS, s);
         if (chosen == SMC_ROUTE_DENSE) {
             const int gi = m->next_grid;
@@ -569,7 +581,8 @@ int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
         }
         if (want_pairs && !fused) {
             StageTimer t_cp(m, SMC_STAGE_COMPACT, s);
-            SMC_HIP(launch_compact(mask, nbr, n, cap, kTileM, st, m->pair_in.as<int32_t>(),
+            SMC_HIP(launch_compact(mask, nbr, n, kernel_size, cap, kTileM, st,
+                                   m->pair_in.as<int32_t>(),
                                    m->pair_out.as<int32_t>(), m->pair_slot.as<int32_t>(),
                                    m->rowbase.as<int32_t>(), m->ws, status, s));
             t_cp.finish();
@@ -578,6 +591,7 @@ int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     m->has_pairs = want_pairs;
     m->has_sort = want_sort;
     m->sorted_order = ord;
+    m->ksize = kernel_size;
     t_map.finish();
     const bool async = (flags & SMC_BUILD_ASYNC) != 0;
     if (!async)
@@ -614,6 +628,9 @@ int smc_map_info(smc_map* m, smc_map_info_t* info) {
     info->batch = m->geom.batch;
     info->tile_m = kTileM;
     info->grid_cells = m->grid_cells;
+    info->kernel_size = m->ksize;
+    const int taps = m->ksize * m->ksize * m->ksize;
+    info->taps = taps;
     const MapState& hs = *m->host_state;
     if (m->n == 0) {
         // nothing was counted
@@ -621,7 +638,7 @@ int smc_map_info(smc_map* m, smc_map_info_t* info) {
         info->pairs = hs.totals[0];
         info->pairs_padded = hs.totals[1];
         info->n_tiles = hs.totals[2];
-        for (int k = 0; k < kTaps; ++k) info->tap_count[k] = hs.tap_count[k];
+        for (int k = 0; k < taps; ++k) info->tap_count[k] = hs.tap_count[k];
     } else {                           // counts from the mask histogram; no lists were written
         for (int k = 0; k < kTaps; ++k) {
             info->tap_count[k] = hs.tap_tot[k];
@@ -651,9 +668,12 @@ int smc_map_export(smc_map* m, int32_t* nbr, uint32_t* mask, int32_t* perm, int3
     SMC_HIP(hipDeviceSynchronize());
     const int64_t n = m->n;
     const MapState& hs = *m->host_state;
+    const int taps = m->ksize * m->ksize * m->ksize;
+    const int mwords = m->ksize == 3 ? 1 : kMaxMaskWords;
     if (n > 0) {
-        if (nbr) SMC_HIP(hipMemcpy(nbr, m->nbr.p, (size_t)n * kTaps * 4, hipMemcpyDeviceToHost));
-        if (mask) SMC_HIP(hipMemcpy(mask, m->mask.p, (size_t)n * 4, hipMemcpyDeviceToHost));
+        if (nbr) SMC_HIP(hipMemcpy(nbr, m->nbr.p, (size_t)n * taps * 4, hipMemcpyDeviceToHost));
+        if (mask)
+            SMC_HIP(hipMemcpy(mask, m->mask.p, (size_t)n * mwords * 4, hipMemcpyDeviceToHost));
         if (perm) {
             // item indices g n + row -> rows, group by group
             const int G = m->sorted_order.n_groups;
@@ -664,7 +684,7 @@ int smc_map_export(smc_map* m, int32_t* nbr, uint32_t* mask, int32_t* perm, int3
     }
     if (tap_off) {
         tap_off[0] = 0;
-        for (int k = 0; k < kTaps; ++k)
+        for (int k = 0; k < taps; ++k)
             tap_off[k + 1] = tap_off[k] + (n == 0 ? 0 : m->has_pairs ? hs.tap_count[k] : hs.tap_tot[k]);
     }
     if ((pair_in || pair_out) && n > 0) {
@@ -674,7 +694,7 @@ int smc_map_export(smc_map* m, int32_t* nbr, uint32_t* mask, int32_t* perm, int3
             if (!dst) continue;
             const int32_t* src = (which == 0 ? m->pair_in : m->pair_out).as<int32_t>();
             int64_t o = 0;
-            for (int k = 0; k < kTaps; ++k) {
+            for (int k = 0; k < taps; ++k) {
                 const int64_t c = hs.tap_count[k];
                 if (c > m->cap) return fail(SMC_ERR_STATE, "tap %d holds %lld pairs", k, (long long)c);
                 if (c > 0)
@@ -687,16 +707,20 @@ int smc_map_export(smc_map* m, int32_t* nbr, uint32_t* mask, int32_t* perm, int3
     return SMC_OK;
 }
 
-size_t smc_weight_packed_bytes(int c_in, int c_out) {
-    if (c_in < 1 || c_out < 1) return 0;
-    return packed_weight_bytes(c_in, c_out);
+size_t smc_weight_packed_bytes(int kernel_size, int c_in, int c_out) {
+    if (c_in < 1 || c_out < 1 || (kernel_size != 3 && kernel_size != 5)) return 0;
+    return packed_weight_bytes(kernel_size * kernel_size * kernel_size, c_in, c_out);
 }
 
-int smc_weight_pack(const uint16_t* w, int c_in, int c_out, void* out, void* stream) {
+int smc_weight_pack(const uint16_t* w, int kernel_size, int c_in, int c_out, void* out,
+                    void* stream) {
     if (!w || !out) return fail(SMC_ERR_ARG, "NULL pointer");
+    if (kernel_size != 3 && kernel_size != 5)
+        return fail(SMC_ERR_UNSUPPORTED, "kernel_size %d (3 or 5)", kernel_size);
     if (c_in < 1 || c_out < 1) return fail(SMC_ERR_ARG, "c_in = %d, c_out = %d", c_in, c_out);
     if (((uintptr_t)out & 15) != 0) return fail(SMC_ERR_ARG, "packed buffer not 16-byte aligned");
-    SMC_HIP(launch_weight_pack(w, c_in, c_out, out, (hipStream_t)stream));
+    SMC_HIP(launch_weight_pack(w, kernel_size * kernel_size * kernel_size, c_in, c_out, out,
+                               (hipStream_t)stream));
     return SMC_OK;
 }
 
@@ -712,6 +736,9 @@ int smc_conv_forward(smc_map* m, const uint16_t* x, int c_in, const void* wpacke
     const bool mask_tiles = (flags & SMC_FWD_MASK_TILES) != 0;
     if (!mask_tiles && !m->has_pairs)
         return fail(SMC_ERR_STATE, "map was built without pair lists (SMC_BUILD_NO_PAIRS)");
+    if (mask_tiles && m->ksize != 3)
+        return fail(SMC_ERR_UNSUPPORTED, "mask tiles need a 3x3x3 map (this one is %d^3)",
+                    m->ksize);
     if (mask_tiles && !m->has_sort)
         return fail(SMC_ERR_STATE, "map was built without the mask order (SMC_BUILD_NO_SORT)");
     if (m->n == 0) return SMC_OK;
@@ -754,8 +781,9 @@ int smc_conv_forward(smc_map* m, const uint16_t* x, int c_in, const void* wpacke
         t_mt.finish();
         return SMC_OK;
     }
-    // slab: 4 c_out bytes per off-centre pair; without the build's counts, 26 pairs a row
-    double slab = (double)(kTaps - 1) * m->n * c_out * 4.0;
+    // slab: 4 c_out bytes per off-centre pair; without the build's counts, taps - 1 a row
+    const int taps = m->ksize * m->ksize * m->ksize;
+    double slab = (double)(taps - 1) * m->n * c_out * 4.0;
     if (m->pending && slab > (double)kSlabBoundBytes) {
         int rc = wait_build(m);
         if (rc) return rc;
@@ -767,12 +795,12 @@ int smc_conv_forward(smc_map* m, const uint16_t* x, int c_in, const void* wpacke
     int rc = m->part.ensure((size_t)slab);
     if (rc) return rc;
     StageTimer t_g(m, SMC_STAGE_GEMM, s);
-    SMC_HIP(launch_gemm_nc(x, c_in, wpacked, c_out, m->pair_in.as<int32_t>(),
+    SMC_HIP(launch_gemm_nc(x, c_in, wpacked, c_out, taps, m->pair_in.as<int32_t>(),
                            m->pair_slot.as<int32_t>(), m->state.as<MapState>() + m->slot, m->cap, m->n,
                            m->n_cu, m->part.as<float>(), s));
     t_g.finish();
     StageTimer t_f(m, SMC_STAGE_CENTRE, s);
-    SMC_HIP(launch_gemm_centre(x, c_in, wpacked, c_out, m->mask.as<uint32_t>(),
+    SMC_HIP(launch_gemm_centre(x, c_in, wpacked, c_out, taps,
                                m->rowbase.as<int32_t>(), m->n, m->part.as<float>(), y,
                                (flags & SMC_FWD_OUT_F32) != 0, (flags & SMC_FWD_RELU) != 0,
                                m->n_cu, s));
@@ -873,6 +901,7 @@ int64_t calib_work(const std::vector<uint32_t>& mask, const int* order, std::vec
 int smc_map_calibrate(smc_map* m, int n_groups, int32_t* bit_order, int32_t* group_of) {
     if (!m || !bit_order || !group_of) return fail(SMC_ERR_ARG, "NULL argument");
     if (!m->built) return fail(SMC_ERR_STATE, "map was never built");
+    if (m->ksize != 3) return fail(SMC_ERR_UNSUPPORTED, "row orders are for 3x3x3 maps");
     if (n_groups < 1 || n_groups > kMaxGroups)
         return fail(SMC_ERR_ARG, "n_groups = %d outside [1, %d]", n_groups, kMaxGroups);
     SMC_HIP(hipSetDevice(m->device));

@@ -47,17 +47,21 @@ def test_static_calls(L):
     assert L.smc_status_string(0) == b"ok"
     assert L.smc_status_string(2) == b"duplicate coordinates"
     assert L.smc_status_string(999) == b"unknown status"
-    # packed weights: 27 taps x ceil(co/16) x ceil(ci/32) x 64 lanes x 16 bytes
-    assert L.smc_weight_packed_bytes(128, 128) == 27 * 8 * 4 * 64 * 16
-    assert L.smc_weight_packed_bytes(1, 1) == 27 * 1 * 1 * 64 * 16
-    assert L.smc_weight_packed_bytes(0, 5) == 0
+    # packed weights: K^3 taps x ceil(co/16) x ceil(ci/32) x 64 lanes x 16 bytes
+    assert L.smc_weight_packed_bytes(3, 128, 128) == 27 * 8 * 4 * 64 * 16
+    assert L.smc_weight_packed_bytes(3, 1, 1) == 27 * 1 * 1 * 64 * 16
+    assert L.smc_weight_packed_bytes(5, 64, 32) == 125 * 2 * 2 * 64 * 16
+    assert L.smc_weight_packed_bytes(3, 0, 5) == 0
+    assert L.smc_weight_packed_bytes(4, 16, 16) == 0
 
 
 def test_argument_errors_without_gpu(L):
     h = ctypes.c_void_p()
     assert L.smc_map_create(ctypes.byref(h)) == 0
-    # kernel_size 5 -> unsupported; ncols 2 -> arg; n < 0 -> arg; no GPU work happens
-    assert L.smc_map_build(h, None, 0, 4, None, 0, 5, 0, 0, None) == 8
+    # kernel_size 4 -> unsupported; 5 without pair lists -> unsupported; ncols 2 -> arg;
+    # n < 0 -> arg; no GPU work happens
+    assert L.smc_map_build(h, None, 0, 4, None, 0, 4, 0, 0, None) == 8
+    assert L.smc_map_build(h, None, 0, 4, None, 0, 5, 0, 2, None) == 8
     assert L.smc_map_build(h, None, 0, 2, None, 0, 3, 0, 0, None) == 1
     assert L.smc_map_build(h, None, -1, 4, None, 0, 3, 0, 0, None) == 1
     assert L.smc_map_build(h, None, 0, 4, None, 0, 3, 7, 0, None) == 1
@@ -67,7 +71,7 @@ def test_argument_errors_without_gpu(L):
     assert L.smc_map_info(h, ctypes.byref(info)) == 7          # never built
     assert L.smc_map_sync(h) == 7
     assert L.smc_conv_forward(h, None, 16, None, 16, None, 0, None) == 7
-    assert L.smc_weight_pack(None, 16, 16, None, None) == 1
+    assert L.smc_weight_pack(None, 3, 16, 16, None, None) == 1
     assert L.smc_map_destroy(h) == 0
     assert L.smc_map_destroy(None) == 0
 
