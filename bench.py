@@ -77,33 +77,37 @@ def dev_bf16(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def stage_model(stage, algo, route, n, p, c_in, c_out):
+def stage_model(stage, algo, route, n, p, c_in, c_out, taps=27):
     """Algorithmic (compulsory) bytes and useful flops of one stage execution.
 
     Each input is counted once and each output once; reads of random grid cells
-    and gathered rows count their payload only.
+    and gathered rows count their payload only. taps: 27 (3x3x3) or 125 (5x5x5);
+    the fused lookup + compaction kernel exists for 27 taps only.
     """
     p_nc = p - n
-    fused = route == "dense" and algo == "pairs"   # lookup runs inside the compaction kernel
+    fused = route == "dense" and algo == "pairs" and taps == 27
+    t4 = 4 * taps                                  # bytes of one neighbour-table row
     if stage == "neighbours":
         if fused:
             # scatter: coords in, grid cell + the row's cell record out; the previous
             # build's cells read and put back (same count, taken as n)
             return 16 * n + 4 * n + 4 * n + 4 * n + 4 * n, 0
+        mw = 4 if taps == 27 else 16              # mask bytes per row
         if route == "dense":
-            # scatter as above; lookup: coords + 27 cells in, nbr + mask out
-            return 16 * n + 16 * n + (16 * n + 108 * n) + (108 * n + 4 * n), 0
-        # sorted: coords -> keys, key sort passes, 9 searches per row (8-byte keys)
-        return 16 * n + 8 * n + 5 * 2 * 12 * n + 9 * 8 * n + 112 * n, 0
+            # scatter as above; lookup: coords + taps cells in, nbr + mask out
+            return 16 * n + 16 * n + (16 * n + t4 * n) + (t4 * n + mw * n), 0
+        # sorted: coords -> keys, key sort passes, K^2 searches per row (8-byte keys)
+        k2 = 9 if taps == 27 else 25
+        return 16 * n + 8 * n + 5 * 2 * 12 * n + k2 * 8 * n + (t4 + mw) * n, 0
     if stage == "mask_sort":
         return 4 * n + 3 * 2 * 8 * n, 0
     if stage == "compact":
         if fused:
             # coords + 27 cells in; nbr, mask, pair lists (in, out, slot), rowbase out
             return 16 * n + 108 * n + 108 * n + 4 * n + 12 * p + 4 * n, 0
-        return 4 * n + 108 * n + 12 * p + 4 * n, 0
+        return (4 if taps == 27 else 16) * n + t4 * n + 12 * p + 4 * n, 0
     if stage == "gemm" and algo == "pairs":
-        return ((2 * c_in + 8 + 4 * c_out) * p_nc + 2 * 26 * c_in * c_out,
+        return ((2 * c_in + 8 + 4 * c_out) * p_nc + 2 * (taps - 1) * c_in * c_out,
                 2.0 * p_nc * c_in * c_out)
     if stage == "gemm":          # mask tiles: x once, all weights, nbr/mask/perm, y once
         return (2 * c_in * n + 2 * 27 * c_in * c_out + 116 * n + 2 * c_out * n,
@@ -167,18 +171,20 @@ def tile_work_ratio(mask, perm, group_rows, group_masks):
 
 
 def run_workload(name, steps, warmup, sync_build=False, algo="pairs", copy_probe_mb=0,
-                 order="plain"):
+                 order="plain", kernel_size=3, frames=1):
     import torch
 
     import submanifold_sparse_convolution_amd as smc
     import synth
 
     w = synth.workload(name)
-    coords = synth.make_coords(w)
+    coords = synth.make_coords(w) if frames == 1 else synth.batched_coords(w, frames)
+    n_rows = len(coords)
+    taps = kernel_size ** 3
     c = w.channels
     coords_d = torch.from_numpy(coords).cuda()
-    x_d = dev_bf16(synth.features(w.n, c, w.seed))
-    w_ds = [dev_bf16(synth.weights(c, c, w.seed, layer)) for layer in range(w.layers)]
+    x_d = dev_bf16(synth.features(n_rows, c, w.seed))
+    w_ds = [dev_bf16(synth.weights(c, c, w.seed, layer, taps)) for layer in range(w.layers)]
     m = smc.KernelMap()
     cal = None
     if algo == "mask_tiles" and order != "plain":
@@ -206,11 +212,11 @@ def run_workload(name, steps, warmup, sync_build=False, algo="pairs", copy_probe
     torch.cuda.synchronize()
     pack_us = ev0.elapsed_time(ev1) * 1e3 / (10 * w.layers)
 
-    ys = [torch.empty((w.n, c), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    ys = [torch.empty((n_rows, c), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
 
     def step():
-        m.build(coords_d, spatial_shape=w.grid, batch_size=1, sync=sync_build,
-                pairs=(algo == "pairs"), sort=(algo == "mask_tiles"))
+        m.build(coords_d, spatial_shape=w.grid, batch_size=frames, sync=sync_build,
+                pairs=(algo == "pairs"), sort=(algo == "mask_tiles"), kernel_size=kernel_size)
         h = x_d
         for layer in range(w.layers):
             h = m.forward(h, packed[layer], relu=layer + 1 < w.layers, out=ys[layer & 1],
@@ -257,7 +263,7 @@ def run_workload(name, steps, warmup, sync_build=False, algo="pairs", copy_probe
     for st in ("neighbours", "mask_sort", "compact", "gemm", "centre"):
         if stage_us.get(st, 0.0) <= 0.0:
             continue
-        by, fl = stage_model(st, algo, info["route"], w.n, pairs, c, c)
+        by, fl = stage_model(st, algo, info["route"], n_rows, pairs, c, c, taps)
         if st == "gemm" and algo == "mask_tiles" and info["n_groups"] > 1:
             # float32 partial sums: written by each early pass and read once after
             by += 8 * c * sum(info["group_rows"][:-1])
@@ -268,7 +274,7 @@ def run_workload(name, steps, warmup, sync_build=False, algo="pairs", copy_probe
                 gpu_ms_per_step=gpu_ms, per_layer_us=per_layer_us, pack_us=pack_us,
                 tflops_effective=flops_layer * w.layers / (wall_ms * 1e-3) / 1e12,
                 stage_us=stage_us, model=model, algo=algo, order=order, calibration=cal,
-                tile_work_ratio=work_ratio)
+                tile_work_ratio=work_ratio, kernel_size=kernel_size, frames=frames, n=n_rows)
 
 
 def source_digest(kernel):
@@ -320,7 +326,9 @@ def roofline(r):
            "peak": PEAK_BF16_TFLOPS if mfma else PEAK_HBM_GBS,
            "unit": "TFLOP/s" if mfma else "GB/s"}
     out["frac"] = round(out["achieved"] / out["peak"], 5)
-    out["traffic"] = traffic_for(r["workload"].name, r["algo"], kernel) if len(kernels) == 1 else None
+    plain = r.get("kernel_size", 3) == 3 and r.get("frames", 1) == 1 and r.get("order") == "plain"
+    out["traffic"] = (traffic_for(r["workload"].name, r["algo"], kernel)
+                      if len(kernels) == 1 and plain else None)
     out["avg_us"] = round(mo["us"], 3)
     out["algorithmic_bytes"] = mo["bytes"]
     out["flops_useful"] = mo["flops"]
@@ -517,17 +525,25 @@ def main():
         line["cpu_baseline"] = cpu_baseline(args.workload)
     if args.report:
         rep = {}
+        runs = []
         for name in ("tiny", "lidar", "deep", "wide", "stage"):
-            for algo, order in [("pairs", "plain")] + [("mask_tiles", o) for o in ORDERS]:
-                rr = run_workload(name, max(20, args.steps // 2), args.warmup, algo=algo,
-                                  order=order)
-                key = f"{name}/{algo}" + ("" if order == "plain" else f"/{order}")
-                rep[key] = {k: rr[k] for k in ("pairs", "ms_per_step", "per_layer_us", "pack_us",
-                                               "tflops_effective", "stage_us", "model",
-                                               "tile_work_ratio", "calibration")}
-                rep[key]["route"] = rr["info"]["route"]
-                rep[key]["n"] = rr["workload"].n
-                rep[key]["roofline"] = roofline(rr)
+            runs += [(name, "pairs", "plain", 3, 1)]
+            runs += [(name, "mask_tiles", o, 3, 1) for o in ORDERS]
+        # 5x5x5 kernels, and several frames as batches of one map
+        runs += [("lidar", "pairs", "plain", 5, 1), ("deep", "pairs", "plain", 5, 1),
+                 ("wide", "pairs", "plain", 5, 1), ("lidar", "pairs", "plain", 3, 4),
+                 ("lidar", "pairs", "plain", 5, 4)]
+        for name, algo, order, ks, frames in runs:
+            rr = run_workload(name, max(20, args.steps // 2), args.warmup, algo=algo,
+                              order=order, kernel_size=ks, frames=frames)
+            key = (f"{name}/{algo}" + ("" if order == "plain" else f"/{order}")
+                   + ("" if ks == 3 else f"/k{ks}") + ("" if frames == 1 else f"/b{frames}"))
+            rep[key] = {k: rr[k] for k in ("pairs", "ms_per_step", "per_layer_us", "pack_us",
+                                           "tflops_effective", "stage_us", "model",
+                                           "tile_work_ratio", "calibration", "kernel_size",
+                                           "frames", "n")}
+            rep[key]["route"] = rr["info"]["route"]
+            rep[key]["roofline"] = roofline(rr)
         with open(args.report, "w") as f:
             json.dump(rep, f, indent=1)
     print(json.dumps(line), flush=True)

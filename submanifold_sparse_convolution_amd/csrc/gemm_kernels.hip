@@ -215,16 +215,30 @@ __global__ __launch_bounds__(kGemmThreads, STREAM ? 1 : 2) void k_gemm_nc(
     __shared__ int32_t s_cnt[kMaxTaps];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
+    __shared__ int32_t s_wave0;
+    static_assert(kMaxTaps <= 128 && kGemmThreads >= 128, "two waves scan the taps");
     const int centre = taps / 2;
-    if (threadIdx.x == 0) {
-        int32_t t = 0;
-        for (int k = 0; k < taps; ++k) {
+    {
+        // per-tap counts read in parallel (one thread per tap), tiles per tap
+        // scanned over the first two waves (taps <= 128)
+        const int k = threadIdx.x;
+        int32_t tiles = 0;
+        if (k < taps) {
             const int32_t c = k == centre ? 0 : st->tap_count[k];
             s_cnt[k] = c;
-            s_first[k] = t;
-            t += (c + kRows - 1) / kRows;
+            tiles = (c + kRows - 1) / kRows;
         }
-        s_first[taps] = t;
+        int32_t inc = tiles;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int32_t t = __shfl_up(inc, o, 64);
+            if (lane >= o) inc += t;
+        }
+        if (k == 63) s_wave0 = inc;
+        __syncthreads();
+        const int32_t ex = inc - tiles + (k >= 64 ? s_wave0 : 0);
+        if (k < taps) s_first[k] = ex;
+        if (k == taps - 1) s_first[taps] = ex + tiles;
     }
     __syncthreads();
     const int n_nc = s_first[taps];

@@ -29,7 +29,7 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "workload", "make_coords", "tiny_coords",
     "ground_box_coords", "bf16_bits_from_f32", "features", "weights",
-    "int_features", "int_weights", "box_coords", "isolated_coords",
+    "int_features", "int_weights", "box_coords", "isolated_coords", "batched_coords",
 ]
 
 
@@ -197,11 +197,24 @@ def features(n: int, c: int, seed: int) -> np.ndarray:
     return bf16_bits_from_f32(rng.standard_normal((n, c), dtype=np.float32))
 
 
-def weights(c_in: int, c_out: int, seed: int, layer: int = 0) -> np.ndarray:
-    """bf16 bits of N(0, 1) / sqrt(27 c_in) draws, shape [27, c_in, c_out]."""
+def weights(c_in: int, c_out: int, seed: int, layer: int = 0, taps: int = 27) -> np.ndarray:
+    """bf16 bits of N(0, 1) / sqrt(taps c_in) draws, shape [taps, c_in, c_out]
+    (27 taps for a 3x3x3 kernel, 125 for 5x5x5)."""
     rng = np.random.default_rng(seed + 2000 + layer)
-    w = rng.standard_normal((27, c_in, c_out), dtype=np.float32)
-    return bf16_bits_from_f32(w / np.float32(np.sqrt(27.0 * c_in)))
+    w = rng.standard_normal((taps, c_in, c_out), dtype=np.float32)
+    return bf16_bits_from_f32(w / np.float32(np.sqrt(float(taps) * c_in)))
+
+
+def batched_coords(w: "Workload", frames: int) -> np.ndarray:
+    """``frames`` independent voxel sets of workload w (seeds seed, seed + 1,
+    ...), stacked as batches b = 0 .. frames - 1 and shuffled together."""
+    parts = []
+    for b in range(frames):
+        c = make_coords(Workload(w.name, w.n, w.grid, w.channels, w.seed + b, w.layers, w.kind))
+        c[:, 0] = b
+        parts.append(c)
+    out = np.concatenate(parts)
+    return out[np.random.default_rng(w.seed + 7000).permutation(len(out))]
 
 
 def int_features(n: int, c: int, seed: int, lo: int = -3, hi: int = 3) -> np.ndarray:
