@@ -64,7 +64,8 @@ STAGE_KERNELS_FUSED = {
 MASK_TILE_GEMM = ("k_conv_masktile",)
 KERNEL_SOURCES = {
     "k_compact": "compact_kernels.hip", "k_mask_hist": "compact_kernels.hip",
-    "k_lookup_compact": "compact_kernels.hip",
+    "k_lookup_compact": "compact_kernels.hip", "k_compact5": "compact_kernels.hip",
+    "k_dense_lookup5": "map_kernels.hip",
     "k_gemm_nc": "gemm_kernels.hip", "k_gemm_centre": "gemm_kernels.hip",
     "k_conv_masktile": "masktile_kernels.hip", "k_dense_scatter": "map_kernels.hip",
     "k_dense_lookup": "map_kernels.hip", "k_os_pass": "radix_sort.hip",
@@ -304,6 +305,24 @@ def traffic_for(workload, algo, kernel):
     return round(k["bytes_per_launch"])
 
 
+def stage_kernels(stage, algo, route, kernel_size=3):
+    """The kernels one execution of a stage launches."""
+    if stage == "gemm" and algo == "mask_tiles":
+        return MASK_TILE_GEMM
+    fused = route == "dense" and algo == "pairs" and kernel_size == 3
+    if stage == "neighbours":
+        if route == "sorted":
+            return ("k_make_keys", "k_key_hist", "k_os_pass", "k_sorted_lookup")
+        if fused:
+            return ("k_dense_scatter",)
+        return ("k_dense_scatter", "k_dense_lookup5" if kernel_size == 5 else "k_dense_lookup")
+    if stage == "compact":
+        if fused:
+            return ("k_lookup_compact",)
+        return ("k_compact5",) if kernel_size == 5 else ("k_compact",)
+    return STAGE_KERNELS[stage]
+
+
 def roofline(r):
     """The dominant stage (largest kernel time) and its roofline."""
     model = r["model"]
@@ -311,12 +330,7 @@ def roofline(r):
         return None
     st = max(model, key=lambda s: model[s]["us"])
     mo = model[st]
-    if st == "gemm" and r["algo"] == "mask_tiles":
-        kernels = MASK_TILE_GEMM
-    elif r["info"]["route"] == "dense" and r["algo"] == "pairs" and st in STAGE_KERNELS_FUSED:
-        kernels = STAGE_KERNELS_FUSED[st]
-    else:
-        kernels = STAGE_KERNELS[st]
+    kernels = stage_kernels(st, r["algo"], r["info"]["route"], r.get("kernel_size", 3))
     kernel = kernels[0] if len(kernels) == 1 else "+".join(kernels)
     intensity = mo["flops"] / mo["bytes"] if mo["bytes"] else 0.0
     mfma = intensity > RIDGE
