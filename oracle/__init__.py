@@ -5,4 +5,5 @@ from .smconv_oracle import (TAPS, CENTRE, DuplicateCoordinate, tap_offsets,  # n
                             bf16_bits_to_f64, round_to_bf16, bf16_bits,
                             build_kernel_map, mask_sort, compact_pairs,
                             group_row_orders, tile_work, calibrate_order,
+                            strided_out_shape, build_strided_map, strided_conv,
                             conv_accumulate, conv_rows, subm_conv, stage)

@@ -37,6 +37,8 @@ Readings fixed here where the pages are silent:
 * calibrated bit order and offset groups: see ``group_row_orders`` and
   ``calibrate_order`` (a greedy search; the pages do not say how the order
   or the groups are chosen).
+* strided layer: stride 2, padding (K-1)/2, outputs ordered by (b, x, y, z);
+  see ``build_strided_map``.
 * pair lists: tap-major, and within a tap in ascending output row (the
   order inside a tap does not change the sum; [P1]'s compaction lists each
   tap's rows in the order it scans them).
@@ -343,6 +345,99 @@ def compact_pairs(nbr: np.ndarray, mask: np.ndarray):
     return (np.concatenate(ins) if ins else np.zeros(0, np.int32),
             np.concatenate(outs) if outs else np.zeros(0, np.int32),
             np.asarray(off, dtype=np.int64))
+
+
+# --------------------------------------------------------------------------
+# strided (downsampling) convolution ([P5] "Calibrated bit order": the
+# strided kernels change the coordinate set; "One kernel family, configured
+# per stage": conv1 to conv4 of the backbone)
+# --------------------------------------------------------------------------
+
+def strided_out_shape(spatial_shape, kernel_size: int = 3, stride: int = 2, padding=None):
+    """Output grid extent per axis: floor((X + 2p - K) / s) + 1 (p = (K-1)/2 by default)."""
+    if padding is None:
+        padding = (kernel_size - 1) // 2
+    return tuple((int(e) + 2 * padding - kernel_size) // stride + 1 for e in spatial_shape)
+
+
+def build_strided_map(coords, spatial_shape, kernel_size: int = 3, stride: int = 2,
+                      padding=None):
+    """Output cells and kernel map of a strided sparse convolution.
+
+    The pages do not define the strided layer beyond its changing the
+    coordinate set. Reading fixed here (the usual downsampling layer): output
+    cell o of a batch exists when some active input c of that batch equals
+    s o - p + d for a tap d in [0, K)^3, with o inside the output grid
+    (``strided_out_shape``); output rows are ordered by (b, x, y, z). Tap k =
+    K^2 dx + K dy + dz, the submanifold numbering with offsets shifted by r;
+    nbr[o, k] is the row of input s o - p + d_k, or -1; bit k of mask[o] is set
+    when it exists. Input coordinates must lie in [0, spatial_shape).
+
+    The default padding is p = (K - 1) / 2 (1 for K = 3, 2 for K = 5), so the
+    taps of output o are the cells s o + d' with d' in [-r, r]^3.
+
+    Returns (out_coords int32 [M, 4], out_shape, nbr int32 [M, K^3],
+    mask uint32 [M] (K = 3) or [M, 4] words (K = 5)).
+    """
+    kv = taps_of(kernel_size)
+    if padding is None:
+        padding = (kernel_size - 1) // 2
+    c = _rows_bxyz(coords)
+    shape = tuple(int(e) for e in spatial_shape)
+    oshape = strided_out_shape(shape, kernel_size, stride, padding)
+    table = {}
+    for i in range(c.shape[0]):
+        key = tuple(c[i].tolist())
+        if key in table:
+            raise DuplicateCoordinate(f"rows {table[key]} and {i} share {key}")
+        if any(not 0 <= key[1 + a] < shape[a] for a in range(3)) or key[0] < 0:
+            raise ValueError(f"row {i} = {key} outside the grid {shape}")
+        table[key] = i
+    taps = [(dx, dy, dz) for dx in range(kernel_size) for dy in range(kernel_size)
+            for dz in range(kernel_size)]
+    outs = set()
+    for (b, x, y, z) in table:
+        for d in taps:
+            t = (x + padding - d[0], y + padding - d[1], z + padding - d[2])
+            if all(v % stride == 0 and 0 <= v // stride < oshape[a] for a, v in enumerate(t)):
+                outs.add((b, t[0] // stride, t[1] // stride, t[2] // stride))
+    out = sorted(outs)
+    m = len(out)
+    nbr = np.full((m, kv), -1, dtype=np.int32)
+    words = (kv + 31) // 32
+    mask = np.zeros((m, words), dtype=np.uint32)
+    for o, (b, ox, oy, oz) in enumerate(out):
+        bits = 0
+        for k, d in enumerate(taps):
+            j = table.get((b, stride * ox - padding + d[0], stride * oy - padding + d[1],
+                           stride * oz - padding + d[2]))
+            if j is not None:
+                nbr[o, k] = j
+                bits |= 1 << k
+        for q in range(words):
+            mask[o, q] = (bits >> (32 * q)) & 0xFFFFFFFF
+    oc = np.asarray(out, dtype=np.int32).reshape(m, 4)
+    return oc, oshape, nbr, (mask[:, 0].copy() if kernel_size == 3 else mask)
+
+
+def strided_conv(coords, spatial_shape, x_bits, w_bits, relu: bool = False,
+                 acc_dtype=np.float64):
+    """One strided layer: Y[o] = sum over taps k with nbr[o, k] >= 0 of
+    X[nbr[o, k]] @ W[k] (the same per-tap accumulation as the submanifold
+    layer, over the strided map). Returns a dict with the map, the
+    accumulator and the bf16 output (ReLU after rounding when ``relu``)."""
+    k_size = {27: 3, 125: 5}[np.asarray(w_bits).shape[0]]
+    oc, oshape, nbr, mask = build_strided_map(coords, spatial_shape, k_size)
+    pin, pout, toff = compact_pairs(nbr, mask)
+    x = bf16_bits_to_f64(x_bits)
+    w = bf16_bits_to_f64(w_bits)
+    acc = conv_accumulate(x, w, pin, pout, toff, oc.shape[0], acc_dtype)
+    y = round_to_bf16(acc)
+    if relu:
+        y = np.maximum(y, 0.0)
+    return dict(out_coords=oc, out_shape=oshape, nbr=nbr, mask=mask,
+                perm=mask_sort(mask) if k_size == 3 else None, pair_in=pin, pair_out=pout,
+                tap_off=toff, acc=acc, y=y, y_bits=bf16_bits(y))
 
 
 # --------------------------------------------------------------------------

@@ -283,6 +283,66 @@ def check_calibration(mask, n_groups, tile=64):
     return order, group_of
 
 
+def brute_force_strided(coords, shape, K=3, s=2, p=None):
+    """Output set and (tap, in_row, out_index) triples by scanning every cell of
+    the output grid against every input (no divisibility arithmetic)."""
+    p = (K - 1) // 2 if p is None else p
+    c = so._rows_bxyz(coords)
+    oshape = [(e + 2 * p - K) // s + 1 for e in shape]
+    tap_of = np.arange(K ** 3).reshape(K, K, K)
+    out, triples = [], set()
+    for b in sorted(set(c[:, 0].tolist())):
+        cb = np.nonzero(c[:, 0] == b)[0]
+        for ox, oy, oz in np.ndindex(*oshape):
+            base = np.array([s * ox - p, s * oy - p, s * oz - p])
+            d = c[cb, 1:] - base
+            hit = ((d >= 0) & (d < K)).all(axis=1)
+            if hit.any():
+                out.append((b, ox, oy, oz))
+                for r, dd in zip(cb[hit], d[hit]):
+                    triples.add((int(tap_of[dd[0], dd[1], dd[2]]), int(r), len(out) - 1))
+    return out, triples
+
+
+def check_strided_map(coords, shape, K=3):
+    oc, oshape, nbr, mask = so.build_strided_map(coords, shape, K)
+    assert list(oshape) == [(e + 2 * ((K - 1) // 2) - K) // 2 + 1 for e in shape]
+    out, triples = brute_force_strided(coords, shape, K)
+    assert [tuple(r) for r in oc.tolist()] == out, "output cells or their order differ"
+    got = {(int(k), int(nbr[o, k]), int(o)) for o, k in zip(*np.nonzero(nbr >= 0))}
+    assert got == triples, "strided map differs from brute force"
+    ms = mask_ints(mask)
+    assert all(bin(ms[o]).count("1") == int((nbr[o] >= 0).sum()) for o in range(len(oc)))
+    assert all(m != 0 for m in ms), "every output has an input"
+
+
+def check_strided_vs_dense(coords, shape, xb, wb, exact=False):
+    """torch conv3d with stride 2, padding 1 (a cross-correlation, float64): the
+    output set is where the all-ones kernel sees an input; values match there."""
+    r = so.strided_conv(coords, shape, xb, wb)
+    K = round(wb.shape[0] ** (1 / 3))
+    x = so.bf16_bits_to_f64(xb)
+    w = so.bf16_bits_to_f64(wb)
+    c = np.asarray(coords)
+    occ = np.zeros(tuple(shape), np.float64)
+    occ[c[:, 1], c[:, 2], c[:, 3]] = 1.0
+    cnt = torch.nn.functional.conv3d(torch.from_numpy(occ)[None, None],
+                                     torch.ones((1, 1, K, K, K), dtype=torch.float64),
+                                     stride=2, padding=(K - 1) // 2)[0, 0].numpy()
+    want_cells = [tuple(v) for v in np.argwhere(cnt > 0).tolist()]
+    assert [tuple(v) for v in r["out_coords"][:, 1:].tolist()] == want_cells, "output set"
+    g = torch.from_numpy(dense_grid(c, x, shape)).permute(3, 0, 1, 2)[None]
+    w5 = torch.from_numpy(w.reshape(K, K, K, w.shape[1], w.shape[2]))
+    wt = w5.permute(4, 3, 0, 1, 2).contiguous()
+    dense = torch.nn.functional.conv3d(g, wt, stride=2, padding=(K - 1) // 2)[0].permute(1, 2, 3, 0)
+    oc = r["out_coords"]
+    ref = dense.numpy()[oc[:, 1], oc[:, 2], oc[:, 3]]
+    if exact:
+        assert np.array_equal(r["acc"], ref), "strided accumulator != conv3d"
+    else:
+        assert np.max(np.abs(r["acc"] - ref) / (1 + np.abs(ref))) < 1e-12, "strided vs conv3d"
+
+
 def check_bf16_vs_torch(vals):
     vals = np.asarray(vals, np.float32)
     want = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
@@ -440,6 +500,58 @@ def test_k5_isolated_and_k3_is_a_subset():
     off5 = {o: k for k, o in enumerate(so.tap_offsets(5))}
     for k3, o in enumerate(so.tap_offsets(3)):
         assert np.array_equal(n3[:, k3], n5[:, off5[o]]), o
+
+
+# --- strided (downsampling) layer ----------------------------------------
+
+@pytest.mark.parametrize("shape,n,seed", [((8, 8, 8), 150, 1), ((9, 7, 5), 120, 2),
+                                          ((1, 6, 11), 30, 3), ((12, 12, 12), 600, 4)])
+def test_strided_map_vs_bruteforce(shape, n, seed):
+    rng = np.random.default_rng(seed)
+    cells = rng.choice(int(np.prod(shape)), size=n, replace=False)
+    xyz = np.stack(np.unravel_index(cells, shape), axis=1)
+    coords = np.concatenate([np.zeros((n, 1), np.int64), xyz], axis=1).astype(np.int32)
+    check_strided_map(coords, shape)
+
+
+def test_strided_map_two_batches_k5():
+    a = synth.tiny_coords(seed=5, n=120, side=8)
+    b = synth.tiny_coords(seed=6, n=90, side=8)
+    b[:, 0] = 1
+    check_strided_map(np.concatenate([b, a]), (8, 8, 8))
+    check_strided_map(synth.tiny_coords(seed=7, n=100, side=9), (9, 9, 9), K=5)
+
+
+def test_strided_conv_vs_dense_conv3d():
+    coords = synth.tiny_coords(seed=8, n=200, side=10)
+    check_strided_vs_dense(coords, (10, 10, 10), synth.features(200, 5, 8),
+                           synth.weights(5, 4, 8))
+    check_strided_vs_dense(coords, (10, 10, 10), synth.int_features(200, 6, 8),
+                           synth.int_weights(6, 3, 8), exact=True)
+    check_strided_vs_dense(coords[:70], (10, 10, 10), synth.int_features(70, 3, 9),
+                           synth.bf16_bits_from_f32(np.random.default_rng(2).integers(
+                               -2, 3, (125, 3, 2)).astype(np.float32)), exact=True)
+
+
+def test_strided_special_cases():
+    # a full 4^3 box: every output of the 2^3 output grid exists, each sees 27 (or
+    # fewer at the low faces) inputs; a single voxel at an even cell has one output
+    box = synth.box_coords(4, 4, 4, seed=1)
+    oc, oshape, nbr, _ = so.build_strided_map(box, (4, 4, 4))
+    assert oshape == (2, 2, 2) and len(oc) == 8
+    per_axis = {0: 2, 1: 3}                      # inputs at 2o-1..2o+1 inside [0, 4)
+    for o, (_, x, y, z) in enumerate(oc.tolist()):
+        assert (nbr[o] >= 0).sum() == per_axis[x] * per_axis[y] * per_axis[z]
+    one = np.array([[0, 4, 6, 2]], np.int32)
+    oc, _, nbr, _ = so.build_strided_map(one, (8, 8, 8))
+    assert oc.tolist() == [[0, 2, 3, 1]] and nbr[0, 13] == 0 and (nbr >= 0).sum() == 1
+    odd = np.array([[0, 3, 3, 3]], np.int32)     # an odd cell feeds 8 outputs
+    oc, _, nbr, _ = so.build_strided_map(odd, (8, 8, 8))
+    assert len(oc) == 8 and (nbr >= 0).sum() == 8
+    with pytest.raises(ValueError):
+        so.build_strided_map(np.array([[0, 8, 0, 0]], np.int32), (8, 8, 8))
+    oc, _, nbr, _ = so.build_strided_map(np.zeros((0, 4), np.int32), (8, 8, 8))
+    assert oc.shape == (0, 4) and nbr.shape == (0, 27)
 
 
 def test_bf16_rounding_matches_torch():
@@ -760,3 +872,25 @@ def test_planted_k5_offsets_clipped_to_one(monkeypatch):
     coords = synth.tiny_coords(seed=0, n=200, side=8)
     assert _fails(check_map_vs_bruteforce, coords, 5)
     assert _fails(check_full_box, 3, 4, 5, 5)
+
+
+def test_planted_strided_padding_sign(monkeypatch):
+    orig = so.build_strided_map
+
+    def broken(coords, shape, kernel_size=3, stride=2, padding=None):
+        return orig(coords, shape, kernel_size, stride, -(kernel_size - 1) // 2)
+    monkeypatch.setattr(so, "build_strided_map", broken)
+    coords = synth.tiny_coords(seed=8, n=120, side=8)
+    assert _fails(check_strided_map, coords, (8, 8, 8))
+    assert _fails(check_strided_vs_dense, coords, (8, 8, 8), synth.int_features(120, 3, 1),
+                  synth.int_weights(3, 2, 1), True)
+
+
+def test_planted_strided_unsorted_outputs(monkeypatch):
+    orig = so.build_strided_map
+
+    def broken(coords, shape, kernel_size=3, stride=2, padding=None):
+        oc, osh, nbr, mask = orig(coords, shape, kernel_size, stride, padding)
+        return oc[::-1].copy(), osh, nbr[::-1].copy(), mask[::-1].copy()
+    monkeypatch.setattr(so, "build_strided_map", broken)
+    assert _fails(check_strided_map, synth.tiny_coords(seed=9, n=100, side=8), (8, 8, 8))
