@@ -105,6 +105,9 @@ typedef struct smc_map_info_s {
     int64_t group_rows[4];  /* rows with a tap of each group (the last group: every row) */
     int32_t kernel_size;    /* K: 3 or 5 */
     int32_t taps;           /* K^3: 27 or 125 */
+    int64_t n_in;           /* input rows (= n except for a strided map) */
+    int32_t strided;        /* 1 for a map from smc_map_build_strided */
+    int32_t out_extent[3];  /* output grid extent (strided: floor((X + 2 - 3) / 2) + 1) */
 } smc_map_info_t;
 
 /* Create an empty map handle. *out receives it. No device memory is taken yet. */
@@ -158,6 +161,36 @@ int smc_map_destroy(smc_map* map);
 int smc_map_build(smc_map* map, const int32_t* coords, int64_t n, int ncols,
                   const int32_t* spatial_shape, int batch_size, int kernel_size,
                   int route, unsigned flags, void* stream);
+
+/*
+ * Strided (downsampling) map: kernel 3, stride 2, padding 1 ("Sparse
+ * convolution in FP32" (DriveRT), section "Calibrated bit order": the
+ * strided layers change the coordinate set and run as mask-sorted tiles).
+ * Output cell o (per batch) exists when an input c = 2 o - 1 + d, d in
+ * [0, 3)^3, is active; its 27 taps are the cells 2 o + d' (d' in [-1, 1]^3,
+ * the submanifold tap numbering), so nbr[o][k] is the input row at
+ * 2 o + d_k or -1. Output rows are ordered by (b, x, y, z); their
+ * coordinates come from smc_map_export_out_coords. The map then carries the
+ * plain mask order over its output rows and no pair lists, and
+ * smc_conv_forward runs the mask-tile algorithm on it (x: n_in input rows,
+ * y: n output rows).
+ * Arguments as smc_map_build; coordinates count from 0: with spatial_shape
+ * NULL the grid is [0, max + 1) per axis, and a negative coordinate is
+ * SMC_ERR_RANGE. kernel_size must be 3 and stride 2 (else
+ * SMC_ERR_UNSUPPORTED); n <= 2^24. The output count is read back to the host
+ * once inside the call (the caller needs it to size y); with SMC_BUILD_ASYNC
+ * the lookups and the mask sort that follow are still only enqueued.
+ * Steps: the input grid or sorted input keys as for smc_map_build; every
+ * input's (at most 8) output cells as packed keys; one radix sort; unique
+ * (count, scan, write); the 27-tap lookup around each query point; mask sort.
+ */
+int smc_map_build_strided(smc_map* map, const int32_t* coords, int64_t n, int ncols,
+                          const int32_t* spatial_shape, int batch_size, int kernel_size,
+                          int stride, int route, unsigned flags, void* stream);
+
+/* Output coordinates of a strided map: host int32 [n, 4] rows (b, x, y, z) in
+ * output-grid cells, in output-row order. SMC_ERR_STATE for other maps. */
+int smc_map_export_out_coords(smc_map* map, int32_t* out_coords);
 
 /* Wait for the map's last build and return the status of its device-side
  * checks (SMC_OK, SMC_ERR_DUPLICATE, SMC_ERR_RANGE). */

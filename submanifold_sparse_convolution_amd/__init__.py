@@ -35,7 +35,8 @@ EXPORTED_SYMBOLS = [
     "smc_map_create", "smc_map_destroy", "smc_map_build", "smc_map_sync", "smc_map_info",
     "smc_map_export", "smc_weight_packed_bytes", "smc_weight_pack", "smc_conv_forward",
     "smc_status_string", "smc_last_error", "smc_version", "smc_timing_enable", "smc_timing_read",
-    "smc_map_set_order", "smc_map_calibrate",
+    "smc_map_set_order", "smc_map_calibrate", "smc_map_build_strided",
+    "smc_map_export_out_coords",
 ]
 STAGES = ["map", "neighbours", "mask_sort", "compact", "gemm", "centre"]
 
@@ -55,6 +56,7 @@ class MapInfo(ctypes.Structure):
         ("tap_count", ctypes.c_int64 * 125), ("status", ctypes.c_int32),
         ("n_groups", ctypes.c_int32), ("group_rows", ctypes.c_int64 * 4),
         ("kernel_size", ctypes.c_int32), ("taps", ctypes.c_int32),
+        ("n_in", ctypes.c_int64), ("strided", ctypes.c_int32), ("out_extent", ctypes.c_int32 * 3),
     ]
 
 
@@ -99,10 +101,12 @@ def lib():
     L.smc_timing_read.argtypes = [vp, vp, vp, i32]
     L.smc_map_set_order.argtypes = [vp, vp, vp]
     L.smc_map_calibrate.argtypes = [vp, i32, vp, vp]
+    L.smc_map_build_strided.argtypes = [vp, vp, i64, i32, vp, i32, i32, i32, i32, u32, vp]
+    L.smc_map_export_out_coords.argtypes = [vp, vp]
     for name in ("smc_map_create", "smc_map_destroy", "smc_map_build", "smc_map_sync",
                  "smc_map_info", "smc_map_export", "smc_weight_pack", "smc_conv_forward",
                  "smc_timing_enable", "smc_timing_read", "smc_map_set_order",
-                 "smc_map_calibrate"):
+                 "smc_map_calibrate", "smc_map_build_strided", "smc_map_export_out_coords"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -173,7 +177,9 @@ class KernelMap:
         self._h = ctypes.c_void_p()
         _check(lib().smc_map_create(ctypes.byref(self._h)))
         self.n = 0
+        self.n_in = 0
         self.kernel_size = 3
+        self.strided = False
         self._coords = None
 
     def close(self):
@@ -207,12 +213,42 @@ class KernelMap:
         if kernel_size == 5:
             flags |= SMC_BUILD_NO_SORT
         self._coords = coords          # keep alive while the stream reads it
-        self.n = n
+        self.n = self.n_in = n
+        self.strided = False
         _check(lib().smc_map_build(self._h, ctypes.c_void_p(coords.data_ptr() if n else 0), n,
                                    ncols, shape, int(batch_size), int(kernel_size), ROUTES[route],
                                    flags, _stream(stream)))
         self.kernel_size = int(kernel_size)
         return self
+
+    def build_strided(self, coords, spatial_shape=None, batch_size: int = 0, route: str = "auto",
+                      sync: bool = True, kernel_size: int = 3, stride: int = 2,
+                      stream=None) -> "KernelMap":
+        """Downsampling map (kernel 3, stride 2, padding 1) of int32 [N, 4] / [N, 3]
+        CUDA coordinates; outputs are new cells (``out_coords()``), ``n`` of them."""
+        import torch
+        _need(coords, torch.int32, "coords", 2)
+        n, ncols = int(coords.shape[0]), int(coords.shape[1])
+        shape = None
+        if spatial_shape is not None:
+            shape = (ctypes.c_int32 * 3)(*[int(v) for v in spatial_shape])
+        self._coords = coords
+        self.n, self.n_in, self.strided = 0, n, True
+        _check(lib().smc_map_build_strided(
+            self._h, ctypes.c_void_p(coords.data_ptr() if n else 0), n, ncols, shape,
+            int(batch_size), int(kernel_size), int(stride), ROUTES[route],
+            0 if sync else SMC_BUILD_ASYNC, _stream(stream)))
+        info = self.info()
+        self.n, self.n_in, self.kernel_size, self.strided = info["n"], n, int(kernel_size), True
+        return self
+
+    def out_coords(self):
+        """Output coordinates of a strided map: numpy int32 [n, 4] (b, x, y, z)."""
+        import numpy as np
+        out = np.empty((self.n, 4), np.int32)
+        _check(lib().smc_map_export_out_coords(
+            self._h, ctypes.c_void_p(out.ctypes.data) if out.size else None))
+        return out
 
     def sync(self):
         _check(lib().smc_map_sync(self._h))
@@ -257,7 +293,8 @@ class KernelMap:
                     pairs_padded=inf.pairs_padded, n_tiles=inf.n_tiles,
                     tap_count=list(inf.tap_count)[:inf.taps], status=inf.status,
                     n_groups=inf.n_groups, group_rows=list(inf.group_rows)[:inf.n_groups],
-                    kernel_size=inf.kernel_size, taps=inf.taps)
+                    kernel_size=inf.kernel_size, taps=inf.taps, n_in=inf.n_in,
+                    strided=bool(inf.strided), out_extent=tuple(inf.out_extent))
 
     def export(self, pairs: bool = True, perm: bool = True) -> dict:
         """Copy nbr, mask, tap offsets (and the mask-tile row orders [G, N], the
@@ -293,8 +330,8 @@ class KernelMap:
             raise ValueError(f"algo must be one of {ALGOS}")
         import torch
         _need(x, torch.bfloat16, "x", 2)
-        if x.shape[0] != self.n:
-            raise ValueError(f"x has {x.shape[0]} rows, the map has {self.n}")
+        if x.shape[0] != self.n_in:
+            raise ValueError(f"x has {x.shape[0]} rows, the map has {self.n_in} inputs")
         if x.shape[1] != w.c_in:
             raise ValueError(f"x has {x.shape[1]} channels, weights expect {w.c_in}")
         if w.kernel_size != self.kernel_size:

@@ -145,8 +145,8 @@ template <int NBW, int NBH, bool OUT_F32, bool VEC, bool CF>
 __device__ __forceinline__ void heavy_tile(
     const uint16_t* __restrict__ x, int c_in, int steps, const u32x4* __restrict__ wp, int n_wt,
     int c_out, const int32_t* __restrict__ nbr, const uint32_t* __restrict__ mask,
-    const PassArgs& pa, int64_t n, const uint16_t* __restrict__ zrow, void* __restrict__ yv,
-    int relu, uint32_t rest, int z, float* s_part, int32_t* s_nb) {
+    const PassArgs& pa, int64_t n, int64_t n_in, const uint16_t* __restrict__ zrow,
+    void* __restrict__ yv, int relu, uint32_t rest, int z, float* s_part, int32_t* s_nb) {
     constexpr int kWh = 16 * NBH;                     // columns of the slice
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
@@ -189,8 +189,8 @@ __device__ __forceinline__ void heavy_tile(
         const u32x4* bsrc_ = wbase + (int64_t)tap_ * n_wt * n16 + (int64_t)st_ * NBW * 64;        \
         _Pragma("unroll") for (int nb_ = 0; nb_ < NBH; ++nb_) B[nb_] = bsrc_[nb_ * 64];         \
         _Pragma("unroll") for (int f_ = 0; f_ < 4; ++f_) {                                        \
-            const int id_ = tap_ == kCentre ? (int)rowf[f_] : s_nb[(f_ * 16 + r) * kTaps + tap_]; \
-            const uint16_t* xr_ = id_ >= 0 && id_ < n ? x + (int64_t)id_ * c_in : zrow;          \
+            const int id_ = CF && tap_ == kCentre ? (int)rowf[f_] : s_nb[(f_ * 16 + r) * kTaps + tap_]; \
+            const uint16_t* xr_ = id_ >= 0 && id_ < n_in ? x + (int64_t)id_ * c_in : zrow;       \
             A[f_] = load_a4<VEC>(xr_, st_ * 32 + g * 8, c_in);                                    \
         }                                                                                         \
     }
@@ -255,7 +255,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_conv_masktile(
     const uint16_t* __restrict__ x, int c_in, int steps, const u32x4* __restrict__ wp, int n_wt,
     int c_out, const int32_t* __restrict__ nbr, const uint32_t* __restrict__ mask,
     const uint32_t* __restrict__ perm, int64_t goff, const int32_t* __restrict__ rows,
-    uint32_t gm, uint32_t prev, int last, float* __restrict__ partial, int64_t n,
+    uint32_t gm, uint32_t prev, int last, float* __restrict__ partial, int64_t n, int64_t n_in,
     const uint16_t* __restrict__ zrow, void* __restrict__ yv, int relu, int max_items) {
     constexpr int kBuf = kChunkSteps * NBW * 64;    // 16-byte words per staged chunk
     constexpr int kPer = kChunkSteps * NBW / 4;     // words per thread
@@ -327,10 +327,10 @@ __global__ __launch_bounds__(kGemmThreads) void k_conv_masktile(
         }
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1) m |= __shfl_xor(m, o, 16);
-        const uint32_t rest = m & ~(1u << kCentre);
+        const uint32_t rest = CF ? m & ~(1u << kCentre) : m;
         if (((CF ? 1 : 0) + __builtin_popcount(rest)) * n_chunks <= max_items) return;
         heavy_tile<NBW, NBH, OUT_F32, VEC, CF>(x, c_in, steps, wp, n_wt, c_out, nbr, mask, pa, n,
-                                               zrow, yv, relu, rest, blockIdx.z,
+                                               n_in, zrow, yv, relu, rest, blockIdx.z,
                                                reinterpret_cast<float*>(s_b), s_nb);
         return;
     }
@@ -361,12 +361,14 @@ __global__ __launch_bounds__(kGemmThreads) void k_conv_masktile(
     uint32_t u = 0;
 #pragma unroll
     for (int v = 0; v < kGemmThreads / 64; ++v) u |= s_u[v];
-    const uint32_t rest = u & ~(1u << kCentre);
+    // without CF (a group without the centre, or a strided map whose centre tap
+    // is an ordinary gathered input) every tap of the union is read through s_nb
+    const uint32_t rest = CF ? u & ~(1u << kCentre) : u;
     const int n_items = ((CF ? 1 : 0) + __builtin_popcount(rest)) * n_chunks;
     const int last_item = n_items - 1;
     if (n_items > max_items) {                        // heavy tile: column slice 0
         heavy_tile<NBW, NBH, OUT_F32, VEC, CF>(x, c_in, steps, wp, n_wt, c_out, nbr, mask, pa, n,
-                                               zrow, yv, relu, rest, 0,
+                                               n_in, zrow, yv, relu, rest, 0,
                                                reinterpret_cast<float*>(s_b), s_nb);
         return;
     }
@@ -375,8 +377,8 @@ __global__ __launch_bounds__(kGemmThreads) void k_conv_masktile(
 #define SMC_XROW(J)                                                                               \
     ({                                                                                            \
         const int kk_ = item_tap<CF>(J, n_chunks, rest);                                          \
-        const int nb_ = kk_ == kCentre ? (int)row_a : s_nb[my_nb * kTaps + kk_];                  \
-        nb_ >= 0 && nb_ < n ? x + (int64_t)nb_ * c_in : zrow;                                     \
+        const int nb_ = CF && kk_ == kCentre ? (int)row_a : s_nb[my_nb * kTaps + kk_];            \
+        nb_ >= 0 && nb_ < n_in ? x + (int64_t)nb_ * c_in : zrow;                                  \
     })
     if (!CF) {                                        // item 0 now that the union is known
         SMC_FETCH_B(bA, item_tap<CF>(0, n_chunks, rest), 0)
@@ -465,7 +467,7 @@ hipError_t launch_mt(dim3 grid, hipStream_t s, const uint16_t* x, int c_in, int 
     grid.z = NBW / nbh_for(NBW);
     launch(k_conv_masktile<NBW, OUT_F32, VEC, CF>, grid, kGemmThreads, lds, s, x, c_in, steps, wp,
            n_wt, c_out, nbr, mask, gp.perm, gp.goff, gp.rows, gp.gm, gp.prev, gp.last ? 1 : 0,
-           gp.partial, n, zrow, y, relu, kMaxLightItems);
+           gp.partial, n, gp.n_in > 0 ? gp.n_in : n, zrow, y, relu, kMaxLightItems);
     return hipGetLastError();
 }
 
@@ -475,7 +477,7 @@ hipError_t launch_mt_v(dim3 grid, hipStream_t s, const uint16_t* x, int c_in, in
                        const uint32_t* mask, const GroupPass& gp, int64_t n, const uint16_t* zrow,
                        void* y, int relu) {
     const bool vec = (c_in & 7) == 0;
-    const bool cf = (gp.gm >> kCentre) & 1u;
+    const bool cf = ((gp.gm >> kCentre) & 1u) && gp.centre_self;
     if (vec) {
         if (cf) return launch_mt<NBW, OUT_F32, true, true>(grid, s, x, c_in, steps, wp, n_wt, c_out, nbr, mask, gp, n, zrow, y, relu);
         return launch_mt<NBW, OUT_F32, true, false>(grid, s, x, c_in, steps, wp, n_wt, c_out, nbr, mask, gp, n, zrow, y, relu);
@@ -502,7 +504,8 @@ hipError_t launch_conv_masktile(const uint16_t* x, int c_in, const void* wpacked
     if (n <= 0) return hipSuccess;
     if (!gp.perm || (!gp.last && !gp.partial) || (gp.prev && !gp.partial) || !gp.gm)
         return hipErrorInvalidValue;
-    if (!gp.last && ((gp.gm >> kCentre) & 1u)) return hipErrorInvalidValue;   // centre is last
+    if (!gp.last && ((gp.gm >> kCentre) & 1u) && gp.centre_self)
+        return hipErrorInvalidValue;                                           // centre is last
     const int steps = (c_in + 31) / 32;
     const int nbw = nbw_for(c_out);
     const int n_wt = (c_out + 16 * nbw - 1) / (16 * nbw);

@@ -48,6 +48,7 @@ struct MapState {
     int32_t tap_count[kMaxTaps];    // pairs per tap (written by the compaction)
     int32_t tap_tot[kTaps];         // pairs per tap, accumulated by the mask histogram (K = 3)
     int32_t group_rows[4];  // rows with a tap in each offset group (mask-tile row orders)
+    int32_t n_out;          // strided map: output rows
 };
 
 constexpr int kMaxGroups = 4;
@@ -135,6 +136,33 @@ hipError_t launch_sorted_lookup(const void* keys, const uint32_t* vals, int64_t 
                                 bool wide, int32_t* nbr, uint32_t* mask, MapState* st,
                                 hipStream_t s);
 
+// ---- strided maps (strided_kernels.hip) ----
+// Output grid of a strided layer and the packing of its cells into 64-bit
+// keys (b | x | y | z, z lowest); sentinel = 1 << (key bits), above every key.
+struct StrideGeom {
+    int32_t oext[3];
+    int32_t wb, wx, wy, wz;
+    int32_t stride, pad, ksize;
+    int32_t origin[3];      // input coordinate of output cell 0's grid origin (0)
+    uint64_t sentinel;
+};
+int64_t unique_blocks(int64_t n_c);
+// coords [n, ncols] -> 8 candidate output keys per row (sentinels where fewer)
+hipError_t launch_stride_candidates(const int32_t* coords, int64_t n, const Geom& g,
+                                    const StrideGeom& sg, uint64_t* keys, MapState* st,
+                                    hipStream_t s);
+// sorted candidate keys -> output coords [M, 4], query points [M, 4] (input
+// coordinates), st->n_out = M; counts: unique_blocks(n_c) words of scratch
+hipError_t launch_unique(const uint64_t* keys, int64_t n_c, const StrideGeom& sg,
+                         uint32_t* counts, int32_t* ocoords, int32_t* qcoords, MapState* st,
+                         hipStream_t s);
+// sorted keys with an equal neighbour: the duplicate-coordinate status bit
+hipError_t launch_key_dups(const void* keys, bool wide, int64_t n, MapState* st, hipStream_t s);
+// sorted route: the 27 taps around each query point from the sorted input keys
+hipError_t launch_query_lookup(const void* keys, const uint32_t* vals, int64_t n_in, const Geom& g,
+                               bool wide, const int32_t* qcoords, int64_t m, int32_t* nbr,
+                               uint32_t* mask, hipStream_t s);
+
 // ---- radix sort (radix_sort.hip) ----
 // Stable LSD sort of (key, value) pairs on the low passes*bits key bits, one
 // kernel per pass. keys_in is only read; if vals_in is null the values are
@@ -214,6 +242,9 @@ struct GroupPass {
     int64_t goff = 0;
     const int32_t* rows = nullptr;
     float* partial = nullptr;
+    bool centre_self = true;    // the centre tap reads the output row itself (submanifold);
+                                // false: it is gathered through the table like every tap
+    int64_t n_in = 0;           // input rows (0: the same as the n output rows)
 };
 hipError_t launch_conv_masktile(const uint16_t* x, int c_in, const void* wpacked, int c_out,
                                 const int32_t* nbr, const uint32_t* mask, const GroupPass& gp,

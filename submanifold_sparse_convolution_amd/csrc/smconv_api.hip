@@ -68,6 +68,7 @@ struct DevBuf {
 };
 
 constexpr int64_t kMaxRows = (int64_t)1 << 26;
+constexpr int64_t kMaxStridedRows = (int64_t)1 << 24;            // 8 candidates per input
 constexpr int kMaxChannels = 4096;
 constexpr int kZeroRowBytes = kMaxChannels * 2;                 // keeps 27 n + pads < 2^31
 constexpr int64_t kDenseBudgetBytes = (int64_t)4 << 30;        // auto route: grid <= 4 GiB
@@ -129,6 +130,11 @@ struct smc_map {
     bool has_pairs = false;
     bool has_sort = false;
     int ksize = 3;                    // kernel size of the last build (taps = ksize^3)
+    // strided builds: outputs differ from inputs (n = output rows, n_in = input rows)
+    bool strided = false;
+    int64_t n_in = 0;
+    StrideGeom sgeom{};
+    DevBuf ck0, ck1, ck2, cv0, cv1, chist, ucounts, ocoords, qcoords;
     // stage timers
     bool timing = false;
     std::vector<hipEvent_t> ev_pool;
@@ -349,9 +355,42 @@ int smc_map_destroy(smc_map* m) {
     return SMC_OK;
 }
 
-int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
-                  const int32_t* spatial_shape, int batch_size, int kernel_size, int route,
-                  unsigned flags, void* stream) {
+// Strided map, output side: candidate output keys of every input, one radix
+// sort, unique (output coords + query points), and one read of the output
+// count (*rows). The input-side structure (grid or sorted keys) is built by
+// the caller.
+static int strided_outputs(smc_map* m, const int32_t* coords, int64_t n, const Geom& g,
+                           const StrideGeom& sg, MapState* st, uint32_t* status, hipStream_t s,
+                           int64_t* rows) {
+    const int64_t n_cand = 8 * n;
+    SMC_HIP(launch_stride_candidates(coords, n, g, sg, m->ck0.as<uint64_t>(), st, s));
+    int bits = 1;
+    while (((uint64_t)1 << bits) <= sg.sentinel) ++bits;   // key bits including the sentinel's
+    const SortPlan plan = sort_plan(bits);
+    if (plan.passes * (1 << plan.bits) > kHistKeyInts)
+        return fail(SMC_ERR_UNSUPPORTED, "output key sort needs %d bins", plan.passes * (1 << plan.bits));
+    SMC_HIP(launch_fill_i32(m->chist.as<int32_t>(), kHistKeyInts, 0, s));
+    SMC_HIP(launch_key_hist(m->ck0.p, true, n_cand, plan, m->chist.as<uint32_t>(), s));
+    const uint64_t* sorted = nullptr;
+    const uint32_t* sv = nullptr;
+    SMC_HIP(radix_sort_u64(m->ck0.as<uint64_t>(), nullptr, n_cand, plan, m->chist.as<uint32_t>(),
+                           m->ck1.as<uint64_t>(), m->ck2.as<uint64_t>(), m->cv0.as<uint32_t>(),
+                           m->cv1.as<uint32_t>(), m->ws, status, &sorted, &sv, s));
+    SMC_HIP(launch_unique(sorted, n_cand, sg, m->ucounts.as<uint32_t>(), m->ocoords.as<int32_t>(),
+                          m->qcoords.as<int32_t>(), st, s));
+    int32_t count = 0;
+    SMC_HIP(hipMemcpyAsync(&m->host_state->n_out, &st->n_out, sizeof(int32_t),
+                           hipMemcpyDeviceToHost, s));
+    SMC_HIP(hipStreamSynchronize(s));
+    count = m->host_state->n_out;
+    if (count < 0 || count > n_cand) return fail(SMC_ERR_STATE, "output count %d", count);
+    *rows = count;
+    return SMC_OK;
+}
+
+static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
+                     const int32_t* spatial_shape, int batch_size, int kernel_size, int route,
+                     unsigned flags, void* stream, bool strided) {
     if (!m) return fail(SMC_ERR_ARG, "map is NULL");
     if (kernel_size != 3 && kernel_size != 5)
         return fail(SMC_ERR_UNSUPPORTED, "kernel_size %d (3 or 5)", kernel_size);
@@ -408,6 +447,15 @@ int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
             g.origin[d] = 0;
             g.ext[d] = spatial_shape[d];
         }
+    } else if (n > 0 && strided) {
+        // output cells are counted from coordinate 0: the grid is [0, max + 1)
+        for (int d = 0; d < 3; ++d) {
+            if (bbox[d] < 0) return fail(SMC_ERR_RANGE, "negative coordinate %d", bbox[d]);
+            int64_t e = (int64_t)bbox[3 + d] + 1;
+            if (e > ((int64_t)1 << 30)) return fail(SMC_ERR_RANGE, "extent %lld too large", (long long)e);
+            g.origin[d] = 0;
+            g.ext[d] = (int32_t)e;
+        }
     } else if (n > 0) {
         for (int d = 0; d < 3; ++d) {
             g.origin[d] = bbox[d];
@@ -459,6 +507,23 @@ int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
         if (key_bits > 64)
             return fail(SMC_ERR_KEY_OVERFLOW, "packed key needs %d bits", key_bits);
     }
+    StrideGeom sg{};
+    if (strided) {
+        sg.stride = 2;
+        sg.pad = 1;
+        sg.ksize = 3;
+        for (int d = 0; d < 3; ++d) {
+            sg.oext[d] = (g.ext[d] + 2 * sg.pad - sg.ksize) / sg.stride + 1;
+            sg.origin[d] = 0;
+        }
+        sg.wb = bit_len((int64_t)g.batch - 1);
+        sg.wx = bit_len((int64_t)sg.oext[0] - 1);
+        sg.wy = bit_len((int64_t)sg.oext[1] - 1);
+        sg.wz = bit_len((int64_t)sg.oext[2] - 1);
+        const int ob = sg.wb + sg.wx + sg.wy + sg.wz;
+        if (ob > 62) return fail(SMC_ERR_KEY_OVERFLOW, "output key needs %d bits", ob);
+        sg.sentinel = (uint64_t)1 << ob;
+    }
     m->geom = g;
     m->route = chosen;
     m->key_bits = key_bits;
@@ -467,24 +532,36 @@ int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     m->n = n;
 
     // ---- buffers ----
-    const bool want_pairs = !(flags & SMC_BUILD_NO_PAIRS);
-    const bool want_sort = !(flags & SMC_BUILD_NO_SORT) && kernel_size == 3;   // mask tiles: 3^3
+    // a strided map: no pair lists, the plain mask order over its output rows
+    const bool want_pairs = !(flags & SMC_BUILD_NO_PAIRS) && !strided;
+    const bool want_sort = (!(flags & SMC_BUILD_NO_SORT) && kernel_size == 3) || strided;
     const int64_t nn = n > 0 ? n : 1;
+    const int64_t n_cand = strided ? 8 * nn : 0;      // candidate output cells (8 per input)
+    const int64_t rows_cap = strided ? n_cand : nn;   // rows of the map's tables
     const int64_t cap = (nn + kCapAlign - 1) / kCapAlign * kCapAlign;
-    const MaskOrder ord = want_sort ? m->order : MaskOrder();
-    const int64_t items = nn * ord.n_groups;          // mask-sort items: one per (group, row)
+    const MaskOrder ord = want_sort && !strided ? m->order : MaskOrder();
+    const int64_t items = rows_cap * ord.n_groups;    // mask-sort items: one per (group, row)
     size_t look_bytes = sort_look_bytes(items > nn ? items : nn);
     const size_t look_c = compact_look_bytes_k(nn, kernel_size);
     if (look_c > look_bytes) look_bytes = look_c;
     const size_t look_before = m->look.bytes;
     // (the neighbour table is read in whole 16-byte words: keep the last one readable)
-    if ((rc = m->nbr.ensure((size_t)nn * taps * 4 + 16)) ||
-        (rc = m->mask.ensure((size_t)nn * mwords * 4)) ||
+    if ((rc = m->nbr.ensure((size_t)rows_cap * taps * 4 + 16)) ||
+        (rc = m->mask.ensure((size_t)rows_cap * mwords * 4)) ||
         (rc = m->mkey0.ensure((size_t)items * 4)) || (rc = m->mkey1.ensure((size_t)items * 4)) ||
         (rc = m->mval0.ensure((size_t)items * 4)) || (rc = m->mval1.ensure((size_t)items * 4)) ||
         (rc = m->look.ensure(look_bytes)))
         return rc;
     if (!ord.plain && (rc = m->okeys.ensure((size_t)items * 4))) return rc;
+    if (strided &&
+        ((rc = m->ck0.ensure((size_t)n_cand * 8)) || (rc = m->ck1.ensure((size_t)n_cand * 8)) ||
+         (rc = m->ck2.ensure((size_t)n_cand * 8)) || (rc = m->cv0.ensure((size_t)n_cand * 4)) ||
+         (rc = m->cv1.ensure((size_t)n_cand * 4)) ||
+         (rc = m->chist.ensure((size_t)kHistKeyInts * 4)) ||
+         (rc = m->ucounts.ensure((size_t)unique_blocks(n_cand) * 4)) ||
+         (rc = m->ocoords.ensure((size_t)n_cand * 16)) ||
+         (rc = m->qcoords.ensure((size_t)n_cand * 16))))
+        return rc;
     if (want_pairs &&
         ((rc = m->pair_in.ensure((size_t)taps * cap * 4)) ||
          (rc = m->pair_out.ensure((size_t)taps * cap * 4)) ||
@@ -497,6 +574,7 @@ int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     m->cap = cap;
     uint32_t* status = &st->status;
 
+    int64_t rows = strided ? 0 : n;                  // rows of the map (strided: output cells)
     if (n > 0) {
         int32_t* nbr = m->nbr.as<int32_t>();
         uint32_t* mask = m->mask.as<uint32_t>();
@@ -523,6 +601,11 @@ int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
                                               m->pair_slot.as<int32_t>(),
                                               m->rowbase.as<int32_t>(), m->ws, status, s));
                 t_cp.finish();
+            } else if (strided) {
+                if ((rc = strided_outputs(m, coords, n, g, sg, st, status, s, &rows))) return rc;
+                Geom gq = g;                          // query points: [M, 4] in input coordinates
+                gq.ncols = 4;
+                SMC_HIP(launch_dense_lookup(m->qcoords.as<int32_t>(), rows, gq, grid, nbr, mask, s));
             } else {
                 SMC_HIP(launch_dense_lookup(coords, n, g, grid, nbr, mask, s));
             }
@@ -553,7 +636,14 @@ int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
                                        m->vals0.as<uint32_t>(), m->vals1.as<uint32_t>(), m->ws,
                                        status, (const uint32_t**)&skeys, &svals, s));
             }
-            SMC_HIP(launch_sorted_lookup(skeys, svals, n, g, m->wide, nbr, mask, st, s));
+            if (strided) {
+                SMC_HIP(launch_key_dups(skeys, m->wide, n, st, s));
+                if ((rc = strided_outputs(m, coords, n, g, sg, st, status, s, &rows))) return rc;
+                SMC_HIP(launch_query_lookup(skeys, svals, n, g, m->wide, m->qcoords.as<int32_t>(),
+                                            rows, nbr, mask, s));
+            } else {
+                SMC_HIP(launch_sorted_lookup(skeys, svals, n, g, m->wide, nbr, mask, st, s));
+            }
         }
         t_nb.finish();
         // the mask histogram also gives the per-tap counts of a map without pair lists
@@ -567,11 +657,12 @@ int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
                 return fail(SMC_ERR_UNSUPPORTED, "mask sort needs %d histogram bins",
                             mp.passes * (1 << mp.bits));
             uint32_t* okeys = ord.plain ? nullptr : m->okeys.as<uint32_t>();
-            SMC_HIP(launch_mask_hist(mask, n, mp, ord, okeys, hist_mask, st->tap_tot,
-                                     st->group_rows, s));
-            if (want_sort) {
+            if (rows > 0)
+                SMC_HIP(launch_mask_hist(mask, rows, mp, ord, okeys, hist_mask, st->tap_tot,
+                                         st->group_rows, s));
+            if (want_sort && rows > 0) {
                 const uint32_t* sorted_keys;
-                SMC_HIP(radix_sort_u32(ord.plain ? mask : okeys, nullptr, n * ord.n_groups, mp,
+                SMC_HIP(radix_sort_u32(ord.plain ? mask : okeys, nullptr, rows * ord.n_groups, mp,
                                        hist_mask, m->mkey0.as<uint32_t>(),
                                        m->mkey1.as<uint32_t>(), m->mval0.as<uint32_t>(),
                                        m->mval1.as<uint32_t>(), m->ws, status, &sorted_keys,
@@ -592,6 +683,10 @@ int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     m->has_sort = want_sort;
     m->sorted_order = ord;
     m->ksize = kernel_size;
+    m->strided = strided;
+    m->n_in = n;
+    m->n = rows;
+    m->sgeom = sg;
     t_map.finish();
     const bool async = (flags & SMC_BUILD_ASYNC) != 0;
     if (!async)
@@ -603,6 +698,38 @@ int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     m->build_status = SMC_OK;
     if (async) return SMC_OK;
     return wait_build(m);
+}
+
+int smc_map_build(smc_map* m, const int32_t* coords, int64_t n, int ncols,
+                  const int32_t* spatial_shape, int batch_size, int kernel_size, int route,
+                  unsigned flags, void* stream) {
+    return build_map(m, coords, n, ncols, spatial_shape, batch_size, kernel_size, route, flags,
+                     stream, false);
+}
+
+int smc_map_build_strided(smc_map* m, const int32_t* coords, int64_t n, int ncols,
+                          const int32_t* spatial_shape, int batch_size, int kernel_size,
+                          int stride, int route, unsigned flags, void* stream) {
+    if (!m) return fail(SMC_ERR_ARG, "map is NULL");
+    if (kernel_size != 3 || stride != 2)
+        return fail(SMC_ERR_UNSUPPORTED, "strided maps: kernel 3, stride 2 (got %d, %d)",
+                    kernel_size, stride);
+    if (n > kMaxStridedRows)
+        return fail(SMC_ERR_ARG, "n = %lld above 2^24 for a strided map", (long long)n);
+    return build_map(m, coords, n, ncols, spatial_shape, batch_size, kernel_size, route,
+                     flags & ~(unsigned)(SMC_BUILD_NO_PAIRS | SMC_BUILD_NO_SORT), stream, true);
+}
+
+int smc_map_export_out_coords(smc_map* m, int32_t* out_coords) {
+    if (!m) return fail(SMC_ERR_ARG, "map is NULL");
+    if (!m->built) return fail(SMC_ERR_STATE, "map was never built");
+    if (!m->strided) return fail(SMC_ERR_STATE, "not a strided map (outputs are the inputs)");
+    SMC_HIP(hipSetDevice(m->device));
+    (void)wait_build(m);
+    SMC_HIP(hipDeviceSynchronize());
+    if (m->n > 0 && out_coords)
+        SMC_HIP(hipMemcpy(out_coords, m->ocoords.p, (size_t)m->n * 16, hipMemcpyDeviceToHost));
+    return SMC_OK;
 }
 
 int smc_map_sync(smc_map* m) {
@@ -629,6 +756,9 @@ int smc_map_info(smc_map* m, smc_map_info_t* info) {
     info->tile_m = kTileM;
     info->grid_cells = m->grid_cells;
     info->kernel_size = m->ksize;
+    info->n_in = m->n_in;
+    info->strided = m->strided ? 1 : 0;
+    for (int d = 0; d < 3; ++d) info->out_extent[d] = m->strided ? m->sgeom.oext[d] : m->geom.ext[d];
     const int taps = m->ksize * m->ksize * m->ksize;
     info->taps = taps;
     const MapState& hs = *m->host_state;
@@ -733,7 +863,8 @@ int smc_conv_forward(smc_map* m, const uint16_t* x, int c_in, const void* wpacke
     if (c_in < 1 || c_out < 1) return fail(SMC_ERR_ARG, "c_in = %d, c_out = %d", c_in, c_out);
     if (c_in > kMaxChannels || c_out > kMaxChannels)
         return fail(SMC_ERR_UNSUPPORTED, "channels above 4096");
-    const bool mask_tiles = (flags & SMC_FWD_MASK_TILES) != 0;
+    // a strided map has mask tiles only (its outputs are not its inputs)
+    const bool mask_tiles = (flags & SMC_FWD_MASK_TILES) != 0 || m->strided;
     if (!mask_tiles && !m->has_pairs)
         return fail(SMC_ERR_STATE, "map was built without pair lists (SMC_BUILD_NO_PAIRS)");
     if (mask_tiles && m->ksize != 3)
@@ -772,6 +903,8 @@ int smc_conv_forward(smc_map* m, const uint16_t* x, int c_in, const void* wpacke
             gp.goff = (int64_t)g * m->n;
             gp.rows = gp.last ? nullptr : dst->group_rows + g;
             gp.partial = o.n_groups > 1 ? m->part.as<float>() : nullptr;
+            gp.centre_self = !m->strided;
+            gp.n_in = m->n_in;
             SMC_HIP(launch_conv_masktile(x, c_in, wpacked, c_out, m->nbr.as<int32_t>(),
                                          m->mask.as<uint32_t>(), gp, m->n,
                                          m->zrow.as<uint16_t>(), y, (flags & SMC_FWD_OUT_F32) != 0,

@@ -1,0 +1,314 @@
+// Kernel map of a strided (downsampling) sparse convolution.
+//
+// "Sparse convolution in FP32" (DriveRT), section "Calibrated bit order":
+// the strided layers change the coordinate set, and their kernels are the
+// same mask-sorted tiles as the submanifold ones. The layer taken here is the
+// usual downsampling one: kernel K = 3, stride 2, padding 1. Output cell o
+// exists when an input c = 2 o - 1 + d (d in [0, 3)^3) is active; its taps are
+// the 27 cells around the query point q = 2 o, numbered like the submanifold
+// taps. Output rows are ordered by (b, x, y, z).
+//
+// Steps: every input emits the (at most 8) output cells it feeds as packed
+// 64-bit keys; one radix sort orders them; a count / scan / write pass keeps
+// the first of each run and writes the output coordinates and query points.
+// The neighbour lookup around the query points then reuses the dense grid, or
+// searches the sorted input keys (k_query_lookup, one search per (dx, dy)
+// column as in the Z-Delta mapper).
+#include "smc_internal.h"
+
+namespace smc {
+namespace {
+
+constexpr int kUThreads = 256;
+constexpr int kUItems = 4;
+constexpr int kUTile = kUThreads * kUItems;     // sorted candidates per unique block
+
+__device__ inline uint64_t pack_out(const StrideGeom& sg, int b, int x, int y, int z) {
+    uint64_t k = (uint64_t)b;
+    k = (k << sg.wx) | (uint64_t)x;
+    k = (k << sg.wy) | (uint64_t)y;
+    k = (k << sg.wz) | (uint64_t)z;
+    return k;
+}
+
+// Output cells along one axis fed by input coordinate v: o = (v + pad - d) / s
+// for taps d with the division exact and o inside [0, oext).
+__device__ inline int axis_cands(int v, int oext, const StrideGeom& sg, int& o0, int& o1) {
+    int cnt = 0;
+#pragma unroll
+    for (int d = 0; d < 3; ++d) {
+        const int t = v + sg.pad - d;
+        const bool ok = t >= 0 && t % sg.stride == 0 && t / sg.stride < oext;
+        if (ok) {
+            if (cnt == 0) o0 = t / sg.stride;
+            else o1 = t / sg.stride;
+            ++cnt;
+        }
+    }
+    return cnt;                                   // at most 2 for K = 3, stride 2
+}
+
+// Eight key slots per input row: the output cells it feeds, then the sentinel
+// (above every key: it sorts last and is dropped).
+__global__ __launch_bounds__(kBlock) void k_stride_candidates(const int32_t* __restrict__ coords,
+                                                              int64_t n, Geom g, StrideGeom sg,
+                                                              uint64_t* __restrict__ keys,
+                                                              MapState* st) {
+    const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const int32_t* c = coords + i * g.ncols;
+    const int b = g.ncols == 4 ? c[0] : 0;
+    const int32_t* p = c + (g.ncols == 4 ? 1 : 0);
+    const int x = p[0] - g.origin[0], y = p[1] - g.origin[1], z = p[2] - g.origin[2];
+    const bool in = (unsigned)b < (unsigned)g.batch && (unsigned)x < (unsigned)g.ext[0] &&
+                    (unsigned)y < (unsigned)g.ext[1] && (unsigned)z < (unsigned)g.ext[2];
+    uint64_t* out = keys + i * 8;
+    int written = 0;
+    if (in) {
+        int x0 = 0, x1 = 0, y0 = 0, y1 = 0, z0 = 0, z1 = 0;
+        const int nx = axis_cands(x, sg.oext[0], sg, x0, x1);
+        const int ny = axis_cands(y, sg.oext[1], sg, y0, y1);
+        const int nz = axis_cands(z, sg.oext[2], sg, z0, z1);
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+#pragma unroll
+                for (int f = 0; f < 2; ++f)
+                    if (a < nx && e < ny && f < nz)
+                        out[written++] = pack_out(sg, b, a ? x1 : x0, e ? y1 : y0, f ? z1 : z0);
+    } else {
+        atomicOr(&st->status, kStRange);
+    }
+    for (int j = written; j < 8; ++j) out[j] = sg.sentinel;
+}
+
+// first of a run of equal keys (and not the sentinel)
+__device__ inline bool run_head(const uint64_t* __restrict__ keys, int64_t i, uint64_t sentinel) {
+    const uint64_t k = keys[i];
+    return k < sentinel && (i == 0 || keys[i - 1] != k);
+}
+
+__device__ inline uint32_t block_sum(uint32_t v, uint32_t* s_w) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    if (lane == 0) s_w[w] = v;
+    __syncthreads();
+    uint32_t t = 0;
+    for (int q = 0; q < (int)(blockDim.x >> 6); ++q) t += s_w[q];
+    return t;
+}
+
+__global__ __launch_bounds__(kUThreads) void k_unique_count(const uint64_t* __restrict__ keys,
+                                                            int64_t n_c, uint64_t sentinel,
+                                                            uint32_t* __restrict__ counts) {
+    __shared__ uint32_t s_w[kUThreads / 64];
+    const int64_t base = (int64_t)blockIdx.x * kUTile;
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < kUItems; ++j) {
+        const int64_t i = base + (int64_t)threadIdx.x * kUItems + j;
+        if (i < n_c && run_head(keys, i, sentinel)) ++c;
+    }
+    const uint32_t t = block_sum(c, s_w);
+    if (threadIdx.x == 0) counts[blockIdx.x] = t;
+}
+
+// Exclusive scan of the per-block counts in place (one block); the total is the
+// number of output rows.
+__global__ __launch_bounds__(1024) void k_scan_counts(uint32_t* __restrict__ counts, int64_t nb,
+                                                      MapState* st) {
+    __shared__ uint32_t s_w[16];
+    __shared__ uint32_t s_carry;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (threadIdx.x == 0) s_carry = 0;
+    __syncthreads();
+    for (int64_t c0 = 0; c0 < nb; c0 += 1024) {
+        const int64_t i = c0 + threadIdx.x;
+        const uint32_t v = i < nb ? counts[i] : 0u;
+        uint32_t inc = v;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t t = __shfl_up(inc, o);
+            if (lane >= o) inc += t;
+        }
+        if (lane == 63) s_w[w] = inc;
+        __syncthreads();
+        uint32_t before = s_carry;
+        for (int q = 0; q < w; ++q) before += s_w[q];
+        if (i < nb) counts[i] = before + inc - v;
+        __syncthreads();
+        if (threadIdx.x == 1023) s_carry = before + inc;
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) st->n_out = (int32_t)s_carry;
+}
+
+// Each run head goes to output row offs[block] + (heads before it in the
+// block): its coordinates (b, x, y, z) and query point (b, s x - pad + r, ...)
+// in input coordinates.
+__global__ __launch_bounds__(kUThreads) void k_unique_write(
+    const uint64_t* __restrict__ keys, int64_t n_c, StrideGeom sg,
+    const uint32_t* __restrict__ offs, int32_t* __restrict__ ocoords,
+    int32_t* __restrict__ qcoords) {
+    __shared__ uint32_t s_w[kUThreads / 64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t base = (int64_t)blockIdx.x * kUTile + (int64_t)threadIdx.x * kUItems;
+    bool h[kUItems];
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < kUItems; ++j) {
+        h[j] = base + j < n_c && run_head(keys, base + j, sg.sentinel);
+        c += h[j] ? 1u : 0u;
+    }
+    uint32_t inc = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = __shfl_up(inc, o);
+        if (lane >= o) inc += t;
+    }
+    if (lane == 63) s_w[w] = inc;
+    __syncthreads();
+    uint32_t pos = offs[blockIdx.x] + inc - c;
+    for (int q = 0; q < w; ++q) pos += s_w[q];
+    const uint64_t mz = (1ull << sg.wz) - 1, my = (1ull << sg.wy) - 1, mx = (1ull << sg.wx) - 1;
+    const int r = (sg.ksize - 1) / 2;
+#pragma unroll
+    for (int j = 0; j < kUItems; ++j) {
+        if (!h[j]) continue;
+        const uint64_t k = keys[base + j];
+        const int z = (int)(k & mz), y = (int)((k >> sg.wz) & my),
+                  x = (int)((k >> (sg.wz + sg.wy)) & mx), b = (int)(k >> (sg.wz + sg.wy + sg.wx));
+        int32_t* oc = ocoords + (int64_t)pos * 4;
+        oc[0] = b;
+        oc[1] = x;
+        oc[2] = y;
+        oc[3] = z;
+        int32_t* qc = qcoords + (int64_t)pos * 4;
+        qc[0] = b;
+        qc[1] = sg.stride * x - sg.pad + r + sg.origin[0];
+        qc[2] = sg.stride * y - sg.pad + r + sg.origin[1];
+        qc[3] = sg.stride * z - sg.pad + r + sg.origin[2];
+        ++pos;
+    }
+}
+
+template <typename K>
+__device__ inline int64_t lower_bound_k(const K* __restrict__ keys, int64_t n, K t) {
+    int64_t lo = 0, len = n;
+    while (len > 0) {
+        const int64_t half = len >> 1;
+        if (keys[lo + half] < t) {
+            lo += half + 1;
+            len -= half + 1;
+        } else {
+            len = half;
+        }
+    }
+    return lo;
+}
+
+// Sorted route: the 27 taps around each query point, searched in the sorted
+// input keys (16 lanes per query, one per (dx, dy) column: a lower_bound for
+// the column's lowest key, then up to 3 compares).
+template <typename K>
+__global__ __launch_bounds__(kBlock) void k_query_lookup(const K* __restrict__ keys,
+                                                         const uint32_t* __restrict__ vals,
+                                                         int64_t n_in, Geom g,
+                                                         const int32_t* __restrict__ qcoords,
+                                                         int64_t m, int32_t* __restrict__ nbr,
+                                                         uint32_t* __restrict__ mask) {
+    const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    const int64_t o = t >> 4;
+    const int c = (int)(t & 15);
+    uint32_t bits = 0;
+    if (o < m && c < 9) {
+        const int32_t* q = qcoords + o * 4;
+        K key = (K)q[0];
+        key = (key << g.wx) | (K)(q[1] - g.origin[0] + g.pad);
+        key = (key << g.wy) | (K)(q[2] - g.origin[1] + g.pad);
+        key = (key << g.wz) | (K)(q[3] - g.origin[2] + g.pad);
+        const int dx = c / 3 - 1, dy = c % 3 - 1;
+        const K delta = (K)((int64_t)dx * ((int64_t)1 << (g.wy + g.wz))) +
+                        (K)((int64_t)dy * ((int64_t)1 << g.wz));
+        const K first = key + delta - (K)1;
+        int64_t j = lower_bound_k(keys, n_in, first);
+#pragma unroll
+        for (int dz = 0; dz < 3; ++dz) {
+            int hit = -1;
+            if (j < n_in && keys[j] == first + (K)dz) {
+                hit = (int)min(vals[j], (uint32_t)(n_in - 1));
+                ++j;
+            }
+            nbr[o * kTaps + 3 * c + dz] = hit;
+            if (hit >= 0) bits |= 1u << (3 * c + dz);
+        }
+    }
+    bits |= __shfl_xor(bits, 8, 16);
+    bits |= __shfl_xor(bits, 4, 16);
+    bits |= __shfl_xor(bits, 2, 16);
+    bits |= __shfl_xor(bits, 1, 16);
+    if (o < m && c == 0) mask[o] = bits;
+}
+
+// Two rows with one key: duplicate coordinates (sorted route of a strided map).
+template <typename K>
+__global__ __launch_bounds__(kBlock) void k_key_dups(const K* __restrict__ keys, int64_t n,
+                                                     MapState* st) {
+    const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (i + 1 < n && keys[i] == keys[i + 1]) atomicOr(&st->status, kStDuplicate);
+}
+
+inline unsigned blocks_of(int64_t threads, int per) {
+    const int64_t b = (threads + per - 1) / per;
+    return (unsigned)(b < 1 ? 1 : b);
+}
+
+}  // namespace
+
+int64_t unique_blocks(int64_t n_c) { return (n_c + kUTile - 1) / kUTile; }
+
+hipError_t launch_stride_candidates(const int32_t* coords, int64_t n, const Geom& g,
+                                    const StrideGeom& sg, uint64_t* keys, MapState* st,
+                                    hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    launch(k_stride_candidates, blocks_of(n, kBlock), kBlock, 0, s, coords, n, g, sg, keys, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_unique(const uint64_t* keys, int64_t n_c, const StrideGeom& sg,
+                         uint32_t* counts, int32_t* ocoords, int32_t* qcoords, MapState* st,
+                         hipStream_t s) {
+    if (n_c <= 0) return hipSuccess;
+    const int64_t nb = unique_blocks(n_c);
+    launch(k_unique_count, (unsigned)nb, kUThreads, 0, s, keys, n_c, sg.sentinel, counts);
+    launch(k_scan_counts, 1u, 1024, 0, s, counts, nb, st);
+    launch(k_unique_write, (unsigned)nb, kUThreads, 0, s, keys, n_c, sg, (const uint32_t*)counts,
+           ocoords, qcoords);
+    return hipGetLastError();
+}
+
+hipError_t launch_query_lookup(const void* keys, const uint32_t* vals, int64_t n_in, const Geom& g,
+                               bool wide, const int32_t* qcoords, int64_t m, int32_t* nbr,
+                               uint32_t* mask, hipStream_t s) {
+    if (m <= 0) return hipSuccess;
+    if (wide)
+        launch(k_query_lookup<uint64_t>, blocks_of(m * 16, kBlock), kBlock, 0, s,
+               (const uint64_t*)keys, vals, n_in, g, qcoords, m, nbr, mask);
+    else
+        launch(k_query_lookup<uint32_t>, blocks_of(m * 16, kBlock), kBlock, 0, s,
+               (const uint32_t*)keys, vals, n_in, g, qcoords, m, nbr, mask);
+    return hipGetLastError();
+}
+
+hipError_t launch_key_dups(const void* keys, bool wide, int64_t n, MapState* st, hipStream_t s) {
+    if (n <= 1) return hipSuccess;
+    if (wide)
+        launch(k_key_dups<uint64_t>, blocks_of(n, kBlock), kBlock, 0, s, (const uint64_t*)keys, n, st);
+    else
+        launch(k_key_dups<uint32_t>, blocks_of(n, kBlock), kBlock, 0, s, (const uint32_t*)keys, n, st);
+    return hipGetLastError();
+}
+
+}  // namespace smc

@@ -1,0 +1,168 @@
+"""Strided (downsampling) layer on the GPU vs the CPU oracle.
+
+"Sparse convolution in FP32" (DriveRT), section "Calibrated bit order": the
+strided layers change the coordinate set and run as mask-sorted tiles. The
+reading (kernel 3, stride 2, padding 1, outputs ordered by (b, x, y, z)) is
+the oracle's build_strided_map. Output coordinates, neighbour table, masks
+and mask order must match bit for bit on both routes; outputs exactly with
+integer inputs, within the bf16 / float32 tolerances otherwise.
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import smconv_oracle as so
+from _util import bf16_bits_of, check_bf16_output, check_f32_acc, to_dev_bf16, to_dev_i32
+
+pytestmark = pytest.mark.gpu
+
+smc = pytest.importorskip("submanifold_sparse_convolution_amd")
+
+
+def oracle_strided(coords, shape):
+    oc, oshape, nbr, mask = so.build_strided_map(coords, shape)
+    return dict(out_coords=oc, out_shape=oshape, nbr=nbr, mask=mask,
+                perm=so.mask_sort(mask)[None, :])
+
+
+def gpu_strided(coords, shape=None, route="auto", batch_size=0, ncols=4, sync=True):
+    c = coords if ncols == 4 else coords[:, 1:]
+    m = smc.KernelMap().build_strided(to_dev_i32(c), spatial_shape=shape, route=route,
+                                      batch_size=batch_size, sync=sync)
+    ex = m.export(pairs=False)
+    ex["out_coords"] = m.out_coords()
+    ex["info"] = m.info()
+    m.close()
+    return ex
+
+
+def check_map(got, want, label):
+    for key in ("out_coords", "nbr", "mask", "perm"):
+        g, w = np.asarray(got[key]), np.asarray(want[key])
+        assert g.shape == w.shape, f"{label} {key}: shape {g.shape} != {w.shape}"
+        assert np.array_equal(g.astype(np.int64), w.astype(np.int64)), f"{label} {key}"
+    assert got["info"]["strided"] and got["info"]["n"] == len(want["out_coords"])
+    assert tuple(got["info"]["out_extent"]) == tuple(want["out_shape"])
+
+
+def random_cells(shape, n, seed, batch=0):
+    rng = np.random.default_rng(seed)
+    cells = rng.choice(int(np.prod(shape)), size=n, replace=False)
+    xyz = np.stack(np.unravel_index(cells, shape), axis=1)
+    return np.concatenate([np.full((n, 1), batch), xyz], axis=1).astype(np.int32)
+
+
+@pytest.mark.parametrize("route", ["dense", "sorted"])
+@pytest.mark.parametrize("shape,n,seed", [((8, 8, 8), 1, 1), ((8, 8, 8), 7, 2),
+                                          ((9, 7, 5), 120, 3), ((1, 6, 11), 30, 4),
+                                          ((24, 24, 24), 3000, 5), ((31, 17, 40), 2500, 6)])
+def test_strided_map_small(shape, n, seed, route):
+    coords = random_cells(shape, n, seed)
+    print(f"strided map {shape} n={n} {route}", flush=True)
+    check_map(gpu_strided(coords, shape, route=route), oracle_strided(coords, shape),
+              f"{shape} n={n} {route}")
+
+
+@pytest.mark.parametrize("route", ["dense", "sorted"])
+def test_strided_batches_derived_shape_ncols3(route):
+    a = random_cells((20, 20, 20), 900, 7, 0)
+    b = random_cells((20, 20, 20), 700, 8, 2)
+    coords = np.concatenate([a, b])
+    coords = coords[np.random.default_rng(1).permutation(len(coords))]
+    want = oracle_strided(coords, (20, 20, 20))
+    check_map(gpu_strided(coords, (20, 20, 20), route=route, batch_size=3), want, "batches")
+    mx = tuple(int(v) + 1 for v in coords[:, 1:].max(0))
+    check_map(gpu_strided(coords, None, route=route), oracle_strided(coords, mx), "derived")
+    check_map(gpu_strided(a, (20, 20, 20), route=route, ncols=3),
+              oracle_strided(a, (20, 20, 20)), "ncols=3")
+
+
+@pytest.mark.parametrize("name", ["lidar", "deep"])
+def test_strided_map_workloads(name):
+    w = synth.workload(name)
+    coords = synth.make_coords(w)
+    print(f"strided map {name} n={w.n}", flush=True)
+    want = oracle_strided(coords, w.grid)
+    got = gpu_strided(coords, w.grid)
+    check_map(got, want, name)
+    got2 = gpu_strided(coords, w.grid, route="sorted", sync=False)
+    check_map(got2, want, name + " sorted")
+
+
+def strided_forward(coords, shape, xb, wb, relu=False, out_f32=False, route="auto"):
+    m = smc.KernelMap().build_strided(to_dev_i32(coords), spatial_shape=shape, route=route)
+    y = m.forward(to_dev_bf16(xb), smc.pack_weights(to_dev_bf16(wb)), relu=relu, out_f32=out_f32)
+    out = y.cpu().numpy() if out_f32 else bf16_bits_of(y)
+    m.close()
+    return out
+
+
+@pytest.mark.parametrize("route", ["dense", "sorted"])
+@pytest.mark.parametrize("ci,co", [(16, 16), (64, 48), (200, 136), (1, 1), (128, 128)])
+def test_strided_layer_integer_exact(ci, co, route):
+    coords = random_cells((30, 30, 30), 4000, 11)
+    print(f"strided layer {ci}x{co} {route}", flush=True)
+    xb = synth.int_features(4000, ci, 5)
+    wb = synth.int_weights(ci, co, 5)
+    r = so.strided_conv(coords, (30, 30, 30), xb, wb)
+    acc = strided_forward(coords, (30, 30, 30), xb, wb, out_f32=True, route=route)
+    assert np.array_equal(acc.astype(np.float64), r["acc"])
+    y = strided_forward(coords, (30, 30, 30), xb, wb, relu=True, route=route)
+    assert np.array_equal(so.bf16_bits_to_f64(y), np.maximum(so.round_to_bf16(r["acc"]), 0.0))
+
+
+@pytest.mark.parametrize("name", ["lidar", "deep"])
+def test_strided_layer_workloads(name):
+    w = synth.workload(name)
+    coords = synth.make_coords(w)
+    c = w.channels
+    xb = synth.features(w.n, c, w.seed)
+    wb = synth.weights(c, c, w.seed)
+    r = so.strided_conv(coords, w.grid, xb, wb)
+    x, wt = so.bf16_bits_to_f64(xb), so.bf16_bits_to_f64(wb)
+    s_abs = so.conv_accumulate(np.abs(x), np.abs(wt), r["pair_in"], r["pair_out"], r["tap_off"],
+                               len(r["out_coords"]))
+    print(f"strided layer {name}: {w.n} -> {len(r['out_coords'])} rows", flush=True)
+    y = strided_forward(coords, w.grid, xb, wb)
+    check_bf16_output(y, r["acc"], name, abs_ref=s_abs, n_terms=27 * c)
+    acc = strided_forward(coords, w.grid, xb, wb, out_f32=True)
+    check_f32_acc(acc, r["acc"], name, abs_ref=s_abs, n_terms=27 * c)
+
+
+def test_strided_errors_and_handle_reuse():
+    import torch
+    m = smc.KernelMap()
+    neg = np.array([[0, -1, 2, 3], [0, 4, 4, 4]], np.int32)
+    with pytest.raises(smc.SmconvError):
+        m.build_strided(to_dev_i32(neg))
+    with pytest.raises(smc.SmconvError):
+        m.build_strided(to_dev_i32(random_cells((8, 8, 8), 10, 1)), kernel_size=5)
+    dup = np.array([[0, 1, 2, 3], [0, 5, 5, 5], [0, 1, 2, 3]], np.int32)
+    for route in ("dense", "sorted"):
+        with pytest.raises(smc.SmconvError):
+            m.build_strided(to_dev_i32(dup), spatial_shape=(8, 8, 8), route=route)
+    # strided, submanifold and strided again on one handle
+    coords = random_cells((16, 16, 16), 800, 3)
+    for step in range(3):
+        if step == 1:
+            m.build(to_dev_i32(coords), spatial_shape=(16, 16, 16))
+            assert m.n == 800 and not m.info()["strided"]
+            continue
+        m.build_strided(to_dev_i32(coords), spatial_shape=(16, 16, 16))
+        want = oracle_strided(coords, (16, 16, 16))
+        ex = m.export(pairs=False)
+        ex["out_coords"] = m.out_coords()
+        ex["info"] = m.info()
+        check_map(ex, want, f"reuse {step}")
+        xb = synth.int_features(800, 8, step)
+        wb = synth.int_weights(8, 8, step)
+        y = m.forward(to_dev_bf16(xb), smc.pack_weights(to_dev_bf16(wb)), out_f32=True)
+        assert np.array_equal(y.cpu().numpy().astype(np.float64),
+                              so.strided_conv(coords, (16, 16, 16), xb, wb)["acc"])
+        with pytest.raises(ValueError):
+            m.forward(torch.zeros((ex["info"]["n"], 8), dtype=torch.bfloat16, device="cuda"),
+                      smc.pack_weights(to_dev_bf16(wb)))
+    empty = m.build_strided(torch.zeros((0, 4), dtype=torch.int32, device="cuda"),
+                            spatial_shape=(8, 8, 8))
+    assert empty.n == 0
+    m.close()
