@@ -172,7 +172,7 @@ def tile_work_ratio(mask, perm, group_rows, group_masks):
 
 
 def run_workload(name, steps, warmup, sync_build=False, algo="pairs", copy_probe_mb=0,
-                 order="plain", kernel_size=3, frames=1):
+                 order="plain", kernel_size=3, frames=1, strided=False):
     import torch
 
     import submanifold_sparse_convolution_amd as smc
@@ -213,9 +213,17 @@ def run_workload(name, steps, warmup, sync_build=False, algo="pairs", copy_probe
     torch.cuda.synchronize()
     pack_us = ev0.elapsed_time(ev1) * 1e3 / (10 * w.layers)
 
-    ys = [torch.empty((n_rows, c), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    if strided:
+        # a downsampling layer: the output rows are new cells (one layer)
+        m.build_strided(coords_d, spatial_shape=w.grid, batch_size=frames)
+        ys = [torch.empty((m.n, c), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    else:
+        ys = [torch.empty((n_rows, c), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
 
     def step():
+        if strided:
+            m.build_strided(coords_d, spatial_shape=w.grid, batch_size=frames, sync=sync_build)
+            return m.forward(x_d, packed[0], out=ys[0], algo="mask_tiles")
         m.build(coords_d, spatial_shape=w.grid, batch_size=frames, sync=sync_build,
                 pairs=(algo == "pairs"), sort=(algo == "mask_tiles"), kernel_size=kernel_size)
         h = x_d
@@ -256,7 +264,8 @@ def run_workload(name, steps, warmup, sync_build=False, algo="pairs", copy_probe
     m.close()
 
     pairs = info["pairs"]
-    per_layer_us = wall_ms * 1e3 / w.layers
+    layers = 1 if strided else w.layers
+    per_layer_us = wall_ms * 1e3 / layers
     flops_layer = 2.0 * pairs * c * c
     stage_us = {k: (v[0] * 1e3 / v[1] if v[1] else 0.0) for k, v in stages.items()}
     # per execution; forward stages run once per layer
@@ -264,7 +273,10 @@ def run_workload(name, steps, warmup, sync_build=False, algo="pairs", copy_probe
     for st in ("neighbours", "mask_sort", "compact", "gemm", "centre"):
         if stage_us.get(st, 0.0) <= 0.0:
             continue
-        by, fl = stage_model(st, algo, info["route"], n_rows, pairs, c, c, taps)
+        if strided:
+            by, fl = strided_model(st, info["route"], n_rows, info["n"], pairs, c, c)
+        else:
+            by, fl = stage_model(st, algo, info["route"], n_rows, pairs, c, c, taps)
         if st == "gemm" and algo == "mask_tiles" and info["n_groups"] > 1:
             # float32 partial sums: written by each early pass and read once after
             by += 8 * c * sum(info["group_rows"][:-1])
@@ -273,9 +285,10 @@ def run_workload(name, steps, warmup, sync_build=False, algo="pairs", copy_probe
                          tflops=fl / (us * 1e-6) / 1e12 if fl else 0.0)
     return dict(workload=w, coords=coords, info=info, pairs=pairs, ms_per_step=wall_ms,
                 gpu_ms_per_step=gpu_ms, per_layer_us=per_layer_us, pack_us=pack_us,
-                tflops_effective=flops_layer * w.layers / (wall_ms * 1e-3) / 1e12,
+                tflops_effective=flops_layer * layers / (wall_ms * 1e-3) / 1e12,
                 stage_us=stage_us, model=model, algo=algo, order=order, calibration=cal,
-                tile_work_ratio=work_ratio, kernel_size=kernel_size, frames=frames, n=n_rows)
+                tile_work_ratio=work_ratio, kernel_size=kernel_size, frames=frames, n=n_rows,
+                strided=strided, n_out=info["n"])
 
 
 def source_digest(kernel):
@@ -305,6 +318,23 @@ def traffic_for(workload, algo, kernel):
     return round(k["bytes_per_launch"])
 
 
+def strided_model(stage, route, n, m, p, c_in, c_out):
+    """Algorithmic bytes and useful flops of a strided layer's stages (n inputs,
+    m outputs, p input-output pairs): candidates 8 keys per input, their sort
+    (4 passes of key + value), unique, the 27-tap lookup of every output, the
+    mask sort of the outputs and the mask-tile GEMM."""
+    if stage == "neighbours":
+        cand = 16 * n + 64 * n + 4 * 2 * 12 * 8 * n + 64 * n + 32 * m
+        look = 16 * m + 108 * m + 4 * m + (108 * m if route == "dense" else 9 * 8 * m)
+        return cand + look + (16 * n if route == "dense" else 16 * n + 8 * n + 5 * 2 * 12 * n), 0
+    if stage == "mask_sort":
+        return 4 * m + 3 * 2 * 8 * m, 0
+    if stage == "gemm":
+        return (2 * c_in * n + 2 * 27 * c_in * c_out + 116 * m + 2 * c_out * m,
+                2.0 * p * c_in * c_out)
+    return 0, 0
+
+
 def stage_kernels(stage, algo, route, kernel_size=3):
     """The kernels one execution of a stage launches."""
     if stage == "gemm" and algo == "mask_tiles":
@@ -331,6 +361,11 @@ def roofline(r):
     st = max(model, key=lambda s: model[s]["us"])
     mo = model[st]
     kernels = stage_kernels(st, r["algo"], r["info"]["route"], r.get("kernel_size", 3))
+    if r.get("strided") and st == "neighbours":
+        kernels = ("k_dense_scatter" if r["info"]["route"] == "dense" else "k_make_keys",
+                   "k_stride_candidates", "k_key_hist", "k_os_pass", "k_unique_count",
+                   "k_scan_counts", "k_unique_write",
+                   "k_dense_lookup" if r["info"]["route"] == "dense" else "k_query_lookup")
     kernel = kernels[0] if len(kernels) == 1 else "+".join(kernels)
     intensity = mo["flops"] / mo["bytes"] if mo["bytes"] else 0.0
     mfma = intensity > RIDGE
@@ -547,15 +582,19 @@ def main():
         runs += [("lidar", "pairs", "plain", 5, 1), ("deep", "pairs", "plain", 5, 1),
                  ("wide", "pairs", "plain", 5, 1), ("lidar", "pairs", "plain", 3, 4),
                  ("lidar", "pairs", "plain", 5, 4)]
-        for name, algo, order, ks, frames in runs:
+        runs = [r + (False,) for r in runs]
+        # strided (downsampling) layers, mask tiles
+        runs += [(nm, "mask_tiles", "plain", 3, 1, True) for nm in ("lidar", "deep", "wide", "stage")]
+        for name, algo, order, ks, frames, strided in runs:
             rr = run_workload(name, max(20, args.steps // 2), args.warmup, algo=algo,
-                              order=order, kernel_size=ks, frames=frames)
+                              order=order, kernel_size=ks, frames=frames, strided=strided)
             key = (f"{name}/{algo}" + ("" if order == "plain" else f"/{order}")
-                   + ("" if ks == 3 else f"/k{ks}") + ("" if frames == 1 else f"/b{frames}"))
+                   + ("" if ks == 3 else f"/k{ks}") + ("" if frames == 1 else f"/b{frames}")
+                   + ("/strided" if strided else ""))
             rep[key] = {k: rr[k] for k in ("pairs", "ms_per_step", "per_layer_us", "pack_us",
                                            "tflops_effective", "stage_us", "model",
                                            "tile_work_ratio", "calibration", "kernel_size",
-                                           "frames", "n")}
+                                           "frames", "n", "n_out", "strided")}
             rep[key]["route"] = rr["info"]["route"]
             rep[key]["roofline"] = roofline(rr)
         with open(args.report, "w") as f:
