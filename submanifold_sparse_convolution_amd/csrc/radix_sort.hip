@@ -17,6 +17,13 @@
 //    counts in LDS, so no block barrier per item), then finds how many keys
 //    of each digit precede its tile by decoupled look-back over the blocks
 //    before it, then scatters.
+// Sorts of many tiles take another route per pass (reduce, then scan): with
+// thousands of digit columns a block's look-back walks back through every
+// earlier tile's aggregate, one round trip per few tiles and digit, and a
+// pass over 8 x 10^5 keys measured about 100 us. There, one kernel counts
+// each tile's digits into a digit-major table, a two-level scan turns the
+// table into global start positions, and a third kernel ranks and scatters
+// exactly like the onesweep pass. No block waits for another.
 // Look-back safety: block indices are taken from a ticket counter in launch
 // order, so a block only ever waits for blocks that already hold a ticket,
 // i.e. are running. Each wait is also bounded; a wait that runs out flags
@@ -197,6 +204,187 @@ __global__ __launch_bounds__(kOsThreads) void k_os_pass(
     if (bid == gridDim.x - 1 && tid == 0) atomicExch(ticket, 0u);   // every block holds its ticket
 }
 
+constexpr int kManyTiles = 64;                  // above this many tiles: reduce, then scan
+constexpr int kScanSeg = 4096;                  // scan segment (1024 threads x 4)
+
+// Stable rank of this thread's kOsItems keys inside its wave's contiguous
+// quarter of the tile, the wave's per-digit counts in s_wcnt (shared by the
+// onesweep and the scatter kernels).
+template <typename K, int BITS>
+__device__ __forceinline__ void rank_tile(const K* __restrict__ kin, const uint32_t* __restrict__ vin,
+                                          int64_t n, int shift, int64_t base, K (&key)[kOsItems],
+                                          uint32_t (&val)[kOsItems], uint32_t (&rank)[kOsItems],
+                                          uint32_t (&dig)[kOsItems],
+                                          uint32_t (*s_wcnt)[1 << BITS]) {
+    constexpr int BINS = 1 << BITS;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+    for (int i = 0; i < kOsItems; ++i) {
+        const int64_t idx = base + i * 64 + lane;
+        const int64_t ic = idx < n ? idx : n - 1;
+        key[i] = kin[ic];
+        val[i] = vin ? vin[ic] : (uint32_t)idx;
+    }
+#pragma unroll
+    for (int i = 0; i < kOsItems; ++i) {
+        const int64_t idx = base + i * 64 + lane;
+        const bool valid = idx < n;
+        const uint32_t d = (uint32_t)(key[i] >> shift) & (BINS - 1);
+        dig[i] = valid ? d : 0xFFFFFFFFu;
+        uint64_t peers = __ballot(valid);
+#pragma unroll
+        for (int b = 0; b < BITS; ++b) {
+            const uint64_t bb = __ballot((d >> b) & 1u);
+            peers &= ((d >> b) & 1u) ? bb : ~bb;
+        }
+        const uint32_t before = valid ? s_wcnt[w][d] : 0u;
+        rank[i] = before + (uint32_t)__popcll(peers & below);
+        if (valid && (peers & below) == 0) s_wcnt[w][d] = before + (uint32_t)__popcll(peers);
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// Reduce: digit counts of tile blockIdx.x into cnt[d * tiles + tile].
+template <typename K, int BITS>
+__global__ __launch_bounds__(kOsThreads) void k_rs_count(const K* __restrict__ kin, int64_t n,
+                                                         int shift, uint32_t* __restrict__ cnt,
+                                                         int64_t tiles) {
+    constexpr int BINS = 1 << BITS;
+    __shared__ uint32_t s_h[BINS];
+    for (int d = threadIdx.x; d < BINS; d += kOsThreads) s_h[d] = 0;
+    __syncthreads();
+    const int64_t base = (int64_t)blockIdx.x * kOsTile;
+#pragma unroll
+    for (int i = 0; i < kOsItems; ++i) {
+        const int64_t idx = base + i * kOsThreads + threadIdx.x;
+        if (idx < n) atomicAdd(&s_h[(uint32_t)(kin[idx] >> shift) & (BINS - 1)], 1u);
+    }
+    __syncthreads();
+    for (int d = threadIdx.x; d < BINS; d += kOsThreads) cnt[(int64_t)d * tiles + blockIdx.x] = s_h[d];
+}
+
+// Exclusive scan of segments of kScanSeg words in place; seg[blockIdx.x] = the
+// segment's total.
+__global__ __launch_bounds__(1024) void k_scan_segments(uint32_t* __restrict__ a, int64_t len,
+                                                        uint32_t* __restrict__ seg) {
+    __shared__ uint32_t s_w[16];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t base = (int64_t)blockIdx.x * kScanSeg + (int64_t)threadIdx.x * 4;
+    uint32_t v[4], t = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        v[j] = base + j < len ? a[base + j] : 0u;
+        t += v[j];
+    }
+    uint32_t inc = t;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t u = __shfl_up(inc, o);
+        if (lane >= o) inc += u;
+    }
+    if (lane == 63) s_w[w] = inc;
+    __syncthreads();
+    uint32_t run = inc - t;
+    for (int q = 0; q < w; ++q) run += s_w[q];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (base + j < len) a[base + j] = run;
+        run += v[j];
+    }
+    if (threadIdx.x == 1023) seg[blockIdx.x] = run;
+}
+
+// Exclusive scan of the segment totals in place (one block, any length).
+__global__ __launch_bounds__(1024) void k_scan_top(uint32_t* __restrict__ a, int64_t len) {
+    __shared__ uint32_t s_w[16];
+    __shared__ uint32_t s_carry;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (threadIdx.x == 0) s_carry = 0;
+    __syncthreads();
+    for (int64_t c0 = 0; c0 < len; c0 += 1024) {
+        const int64_t i = c0 + threadIdx.x;
+        const uint32_t v = i < len ? a[i] : 0u;
+        uint32_t inc = v;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t u = __shfl_up(inc, o);
+            if (lane >= o) inc += u;
+        }
+        if (lane == 63) s_w[w] = inc;
+        __syncthreads();
+        uint32_t before = s_carry;
+        for (int q = 0; q < w; ++q) before += s_w[q];
+        if (i < len) a[i] = before + inc - v;
+        __syncthreads();
+        if (threadIdx.x == 1023) s_carry = before + inc;
+        __syncthreads();
+    }
+}
+
+// Scatter: rank the tile as the onesweep pass does; each digit's run of the
+// tile starts at the scanned count table entry (plus its segment's prefix).
+template <typename K, int BITS>
+__global__ __launch_bounds__(kOsThreads) void k_rs_scatter(
+    const K* __restrict__ kin, const uint32_t* __restrict__ vin, K* __restrict__ kout,
+    uint32_t* __restrict__ vout, int64_t n, int shift, const uint32_t* __restrict__ cnt,
+    const uint32_t* __restrict__ seg, int64_t tiles) {
+    constexpr int BINS = 1 << BITS;
+    constexpr int DPT = BINS / kOsThreads;
+    __shared__ uint32_t s_wcnt[kOsWaves][BINS];
+    __shared__ uint32_t s_base[BINS];
+    const int tid = threadIdx.x, w = tid >> 6;
+#pragma unroll
+    for (int j = 0; j < DPT; ++j)
+#pragma unroll
+        for (int v = 0; v < kOsWaves; ++v) s_wcnt[v][tid * DPT + j] = 0;
+    __syncthreads();
+    const int64_t bid = blockIdx.x;
+    const int64_t base = bid * kOsTile + (int64_t)w * (kOsTile / kOsWaves);
+    K key[kOsItems];
+    uint32_t val[kOsItems], rank[kOsItems], dig[kOsItems];
+    rank_tile<K, BITS>(kin, vin, n, shift, base, key, val, rank, dig, s_wcnt);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < DPT; ++j) {
+        const int d = tid * DPT + j;
+        uint32_t run = 0;
+#pragma unroll
+        for (int v = 0; v < kOsWaves; ++v) {
+            const uint32_t c = s_wcnt[v][d];
+            s_wcnt[v][d] = run;
+            run += c;
+        }
+        const int64_t e = (int64_t)d * tiles + bid;
+        s_base[d] = cnt[e] + seg[e / kScanSeg];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kOsItems; ++i) {
+        const uint32_t d = dig[i];
+        if (d == 0xFFFFFFFFu) continue;
+        int64_t pos = (int64_t)s_base[d] + s_wcnt[w][d] + rank[i];
+        if (pos >= n) pos = n - 1;
+        kout[pos] = key[i];
+        vout[pos] = val[i];
+    }
+}
+
+template <typename K, int BITS>
+hipError_t launch_rs_pass(const K* kin, const uint32_t* vin, K* kout, uint32_t* vout, int64_t n,
+                          int shift, uint32_t* cnt, hipStream_t s) {
+    const int64_t tiles = (n + kOsTile - 1) / kOsTile;
+    const int64_t len = tiles * (1 << BITS);
+    const int64_t nseg = (len + kScanSeg - 1) / kScanSeg;
+    uint32_t* seg = cnt + len;
+    launch(k_rs_count<K, BITS>, (unsigned)tiles, kOsThreads, 0, s, kin, n, shift, cnt, tiles);
+    launch(k_scan_segments, (unsigned)nseg, 1024, 0, s, cnt, len, seg);
+    launch(k_scan_top, 1u, 1024, 0, s, seg, nseg);
+    launch(k_rs_scatter<K, BITS>, (unsigned)tiles, kOsThreads, 0, s, kin, vin, kout, vout, n, shift,
+           (const uint32_t*)cnt, (const uint32_t*)seg, tiles);
+    return hipGetLastError();
+}
+
 // Global digit histograms of every pass in one read of the keys.
 template <typename K>
 __global__ __launch_bounds__(kOsThreads) void k_key_hist(const K* __restrict__ keys, int64_t n,
@@ -245,6 +433,19 @@ hipError_t sort_impl(const K* keys_in, const uint32_t* vals_in, int64_t n, const
         if (epoch == 0) epoch = ++ws.epoch & 0x3FFFFFFFu;
         const uint32_t* h = hist + (size_t)p * bins;
         hipError_t e;
+        const int64_t tiles = (n + kOsTile - 1) / kOsTile;
+        if (tiles > kManyTiles && ws.cnt && ws.cnt_ints >= sort_scan_ints(n)) {
+            switch (plan.bits) {
+                case 8: e = launch_rs_pass<K, 8>(kcur, vcur, kdst[p & 1], vdst[p & 1], n, p * 8, ws.cnt, s); break;
+                case 9: e = launch_rs_pass<K, 9>(kcur, vcur, kdst[p & 1], vdst[p & 1], n, p * 9, ws.cnt, s); break;
+                case 10: e = launch_rs_pass<K, 10>(kcur, vcur, kdst[p & 1], vdst[p & 1], n, p * 10, ws.cnt, s); break;
+                default: e = launch_rs_pass<K, 11>(kcur, vcur, kdst[p & 1], vdst[p & 1], n, p * 11, ws.cnt, s); break;
+            }
+            if (e != hipSuccess) return e;
+            kcur = kdst[p & 1];
+            vcur = vdst[p & 1];
+            continue;
+        }
         switch (plan.bits) {
             case 8: e = launch_pass<K, 8>(kcur, vcur, kdst[p & 1], vdst[p & 1], n, p * 8, h, ws.look, ws.ticket, epoch, status, s); break;
             case 9: e = launch_pass<K, 9>(kcur, vcur, kdst[p & 1], vdst[p & 1], n, p * 9, h, ws.look, ws.ticket, epoch, status, s); break;
@@ -272,6 +473,13 @@ SortPlan sort_plan(int key_bits) {
 }
 
 int64_t sort_tiles(int64_t n) { return (n + kOsTile - 1) / kOsTile; }
+
+int64_t sort_scan_ints(int64_t n) {
+    const int64_t tiles = sort_tiles(n);
+    if (tiles <= kManyTiles) return 0;
+    const int64_t len = tiles * 2048;              // the widest digit (11 bits)
+    return len + (len + kScanSeg - 1) / kScanSeg;
+}
 
 size_t sort_look_bytes(int64_t n) {
     int64_t t = sort_tiles(n);

@@ -77,6 +77,10 @@ struct SortWork {
     uint64_t* look = nullptr;
     uint32_t* ticket = nullptr;
     uint32_t epoch = 0;
+    // many-tile sorts (reduce, then scan): per-(digit, tile) counts and the
+    // scan's per-segment sums, sized by sort_scan_ints(n) (nullptr: onesweep only)
+    uint32_t* cnt = nullptr;
+    int64_t cnt_ints = 0;
 };
 
 constexpr int kMaskBits = 27;
@@ -172,6 +176,8 @@ hipError_t launch_query_lookup(const void* keys, const uint32_t* vals, int64_t n
 SortPlan sort_plan(int key_bits);
 int64_t sort_tiles(int64_t n);
 size_t sort_look_bytes(int64_t n);
+// u32 words a many-tile sort of n keys needs in SortWork::cnt (0: onesweep)
+int64_t sort_scan_ints(int64_t n);
 hipError_t launch_key_hist(const void* keys, bool wide, int64_t n, const SortPlan& plan,
                            uint32_t* hist, hipStream_t s);
 hipError_t radix_sort_u32(const uint32_t* keys_in, const uint32_t* vals_in, int64_t n,

@@ -135,6 +135,7 @@ struct smc_map {
     int64_t n_in = 0;
     StrideGeom sgeom{};
     DevBuf ck0, ck1, ck2, cv0, cv1, chist, ucounts, ocoords, qcoords;
+    DevBuf scan;                      // count table of many-tile sorts
     // stage timers
     bool timing = false;
     std::vector<hipEvent_t> ev_pool;
@@ -369,8 +370,11 @@ static int strided_outputs(smc_map* m, const int32_t* coords, int64_t n, const G
     const SortPlan plan = sort_plan(bits);
     if (plan.passes * (1 << plan.bits) > kHistKeyInts)
         return fail(SMC_ERR_UNSUPPORTED, "output key sort needs %d bins", plan.passes * (1 << plan.bits));
-    SMC_HIP(launch_fill_i32(m->chist.as<int32_t>(), kHistKeyInts, 0, s));
-    SMC_HIP(launch_key_hist(m->ck0.p, true, n_cand, plan, m->chist.as<uint32_t>(), s));
+    // (a many-tile sort counts per tile itself: no global histogram needed)
+    if (sort_scan_ints(n_cand) == 0 || !m->ws.cnt) {
+        SMC_HIP(launch_fill_i32(m->chist.as<int32_t>(), kHistKeyInts, 0, s));
+        SMC_HIP(launch_key_hist(m->ck0.p, true, n_cand, plan, m->chist.as<uint32_t>(), s));
+    }
     const uint64_t* sorted = nullptr;
     const uint32_t* sv = nullptr;
     SMC_HIP(radix_sort_u64(m->ck0.as<uint64_t>(), nullptr, n_cand, plan, m->chist.as<uint32_t>(),
@@ -568,6 +572,16 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
          (rc = m->pair_slot.ensure((size_t)taps * cap * 4)) ||
          (rc = m->rowbase.ensure((size_t)(nn + 1) * 4))))
         return rc;
+    {
+        // the largest sort of the build: input keys, strided candidates or mask-sort items
+        int64_t big = nn;
+        if (n_cand > big) big = n_cand;
+        if (items > big) big = items;
+        const int64_t scan_ints = sort_scan_ints(big);
+        if (scan_ints > 0 && (rc = m->scan.ensure((size_t)scan_ints * 4))) return rc;
+        m->ws.cnt = scan_ints > 0 ? m->scan.as<uint32_t>() : nullptr;
+        m->ws.cnt_ints = scan_ints > 0 ? (int64_t)(m->scan.bytes / 4) : 0;
+    }
     if (m->look.bytes != look_before || look_before == 0)   // new table: epoch 0 everywhere
         SMC_HIP(launch_fill_i32(m->look.as<int32_t>(), (int64_t)(m->look.bytes / 4), 0, s));
     m->ws.look = m->look.as<uint64_t>();
