@@ -393,15 +393,16 @@ __global__ __launch_bounds__(kCThreads) void k_compact(
 }
 
 // Dense route: lookup and compaction in one kernel. Each thread looks up its
-// row's 27 cells as 9 (dx, dy) columns of 3 consecutive cells (z fastest),
+// row's 27 cells as 9 (dx, dy) columns of 3 consecutive cells (z fastest):
+// first their occupancy bits, then the row ids of the occupied ones;
 // writes the neighbour row to LDS and its mask; the chunk's neighbour rows go
 // to the table with coalesced stores, then the chunk is compacted.
 __global__ __launch_bounds__(kCThreads) void k_lookup_compact(
     const int32_t* __restrict__ coords, int64_t n, Geom g, const int32_t* __restrict__ grid,
-    int32_t* __restrict__ nbr, uint32_t* __restrict__ mask, int64_t cap, int tile_m, MapState* st,
-    int32_t* __restrict__ pair_in, int32_t* __restrict__ pair_out, int32_t* __restrict__ pair_slot,
-    int32_t* __restrict__ rowbase, uint64_t* __restrict__ look, uint32_t* ticket, uint32_t epoch,
-    uint32_t* status) {
+    const uint32_t* __restrict__ bits, int32_t* __restrict__ nbr, uint32_t* __restrict__ mask,
+    int64_t cap, int tile_m, MapState* st, int32_t* __restrict__ pair_in,
+    int32_t* __restrict__ pair_out, int32_t* __restrict__ pair_slot, int32_t* __restrict__ rowbase,
+    uint64_t* __restrict__ look, uint32_t* ticket, uint32_t epoch, uint32_t* status) {
     __shared__ CompactLds L;
     const int tid = threadIdx.x;
     if (tid == 0) L.bid = atomicAdd(ticket, 1u);
@@ -421,15 +422,33 @@ __global__ __launch_bounds__(kCThreads) void k_lookup_compact(
     // padded cell (1, 1, 0) instead, which lies inside the grid; their values are unused.
     const int64_t c0 = ok ? b * g.sz_b + (int64_t)(x + 1) * g.sz_x + (int64_t)(y + 1) * g.sz_y + z
                           : g.sz_x + g.sz_y;
+    // occupancy of the 9 (dx, dy) columns (3 bits each, two words per column) ...
+    uint32_t cb[9];
+#pragma unroll
+    for (int dx = 0; dx < 3; ++dx)
+#pragma unroll
+        for (int dy = 0; dy < 3; ++dy)
+            cb[3 * dx + dy] =
+                cell_bits(bits, c0 + (int64_t)(dx - 1) * g.sz_x + (int64_t)(dy - 1) * g.sz_y, 3);
+    // ... then row ids of the occupied cells only. Every tap issues its load; an
+    // empty one reads cell 0 (one line, cached for the whole launch), so no load
+    // is conditional.
+    const int64_t c_self = 0;
     int32_t v[kTaps];
 #pragma unroll
     for (int dx = 0; dx < 3; ++dx)
 #pragma unroll
-        for (int dy = 0; dy < 3; ++dy) {
-            const int32_t* p3 = grid + c0 + (int64_t)(dx - 1) * g.sz_x + (int64_t)(dy - 1) * g.sz_y;
+        for (int dy = 0; dy < 3; ++dy)
 #pragma unroll
-            for (int dz = 0; dz < 3; ++dz) v[9 * dx + 3 * dy + dz] = p3[dz];
-        }
+            for (int dz = 0; dz < 3; ++dz) {
+                const int k = 9 * dx + 3 * dy + dz;
+                if (k == kCentre) continue;
+                const bool on = (cb[3 * dx + dy] >> dz) & 1u;
+                const int64_t cc = c0 + (int64_t)(dx - 1) * g.sz_x + (int64_t)(dy - 1) * g.sz_y + dz;
+                v[k] = grid[on ? cc : c_self];
+                v[k] = on ? v[k] : -1;
+            }
+    v[kCentre] = (int32_t)row;
     uint32_t m = 0;
 #pragma unroll
     for (int k = 0; k < kTaps; ++k) {
@@ -617,14 +636,15 @@ hipError_t launch_compact(const uint32_t* mask, const int32_t* nbr, int64_t n, i
 }
 
 hipError_t launch_lookup_compact(const int32_t* coords, int64_t n, const Geom& g,
-                                 const int32_t* grid, int32_t* nbr, uint32_t* mask, int64_t cap,
+                                 const int32_t* grid, const uint32_t* bits, int32_t* nbr,
+                                 uint32_t* mask, int64_t cap,
                                  int tile_m, MapState* st, int32_t* pair_in, int32_t* pair_out,
                                  int32_t* pair_slot, int32_t* rowbase, SortWork& ws,
                                  uint32_t* status, hipStream_t s) {
     const uint32_t epoch = next_epoch(ws);
-    launch(k_lookup_compact, (unsigned)compact_chunks(n), kCThreads, 0, s, coords, n, g, grid, nbr,
-           mask, cap, tile_m, st, pair_in, pair_out, pair_slot, rowbase, ws.look, ws.ticket, epoch,
-           status);
+    launch(k_lookup_compact, (unsigned)compact_chunks(n), kCThreads, 0, s, coords, n, g, grid, bits,
+           nbr, mask, cap, tile_m, st, pair_in, pair_out, pair_slot, rowbase, ws.look, ws.ticket,
+           epoch, status);
     return hipGetLastError();
 }
 

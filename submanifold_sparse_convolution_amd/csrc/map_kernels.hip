@@ -109,13 +109,15 @@ __global__ __launch_bounds__(kBlock) void k_fill_i32(int32_t* p, int64_t n, int3
         p[i] = v;
 }
 
-// One thread per row: claim the row's grid cell and record it in cells. A
-// second claimant of a cell means two rows share coordinates. Thread i first
-// puts back to empty cell i of the previous dense build (other grid), so the
-// launch covers max(n, prev.n) threads.
+// One thread per row: set the row's occupancy bit (its previous value
+// flags a second row at the same coordinates), store the row id in the int32
+// grid and record the cell in cells. Thread i first clears the word of
+// occupancy bits that holds cell i of the previous dense build (other grid),
+// so the launch covers max(n, prev.n) threads.
 __global__ __launch_bounds__(kBlock) void k_dense_scatter(const int32_t* __restrict__ coords,
                                                           int64_t n, Geom g,
                                                           int32_t* __restrict__ grid,
+                                                          uint32_t* __restrict__ bits,
                                                           int32_t* __restrict__ cells,
                                                           MapState* st, NextRecord next,
                                                           PrevCells prev) {
@@ -123,7 +125,7 @@ __global__ __launch_bounds__(kBlock) void k_dense_scatter(const int32_t* __restr
     const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
     if (i < prev.n) {
         const int32_t c = prev.cells[i];
-        if (c >= 0) prev.grid[c] = -1;
+        if (c >= 0) prev.bits[c >> 5] = 0u;
     }
     if (i >= n) return;
     int b, x, y, z;
@@ -134,8 +136,10 @@ __global__ __launch_bounds__(kBlock) void k_dense_scatter(const int32_t* __restr
     }
     const int64_t cell = dense_cell(g, b, x, y, z);
     cells[i] = (int32_t)cell;
-    int old = atomicCAS(&grid[cell], -1, (int)i);
-    if (old != -1) atomicOr(&st->status, kStDuplicate);
+    const uint32_t bit = 1u << (cell & 31);
+    const uint32_t old = atomicOr(&bits[cell >> 5], bit);
+    if (old & bit) atomicOr(&st->status, kStDuplicate);
+    grid[cell] = (int32_t)i;
 }
 
 // Only the cleanup part of k_dense_scatter (a build that writes no grid).
@@ -143,7 +147,7 @@ __global__ __launch_bounds__(kBlock) void k_clear_cells(PrevCells prev) {
     const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
     if (i < prev.n) {
         const int32_t c = prev.cells[i];
-        if (c >= 0) prev.grid[c] = -1;
+        if (c >= 0) prev.bits[c >> 5] = 0u;
     }
 }
 
@@ -152,6 +156,7 @@ __global__ __launch_bounds__(kBlock) void k_clear_cells(PrevCells prev) {
 __global__ __launch_bounds__(kBlock) void k_dense_lookup(const int32_t* __restrict__ coords,
                                                          int64_t n, Geom g,
                                                          const int32_t* __restrict__ grid,
+                                                         const uint32_t* __restrict__ bits,
                                                          int32_t* __restrict__ nbr,
                                                          uint32_t* __restrict__ mask) {
     int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
@@ -163,7 +168,8 @@ __global__ __launch_bounds__(kBlock) void k_dense_lookup(const int32_t* __restri
         int b, x, y, z;
         if (load_rel(coords, row, g, b, x, y, z)) {
             int dx = k / 9 - 1, dy = (k / 3) % 3 - 1, dz = k % 3 - 1;
-            v = grid[dense_cell(g, b, x, y, z) + dx * g.sz_x + dy * g.sz_y + dz];
+            const int64_t c = dense_cell(g, b, x, y, z) + dx * g.sz_x + dy * g.sz_y + dz;
+            if ((bits[c >> 5] >> (c & 31)) & 1u) v = grid[c];
         }
         nbr[row * kTaps + k] = v;
     }
@@ -177,6 +183,7 @@ __global__ __launch_bounds__(kBlock) void k_dense_lookup(const int32_t* __restri
 __global__ __launch_bounds__(kBlock) void k_dense_lookup5(const int32_t* __restrict__ coords,
                                                           int64_t n, Geom g,
                                                           const int32_t* __restrict__ grid,
+                                                          const uint32_t* __restrict__ bits,
                                                           int32_t* __restrict__ nbr,
                                                           uint32_t* __restrict__ mask) {
     constexpr int kT = 125;
@@ -189,7 +196,8 @@ __global__ __launch_bounds__(kBlock) void k_dense_lookup5(const int32_t* __restr
         int b, x, y, z;
         if (load_rel(coords, row, g, b, x, y, z)) {
             const int dx = k / 25 - 2, dy = (k / 5) % 5 - 2, dz = k % 5 - 2;
-            v = grid[dense_cell(g, b, x, y, z) + dx * g.sz_x + dy * g.sz_y + dz];
+            const int64_t c = dense_cell(g, b, x, y, z) + dx * g.sz_x + dy * g.sz_y + dz;
+            if ((bits[c >> 5] >> (c & 31)) & 1u) v = grid[c];
         }
         nbr[row * kT + k] = v;
     }
@@ -343,10 +351,10 @@ hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s) {
 }
 
 hipError_t launch_dense_scatter(const int32_t* coords, int64_t n, const Geom& g, int32_t* grid,
-                                int32_t* cells, MapState* st, const NextRecord& next,
-                                const PrevCells& prev, hipStream_t s) {
+                                uint32_t* bits, int32_t* cells, MapState* st,
+                                const NextRecord& next, const PrevCells& prev, hipStream_t s) {
     launch(k_dense_scatter, blocks_for(n > prev.n ? n : prev.n), kBlock, 0, s, coords, n, g, grid,
-           cells, st, next, prev);
+           bits, cells, st, next, prev);
     return hipGetLastError();
 }
 
@@ -357,11 +365,13 @@ hipError_t launch_clear_cells(const PrevCells& prev, hipStream_t s) {
 }
 
 hipError_t launch_dense_lookup(const int32_t* coords, int64_t n, const Geom& g, const int32_t* grid,
-                               int32_t* nbr, uint32_t* mask, hipStream_t s) {
+                               const uint32_t* bits, int32_t* nbr, uint32_t* mask, hipStream_t s) {
     if (g.ksize == 5)
-        launch(k_dense_lookup5, blocks_for(n * 128), kBlock, 0, s, coords, n, g, grid, nbr, mask);
+        launch(k_dense_lookup5, blocks_for(n * 128), kBlock, 0, s, coords, n, g, grid, bits, nbr,
+               mask);
     else
-        launch(k_dense_lookup, blocks_for(n * 32), kBlock, 0, s, coords, n, g, grid, nbr, mask);
+        launch(k_dense_lookup, blocks_for(n * 32), kBlock, 0, s, coords, n, g, grid, bits, nbr,
+               mask);
     return hipGetLastError();
 }
 

@@ -120,20 +120,31 @@ struct NextRecord {
 struct PrevCells {
     const int32_t* cells = nullptr;   // grid cell of each row of that build (-1: none)
     int64_t n = 0;
-    int32_t* grid = nullptr;
+    uint32_t* bits = nullptr;         // occupancy bits of that build's grid
 };
+
+// Occupancy bits of len (<= 5) consecutive cells from c0 (bit j = cell c0 + j).
+__device__ inline uint32_t cell_bits(const uint32_t* __restrict__ bits, int64_t c0, int len) {
+    const int64_t w = c0 >> 5;
+    const uint64_t two = (uint64_t)bits[w] | ((uint64_t)bits[w + 1] << 32);
+    return (uint32_t)(two >> (c0 & 31)) & ((1u << len) - 1u);
+}
 
 // ---- map kernels (map_kernels.hip) ----
 hipError_t launch_state_init(MapState* st, uint32_t* hist, int hist_ints, hipStream_t s);
 hipError_t launch_bbox(const int32_t* coords, int64_t n, int ncols, MapState* st, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
+// Dense route: an int32 grid of row ids plus one occupancy bit per cell. A
+// cell's row id is only read when its bit is set, so the int32 grid needs no
+// initial fill and no reset; the bits of a build are cleared (whole words)
+// by the next build that uses the other grid. bits has 2 words of padding.
 hipError_t launch_dense_scatter(const int32_t* coords, int64_t n, const Geom& g, int32_t* grid,
-                                int32_t* cells, MapState* st, const NextRecord& next,
-                                const PrevCells& prev, hipStream_t s);
+                                uint32_t* bits, int32_t* cells, MapState* st,
+                                const NextRecord& next, const PrevCells& prev, hipStream_t s);
 hipError_t launch_clear_cells(const PrevCells& prev, hipStream_t s);
 // nbr [n, K^3]; mask [n] (K = 3) or [n, 4] words (K = 5): g.ksize decides.
 hipError_t launch_dense_lookup(const int32_t* coords, int64_t n, const Geom& g, const int32_t* grid,
-                               int32_t* nbr, uint32_t* mask, hipStream_t s);
+                               const uint32_t* bits, int32_t* nbr, uint32_t* mask, hipStream_t s);
 hipError_t launch_make_keys(const int32_t* coords, int64_t n, const Geom& g, bool wide, void* keys,
                             MapState* st, const NextRecord& next, hipStream_t s);
 hipError_t launch_sorted_lookup(const void* keys, const uint32_t* vals, int64_t n, const Geom& g,
@@ -216,7 +227,8 @@ hipError_t launch_compact(const uint32_t* mask, const int32_t* nbr, int64_t n, i
 // Dense route: neighbour lookup and compaction in one kernel (also writes nbr
 // and mask).
 hipError_t launch_lookup_compact(const int32_t* coords, int64_t n, const Geom& g,
-                                 const int32_t* grid, int32_t* nbr, uint32_t* mask, int64_t cap,
+                                 const int32_t* grid, const uint32_t* bits, int32_t* nbr,
+                                 uint32_t* mask, int64_t cap,
                                  int tile_m, MapState* st, int32_t* pair_in, int32_t* pair_out,
                                  int32_t* pair_slot, int32_t* rowbase, SortWork& ws,
                                  uint32_t* status, hipStream_t s);

@@ -107,8 +107,9 @@ struct smc_map {
     // all -1 between them. cells[i] records the cell of every row of the last build
     // on grid i; the next dense build (on the other grid) or, before a sorted build,
     // a small kernel puts those cells back to -1.
-    DevBuf grid[2];
-    int64_t grid_clean_cells[2] = {0, 0};   // prefix of each grid known to be -1
+    DevBuf grid[2];                          // int32 row ids (read only where a bit is set)
+    DevBuf bits[2];                          // one occupancy bit per cell (+2 words)
+    int64_t bits_clean_words[2] = {0, 0};    // prefix of each bitmap known to be zero
     DevBuf cells[2];
     int next_grid = 0;                       // grid of the next dense build
     PrevCells stale;                         // cells not yet put back (stale.n = 0: none)
@@ -206,19 +207,21 @@ int wait_build(smc_map* m) {
 }
 
 int ensure_grid(smc_map* m, int gi, int64_t cells, hipStream_t s) {
-    size_t bytes = (size_t)cells * 4;
+    const int64_t words = cells / 32 + 2;
     DevBuf& grid = m->grid[gi];
-    if (bytes > grid.bytes) {
-        if (m->stale.n > 0 && m->stale.grid == grid.as<int32_t>()) m->stale = PrevCells();
-        int rc = grid.ensure(bytes);
-        if (rc) return rc;
-        m->grid_clean_cells[gi] = 0;
+    DevBuf& bits = m->bits[gi];
+    int rc = grid.ensure((size_t)cells * 4);       // never filled: read only under a set bit
+    if (rc) return rc;
+    if ((size_t)words * 4 > bits.bytes) {
+        if (m->stale.n > 0 && m->stale.bits == bits.as<uint32_t>()) m->stale = PrevCells();
+        if ((rc = bits.ensure((size_t)words * 4))) return rc;
+        m->bits_clean_words[gi] = 0;
     }
-    if (m->grid_clean_cells[gi] < cells) {
-        // fill the whole allocation once; later builds only clear what they used
-        int64_t all = (int64_t)(grid.bytes / 4);
-        SMC_HIP(launch_fill_i32(grid.as<int32_t>(), all, -1, s));
-        m->grid_clean_cells[gi] = all;
+    if (m->bits_clean_words[gi] < words) {
+        // zero the whole allocation once; later builds only clear the words they used
+        const int64_t all = (int64_t)(bits.bytes / 4);
+        SMC_HIP(launch_fill_i32(bits.as<int32_t>(), all, 0, s));
+        m->bits_clean_words[gi] = all;
     }
     return SMC_OK;
 }
@@ -335,12 +338,13 @@ int smc_map_destroy(smc_map* m) {
         (void)hipGetDevice(&cur);
         (void)hipSetDevice(m->device);
         (void)hipDeviceSynchronize();
-        DevBuf* bufs[] = {&m->state, &m->grid[0], &m->grid[1], &m->cells[0], &m->cells[1],
-                          &m->keys0, &m->keys1, &m->keys2,
+        DevBuf* bufs[] = {&m->state, &m->grid[0], &m->grid[1], &m->bits[0], &m->bits[1],
+                          &m->cells[0], &m->cells[1], &m->keys0, &m->keys1, &m->keys2,
                           &m->vals0, &m->vals1, &m->hist, &m->look, &m->ticket, &m->nbr,
-                          &m->mask, &m->mkey0, &m->mkey1, &m->mval0, &m->mval1,
+                          &m->mask, &m->mkey0, &m->mkey1, &m->mval0, &m->mval1, &m->okeys,
                           &m->pair_in, &m->pair_out, &m->pair_slot, &m->rowbase, &m->part,
-                          &m->zrow};
+                          &m->zrow, &m->ck0, &m->ck1, &m->ck2, &m->cv0, &m->cv1, &m->chist,
+                          &m->ucounts, &m->ocoords, &m->qcoords, &m->scan};
         for (DevBuf* b : bufs) b->release();
         for (auto& v : m->ev_open)
             for (auto& pr : v) {
@@ -600,17 +604,18 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
                 (rc = m->cells[gi].ensure((size_t)nn * 4)))
                 return rc;
             int32_t* grid = m->grid[gi].as<int32_t>();
-            SMC_HIP(launch_dense_scatter(coords, n, g, grid, m->cells[gi].as<int32_t>(), st, next,
-                                         m->stale, s));
+            uint32_t* bits = m->bits[gi].as<uint32_t>();
+            SMC_HIP(launch_dense_scatter(coords, n, g, grid, bits, m->cells[gi].as<int32_t>(), st,
+                                         next, m->stale, s));
             m->slot_clean[slot ^ 1] = true;
             m->stale.cells = m->cells[gi].as<int32_t>();
             m->stale.n = n;
-            m->stale.grid = grid;
+            m->stale.bits = bits;
             m->next_grid = gi ^ 1;
             if (fused) {
                 t_nb.finish();
                 StageTimer t_cp(m, SMC_STAGE_COMPACT, s);
-                SMC_HIP(launch_lookup_compact(coords, n, g, grid, nbr, mask, cap, kTileM, st,
+                SMC_HIP(launch_lookup_compact(coords, n, g, grid, bits, nbr, mask, cap, kTileM, st,
                                               m->pair_in.as<int32_t>(), m->pair_out.as<int32_t>(),
                                               m->pair_slot.as<int32_t>(),
                                               m->rowbase.as<int32_t>(), m->ws, status, s));
@@ -619,9 +624,10 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
                 if ((rc = strided_outputs(m, coords, n, g, sg, st, status, s, &rows))) return rc;
                 Geom gq = g;                          // query points: [M, 4] in input coordinates
                 gq.ncols = 4;
-                SMC_HIP(launch_dense_lookup(m->qcoords.as<int32_t>(), rows, gq, grid, nbr, mask, s));
+                SMC_HIP(launch_dense_lookup(m->qcoords.as<int32_t>(), rows, gq, grid, bits, nbr,
+                                            mask, s));
             } else {
-                SMC_HIP(launch_dense_lookup(coords, n, g, grid, nbr, mask, s));
+                SMC_HIP(launch_dense_lookup(coords, n, g, grid, bits, nbr, mask, s));
             }
         } else {
             if (m->stale.n > 0) {             // the last dense build's cells
