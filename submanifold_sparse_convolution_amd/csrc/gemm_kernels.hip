@@ -474,12 +474,13 @@ __global__ __launch_bounds__(kGemmThreads, STREAM ? 1 : 2) void k_gemm_centre(
 template <int NBW, bool STREAM>
 constexpr size_t gemm_lds_bytes() { return (STREAM ? 2 : 1) * (size_t)kChunk * NBW * 64 * 16; }
 
-// Row fragments per wave: wide inputs reuse each streamed weight chunk over
-// more rows (only with 16-byte row loads, which keep the register budget);
-// narrow ones keep more, smaller tiles in flight (the pair lists of a
-// sparse scan hold few pairs per tap).
-inline int mw_for(int c_in) { return c_in >= 256 && (c_in & 7) == 0 ? 4 : 2; }
-inline int mw_nc_for(int c_in) { return c_in >= 256 && (c_in & 7) == 0 ? 4 : 1; }
+// Row fragments per wave. Streamed (C_in > 128) tiles use 2: measured on the
+// C = 512 set, 4 fragments (more weight reuse per chunk) left too few blocks
+// to cover each block's serial chain of chunk loads and the slab epilogue
+// (centre 48 -> 38 us, off-centre 31 -> 24 us with 2). One-chunk slabs keep 2
+// (centre) and 1 (off-centre: the pair lists of a sparse scan are short).
+inline int mw_for(int /*c_in*/) { return 2; }
+inline int mw_nc_for(int c_in) { return (c_in + 31) / 32 > kChunk && (c_in & 7) == 0 ? 2 : 1; }
 
 // Lets a kernel take `bytes` of dynamic LDS (once per kernel; the default cap
 // is 64 KiB including the kernel's static LDS).
@@ -506,8 +507,8 @@ void launch_nc(dim3 grid, hipStream_t s, int mw, const uint16_t* x, int c_in, in
                const u32x4* wp, int n_wt, int c_out, int taps, const int32_t* pi,
                const int32_t* ps, const MapState* st, int64_t cap, int64_t n, float* part) {
     const bool vec = (c_in & 7) == 0;
-    if (mw == 4)                                   // mw_nc_for: wide, 16-byte row loads
-        launch_nc_t<NBW, 4, true, true>(grid, s, x, c_in, steps, wp, n_wt, c_out, taps, pi, ps, st, cap, n, part);
+    if (mw == 2)                                   // mw_nc_for: streamed, 16-byte row loads
+        launch_nc_t<NBW, 2, true, true>(grid, s, x, c_in, steps, wp, n_wt, c_out, taps, pi, ps, st, cap, n, part);
     else if (steps > kChunk)
         launch_nc_t<NBW, 1, false, true>(grid, s, x, c_in, steps, wp, n_wt, c_out, taps, pi, ps, st, cap, n, part);
     else if (vec)
@@ -542,8 +543,9 @@ void launch_centre(dim3 grid, hipStream_t s, int mw, bool out_f32, const uint16_
                    int steps, const u32x4* wp, int n_wt, int c_out, int centre,
                    const int32_t* rowbase, int64_t n, const float* part, void* y, int relu) {
     const bool vec = (c_in & 7) == 0;
-    if (mw == 4)                                   // mw_for: wide, 16-byte row loads
-        launch_centre_mw<NBW, 4, true, true>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, centre, rowbase, n, part, y, relu);
+    (void)mw;
+    if (steps > kChunk && vec)                     // streamed, 16-byte row loads
+        launch_centre_mw<NBW, 2, true, true>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, centre, rowbase, n, part, y, relu);
     else if (steps > kChunk)
         launch_centre_mw<NBW, 2, false, true>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, centre, rowbase, n, part, y, relu);
     else if (vec)
