@@ -477,9 +477,12 @@ constexpr size_t gemm_lds_bytes() { return (STREAM ? 2 : 1) * (size_t)kChunk * N
 // Row fragments per wave. Streamed (C_in > 128) tiles use 2: measured on the
 // C = 512 set, 4 fragments (more weight reuse per chunk) left too few blocks
 // to cover each block's serial chain of chunk loads and the slab epilogue
-// (centre 48 -> 38 us, off-centre 31 -> 24 us with 2). One-chunk slabs keep 2
-// (centre) and 1 (off-centre: the pair lists of a sparse scan are short).
-inline int mw_for(int /*c_in*/) { return 2; }
+// (centre 48 -> 38 us, off-centre 31 -> 24 us with 2). One-chunk slabs with
+// 16-byte row loads use 1: twice the blocks, two per CU, hide the same chain
+// (centre at C = 128: LiDAR 11.0 -> 9.4 us, the 91k-row set 22.5 -> 17.6 us).
+// The off-centre GEMM uses 1 there too (the pair lists of a sparse scan are
+// short).
+inline int mw_for(int c_in) { return (c_in + 31) / 32 <= kChunk && (c_in & 7) == 0 ? 1 : 2; }
 inline int mw_nc_for(int c_in) { return (c_in + 31) / 32 > kChunk && (c_in & 7) == 0 ? 2 : 1; }
 
 // Lets a kernel take `bytes` of dynamic LDS (once per kernel; the default cap
@@ -549,7 +552,7 @@ void launch_centre(dim3 grid, hipStream_t s, int mw, bool out_f32, const uint16_
     else if (steps > kChunk)
         launch_centre_mw<NBW, 2, false, true>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, centre, rowbase, n, part, y, relu);
     else if (vec)
-        launch_centre_mw<NBW, 2, true, false>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, centre, rowbase, n, part, y, relu);
+        launch_centre_mw<NBW, 1, true, false>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, centre, rowbase, n, part, y, relu);
     else
         launch_centre_mw<NBW, 2, false, false>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, centre, rowbase, n, part, y, relu);
 }
