@@ -16,6 +16,8 @@
 // the pair's product, and rowbase[i] is the first slab row of output row i.
 // The centre-tap GEMM then sums each row's slab rows in its epilogue: no
 // atomics and no accumulator to clear.
+#include <atomic>
+
 #include "smc_internal.h"
 
 namespace smc {
@@ -74,15 +76,19 @@ __device__ inline uint32_t lookback(uint64_t* look, int stride, int d, int64_t p
 // Prefix of column k (k < NC) over blocks pb, pb-1, ..., read by the whole
 // block: thread t < kLanes NC covers column t % NC and every kLanes-th
 // predecessor starting at pb - t / NC, W of them per round trip (kLanes W
-// predecessors per column per round; 9 lanes for 28 columns, 2 for 126). A round finds, per column, the nearest entry that
-// holds an inclusive prefix (LDS minimum of the distance), and sums the
-// entries up to and including it; columns without one go on to the next
-// round. Every thread of the block must call this. The result is in
-// s_sum[k] on return.
-template <int NC, int W, int kLanes = 9>
+// predecessors per column per round). A round finds, per column, the nearest
+// entry that holds an inclusive prefix (LDS minimum of the distance), and
+// sums the entries up to and including it; columns without one go on to the
+// next round. Two barriers per round: the distance minima and the "some
+// column still open" flag alternate between two LDS slots by round parity,
+// so a slot is reset only after every thread has read it. Every thread of the
+// block must call this. The result is in s_sum[k] on return.
+template <int NC, int W, int kLanes>
 __device__ void block_lookback(uint64_t* look, int64_t pb, uint32_t epoch, uint32_t* status,
-                               uint32_t* s_sum, uint32_t* s_near, uint32_t* s_done) {
+                               uint32_t* s_sum, uint32_t* s_done) {
     static_assert(kLanes * NC <= 256, "one thread per (column, lane)");
+    __shared__ uint32_t s_near[2][NC];
+    __shared__ uint32_t s_open[2];
     const int tid = threadIdx.x;
     const int k = tid % NC, j0 = tid / NC;
     const bool active = tid < kLanes * NC;
@@ -90,12 +96,12 @@ __device__ void block_lookback(uint64_t* look, int64_t pb, uint32_t epoch, uint3
     if (tid < NC) {
         s_sum[tid] = 0;
         s_done[tid] = pb < 0 ? 1u : 0u;
+        s_near[0][tid] = 0xFFFFFFFFu;
     }
     __syncthreads();
     uint32_t spins = 0;
-    for (int64_t top = pb; top >= 0; top -= kLanes * W) {
-        if (tid < NC) s_near[tid] = 0xFFFFFFFFu;
-        __syncthreads();
+    int r = 0;
+    for (int64_t top = pb; top >= 0; top -= kLanes * W, r ^= 1) {
         const bool go = active && !s_done[k];
         uint64_t e[W];
         uint32_t near = 0xFFFFFFFFu;
@@ -121,9 +127,10 @@ __device__ void block_lookback(uint64_t* look, int64_t pb, uint32_t epoch, uint3
             }
             if (((e[j] >> 32) & 3u) == kIncl) near = min(near, (uint32_t)(top - idx));
         }
-        if (go && near != 0xFFFFFFFFu) atomicMin(&s_near[k], near);
+        if (go && near != 0xFFFFFFFFu) atomicMin(&s_near[r][k], near);
+        if (tid == 0) s_open[r] = 0u;
         __syncthreads();
-        const uint32_t lim = go ? s_near[k] : 0u;
+        const uint32_t lim = go ? s_near[r][k] : 0u;
         uint32_t part = 0;
 #pragma unroll
         for (int j = 0; j < W; ++j) {
@@ -131,14 +138,40 @@ __device__ void block_lookback(uint64_t* look, int64_t pb, uint32_t epoch, uint3
             if (go && idx >= 0 && (uint32_t)(top - idx) <= lim) part += (uint32_t)e[j];
         }
         if (part) atomicAdd(&s_sum[k], part);
+        if (tid < NC) {
+            if (!s_done[tid]) {
+                if (s_near[r][tid] != 0xFFFFFFFFu || top - kLanes * W < 0)
+                    s_done[tid] = 1u;
+                else
+                    s_open[r] = 1u;
+            }
+            s_near[r ^ 1][tid] = 0xFFFFFFFFu;     // the next round's slot
+        }
         __syncthreads();
-        if (tid < NC && !s_done[tid] && (s_near[tid] != 0xFFFFFFFFu || top - kLanes * W < 0))
-            s_done[tid] = 1u;
-        __syncthreads();
-        bool all = true;
-        for (int q = 0; q < NC; ++q) all = all && s_done[q];
-        if (all) break;
+        if (!s_open[r]) break;
     }
+}
+
+// Exclusive prefix over the wave's lanes of a value below 2^B, from one
+// ballot per bit plane: the count of lower lanes with bit b set, times 2^b.
+// The wave total comes back in *total.
+template <int B>
+__device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, uint32_t* total) {
+    uint32_t excl = 0, tot = 0;
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        const uint64_t m = __ballot((v >> b) & 1u);
+        excl += __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u)) << b;
+        tot += (uint32_t)__popcll(m) << b;
+    }
+    *total = tot;
+    return excl;
+}
+
+// Count of lower lanes of the wave whose bit is set in m.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
 // One read of the masks: digit histograms of every mask-sort pass and pairs
@@ -220,6 +253,20 @@ __global__ __launch_bounds__(kHThreads) void k_mask_hist(const uint32_t* __restr
         atomicAdd(&group_rows[threadIdx.x], (int32_t)s_grp[threadIdx.x]);
 }
 
+// Chunk of this block. A chunk waits only on lower chunks. When the whole
+// grid fits on the device at once (by_index), every block gets dispatched
+// whatever the order, so the chunk is the block index; otherwise a ticket
+// taken on arrival orders the chunks by dispatch, so every chunk a block waits
+// on belongs to a block that is already running. The ticket is reset by the
+// last chunk's block.
+__device__ __forceinline__ uint32_t chunk_of_block(bool by_index, uint32_t* ticket,
+                                                   uint32_t* s_slot) {
+    if (by_index) return blockIdx.x;
+    if (threadIdx.x == 0) *s_slot = atomicAdd(ticket, 1u);
+    __syncthreads();
+    return *s_slot;
+}
+
 // LDS of one compaction chunk.
 struct CompactLds {
     uint32_t bid;
@@ -227,7 +274,7 @@ struct CompactLds {
     uint32_t pre[kTaps + 1];                      // counts of earlier chunks
     uint32_t loc[kTaps + 1];                      // chunk-local start of each tap's pairs
     uint32_t tot[kTaps + 1];                      // the chunk's own counts
-    uint32_t near_[kTaps + 1], done[kTaps + 1];   // look-back scratch
+    uint32_t done[kTaps + 1];                     // look-back scratch
     int32_t nb[kCChunk * kTaps];                  // the chunk's neighbour rows
     uint16_t list[kCChunk * kTaps];               // (row | tap << 8) in output order
     uint32_t m[kCChunk], rb[kCChunk];
@@ -237,7 +284,9 @@ struct CompactLds {
 // L.nb filled): per-tap counts, look-back over earlier chunks, the chunk's
 // pairs listed in LDS as (row, tap) entries in output order, then written out
 // with consecutive threads on consecutive pair positions. The last chunk
-// publishes the totals. Starts and ends with all threads in step.
+// publishes the totals. With nbr_out, the chunk's neighbour rows are stored
+// there (coalesced) between publishing the counts and the look-back, where
+// the block would otherwise wait. Starts and ends with all threads in step.
 __device__ __forceinline__ void compact_chunk(CompactLds& L, uint32_t m, uint32_t bid, int64_t n,
                                               int64_t cap, int tile_m, MapState* st,
                                               int32_t* __restrict__ pair_in,
@@ -245,12 +294,11 @@ __device__ __forceinline__ void compact_chunk(CompactLds& L, uint32_t m, uint32_
                                               int32_t* __restrict__ pair_slot,
                                               int32_t* __restrict__ rowbase,
                                               uint64_t* __restrict__ look, uint32_t epoch,
-                                              uint32_t* status) {
+                                              uint32_t* status, int32_t* __restrict__ nbr_out) {
     constexpr int kCols = kTaps + 1;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int64_t base0 = (int64_t)bid * kCChunk;
     const int64_t row = base0 + tid;
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     const uint32_t deg = m ? (uint32_t)__popc(m & ~(1u << kCentre)) : 0u;
     // per-wave count of each tap (lane k keeps tap k) and of slab rows (lane kTaps)
     uint32_t cnt = 0;
@@ -259,13 +307,8 @@ __device__ __forceinline__ void compact_chunk(CompactLds& L, uint32_t m, uint32_
         const uint32_t c = (uint32_t)__popcll(__ballot((m >> k) & 1u));
         if (lane == k) cnt = c;
     }
-    uint32_t incl = deg;                          // inclusive wave scan of the slab rows
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t t = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += t;
-    }
-    const uint32_t wave_slab = __shfl(incl, 63, 64);
+    uint32_t wave_slab;                           // slab rows of the wave's earlier rows
+    const uint32_t excl = wave_excl_scan<5>(deg, &wave_slab);
     if (lane < kTaps) L.wc[w][lane] = cnt;
     if (lane == kTaps) L.wc[w][kTaps] = wave_slab;
     L.m[tid] = m;
@@ -284,7 +327,23 @@ __device__ __forceinline__ void compact_chunk(CompactLds& L, uint32_t m, uint32_
                            lb_pack(epoch, bid == 0 ? kIncl : kAgg, run), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
-    block_lookback<kCols, 8>(look, (int64_t)bid - 1, epoch, status, L.pre, L.near_, L.done);
+    if (nbr_out) {                                // neighbour rows out, coalesced
+        const int4* nb4 = reinterpret_cast<const int4*>(L.nb);
+        int4* dst = reinterpret_cast<int4*>(nbr_out + base0 * kTaps);
+        const int64_t q_end = ((n - base0) * kTaps + 3) / 4;      // words holding rows < n
+        int4 t4[kCNbrPer];                        // all LDS reads first, then the stores
+#pragma unroll
+        for (int j = 0; j < kCNbrPer; ++j) {
+            const int q = tid + j * kCThreads;
+            t4[j] = nb4[q < kCNbrVec ? q : 0];
+        }
+#pragma unroll
+        for (int j = 0; j < kCNbrPer; ++j) {
+            const int q = tid + j * kCThreads;
+            if (q < kCNbrVec && q < q_end) dst[q] = t4[j];
+        }
+    }
+    block_lookback<kCols, 16, 9>(look, (int64_t)bid - 1, epoch, status, L.pre, L.done);
     if (tid < kCols) {
         const int k = tid;
         const uint32_t run = L.tot[k];
@@ -306,34 +365,40 @@ __device__ __forceinline__ void compact_chunk(CompactLds& L, uint32_t m, uint32_
         }
     }
     __syncthreads();
-    if (tid == 0) {                               // chunk-local tap starts, totals
-        uint32_t loc = 0;
-        int32_t p = 0, padded = 0;
-        for (int k = 0; k < kTaps; ++k) {
-            L.loc[k] = loc;
-            loc += L.tot[k];
-            const int32_t c = (int32_t)(L.pre[k] + L.tot[k]);
-            p += c;
-            padded += (c + tile_m - 1) / tile_m * tile_m;
-        }
-        L.loc[kTaps] = loc;
-        if (bid == gridDim.x - 1) {
-            st->totals[0] = p;
-            st->totals[1] = padded;
-            st->totals[2] = padded / tile_m;
+    if (tid < 64) {                               // wave 0, lane k: tap k's chunk-local start
+        const int k = tid;
+        const uint32_t t = k < kTaps ? L.tot[k] : 0u;             // at most kCChunk
+        uint32_t all;
+        const uint32_t loc = wave_excl_scan<9>(t, &all);
+        if (k <= kTaps) L.loc[k] = loc;                           // lane kTaps: the chunk's pairs
+        if (bid == gridDim.x - 1) {               // the last chunk: pairs and padded tiles
+            int32_t c = k < kTaps ? (int32_t)(L.pre[k] + t) : 0;
+            int32_t padded = (c + tile_m - 1) / tile_m * tile_m;
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                c += __shfl_xor(c, o, 64);
+                padded += __shfl_xor(padded, o, 64);
+            }
+            if (k == 0) {
+                st->totals[0] = c;
+                st->totals[1] = padded;
+                st->totals[2] = padded / tile_m;
+            }
         }
     }
     // first slab row of the row
-    const uint32_t rb = L.pre[kTaps] + L.wc[w][kTaps] + incl - deg;
+    const uint32_t rb = L.pre[kTaps] + L.wc[w][kTaps] + excl;
     if (row < n) rowbase[row] = (int32_t)rb;
     L.rb[tid] = rb;
     __syncthreads();
-    // list the chunk's pairs in output order: tap-major, rows ascending
+    // list the chunk's pairs in output order: tap-major, rows ascending. Lane k
+    // holds the wave's first list slot of tap k; the loop reads it with readlane.
+    const uint32_t first = lane < kTaps ? L.loc[lane] + L.wc[w][lane] : 0u;
 #pragma unroll
     for (int k = 0; k < kTaps; ++k) {
         const uint64_t b = __ballot((m >> k) & 1u);
-        if ((m >> k) & 1u)
-            L.list[L.loc[k] + L.wc[w][k] + (uint32_t)__popcll(b & below)] = (uint16_t)(tid | (k << 8));
+        const uint32_t f = (uint32_t)__builtin_amdgcn_readlane((int)first, k);
+        if ((m >> k) & 1u) L.list[f + lanes_below(b)] = (uint16_t)(tid | (k << 8));
     }
     __syncthreads();
     // write them out: entry p of tap k goes to k cap + (pairs of k in earlier chunks) + its rank
@@ -360,12 +425,10 @@ __global__ __launch_bounds__(kCThreads) void k_compact(
     const uint32_t* __restrict__ mask, const int32_t* __restrict__ nbr, int64_t n, int64_t cap,
     int tile_m, MapState* st, int32_t* __restrict__ pair_in, int32_t* __restrict__ pair_out,
     int32_t* __restrict__ pair_slot, int32_t* __restrict__ rowbase, uint64_t* __restrict__ look,
-    uint32_t* ticket, uint32_t epoch, uint32_t* status) {
+    uint32_t* ticket, bool by_index, uint32_t epoch, uint32_t* status) {
     __shared__ CompactLds L;
     const int tid = threadIdx.x;
-    if (tid == 0) L.bid = atomicAdd(ticket, 1u);
-    __syncthreads();
-    const uint32_t bid = L.bid;
+    const uint32_t bid = chunk_of_block(by_index, ticket, &L.bid);
     const int64_t base0 = (int64_t)bid * kCChunk;
     const int64_t row = base0 + tid;
     // mask, neighbour rows (whole 16-byte words; the table is padded so the last word
@@ -388,26 +451,25 @@ __global__ __launch_bounds__(kCThreads) void k_compact(
         if (q < kCNbrVec) nb4[q] = nv4[j];
     }
     compact_chunk(L, row < n ? mv : 0u, bid, n, cap, tile_m, st, pair_in, pair_out, pair_slot,
-                  rowbase, look, epoch, status);
-    if (bid == gridDim.x - 1 && tid == 0) atomicExch(ticket, 0u);
+                  rowbase, look, epoch, status, nullptr);
+    if (!by_index && bid == gridDim.x - 1 && tid == 0) atomicExch(ticket, 0u);
 }
 
 // Dense route: lookup and compaction in one kernel. Each thread looks up its
 // row's 27 cells as 9 (dx, dy) columns of 3 consecutive cells (z fastest):
 // first their occupancy bits, then the row ids of the occupied ones;
-// writes the neighbour row to LDS and its mask; the chunk's neighbour rows go
-// to the table with coalesced stores, then the chunk is compacted.
+// writes the neighbour row to LDS and its mask, then the chunk is compacted
+// (which also stores the chunk's neighbour rows to the table, coalesced).
 __global__ __launch_bounds__(kCThreads) void k_lookup_compact(
     const int32_t* __restrict__ coords, int64_t n, Geom g, const int32_t* __restrict__ grid,
     const uint32_t* __restrict__ bits, int32_t* __restrict__ nbr, uint32_t* __restrict__ mask,
     int64_t cap, int tile_m, MapState* st, int32_t* __restrict__ pair_in,
     int32_t* __restrict__ pair_out, int32_t* __restrict__ pair_slot, int32_t* __restrict__ rowbase,
-    uint64_t* __restrict__ look, uint32_t* ticket, uint32_t epoch, uint32_t* status) {
+    uint64_t* __restrict__ look, uint32_t* ticket, bool by_index, uint32_t epoch,
+    uint32_t* status) {
     __shared__ CompactLds L;
     const int tid = threadIdx.x;
-    if (tid == 0) L.bid = atomicAdd(ticket, 1u);
-    __syncthreads();
-    const uint32_t bid = L.bid;
+    const uint32_t bid = chunk_of_block(by_index, ticket, &L.bid);
     const int64_t base0 = (int64_t)bid * kCChunk;
     const int64_t row = base0 + tid;
     const int64_t rc = row < n ? row : n - 1;
@@ -458,16 +520,9 @@ __global__ __launch_bounds__(kCThreads) void k_lookup_compact(
     }
     if (row < n) mask[row] = m;
     __syncthreads();
-    {                                             // neighbour rows out, coalesced
-        const int4* nb4 = reinterpret_cast<const int4*>(L.nb);
-        int4* dst = reinterpret_cast<int4*>(nbr + base0 * kTaps);
-        const int64_t q_end = ((n - base0) * kTaps + 3) / 4;      // words holding rows < n
-        for (int j = tid; j < kCNbrVec; j += kCThreads)
-            if (j < q_end) dst[j] = nb4[j];
-    }
     compact_chunk(L, m, bid, n, cap, tile_m, st, pair_in, pair_out, pair_slot, rowbase, look,
-                  epoch, status);
-    if (bid == gridDim.x - 1 && tid == 0) atomicExch(ticket, 0u);
+                  epoch, status, nbr);
+    if (!by_index && bid == gridDim.x - 1 && tid == 0) atomicExch(ticket, 0u);
 }
 
 // Compaction for the 5 x 5 x 5 kernel: 125 taps, masks of 4 words. One row
@@ -482,21 +537,18 @@ __global__ __launch_bounds__(kCThreads) void k_compact5(
     const uint32_t* __restrict__ mask, const int32_t* __restrict__ nbr, int64_t n, int64_t cap,
     int tile_m, MapState* st, int32_t* __restrict__ pair_in, int32_t* __restrict__ pair_out,
     int32_t* __restrict__ pair_slot, int32_t* __restrict__ rowbase, uint64_t* __restrict__ look,
-    uint32_t* ticket, uint32_t epoch, uint32_t* status) {
+    uint32_t* ticket, bool by_index, uint32_t epoch, uint32_t* status) {
     __shared__ uint32_t s_bid;
     __shared__ uint32_t s_wc[kCWaves][kK5Cols];   // per-wave counts, then offsets in the chunk
-    __shared__ uint32_t s_pre[kK5Cols], s_tot[kK5Cols], s_near[kK5Cols], s_done[kK5Cols];
+    __shared__ uint32_t s_pre[kK5Cols], s_tot[kK5Cols], s_done[kK5Cols];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    if (tid == 0) s_bid = atomicAdd(ticket, 1u);
-    __syncthreads();
-    const uint32_t bid = s_bid;
+    const uint32_t bid = chunk_of_block(by_index, ticket, &s_bid);
     const int64_t row = (int64_t)bid * kCChunk + tid;
     const bool valid = row < n;
     const int64_t rc = valid ? row : n - 1;
     uint32_t mw[kMaxMaskWords];
 #pragma unroll
     for (int q = 0; q < kMaxMaskWords; ++q) mw[q] = valid ? mask[rc * kMaxMaskWords + q] : 0u;
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     uint32_t pop = 0;
 #pragma unroll
     for (int q = 0; q < kMaxMaskWords; ++q) pop += (uint32_t)__popc(mw[q]);
@@ -506,13 +558,9 @@ __global__ __launch_bounds__(kCThreads) void k_compact5(
         const uint64_t b = __ballot((mw[k >> 5] >> (k & 31)) & 1u);
         if (lane == 0) s_wc[w][k] = (uint32_t)__popcll(b);
     }
-    uint32_t incl = deg;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t t = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += t;
-    }
-    if (lane == 63) s_wc[w][kK5Taps] = incl;
+    uint32_t wave_slab;
+    const uint32_t excl = wave_excl_scan<7>(deg, &wave_slab);     // deg < 125
+    if (lane == 0) s_wc[w][kK5Taps] = wave_slab;
     __syncthreads();
     if (tid < kK5Cols) {
         uint32_t run = 0;
@@ -527,7 +575,7 @@ __global__ __launch_bounds__(kCThreads) void k_compact5(
                            lb_pack(epoch, bid == 0 ? kIncl : kAgg, run), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
-    block_lookback<kK5Cols, 8, 2>(look, (int64_t)bid - 1, epoch, status, s_pre, s_near, s_done);
+    block_lookback<kK5Cols, 32, 2>(look, (int64_t)bid - 1, epoch, status, s_pre, s_done);
     if (tid < kK5Cols) {
         const uint32_t run = s_tot[tid], prefix = s_pre[tid];
         if (bid > 0)
@@ -547,18 +595,30 @@ __global__ __launch_bounds__(kCThreads) void k_compact5(
         }
     }
     __syncthreads();
-    if (tid == 0 && bid == gridDim.x - 1) {
-        int32_t p = 0, padded = 0;
-        for (int k = 0; k < kK5Taps; ++k) {
-            const int32_t c = (int32_t)(s_pre[k] + s_tot[k]);
-            p += c;
-            padded += (c + tile_m - 1) / tile_m * tile_m;
+    if (bid == gridDim.x - 1) {                   // the last chunk: pairs and padded tiles
+        __shared__ int32_t s_red[2][2];
+        if (tid < 128) {                          // waves 0 and 1 cover the 125 taps
+            int32_t c = tid < kK5Taps ? (int32_t)(s_pre[tid] + s_tot[tid]) : 0;
+            int32_t padded = (c + tile_m - 1) / tile_m * tile_m;
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                c += __shfl_xor(c, o, 64);
+                padded += __shfl_xor(padded, o, 64);
+            }
+            if (lane == 0) {
+                s_red[w][0] = c;
+                s_red[w][1] = padded;
+            }
         }
-        st->totals[0] = p;
-        st->totals[1] = padded;
-        st->totals[2] = padded / tile_m;
+        __syncthreads();
+        if (tid == 0) {
+            const int32_t padded = s_red[0][1] + s_red[1][1];
+            st->totals[0] = s_red[0][0] + s_red[1][0];
+            st->totals[1] = padded;
+            st->totals[2] = padded / tile_m;
+        }
     }
-    const uint32_t rb = s_pre[kK5Taps] + s_wc[w][kK5Taps] + incl - deg;
+    const uint32_t rb = s_pre[kK5Taps] + s_wc[w][kK5Taps] + excl;
     if (valid) rowbase[row] = (int32_t)rb;
     const int32_t* nrow = nbr + rc * kK5Taps;
     uint32_t rank = 0;                            // off-centre pairs of the row so far
@@ -573,7 +633,7 @@ __global__ __launch_bounds__(kCThreads) void k_compact5(
             const uint64_t b = __ballot(has);
             if (has) {
                 const int64_t pos =
-                    (int64_t)k * cap + s_pre[k] + s_wc[w][k] + (uint32_t)__popcll(b & below);
+                    (int64_t)k * cap + s_pre[k] + s_wc[w][k] + lanes_below(b);
                 if (pos < (int64_t)k * cap + cap) {       // (only false after a stalled wait)
                     pair_in[pos] = k == kK5Centre ? (int32_t)row : nrow[k];
                     pair_out[pos] = (int32_t)row;
@@ -583,7 +643,7 @@ __global__ __launch_bounds__(kCThreads) void k_compact5(
             }
         }
     }
-    if (bid == gridDim.x - 1 && tid == 0) atomicExch(ticket, 0u);
+    if (!by_index && bid == gridDim.x - 1 && tid == 0) atomicExch(ticket, 0u);
 }
 
 }  // namespace
@@ -615,6 +675,25 @@ size_t compact_look_bytes_k(int64_t n, int ksize) {
     return (size_t)compact_chunks(n) * (ksize == 5 ? kK5Cols : kTaps + 1) * 8;
 }
 
+// Whether `blocks` blocks of 256 threads of `kern` fit on the current device at
+// once (occupancy per CU times CUs, queried once per kernel and device).
+static bool fits_at_once(const void* kern, int slot, unsigned blocks) {
+    constexpr int kDevs = 64;
+    static std::atomic<int64_t> cache[kDevs][3];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) return false;
+    int64_t cap = cache[dev][slot].load(std::memory_order_relaxed);
+    if (cap == 0) {
+        int per_cu = 0, n_cu = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kCThreads, 0) != hipSuccess ||
+            hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return false;
+        cap = (int64_t)per_cu * n_cu;
+        cache[dev][slot].store(cap > 0 ? cap : -1, std::memory_order_relaxed);
+    }
+    return (int64_t)blocks <= cap;
+}
+
 static uint32_t next_epoch(SortWork& ws) {
     uint32_t epoch = ++ws.epoch & 0x3FFFFFFFu;
     if (epoch == 0) epoch = ++ws.epoch & 0x3FFFFFFFu;
@@ -626,12 +705,16 @@ hipError_t launch_compact(const uint32_t* mask, const int32_t* nbr, int64_t n, i
                           int32_t* pair_out, int32_t* pair_slot, int32_t* rowbase, SortWork& ws,
                           uint32_t* status, hipStream_t s) {
     const uint32_t epoch = next_epoch(ws);
-    if (ksize == 5)
-        launch(k_compact5, (unsigned)compact_chunks(n), kCThreads, 0, s, mask, nbr, n, cap, tile_m,
-               st, pair_in, pair_out, pair_slot, rowbase, ws.look, ws.ticket, epoch, status);
-    else
-        launch(k_compact, (unsigned)compact_chunks(n), kCThreads, 0, s, mask, nbr, n, cap, tile_m,
-               st, pair_in, pair_out, pair_slot, rowbase, ws.look, ws.ticket, epoch, status);
+    const unsigned blocks = (unsigned)compact_chunks(n);
+    if (ksize == 5) {
+        const bool by_index = fits_at_once((const void*)k_compact5, 0, blocks);
+        launch(k_compact5, blocks, kCThreads, 0, s, mask, nbr, n, cap, tile_m, st, pair_in,
+               pair_out, pair_slot, rowbase, ws.look, ws.ticket, by_index, epoch, status);
+    } else {
+        const bool by_index = fits_at_once((const void*)k_compact, 1, blocks);
+        launch(k_compact, blocks, kCThreads, 0, s, mask, nbr, n, cap, tile_m, st, pair_in,
+               pair_out, pair_slot, rowbase, ws.look, ws.ticket, by_index, epoch, status);
+    }
     return hipGetLastError();
 }
 
@@ -642,9 +725,11 @@ hipError_t launch_lookup_compact(const int32_t* coords, int64_t n, const Geom& g
                                  int32_t* pair_slot, int32_t* rowbase, SortWork& ws,
                                  uint32_t* status, hipStream_t s) {
     const uint32_t epoch = next_epoch(ws);
-    launch(k_lookup_compact, (unsigned)compact_chunks(n), kCThreads, 0, s, coords, n, g, grid, bits,
-           nbr, mask, cap, tile_m, st, pair_in, pair_out, pair_slot, rowbase, ws.look, ws.ticket,
-           epoch, status);
+    const unsigned blocks = (unsigned)compact_chunks(n);
+    const bool by_index = fits_at_once((const void*)k_lookup_compact, 2, blocks);
+    launch(k_lookup_compact, blocks, kCThreads, 0, s, coords, n, g, grid, bits, nbr, mask, cap,
+           tile_m, st, pair_in, pair_out, pair_slot, rowbase, ws.look, ws.ticket, by_index, epoch,
+           status);
     return hipGetLastError();
 }
 
