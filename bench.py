@@ -22,6 +22,11 @@ that kernel's average duration, as rocprofv3's kernel trace reports it.
       / `--pmc WRITE_SIZE` runs of this script (with --copy-probe-mb) into
       profiles/traffic_<workload>_<algo>.json, which later runs read for the
       roofline's "traffic" (null when a kernel source changed since).
+  --summarize-mfma PMC_DIR   turn one `rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16
+      SQ_VALU_MFMA_BUSY_CYCLES` run into
+      profiles/mfma_<workload>_<algo>.json: executed vs useful MFMA flops and
+      the MFMA busy share of the GEMM kernels (builds the workload's map, so
+      it needs a GPU).
 """
 from __future__ import annotations
 
@@ -427,6 +432,72 @@ def _pmc_rows(d, counter):
     return rows
 
 
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES")
+N_SIMD = 256 * 4                 # MI355X: 256 CUs of 4 SIMDs
+CLOCK_HZ = 2.4e9                 # MI355X peak engine clock
+
+
+def summarize_mfma(pmc_dir, workload, algo):
+    """Per-dispatch MFMA counters of the GEMM kernels from one `rocprofv3 --pmc
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES` run: executed bf16
+    MFMA flops (MOPS x 512) next to the useful flops of the same launch
+    (2 x pairs x C_in x C_out over the pairs that launch covers, from a map of
+    the workload built here), and the MFMA busy share of all SIMD cycles over
+    the dispatch's own (profiled) duration."""
+    import re
+
+    import torch
+
+    import submanifold_sparse_convolution_amd as smc
+    import synth
+
+    def short(k):
+        k = k.replace("(anonymous namespace)::", "").replace("void ", "").replace("smc::", "")
+        return re.sub(r"\(.*", "", k).split("<")[0].strip()
+
+    w = synth.workload(workload)
+    m = smc.KernelMap().build(torch.from_numpy(synth.make_coords(w)).cuda(), spatial_shape=w.grid,
+                              batch_size=1, pairs=(algo == "pairs"), sort=(algo == "mask_tiles"))
+    info = m.info()
+    m.close()
+    n, p, c = w.n, info["pairs"], w.channels
+    useful = {"k_gemm_nc": 2.0 * (p - n) * c * c, "k_gemm_centre": 2.0 * n * c * c,
+              "k_conv_masktile": 2.0 * p * c * c}
+    files = glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {pmc_dir}")
+    per = {}                       # kernel -> dispatch -> {counter: value, "ns": duration}
+    for fn in files:
+        with open(fn) as f:
+            for row in csv.DictReader(f):
+                k = short(row["Kernel_Name"])
+                if k not in useful or row["Counter_Name"] not in MFMA_COUNTERS:
+                    continue
+                d = per.setdefault(k, {}).setdefault(row["Dispatch_Id"], {})
+                d[row["Counter_Name"]] = float(row["Counter_Value"])
+                d["ns"] = float(row["End_Timestamp"]) - float(row["Start_Timestamp"])
+    out = {"workload": workload, "algo": algo, "n": n, "pairs": p, "c": c,
+           "clock_hz": CLOCK_HZ, "simds": N_SIMD, "kernels": {}}
+    for k, ds in sorted(per.items()):
+        mops = statistics.mean(d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) for d in ds.values())
+        busy = statistics.mean(d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for d in ds.values())
+        ns = statistics.mean(d["ns"] for d in ds.values())
+        executed = mops * 512.0
+        out["kernels"][k] = {
+            "dispatches": len(ds), "mfma_flops_executed": executed, "flops_useful": useful[k],
+            "useful_over_executed": useful[k] / executed if executed else None,
+            "mfma_busy_cycles": busy, "profiled_ns": ns,
+            "mfma_busy_frac": busy / (ns * 1e-9 * CLOCK_HZ * N_SIMD) if ns else None}
+    path = os.path.join(ROOT, "profiles", f"mfma_{workload}_{algo}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(f"wrote {path}")
+    for k, v in out["kernels"].items():
+        print(f"{k}: executed {v['mfma_flops_executed']:.4g} flop, useful {v['flops_useful']:.4g} "
+              f"({v['useful_over_executed']:.3f}); MFMA busy {v['mfma_busy_frac']:.4f} of the "
+              f"SIMD cycles over {v['profiled_ns'] / 1e3:.2f} us (profiled)")
+
+
 def summarize_pmc(fetch_dir, write_dir, workload, algo, copy_mb):
     """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of every kernel, scaled by what the
     same counters read for a plain device copy of copy_mb MiB."""
@@ -496,10 +567,15 @@ def main():
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB first (PMC calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-mfma", metavar="PMC_DIR",
+                    help="summarise a rocprofv3 --pmc run of the MFMA counters (needs a GPU)")
     ap.add_argument("--report", default="",
                     help="also run every workload and write their figures to this JSON file")
     args = ap.parse_args()
 
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma, args.workload, args.algo)
+        return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.algo,
                       args.copy_probe_mb or 256)

@@ -186,13 +186,18 @@ __device__ __forceinline__ void block_gemm(const uint16_t* const (&xrow)[MW], in
 }
 
 // Store NBW float values of one slab or output row (columns col0 ..).
+// Whole 16-byte words are streaming (non-temporal) stores: the row is read
+// once, by a later launch, and lines that do not stay dirty in L2 shorten the
+// write-back at the end of this launch (measured: LiDAR forward 15.2 -> 14.7
+// us with the bf16 output stores streamed too).
 template <int NBW>
 __device__ __forceinline__ void store_f32(float* __restrict__ dst, int col0, int c_out,
                                           const float (&v)[NBW]) {
     if (NBW >= 4 && col0 + NBW <= c_out && (c_out & 3) == 0) {
 #pragma unroll
         for (int q = 0; q < NBW; q += 4)
-            *reinterpret_cast<float4*>(dst + q) = make_float4(v[q], v[q + 1], v[q + 2], v[q + 3]);
+            __builtin_nontemporal_store((f32x4){v[q], v[q + 1], v[q + 2], v[q + 3]},
+                                        reinterpret_cast<f32x4*>(dst + q));
     } else {
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb)
