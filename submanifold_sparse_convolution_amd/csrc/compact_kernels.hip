@@ -494,11 +494,8 @@ __global__ __launch_bounds__(kCThreads) void k_lookup_compact(
                 cell_bits(bits, c0 + (int64_t)(dx - 1) * g.sz_x + (int64_t)(dy - 1) * g.sz_y, 3);
     // ... then row ids of the occupied cells only. Every tap issues its load; an
     // empty one reads cell 0 (one line, cached for the whole launch), so no load
-    // is conditional. The row's own cell is read too: it holds another row's id
-    // when two rows share the cell (the scatter, which did not check, stored
-    // both ids there and one store won).
+    // is conditional.
     const int64_t c_self = 0;
-    const int32_t own = grid[c0 + 1];
     int32_t v[kTaps];
 #pragma unroll
     for (int dx = 0; dx < 3; ++dx)
@@ -514,7 +511,6 @@ __global__ __launch_bounds__(kCThreads) void k_lookup_compact(
                 v[k] = on ? v[k] : -1;
             }
     v[kCentre] = (int32_t)row;
-    if (ok && own != (int32_t)row) atomicOr(&st->status, kStDuplicate);
     uint32_t m = 0;
 #pragma unroll
     for (int k = 0; k < kTaps; ++k) {

@@ -138,12 +138,9 @@ hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 // cell's row id is only read when its bit is set, so the int32 grid needs no
 // initial fill and no reset; the bits of a build are cleared (whole words)
 // by the next build that uses the other grid. bits has 2 words of padding.
-// dup_check false: the scatter does not flag two rows on one cell; the
-// caller's lookup must (k_lookup_compact does).
 hipError_t launch_dense_scatter(const int32_t* coords, int64_t n, const Geom& g, int32_t* grid,
                                 uint32_t* bits, int32_t* cells, MapState* st,
-                                const NextRecord& next, const PrevCells& prev, bool dup_check,
-                                hipStream_t s);
+                                const NextRecord& next, const PrevCells& prev, hipStream_t s);
 hipError_t launch_clear_cells(const PrevCells& prev, hipStream_t s);
 // nbr [n, K^3]; mask [n] (K = 3) or [n, 4] words (K = 5): g.ksize decides.
 hipError_t launch_dense_lookup(const int32_t* coords, int64_t n, const Geom& g, const int32_t* grid,

@@ -606,7 +606,7 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
             int32_t* grid = m->grid[gi].as<int32_t>();
             uint32_t* bits = m->bits[gi].as<uint32_t>();
             SMC_HIP(launch_dense_scatter(coords, n, g, grid, bits, m->cells[gi].as<int32_t>(), st,
-                                         next, m->stale, !fused, s));
+                                         next, m->stale, s));
             m->slot_clean[slot ^ 1] = true;
             m->stale.cells = m->cells[gi].as<int32_t>();
             m->stale.n = n;
