@@ -205,11 +205,43 @@ __device__ __forceinline__ void store_f32(float* __restrict__ dst, int col0, int
     }
 }
 
+// Tile table of the non-centre taps, tiles of kRows pairs: on return
+// s_first[k] is tap k's first tile (s_first[taps]: the tile count) and
+// s_cnt[k] its pairs (the centre: none). Per-tap counts are read in parallel
+// (one thread per tap), tiles per tap scanned over the first two waves.
+// Every thread of the block calls this.
+template <int kRows>
+__device__ __forceinline__ void nc_tap_table(int taps, const MapState* __restrict__ st,
+                                             int32_t* s_first, int32_t* s_cnt, int32_t* s_wave0) {
+    static_assert(kMaxTaps <= 128 && kGemmThreads >= 128, "two waves scan the taps");
+    const int centre = taps / 2;
+    const int lane = threadIdx.x & 63;
+    const int k = threadIdx.x;
+    int32_t tiles = 0;
+    if (k < taps) {
+        const int32_t c = k == centre ? 0 : st->tap_count[k];
+        s_cnt[k] = c;
+        tiles = (c + kRows - 1) / kRows;
+    }
+    int32_t inc = tiles;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int32_t t = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += t;
+    }
+    if (k == 63) *s_wave0 = inc;
+    __syncthreads();
+    const int32_t ex = inc - tiles + (k >= 64 ? *s_wave0 : 0);
+    if (k < taps) s_first[k] = ex;
+    if (k == taps - 1) s_first[taps] = ex + tiles;
+    __syncthreads();
+}
+
 // Non-centre taps: blocks stride over tiles of 64 MW pairs of one tap (tap k
 // holds tap_count[k] pairs from k * cap on, cap a multiple of 256; the counts
 // are read on the device). Each pair's product row goes to its slab row.
 template <int NBW, int MW, bool VEC, bool STREAM>
-__global__ __launch_bounds__(kGemmThreads, STREAM ? 1 : 2) void k_gemm_nc(
+__global__ __launch_bounds__(kGemmThreads, 2) void k_gemm_nc(
     const uint16_t* __restrict__ x, int c_in, int steps, const u32x4* __restrict__ wp, int n_wt,
     int c_out, int taps, const int32_t* __restrict__ pair_in,
     const int32_t* __restrict__ pair_slot, const MapState* __restrict__ st, int64_t cap, int64_t n,
@@ -221,31 +253,7 @@ __global__ __launch_bounds__(kGemmThreads, STREAM ? 1 : 2) void k_gemm_nc(
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
     __shared__ int32_t s_wave0;
-    static_assert(kMaxTaps <= 128 && kGemmThreads >= 128, "two waves scan the taps");
-    const int centre = taps / 2;
-    {
-        // per-tap counts read in parallel (one thread per tap), tiles per tap
-        // scanned over the first two waves (taps <= 128)
-        const int k = threadIdx.x;
-        int32_t tiles = 0;
-        if (k < taps) {
-            const int32_t c = k == centre ? 0 : st->tap_count[k];
-            s_cnt[k] = c;
-            tiles = (c + kRows - 1) / kRows;
-        }
-        int32_t inc = tiles;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int32_t t = __shfl_up(inc, o, 64);
-            if (lane >= o) inc += t;
-        }
-        if (k == 63) s_wave0 = inc;
-        __syncthreads();
-        const int32_t ex = inc - tiles + (k >= 64 ? s_wave0 : 0);
-        if (k < taps) s_first[k] = ex;
-        if (k == taps - 1) s_first[taps] = ex + tiles;
-    }
-    __syncthreads();
+    nc_tap_table<kRows>(taps, st, s_first, s_cnt, &s_wave0);
     const int n_nc = s_first[taps];
     const int wt_i = blockIdx.y;
     const int col0 = wt_i * 16 * NBW + r * NBW;
@@ -420,7 +428,7 @@ __device__ __forceinline__ int centre_runs(int64_t row0, int g, int64_t n, int32
 }
 
 template <int NBW, int MW, bool OUT_F32, bool VEC, bool STREAM>
-__global__ __launch_bounds__(kGemmThreads, STREAM ? 1 : 2) void k_gemm_centre(
+__global__ __launch_bounds__(kGemmThreads, (STREAM && MW == 2) ? 1 : 2) void k_gemm_centre(
     const uint16_t* __restrict__ x, int c_in, int steps, const u32x4* __restrict__ wp, int n_wt,
     int c_out, int centre, const int32_t* __restrict__ rowbase, int64_t n,
     const float* __restrict__ part, void* __restrict__ yv, int relu) {
@@ -479,16 +487,23 @@ __global__ __launch_bounds__(kGemmThreads, STREAM ? 1 : 2) void k_gemm_centre(
 template <int NBW, bool STREAM>
 constexpr size_t gemm_lds_bytes() { return (STREAM ? 2 : 1) * (size_t)kChunk * NBW * 64 * 16; }
 
-// Row fragments per wave. Streamed (C_in > 128) tiles use 2: measured on the
-// C = 512 set, 4 fragments (more weight reuse per chunk) left too few blocks
-// to cover each block's serial chain of chunk loads and the slab epilogue
-// (centre 48 -> 38 us, off-centre 31 -> 24 us with 2). One-chunk slabs with
-// 16-byte row loads use 1: twice the blocks, two per CU, hide the same chain
-// (centre at C = 128: LiDAR 11.0 -> 9.4 us, the 91k-row set 22.5 -> 17.6 us).
-// The off-centre GEMM uses 1 there too (the pair lists of a sparse scan are
-// short).
-inline int mw_for(int c_in) { return (c_in + 31) / 32 <= kChunk && (c_in & 7) == 0 ? 1 : 2; }
+// Row fragments per wave. The centre GEMM with 16-byte row loads uses 1:
+// twice the blocks of 2, and registers for two blocks per CU, so the
+// serial chain of a tile (row and weight loads, the slab epilogue) overlaps
+// another block's (centre at C = 128: LiDAR 11.0 -> 9.4 us, the 91k-row set
+// 22.5 -> 17.6 us; streamed at C = 512: forward 62.5 -> 49.7 us). Measured
+// on the C = 512 set, the streamed off-centre GEMM is best at 2 (4 left too
+// few blocks: 31 -> 24 us with 2); at C <= 128 it uses 1 (the pair lists of
+// a sparse scan are short). A tile's loads are latency-bound at one block
+// per CU: with 128 KiB of weights in LDS and every load issued at once, one
+// block per CU took longer (Deep forward 62 -> 73 us) than two streaming.
+inline int mw_for(int c_in) { return (c_in & 7) == 0 || (c_in + 31) / 32 <= kChunk ? 1 : 2; }
 inline int mw_nc_for(int c_in) { return (c_in + 31) / 32 > kChunk && (c_in & 7) == 0 ? 2 : 1; }
+
+// Grid x rounded up to a multiple of 8: block (x, y) is then on die x mod 8
+// for every y (blocks go to the 8 dies round robin by linear index), so the
+// wave tiles of one row tile share that die's L2 for the rows they gather.
+inline int64_t xcd_round(int64_t gx) { return (gx + 7) / 8 * 8; }
 
 // Lets a kernel take `bytes` of dynamic LDS (once per kernel; the default cap
 // is 64 KiB including the kernel's static LDS).
@@ -553,13 +568,13 @@ void launch_centre(dim3 grid, hipStream_t s, int mw, bool out_f32, const uint16_
     const bool vec = (c_in & 7) == 0;
     (void)mw;
     if (steps > kChunk && vec)                     // streamed, 16-byte row loads
-        launch_centre_mw<NBW, 2, true, true>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, centre, rowbase, n, part, y, relu);
+        launch_centre_mw<NBW, 1, true, true>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, centre, rowbase, n, part, y, relu);
     else if (steps > kChunk)
         launch_centre_mw<NBW, 2, false, true>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, centre, rowbase, n, part, y, relu);
     else if (vec)
         launch_centre_mw<NBW, 1, true, false>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, centre, rowbase, n, part, y, relu);
     else
-        launch_centre_mw<NBW, 2, false, false>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, centre, rowbase, n, part, y, relu);
+        launch_centre_mw<NBW, 1, false, false>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, centre, rowbase, n, part, y, relu);
 }
 
 }  // namespace
@@ -593,6 +608,7 @@ hipError_t launch_gemm_nc(const uint16_t* x, int c_in, const void* wpacked, int 
     int64_t gx = (taps - 1) * (cap / (64 * mw));  // tiles if every tap were full
     if (gx > (int64_t)n_cu * 2) gx = (int64_t)n_cu * 2;
     if (gx < 1) gx = 1;
+    gx = xcd_round(gx);
     dim3 grid((unsigned)gx, (unsigned)n_wt);
     const u32x4* wp = (const u32x4*)wpacked;
     switch (nbw) {
@@ -614,7 +630,7 @@ hipError_t launch_gemm_centre(const uint16_t* x, int c_in, const void* wpacked, 
     const int n_wt = (c_out + 16 * nbw - 1) / (16 * nbw);
     const int mw = mw_for(c_in);
     const int64_t row_tiles = (n + 64 * mw - 1) / (64 * mw);
-    const int64_t gx = row_tiles < (int64_t)n_cu * 2 ? row_tiles : (int64_t)n_cu * 2;
+    const int64_t gx = xcd_round(row_tiles < (int64_t)n_cu * 2 ? row_tiles : (int64_t)n_cu * 2);
     dim3 grid((unsigned)gx, (unsigned)n_wt);
     const u32x4* wp = (const u32x4*)wpacked;
     const int rl = relu ? 1 : 0;

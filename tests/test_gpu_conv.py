@@ -105,7 +105,7 @@ def test_one_hot_tap_is_shifted_copy(k, algo):
 @pytest.mark.parametrize("algo", ALGOS)
 @pytest.mark.parametrize("cin,cout", [(1, 1), (3, 5), (8, 8), (16, 16), (20, 36), (32, 32),
                                       (40, 24), (64, 128), (128, 64), (96, 160), (256, 256),
-                                      (200, 72)])
+                                      (200, 72), (384, 96), (456, 48), (520, 64), (300, 40)])
 def test_channel_shapes(cin, cout, algo):
     coords = synth.tiny_coords(seed=cin * 7 + cout, n=1500, side=16)
     xb = synth.features(1500, cin, cin)
