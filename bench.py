@@ -22,11 +22,10 @@ that kernel's average duration, as rocprofv3's kernel trace reports it.
       / `--pmc WRITE_SIZE` runs of this script (with --copy-probe-mb) into
       profiles/traffic_<workload>_<algo>.json, which later runs read for the
       roofline's "traffic" (null when a kernel source changed since).
-  --summarize-mfma PMC_DIR   turn one `rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16
-      SQ_VALU_MFMA_BUSY_CYCLES` run into
-      profiles/mfma_<workload>_<algo>.json: executed vs useful MFMA flops and
-      the MFMA busy share of the GEMM kernels (builds the workload's map, so
-      it needs a GPU).
+  --summarize-mfma PMC_DIR BENCH_OUT   turn one `rocprofv3 --pmc
+      SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES` run of this script
+      (its stdout saved in BENCH_OUT) into profiles/mfma_<workload>_<algo>.json:
+      executed vs useful MFMA flops and the MFMA busy share of the GEMM kernels.
 """
 from __future__ import annotations
 
@@ -437,30 +436,29 @@ N_SIMD = 256 * 4                 # MI355X: 256 CUs of 4 SIMDs
 CLOCK_HZ = 2.4e9                 # MI355X peak engine clock
 
 
-def summarize_mfma(pmc_dir, workload, algo):
+def summarize_mfma(pmc_dir, workload, algo, bench_out):
     """Per-dispatch MFMA counters of the GEMM kernels from one `rocprofv3 --pmc
-    SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES` run: executed bf16
-    MFMA flops (MOPS x 512) next to the useful flops of the same launch
-    (2 x pairs x C_in x C_out over the pairs that launch covers, from a map of
-    the workload built here), and the MFMA busy share of all SIMD cycles over
-    the dispatch's own (profiled) duration."""
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES` run of this script:
+    executed bf16 MFMA flops (MOPS x 512) next to the useful flops of the same
+    launch (2 x pairs x C_in x C_out over the pairs that launch covers; n,
+    pairs and C from the JSON line the profiled run printed, in bench_out),
+    and the MFMA busy share of all SIMD cycles over the dispatch's own
+    (profiled) duration. Runs on the CPU."""
     import re
-
-    import torch
-
-    import submanifold_sparse_convolution_amd as smc
-    import synth
 
     def short(k):
         k = k.replace("(anonymous namespace)::", "").replace("void ", "").replace("smc::", "")
         return re.sub(r"\(.*", "", k).split("<")[0].strip()
 
-    w = synth.workload(workload)
-    m = smc.KernelMap().build(torch.from_numpy(synth.make_coords(w)).cuda(), spatial_shape=w.grid,
-                              batch_size=1, pairs=(algo == "pairs"), sort=(algo == "mask_tiles"))
-    info = m.info()
-    m.close()
-    n, p, c = w.n, info["pairs"], w.channels
+    line = None
+    with open(bench_out) as f:
+        for ln in f:
+            if ln.startswith('{"metric"'):
+                line = json.loads(ln)
+    if line is None:
+        raise SystemExit(f"no bench JSON line in {bench_out}")
+    cfg = line["config"]
+    n, p, c = cfg["n"], cfg["pairs"], cfg["c_in"]
     useful = {"k_gemm_nc": 2.0 * (p - n) * c * c, "k_gemm_centre": 2.0 * n * c * c,
               "k_conv_masktile": 2.0 * p * c * c}
     files = glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True)
@@ -567,14 +565,15 @@ def main():
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB first (PMC calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
-    ap.add_argument("--summarize-mfma", metavar="PMC_DIR",
-                    help="summarise a rocprofv3 --pmc run of the MFMA counters (needs a GPU)")
+    ap.add_argument("--summarize-mfma", nargs=2, metavar=("PMC_DIR", "BENCH_OUT"),
+                    help="summarise a rocprofv3 --pmc run of the MFMA counters and the "
+                         "JSON line that run printed")
     ap.add_argument("--report", default="",
                     help="also run every workload and write their figures to this JSON file")
     args = ap.parse_args()
 
     if args.summarize_mfma:
-        summarize_mfma(args.summarize_mfma, args.workload, args.algo)
+        summarize_mfma(args.summarize_mfma[0], args.workload, args.algo, args.summarize_mfma[1])
         return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.algo,
