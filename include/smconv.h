@@ -29,11 +29,12 @@
  *    alive and unmodified until the stream has run the work.
  *  - The caller owns every buffer it passes. The library keeps no caller
  *    pointer after a call returns (except in work already enqueued).
- *  - A map handle owns its own device buffers, allocated with hipMalloc
- *    when a build needs more room than it has (grow-only), and freed by
- *    smc_map_destroy. A handle is not thread-safe; all builds and forwards
- *    that use one handle must be issued on one stream, or the caller must
- *    order them.
+ *  - A map handle owns its own device buffers, allocated when a build or
+ *    forward needs more room than it has (grow-only) and freed by
+ *    smc_map_destroy: with hipMalloc/hipFree, or with the caller's allocator
+ *    (smc_set_allocator). A handle is not thread-safe; all builds and
+ *    forwards that use one handle must be issued on one stream, or the
+ *    caller must order them.
  *  - bf16 tensors are passed as uint16_t bit patterns.
  */
 #ifndef SMCONV_H
@@ -109,6 +110,24 @@ typedef struct smc_map_info_s {
     int32_t strided;        /* 1 for a map from smc_map_build_strided */
     int32_t out_extent[3];  /* output grid extent (strided: floor((X + 2 - 3) / 2) + 1) */
 } smc_map_info_t;
+
+/*
+ * Device allocator for every buffer a map handle takes from now on, for the
+ * whole process: alloc(ctx, bytes, stream) returns a device pointer on the
+ * current device, usable on `stream` (the hipStream_t of the call that needs
+ * it, as void*; NULL: the null stream), or NULL on failure (the call then
+ * returns SMC_ERR_ALLOC); free(ctx, ptr, stream) gives it back. A caller with
+ * its own pool (e.g. torch's caching allocator, bound from Python) keeps all
+ * device memory in that pool this way. Both NULL restores hipMalloc/hipFree.
+ * A buffer is always freed by the allocator that made it, even after the
+ * allocator changed. The functions are called from the library's calls
+ * (build, forward, destroy) on the calling thread, never from a GPU
+ * callback; they must not call back into the library. Returns SMC_ERR_ARG
+ * when only one of the two is NULL.
+ */
+typedef void* (*smc_alloc_fn)(void* ctx, size_t bytes, void* stream);
+typedef void (*smc_free_fn)(void* ctx, void* ptr, void* stream);
+int smc_set_allocator(smc_alloc_fn alloc, smc_free_fn free_fn, void* ctx);
 
 /* Create an empty map handle. *out receives it. No device memory is taken yet. */
 int smc_map_create(smc_map** out);

@@ -16,7 +16,7 @@ import ctypes
 import os
 
 __all__ = ["KernelMap", "PackedWeights", "pack_weights", "subm_conv3d", "lib", "library_path",
-           "SmconvError", "ROUTES", "EXPORTED_SYMBOLS"]
+           "SmconvError", "ROUTES", "EXPORTED_SYMBOLS", "use_torch_allocator"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libsmconv.so")
@@ -36,7 +36,7 @@ EXPORTED_SYMBOLS = [
     "smc_map_export", "smc_weight_packed_bytes", "smc_weight_pack", "smc_conv_forward",
     "smc_status_string", "smc_last_error", "smc_version", "smc_timing_enable", "smc_timing_read",
     "smc_map_set_order", "smc_map_calibrate", "smc_map_build_strided",
-    "smc_map_export_out_coords",
+    "smc_map_export_out_coords", "smc_set_allocator",
 ]
 STAGES = ["map", "neighbours", "mask_sort", "compact", "gemm", "centre"]
 
@@ -103,13 +103,50 @@ def lib():
     L.smc_map_calibrate.argtypes = [vp, i32, vp, vp]
     L.smc_map_build_strided.argtypes = [vp, vp, i64, i32, vp, i32, i32, i32, i32, u32, vp]
     L.smc_map_export_out_coords.argtypes = [vp, vp]
+    L.smc_set_allocator.argtypes = [vp, vp, vp]
     for name in ("smc_map_create", "smc_map_destroy", "smc_map_build", "smc_map_sync",
                  "smc_map_info", "smc_map_export", "smc_weight_pack", "smc_conv_forward",
                  "smc_timing_enable", "smc_timing_read", "smc_map_set_order",
-                 "smc_map_calibrate", "smc_map_build_strided", "smc_map_export_out_coords"):
+                 "smc_map_calibrate", "smc_map_build_strided", "smc_map_export_out_coords",
+                 "smc_set_allocator"):
         getattr(L, name).restype = i32
     _lib = L
     return L
+
+
+_ALLOC_T = ctypes.CFUNCTYPE(ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p)
+_FREE_T = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p)
+_allocator_refs = []        # every callback pair ever handed over: buffers free through them
+
+
+def use_torch_allocator(on: bool = True):
+    """Take every device buffer that map handles allocate from now on (builds,
+    forwards, growth) from torch's caching allocator, on the stream of the call
+    that needs it, so that torch's pool holds all of the library's device
+    memory; on=False goes back to hipMalloc/hipFree. Buffers keep the
+    allocator that made them (smc_set_allocator)."""
+    import torch
+    L = lib()
+    if not on:
+        _check(L.smc_set_allocator(None, None, None))
+        return
+
+    def _alloc(ctx, nbytes, stream):
+        try:
+            return torch.cuda.caching_allocator_alloc(int(nbytes), stream=stream or None)
+        except Exception:
+            return None                # the library reports SMC_ERR_ALLOC
+
+    def _free(ctx, ptr, stream):
+        try:
+            torch.cuda.caching_allocator_delete(ptr)
+        except Exception:
+            pass
+
+    fa, ff = _ALLOC_T(_alloc), _FREE_T(_free)
+    _allocator_refs.append((fa, ff))
+    _check(L.smc_set_allocator(ctypes.cast(fa, ctypes.c_void_p), ctypes.cast(ff, ctypes.c_void_p),
+                               None))
 
 
 def _check(status: int):
@@ -183,9 +220,11 @@ class KernelMap:
         self._coords = None
 
     def close(self):
+        """Destroy the handle (waits for its work) and drop the last coordinates."""
         if self._h:
             lib().smc_map_destroy(self._h)
             self._h = ctypes.c_void_p()
+        self._coords = None
 
     def __del__(self):
         try:

@@ -3,6 +3,8 @@
 #include "smconv.h"
 #include "smc_internal.h"
 
+#include <mutex>
+
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
@@ -39,30 +41,55 @@ int fail(int status, const char* fmt, ...) {
                         __FILE__, __LINE__);                                                   \
     } while (0)
 
-// Grow-only device buffer.
+// Device allocator of the process (smc_set_allocator); both null: hipMalloc
+// and hipFree.
+struct Allocator {
+    smc_alloc_fn alloc = nullptr;
+    smc_free_fn free = nullptr;
+    void* ctx = nullptr;
+};
+std::mutex g_alloc_mu;
+Allocator g_alloc;
+
+Allocator current_allocator() {
+    std::lock_guard<std::mutex> lock(g_alloc_mu);
+    return g_alloc;
+}
+
+// Grow-only device buffer. It keeps the allocator that made it and frees
+// with that one, whatever the process allocator is by then; s is the stream
+// the buffer is about to be used on (handed to a caller's allocator).
 struct DevBuf {
     void* p = nullptr;
     size_t bytes = 0;
-    int ensure(size_t want) {
+    Allocator by;
+    int ensure(size_t want, hipStream_t s = nullptr) {
         if (want <= bytes) return SMC_OK;
-        if (p) {
-            (void)hipFree(p);
-            p = nullptr;
-            bytes = 0;
-        }
-        size_t alloc = want < 256 ? 256 : want;
-        if (hipMalloc(&p, alloc) != hipSuccess) {
+        release(s);
+        const size_t alloc = want < 256 ? 256 : want;
+        const Allocator a = current_allocator();
+        if (a.alloc) {
+            p = a.alloc(a.ctx, alloc, (void*)s);
+            if (!p) return fail(SMC_ERR_ALLOC, "the caller's allocator returned NULL for %zu bytes", alloc);
+        } else if (hipMalloc(&p, alloc) != hipSuccess) {
             (void)hipGetLastError();
             p = nullptr;
             return fail(SMC_ERR_ALLOC, "hipMalloc(%zu) failed", alloc);
         }
+        by = a;
         bytes = alloc;
         return SMC_OK;
     }
-    void release() {
-        if (p) (void)hipFree(p);
+    void release(hipStream_t s = nullptr) {
+        if (p) {
+            if (by.free)
+                by.free(by.ctx, p, (void*)s);
+            else
+                (void)hipFree(p);
+        }
         p = nullptr;
         bytes = 0;
+        by = Allocator();
     }
     template <typename T> T* as() const { return static_cast<T*>(p); }
 };
@@ -210,11 +237,11 @@ int ensure_grid(smc_map* m, int gi, int64_t cells, hipStream_t s) {
     const int64_t words = cells / 32 + 2;
     DevBuf& grid = m->grid[gi];
     DevBuf& bits = m->bits[gi];
-    int rc = grid.ensure((size_t)cells * 4);       // never filled: read only under a set bit
+    int rc = grid.ensure((size_t)cells * 4, s);       // never filled: read only under a set bit
     if (rc) return rc;
     if ((size_t)words * 4 > bits.bytes) {
         if (m->stale.n > 0 && m->stale.bits == bits.as<uint32_t>()) m->stale = PrevCells();
-        if ((rc = bits.ensure((size_t)words * 4))) return rc;
+        if ((rc = bits.ensure((size_t)words * 4, s))) return rc;
         m->bits_clean_words[gi] = 0;
     }
     if (m->bits_clean_words[gi] < words) {
@@ -304,6 +331,16 @@ struct StageTimer {
 extern "C" {
 
 int smc_version(void) { return 100; }
+
+int smc_set_allocator(smc_alloc_fn alloc, smc_free_fn free_fn, void* ctx) {
+    if ((alloc == nullptr) != (free_fn == nullptr))
+        return fail(SMC_ERR_ARG, "alloc and free must both be set or both be NULL");
+    std::lock_guard<std::mutex> lock(g_alloc_mu);
+    g_alloc.alloc = alloc;
+    g_alloc.free = free_fn;
+    g_alloc.ctx = alloc ? ctx : nullptr;
+    return SMC_OK;
+}
 
 const char* smc_status_string(int status) {
     switch (status) {
@@ -554,27 +591,27 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     if (look_c > look_bytes) look_bytes = look_c;
     const size_t look_before = m->look.bytes;
     // (the neighbour table is read in whole 16-byte words: keep the last one readable)
-    if ((rc = m->nbr.ensure((size_t)rows_cap * taps * 4 + 16)) ||
-        (rc = m->mask.ensure((size_t)rows_cap * mwords * 4)) ||
-        (rc = m->mkey0.ensure((size_t)items * 4)) || (rc = m->mkey1.ensure((size_t)items * 4)) ||
-        (rc = m->mval0.ensure((size_t)items * 4)) || (rc = m->mval1.ensure((size_t)items * 4)) ||
-        (rc = m->look.ensure(look_bytes)))
+    if ((rc = m->nbr.ensure((size_t)rows_cap * taps * 4 + 16, s)) ||
+        (rc = m->mask.ensure((size_t)rows_cap * mwords * 4, s)) ||
+        (rc = m->mkey0.ensure((size_t)items * 4, s)) || (rc = m->mkey1.ensure((size_t)items * 4, s)) ||
+        (rc = m->mval0.ensure((size_t)items * 4, s)) || (rc = m->mval1.ensure((size_t)items * 4, s)) ||
+        (rc = m->look.ensure(look_bytes, s)))
         return rc;
-    if (!ord.plain && (rc = m->okeys.ensure((size_t)items * 4))) return rc;
+    if (!ord.plain && (rc = m->okeys.ensure((size_t)items * 4, s))) return rc;
     if (strided &&
-        ((rc = m->ck0.ensure((size_t)n_cand * 8)) || (rc = m->ck1.ensure((size_t)n_cand * 8)) ||
-         (rc = m->ck2.ensure((size_t)n_cand * 8)) || (rc = m->cv0.ensure((size_t)n_cand * 4)) ||
-         (rc = m->cv1.ensure((size_t)n_cand * 4)) ||
-         (rc = m->chist.ensure((size_t)kHistKeyInts * 4)) ||
-         (rc = m->ucounts.ensure((size_t)unique_blocks(n_cand) * 4)) ||
-         (rc = m->ocoords.ensure((size_t)n_cand * 16)) ||
-         (rc = m->qcoords.ensure((size_t)n_cand * 16))))
+        ((rc = m->ck0.ensure((size_t)n_cand * 8, s)) || (rc = m->ck1.ensure((size_t)n_cand * 8, s)) ||
+         (rc = m->ck2.ensure((size_t)n_cand * 8, s)) || (rc = m->cv0.ensure((size_t)n_cand * 4, s)) ||
+         (rc = m->cv1.ensure((size_t)n_cand * 4, s)) ||
+         (rc = m->chist.ensure((size_t)kHistKeyInts * 4, s)) ||
+         (rc = m->ucounts.ensure((size_t)unique_blocks(n_cand) * 4, s)) ||
+         (rc = m->ocoords.ensure((size_t)n_cand * 16, s)) ||
+         (rc = m->qcoords.ensure((size_t)n_cand * 16, s))))
         return rc;
     if (want_pairs &&
-        ((rc = m->pair_in.ensure((size_t)taps * cap * 4)) ||
-         (rc = m->pair_out.ensure((size_t)taps * cap * 4)) ||
-         (rc = m->pair_slot.ensure((size_t)taps * cap * 4)) ||
-         (rc = m->rowbase.ensure((size_t)(nn + 1) * 4))))
+        ((rc = m->pair_in.ensure((size_t)taps * cap * 4, s)) ||
+         (rc = m->pair_out.ensure((size_t)taps * cap * 4, s)) ||
+         (rc = m->pair_slot.ensure((size_t)taps * cap * 4, s)) ||
+         (rc = m->rowbase.ensure((size_t)(nn + 1) * 4, s))))
         return rc;
     {
         // the largest sort of the build: input keys, strided candidates or mask-sort items
@@ -582,7 +619,7 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
         if (n_cand > big) big = n_cand;
         if (items > big) big = items;
         const int64_t scan_ints = sort_scan_ints(big);
-        if (scan_ints > 0 && (rc = m->scan.ensure((size_t)scan_ints * 4))) return rc;
+        if (scan_ints > 0 && (rc = m->scan.ensure((size_t)scan_ints * 4, s))) return rc;
         m->ws.cnt = scan_ints > 0 ? m->scan.as<uint32_t>() : nullptr;
         m->ws.cnt_ints = scan_ints > 0 ? (int64_t)(m->scan.bytes / 4) : 0;
     }
@@ -601,7 +638,7 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
         if (chosen == SMC_ROUTE_DENSE) {
             const int gi = m->next_grid;
             if ((rc = ensure_grid(m, gi, m->grid_cells, s)) ||
-                (rc = m->cells[gi].ensure((size_t)nn * 4)))
+                (rc = m->cells[gi].ensure((size_t)nn * 4, s)))
                 return rc;
             int32_t* grid = m->grid[gi].as<int32_t>();
             uint32_t* bits = m->bits[gi].as<uint32_t>();
@@ -635,9 +672,9 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
                 m->stale = PrevCells();
             }
             const size_t kb = (size_t)nn * (m->wide ? 8 : 4);
-            if ((rc = m->keys0.ensure(kb)) || (rc = m->keys1.ensure(kb)) ||
-                (rc = m->keys2.ensure(kb)) || (rc = m->vals0.ensure((size_t)nn * 4)) ||
-                (rc = m->vals1.ensure((size_t)nn * 4)))
+            if ((rc = m->keys0.ensure(kb, s)) || (rc = m->keys1.ensure(kb, s)) ||
+                (rc = m->keys2.ensure(kb, s)) || (rc = m->vals0.ensure((size_t)nn * 4, s)) ||
+                (rc = m->vals1.ensure((size_t)nn * 4, s)))
                 return rc;
             SMC_HIP(launch_make_keys(coords, n, g, m->wide, m->keys0.p, st, next, s));
             m->slot_clean[slot ^ 1] = true;
@@ -906,7 +943,7 @@ int smc_conv_forward(smc_map* m, const uint16_t* x, int c_in, const void* wpacke
         // one pass per offset group; the earlier ones leave float32 partial sums
         const MaskOrder& o = m->sorted_order;
         if (o.n_groups > 1) {
-            int rc = m->part.ensure((size_t)m->n * c_out * 4);
+            int rc = m->part.ensure((size_t)m->n * c_out * 4, s);
             if (rc) return rc;
         }
         const MapState* dst = m->state.as<MapState>() + m->slot;
@@ -945,7 +982,7 @@ int smc_conv_forward(smc_map* m, const uint16_t* x, int c_in, const void* wpacke
     if (slab > (double)((size_t)1 << 46)) return fail(SMC_ERR_ALLOC, "slab of %.3g bytes", slab);
     // at least one row: lanes with nothing to add read row 0
     if (slab < (double)c_out * 4.0) slab = (double)c_out * 4.0;
-    int rc = m->part.ensure((size_t)slab);
+    int rc = m->part.ensure((size_t)slab, s);
     if (rc) return rc;
     StageTimer t_g(m, SMC_STAGE_GEMM, s);
     SMC_HIP(launch_gemm_nc(x, c_in, wpacked, c_out, taps, m->pair_in.as<int32_t>(),

@@ -74,6 +74,12 @@ def test_argument_errors_without_gpu(L):
     assert L.smc_weight_pack(None, 3, 16, 16, None, None) == 1
     assert L.smc_map_destroy(h) == 0
     assert L.smc_map_destroy(None) == 0
+    # the allocator pair: both set or both NULL
+    free_only = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p)(
+        lambda ctx, p, s: None)
+    assert L.smc_set_allocator(None, ctypes.cast(free_only, ctypes.c_void_p), None) == 1
+    assert b"both" in L.smc_last_error()
+    assert L.smc_set_allocator(None, None, None) == 0
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
