@@ -54,42 +54,65 @@ __device__ inline void st_release(uint64_t* p, uint64_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Sum of the counts of entry column d over blocks pb, pb-1, ... back to the
-// first block that has published its inclusive prefix (or block 0). Entries
-// are read 8 at a time so a walk over many blocks costs few round trips.
-__device__ inline uint32_t lookback8(uint64_t* look, int stride, int d, int64_t pb,
-                                     uint32_t epoch, uint32_t* status) {
+// Look-back for the DPT consecutive digits d0 .. d0 + DPT - 1 of one thread
+// at once: prefix[j] = the counts of digit d0 + j over blocks pb, pb - 1, ...
+// back to the first that has published its inclusive prefix (or block 0).
+// Each round trip reads W predecessors of every digit still open (W DPT =
+// 16 entries in flight), so the digits' walks overlap instead of running one
+// after another.
+template <int DPT>
+__device__ inline void lookback_multi(uint64_t* look, int stride, int d0, int64_t pb,
+                                      uint32_t epoch, uint32_t* status, uint32_t (&prefix)[DPT]) {
+    constexpr int W = 16 / DPT > 1 ? 16 / DPT : 2;
     const uint32_t ep = epoch & 0x3FFFFFFFu;
-    uint32_t prefix = 0;
-    uint32_t spins = 0;
-    while (pb >= 0) {
-        uint64_t e[8];
+    bool open[DPT];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) e[j] = pb - j >= 0 ? ld_acquire(&look[(pb - j) * stride + d]) : 0;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (pb - j < 0) return prefix;
-            while ((uint32_t)(e[j] >> 34) != ep) {
-                if (++spins > kSpinLimit) {
-                    atomicOr(status, kStSortStall);
-                    return prefix;
-                }
-                __builtin_amdgcn_s_sleep(1);
-                e[j] = ld_acquire(&look[(pb - j) * stride + d]);
-            }
-            prefix += (uint32_t)e[j];
-            if (((e[j] >> 32) & 3u) == kIncl) return prefix;
-        }
-        pb -= 8;
+    for (int j = 0; j < DPT; ++j) {
+        prefix[j] = 0;
+        open[j] = pb >= 0;
     }
-    return prefix;
+    uint32_t spins = 0;
+    for (int64_t top = pb; top >= 0; top -= W) {
+        uint64_t e[DPT][W];
+#pragma unroll
+        for (int j = 0; j < DPT; ++j)
+#pragma unroll
+            for (int i = 0; i < W; ++i)
+                e[j][i] = open[j] && top - i >= 0 ? ld_acquire(&look[(top - i) * stride + d0 + j]) : 0;
+        bool any = false;
+#pragma unroll
+        for (int j = 0; j < DPT; ++j) {
+#pragma unroll
+            for (int i = 0; i < W; ++i) {
+                if (!open[j]) break;
+                if (top - i < 0) {
+                    open[j] = false;
+                    break;
+                }
+                while ((uint32_t)(e[j][i] >> 34) != ep) {
+                    if (++spins > kSpinLimit) {
+                        atomicOr(status, kStSortStall);
+                        e[j][i] = (uint64_t)kIncl << 32;           // give up: count 0, closes
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                    e[j][i] = ld_acquire(&look[(top - i) * stride + d0 + j]);
+                }
+                prefix[j] += (uint32_t)e[j][i];
+                if (((e[j][i] >> 32) & 3u) == kIncl) open[j] = false;
+            }
+            any = any || open[j];
+        }
+        if (!any) break;
+    }
 }
 
 template <typename K, int BITS>
 __global__ __launch_bounds__(kOsThreads) void k_os_pass(
     const K* __restrict__ kin, const uint32_t* __restrict__ vin, K* __restrict__ kout,
     uint32_t* __restrict__ vout, int64_t n, int shift, const uint32_t* __restrict__ hist,
-    uint64_t* __restrict__ look, uint32_t* ticket, uint32_t epoch, uint32_t* status) {
+    uint64_t* __restrict__ look, uint32_t* ticket, bool by_index, uint32_t epoch,
+    uint32_t* status) {
     constexpr int BINS = 1 << BITS;
     constexpr int DPT = BINS / kOsThreads;      // digits per thread
     __shared__ uint32_t s_bid;
@@ -98,13 +121,16 @@ __global__ __launch_bounds__(kOsThreads) void k_os_pass(
     __shared__ uint32_t s_part[kOsThreads];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
 
-    if (tid == 0) s_bid = atomicAdd(ticket, 1u);
+    // tile of this block: the block index when the grid fits on the device at
+    // once (every block then runs whatever the dispatch order), else a ticket
+    // taken on arrival, so every tile a block waits on is already running
+    if (tid == 0 && !by_index) s_bid = atomicAdd(ticket, 1u);
 #pragma unroll
     for (int j = 0; j < DPT; ++j)
 #pragma unroll
         for (int v = 0; v < kOsWaves; ++v) s_wcnt[v][tid * DPT + j] = 0;
     __syncthreads();
-    const uint32_t bid = s_bid;
+    const uint32_t bid = by_index ? blockIdx.x : s_bid;
     const int64_t base = (int64_t)bid * kOsTile + (int64_t)w * (kOsTile / kOsWaves);
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
@@ -178,16 +204,16 @@ __global__ __launch_bounds__(kOsThreads) void k_os_pass(
         }
     }
 
-    // decoupled look-back over the blocks before this one, 8 entries per round trip
+    // decoupled look-back over the blocks before this one, the thread's digits together
+    if (bid > 0) {
+        uint32_t prefix[DPT];
+        lookback_multi<DPT>(look, BINS, tid * DPT, (int64_t)bid - 1, epoch, status, prefix);
 #pragma unroll
-    for (int j = 0; j < DPT; ++j) {
-        int d = tid * DPT + j;
-        uint32_t prefix = 0;
-        if (bid > 0) {
-            prefix = lookback8(look, BINS, d, (int64_t)bid - 1, epoch, status);
-            st_release(&look[(int64_t)bid * BINS + d], lb_pack(epoch, kIncl, prefix + tile_cnt[j]));
+        for (int j = 0; j < DPT; ++j) {
+            const int d = tid * DPT + j;
+            st_release(&look[(int64_t)bid * BINS + d], lb_pack(epoch, kIncl, prefix[j] + tile_cnt[j]));
+            s_base[d] += prefix[j];
         }
-        s_base[d] += prefix;
     }
     __syncthreads();
 
@@ -201,7 +227,7 @@ __global__ __launch_bounds__(kOsThreads) void k_os_pass(
         kout[pos] = key[i];
         vout[pos] = val[i];
     }
-    if (bid == gridDim.x - 1 && tid == 0) atomicExch(ticket, 0u);   // every block holds its ticket
+    if (!by_index && bid == gridDim.x - 1 && tid == 0) atomicExch(ticket, 0u);   // all tickets taken
 }
 
 constexpr int kManyTiles = 64;                  // above this many tiles: reduce, then scan
@@ -408,13 +434,33 @@ __global__ __launch_bounds__(kOsThreads) void k_key_hist(const K* __restrict__ k
         if (s_h[i]) atomicAdd(&hist[i], s_h[i]);
 }
 
+// Whether `blocks` blocks of k_os_pass<K, BITS> fit on the current device at
+// once (occupancy per CU times CUs, queried once per instance and device).
+template <typename K, int BITS>
+bool pass_fits(unsigned blocks) {
+    constexpr int kDevs = 64;
+    static int64_t cap[kDevs] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) return false;
+    if (cap[dev] == 0) {
+        int per_cu = 0, n_cu = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_os_pass<K, BITS>, kOsThreads,
+                                                         0) != hipSuccess ||
+            hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return false;
+        cap[dev] = (int64_t)per_cu * n_cu > 0 ? (int64_t)per_cu * n_cu : -1;
+    }
+    return (int64_t)blocks <= cap[dev];
+}
+
 template <typename K, int BITS>
 hipError_t launch_pass(const K* kin, const uint32_t* vin, K* kout, uint32_t* vout, int64_t n,
                        int shift, const uint32_t* hist, uint64_t* look, uint32_t* ticket,
                        uint32_t epoch, uint32_t* status, hipStream_t s) {
     unsigned blocks = (unsigned)((n + kOsTile - 1) / kOsTile);
+    const bool by_index = pass_fits<K, BITS>(blocks);
     launch(k_os_pass<K, BITS>, blocks, kOsThreads, 0, s, kin, vin, kout, vout, n, shift, hist, look,
-                                                     ticket, epoch, status);
+           ticket, by_index, epoch, status);
     return hipGetLastError();
 }
 
