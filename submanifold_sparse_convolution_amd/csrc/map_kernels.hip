@@ -251,6 +251,29 @@ __device__ inline int64_t lower_bound(const K* __restrict__ keys, int64_t n, K t
     return lo;
 }
 
+// lower_bound of t in the sorted keys, in two levels: first over the
+// splitter table in LDS (s_split[i] = keys[i << sh], ns entries), then over
+// the one run of 2^sh keys that can hold the answer (keys of run i - 1 are
+// below t when splitter i - 1 is, and splitter i is not).
+template <typename K>
+__device__ inline int64_t lower_bound_split(const K* __restrict__ keys, int64_t n, K t,
+                                            const K* s_split, int ns, int sh) {
+    int lo = 0, len = ns;
+    while (len > 0) {
+        const int half = len >> 1;
+        if (s_split[lo + half] < t) {
+            lo += half + 1;
+            len -= half + 1;
+        } else {
+            len = half;
+        }
+    }
+    if (lo == 0) return 0;                        // keys[0] >= t
+    const int64_t a = ((int64_t)(lo - 1) << sh) + 1;
+    const int64_t b = lo < ns ? (int64_t)lo << sh : n;
+    return a + lower_bound(keys + a, b - a, t);
+}
+
 // Lanes per sorted key: one per (dx, dy) column (9 for K = 3, 25 for K = 5),
 // rounded up to a power of two. The K taps of a column (dz = -r .. r) have
 // consecutive keys, and so sit at consecutive sorted positions when
@@ -261,12 +284,17 @@ template <typename K, int KS>
 __global__ __launch_bounds__(kBlock) void k_sorted_lookup(const K* __restrict__ keys,
                                                           const uint32_t* __restrict__ vals,
                                                           int64_t n, Geom g,
+                                                          const K* __restrict__ split, int sh,
                                                           int32_t* __restrict__ nbr,
                                                           uint32_t* __restrict__ mask,
                                                           MapState* st) {
     constexpr int R = (KS - 1) / 2, COLS = KS * KS, KV = KS * KS * KS;
     constexpr int LANES = KS == 3 ? 16 : 32;
     constexpr int MW = (KV + 31) / 32;
+    __shared__ K s_split[kMaxSplit];
+    const int ns = (int)((n + ((int64_t)1 << sh) - 1) >> sh);
+    for (int i = threadIdx.x; i < ns; i += blockDim.x) s_split[i] = split[i];
+    __syncthreads();
     const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
     const int64_t s = t / LANES;
     const int c = (int)(t % LANES);
@@ -289,7 +317,7 @@ __global__ __launch_bounds__(kBlock) void k_sorted_lookup(const K* __restrict__ 
                 if (j > 0 && keys[j - 1] >= first) --j;
             if (s + 1 < n && keys[s + 1] == q) atomicOr(&st->status, kStDuplicate);
         } else {
-            j = lower_bound(keys, n, first);
+            j = lower_bound_split(keys, n, first, s_split, ns, sh);
         }
 #pragma unroll
         for (int dz = 0; dz < KS; ++dz) {
@@ -387,21 +415,26 @@ hipError_t launch_make_keys(const int32_t* coords, int64_t n, const Geom& g, boo
 }
 
 hipError_t launch_sorted_lookup(const void* keys, const uint32_t* vals, int64_t n, const Geom& g,
-                                bool wide, int32_t* nbr, uint32_t* mask, MapState* st,
-                                hipStream_t s) {
+                                bool wide, const void* split, int split_shift, int32_t* nbr,
+                                uint32_t* mask, MapState* st, hipStream_t s) {
+    if (((n + ((int64_t)1 << split_shift) - 1) >> split_shift) > kMaxSplit) return hipErrorInvalidValue;
     if (g.ksize == 5) {
         if (wide)
             launch(k_sorted_lookup<uint64_t, 5>, blocks_for(n * 32), kBlock, 0, s,
-                   (const uint64_t*)keys, vals, n, g, nbr, mask, st);
+                   (const uint64_t*)keys, vals, n, g, (const uint64_t*)split, split_shift, nbr,
+                   mask, st);
         else
             launch(k_sorted_lookup<uint32_t, 5>, blocks_for(n * 32), kBlock, 0, s,
-                   (const uint32_t*)keys, vals, n, g, nbr, mask, st);
+                   (const uint32_t*)keys, vals, n, g, (const uint32_t*)split, split_shift, nbr,
+                   mask, st);
     } else if (wide) {
         launch(k_sorted_lookup<uint64_t, 3>, blocks_for(n * 16), kBlock, 0, s,
-               (const uint64_t*)keys, vals, n, g, nbr, mask, st);
+               (const uint64_t*)keys, vals, n, g, (const uint64_t*)split, split_shift, nbr, mask,
+               st);
     } else {
         launch(k_sorted_lookup<uint32_t, 3>, blocks_for(n * 16), kBlock, 0, s,
-               (const uint32_t*)keys, vals, n, g, nbr, mask, st);
+               (const uint32_t*)keys, vals, n, g, (const uint32_t*)split, split_shift, nbr, mask,
+               st);
     }
     return hipGetLastError();
 }

@@ -112,7 +112,7 @@ __global__ __launch_bounds__(kOsThreads) void k_os_pass(
     const K* __restrict__ kin, const uint32_t* __restrict__ vin, K* __restrict__ kout,
     uint32_t* __restrict__ vout, int64_t n, int shift, const uint32_t* __restrict__ hist,
     uint64_t* __restrict__ look, uint32_t* ticket, bool by_index, uint32_t epoch,
-    uint32_t* status) {
+    uint32_t* status, K* __restrict__ split, int split_shift) {
     constexpr int BINS = 1 << BITS;
     constexpr int DPT = BINS / kOsThreads;      // digits per thread
     __shared__ uint32_t s_bid;
@@ -226,6 +226,7 @@ __global__ __launch_bounds__(kOsThreads) void k_os_pass(
         if (pos >= n) pos = n - 1;               // only reachable after a stalled wait
         kout[pos] = key[i];
         vout[pos] = val[i];
+        if (split && (pos & (((int64_t)1 << split_shift) - 1)) == 0) split[pos >> split_shift] = key[i];
     }
     if (!by_index && bid == gridDim.x - 1 && tid == 0) atomicExch(ticket, 0u);   // all tickets taken
 }
@@ -354,7 +355,7 @@ template <typename K, int BITS>
 __global__ __launch_bounds__(kOsThreads) void k_rs_scatter(
     const K* __restrict__ kin, const uint32_t* __restrict__ vin, K* __restrict__ kout,
     uint32_t* __restrict__ vout, int64_t n, int shift, const uint32_t* __restrict__ cnt,
-    const uint32_t* __restrict__ seg, int64_t tiles) {
+    const uint32_t* __restrict__ seg, int64_t tiles, K* __restrict__ split, int split_shift) {
     constexpr int BINS = 1 << BITS;
     constexpr int DPT = BINS / kOsThreads;
     __shared__ uint32_t s_wcnt[kOsWaves][BINS];
@@ -393,12 +394,13 @@ __global__ __launch_bounds__(kOsThreads) void k_rs_scatter(
         if (pos >= n) pos = n - 1;
         kout[pos] = key[i];
         vout[pos] = val[i];
+        if (split && (pos & (((int64_t)1 << split_shift) - 1)) == 0) split[pos >> split_shift] = key[i];
     }
 }
 
 template <typename K, int BITS>
 hipError_t launch_rs_pass(const K* kin, const uint32_t* vin, K* kout, uint32_t* vout, int64_t n,
-                          int shift, uint32_t* cnt, hipStream_t s) {
+                          int shift, uint32_t* cnt, K* split, int split_shift, hipStream_t s) {
     const int64_t tiles = (n + kOsTile - 1) / kOsTile;
     const int64_t len = tiles * (1 << BITS);
     const int64_t nseg = (len + kScanSeg - 1) / kScanSeg;
@@ -407,7 +409,7 @@ hipError_t launch_rs_pass(const K* kin, const uint32_t* vin, K* kout, uint32_t* 
     launch(k_scan_segments, (unsigned)nseg, 1024, 0, s, cnt, len, seg);
     launch(k_scan_top, 1u, 1024, 0, s, seg, nseg);
     launch(k_rs_scatter<K, BITS>, (unsigned)tiles, kOsThreads, 0, s, kin, vin, kout, vout, n, shift,
-           (const uint32_t*)cnt, (const uint32_t*)seg, tiles);
+           (const uint32_t*)cnt, (const uint32_t*)seg, tiles, split, split_shift);
     return hipGetLastError();
 }
 
@@ -456,11 +458,11 @@ bool pass_fits(unsigned blocks) {
 template <typename K, int BITS>
 hipError_t launch_pass(const K* kin, const uint32_t* vin, K* kout, uint32_t* vout, int64_t n,
                        int shift, const uint32_t* hist, uint64_t* look, uint32_t* ticket,
-                       uint32_t epoch, uint32_t* status, hipStream_t s) {
+                       uint32_t epoch, uint32_t* status, K* split, int split_shift, hipStream_t s) {
     unsigned blocks = (unsigned)((n + kOsTile - 1) / kOsTile);
     const bool by_index = pass_fits<K, BITS>(blocks);
     launch(k_os_pass<K, BITS>, blocks, kOsThreads, 0, s, kin, vin, kout, vout, n, shift, hist, look,
-           ticket, by_index, epoch, status);
+           ticket, by_index, epoch, status, split, split_shift);
     return hipGetLastError();
 }
 
@@ -468,7 +470,7 @@ template <typename K>
 hipError_t sort_impl(const K* keys_in, const uint32_t* vals_in, int64_t n, const SortPlan& plan,
                      const uint32_t* hist, K* kbuf0, K* kbuf1, uint32_t* vbuf0, uint32_t* vbuf1,
                      SortWork& ws, uint32_t* status, const K** keys_out,
-                     const uint32_t** vals_out, hipStream_t s) {
+                     const uint32_t** vals_out, K* split, int split_shift, hipStream_t s) {
     const K* kcur = keys_in;
     const uint32_t* vcur = vals_in;
     K* kdst[2] = {kbuf0, kbuf1};
@@ -480,12 +482,13 @@ hipError_t sort_impl(const K* keys_in, const uint32_t* vals_in, int64_t n, const
         const uint32_t* h = hist + (size_t)p * bins;
         hipError_t e;
         const int64_t tiles = (n + kOsTile - 1) / kOsTile;
+        K* sp = p == plan.passes - 1 ? split : nullptr;           // the last pass lists splitters
         if (tiles > kManyTiles && ws.cnt && ws.cnt_ints >= sort_scan_ints(n)) {
             switch (plan.bits) {
-                case 8: e = launch_rs_pass<K, 8>(kcur, vcur, kdst[p & 1], vdst[p & 1], n, p * 8, ws.cnt, s); break;
-                case 9: e = launch_rs_pass<K, 9>(kcur, vcur, kdst[p & 1], vdst[p & 1], n, p * 9, ws.cnt, s); break;
-                case 10: e = launch_rs_pass<K, 10>(kcur, vcur, kdst[p & 1], vdst[p & 1], n, p * 10, ws.cnt, s); break;
-                default: e = launch_rs_pass<K, 11>(kcur, vcur, kdst[p & 1], vdst[p & 1], n, p * 11, ws.cnt, s); break;
+                case 8: e = launch_rs_pass<K, 8>(kcur, vcur, kdst[p & 1], vdst[p & 1], n, p * 8, ws.cnt, sp, split_shift, s); break;
+                case 9: e = launch_rs_pass<K, 9>(kcur, vcur, kdst[p & 1], vdst[p & 1], n, p * 9, ws.cnt, sp, split_shift, s); break;
+                case 10: e = launch_rs_pass<K, 10>(kcur, vcur, kdst[p & 1], vdst[p & 1], n, p * 10, ws.cnt, sp, split_shift, s); break;
+                default: e = launch_rs_pass<K, 11>(kcur, vcur, kdst[p & 1], vdst[p & 1], n, p * 11, ws.cnt, sp, split_shift, s); break;
             }
             if (e != hipSuccess) return e;
             kcur = kdst[p & 1];
@@ -493,10 +496,10 @@ hipError_t sort_impl(const K* keys_in, const uint32_t* vals_in, int64_t n, const
             continue;
         }
         switch (plan.bits) {
-            case 8: e = launch_pass<K, 8>(kcur, vcur, kdst[p & 1], vdst[p & 1], n, p * 8, h, ws.look, ws.ticket, epoch, status, s); break;
-            case 9: e = launch_pass<K, 9>(kcur, vcur, kdst[p & 1], vdst[p & 1], n, p * 9, h, ws.look, ws.ticket, epoch, status, s); break;
-            case 10: e = launch_pass<K, 10>(kcur, vcur, kdst[p & 1], vdst[p & 1], n, p * 10, h, ws.look, ws.ticket, epoch, status, s); break;
-            default: e = launch_pass<K, 11>(kcur, vcur, kdst[p & 1], vdst[p & 1], n, p * 11, h, ws.look, ws.ticket, epoch, status, s); break;
+            case 8: e = launch_pass<K, 8>(kcur, vcur, kdst[p & 1], vdst[p & 1], n, p * 8, h, ws.look, ws.ticket, epoch, status, sp, split_shift, s); break;
+            case 9: e = launch_pass<K, 9>(kcur, vcur, kdst[p & 1], vdst[p & 1], n, p * 9, h, ws.look, ws.ticket, epoch, status, sp, split_shift, s); break;
+            case 10: e = launch_pass<K, 10>(kcur, vcur, kdst[p & 1], vdst[p & 1], n, p * 10, h, ws.look, ws.ticket, epoch, status, sp, split_shift, s); break;
+            default: e = launch_pass<K, 11>(kcur, vcur, kdst[p & 1], vdst[p & 1], n, p * 11, h, ws.look, ws.ticket, epoch, status, sp, split_shift, s); break;
         }
         if (e != hipSuccess) return e;
         kcur = kdst[p & 1];
@@ -549,18 +552,18 @@ hipError_t radix_sort_u32(const uint32_t* keys_in, const uint32_t* vals_in, int6
                           const SortPlan& plan, const uint32_t* hist, uint32_t* kbuf0,
                           uint32_t* kbuf1, uint32_t* vbuf0, uint32_t* vbuf1, SortWork& ws,
                           uint32_t* status, const uint32_t** keys_out, const uint32_t** vals_out,
-                          hipStream_t s) {
+                          hipStream_t s, void* split, int split_shift) {
     return sort_impl<uint32_t>(keys_in, vals_in, n, plan, hist, kbuf0, kbuf1, vbuf0, vbuf1, ws,
-                               status, keys_out, vals_out, s);
+                               status, keys_out, vals_out, (uint32_t*)split, split_shift, s);
 }
 
 hipError_t radix_sort_u64(const uint64_t* keys_in, const uint32_t* vals_in, int64_t n,
                           const SortPlan& plan, const uint32_t* hist, uint64_t* kbuf0,
                           uint64_t* kbuf1, uint32_t* vbuf0, uint32_t* vbuf1, SortWork& ws,
                           uint32_t* status, const uint64_t** keys_out, const uint32_t** vals_out,
-                          hipStream_t s) {
+                          hipStream_t s, void* split, int split_shift) {
     return sort_impl<uint64_t>(keys_in, vals_in, n, plan, hist, kbuf0, kbuf1, vbuf0, vbuf1, ws,
-                               status, keys_out, vals_out, s);
+                               status, keys_out, vals_out, (uint64_t*)split, split_shift, s);
 }
 
 }  // namespace smc

@@ -15,6 +15,7 @@ constexpr int kTileM = 64;          // granularity of the per-tap pair counts re
 constexpr int kCapAlign = 256;      // each tap's run of the pair arrays: n rounded up to this
                                     // (a multiple of every GEMM tile height)
 constexpr int kBlock = 256;         // threads per block for the map kernels
+constexpr int kMaxSplit = 1024;     // splitter table entries of the sorted route's searches
 
 // Per-kernel timing. While a stage timer of the API is active, take() hands
 // out a start/stop event pair for every kernel launched, and the launch
@@ -147,9 +148,17 @@ hipError_t launch_dense_lookup(const int32_t* coords, int64_t n, const Geom& g, 
                                const uint32_t* bits, int32_t* nbr, uint32_t* mask, hipStream_t s);
 hipError_t launch_make_keys(const int32_t* coords, int64_t n, const Geom& g, bool wide, void* keys,
                             MapState* st, const NextRecord& next, hipStream_t s);
+// split: the key sort's splitter table (keys i << split_shift), which every
+// block reads into LDS for the top levels of its searches.
 hipError_t launch_sorted_lookup(const void* keys, const uint32_t* vals, int64_t n, const Geom& g,
-                                bool wide, int32_t* nbr, uint32_t* mask, MapState* st,
-                                hipStream_t s);
+                                bool wide, const void* split, int split_shift, int32_t* nbr,
+                                uint32_t* mask, MapState* st, hipStream_t s);
+// Smallest shift with ceil(n / 2^shift) <= kMaxSplit.
+inline int split_shift_for(int64_t n) {
+    int sh = 0;
+    while (((n + ((int64_t)1 << sh) - 1) >> sh) > kMaxSplit) ++sh;
+    return sh;
+}
 
 // ---- strided maps (strided_kernels.hip) ----
 // Output grid of a strided layer and the packing of its cells into 64-bit
@@ -195,12 +204,16 @@ hipError_t radix_sort_u32(const uint32_t* keys_in, const uint32_t* vals_in, int6
                           const SortPlan& plan, const uint32_t* hist, uint32_t* kbuf0,
                           uint32_t* kbuf1, uint32_t* vbuf0, uint32_t* vbuf1, SortWork& ws,
                           uint32_t* status, const uint32_t** keys_out, const uint32_t** vals_out,
-                          hipStream_t s);
+                          hipStream_t s, void* split = nullptr, int split_shift = 0);
 hipError_t radix_sort_u64(const uint64_t* keys_in, const uint32_t* vals_in, int64_t n,
                           const SortPlan& plan, const uint32_t* hist, uint64_t* kbuf0,
                           uint64_t* kbuf1, uint32_t* vbuf0, uint32_t* vbuf1, SortWork& ws,
                           uint32_t* status, const uint64_t** keys_out, const uint32_t** vals_out,
-                          hipStream_t s);
+                          hipStream_t s, void* split = nullptr, int split_shift = 0);
+// split (optional): the sort's last pass also writes split[i] = sorted key
+// i << split_shift, for every i with i << split_shift < n (a splitter table
+// for two-level searches of the sorted keys).
+
 
 // ---- compaction (compact_kernels.hip) ----
 // Digit histograms of the mask sort and pairs per tap, in one read of the

@@ -154,6 +154,7 @@ struct smc_map {
     DevBuf pair_in, pair_out, pair_slot, rowbase;
     int64_t cap = 0;                  // pairs per tap the pair arrays hold (n rounded up to a tile)
     DevBuf part;                      // float32 partial-product slab of the pair-list forward
+    DevBuf split;                     // splitter table of the sorted route's key sort
     DevBuf zrow;                      // zero row read for absent neighbours (mask-tile GEMM)
     bool has_pairs = false;
     bool has_sort = false;
@@ -381,7 +382,7 @@ int smc_map_destroy(smc_map* m) {
                           &m->mask, &m->mkey0, &m->mkey1, &m->mval0, &m->mval1, &m->okeys,
                           &m->pair_in, &m->pair_out, &m->pair_slot, &m->rowbase, &m->part,
                           &m->zrow, &m->ck0, &m->ck1, &m->ck2, &m->cv0, &m->cv1, &m->chist,
-                          &m->ucounts, &m->ocoords, &m->qcoords, &m->scan};
+                          &m->ucounts, &m->ocoords, &m->qcoords, &m->scan, &m->split};
         for (DevBuf* b : bufs) b->release();
         for (auto& v : m->ev_open)
             for (auto& pr : v) {
@@ -682,16 +683,23 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
             SMC_HIP(launch_key_hist(m->keys0.p, m->wide, n, kp, hist_key, s));
             const void* skeys;
             const uint32_t* svals;
+            // the key sort's last pass also lists splitters for the lookup's searches
+            const int sh = split_shift_for(n);
+            void* split = nullptr;
+            if (!strided) {
+                if ((rc = m->split.ensure((size_t)kMaxSplit * 8, s))) return rc;
+                split = m->split.p;
+            }
             if (m->wide) {
                 SMC_HIP(radix_sort_u64(m->keys0.as<uint64_t>(), nullptr, n, kp, hist_key,
                                        m->keys1.as<uint64_t>(), m->keys2.as<uint64_t>(),
                                        m->vals0.as<uint32_t>(), m->vals1.as<uint32_t>(), m->ws,
-                                       status, (const uint64_t**)&skeys, &svals, s));
+                                       status, (const uint64_t**)&skeys, &svals, s, split, sh));
             } else {
                 SMC_HIP(radix_sort_u32(m->keys0.as<uint32_t>(), nullptr, n, kp, hist_key,
                                        m->keys1.as<uint32_t>(), m->keys2.as<uint32_t>(),
                                        m->vals0.as<uint32_t>(), m->vals1.as<uint32_t>(), m->ws,
-                                       status, (const uint32_t**)&skeys, &svals, s));
+                                       status, (const uint32_t**)&skeys, &svals, s, split, sh));
             }
             if (strided) {
                 SMC_HIP(launch_key_dups(skeys, m->wide, n, st, s));
@@ -699,7 +707,8 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
                 SMC_HIP(launch_query_lookup(skeys, svals, n, g, m->wide, m->qcoords.as<int32_t>(),
                                             rows, nbr, mask, s));
             } else {
-                SMC_HIP(launch_sorted_lookup(skeys, svals, n, g, m->wide, nbr, mask, st, s));
+                SMC_HIP(launch_sorted_lookup(skeys, svals, n, g, m->wide, split, sh, nbr, mask, st,
+                                             s));
             }
         }
         t_nb.finish();
