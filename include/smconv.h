@@ -114,9 +114,11 @@ typedef struct smc_map_info_s {
 /*
  * Device allocator for every buffer a map handle takes from now on, for the
  * whole process: alloc(ctx, bytes, stream) returns a device pointer on the
- * current device, usable on `stream` (the hipStream_t of the call that needs
- * it, as void*; NULL: the null stream), or NULL on failure (the call then
- * returns SMC_ERR_ALLOC); free(ctx, ptr, stream) gives it back. A caller with
+ * current device, aligned to 256 bytes, usable on `stream` (the hipStream_t of
+ * the call that needs it, as void*; NULL: the null stream), or NULL on failure
+ * (the call then returns SMC_ERR_ALLOC; a pointer not aligned to 256 bytes is
+ * given back and the call returns SMC_ERR_ALLOC too); free(ctx, ptr, stream)
+ * gives it back. A caller with
  * its own pool (e.g. torch's caching allocator, bound from Python) keeps all
  * device memory in that pool this way. Both NULL restores hipMalloc/hipFree.
  * A buffer is always freed by the allocator that made it, even after the

@@ -169,6 +169,13 @@ __device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, uint32_t* total) 
     return excl;
 }
 
+// OR of v over the wave's lanes (the same value in every lane).
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o, 64);
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);   // uniform: kept in a scalar register
+}
+
 // Count of lower lanes of the wave whose bit is set in m.
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
@@ -300,10 +307,12 @@ __device__ __forceinline__ void compact_chunk(CompactLds& L, uint32_t m, uint32_
     const int64_t base0 = (int64_t)bid * kCChunk;
     const int64_t row = base0 + tid;
     const uint32_t deg = m ? (uint32_t)__popc(m & ~(1u << kCentre)) : 0u;
-    // per-wave count of each tap (lane k keeps tap k) and of slab rows (lane kTaps)
+    // per-wave count of each tap (lane k keeps tap k) and of slab rows (lane kTaps),
+    // over the taps some row of the wave has (the wave's OR of masks)
+    const uint32_t uni = wave_or(m);
     uint32_t cnt = 0;
-#pragma unroll
-    for (int k = 0; k < kTaps; ++k) {
+    for (uint32_t u = uni; u; u &= u - 1) {
+        const int k = __builtin_ctz(u);
         const uint32_t c = (uint32_t)__popcll(__ballot((m >> k) & 1u));
         if (lane == k) cnt = c;
     }
@@ -394,8 +403,8 @@ __device__ __forceinline__ void compact_chunk(CompactLds& L, uint32_t m, uint32_
     // list the chunk's pairs in output order: tap-major, rows ascending. Lane k
     // holds the wave's first list slot of tap k; the loop reads it with readlane.
     const uint32_t first = lane < kTaps ? L.loc[lane] + L.wc[w][lane] : 0u;
-#pragma unroll
-    for (int k = 0; k < kTaps; ++k) {
+    for (uint32_t u = uni; u; u &= u - 1) {
+        const int k = __builtin_ctz(u);
         const uint64_t b = __ballot((m >> k) & 1u);
         const uint32_t f = (uint32_t)__builtin_amdgcn_readlane((int)first, k);
         if ((m >> k) & 1u) L.list[f + lanes_below(b)] = (uint16_t)(tid | (k << 8));
@@ -525,14 +534,34 @@ __global__ __launch_bounds__(kCThreads) void k_lookup_compact(
     if (!by_index && bid == gridDim.x - 1 && tid == 0) atomicExch(ticket, 0u);
 }
 
-// Compaction for the 5 x 5 x 5 kernel: 125 taps, masks of 4 words. One row
-// per thread, 256-row chunks in row order; per-tap counts per wave from
-// ballots, block look-back over 126 columns (125 taps + slab rows, 2 lanes
-// per column), then each row writes its own pairs (positions from the wave
-// offsets and its rank in the ballot), its neighbour rows read straight
-// from the table. Same outputs and layout as the 3 x 3 x 3 compaction.
+// Compaction for the 5 x 5 x 5 kernel: 125 taps, masks of 4 words, 256-row
+// chunks in row order, a block look-back over 126 columns (125 taps + slab
+// rows, 2 lanes per column). Same outputs and layout as the 3 x 3 x 3
+// compaction.
 constexpr int kK5Taps = 125, kK5Centre = 62, kK5Cols = kK5Taps + 1;
 
+// Index of the r-th set bit (r < popcount) of m.
+__device__ __forceinline__ int select_bit(uint64_t m, uint32_t r) {
+    int pos = 0;
+#pragma unroll
+    for (int w = 32; w > 0; w >>= 1) {
+        const uint32_t c = (uint32_t)__popcll(m & ((1ull << w) - 1));
+        if (r >= c) {
+            r -= c;
+            m >>= w;
+            pos += w;
+        }
+    }
+    return pos;
+}
+
+// K = 5 compaction, one 256-row chunk per block (a row per thread). Each wave
+// transposes its 64 masks through LDS so that lane j holds taps j and 64 + j: the
+// rows with the tap (a 64-bit lane set) and their count. After the column
+// look-back the wave lists its pairs in (tap, row) order, 64 at a time, one per
+// lane: the tap by a binary search over the wave's per-tap starts, the row as the
+// r-th member of the tap's lane set; consecutive lanes then write consecutive
+// places of one tap's list, and only real pairs read the neighbour table.
 __global__ __launch_bounds__(kCThreads) void k_compact5(
     const uint32_t* __restrict__ mask, const int32_t* __restrict__ nbr, int64_t n, int64_t cap,
     int tile_m, MapState* st, int32_t* __restrict__ pair_in, int32_t* __restrict__ pair_out,
@@ -541,23 +570,44 @@ __global__ __launch_bounds__(kCThreads) void k_compact5(
     __shared__ uint32_t s_bid;
     __shared__ uint32_t s_wc[kCWaves][kK5Cols];   // per-wave counts, then offsets in the chunk
     __shared__ uint32_t s_pre[kK5Cols], s_tot[kK5Cols], s_done[kK5Cols];
+    __shared__ uint4 s_m[kCWaves][64];            // the wave's masks
+    __shared__ uint64_t s_set[kCWaves][128];      // per tap: the wave's rows with it (bit = lane)
+    __shared__ uint32_t s_beg[kCWaves][128];      // per tap: its first pair in the wave's order
+    __shared__ uint32_t s_rb[kCWaves][64];        // first slab row of each of the wave's rows
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const uint32_t bid = chunk_of_block(by_index, ticket, &s_bid);
     const int64_t row = (int64_t)bid * kCChunk + tid;
     const bool valid = row < n;
-    const int64_t rc = valid ? row : n - 1;
-    uint32_t mw[kMaxMaskWords];
-#pragma unroll
-    for (int q = 0; q < kMaxMaskWords; ++q) mw[q] = valid ? mask[rc * kMaxMaskWords + q] : 0u;
-    uint32_t pop = 0;
-#pragma unroll
-    for (int q = 0; q < kMaxMaskWords; ++q) pop += (uint32_t)__popc(mw[q]);
+    uint4 mv = make_uint4(0u, 0u, 0u, 0u);
+    if (valid) mv = reinterpret_cast<const uint4*>(mask)[row];
+    const uint32_t pop = (uint32_t)(__popc(mv.x) + __popc(mv.y) + __popc(mv.z) + __popc(mv.w));
     const uint32_t deg = pop ? pop - 1u : 0u;     // off-centre pairs of the row
-#pragma unroll
-    for (int k = 0; k < kK5Taps; ++k) {
-        const uint64_t b = __ballot((mw[k >> 5] >> (k & 31)) & 1u);
-        if (lane == 0) s_wc[w][k] = (uint32_t)__popcll(b);
+    s_m[w][lane] = mv;
+    __builtin_amdgcn_wave_barrier();
+    // lane j: bit j % 32 of words j / 32 (tap j) and 2 + j / 32 (tap 64 + j) of each row
+    uint64_t set_lo = 0, set_hi = 0;
+    {
+        const int sh = lane & 31;
+        const bool upper = lane >= 32;
+#pragma unroll 16
+        for (int r = 0; r < 64; ++r) {
+            const uint4 v = s_m[w][r];
+            set_lo |= (uint64_t)(((upper ? v.y : v.x) >> sh) & 1u) << r;
+            set_hi |= (uint64_t)(((upper ? v.w : v.z) >> sh) & 1u) << r;
+        }
     }
+    if (lane >= kK5Taps - 64) set_hi = 0;
+    const uint32_t cnt_lo = (uint32_t)__popcll(set_lo), cnt_hi = (uint32_t)__popcll(set_hi);
+    uint32_t tot_lo, tot_hi;
+    const uint32_t beg_lo = wave_excl_scan<7>(cnt_lo, &tot_lo);
+    const uint32_t beg_hi = tot_lo + wave_excl_scan<7>(cnt_hi, &tot_hi);
+    const uint32_t n_pairs = tot_lo + tot_hi;     // the wave's pairs, centre ones included
+    s_set[w][lane] = set_lo;
+    s_set[w][64 + lane] = set_hi;
+    s_beg[w][lane] = beg_lo;
+    s_beg[w][64 + lane] = lane < kK5Taps - 64 ? beg_hi : n_pairs;
+    s_wc[w][lane] = cnt_lo;
+    if (lane < kK5Taps - 64) s_wc[w][64 + lane] = cnt_hi;
     uint32_t wave_slab;
     const uint32_t excl = wave_excl_scan<7>(deg, &wave_slab);     // deg < 125
     if (lane == 0) s_wc[w][kK5Taps] = wave_slab;
@@ -575,7 +625,7 @@ __global__ __launch_bounds__(kCThreads) void k_compact5(
                            lb_pack(epoch, bid == 0 ? kIncl : kAgg, run), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
-    block_lookback<kK5Cols, 32, 2>(look, (int64_t)bid - 1, epoch, status, s_pre, s_done);
+    block_lookback<kK5Cols, 16, 2>(look, (int64_t)bid - 1, epoch, status, s_pre, s_done);
     if (tid < kK5Cols) {
         const uint32_t run = s_tot[tid], prefix = s_pre[tid];
         if (bid > 0)
@@ -620,27 +670,36 @@ __global__ __launch_bounds__(kCThreads) void k_compact5(
     }
     const uint32_t rb = s_pre[kK5Taps] + s_wc[w][kK5Taps] + excl;
     if (valid) rowbase[row] = (int32_t)rb;
-    const int32_t* nrow = nbr + rc * kK5Taps;
-    uint32_t rank = 0;                            // off-centre pairs of the row so far
+    s_rb[w][lane] = rb;
+    __builtin_amdgcn_wave_barrier();
+    const uint32_t cap32 = cap < (int64_t)UINT32_MAX ? (uint32_t)cap : UINT32_MAX;
+    const int64_t wave_row0 = (int64_t)bid * kCChunk + 64 * w;
+    for (uint32_t e0 = 0; e0 < n_pairs; e0 += 64) {
+        const uint32_t e = e0 + (uint32_t)lane;
+        if (e >= n_pairs) break;
+        int k = 0;                                // the last tap whose pairs start at or before e
 #pragma unroll
-    for (int q = 0; q < kMaxMaskWords; ++q) {
-        const uint32_t word = mw[q];
-#pragma unroll 4
-        for (int bb = 0; bb < 32; ++bb) {
-            const int k = 32 * q + bb;
-            if (k >= kK5Taps) break;
-            const bool has = (word >> bb) & 1u;
-            const uint64_t b = __ballot(has);
-            if (has) {
-                const int64_t pos =
-                    (int64_t)k * cap + s_pre[k] + s_wc[w][k] + lanes_below(b);
-                if (pos < (int64_t)k * cap + cap) {       // (only false after a stalled wait)
-                    pair_in[pos] = k == kK5Centre ? (int32_t)row : nrow[k];
-                    pair_out[pos] = (int32_t)row;
-                    pair_slot[pos] = k == kK5Centre ? -1 : (int32_t)(rb + rank);
-                }
-                if (k != kK5Centre) ++rank;
-            }
+        for (int step = 64; step > 0; step >>= 1)
+            if (s_beg[w][k + step] <= e) k += step;
+        const uint32_t r = e - s_beg[w][k];       // e is the tap's r-th pair of the wave
+        const int rl = select_bit(s_set[w][k], r);
+        const uint32_t p = s_pre[k] + s_wc[w][k] + r;
+        const int64_t rg = wave_row0 + rl;
+        const uint4 m = s_m[w][rl];
+        // off-centre taps of the row below k
+        const uint32_t lowk = k & 31, q = (uint32_t)k >> 5;
+        const uint32_t part = (q == 0 ? m.x : q == 1 ? m.y : q == 2 ? m.z : m.w) & ((1u << lowk) - 1u);
+        const uint32_t below = (uint32_t)__popc(part) + (q > 0 ? (uint32_t)__popc(m.x) : 0u) +
+                               (q > 1 ? (uint32_t)__popc(m.y) : 0u) +
+                               (q > 2 ? (uint32_t)__popc(m.z) : 0u) -
+                               (k > kK5Centre ? (m.y >> (kK5Centre - 32)) & 1u : 0u);
+        const bool centre = k == kK5Centre;
+        if (p < cap32 && rg < n) {                // (only false after a stalled wait)
+            const int32_t src = centre ? (int32_t)rg : nbr[rg * kK5Taps + k];
+            const int64_t pos = (int64_t)k * cap + p;
+            pair_in[pos] = src;
+            pair_out[pos] = (int32_t)rg;
+            pair_slot[pos] = centre ? -1 : (int32_t)(s_rb[w][rl] + below);
         }
     }
     if (!by_index && bid == gridDim.x - 1 && tid == 0) atomicExch(ticket, 0u);

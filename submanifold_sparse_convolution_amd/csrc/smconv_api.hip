@@ -71,6 +71,11 @@ struct DevBuf {
         if (a.alloc) {
             p = a.alloc(a.ctx, alloc, (void*)s);
             if (!p) return fail(SMC_ERR_ALLOC, "the caller's allocator returned NULL for %zu bytes", alloc);
+            if (((uintptr_t)p & 255) != 0) {     // the kernels read rows in 16-byte words
+                a.free(a.ctx, p, (void*)s);
+                p = nullptr;
+                return fail(SMC_ERR_ALLOC, "the caller's allocator returned a pointer not aligned to 256 bytes");
+            }
         } else if (hipMalloc(&p, alloc) != hipSuccess) {
             (void)hipGetLastError();
             p = nullptr;
