@@ -31,7 +31,8 @@ __device__ inline bool load_rel(const int32_t* __restrict__ coords, int64_t i, c
            (unsigned)y < (unsigned)g.ext[1] && (unsigned)z < (unsigned)g.ext[2];
 }
 
-// cell of a voxel in the grid padded by one cell on every side
+// cell of a voxel in the grid padded by r cells on every side (also the
+// sorted route's key)
 __device__ inline int64_t dense_cell(const Geom& g, int b, int x, int y, int z) {
     return b * g.sz_b + (int64_t)(x + g.pad) * g.sz_x + (int64_t)(y + g.pad) * g.sz_y + (z + g.pad);
 }
@@ -211,10 +212,12 @@ __global__ __launch_bounds__(kBlock) void k_dense_lookup5(const int32_t* __restr
     }
 }
 
-// Packed key of a voxel, fields (b | x+r | y+r | z+r) from high to low. The
-// r-cell padding keeps every neighbour query inside its field, so the key
-// of q + d is key(q) + packed(d) with no carry between fields (the
-// packed(q+d) = packed(q) + packed(d) property of the Z-Delta mapper).
+// Key of a voxel: its cell in the grid padded by r cells on every side,
+// b (X + 2r)(Y + 2r)(Z + 2r) + (x + r)(Y + 2r)(Z + 2r) + (y + r)(Z + 2r) + z + r,
+// i.e. (b, x, y, z) packed with mixed radices instead of power-of-two bit
+// fields: the same order, and since the padding keeps every neighbour inside
+// its field, key(q + d) = key(q) + key offset of d (the packed(q + d) =
+// packed(q) + packed(d) property of the Z-Delta mapper), in fewer bits.
 template <typename K>
 __global__ __launch_bounds__(kBlock) void k_make_keys(const int32_t* __restrict__ coords,
                                                       int64_t n, Geom g, K* __restrict__ keys,
@@ -225,10 +228,7 @@ __global__ __launch_bounds__(kBlock) void k_make_keys(const int32_t* __restrict_
     int b, x, y, z;
     K key;
     if (load_rel(coords, i, g, b, x, y, z)) {
-        key = (K)b;
-        key = (key << g.wx) | (K)(x + g.pad);
-        key = (key << g.wy) | (K)(y + g.pad);
-        key = (key << g.wz) | (K)(z + g.pad);
+        key = (K)dense_cell(g, b, x, y, z);
     } else {
         atomicOr(&st->status, kStRange);
         key = ~(K)0;
@@ -306,8 +306,7 @@ __global__ __launch_bounds__(kBlock) void k_sorted_lookup(const K* __restrict__ 
         // vals is a permutation of [0, n); the clamps only matter if a sort wait stalled
         const int row = (int)min(vals[s], (uint32_t)(n - 1));
         const int dx = c / KS - R, dy = c % KS - R;
-        const K delta = (K)((int64_t)dx * ((int64_t)1 << (g.wy + g.wz))) +
-                        (K)((int64_t)dy * ((int64_t)1 << g.wz));
+        const K delta = (K)(dx * g.sz_x + dy * g.sz_y);
         const K first = q + delta - (K)R;
         int64_t j;
         if (c == COLS / 2) {

@@ -14,22 +14,24 @@
 //    or by k_key_hist;
 //  * each pass is a single kernel: a block ranks its tile stably (each wave
 //    owns a contiguous quarter of the tile and keeps per-digit running
-//    counts in LDS, so no block barrier per item), then finds how many keys
-//    of each digit precede its tile by decoupled look-back over the blocks
-//    before it, then scatters.
+//    counts in LDS, so no block barrier per item), publishes its digit
+//    counts, adds up the counts of every tile before it (at most 64 tiles:
+//    one or two round trips, all loads in flight; a chain of inclusive
+//    prefixes, as in decoupled look-back, cost one round trip per few tiles:
+//    Wide key sort 11.8 us per pass), then scatters.
 // Sorts of many tiles take another route per pass (reduce, then scan): with
-// thousands of digit columns a block's look-back walks back through every
-// earlier tile's aggregate, one round trip per few tiles and digit, and a
-// pass over 8 x 10^5 keys measured about 100 us. There, one kernel counts
+// thousands of digit columns a block would read through every earlier tile's
+// counts (a look-back pass over 8 x 10^5 keys measured about 100 us). There, one kernel counts
 // each tile's digits into a digit-major table, a two-level scan turns the
 // table into global start positions, and a third kernel ranks and scatters
 // exactly like the onesweep pass. No block waits for another.
-// Look-back safety: block indices are taken from a ticket counter in launch
-// order, so a block only ever waits for blocks that already hold a ticket,
-// i.e. are running. Each wait is also bounded; a wait that runs out flags
-// the status word and the block carries on with in-bounds (wrong) output.
-// Look-back entries carry an epoch, so stale entries from earlier passes are
-// never taken for ready ones and the table needs no clearing.
+// Wait safety: when the grid does not fit on the device at once, block
+// indices are taken from a ticket counter in launch order, so a block only
+// ever waits for blocks that already hold a ticket, i.e. are running. Each
+// wait is also bounded; a wait that runs out flags the status word and the
+// block carries on with in-bounds (wrong) output. Count entries carry an
+// epoch, so stale entries from earlier passes are never taken for ready ones
+// and the table needs no clearing.
 #include "smc_internal.h"
 
 namespace smc {
@@ -41,12 +43,6 @@ constexpr int kOsItems = 8;                     // keys per thread
 constexpr int kOsTile = kOsThreads * kOsItems;  // 2048 keys per block
 constexpr uint32_t kSpinLimit = 1u << 22;
 
-// look-back entry: epoch (30 bits) | state (2 bits) | count (32 bits)
-constexpr uint64_t kAgg = 1, kIncl = 2;
-__device__ inline uint64_t lb_pack(uint32_t epoch, uint64_t state, uint32_t count) {
-    return ((uint64_t)epoch << 34) | (state << 32) | count;
-}
-
 __device__ inline uint64_t ld_acquire(const uint64_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -54,56 +50,55 @@ __device__ inline void st_release(uint64_t* p, uint64_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Look-back for the DPT consecutive digits d0 .. d0 + DPT - 1 of one thread
-// at once: prefix[j] = the counts of digit d0 + j over blocks pb, pb - 1, ...
-// back to the first that has published its inclusive prefix (or block 0).
-// Each round trip reads W predecessors of every digit still open (W DPT =
-// 16 entries in flight), so the digits' walks overlap instead of running one
-// after another.
+// Tile counts, two digits per look-back entry: entry (tile, q) of thread t
+// holds the tile's counts of digits t DPT + 2q and t DPT + 2q + 1 (16 bits
+// each: a tile has at most 2048 keys) under the pass's epoch.
+__device__ inline uint64_t agg_pack(uint32_t epoch, uint32_t c0, uint32_t c1) {
+    return ((uint64_t)epoch << 34) | ((uint64_t)c1 << 16) | c0;
+}
+
+// prefix[j] = the count of digit d0 + j (d0 = t DPT) over tiles 0 .. tiles - 1,
+// read from every one of those tiles' entries. A tile publishes its counts
+// before it waits on anything, so with all tiles running these reads take one
+// or two round trips, where a chain of inclusive prefixes would take one per
+// few tiles.
 template <int DPT>
-__device__ inline void lookback_multi(uint64_t* look, int stride, int d0, int64_t pb,
-                                      uint32_t epoch, uint32_t* status, uint32_t (&prefix)[DPT]) {
-    constexpr int W = 16 / DPT > 1 ? 16 / DPT : 2;
+__device__ inline void prefix_all(const uint64_t* look, int t, int64_t tiles, uint32_t epoch,
+                                  uint32_t* status, uint32_t (&prefix)[DPT]) {
+    constexpr int NW = (DPT + 1) / 2;
+    constexpr int B = 32 / NW;                    // tiles per batch of loads
     const uint32_t ep = epoch & 0x3FFFFFFFu;
-    bool open[DPT];
 #pragma unroll
-    for (int j = 0; j < DPT; ++j) {
-        prefix[j] = 0;
-        open[j] = pb >= 0;
-    }
+    for (int j = 0; j < DPT; ++j) prefix[j] = 0;
     uint32_t spins = 0;
-    for (int64_t top = pb; top >= 0; top -= W) {
-        uint64_t e[DPT][W];
+    for (int64_t p0 = 0; p0 < tiles; p0 += B) {
+        // (clamped, not branched: each branch around a load made the compiler wait for
+        // the load before it, so the loads went out one or two at a time)
+        uint64_t e[B][NW];
 #pragma unroll
-        for (int j = 0; j < DPT; ++j)
+        for (int i = 0; i < B; ++i) {
+            const int64_t pi = p0 + i < tiles ? p0 + i : tiles - 1;
 #pragma unroll
-            for (int i = 0; i < W; ++i)
-                e[j][i] = open[j] && top - i >= 0 ? ld_acquire(&look[(top - i) * stride + d0 + j]) : 0;
-        bool any = false;
+            for (int q = 0; q < NW; ++q) e[i][q] = ld_acquire(&look[(pi * NW + q) * kOsThreads + t]);
+        }
 #pragma unroll
-        for (int j = 0; j < DPT; ++j) {
+        for (int i = 0; i < B; ++i) {
+            if (p0 + i >= tiles) break;
 #pragma unroll
-            for (int i = 0; i < W; ++i) {
-                if (!open[j]) break;
-                if (top - i < 0) {
-                    open[j] = false;
-                    break;
-                }
-                while ((uint32_t)(e[j][i] >> 34) != ep) {
+            for (int q = 0; q < NW; ++q) {
+                while ((uint32_t)(e[i][q] >> 34) != ep) {
                     if (++spins > kSpinLimit) {
                         atomicOr(status, kStSortStall);
-                        e[j][i] = (uint64_t)kIncl << 32;           // give up: count 0, closes
+                        e[i][q] = 0;                       // give up: counts 0
                         break;
                     }
                     __builtin_amdgcn_s_sleep(1);
-                    e[j][i] = ld_acquire(&look[(top - i) * stride + d0 + j]);
+                    e[i][q] = ld_acquire(&look[((p0 + i) * NW + q) * kOsThreads + t]);
                 }
-                prefix[j] += (uint32_t)e[j][i];
-                if (((e[j][i] >> 32) & 3u) == kIncl) open[j] = false;
+                prefix[2 * q] += (uint32_t)e[i][q] & 0xFFFFu;
+                if (2 * q + 1 < DPT) prefix[2 * q + 1] += (uint32_t)(e[i][q] >> 16) & 0xFFFFu;
             }
-            any = any || open[j];
         }
-        if (!any) break;
     }
 }
 
@@ -163,8 +158,9 @@ __global__ __launch_bounds__(kOsThreads) void k_os_pass(
     }
     __syncthreads();
 
-    // per digit: wave offsets inside the tile, tile count
-    uint32_t tile_cnt[DPT];
+    // per digit: wave offsets inside the tile, tile count (published)
+    constexpr int NW = (DPT + 1) / 2;
+    uint32_t tile_cnt[2 * NW];
 #pragma unroll
     for (int j = 0; j < DPT; ++j) {
         int d = tid * DPT + j;
@@ -176,8 +172,12 @@ __global__ __launch_bounds__(kOsThreads) void k_os_pass(
             run += c;
         }
         tile_cnt[j] = run;
-        st_release(&look[(int64_t)bid * BINS + d], lb_pack(epoch, bid == 0 ? kIncl : kAgg, run));
     }
+    if (DPT & 1) tile_cnt[DPT] = 0;
+#pragma unroll
+    for (int q = 0; q < NW; ++q)
+        st_release(&look[((int64_t)bid * NW + q) * kOsThreads + tid],
+                   agg_pack(epoch, tile_cnt[2 * q], tile_cnt[2 * q + 1]));
 
     // global start of each digit: exclusive scan of the pass histogram
     uint32_t hsum = 0, hv[DPT];
@@ -204,16 +204,12 @@ __global__ __launch_bounds__(kOsThreads) void k_os_pass(
         }
     }
 
-    // decoupled look-back over the blocks before this one, the thread's digits together
+    // keys of each digit in the tiles before this one
     if (bid > 0) {
         uint32_t prefix[DPT];
-        lookback_multi<DPT>(look, BINS, tid * DPT, (int64_t)bid - 1, epoch, status, prefix);
+        prefix_all<DPT>(look, tid, (int64_t)bid, epoch, status, prefix);
 #pragma unroll
-        for (int j = 0; j < DPT; ++j) {
-            const int d = tid * DPT + j;
-            st_release(&look[(int64_t)bid * BINS + d], lb_pack(epoch, kIncl, prefix[j] + tile_cnt[j]));
-            s_base[d] += prefix[j];
-        }
+        for (int j = 0; j < DPT; ++j) s_base[tid * DPT + j] += prefix[j];
     }
     __syncthreads();
 
@@ -512,13 +508,20 @@ hipError_t sort_impl(const K* keys_in, const uint32_t* vals_in, int64_t n, const
 
 }  // namespace
 
-SortPlan sort_plan(int key_bits) {
+SortPlan sort_plan(int key_bits, int max_bits) {
     SortPlan p;
     if (key_bits < 1) key_bits = 1;
-    p.passes = (key_bits + 10) / 11;
+    p.passes = (key_bits + max_bits - 1) / max_bits;
     int b = (key_bits + p.passes - 1) / p.passes;
     p.bits = b < 8 ? 8 : b;
     return p;
+}
+
+// Coordinate keys: at most 9-bit digits while the passes are single kernels
+// (a thread reads 2^bits / 512 count entries per earlier tile, so wider
+// digits cost more reads per pass than the pass they save), 11 otherwise.
+SortPlan key_sort_plan(int key_bits, int64_t n) {
+    return sort_plan(key_bits, sort_tiles(n) <= kManyTiles ? 9 : 11);
 }
 
 int64_t sort_tiles(int64_t n) { return (n + kOsTile - 1) / kOsTile; }

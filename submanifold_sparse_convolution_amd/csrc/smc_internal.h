@@ -98,12 +98,11 @@ struct Geom {
     int32_t ncols;
     int32_t ksize;          // kernel size K (3 or 5)
     int32_t pad;            // r = (K - 1) / 2: padding cells per side (grid) / key offset
-    // dense route: strides of the grid padded by r cells on every side
+    // strides of the grid padded by r cells on every side (dense route: the
+    // grid's cells; sorted route: the keys)
     int64_t sz_y;           // (Z + 2r)
     int64_t sz_x;           // (Y + 2r) (Z + 2r)
     int64_t sz_b;           // (X + 2r) (Y + 2r) (Z + 2r)
-    // sorted route: bit widths of the packed key fields (z lowest)
-    int32_t wz, wy, wx, wb;
 };
 
 // The record (and sort histograms) the next build will use: the first kernel
@@ -193,7 +192,8 @@ hipError_t launch_query_lookup(const void* keys, const uint32_t* vals, int64_t n
 // the input indices. hist holds the global digit counts of every pass
 // ([passes][1 << bits], e.g. from launch_key_hist). *keys_out / *vals_out
 // receive the scratch buffers that hold the result.
-SortPlan sort_plan(int key_bits);
+SortPlan sort_plan(int key_bits, int max_bits = 11);
+SortPlan key_sort_plan(int key_bits, int64_t n);
 int64_t sort_tiles(int64_t n);
 size_t sort_look_bytes(int64_t n);
 // u32 words a many-tile sort of n keys needs in SortWork::cnt (0: onesweep)

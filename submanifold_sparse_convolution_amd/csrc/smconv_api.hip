@@ -549,14 +549,10 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     g.sz_b = (int64_t)(g.ext[0] + 2 * g.pad) * g.sz_x;
     int key_bits = 0;
     if (chosen == SMC_ROUTE_SORTED) {
-        // a field holds c + r + d for d in [-r, r]: 0 .. ext - 1 + 2r
-        g.wz = bit_len((int64_t)g.ext[2] - 1 + 2 * g.pad);
-        g.wy = bit_len((int64_t)g.ext[1] - 1 + 2 * g.pad);
-        g.wx = bit_len((int64_t)g.ext[0] - 1 + 2 * g.pad);
-        g.wb = bit_len((int64_t)g.batch - 1);
-        key_bits = g.wz + g.wy + g.wx + g.wb;
-        if (key_bits > 64)
-            return fail(SMC_ERR_KEY_OVERFLOW, "packed key needs %d bits", key_bits);
+        // keys are cells of the padded grid: 0 .. cells - 1
+        if (cells_d >= 9.0e18)
+            return fail(SMC_ERR_KEY_OVERFLOW, "packed key of %.3g cells exceeds 63 bits", cells_d);
+        key_bits = bit_len((int64_t)g.batch * g.sz_b - 1);
     }
     StrideGeom sg{};
     if (strided) {
@@ -684,7 +680,7 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
                 return rc;
             SMC_HIP(launch_make_keys(coords, n, g, m->wide, m->keys0.p, st, next, s));
             m->slot_clean[slot ^ 1] = true;
-            const SortPlan kp = sort_plan(key_bits);
+            const SortPlan kp = key_sort_plan(key_bits, n);
             SMC_HIP(launch_key_hist(m->keys0.p, m->wide, n, kp, hist_key, s));
             const void* skeys;
             const uint32_t* svals;

@@ -225,13 +225,12 @@ __global__ __launch_bounds__(kBlock) void k_query_lookup(const K* __restrict__ k
     uint32_t bits = 0;
     if (o < m && c < 9) {
         const int32_t* q = qcoords + o * 4;
-        K key = (K)q[0];
-        key = (key << g.wx) | (K)(q[1] - g.origin[0] + g.pad);
-        key = (key << g.wy) | (K)(q[2] - g.origin[1] + g.pad);
-        key = (key << g.wz) | (K)(q[3] - g.origin[2] + g.pad);
+        // the input's key of the query point: its cell in the padded input grid
+        const K key = (K)(q[0] * g.sz_b + (int64_t)(q[1] - g.origin[0] + g.pad) * g.sz_x +
+                          (int64_t)(q[2] - g.origin[1] + g.pad) * g.sz_y +
+                          (q[3] - g.origin[2] + g.pad));
         const int dx = c / 3 - 1, dy = c % 3 - 1;
-        const K delta = (K)((int64_t)dx * ((int64_t)1 << (g.wy + g.wz))) +
-                        (K)((int64_t)dy * ((int64_t)1 << g.wz));
+        const K delta = (K)(dx * g.sz_x + dy * g.sz_y);
         const K first = key + delta - (K)1;
         int64_t j = lower_bound_k(keys, n_in, first);
 #pragma unroll

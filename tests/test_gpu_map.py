@@ -43,11 +43,31 @@ def test_dense_equals_sorted(name):
     assert_map_equal(a, b, name)
 
 
-def test_sorted_64bit_keys_and_derived_shape():
+def test_sorted_derived_shape_32bit_keys():
+    """Keys are cells of the padded grid: the wide set's box (2095 x 2095 x 695 at
+    most, 2 cells of padding per axis) needs 32 bits, not the 34 of bit fields."""
     _, coords = config("wide")
     got = gpu_map(coords)                      # bounding box derived on the device
-    assert got["info"]["key_bits"] > 32
+    ext = coords[:, 1:].max(0) - coords[:, 1:].min(0) + 1
+    cells = int(np.prod(ext.astype(np.int64) + 2))
+    assert got["info"]["route"] == "sorted"
+    assert got["info"]["key_bits"] == (cells - 1).bit_length() <= 32
     assert_map_equal(got, oracle_map("wide"), "wide/derived")
+
+
+def test_sorted_64bit_keys():
+    """A padded grid of more than 2^32 cells: 64-bit keys."""
+    rng = np.random.default_rng(5)
+    parts = []
+    for i, off in enumerate([(0, 0, 0), (4000, 0, 0), (0, 4000, 9), (4000, 4000, 1000)]):
+        c = synth.tiny_coords(seed=5 + i, n=700, side=12)       # dense clusters, far apart
+        c[:, 1:] += np.array(off, np.int32)
+        parts.append(c)
+    coords = np.concatenate(parts)
+    coords = coords[rng.permutation(len(coords))].astype(np.int32)
+    got = gpu_map(coords)
+    assert got["info"]["route"] == "sorted" and got["info"]["key_bits"] > 32
+    assert_map_equal(got, oracle_map_of(coords), "64-bit keys")
 
 
 def test_derived_shape_dense():
