@@ -180,36 +180,52 @@ __global__ __launch_bounds__(kBlock) void k_dense_lookup(const int32_t* __restri
     if (row < n && k == 0) mask[row] = (uint32_t)(hits >> (threadIdx.x & 32));
 }
 
-// 5 x 5 x 5 kernel: 128 lanes per row (125 active), lane k reads the cell at
-// offset d_k. The two waves of a row hold taps 0..63 and 64..127; each
-// wave's ballot of hits is two words of the row's 4-word mask.
+// 5 x 5 x 5 kernel: 32 lanes per row (25 active), lane c for the (dx, dy)
+// column c = 5 (dx + 2) + (dy + 2). The column's cells z - 2 .. z + 2 are
+// consecutive in the grid, so one 64-bit window of occupancy bits (two
+// words) gives its 5 taps 5c .. 5c + 4, and only occupied cells read the
+// grid. The lane writes those 5 neighbour entries (a row's 125 are
+// contiguous); the row's 4 mask words are ORed together from the lanes'
+// 5-bit patterns.
 __global__ __launch_bounds__(kBlock) void k_dense_lookup5(const int32_t* __restrict__ coords,
                                                           int64_t n, Geom g,
                                                           const int32_t* __restrict__ grid,
                                                           const uint32_t* __restrict__ bits,
                                                           int32_t* __restrict__ nbr,
                                                           uint32_t* __restrict__ mask) {
-    constexpr int kT = 125;
+    constexpr int kT = 125, kCols = 25;
     const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-    const int64_t row = t >> 7;
-    const int k = (int)(t & 127);
-    const bool live = row < n && k < kT;
-    int v = -1;
-    if (live) {
+    const int64_t row = t >> 5;
+    const int c = (int)(t & 31);
+    uint32_t pat = 0;
+    if (row < n && c < kCols) {
+        int v[5] = {-1, -1, -1, -1, -1};
         int b, x, y, z;
         if (load_rel(coords, row, g, b, x, y, z)) {
-            const int dx = k / 25 - 2, dy = (k / 5) % 5 - 2, dz = k % 5 - 2;
-            const int64_t c = dense_cell(g, b, x, y, z) + dx * g.sz_x + dy * g.sz_y + dz;
-            if ((bits[c >> 5] >> (c & 31)) & 1u) v = grid[c];
+            const int dx = c / 5 - 2, dy = c % 5 - 2;
+            const int64_t c0 = dense_cell(g, b, x, y, z) + dx * g.sz_x + dy * g.sz_y - 2;
+            // (the bit array has a word of slack past the last cell's)
+            const uint64_t win = ((uint64_t)bits[(c0 >> 5) + 1] << 32) | bits[c0 >> 5];
+            pat = (uint32_t)(win >> (c0 & 31)) & 31u;
+#pragma unroll
+            for (int j = 0; j < 5; ++j)
+                if ((pat >> j) & 1u) v[j] = grid[c0 + j];
         }
-        nbr[row * kT + k] = v;
+        int32_t* dst = nbr + row * kT + 5 * c;
+#pragma unroll
+        for (int j = 0; j < 5; ++j) dst[j] = v[j];
     }
-    const uint64_t hits = __ballot(v >= 0);
-    if (row < n && (k & 63) == 0) {
-        const int h = k >> 6;
-        mask[row * kMaxMaskWords + 2 * h] = (uint32_t)hits;
-        mask[row * kMaxMaskWords + 2 * h + 1] = (uint32_t)(hits >> 32);
+    // mask word q: the patterns' bits 5c + j that fall in [32 q, 32 q + 32)
+    uint32_t w[kMaxMaskWords];
+#pragma unroll
+    for (int q = 0; q < kMaxMaskWords; ++q) {
+        const int sh = 5 * c - 32 * q;
+        w[q] = sh >= 32 || sh <= -5 ? 0u : sh >= 0 ? pat << sh : pat >> -sh;
+#pragma unroll
+        for (int o = 16; o > 0; o >>= 1) w[q] |= __shfl_xor(w[q], o, 32);
     }
+    if (row < n && c < kMaxMaskWords)
+        mask[row * kMaxMaskWords + c] = c == 0 ? w[0] : c == 1 ? w[1] : c == 2 ? w[2] : w[3];
 }
 
 // Key of a voxel: its cell in the grid padded by r cells on every side,
@@ -396,7 +412,7 @@ hipError_t launch_clear_cells(const PrevCells& prev, hipStream_t s) {
 hipError_t launch_dense_lookup(const int32_t* coords, int64_t n, const Geom& g, const int32_t* grid,
                                const uint32_t* bits, int32_t* nbr, uint32_t* mask, hipStream_t s) {
     if (g.ksize == 5)
-        launch(k_dense_lookup5, blocks_for(n * 128), kBlock, 0, s, coords, n, g, grid, bits, nbr,
+        launch(k_dense_lookup5, blocks_for(n * 32), kBlock, 0, s, coords, n, g, grid, bits, nbr,
                mask);
     else
         launch(k_dense_lookup, blocks_for(n * 32), kBlock, 0, s, coords, n, g, grid, bits, nbr,
