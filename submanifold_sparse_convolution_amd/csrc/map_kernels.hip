@@ -154,30 +154,44 @@ __global__ __launch_bounds__(kBlock) void k_clear_cells(PrevCells prev) {
     }
 }
 
-// 32 lanes per row (27 active): lane k reads the cell at offset d_k. The
-// wave's ballot of hits gives both rows' masks directly.
+// 16 lanes per row (9 active), lane c for the (dx, dy) column c = 3 (dx + 1) +
+// (dy + 1). The column's cells z - 1 .. z + 1 are consecutive in the grid, so
+// one 64-bit window of occupancy bits (two words) gives its 3 taps 3c .. 3c +
+// 2, and only occupied cells read the grid. The lane writes those 3
+// neighbour entries (a row's 27 are contiguous); the row's mask is ORed
+// together from the lanes' 3-bit patterns.
 __global__ __launch_bounds__(kBlock) void k_dense_lookup(const int32_t* __restrict__ coords,
                                                          int64_t n, Geom g,
                                                          const int32_t* __restrict__ grid,
                                                          const uint32_t* __restrict__ bits,
                                                          int32_t* __restrict__ nbr,
                                                          uint32_t* __restrict__ mask) {
-    int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-    int64_t row = t >> 5;
-    int k = (int)(t & 31);
-    bool live = row < n && k < kTaps;
-    int v = -1;
-    if (live) {
+    constexpr int kCols = 9;
+    const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    const int64_t row = t >> 4;
+    const int c = (int)(t & 15);
+    uint32_t pat = 0;
+    if (row < n && c < kCols) {
+        int v[3] = {-1, -1, -1};
         int b, x, y, z;
         if (load_rel(coords, row, g, b, x, y, z)) {
-            int dx = k / 9 - 1, dy = (k / 3) % 3 - 1, dz = k % 3 - 1;
-            const int64_t c = dense_cell(g, b, x, y, z) + dx * g.sz_x + dy * g.sz_y + dz;
-            if ((bits[c >> 5] >> (c & 31)) & 1u) v = grid[c];
+            const int dx = c / 3 - 1, dy = c % 3 - 1;
+            const int64_t c0 = dense_cell(g, b, x, y, z) + dx * g.sz_x + dy * g.sz_y - 1;
+            // (the bit array has a word of slack past the last cell's)
+            const uint64_t win = ((uint64_t)bits[(c0 >> 5) + 1] << 32) | bits[c0 >> 5];
+            pat = (uint32_t)(win >> (c0 & 31)) & 7u;
+#pragma unroll
+            for (int j = 0; j < 3; ++j)
+                if ((pat >> j) & 1u) v[j] = grid[c0 + j];
         }
-        nbr[row * kTaps + k] = v;
+        int32_t* dst = nbr + row * kTaps + 3 * c;
+#pragma unroll
+        for (int j = 0; j < 3; ++j) dst[j] = v[j];
     }
-    uint64_t hits = __ballot(v >= 0);
-    if (row < n && k == 0) mask[row] = (uint32_t)(hits >> (threadIdx.x & 32));
+    uint32_t m = pat << (3 * (c < kCols ? c : 0));
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) m |= __shfl_xor(m, o, 16);
+    if (row < n && c == 0) mask[row] = m;
 }
 
 // 5 x 5 x 5 kernel: 32 lanes per row (25 active), lane c for the (dx, dy)
@@ -415,7 +429,7 @@ hipError_t launch_dense_lookup(const int32_t* coords, int64_t n, const Geom& g, 
         launch(k_dense_lookup5, blocks_for(n * 32), kBlock, 0, s, coords, n, g, grid, bits, nbr,
                mask);
     else
-        launch(k_dense_lookup, blocks_for(n * 32), kBlock, 0, s, coords, n, g, grid, bits, nbr,
+        launch(k_dense_lookup, blocks_for(n * 16), kBlock, 0, s, coords, n, g, grid, bits, nbr,
                mask);
     return hipGetLastError();
 }
