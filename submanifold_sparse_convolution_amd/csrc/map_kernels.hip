@@ -304,12 +304,15 @@ __device__ inline int64_t lower_bound_split(const K* __restrict__ keys, int64_t 
     return a + lower_bound(keys + a, b - a, t);
 }
 
-// Lanes per sorted key: one per (dx, dy) column (9 for K = 3, 25 for K = 5),
-// rounded up to a power of two. The K taps of a column (dz = -r .. r) have
-// consecutive keys, and so sit at consecutive sorted positions when
-// present: one binary search for the column's lowest key, then up to K
-// compares walking forward. The centre column needs no search: its keys
-// are at s - r .. s + r, found by stepping back from s.
+// Lanes per sorted key: one per dx plane (3 for K = 3, 5 for K = 5), rounded
+// up to a power of two. The K^2 taps of a plane (dy, dz in -r .. r) have keys
+// in [lo, hi] = key(x + dx, y - r, z - r) .. key(x + dx, y + r, z + r), and
+// so sit in one run of the sorted keys: one search for lo, then a walk
+// forward to hi, each key's offset from lo giving its (dy, dz) (keys between
+// the columns, other z of the same (x, y), are skipped). On sparse sets a
+// run holds a few keys, so a row takes K searches instead of K^2. A run of
+// more than kWalk keys (a dense slab) falls back to one search per (dx, dy)
+// column and K compares.
 template <typename K, int KS>
 __global__ __launch_bounds__(kBlock) void k_sorted_lookup(const K* __restrict__ keys,
                                                           const uint32_t* __restrict__ vals,
@@ -318,9 +321,10 @@ __global__ __launch_bounds__(kBlock) void k_sorted_lookup(const K* __restrict__ 
                                                           int32_t* __restrict__ nbr,
                                                           uint32_t* __restrict__ mask,
                                                           MapState* st) {
-    constexpr int R = (KS - 1) / 2, COLS = KS * KS, KV = KS * KS * KS;
-    constexpr int LANES = KS == 3 ? 16 : 32;
+    constexpr int R = (KS - 1) / 2, KV = KS * KS * KS, PL = KS * KS;
+    constexpr int LANES = KS == 3 ? 4 : 8;
     constexpr int MW = (KV + 31) / 32;
+    constexpr int kWalk = 4 * KS;
     __shared__ K s_split[kMaxSplit];
     const int ns = (int)((n + ((int64_t)1 << sh) - 1) >> sh);
     for (int i = threadIdx.x; i < ns; i += blockDim.x) s_split[i] = split[i];
@@ -331,35 +335,61 @@ __global__ __launch_bounds__(kBlock) void k_sorted_lookup(const K* __restrict__ 
     uint32_t bits[MW];
 #pragma unroll
     for (int q = 0; q < MW; ++q) bits[q] = 0;
-    if (s < n && c < COLS) {
+    if (s < n && c < KS) {
         const K q = keys[s];
         // vals is a permutation of [0, n); the clamps only matter if a sort wait stalled
         const int row = (int)min(vals[s], (uint32_t)(n - 1));
-        const int dx = c / KS - R, dy = c % KS - R;
-        const K delta = (K)(dx * g.sz_x + dy * g.sz_y);
-        const K first = q + delta - (K)R;
-        int64_t j;
-        if (c == COLS / 2) {
-            j = s;
+        const int dx = c - R;
+        const K lo = q + (K)(dx * g.sz_x - R * g.sz_y - R);
+        const K hi = q + (K)(dx * g.sz_x + R * g.sz_y + R);
+        int32_t* out = nbr + (int64_t)row * KV + PL * c;    // the plane's K^2 entries
 #pragma unroll
-            for (int i = 0; i < R; ++i)
-                if (j > 0 && keys[j - 1] >= first) --j;
-            if (s + 1 < n && keys[s + 1] == q) atomicOr(&st->status, kStDuplicate);
-        } else {
-            j = lower_bound_split(keys, n, first, s_split, ns, sh);
-        }
+        for (int e = 0; e < PL; ++e) out[e] = -1;
+        if (dx == 0 && s + 1 < n && keys[s + 1] == q) atomicOr(&st->status, kStDuplicate);
+        int64_t j = lower_bound_split(keys, n, lo, s_split, ns, sh);
+        int walked = 0;
+        for (; j < n && walked < kWalk; ++j, ++walked) {
+            const K kj = keys[j];
+            if (kj > hi) break;
+            const K off = kj - lo;                    // <= 2r (Z + 2r) + 2r
+            int dy = 0;
 #pragma unroll
-        for (int dz = 0; dz < KS; ++dz) {
-            int hit = -1;
-            if (j < n && keys[j] == first + (K)dz) {
-                hit = (int)min(vals[j], (uint32_t)(n - 1));
-                ++j;
-            }
-            const int kk = KS * c + dz;
-            nbr[(int64_t)row * KV + kk] = hit;
-            if (hit >= 0) {
+            for (int i = 1; i < KS; ++i) dy += off >= (K)(i * g.sz_y) ? 1 : 0;
+            const K dz = off - (K)(dy * g.sz_y);
+            if (dz < (K)KS) {
+                const int kk = PL * c + KS * dy + (int)dz;
+                out[KS * dy + dz] = (int)min(vals[j], (uint32_t)(n - 1));
 #pragma unroll
                 for (int w = 0; w < MW; ++w) bits[w] |= (kk >> 5) == w ? 1u << (kk & 31) : 0u;
+            }
+        }
+        if (walked == kWalk && j < n && keys[j] <= hi) {
+            // a dense run: the plane's columns one by one (entries rewritten in order)
+#pragma unroll
+            for (int w = 0; w < MW; ++w) {
+                const int first = 32 * w - PL * c;  // this plane's taps in word w
+                uint32_t keep = 0xFFFFFFFFu;
+                for (int e = 0; e < PL; ++e)
+                    if (e - first >= 0 && e - first < 32) keep &= ~(1u << (e - first));
+                bits[w] &= keep;
+            }
+            for (int dy = 0; dy < KS; ++dy) {
+                const K first = lo + (K)(dy * g.sz_y);
+                int64_t jc = lower_bound_split(keys, n, first, s_split, ns, sh);
+#pragma unroll
+                for (int dz = 0; dz < KS; ++dz) {
+                    int hit = -1;
+                    if (jc < n && keys[jc] == first + (K)dz) {
+                        hit = (int)min(vals[jc], (uint32_t)(n - 1));
+                        ++jc;
+                    }
+                    const int kk = PL * c + KS * dy + dz;
+                    out[KS * dy + dz] = hit;
+                    if (hit >= 0) {
+#pragma unroll
+                        for (int w = 0; w < MW; ++w) bits[w] |= (kk >> 5) == w ? 1u << (kk & 31) : 0u;
+                    }
+                }
             }
         }
     }
@@ -449,19 +479,19 @@ hipError_t launch_sorted_lookup(const void* keys, const uint32_t* vals, int64_t 
     if (((n + ((int64_t)1 << split_shift) - 1) >> split_shift) > kMaxSplit) return hipErrorInvalidValue;
     if (g.ksize == 5) {
         if (wide)
-            launch(k_sorted_lookup<uint64_t, 5>, blocks_for(n * 32), kBlock, 0, s,
+            launch(k_sorted_lookup<uint64_t, 5>, blocks_for(n * 8), kBlock, 0, s,
                    (const uint64_t*)keys, vals, n, g, (const uint64_t*)split, split_shift, nbr,
                    mask, st);
         else
-            launch(k_sorted_lookup<uint32_t, 5>, blocks_for(n * 32), kBlock, 0, s,
+            launch(k_sorted_lookup<uint32_t, 5>, blocks_for(n * 8), kBlock, 0, s,
                    (const uint32_t*)keys, vals, n, g, (const uint32_t*)split, split_shift, nbr,
                    mask, st);
     } else if (wide) {
-        launch(k_sorted_lookup<uint64_t, 3>, blocks_for(n * 16), kBlock, 0, s,
+        launch(k_sorted_lookup<uint64_t, 3>, blocks_for(n * 4), kBlock, 0, s,
                (const uint64_t*)keys, vals, n, g, (const uint64_t*)split, split_shift, nbr, mask,
                st);
     } else {
-        launch(k_sorted_lookup<uint32_t, 3>, blocks_for(n * 16), kBlock, 0, s,
+        launch(k_sorted_lookup<uint32_t, 3>, blocks_for(n * 4), kBlock, 0, s,
                (const uint32_t*)keys, vals, n, g, (const uint32_t*)split, split_shift, nbr, mask,
                st);
     }
