@@ -210,8 +210,10 @@ __device__ inline int64_t lower_bound_k(const K* __restrict__ keys, int64_t n, K
 }
 
 // Sorted route: the 27 taps around each query point, searched in the sorted
-// input keys (16 lanes per query, one per (dx, dy) column: a lower_bound for
-// the column's lowest key, then up to 3 compares).
+// input keys with 4 lanes per query, one per dx plane: the plane's 9 taps
+// have keys in one run [key(x + dx, y - 1, z - 1), key(x + dx, y + 1, z + 1)],
+// found by one lower_bound and walked, each key's offset giving its (dy, dz).
+// A run of more than 12 keys falls back to a search per (dx, dy) column.
 template <typename K>
 __global__ __launch_bounds__(kBlock) void k_query_lookup(const K* __restrict__ keys,
                                                          const uint32_t* __restrict__ vals,
@@ -219,35 +221,56 @@ __global__ __launch_bounds__(kBlock) void k_query_lookup(const K* __restrict__ k
                                                          const int32_t* __restrict__ qcoords,
                                                          int64_t m, int32_t* __restrict__ nbr,
                                                          uint32_t* __restrict__ mask) {
+    constexpr int kWalk = 12;
     const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-    const int64_t o = t >> 4;
-    const int c = (int)(t & 15);
+    const int64_t o = t >> 2;
+    const int c = (int)(t & 3);
     uint32_t bits = 0;
-    if (o < m && c < 9) {
+    if (o < m && c < 3) {
         const int32_t* q = qcoords + o * 4;
         // the input's key of the query point: its cell in the padded input grid
         const K key = (K)(q[0] * g.sz_b + (int64_t)(q[1] - g.origin[0] + g.pad) * g.sz_x +
                           (int64_t)(q[2] - g.origin[1] + g.pad) * g.sz_y +
                           (q[3] - g.origin[2] + g.pad));
-        const int dx = c / 3 - 1, dy = c % 3 - 1;
-        const K delta = (K)(dx * g.sz_x + dy * g.sz_y);
-        const K first = key + delta - (K)1;
-        int64_t j = lower_bound_k(keys, n_in, first);
+        const int dx = c - 1;
+        const K lo = key + (K)(dx * g.sz_x - g.sz_y - 1);
+        const K hi = key + (K)(dx * g.sz_x + g.sz_y + 1);
+        int32_t* out = nbr + o * kTaps + 9 * c;           // the plane's 9 entries
 #pragma unroll
-        for (int dz = 0; dz < 3; ++dz) {
-            int hit = -1;
-            if (j < n_in && keys[j] == first + (K)dz) {
-                hit = (int)min(vals[j], (uint32_t)(n_in - 1));
-                ++j;
+        for (int e = 0; e < 9; ++e) out[e] = -1;
+        int64_t j = lower_bound_k(keys, n_in, lo);
+        int walked = 0;
+        for (; j < n_in && walked < kWalk; ++j, ++walked) {
+            const K kj = keys[j];
+            if (kj > hi) break;
+            const K off = kj - lo;
+            const int dy = (off >= (K)g.sz_y ? 1 : 0) + (off >= (K)(2 * g.sz_y) ? 1 : 0);
+            const K dz = off - (K)(dy * g.sz_y);
+            if (dz < (K)3) {
+                out[3 * dy + dz] = (int)min(vals[j], (uint32_t)(n_in - 1));
+                bits |= 1u << (9 * c + 3 * dy + (int)dz);
             }
-            nbr[o * kTaps + 3 * c + dz] = hit;
-            if (hit >= 0) bits |= 1u << (3 * c + dz);
+        }
+        if (walked == kWalk && j < n_in && keys[j] <= hi) {   // a dense run: column by column
+            bits = 0;
+            for (int dy = 0; dy < 3; ++dy) {
+                const K first = lo + (K)(dy * g.sz_y);
+                int64_t jc = lower_bound_k(keys, n_in, first);
+#pragma unroll
+                for (int dz = 0; dz < 3; ++dz) {
+                    int hit = -1;
+                    if (jc < n_in && keys[jc] == first + (K)dz) {
+                        hit = (int)min(vals[jc], (uint32_t)(n_in - 1));
+                        ++jc;
+                    }
+                    out[3 * dy + dz] = hit;
+                    if (hit >= 0) bits |= 1u << (9 * c + 3 * dy + dz);
+                }
+            }
         }
     }
-    bits |= __shfl_xor(bits, 8, 16);
-    bits |= __shfl_xor(bits, 4, 16);
-    bits |= __shfl_xor(bits, 2, 16);
-    bits |= __shfl_xor(bits, 1, 16);
+    bits |= __shfl_xor(bits, 2, 4);
+    bits |= __shfl_xor(bits, 1, 4);
     if (o < m && c == 0) mask[o] = bits;
 }
 
@@ -293,10 +316,10 @@ hipError_t launch_query_lookup(const void* keys, const uint32_t* vals, int64_t n
                                uint32_t* mask, hipStream_t s) {
     if (m <= 0) return hipSuccess;
     if (wide)
-        launch(k_query_lookup<uint64_t>, blocks_of(m * 16, kBlock), kBlock, 0, s,
+        launch(k_query_lookup<uint64_t>, blocks_of(m * 4, kBlock), kBlock, 0, s,
                (const uint64_t*)keys, vals, n_in, g, qcoords, m, nbr, mask);
     else
-        launch(k_query_lookup<uint32_t>, blocks_of(m * 16, kBlock), kBlock, 0, s,
+        launch(k_query_lookup<uint32_t>, blocks_of(m * 4, kBlock), kBlock, 0, s,
                (const uint32_t*)keys, vals, n_in, g, qcoords, m, nbr, mask);
     return hipGetLastError();
 }
