@@ -166,3 +166,19 @@ def test_strided_errors_and_handle_reuse():
                             spatial_shape=(8, 8, 8))
     assert empty.n == 0
     m.close()
+
+
+def test_strided_sorted_64bit_keys():
+    """A padded input grid of more than 2^32 cells: the sorted route with 64-bit keys
+    (dense clusters far apart, so every query plane has neighbours to find)."""
+    parts = []
+    for i, off in enumerate([(0, 0, 0), (4000, 0, 0), (0, 4000, 9), (4000, 4000, 1000)]):
+        c = synth.tiny_coords(seed=11 + i, n=600, side=12)
+        c[:, 1:] += np.array(off, np.int32)
+        parts.append(c)
+    coords = np.concatenate(parts)
+    coords = coords[np.random.default_rng(12).permutation(len(coords))].astype(np.int32)
+    shape = tuple(int(v) + 1 for v in coords[:, 1:].max(0))
+    got = gpu_strided(coords, shape)
+    assert got["info"]["route"] == "sorted" and got["info"]["key_bits"] > 32
+    check_map(got, oracle_strided(coords, shape), "64-bit keys")
