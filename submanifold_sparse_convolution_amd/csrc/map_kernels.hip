@@ -248,22 +248,40 @@ __global__ __launch_bounds__(kBlock) void k_dense_lookup5(const int32_t* __restr
 // fields: the same order, and since the padding keeps every neighbour inside
 // its field, key(q + d) = key(q) + key offset of d (the packed(q + d) =
 // packed(q) + packed(d) property of the Z-Delta mapper), in fewer bits.
+// 8 keys per thread (2048 per block). The same pass also counts every sort
+// pass's digits (block counts in LDS, then one global add per non-zero bin),
+// so the sort needs no histogram read of its own. (Spatial keys spread over
+// the bins, so the LDS atomics rarely collide.)
+constexpr int kKeyItems = 8;
 template <typename K>
 __global__ __launch_bounds__(kBlock) void k_make_keys(const int32_t* __restrict__ coords,
                                                       int64_t n, Geom g, K* __restrict__ keys,
-                                                      MapState* st, NextRecord next) {
+                                                      MapState* st, NextRecord next, int bits,
+                                                      int passes, uint32_t* __restrict__ hist) {
+    extern __shared__ uint32_t s_h[];             // passes << bits digit counters
     if (next.st) clear_record(next.st, next.hist, next.hist_ints);
-    int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-    if (i >= n) return;
-    int b, x, y, z;
-    K key;
-    if (load_rel(coords, i, g, b, x, y, z)) {
-        key = (K)dense_cell(g, b, x, y, z);
-    } else {
-        atomicOr(&st->status, kStRange);
-        key = ~(K)0;
+    const int bins = 1 << bits;
+    for (int i = threadIdx.x; i < passes * bins; i += kBlock) s_h[i] = 0;
+    __syncthreads();
+    const int64_t base = (int64_t)blockIdx.x * kBlock * kKeyItems;
+    for (int it = 0; it < kKeyItems; ++it) {
+        const int64_t i = base + it * kBlock + threadIdx.x;
+        if (i >= n) break;
+        int b, x, y, z;
+        K key;
+        if (load_rel(coords, i, g, b, x, y, z)) {
+            key = (K)dense_cell(g, b, x, y, z);
+        } else {
+            atomicOr(&st->status, kStRange);
+            key = ~(K)0;
+        }
+        keys[i] = key;
+        for (int p = 0; p < passes; ++p)
+            atomicAdd(&s_h[p * bins + ((uint32_t)(key >> (p * bits)) & (bins - 1))], 1u);
     }
-    keys[i] = key;
+    __syncthreads();
+    for (int i = threadIdx.x; i < passes * bins; i += kBlock)
+        if (s_h[i]) atomicAdd(&hist[i], s_h[i]);
 }
 
 template <typename K>
@@ -465,11 +483,16 @@ hipError_t launch_dense_lookup(const int32_t* coords, int64_t n, const Geom& g, 
 }
 
 hipError_t launch_make_keys(const int32_t* coords, int64_t n, const Geom& g, bool wide, void* keys,
-                            MapState* st, const NextRecord& next, hipStream_t s) {
+                            MapState* st, const NextRecord& next, const SortPlan& plan,
+                            uint32_t* hist, hipStream_t s) {
+    const unsigned blocks = blocks_for((n + kKeyItems - 1) / kKeyItems);
+    const size_t lds = (size_t)plan.passes * (1u << plan.bits) * 4;
     if (wide)
-        launch(k_make_keys<uint64_t>, blocks_for(n), kBlock, 0, s, coords, n, g, (uint64_t*)keys, st, next);
+        launch(k_make_keys<uint64_t>, blocks, kBlock, lds, s, coords, n, g, (uint64_t*)keys, st,
+               next, plan.bits, plan.passes, hist);
     else
-        launch(k_make_keys<uint32_t>, blocks_for(n), kBlock, 0, s, coords, n, g, (uint32_t*)keys, st, next);
+        launch(k_make_keys<uint32_t>, blocks, kBlock, lds, s, coords, n, g, (uint32_t*)keys, st,
+               next, plan.bits, plan.passes, hist);
     return hipGetLastError();
 }
 

@@ -145,8 +145,11 @@ hipError_t launch_clear_cells(const PrevCells& prev, hipStream_t s);
 // nbr [n, K^3]; mask [n] (K = 3) or [n, 4] words (K = 5): g.ksize decides.
 hipError_t launch_dense_lookup(const int32_t* coords, int64_t n, const Geom& g, const int32_t* grid,
                                const uint32_t* bits, int32_t* nbr, uint32_t* mask, hipStream_t s);
+// Keys of the sorted route, and the digit histograms of every pass of `plan`
+// added into hist (which must start at zero).
 hipError_t launch_make_keys(const int32_t* coords, int64_t n, const Geom& g, bool wide, void* keys,
-                            MapState* st, const NextRecord& next, hipStream_t s);
+                            MapState* st, const NextRecord& next, const SortPlan& plan,
+                            uint32_t* hist, hipStream_t s);
 // split: the key sort's splitter table (keys i << split_shift), which every
 // block reads into LDS for the top levels of its searches.
 hipError_t launch_sorted_lookup(const void* keys, const uint32_t* vals, int64_t n, const Geom& g,

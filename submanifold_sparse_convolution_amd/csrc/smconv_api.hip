@@ -678,10 +678,9 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
                 (rc = m->keys2.ensure(kb, s)) || (rc = m->vals0.ensure((size_t)nn * 4, s)) ||
                 (rc = m->vals1.ensure((size_t)nn * 4, s)))
                 return rc;
-            SMC_HIP(launch_make_keys(coords, n, g, m->wide, m->keys0.p, st, next, s));
-            m->slot_clean[slot ^ 1] = true;
             const SortPlan kp = key_sort_plan(key_bits, n);
-            SMC_HIP(launch_key_hist(m->keys0.p, m->wide, n, kp, hist_key, s));
+            SMC_HIP(launch_make_keys(coords, n, g, m->wide, m->keys0.p, st, next, kp, hist_key, s));
+            m->slot_clean[slot ^ 1] = true;
             const void* skeys;
             const uint32_t* svals;
             // the key sort's last pass also lists splitters for the lookup's searches
