@@ -173,6 +173,17 @@ struct StrideGeom {
     uint64_t sentinel;
 };
 int64_t unique_blocks(int64_t n_c);
+// Output cells through a bitmap of the output grid (words of it, zero on entry
+// and left zero): coords -> output coords [M, 4] and query points [M, 4] in
+// (b, x, y, z) order, st->n_out = M; counts: out_bitmap_blocks(words) words of
+// scratch.
+constexpr int64_t kOutBitmapWords = (int64_t)1 << 22;   // 16 MiB: larger grids sort candidates
+int64_t out_bitmap_words(const StrideGeom& sg, int batch);
+int64_t out_bitmap_blocks(int64_t words);
+hipError_t launch_stride_bitmap(const int32_t* coords, int64_t n, const Geom& g,
+                                const StrideGeom& sg, uint32_t* obits, int64_t words,
+                                uint32_t* counts, int32_t* ocoords, int32_t* qcoords,
+                                MapState* st, hipStream_t s);
 // coords [n, ncols] -> 8 candidate output keys per row (sentinels where fewer)
 hipError_t launch_stride_candidates(const int32_t* coords, int64_t n, const Geom& g,
                                     const StrideGeom& sg, uint64_t* keys, MapState* st,

@@ -169,6 +169,7 @@ struct smc_map {
     int64_t n_in = 0;
     StrideGeom sgeom{};
     DevBuf ck0, ck1, ck2, cv0, cv1, chist, ucounts, ocoords, qcoords;
+    DevBuf obits;                 // output-grid bitmap of strided builds (kept zero between builds)
     DevBuf scan;                      // count table of many-tile sorts
     // stage timers
     bool timing = false;
@@ -387,7 +388,8 @@ int smc_map_destroy(smc_map* m) {
                           &m->mask, &m->mkey0, &m->mkey1, &m->mval0, &m->mval1, &m->okeys,
                           &m->pair_in, &m->pair_out, &m->pair_slot, &m->rowbase, &m->part,
                           &m->zrow, &m->ck0, &m->ck1, &m->ck2, &m->cv0, &m->cv1, &m->chist,
-                          &m->ucounts, &m->ocoords, &m->qcoords, &m->scan, &m->split};
+                          &m->ucounts, &m->ocoords, &m->qcoords, &m->scan, &m->split,
+                          &m->obits};
         for (DevBuf* b : bufs) b->release();
         for (auto& v : m->ev_open)
             for (auto& pr : v) {
@@ -411,24 +413,43 @@ static int strided_outputs(smc_map* m, const int32_t* coords, int64_t n, const G
                            const StrideGeom& sg, MapState* st, uint32_t* status, hipStream_t s,
                            int64_t* rows) {
     const int64_t n_cand = 8 * n;
-    SMC_HIP(launch_stride_candidates(coords, n, g, sg, m->ck0.as<uint64_t>(), st, s));
-    int bits = 1;
-    while (((uint64_t)1 << bits) <= sg.sentinel) ++bits;   // key bits including the sentinel's
-    const SortPlan plan = sort_plan(bits);
-    if (plan.passes * (1 << plan.bits) > kHistKeyInts)
-        return fail(SMC_ERR_UNSUPPORTED, "output key sort needs %d bins", plan.passes * (1 << plan.bits));
-    // (a many-tile sort counts per tile itself: no global histogram needed)
-    if (sort_scan_ints(n_cand) == 0 || !m->ws.cnt) {
-        SMC_HIP(launch_fill_i32(m->chist.as<int32_t>(), kHistKeyInts, 0, s));
-        SMC_HIP(launch_key_hist(m->ck0.p, true, n_cand, plan, m->chist.as<uint32_t>(), s));
+    // a small output grid: its cells through a bitmap, no candidate sort
+    const int64_t words = out_bitmap_words(sg, g.batch);
+    if (words <= kOutBitmapWords) {
+        const size_t want = (size_t)words * 4 + 4;
+        if (want > m->obits.bytes) {
+            int rc;
+            if ((rc = m->obits.ensure(want, s))) return rc;
+            SMC_HIP(launch_fill_i32(m->obits.as<int32_t>(), (int64_t)(m->obits.bytes / 4), 0, s));
+        }
+        const int64_t nb = out_bitmap_blocks(words);
+        if ((size_t)nb * 4 > m->ucounts.bytes) {
+            int rc;
+            if ((rc = m->ucounts.ensure((size_t)nb * 4, s))) return rc;
+        }
+        SMC_HIP(launch_stride_bitmap(coords, n, g, sg, m->obits.as<uint32_t>(), words,
+                                     m->ucounts.as<uint32_t>(), m->ocoords.as<int32_t>(),
+                                     m->qcoords.as<int32_t>(), st, s));
+    } else {
+        SMC_HIP(launch_stride_candidates(coords, n, g, sg, m->ck0.as<uint64_t>(), st, s));
+        int bits = 1;
+        while (((uint64_t)1 << bits) <= sg.sentinel) ++bits;   // key bits including the sentinel's
+        const SortPlan plan = sort_plan(bits);
+        if (plan.passes * (1 << plan.bits) > kHistKeyInts)
+            return fail(SMC_ERR_UNSUPPORTED, "output key sort needs %d bins", plan.passes * (1 << plan.bits));
+        // (a many-tile sort counts per tile itself: no global histogram needed)
+        if (sort_scan_ints(n_cand) == 0 || !m->ws.cnt) {
+            SMC_HIP(launch_fill_i32(m->chist.as<int32_t>(), kHistKeyInts, 0, s));
+            SMC_HIP(launch_key_hist(m->ck0.p, true, n_cand, plan, m->chist.as<uint32_t>(), s));
+        }
+        const uint64_t* sorted = nullptr;
+        const uint32_t* sv = nullptr;
+        SMC_HIP(radix_sort_u64(m->ck0.as<uint64_t>(), nullptr, n_cand, plan, m->chist.as<uint32_t>(),
+                               m->ck1.as<uint64_t>(), m->ck2.as<uint64_t>(), m->cv0.as<uint32_t>(),
+                               m->cv1.as<uint32_t>(), m->ws, status, &sorted, &sv, s));
+        SMC_HIP(launch_unique(sorted, n_cand, sg, m->ucounts.as<uint32_t>(), m->ocoords.as<int32_t>(),
+                              m->qcoords.as<int32_t>(), st, s));
     }
-    const uint64_t* sorted = nullptr;
-    const uint32_t* sv = nullptr;
-    SMC_HIP(radix_sort_u64(m->ck0.as<uint64_t>(), nullptr, n_cand, plan, m->chist.as<uint32_t>(),
-                           m->ck1.as<uint64_t>(), m->ck2.as<uint64_t>(), m->cv0.as<uint32_t>(),
-                           m->cv1.as<uint32_t>(), m->ws, status, &sorted, &sv, s));
-    SMC_HIP(launch_unique(sorted, n_cand, sg, m->ucounts.as<uint32_t>(), m->ocoords.as<int32_t>(),
-                          m->qcoords.as<int32_t>(), st, s));
     int32_t count = 0;
     SMC_HIP(hipMemcpyAsync(&m->host_state->n_out, &st->n_out, sizeof(int32_t),
                            hipMemcpyDeviceToHost, s));

@@ -194,6 +194,118 @@ __global__ __launch_bounds__(kUThreads) void k_unique_write(
     }
 }
 
+// ---- output cells through a bitmap of the output grid (small output grids) ----
+// Bit L = ((b OX + x) OY + y) OZ + z: the same (b, x, y, z) order as the packed
+// keys, so reading the set bits in order lists the output cells sorted and
+// without repeats, with no candidate sort.
+constexpr int kBWords = 4;                        // bitmap words per thread
+constexpr int kBTile = kUThreads * kBWords;       // words per count / write block
+
+__device__ inline int64_t out_bit(const StrideGeom& sg, int b, int x, int y, int z) {
+    return (((int64_t)b * sg.oext[0] + x) * sg.oext[1] + y) * sg.oext[2] + z;
+}
+
+__global__ __launch_bounds__(kBlock) void k_stride_mark(const int32_t* __restrict__ coords,
+                                                        int64_t n, Geom g, StrideGeom sg,
+                                                        uint32_t* __restrict__ obits,
+                                                        MapState* st) {
+    const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const int32_t* c = coords + i * g.ncols;
+    const int b = g.ncols == 4 ? c[0] : 0;
+    const int32_t* p = c + (g.ncols == 4 ? 1 : 0);
+    const int x = p[0] - g.origin[0], y = p[1] - g.origin[1], z = p[2] - g.origin[2];
+    const bool in = (unsigned)b < (unsigned)g.batch && (unsigned)x < (unsigned)g.ext[0] &&
+                    (unsigned)y < (unsigned)g.ext[1] && (unsigned)z < (unsigned)g.ext[2];
+    if (!in) {
+        atomicOr(&st->status, kStRange);
+        return;
+    }
+    int x0 = 0, x1 = 0, y0 = 0, y1 = 0, z0 = 0, z1 = 0;
+    const int nx = axis_cands(x, sg.oext[0], sg, x0, x1);
+    const int ny = axis_cands(y, sg.oext[1], sg, y0, y1);
+    const int nz = axis_cands(z, sg.oext[2], sg, z0, z1);
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+            for (int f = 0; f < 2; ++f)
+                if (a < nx && e < ny && f < nz) {
+                    const int64_t L = out_bit(sg, b, a ? x1 : x0, e ? y1 : y0, f ? z1 : z0);
+                    atomicOr(&obits[L >> 5], 1u << (L & 31));
+                }
+}
+
+__global__ __launch_bounds__(kUThreads) void k_bits_count(const uint32_t* __restrict__ obits,
+                                                          int64_t words,
+                                                          uint32_t* __restrict__ counts) {
+    __shared__ uint32_t s_w[kUThreads / 64];
+    const int64_t base = (int64_t)blockIdx.x * kBTile + (int64_t)threadIdx.x * kBWords;
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < kBWords; ++j)
+        if (base + j < words) c += (uint32_t)__popc(obits[base + j]);
+    const uint32_t t = block_sum(c, s_w);
+    if (threadIdx.x == 0) counts[blockIdx.x] = t;
+}
+
+// The set bits of each block's words go to output rows offs[block] + (set bits
+// before them in the block), as k_unique_write does for run heads; each word is
+// cleared once read, so the bitmap is empty again for the next build.
+__global__ __launch_bounds__(kUThreads) void k_bits_write(uint32_t* __restrict__ obits,
+                                                          int64_t words, StrideGeom sg,
+                                                          const uint32_t* __restrict__ offs,
+                                                          int32_t* __restrict__ ocoords,
+                                                          int32_t* __restrict__ qcoords) {
+    __shared__ uint32_t s_w[kUThreads / 64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t base = (int64_t)blockIdx.x * kBTile + (int64_t)threadIdx.x * kBWords;
+    uint32_t v[kBWords];
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < kBWords; ++j) {
+        v[j] = base + j < words ? obits[base + j] : 0u;
+        c += (uint32_t)__popc(v[j]);
+    }
+    uint32_t inc = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = __shfl_up(inc, o);
+        if (lane >= o) inc += t;
+    }
+    if (lane == 63) s_w[w] = inc;
+    __syncthreads();
+    uint32_t pos = offs[blockIdx.x] + inc - c;
+    for (int q = 0; q < w; ++q) pos += s_w[q];
+    const int r = (sg.ksize - 1) / 2;
+#pragma unroll
+    for (int j = 0; j < kBWords; ++j) {
+        if (base + j >= words) break;
+        if (v[j]) obits[base + j] = 0u;
+        for (uint32_t bits = v[j]; bits; bits &= bits - 1) {
+            int64_t L = ((base + j) << 5) + __builtin_ctz(bits);
+            const int z = (int)(L % sg.oext[2]);
+            L /= sg.oext[2];
+            const int y = (int)(L % sg.oext[1]);
+            L /= sg.oext[1];
+            const int x = (int)(L % sg.oext[0]);
+            const int b = (int)(L / sg.oext[0]);
+            int32_t* oc = ocoords + (int64_t)pos * 4;
+            oc[0] = b;
+            oc[1] = x;
+            oc[2] = y;
+            oc[3] = z;
+            int32_t* qc = qcoords + (int64_t)pos * 4;
+            qc[0] = b;
+            qc[1] = sg.stride * x - sg.pad + r + sg.origin[0];
+            qc[2] = sg.stride * y - sg.pad + r + sg.origin[1];
+            qc[3] = sg.stride * z - sg.pad + r + sg.origin[2];
+            ++pos;
+        }
+    }
+}
+
 template <typename K>
 __device__ inline int64_t lower_bound_k(const K* __restrict__ keys, int64_t n, K t) {
     int64_t lo = 0, len = n;
@@ -307,6 +419,26 @@ hipError_t launch_unique(const uint64_t* keys, int64_t n_c, const StrideGeom& sg
     launch(k_unique_count, (unsigned)nb, kUThreads, 0, s, keys, n_c, sg.sentinel, counts);
     launch(k_scan_counts, 1u, 1024, 0, s, counts, nb, st);
     launch(k_unique_write, (unsigned)nb, kUThreads, 0, s, keys, n_c, sg, (const uint32_t*)counts,
+           ocoords, qcoords);
+    return hipGetLastError();
+}
+
+int64_t out_bitmap_words(const StrideGeom& sg, int batch) {
+    return ((int64_t)batch * sg.oext[0] * sg.oext[1] * sg.oext[2] + 31) / 32;
+}
+
+int64_t out_bitmap_blocks(int64_t words) { return (words + kBTile - 1) / kBTile; }
+
+hipError_t launch_stride_bitmap(const int32_t* coords, int64_t n, const Geom& g,
+                                const StrideGeom& sg, uint32_t* obits, int64_t words,
+                                uint32_t* counts, int32_t* ocoords, int32_t* qcoords,
+                                MapState* st, hipStream_t s) {
+    if (n <= 0 || words <= 0) return hipSuccess;
+    const int64_t nb = out_bitmap_blocks(words);
+    launch(k_stride_mark, blocks_of(n, kBlock), kBlock, 0, s, coords, n, g, sg, obits, st);
+    launch(k_bits_count, (unsigned)nb, kUThreads, 0, s, (const uint32_t*)obits, words, counts);
+    launch(k_scan_counts, 1u, 1024, 0, s, counts, nb, st);
+    launch(k_bits_write, (unsigned)nb, kUThreads, 0, s, obits, words, sg, (const uint32_t*)counts,
            ocoords, qcoords);
     return hipGetLastError();
 }
