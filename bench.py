@@ -1,22 +1,42 @@
 #!/usr/bin/env python3
 """Benchmark: microseconds per submanifold 3x3x3 layer including the kernel
 map, effective TFLOP/s on useful MACs, and the roofline of the dominant
-kernel.
+kernel, on the five seeded synthetic voxel sets.
 
-One step = one pass of the whole hot path over one seeded synthetic voxel
-set already resident in HBM: build the kernel map from raw coordinates
-(route, neighbour search with masks, compaction into per-tap pair lists --
-or the mask sort for the mask-tile algorithm) and run the layer(s) (gather
--> MFMA -> slab -> centre-tap GEMM with the bf16 finalize). Weights are
-packed once before the timed region (a packed weight is reused for every
-forward) and the packing time is reported on its own.
+One step = one pass of the whole hot path over one voxel set already
+resident in HBM: build the kernel map from raw coordinates (route, neighbour
+search with masks, compaction into per-tap pair lists) and run the layer(s)
+(gather -> MFMA -> slab -> centre-tap GEMM with the bf16 finalize). Weights
+are packed once before the timed region (a packed weight is reused by every
+forward); the packing time is reported on its own.
+
+The headline (the JSON line's "value") is the Stage set: 91,000 voxels,
+C = 128, six layers with independent weights sharing one map built every
+step, ReLU between layers; value = (map + 6 layers) / 6 microseconds per
+layer. Beside it, "configs" holds every set (tiny, lidar, deep, wide,
+stage) with its own timing, roofline, cold and warm map builds and the CPU
+oracle timed on the host cores (map and compute apart). "strided" holds the
+downsampling layers, "peaks_measured" an MFMA-only loop and a device copy.
 
 Prints ONE JSON line. --gpus above 1 exits: this build measures one GPU.
 
-Per-stage times come from a second pass with the library's stage timers:
+Kernel durations come from a second pass with the library's stage timers:
 every kernel launched in a stage carries its own HIP start/stop events
-(stamped by the kernel's dispatch), so a single-kernel stage's average is
-that kernel's average duration, as rocprofv3's kernel trace reports it.
+(stamped by the kernel's dispatch on the library's stream), so a
+single-kernel stage's average is that kernel's average duration.
+
+Algorithmic bytes of a launch are the compulsory ones only: every input
+that comes from outside the layer and every output it leaves, each once.
+Intermediates of the method (the grid, keys, sort passes, the slab, row
+bases) count zero.
+  k_gemm_centre     2 N C_in (x) + 2 C_in C_out (centre weights) + 2 N C_out (y)
+  k_gemm_nc         2 (T-1) C_in C_out (off-centre weights) + 8 (P - N) (pair lists)
+  k_dense_scatter / k_make_keys   16 N (coordinates)
+  k_lookup_compact  16 N (coordinates) + 4 N (masks) + 8 P (pair lists) [+ 4 T N table]
+  k_compact         4 N (masks) + 8 P (pair lists)
+  k_sorted_lookup / k_dense_lookup   4 N masks [+ 4 T N table]
+  k_conv_masktile   2 N C_in + 2 T C_in C_out + 2 N C_out (+ 8 N C_out per extra group pass)
+  sort passes, k_weight_pack (outside the step), fills: 0
 
   --summarize-pmc FETCH_DIR WRITE_DIR   turn two `rocprofv3 --pmc FETCH_SIZE`
       / `--pmc WRITE_SIZE` runs of this script (with --copy-probe-mb) into
@@ -48,31 +68,22 @@ PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
 RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # flop per byte
 CSRC = os.path.join(ROOT, "submanifold_sparse_convolution_amd", "csrc")
+CONFIG_NAMES = ("tiny", "lidar", "deep", "wide", "stage")
+HEADLINE = "stage"
 
-# stage -> the kernels it launches (dense route; the sorted route's neighbour
-# stage is k_make_keys + k_key_hist + k_os_pass + k_sorted_lookup)
-STAGE_KERNELS = {
-    "neighbours": ("k_dense_scatter", "k_dense_lookup"),
-    "mask_sort": ("k_mask_hist", "k_os_pass"),
-    "compact": ("k_compact",),
-    "gemm": ("k_gemm_nc",),
-    "centre": ("k_gemm_centre",),
-}
-# dense route with pair lists: the lookup is fused into the compaction kernel
-STAGE_KERNELS_FUSED = {
-    "neighbours": ("k_dense_scatter",),
-    "compact": ("k_lookup_compact",),
-    "gemm": ("k_gemm_nc",),
-    "centre": ("k_gemm_centre",),
-}
-MASK_TILE_GEMM = ("k_conv_masktile",)
+# stage timer index -> name (include/smconv.h SMC_STAGE_*)
+STAGES = ("map", "neighbours", "mask_sort", "compact", "gemm", "centre")
+# the sources that define each kernel (the digest of a traffic record)
 KERNEL_SOURCES = {
-    "k_compact": "compact_kernels.hip", "k_mask_hist": "compact_kernels.hip",
-    "k_lookup_compact": "compact_kernels.hip", "k_compact5": "compact_kernels.hip",
-    "k_dense_lookup5": "map_kernels.hip",
-    "k_gemm_nc": "gemm_kernels.hip", "k_gemm_centre": "gemm_kernels.hip",
-    "k_conv_masktile": "masktile_kernels.hip", "k_dense_scatter": "map_kernels.hip",
-    "k_dense_lookup": "map_kernels.hip", "k_os_pass": "radix_sort.hip",
+    "k_compact": ("compact_kernels.hip",), "k_mask_hist": ("compact_kernels.hip",),
+    "k_lookup_compact": ("compact_kernels.hip",), "k_compact5": ("compact_kernels.hip",),
+    "k_dense_lookup5": ("map_kernels.hip",), "k_dense_lookup": ("map_kernels.hip",),
+    "k_dense_scatter": ("map_kernels.hip",), "k_make_keys": ("map_kernels.hip",),
+    "k_sorted_lookup": ("map_kernels.hip",),
+    "k_gemm_nc": ("gemm_kernels.hip", "gemm_common.h"),
+    "k_gemm_centre": ("gemm_kernels.hip", "gemm_common.h"),
+    "k_conv_masktile": ("masktile_kernels.hip", "gemm_common.h"),
+    "k_os_pass": ("radix_sort.hip",),
 }
 
 
@@ -82,46 +93,50 @@ def dev_bf16(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def stage_model(stage, algo, route, n, p, c_in, c_out, taps=27):
-    """Algorithmic (compulsory) bytes and useful flops of one stage execution.
+# --------------------------------------------------------------------------
+# byte and flop models
+# --------------------------------------------------------------------------
 
-    Each input is counted once and each output once; reads of random grid cells
-    and gathered rows count their payload only. taps: 27 (3x3x3) or 125 (5x5x5);
-    the fused lookup + compaction kernel exists for 27 taps only.
-    """
+def kernel_model(kernel, n, p, c_in, c_out, taps=27, table=False, n_out=None, groups=1):
+    """Compulsory bytes and useful flops of one launch of `kernel` (module
+    docstring). n input rows, p pairs, n_out output rows (strided layers)."""
+    m = n if n_out is None else n_out
     p_nc = p - n
-    fused = route == "dense" and algo == "pairs" and taps == 27
-    t4 = 4 * taps                                  # bytes of one neighbour-table row
-    if stage == "neighbours":
-        if fused:
-            # scatter: coords in, grid cell + the row's cell record out; the previous
-            # build's cells read and put back (same count, taken as n)
-            return 16 * n + 4 * n + 4 * n + 4 * n + 4 * n, 0
-        mw = 4 if taps == 27 else 16              # mask bytes per row
-        if route == "dense":
-            # scatter as above; lookup: coords + taps cells in, nbr + mask out
-            return 16 * n + 16 * n + (16 * n + t4 * n) + (t4 * n + mw * n), 0
-        # sorted: coords -> keys, key sort passes, K^2 searches per row (8-byte keys)
-        k2 = 9 if taps == 27 else 25
-        return 16 * n + 8 * n + 5 * 2 * 12 * n + k2 * 8 * n + (t4 + mw) * n, 0
-    if stage == "mask_sort":
-        return 4 * n + 3 * 2 * 8 * n, 0
-    if stage == "compact":
-        if fused:
-            # coords + 27 cells in; nbr, mask, pair lists (in, out, slot), rowbase out
-            return 16 * n + 108 * n + 108 * n + 4 * n + 12 * p + 4 * n, 0
-        return (4 if taps == 27 else 16) * n + t4 * n + 12 * p + 4 * n, 0
-    if stage == "gemm" and algo == "pairs":
-        return ((2 * c_in + 8 + 4 * c_out) * p_nc + 2 * (taps - 1) * c_in * c_out,
-                2.0 * p_nc * c_in * c_out)
-    if stage == "gemm":          # mask tiles: x once, all weights, nbr/mask/perm, y once
-        return (2 * c_in * n + 2 * 27 * c_in * c_out + 116 * n + 2 * c_out * n,
+    t4 = 4 * taps * m if table else 0
+    if kernel == "k_gemm_centre":
+        return 2 * n * c_in + 2 * c_in * c_out + 2 * n * c_out, 2.0 * n * c_in * c_out
+    if kernel == "k_gemm_nc":
+        return 2 * (taps - 1) * c_in * c_out + 8 * p_nc, 2.0 * p_nc * c_in * c_out
+    if kernel == "k_conv_masktile":
+        extra = 8 * m * c_out * (groups - 1)
+        return (2 * n * c_in + 2 * taps * c_in * c_out + 2 * m * c_out + extra,
                 2.0 * p * c_in * c_out)
-    if stage == "centre":
-        return (2 * c_in * n + 2 * c_in * c_out + 8 * n + 4 * c_out * p_nc + 2 * c_out * n,
-                2.0 * n * c_in * c_out)
-    return 0, 0
+    if kernel in ("k_dense_scatter", "k_make_keys"):
+        return 16 * n, 0.0
+    if kernel == "k_lookup_compact":
+        return 16 * n + 4 * n + 8 * p + t4, 0.0
+    if kernel in ("k_compact", "k_compact5"):
+        return (4 if taps == 27 else 16) * n + 8 * p, 0.0
+    if kernel in ("k_sorted_lookup", "k_dense_lookup", "k_dense_lookup5", "k_query_lookup"):
+        return (4 if taps == 27 else 16) * m + t4, 0.0
+    return 0, 0.0
 
+
+def map_bytes(n, p, taps=27, table=False, perm=False):
+    """Compulsory bytes of a whole map build: coordinates in; masks, pair
+    lists (and the neighbour table / mask order when kept) out."""
+    return 16 * n + (4 if taps == 27 else 16) * n + 8 * p + (4 * taps * n if table else 0) + \
+        (4 * n if perm else 0)
+
+
+def layer_bytes(n, p, c_in, c_out, taps=27):
+    """Compulsory bytes of one layer's GEMM: x, all weights, pair lists, y."""
+    return 2 * n * c_in + 2 * taps * c_in * c_out + 8 * p + 2 * n * c_out
+
+
+# --------------------------------------------------------------------------
+# one workload on the GPU
+# --------------------------------------------------------------------------
 
 ORDERS = {"plain": 0, "calibrated": 1, "grouped": 3}   # mask-tile row order -> offset groups
 CALIBRATION_SEED_OFFSET = 1000
@@ -175,8 +190,32 @@ def tile_work_ratio(mask, perm, group_rows, group_masks):
     return executed / useful if useful else 1.0
 
 
+def stage_kernels(stage, algo, route, kernel_size=3, strided=False):
+    """The kernels one execution of a stage launches (pair path unless stated)."""
+    if stage == "gemm":
+        return ("k_conv_masktile",) if algo == "mask_tiles" or strided else ("k_gemm_nc",)
+    if stage == "centre":
+        return ("k_gemm_centre",)
+    if stage == "mask_sort":
+        return ("k_mask_hist", "k_os_pass")
+    fused = route == "dense" and algo == "pairs" and kernel_size == 3 and not strided
+    if stage == "neighbours":
+        if strided:
+            return ("k_stride_outputs", "k_dense_lookup" if route == "dense" else "k_query_lookup")
+        if route == "sorted":
+            return ("k_make_keys", "k_os_pass", "k_sorted_lookup")
+        if fused:
+            return ("k_dense_scatter",)
+        return ("k_dense_scatter", "k_dense_lookup5" if kernel_size == 5 else "k_dense_lookup")
+    if stage == "compact":
+        if fused:
+            return ("k_lookup_compact",)
+        return ("k_compact5",) if kernel_size == 5 else ("k_compact",)
+    return ()
+
+
 def run_workload(name, steps, warmup, sync_build=False, algo="pairs", copy_probe_mb=0,
-                 order="plain", kernel_size=3, frames=1, strided=False):
+                 order="plain", kernel_size=3, frames=1, strided=False, cold=False):
     import torch
 
     import submanifold_sparse_convolution_amd as smc
@@ -190,8 +229,21 @@ def run_workload(name, steps, warmup, sync_build=False, algo="pairs", copy_probe
     coords_d = torch.from_numpy(coords).cuda()
     x_d = dev_bf16(synth.features(n_rows, c, w.seed))
     w_ds = [dev_bf16(synth.weights(c, c, w.seed, layer, taps)) for layer in range(w.layers)]
-    m = smc.KernelMap()
     cal = None
+    cold_us = None
+    build_kw = dict(spatial_shape=w.grid, batch_size=frames, pairs=(algo == "pairs"),
+                    sort=(algo == "mask_tiles"), kernel_size=kernel_size)
+    if cold and not strided:
+        # the first build on a fresh handle: its buffers are allocated, the
+        # dense route's occupancy bitmap zero-filled once (host clock around
+        # a synchronous build)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        mc = smc.KernelMap().build(coords_d, **build_kw)
+        torch.cuda.synchronize()
+        cold_us = (time.perf_counter() - t0) * 1e6
+        mc.close()
+    m = smc.KernelMap()
     if algo == "mask_tiles" and order != "plain":
         bo, go, secs = calibrate(w, ORDERS[order])
         m.set_order(bo, go)
@@ -202,7 +254,7 @@ def run_workload(name, steps, warmup, sync_build=False, algo="pairs", copy_probe
         a = torch.empty(copy_probe_mb << 20, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
         torch.cuda.synchronize()
-        b.copy_(a)
+        smc.probe_copy(b, a)
         torch.cuda.synchronize()
         del a, b
     # weight packing, once per weight (timed on its own)
@@ -228,8 +280,7 @@ def run_workload(name, steps, warmup, sync_build=False, algo="pairs", copy_probe
         if strided:
             m.build_strided(coords_d, spatial_shape=w.grid, batch_size=frames, sync=sync_build)
             return m.forward(x_d, packed[0], out=ys[0], algo="mask_tiles")
-        m.build(coords_d, spatial_shape=w.grid, batch_size=frames, sync=sync_build,
-                pairs=(algo == "pairs"), sort=(algo == "mask_tiles"), kernel_size=kernel_size)
+        m.build(coords_d, sync=sync_build, **build_kw)
         h = x_d
         for layer in range(w.layers):
             h = m.forward(h, packed[layer], relu=layer + 1 < w.layers, out=ys[layer & 1],
@@ -260,7 +311,7 @@ def run_workload(name, steps, warmup, sync_build=False, algo="pairs", copy_probe
     m.timing(False)
     info = m.info()
     work_ratio = None
-    if algo == "mask_tiles":
+    if algo == "mask_tiles" and not strided:
         ex = m.export(pairs=False)
         go = cal["group_of"] if cal else [0] * 27
         gms = [sum(1 << t for t in range(27) if go[t] == g) for g in range(info["n_groups"])]
@@ -271,37 +322,32 @@ def run_workload(name, steps, warmup, sync_build=False, algo="pairs", copy_probe
     layers = 1 if strided else w.layers
     per_layer_us = wall_ms * 1e3 / layers
     flops_layer = 2.0 * pairs * c * c
+    # per execution, and executions per step
     stage_us = {k: (v[0] * 1e3 / v[1] if v[1] else 0.0) for k, v in stages.items()}
-    # per execution; forward stages run once per layer
-    model = {}
-    for st in ("neighbours", "mask_sort", "compact", "gemm", "centre"):
-        if stage_us.get(st, 0.0) <= 0.0:
-            continue
-        if strided:
-            by, fl = strided_model(st, info["route"], n_rows, info["n"], pairs, c, c)
-        else:
-            by, fl = stage_model(st, algo, info["route"], n_rows, pairs, c, c, taps)
-        if st == "gemm" and algo == "mask_tiles" and info["n_groups"] > 1:
-            # float32 partial sums: written by each early pass and read once after
-            by += 8 * c * sum(info["group_rows"][:-1])
-        us = stage_us[st]
-        model[st] = dict(us=us, bytes=by, flops=fl, gbs=by / (us * 1e-6) / 1e9,
-                         tflops=fl / (us * 1e-6) / 1e12 if fl else 0.0)
+    stage_per_step = {k: (v[1] / steps if steps else 0.0) for k, v in stages.items()}
+    # warm build: the build's own event bracket (first to last kernel, the
+    # handle's grids already resident)
+    warm_us = None if strided else stage_us.get("map")
     return dict(workload=w, coords=coords, info=info, pairs=pairs, ms_per_step=wall_ms,
                 gpu_ms_per_step=gpu_ms, per_layer_us=per_layer_us, pack_us=pack_us,
                 tflops_effective=flops_layer * layers / (wall_ms * 1e-3) / 1e12,
-                stage_us=stage_us, model=model, algo=algo, order=order, calibration=cal,
-                tile_work_ratio=work_ratio, kernel_size=kernel_size, frames=frames, n=n_rows,
-                strided=strided, n_out=info["n"])
+                stage_us=stage_us, stage_per_step=stage_per_step, algo=algo, order=order,
+                calibration=cal, tile_work_ratio=work_ratio, kernel_size=kernel_size,
+                frames=frames, n=n_rows, strided=strided, n_out=info["n"], layers=layers,
+                map_cold_us=cold_us, map_warm_us=warm_us, steps=steps)
 
+
+# --------------------------------------------------------------------------
+# roofline
+# --------------------------------------------------------------------------
 
 def source_digest(kernel):
-    f = KERNEL_SOURCES.get(kernel)
-    if f is None:
+    files = KERNEL_SOURCES.get(kernel)
+    if files is None:
         return None
     h = hashlib.sha256()
-    for path in sorted([os.path.join(CSRC, f), os.path.join(CSRC, "gemm_common.h"),
-                        os.path.join(CSRC, "smc_internal.h")]):
+    for f in files:
+        path = os.path.join(CSRC, f)
         if os.path.exists(path):
             with open(path, "rb") as fh:
                 h.update(fh.read())
@@ -322,100 +368,211 @@ def traffic_for(workload, algo, kernel):
     return round(k["bytes_per_launch"])
 
 
-def strided_model(stage, route, n, m, p, c_in, c_out):
-    """Algorithmic bytes and useful flops of a strided layer's stages (n inputs,
-    m outputs, p input-output pairs): candidates 8 keys per input, their sort
-    (4 passes of key + value), unique, the 27-tap lookup of every output, the
-    mask sort of the outputs and the mask-tile GEMM."""
-    if stage == "neighbours":
-        cand = 16 * n + 64 * n + 4 * 2 * 12 * 8 * n + 64 * n + 32 * m
-        look = 16 * m + 108 * m + 4 * m + (108 * m if route == "dense" else 9 * 8 * m)
-        return cand + look + (16 * n if route == "dense" else 16 * n + 8 * n + 5 * 2 * 12 * n), 0
-    if stage == "mask_sort":
-        return 4 * m + 3 * 2 * 8 * m, 0
-    if stage == "gemm":
-        return (2 * c_in * n + 2 * 27 * c_in * c_out + 116 * m + 2 * c_out * m,
-                2.0 * p * c_in * c_out)
-    return 0, 0
-
-
-def stage_kernels(stage, algo, route, kernel_size=3):
-    """The kernels one execution of a stage launches."""
-    if stage == "gemm" and algo == "mask_tiles":
-        return MASK_TILE_GEMM
-    fused = route == "dense" and algo == "pairs" and kernel_size == 3
-    if stage == "neighbours":
-        if route == "sorted":
-            return ("k_make_keys", "k_key_hist", "k_os_pass", "k_sorted_lookup")
-        if fused:
-            return ("k_dense_scatter",)
-        return ("k_dense_scatter", "k_dense_lookup5" if kernel_size == 5 else "k_dense_lookup")
-    if stage == "compact":
-        if fused:
-            return ("k_lookup_compact",)
-        return ("k_compact5",) if kernel_size == 5 else ("k_compact",)
-    return STAGE_KERNELS[stage]
-
-
-def roofline(r):
-    """The dominant stage (largest kernel time) and its roofline."""
-    model = r["model"]
-    if not model:
-        return None
-    st = max(model, key=lambda s: model[s]["us"])
-    mo = model[st]
-    kernels = stage_kernels(st, r["algo"], r["info"]["route"], r.get("kernel_size", 3))
-    if r.get("strided") and st == "neighbours":
-        kernels = ("k_dense_scatter" if r["info"]["route"] == "dense" else "k_make_keys",
-                   "k_stride_candidates", "k_key_hist", "k_os_pass", "k_unique_count",
-                   "k_scan_counts", "k_unique_write",
-                   "k_dense_lookup" if r["info"]["route"] == "dense" else "k_query_lookup")
-    kernel = kernels[0] if len(kernels) == 1 else "+".join(kernels)
-    intensity = mo["flops"] / mo["bytes"] if mo["bytes"] else 0.0
-    mfma = intensity > RIDGE
-    out = {"kernel": kernel, "stage": st,
-           "bound": "mfma" if mfma else "hbm",
-           "achieved": round(mo["tflops"] if mfma else mo["gbs"], 3 if mfma else 1),
-           "peak": PEAK_BF16_TFLOPS if mfma else PEAK_HBM_GBS,
-           "unit": "TFLOP/s" if mfma else "GB/s"}
-    out["frac"] = round(out["achieved"] / out["peak"], 5)
-    plain = r.get("kernel_size", 3) == 3 and r.get("frames", 1) == 1 and r.get("order") == "plain"
-    out["traffic"] = (traffic_for(r["workload"].name, r["algo"], kernel)
-                      if len(kernels) == 1 and plain else None)
-    out["avg_us"] = round(mo["us"], 3)
-    out["algorithmic_bytes"] = mo["bytes"]
-    out["flops_useful"] = mo["flops"]
-    out["mfma_frac_useful"] = round(mo["tflops"] / PEAK_BF16_TFLOPS, 5)
+def stage_rows(r):
+    """Per stage: kernels, us per execution, executions per step, and for a
+    single-kernel stage its compulsory bytes and flops."""
+    info = r["info"]
+    route = info["route"]
+    c = r["workload"].channels
+    taps = r["kernel_size"] ** 3
+    out = {}
+    for st in STAGES[1:]:
+        us = r["stage_us"].get(st, 0.0)
+        if us <= 0.0:
+            continue
+        ks = stage_kernels(st, r["algo"], route, r["kernel_size"], r["strided"])
+        row = dict(kernels=list(ks), us=us, per_step=r["stage_per_step"].get(st, 0.0))
+        if len(ks) == 1:
+            groups = info["n_groups"] if r["algo"] == "mask_tiles" else 1
+            by, fl = kernel_model(ks[0], r["n"], r["pairs"], c, c, taps,
+                                  table=r["algo"] == "mask_tiles" or r["strided"],
+                                  n_out=r["n_out"] if r["strided"] else None, groups=groups)
+            row.update(bytes=by, flops=fl)
+        out[st] = row
     return out
 
 
-def cpu_baseline(name, budget_s=12.0):
-    """The CPU oracle (untouched) on the same workload, repeated for ~budget_s."""
-    import synth
-    from oracle import smconv_oracle as so
+def roofline(r):
+    """The dominant kernel (largest time per step among single-kernel stages)
+    and its roofline on compulsory bytes (or useful flops)."""
+    rows = {k: v for k, v in stage_rows(r).items() if "bytes" in v}
+    if not rows:
+        return None
+    st = max(rows, key=lambda s: rows[s]["us"] * rows[s]["per_step"])
+    mo = rows[st]
+    kernel = mo["kernels"][0]
+    intensity = mo["flops"] / mo["bytes"] if mo["bytes"] else 0.0
+    mfma = intensity > RIDGE
+    us = mo["us"]
+    gbs = mo["bytes"] / (us * 1e-6) / 1e9
+    tfl = mo["flops"] / (us * 1e-6) / 1e12
+    out = {"kernel": kernel, "stage": st, "bound": "mfma" if mfma else "hbm",
+           "achieved": round(tfl if mfma else gbs, 3 if mfma else 1),
+           "peak": PEAK_BF16_TFLOPS if mfma else PEAK_HBM_GBS,
+           "unit": "TFLOP/s" if mfma else "GB/s"}
+    out["frac"] = round(out["achieved"] / out["peak"], 5)
+    plain = r["kernel_size"] == 3 and r["frames"] == 1 and r["order"] == "plain" and not r["strided"]
+    out["traffic"] = traffic_for(r["workload"].name, r["algo"], kernel) if plain else None
+    out["avg_us"] = round(us, 3)
+    out["launches_per_step"] = round(mo["per_step"], 3)
+    out["algorithmic_bytes"] = mo["bytes"]
+    out["flops_useful"] = mo["flops"]
+    out["hbm_frac"] = round(gbs / PEAK_HBM_GBS, 5)
+    out["mfma_frac_useful"] = round(tfl / PEAK_BF16_TFLOPS, 5)
+    return out
+
+
+def summary(r):
+    """The figures of one run: time per layer, throughput, stages, roofline."""
+    info = r["info"]
+    w = r["workload"]
+    c = w.channels
+    n, p = r["n"], r["pairs"]
+    taps = r["kernel_size"] ** 3
+    out = {
+        "workload": w.name, "n": n, "pairs": p, "pairs_per_voxel": round(p / n, 4) if n else 0,
+        "route": info["route"], "key_bits": info["key_bits"], "c_in": c, "c_out": c,
+        "layers": r["layers"], "us_per_layer": round(r["per_layer_us"], 2),
+        "ms_per_step": round(r["ms_per_step"], 4),
+        "gpu_ms_per_step_events": round(r["gpu_ms_per_step"], 4),
+        "tflops_effective": round(r["tflops_effective"], 3),
+        "frac_bf16_peak": round(r["tflops_effective"] / PEAK_BF16_TFLOPS, 5),
+        "weight_pack_us": round(r["pack_us"], 2),
+        "stages": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                   for k, v in stage_rows(r).items()},
+        "map_us_events": round(r["stage_us"].get("map", 0.0), 2),
+        "roofline": roofline(r),
+    }
+    if not r["strided"]:
+        step_bytes = map_bytes(n, p, taps) + r["layers"] * layer_bytes(n, p, c, c, taps)
+        out["step_compulsory_bytes"] = step_bytes
+        out["step_hbm_frac"] = round(step_bytes / (r["ms_per_step"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 5)
+    else:
+        out["n_out"] = r["n_out"]
+    if r["map_cold_us"] is not None:
+        out["map_cold_us"] = round(r["map_cold_us"], 1)
+        out["map_cold_note"] = ("first build on a fresh handle, host clock around a synchronous "
+                                "build: buffer allocation and the occupancy-bitmap zero fill "
+                                "(dense route) included")
+    if r["map_warm_us"] is not None:
+        out["map_warm_us"] = round(r["map_warm_us"], 2)
+    if info["route"] == "dense":
+        out["dense_grid_cells"] = info["grid_cells"]
+    if r["tile_work_ratio"] is not None:
+        out["tile_work_ratio"] = round(r["tile_work_ratio"], 4)
+    return out
+
+
+# --------------------------------------------------------------------------
+# CPU oracle and measured peaks
+# --------------------------------------------------------------------------
+
+def blas_threads():
     try:
         from threadpoolctl import threadpool_info
         blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
-        cores = max(blas) if blas else 1
+        return max(blas) if blas else 1
     except Exception:
-        cores = os.cpu_count() or 1
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(name, budget_s=8.0, reps=3):
+    """The CPU oracle, as it stands, on the same workload: its map (dict
+    lookups, mask sort, pair lists) and one layer's compute (per-tap float64
+    matmuls, bf16 rounding) timed apart, median of up to `reps` runs within
+    about budget_s seconds each. Per layer = map / layers + compute."""
+    import synth
+    from oracle import smconv_oracle as so
     w = synth.workload(name)
     coords = synth.make_coords(w)
     xb = synth.features(w.n, w.channels, w.seed)
     wb = synth.weights(w.channels, w.channels, w.seed)
-    times = []
+    x = so.bf16_bits_to_f64(xb)
+    wf = so.bf16_bits_to_f64(wb)
+    map_t, comp_t = [], []
     t_start = time.perf_counter()
-    while True:
+    while len(map_t) < reps:
         t0 = time.perf_counter()
-        so.subm_conv(coords, xb, wb)
-        times.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_start > budget_s or len(times) >= 20:
+        nbr, mask = so.build_kernel_map(coords)
+        so.mask_sort(mask)
+        pin, pout, toff = so.compact_pairs(nbr, mask)
+        map_t.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > budget_s:
             break
-    med = statistics.median(times)
-    return {"value": med * 1e6, "unit": "us/layer", "cores": cores, "kind": "oracle",
-            "sample": f"{len(times)} full {name} layers (map from a dict, float64 per-tap matmuls),"
-                      f" median; the map part is single-threaded Python, the matmuls use "
-                      f"{cores} BLAS threads"}
+    t_start = time.perf_counter()
+    while len(comp_t) < reps:
+        t0 = time.perf_counter()
+        acc = so.conv_accumulate(x, wf, pin, pout, toff, x.shape[0])
+        so.round_to_bf16(acc)
+        comp_t.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > budget_s:
+            break
+    mp, cp = statistics.median(map_t), statistics.median(comp_t)
+    cores = blas_threads()
+    return {"value": round((mp / w.layers + cp) * 1e6, 1), "unit": "us/layer", "cores": cores,
+            "kind": "oracle", "map_us": round(mp * 1e6, 1), "compute_us_per_layer": round(cp * 1e6, 1),
+            "sample": (f"{name}: {len(map_t)} map build(s) (dict lookups, mask sort, pair lists; "
+                       f"single-threaded Python) and {len(comp_t)} layer computation(s) "
+                       f"(per-tap float64 matmuls on {cores} BLAS threads, bf16 rounding), "
+                       f"medians; per layer = map / {w.layers} + one layer"),
+            "host_cpus": os.cpu_count()}
+
+
+def measured_peaks():
+    """An MFMA-only loop and a device copy on this GPU, next to the spec peaks."""
+    import torch
+
+    import submanifold_sparse_convolution_amd as smc
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = {}
+    smc.probe_mfma_bf16(1000)                           # warm-up
+    torch.cuda.synchronize()
+    ev0.record()
+    flops = smc.probe_mfma_bf16(200000)
+    ev1.record()
+    torch.cuda.synchronize()
+    tf = flops / (ev0.elapsed_time(ev1) * 1e-3) / 1e12
+    out["mfma_bf16_tflops"] = round(tf, 1)
+    out["mfma_frac_of_spec"] = round(tf / PEAK_BF16_TFLOPS, 4)
+    nbytes = 1 << 30
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    smc.probe_copy(b, a)
+    torch.cuda.synchronize()
+    reps = 10
+    ev0.record()
+    for _ in range(reps):
+        smc.probe_copy(b, a)
+    ev1.record()
+    torch.cuda.synchronize()
+    gbs = 2.0 * nbytes * reps / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+    out["copy_gbs"] = round(gbs, 1)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    ev1.record()
+    torch.cuda.synchronize()
+    gbs_t = 2.0 * nbytes * reps / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+    out["torch_copy_gbs"] = round(gbs_t, 1)
+    out["copy_frac_of_spec"] = round(max(gbs, gbs_t) / PEAK_HBM_GBS, 4)
+    out["note"] = ("k_probe_mfma: 8 waves per CU, 8 independent v_mfma_f32_16x16x32_bf16 chains "
+                   "each; k_probe_copy and torch's copy_: 1 GiB device-to-device, read + write "
+                   "bytes counted; copy_frac_of_spec takes the faster")
+    del a, b
+    return out
+
+
+# --------------------------------------------------------------------------
+# rocprofv3 summaries (run on the CPU)
+# --------------------------------------------------------------------------
+
+def _short(k):
+    import re
+    k = k.replace("(anonymous namespace)::", "").replace("void ", "").replace("smc::", "")
+    return re.sub(r"\(.*", "", k).split("<")[0].strip()
 
 
 def _pmc_rows(d, counter):
@@ -443,13 +600,7 @@ def summarize_mfma(pmc_dir, workload, algo, bench_out):
     launch (2 x pairs x C_in x C_out over the pairs that launch covers; n,
     pairs and C from the JSON line the profiled run printed, in bench_out),
     and the MFMA busy share of all SIMD cycles over the dispatch's own
-    (profiled) duration. Runs on the CPU."""
-    import re
-
-    def short(k):
-        k = k.replace("(anonymous namespace)::", "").replace("void ", "").replace("smc::", "")
-        return re.sub(r"\(.*", "", k).split("<")[0].strip()
-
+    (profiled) duration."""
     line = None
     with open(bench_out) as f:
         for ln in f:
@@ -468,7 +619,7 @@ def summarize_mfma(pmc_dir, workload, algo, bench_out):
     for fn in files:
         with open(fn) as f:
             for row in csv.DictReader(f):
-                k = short(row["Kernel_Name"])
+                k = _short(row["Kernel_Name"])
                 if k not in useful or row["Counter_Name"] not in MFMA_COUNTERS:
                     continue
                 d = per.setdefault(k, {}).setdefault(row["Dispatch_Id"], {})
@@ -485,7 +636,9 @@ def summarize_mfma(pmc_dir, workload, algo, bench_out):
             "dispatches": len(ds), "mfma_flops_executed": executed, "flops_useful": useful[k],
             "useful_over_executed": useful[k] / executed if executed else None,
             "mfma_busy_cycles": busy, "profiled_ns": ns,
-            "mfma_busy_frac": busy / (ns * 1e-9 * CLOCK_HZ * N_SIMD) if ns else None}
+            "mfma_busy_frac": busy / (ns * 1e-9 * CLOCK_HZ * N_SIMD) if ns else None,
+            "useful_tflops_profiled": useful[k] / (ns * 1e-9) / 1e12 if ns else None,
+            "source_digest": source_digest(k)}
     path = os.path.join(ROOT, "profiles", f"mfma_{workload}_{algo}.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
@@ -498,24 +651,17 @@ def summarize_mfma(pmc_dir, workload, algo, bench_out):
 
 def summarize_pmc(fetch_dir, write_dir, workload, algo, copy_mb):
     """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of every kernel, scaled by what the
-    same counters read for a plain device copy of copy_mb MiB."""
-    import re
-
-    def short(k):
-        k = k.replace("(anonymous namespace)::", "").replace("void ", "").replace("smc::", "")
-        return re.sub(r"\(.*", "", k).split("<")[0].strip()
-
+    same counters read for a plain device copy (k_probe_copy) of copy_mb MiB."""
     out = {"workload": workload, "algo": algo, "copy_probe_mib": copy_mb, "kernels": {}}
     per = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         vals = {}
         for k, v in _pmc_rows(d, counter):
-            vals.setdefault(short(k), []).append(v)
+            vals.setdefault(_short(k), []).append(v)
         per[counter] = vals
-    copy_names = [k for k in per["FETCH_SIZE"] if "copyBuffer" in k or "elementwise" in k.lower()]
-    if not copy_names:
-        raise SystemExit("no copy kernel found for the calibration")
-    cname = max(copy_names, key=lambda k: max(per["FETCH_SIZE"][k]))
+    if "k_probe_copy" not in per["FETCH_SIZE"]:
+        raise SystemExit("no k_probe_copy dispatch found for the calibration")
+    cname = "k_probe_copy"
     kib = copy_mb * 1024.0
     f_copy = max(per["FETCH_SIZE"][cname])
     w_copy = max(per["WRITE_SIZE"].get(cname, [0.0]))
@@ -525,7 +671,7 @@ def summarize_pmc(fetch_dir, write_dir, workload, algo, copy_mb):
     out["fetch_scale"] = kib / f_copy if f_copy else None
     out["write_scale"] = kib / w_copy if w_copy else None
     for k in sorted(set(per["FETCH_SIZE"]) | set(per["WRITE_SIZE"])):
-        if not k.startswith("k_"):
+        if not k.startswith("k_") or k.startswith("k_probe"):
             continue
         fv = per["FETCH_SIZE"].get(k, [])
         wv = per["WRITE_SIZE"].get(k, [])
@@ -546,22 +692,32 @@ def summarize_pmc(fetch_dir, write_dir, workload, algo, copy_mb):
               f"  ({v['dispatches']} dispatches)")
 
 
+# --------------------------------------------------------------------------
+# main
+# --------------------------------------------------------------------------
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="lidar",
-                    choices=["tiny", "lidar", "deep", "wide", "stage"])
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE, choices=list(CONFIG_NAMES))
     ap.add_argument("--algo", default="pairs", choices=["pairs", "mask_tiles"],
-                    help="forward algorithm of the headline line (the other is reported too)")
+                    help="forward algorithm of the headline line")
     ap.add_argument("--order", default="plain", choices=list(ORDERS),
                     help="mask-tile row order: plain mask value, calibrated bit order, or "
                          "calibrated order with 3 offset groups (calibrated on another seed)")
     ap.add_argument("--sync-build", action="store_true",
                     help="wait for the map's device-side checks inside every step")
+    ap.add_argument("--configs", default=",".join(CONFIG_NAMES),
+                    help="comma-separated sets timed beside the headline ('none': only it)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-other-algo", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=6.0,
+                    help="seconds per oracle part (map, compute) and set")
+    ap.add_argument("--no-strided", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true")
+    ap.add_argument("--other-algo", action="store_true",
+                    help="also time the mask-tile forward (three row orders) on the headline set")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB first (PMC calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -569,7 +725,8 @@ def main():
                     help="summarise a rocprofv3 --pmc run of the MFMA counters and the "
                          "JSON line that run printed")
     ap.add_argument("--report", default="",
-                    help="also run every workload and write their figures to this JSON file")
+                    help="also run the mask-tile orders, 5x5x5 kernels and batched frames of "
+                         "every set and write their figures to this JSON file")
     args = ap.parse_args()
 
     if args.summarize_mfma:
@@ -590,11 +747,16 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    configs = [] if args.configs == "none" else [c for c in args.configs.split(",") if c]
+    for cname in configs:
+        if cname not in CONFIG_NAMES:
+            raise SystemExit(f"unknown set {cname}")
 
     r = run_workload(args.workload, args.steps, args.warmup, args.sync_build, args.algo,
-                     args.copy_probe_mb, args.order)
+                     args.copy_probe_mb, args.order, cold=True)
     w, info = r["workload"], r["info"]
     c = w.channels
+    s = summary(r)
     line = {
         "metric": METRIC,
         "value": round(r["per_layer_us"], 2),
@@ -610,68 +772,79 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"{w.name}: {w.n} voxels, grid {w.grid[0]}x{w.grid[1]}x{w.grid[2]}, "
-                        f"C_in=C_out={c}, {w.layers} layer(s), seed {w.seed}",
+                        f"C_in=C_out={c}, {w.layers} layer(s) sharing one map, seed {w.seed}",
             "n": w.n, "pairs": r["pairs"], "pairs_per_voxel": round(r["pairs"] / w.n, 4),
             "route": info["route"], "c_in": c, "c_out": c, "layers": w.layers,
             "map_built_every_step": True, "build_mode": "sync" if args.sync_build else "async",
-            "algo": args.algo,
+            "algo": args.algo, "value_is": "(map + all layers) / layers, microseconds",
             **({"order": args.order} if args.algo == "mask_tiles" else {}),
         },
-        "tflops_effective": round(r["tflops_effective"], 3),
-        "frac_bf16_peak": round(r["tflops_effective"] / PEAK_BF16_TFLOPS, 5),
-        "gpu_ms_per_step_events": round(r["gpu_ms_per_step"], 4),
-        "stage_us": {k: round(v, 2) for k, v in r["stage_us"].items()},
-        "stages": {k: {"us": round(v["us"], 2), "GB/s": round(v["gbs"], 1),
-                       "hbm_frac": round(v["gbs"] / PEAK_HBM_GBS, 4),
-                       "TFLOP/s": round(v["tflops"], 2)} for k, v in r["model"].items()},
-        "weight_pack_us": round(r["pack_us"], 2),
-        "roofline": roofline(r),
+        "tflops_effective": s["tflops_effective"],
+        "frac_bf16_peak": s["frac_bf16_peak"],
+        "gpu_ms_per_step_events": s["gpu_ms_per_step_events"],
+        "stages": s["stages"],
+        "weight_pack_us": s["weight_pack_us"],
+        "map_cold_us": s.get("map_cold_us"),
+        "map_warm_us": s.get("map_warm_us"),
+        "step_hbm_frac": s.get("step_hbm_frac"),
+        "roofline": s["roofline"],
     }
     if r["tile_work_ratio"] is not None:
         line["tile_work_ratio"] = round(r["tile_work_ratio"], 4)
-    if not args.no_other_algo:
-        # the other forward algorithm, and the mask-tile row orders
-        variants = [("pairs", "plain")] if args.algo == "mask_tiles" else []
-        variants += [("mask_tiles", o) for o in ORDERS
-                     if not (args.algo == "mask_tiles" and o == args.order)]
-        line["other_algo"] = []
-        for algo2, order2 in variants:
-            r2 = run_workload(args.workload, args.steps, args.warmup, args.sync_build, algo2,
-                              order=order2)
-            e = {"algo": algo2, "us_per_layer": round(r2["per_layer_us"], 2),
-                 "tflops_effective": round(r2["tflops_effective"], 3),
-                 "stage_us": {k: round(v, 2) for k, v in r2["stage_us"].items()}}
-            if algo2 == "mask_tiles":
-                e["order"] = order2
-                e["tile_work_ratio"] = round(r2["tile_work_ratio"], 4)
-            line["other_algo"].append(e)
+    if not args.no_peaks:
+        line["peaks_measured"] = measured_peaks()
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(args.workload)
+        line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_budget)
+    if configs:
+        entries = []
+        for cname in configs:
+            if cname == args.workload and args.algo == "pairs" and args.order == "plain":
+                e = dict(s)
+            else:
+                rr = run_workload(cname, args.steps, args.warmup, args.sync_build, cold=True)
+                e = summary(rr)
+            if not args.no_cpu_baseline:
+                e["cpu_baseline"] = (line["cpu_baseline"] if cname == args.workload
+                                     and "cpu_baseline" in line
+                                     else cpu_baseline(cname, args.cpu_budget))
+            entries.append(e)
+        line["configs"] = entries
+    if not args.no_strided:
+        # downsampling layers (kernel 3, stride 2) on the same sets: new output cells,
+        # mask-tile forward; map built every step
+        line["strided"] = []
+        for cname in ("lidar", "deep", "wide", "stage"):
+            rr = run_workload(cname, max(10, args.steps // 2), args.warmup, strided=True)
+            e = summary(rr)
+            line["strided"].append({k: e[k] for k in ("workload", "n", "n_out", "pairs", "route",
+                                                      "us_per_layer", "tflops_effective",
+                                                      "stages", "roofline")})
+    if args.other_algo:
+        line["other_algo"] = []
+        for order2 in ORDERS:
+            r2 = run_workload(args.workload, args.steps, args.warmup, args.sync_build,
+                              "mask_tiles", order=order2)
+            e = summary(r2)
+            line["other_algo"].append({"algo": "mask_tiles", "order": order2,
+                                       "us_per_layer": e["us_per_layer"],
+                                       "tflops_effective": e["tflops_effective"],
+                                       "tile_work_ratio": e.get("tile_work_ratio"),
+                                       "stages": e["stages"]})
     if args.report:
         rep = {}
         runs = []
-        for name in ("tiny", "lidar", "deep", "wide", "stage"):
-            runs += [(name, "pairs", "plain", 3, 1)]
+        for name in CONFIG_NAMES:
             runs += [(name, "mask_tiles", o, 3, 1) for o in ORDERS]
-        # 5x5x5 kernels, and several frames as batches of one map
         runs += [("lidar", "pairs", "plain", 5, 1), ("deep", "pairs", "plain", 5, 1),
                  ("wide", "pairs", "plain", 5, 1), ("lidar", "pairs", "plain", 3, 4),
                  ("lidar", "pairs", "plain", 5, 4)]
-        runs = [r + (False,) for r in runs]
-        # strided (downsampling) layers, mask tiles
-        runs += [(nm, "mask_tiles", "plain", 3, 1, True) for nm in ("lidar", "deep", "wide", "stage")]
-        for name, algo, order, ks, frames, strided in runs:
+        for name, algo, order, ks, frames in runs:
             rr = run_workload(name, max(20, args.steps // 2), args.warmup, algo=algo,
-                              order=order, kernel_size=ks, frames=frames, strided=strided)
+                              order=order, kernel_size=ks, frames=frames)
             key = (f"{name}/{algo}" + ("" if order == "plain" else f"/{order}")
-                   + ("" if ks == 3 else f"/k{ks}") + ("" if frames == 1 else f"/b{frames}")
-                   + ("/strided" if strided else ""))
-            rep[key] = {k: rr[k] for k in ("pairs", "ms_per_step", "per_layer_us", "pack_us",
-                                           "tflops_effective", "stage_us", "model",
-                                           "tile_work_ratio", "calibration", "kernel_size",
-                                           "frames", "n", "n_out", "strided")}
-            rep[key]["route"] = rr["info"]["route"]
-            rep[key]["roofline"] = roofline(rr)
+                   + ("" if ks == 3 else f"/k{ks}") + ("" if frames == 1 else f"/b{frames}"))
+            rep[key] = summary(rr)
+            rep[key].update(kernel_size=ks, frames=frames, calibration=rr["calibration"])
         with open(args.report, "w") as f:
             json.dump(rep, f, indent=1)
     print(json.dumps(line), flush=True)

@@ -341,11 +341,16 @@ enum {
 };
 
 /*
- * Turn per-stage timing on or off for one handle. While on, every kernel a
- * stage launches carries its own start/stop HIP events, stamped by the
- * kernel's dispatch (hipExtLaunchKernel), so a stage's time is the sum of
- * its kernels' durations; SMC_STAGE_MAP instead brackets the whole build
- * with one event pair (gaps between kernels included). Off by default.
+ * Turn per-stage timing on or off for one handle. While on, every kernel the
+ * handle launches carries one stop event, stamped by the kernel's own
+ * dispatch (hipExtLaunchKernel) when it ends, and a kernel's time is the
+ * interval from the previous timed kernel's stop (or from a start marker
+ * before the first kernel after timing was turned on) to its own: on a stream
+ * that the GPU runs back to back, the kernel's duration plus the dispatch gap
+ * before it, so the stage times of a sequence add up to its elapsed time. All
+ * timed work of a handle must go to one stream. A stage's time is the sum of
+ * its kernels'; SMC_STAGE_MAP is the sum over every kernel of the build. Off
+ * by default.
  */
 int smc_timing_enable(smc_map* map, int on);
 
@@ -356,6 +361,28 @@ int smc_timing_enable(smc_map* map, int on);
  * reset != 0 clears the totals after reading.
  */
 int smc_timing_read(smc_map* map, double* ms, int64_t* calls, int reset);
+
+/*
+ * Attainable-peak probes (measurement only; they compute nothing of the
+ * convolution). The spec peaks used as roofline denominators are 2.5 PFLOP/s
+ * dense bf16 MFMA and 8 TB/s HBM; these give what the part reaches here.
+ *
+ * smc_probe_mfma_bf16: enqueues one kernel of 8 waves per compute unit (2 per SIMD),
+ * each running iters rounds of 8 independent v_mfma_f32_16x16x32_bf16 on
+ * register operands (iters rounded up to a multiple of 16). out is a device buffer of out_bytes bytes, at least
+ * smc_probe_mfma_out_bytes(compute units of the current device) (one float
+ * per thread is written). *flops (host, may be NULL) receives the flops the
+ * kernel executes. The caller times it on the stream. SMC_ERR_ARG for
+ * iters < 1, out NULL or out_bytes too small.
+ *
+ * smc_probe_copy: dst[0, bytes) = src[0, bytes) by a grid-stride kernel of
+ * 16-byte loads and stores; device pointers, 16-byte aligned, bytes a
+ * multiple of 16, the ranges must not overlap (SMC_ERR_ARG otherwise).
+ */
+size_t smc_probe_mfma_out_bytes(int n_cu);
+int smc_probe_mfma_bf16(int64_t iters, float* out, size_t out_bytes, double* flops,
+                        void* stream);
+int smc_probe_copy(void* dst, const void* src, size_t bytes, void* stream);
 
 /* Static text for a status code. */
 const char* smc_status_string(int status);

@@ -16,7 +16,8 @@ import ctypes
 import os
 
 __all__ = ["KernelMap", "PackedWeights", "pack_weights", "subm_conv3d", "lib", "library_path",
-           "SmconvError", "ROUTES", "EXPORTED_SYMBOLS", "use_torch_allocator"]
+           "SmconvError", "ROUTES", "EXPORTED_SYMBOLS", "use_torch_allocator", "probe_mfma_bf16",
+           "probe_copy"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libsmconv.so")
@@ -36,7 +37,8 @@ EXPORTED_SYMBOLS = [
     "smc_map_export", "smc_weight_packed_bytes", "smc_weight_pack", "smc_conv_forward",
     "smc_status_string", "smc_last_error", "smc_version", "smc_timing_enable", "smc_timing_read",
     "smc_map_set_order", "smc_map_calibrate", "smc_map_build_strided",
-    "smc_map_export_out_coords", "smc_set_allocator",
+    "smc_map_export_out_coords", "smc_set_allocator", "smc_probe_mfma_out_bytes",
+    "smc_probe_mfma_bf16", "smc_probe_copy",
 ]
 STAGES = ["map", "neighbours", "mask_sort", "compact", "gemm", "centre"]
 
@@ -104,11 +106,15 @@ def lib():
     L.smc_map_build_strided.argtypes = [vp, vp, i64, i32, vp, i32, i32, i32, i32, u32, vp]
     L.smc_map_export_out_coords.argtypes = [vp, vp]
     L.smc_set_allocator.argtypes = [vp, vp, vp]
+    L.smc_probe_mfma_out_bytes.argtypes = [i32]
+    L.smc_probe_mfma_out_bytes.restype = ctypes.c_size_t
+    L.smc_probe_mfma_bf16.argtypes = [i64, vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_double), vp]
+    L.smc_probe_copy.argtypes = [vp, vp, ctypes.c_size_t, vp]
     for name in ("smc_map_create", "smc_map_destroy", "smc_map_build", "smc_map_sync",
                  "smc_map_info", "smc_map_export", "smc_weight_pack", "smc_conv_forward",
                  "smc_timing_enable", "smc_timing_read", "smc_map_set_order",
                  "smc_map_calibrate", "smc_map_build_strided", "smc_map_export_out_coords",
-                 "smc_set_allocator"):
+                 "smc_set_allocator", "smc_probe_mfma_bf16", "smc_probe_copy"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -399,3 +405,27 @@ def subm_conv3d(coords, x, w, spatial_shape=None, relu: bool = False, route: str
     m = KernelMap().build(coords, spatial_shape=spatial_shape, route=route,
                           kernel_size=wp.kernel_size)
     return m.forward(x, wp, relu=relu)
+
+
+def probe_mfma_bf16(iters: int, stream=None) -> float:
+    """Enqueue the MFMA-only probe kernel on the stream; returns the flops it
+    executes (the caller times it)."""
+    import torch
+    L = lib()
+    n_cu = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    nbytes = L.smc_probe_mfma_out_bytes(n_cu)
+    out = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    flops = ctypes.c_double()
+    _check(L.smc_probe_mfma_bf16(int(iters), ctypes.c_void_p(out.data_ptr()), nbytes,
+                                 ctypes.byref(flops), _stream(stream)))
+    probe_mfma_bf16._keep = out          # alive until the stream has run the kernel
+    return flops.value
+
+
+def probe_copy(dst, src, stream=None):
+    """dst[:] = src[:] (CUDA tensors of equal byte size) by the library's copy probe."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("dst and src differ in size")
+    _check(lib().smc_probe_copy(ctypes.c_void_p(dst.data_ptr()), ctypes.c_void_p(src.data_ptr()),
+                                nbytes, _stream(stream)))

@@ -18,12 +18,12 @@ constexpr int kBlock = 256;         // threads per block for the map kernels
 constexpr int kMaxSplit = 1024;     // splitter table entries of the sorted route's searches
 
 // Per-kernel timing. While a stage timer of the API is active, take() hands
-// out a start/stop event pair for every kernel launched, and the launch
-// carries them (hipExtLaunchKernel: the events are stamped by the kernel's
-// own dispatch, so they time the kernel and nothing around it).
+// out a stop event for every kernel launched, and the launch carries it
+// (hipExtLaunchKernel: the event is stamped by the kernel's own dispatch when
+// the kernel ends).
 struct KernelTimer {
     void* ctx = nullptr;
-    bool (*take)(void* ctx, hipEvent_t* start, hipEvent_t* stop) = nullptr;
+    bool (*take)(void* ctx, hipEvent_t* stop) = nullptr;
 };
 extern thread_local KernelTimer g_ktimer;
 
@@ -32,9 +32,10 @@ template <typename... P, typename... A>
 inline void launch(void (*kern)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t s,
                    A... args) {
     static_assert(sizeof...(P) == sizeof...(A), "argument count");
-    hipEvent_t a = nullptr, b = nullptr;
-    if (g_ktimer.take && !g_ktimer.take(g_ktimer.ctx, &a, &b)) a = b = nullptr;
-    hipExtLaunchKernelGGL(kern, grid, block, (uint32_t)lds, s, a, b, 0u, static_cast<P>(args)...);
+    hipEvent_t b = nullptr;
+    if (g_ktimer.take && !g_ktimer.take(g_ktimer.ctx, &b)) b = nullptr;
+    hipExtLaunchKernelGGL(kern, grid, block, (uint32_t)lds, s, nullptr, b, 0u,
+                          static_cast<P>(args)...);
 }
 
 // bits of the device status word

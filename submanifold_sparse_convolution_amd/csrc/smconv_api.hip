@@ -174,7 +174,15 @@ struct smc_map {
     // stage timers
     bool timing = false;
     std::vector<hipEvent_t> ev_pool;
-    std::vector<std::pair<hipEvent_t, hipEvent_t>> ev_open[SMC_STAGE_COUNT];
+    struct TimedKernel {
+        hipEvent_t start;             // set on the first kernel of a sequence
+        hipEvent_t stop;
+        int stage;
+        bool in_build;
+    };
+    std::vector<TimedKernel> seq;     // timed kernels in launch order, not yet read
+    bool seq_open = false;            // the last timed kernel's stop starts the next interval
+    bool in_build = false;            // inside a timed build
     double stage_ms[SMC_STAGE_COUNT] = {};
     int64_t stage_calls[SMC_STAGE_COUNT] = {};
     int64_t stage_exec[SMC_STAGE_COUNT] = {};   // timed executions not yet read
@@ -266,69 +274,74 @@ hipEvent_t take_event(smc_map* m) {
         m->ev_pool.pop_back();
         return e;
     }
+    // timing only: no system-scope fence (cache write-back and invalidate) at
+    // the event, which would lengthen the kernel it is bound to
     hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess) {
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) {
         (void)hipGetLastError();
         return nullptr;
     }
     return e;
 }
 
-// Stage timer (only while timing is on). Kernel mode: every kernel launched
-// while the timer is active carries its own start/stop events, and the
-// stage's time is the sum of its kernels' durations. Bracket mode (the whole
-// build): one event before and one after, gaps between kernels included.
+// Stage timer (only while timing is on). Every kernel launched while a timer
+// is active carries one stop event, stamped by its own dispatch
+// (hipExtLaunchKernel), and a kernel's time is the interval from the stop of
+// the kernel before it in the handle's timed sequence (or from a start marker
+// recorded before the sequence's first kernel) to its own stop. On a stream
+// the GPU runs back to back, that is the kernel's duration plus the dispatch
+// gap before it, and the times of a sequence add up to its elapsed time. A
+// start event beside each kernel instead adds its own marker's latency to
+// every kernel (about 2 us each on MI355X). Kernel mode: the kernels count
+// for the timer's stage (and for SMC_STAGE_MAP inside a build). Bracket mode
+// (the whole build): kernels not inside a nested stage count for the build
+// only.
 struct StageTimer {
     smc_map* m;
     int stage;
     hipStream_t s;
     bool bracket;
     bool active = false;
-    hipEvent_t a = nullptr;
     KernelTimer saved;
-    static bool take_pair(void* ctx, hipEvent_t* e0, hipEvent_t* e1) {
+    static bool take_stop(void* ctx, hipEvent_t* stop) {
         StageTimer* t = static_cast<StageTimer*>(ctx);
-        hipEvent_t x = take_event(t->m), y = take_event(t->m);
-        if (!x || !y) {
-            if (x) t->m->ev_pool.push_back(x);
-            if (y) t->m->ev_pool.push_back(y);
+        smc_map* mm = t->m;
+        hipEvent_t start = nullptr;
+        if (!mm->seq_open) {
+            start = take_event(mm);
+            if (!start) return false;
+            if (hipEventRecord(start, t->s) != hipSuccess) {
+                (void)hipGetLastError();
+                mm->ev_pool.push_back(start);
+                return false;
+            }
+            mm->seq_open = true;
+        }
+        hipEvent_t e = take_event(mm);
+        if (!e) {
+            if (start) mm->ev_pool.push_back(start);
+            mm->seq_open = false;
             return false;
         }
-        t->m->ev_open[t->stage].push_back({x, y});
-        *e0 = x;
-        *e1 = y;
+        mm->seq.push_back({start, e, t->stage, mm->in_build});
+        *stop = e;
         return true;
     }
     StageTimer(smc_map* m_, int stage_, hipStream_t s_, bool bracket_ = false)
         : m(m_), stage(stage_), s(s_), bracket(bracket_) {
         if (!m->timing) return;
         active = true;
-        if (bracket) {
-            a = take_event(m);
-            if (a) (void)hipEventRecord(a, s);
-        } else {
-            saved = g_ktimer;
-            g_ktimer.ctx = this;
-            g_ktimer.take = &take_pair;
-        }
+        saved = g_ktimer;
+        g_ktimer.ctx = this;
+        g_ktimer.take = &take_stop;
+        if (bracket) m->in_build = true;
     }
     ~StageTimer() { finish(); }
     void finish() {
         if (!active) return;
         active = false;
-        if (bracket) {
-            if (!a) return;
-            hipEvent_t b = take_event(m);
-            if (b) {
-                (void)hipEventRecord(b, s);
-                m->ev_open[stage].push_back({a, b});
-            } else {
-                m->ev_pool.push_back(a);
-            }
-            a = nullptr;
-        } else {
-            g_ktimer = saved;
-        }
+        g_ktimer = saved;
+        if (bracket) m->in_build = false;
         m->stage_exec[stage] += 1;
     }
 };
@@ -391,11 +404,10 @@ int smc_map_destroy(smc_map* m) {
                           &m->ucounts, &m->ocoords, &m->qcoords, &m->scan, &m->split,
                           &m->obits};
         for (DevBuf* b : bufs) b->release();
-        for (auto& v : m->ev_open)
-            for (auto& pr : v) {
-                m->ev_pool.push_back(pr.first);
-                m->ev_pool.push_back(pr.second);
-            }
+        for (auto& tk : m->seq) {
+            if (tk.start) m->ev_pool.push_back(tk.start);
+            m->ev_pool.push_back(tk.stop);
+        }
         for (hipEvent_t e : m->ev_pool) (void)hipEventDestroy(e);
         if (m->host_state) (void)hipHostFree(m->host_state);
         if (m->done) (void)hipEventDestroy(m->done);
@@ -1172,21 +1184,29 @@ int smc_map_calibrate(smc_map* m, int n_groups, int32_t* bit_order, int32_t* gro
 int smc_timing_enable(smc_map* m, int on) {
     if (!m) return fail(SMC_ERR_ARG, "map is NULL");
     m->timing = on != 0;
+    m->seq_open = false;              // untimed work may follow: the next kernel starts anew
     return SMC_OK;
 }
 
 int smc_timing_read(smc_map* m, double* ms, int64_t* calls, int reset) {
     if (!m) return fail(SMC_ERR_ARG, "map is NULL");
+    hipEvent_t prev = nullptr;
+    for (const auto& tk : m->seq) {
+        if (tk.start) prev = tk.start;
+        SMC_HIP(hipEventSynchronize(tk.stop));
+        float e = 0.f;
+        if (prev) SMC_HIP(hipEventElapsedTime(&e, prev, tk.stop));
+        m->stage_ms[tk.stage] += e;
+        if (tk.in_build && tk.stage != SMC_STAGE_MAP) m->stage_ms[SMC_STAGE_MAP] += e;
+        prev = tk.stop;
+    }
+    for (const auto& tk : m->seq) {
+        if (tk.start) m->ev_pool.push_back(tk.start);
+        m->ev_pool.push_back(tk.stop);
+    }
+    m->seq.clear();
+    m->seq_open = false;
     for (int st = 0; st < SMC_STAGE_COUNT; ++st) {
-        for (auto& pr : m->ev_open[st]) {
-            SMC_HIP(hipEventSynchronize(pr.second));
-            float e = 0.f;
-            SMC_HIP(hipEventElapsedTime(&e, pr.first, pr.second));
-            m->stage_ms[st] += e;
-            m->ev_pool.push_back(pr.first);
-            m->ev_pool.push_back(pr.second);
-        }
-        m->ev_open[st].clear();
         m->stage_calls[st] += m->stage_exec[st];
         m->stage_exec[st] = 0;
         if (ms) ms[st] = m->stage_ms[st];
