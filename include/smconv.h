@@ -329,6 +329,27 @@ int smc_weight_pack(const uint16_t* w, int kernel_size, int c_in, int c_out, voi
 int smc_conv_forward(smc_map* map, const uint16_t* x, int c_in, const void* wpacked,
                      int c_out, void* y, unsigned flags, void* stream);
 
+/*
+ * smc_conv_forward without any allocation, for callers that cannot allocate
+ * device memory during the call: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. Same arguments, flags, algorithms,
+ * kernels and results as smc_conv_forward on the same map. The pair-list
+ * slab (4 c_out bytes per off-centre pair), or the float32 partial sums of a
+ * grouped mask-tile forward (4 n c_out bytes), lives in a fixed device array
+ * of 32 MiB that the library holds on every GPU it runs on until the process
+ * ends (its address is looked up when a map is first built on that GPU);
+ * larger needs return SMC_ERR_UNSUPPORTED before any work is enqueued. When
+ * the map's build has not been waited for and 26 pairs per row could exceed
+ * the array, the call waits for the build's counts first (one host read).
+ * The array is shared by every call on that GPU and keeps the last call's
+ * contents; nothing in it needs to start at zero. Calls that overlap on one
+ * GPU (other streams, other threads, other handles) race on it: the caller
+ * must order them. Stage timers do not run in this call. SMC_ERR_HIP if the
+ * array's device address could not be looked up on the map's GPU.
+ */
+int smc_conv_forward_noalloc(smc_map* map, const uint16_t* x, int c_in, const void* wpacked,
+                             int c_out, void* y, unsigned flags, void* stream);
+
 /* Stage timers. Stages of a build and of a forward, for measurement. */
 enum {
     SMC_STAGE_MAP = 0,         /* the whole smc_map_build enqueue (all steps below it) */

@@ -18,6 +18,9 @@ namespace smc {
 thread_local KernelTimer g_ktimer;
 }
 
+// One copy per GPU, held until the process ends; calls on one GPU share it.
+static __device__ __align__(256) unsigned char scratch[(size_t)32 << 20];
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -98,6 +101,15 @@ struct DevBuf {
     }
     template <typename T> T* as() const { return static_cast<T*>(p); }
 };
+
+// Scratch of the no-allocation forward (smc_conv_forward_noalloc): the
+// pair-list slab or the grouped mask tiles' float32 partial sums. The array is
+// a host-side stand-in in host code; kernels get its device address, looked
+// up once per device (scratch_ptr).
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
 
 constexpr int64_t kMaxRows = (int64_t)1 << 26;
 constexpr int64_t kMaxStridedRows = (int64_t)1 << 24;            // 8 candidates per input
@@ -190,10 +202,34 @@ struct smc_map {
 
 namespace {
 
+// Device address of this GPU's copy of `scratch`, looked up once per device
+// with that device current (the library's first map use on it). A failed
+// lookup leaves it null: only the no-allocation forward needs it, and it
+// reports the failure.
+void lookup_scratch(int dev) {
+    static_assert(sizeof(scratch) == kScratchBytes, "scratch size");
+    if (dev < 0 || dev >= kMaxDevices) return;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev]) return;
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) {
+        (void)hipGetLastError();
+        return;
+    }
+    g_scratch_ptr[dev] = p;
+}
+
+void* scratch_ptr(int dev) {
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    return g_scratch_ptr[dev];
+}
+
 int ensure_device(smc_map* m) {
     int dev = 0;
     SMC_HIP(hipGetDevice(&dev));
     if (m->device < 0) {
+        lookup_scratch(dev);
         m->device = dev;
         SMC_HIP(hipDeviceGetAttribute(&m->n_cu, hipDeviceAttributeMultiprocessorCount, dev));
         SMC_HIP(hipEventCreateWithFlags(&m->done, hipEventDisableTiming));
@@ -327,9 +363,9 @@ struct StageTimer {
         *stop = e;
         return true;
     }
-    StageTimer(smc_map* m_, int stage_, hipStream_t s_, bool bracket_ = false)
+    StageTimer(smc_map* m_, int stage_, hipStream_t s_, bool bracket_ = false, bool enable = true)
         : m(m_), stage(stage_), s(s_), bracket(bracket_) {
-        if (!m->timing) return;
+        if (!m->timing || !enable) return;
         active = true;
         saved = g_ktimer;
         g_ktimer.ctx = this;
@@ -953,8 +989,14 @@ int smc_weight_pack(const uint16_t* w, int kernel_size, int c_in, int c_out, voi
     return SMC_OK;
 }
 
-int smc_conv_forward(smc_map* m, const uint16_t* x, int c_in, const void* wpacked, int c_out,
-                     void* y, unsigned flags, void* stream) {
+}  // extern "C"
+
+// The forward of both entry points. fixed == nullptr: the handle's slab
+// (grow-only, allocated here when short). Otherwise fixed (fixed_bytes long)
+// holds the slab or partial sums, nothing is allocated and no stage timer
+// runs (an event pool may grow).
+static int conv_forward(smc_map* m, const uint16_t* x, int c_in, const void* wpacked, int c_out,
+                        void* y, unsigned flags, void* stream, float* fixed, size_t fixed_bytes) {
     if (!m) return fail(SMC_ERR_ARG, "map is NULL");
     if (!m->built) return fail(SMC_ERR_STATE, "map was never built");
     if (!m->pending && m->build_status != SMC_OK)
@@ -984,12 +1026,23 @@ int smc_conv_forward(smc_map* m, const uint16_t* x, int c_in, const void* wpacke
     if (mask_tiles) {
         // one pass per offset group; the earlier ones leave float32 partial sums
         const MaskOrder& o = m->sorted_order;
+        float* partial = nullptr;
         if (o.n_groups > 1) {
-            int rc = m->part.ensure((size_t)m->n * c_out * 4, s);
-            if (rc) return rc;
+            const size_t need = (size_t)m->n * c_out * 4;
+            if (fixed) {
+                if (need > fixed_bytes)
+                    return fail(SMC_ERR_UNSUPPORTED,
+                                "partial sums of %zu bytes exceed the fixed scratch of %zu bytes",
+                                need, fixed_bytes);
+                partial = fixed;
+            } else {
+                int rc = m->part.ensure(need, s);
+                if (rc) return rc;
+                partial = m->part.as<float>();
+            }
         }
         const MapState* dst = m->state.as<MapState>() + m->slot;
-        StageTimer t_mt(m, SMC_STAGE_GEMM, s);
+        StageTimer t_mt(m, SMC_STAGE_GEMM, s, false, fixed == nullptr);
         uint32_t prev = 0;
         for (int g = 0; g < o.n_groups; ++g) {
             GroupPass gp;
@@ -1001,7 +1054,7 @@ int smc_conv_forward(smc_map* m, const uint16_t* x, int c_in, const void* wpacke
             gp.perm = m->perm + (int64_t)g * m->n;
             gp.goff = (int64_t)g * m->n;
             gp.rows = gp.last ? nullptr : dst->group_rows + g;
-            gp.partial = o.n_groups > 1 ? m->part.as<float>() : nullptr;
+            gp.partial = partial;
             gp.centre_self = !m->strided;
             gp.n_in = m->n_in;
             SMC_HIP(launch_conv_masktile(x, c_in, wpacked, c_out, m->nbr.as<int32_t>(),
@@ -1020,24 +1073,54 @@ int smc_conv_forward(smc_map* m, const uint16_t* x, int c_in, const void* wpacke
         int rc = wait_build(m);
         if (rc) return rc;
     }
+    if (fixed && m->pending && slab > (double)fixed_bytes) {
+        int rc = wait_build(m);                  // the exact count decides
+        if (rc) return rc;
+    }
     if (!m->pending) slab = (double)m->host_state->totals[3] * c_out * 4.0;
     if (slab > (double)((size_t)1 << 46)) return fail(SMC_ERR_ALLOC, "slab of %.3g bytes", slab);
     // at least one row: lanes with nothing to add read row 0
     if (slab < (double)c_out * 4.0) slab = (double)c_out * 4.0;
-    int rc = m->part.ensure((size_t)slab, s);
-    if (rc) return rc;
-    StageTimer t_g(m, SMC_STAGE_GEMM, s);
+    float* part = fixed;
+    if (fixed) {
+        if (slab > (double)fixed_bytes)
+            return fail(SMC_ERR_UNSUPPORTED, "slab of %.0f bytes exceeds the fixed scratch of %zu bytes",
+                        slab, fixed_bytes);
+    } else {
+        int rc = m->part.ensure((size_t)slab, s);
+        if (rc) return rc;
+        part = m->part.as<float>();
+    }
+    StageTimer t_g(m, SMC_STAGE_GEMM, s, false, fixed == nullptr);
     SMC_HIP(launch_gemm_nc(x, c_in, wpacked, c_out, taps, m->pair_in.as<int32_t>(),
                            m->pair_slot.as<int32_t>(), m->state.as<MapState>() + m->slot, m->cap, m->n,
-                           m->n_cu, m->part.as<float>(), s));
+                           m->n_cu, part, s));
     t_g.finish();
-    StageTimer t_f(m, SMC_STAGE_CENTRE, s);
+    StageTimer t_f(m, SMC_STAGE_CENTRE, s, false, fixed == nullptr);
     SMC_HIP(launch_gemm_centre(x, c_in, wpacked, c_out, taps,
-                               m->rowbase.as<int32_t>(), m->n, m->part.as<float>(), y,
+                               m->rowbase.as<int32_t>(), m->n, part, y,
                                (flags & SMC_FWD_OUT_F32) != 0, (flags & SMC_FWD_RELU) != 0,
                                m->n_cu, s));
     t_f.finish();
     return SMC_OK;
+}
+
+extern "C" {
+
+int smc_conv_forward(smc_map* m, const uint16_t* x, int c_in, const void* wpacked, int c_out,
+                     void* y, unsigned flags, void* stream) {
+    return conv_forward(m, x, c_in, wpacked, c_out, y, flags, stream, nullptr, 0);
+}
+
+int smc_conv_forward_noalloc(smc_map* m, const uint16_t* x, int c_in, const void* wpacked,
+                             int c_out, void* y, unsigned flags, void* stream) {
+    if (!m) return fail(SMC_ERR_ARG, "map is NULL");
+    if (!m->built) return fail(SMC_ERR_STATE, "map was never built");
+    void* p = scratch_ptr(m->device);
+    if (!p) return fail(SMC_ERR_HIP, "device address of the fixed scratch unavailable on device %d",
+                        m->device);
+    return conv_forward(m, x, c_in, wpacked, c_out, y, flags, stream, static_cast<float*>(p),
+                        kScratchBytes);
 }
 
 int smc_map_set_order(smc_map* m, const int32_t* bit_order, const int32_t* group_of) {
