@@ -77,8 +77,13 @@ enum {
     SMC_BUILD_ASYNC = 1,    /* do not wait for the device-side checks; call smc_map_sync() later */
     SMC_BUILD_NO_PAIRS = 2, /* skip the per-tap pair lists: the pair-list forward and the
                                pair exports are then refused */
-    SMC_BUILD_NO_SORT = 4   /* skip the mask-sorted row order: SMC_FWD_MASK_TILES forwards
+    SMC_BUILD_NO_SORT = 4,  /* skip the mask-sorted row order: SMC_FWD_MASK_TILES forwards
                                and the perm export are then refused */
+    SMC_BUILD_TABLE = 8     /* keep the [n, K^3] neighbour table in device memory. Only the
+                               dense-route 3x3x3 build with pair lists and without the mask
+                               order leaves it out otherwise (its fused lookup and compaction
+                               write the pair lists straight from the lookups); every other
+                               build keeps it, because its later steps read it */
 };
 
 /* smc_conv_forward flags */
@@ -178,6 +183,9 @@ int smc_map_destroy(smc_map* map);
  * The dense route keeps its presence grid (4 bytes per padded cell) in the
  * handle between builds and leaves it cleared, so only the first build on
  * a handle pays for filling it.
+ * A build without the neighbour table in memory (see SMC_BUILD_TABLE) still
+ * exports it: smc_map_export fills it on the host from the pair lists, which
+ * hold every (input row, output row, tap) of the map.
  */
 int smc_map_build(smc_map* map, const int32_t* coords, int64_t n, int ncols,
                   const int32_t* spatial_shape, int batch_size, int kernel_size,

@@ -30,6 +30,7 @@ SMC_FWD_OUT_F32 = 2
 SMC_FWD_MASK_TILES = 4
 SMC_BUILD_NO_PAIRS = 2
 SMC_BUILD_NO_SORT = 4
+SMC_BUILD_TABLE = 8
 ALGOS = ("pairs", "mask_tiles")
 
 EXPORTED_SYMBOLS = [
@@ -242,13 +243,15 @@ class KernelMap:
 
     def build(self, coords, spatial_shape=None, batch_size: int = 0, route: str = "auto",
               sync: bool = True, pairs: bool = True, sort: bool = True,
-              kernel_size: int = 3, stream=None) -> "KernelMap":
+              kernel_size: int = 3, table: bool = False, stream=None) -> "KernelMap":
         """coords: int32 [N, 4] (b, x, y, z) or [N, 3] (x, y, z) CUDA tensor.
 
         pairs=False skips the per-tap pair lists (algo="pairs" then refuses the
         map); sort=False skips the mask-sorted row order (algo="mask_tiles"
         then refuses it). kernel_size 3 or 5 (a 5x5x5 map has pair lists and
-        no mask order)."""
+        no mask order). table=True keeps the neighbour table in device memory
+        where the build would leave it out (dense route, 3x3x3, pair lists
+        without the mask order); export() returns the table either way."""
         import torch
         _need(coords, torch.int32, "coords", 2)
         n, ncols = int(coords.shape[0]), int(coords.shape[1])
@@ -256,7 +259,7 @@ class KernelMap:
         if spatial_shape is not None:
             shape = (ctypes.c_int32 * 3)(*[int(v) for v in spatial_shape])
         flags = ((0 if sync else SMC_BUILD_ASYNC) | (0 if pairs else SMC_BUILD_NO_PAIRS)
-                 | (0 if sort else SMC_BUILD_NO_SORT))
+                 | (0 if sort else SMC_BUILD_NO_SORT) | (SMC_BUILD_TABLE if table else 0))
         if kernel_size == 5:
             flags |= SMC_BUILD_NO_SORT
         self._coords = coords          # keep alive while the stream reads it

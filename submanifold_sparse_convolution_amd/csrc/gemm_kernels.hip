@@ -35,6 +35,8 @@
 // of its rows (one vector store per row). The packed weights follow both.
 #include "gemm_common.h"
 
+#include <algorithm>
+
 namespace smc {
 namespace {
 
@@ -132,10 +134,10 @@ __device__ __forceinline__ void bg_fetch0(const u32x4* __restrict__ src, int ste
 // as is. All threads of the block call this. Loads past the last chunk
 // re-read it (valid addresses, unused), so the loop has no conditional
 // loads.
-template <int NBW, int MW, bool VEC, bool STREAM>
+template <int NBW, int MW, bool VEC, bool STREAM, int BWN>
 __device__ __forceinline__ void block_gemm(const uint16_t* const (&xrow)[MW], int c_in, int steps,
                                            const u32x4* __restrict__ src, u32x4* s_b, int lane, int g,
-                                           u32x4 (&a)[4][MW], u32x4 (&bw)[bg_per<NBW>()],
+                                           u32x4 (&a)[4][MW], u32x4 (&bw)[BWN],
                                            bool resident, f32x4 (&c)[MW][NBW]) {
     constexpr int kBufW = kChunk * NBW * 64;           // words per LDS buffer
     constexpr int kPer = bg_per<NBW>();                // words per thread per chunk
@@ -185,19 +187,18 @@ __device__ __forceinline__ void block_gemm(const uint16_t* const (&xrow)[MW], in
 #undef SMC_BG_STEP
 }
 
-// Store NBW float values of one slab or output row (columns col0 ..).
-// Whole 16-byte words are streaming (non-temporal) stores: the row is read
-// once, by a later launch, and lines that do not stay dirty in L2 shorten the
-// write-back at the end of this launch (measured: LiDAR forward 15.2 -> 14.7
-// us with the bf16 output stores streamed too).
+// Store NBW float values of one slab row (columns col0 ..). Plain stores: the
+// centre-tap GEMM that follows reads the slab, and lines kept in the caches
+// make that read cheaper than the store's extra write-back costs (measured:
+// 91k-row set, off-centre + centre 31.9 -> 31.6 us, wide 32.0 -> 29.9 us,
+// against streaming stores).
 template <int NBW>
 __device__ __forceinline__ void store_f32(float* __restrict__ dst, int col0, int c_out,
                                           const float (&v)[NBW]) {
     if (NBW >= 4 && col0 + NBW <= c_out && (c_out & 3) == 0) {
 #pragma unroll
         for (int q = 0; q < NBW; q += 4)
-            __builtin_nontemporal_store((f32x4){v[q], v[q + 1], v[q + 2], v[q + 3]},
-                                        reinterpret_cast<f32x4*>(dst + q));
+            *reinterpret_cast<f32x4*>(dst + q) = (f32x4){v[q], v[q + 1], v[q + 2], v[q + 3]};
     } else {
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb)
@@ -283,7 +284,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_gemm_nc(
         bg_fetch0<NBW>(src, steps, bw);
         if (!resident) __syncthreads();            // the previous tile's reads of s_b are done
         f32x4 c[MW][NBW];
-        block_gemm<NBW, MW, VEC, STREAM>(xrow, c_in, steps, src, s_b, lane, g, a, bw, resident, c);
+        block_gemm<NBW, MW, VEC, STREAM, bg_per<NBW>()>(xrow, c_in, steps, src, s_b, lane, g, a, bw, resident, c);
         if (col0 >= c_out) continue;
 #pragma unroll
         for (int m = 0; m < MW; ++m) {
@@ -304,10 +305,14 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_gemm_nc(
 // wave w takes rows +16 MW w .. +16 MW w + 16 MW - 1. A lane's 4 output rows
 // of a fragment are consecutive, so their slab rows form one consecutive run
 // [rowbase[first], rowbase[last] + deg(last)). The tile's independent loads
-// (gathered rows, run bounds) are issued first; the first kSlabBatch slab
+// (gathered rows, run bounds) are issued first; the first slab_batch() slab
 // rows of the lane's runs are in flight while the weights stream and the
-// MFMAs run; longer runs take further batches afterwards.
-constexpr int kSlabBatch = 4;
+// MFMAs run; longer runs take further batches afterwards. With the weights
+// resident (C_in <= 128) they are staged in LDS once, before the tile loop,
+// and the batch is 2, which keeps a wave within 128 registers: four waves per
+// SIMD (measured on the 91k-row set: 19.6 -> 18.9 us).
+template <bool STREAM>
+constexpr int slab_batch() { return STREAM ? 4 : 2; }
 
 // Slab row of flat index t over a lane's MW runs [rb[m][0], rb[m][0] + len[m])
 // (past the end: row 0, read but unused).
@@ -324,14 +329,14 @@ __device__ __forceinline__ int32_t slab_row(const int32_t (&rb)[MW][4], const in
     return t < tot ? sr : 0;
 }
 
-// kSlabBatch slab rows from flat index t0 on, NBW columns from col.
-template <int NBW, int MW>
+// SB slab rows from flat index t0 on, NBW columns from col.
+template <int NBW, int MW, int SB>
 __device__ __forceinline__ void load_slab(const float* __restrict__ part, int c_out, int col,
                                           bool vec, const int32_t (&rb)[MW][4],
                                           const int32_t (&len)[MW], int tot, int t0,
-                                          float (&pv)[kSlabBatch][NBW]) {
+                                          float (&pv)[SB][NBW]) {
 #pragma unroll
-    for (int u = 0; u < kSlabBatch; ++u) {
+    for (int u = 0; u < SB; ++u) {
         const float* prow = part + (int64_t)slab_row<MW>(rb, len, tot, t0 + u) * c_out + col;
         if (vec) {
 #pragma unroll
@@ -349,15 +354,15 @@ __device__ __forceinline__ void load_slab(const float* __restrict__ part, int c_
     }
 }
 
-// Add slab rows t0 .. t0 + kSlabBatch - 1 (those below tot) to the output rows
-// they belong to.
-template <int NBW, int MW>
+// Add slab rows t0 .. t0 + SB - 1 (those below tot) to the output rows they
+// belong to.
+template <int NBW, int MW, int SB>
 __device__ __forceinline__ void add_slab(const int32_t (&rb)[MW][4], const int32_t (&re)[MW],
                                          const int32_t (&len)[MW], int tot, int t0,
-                                         const float (&pv)[kSlabBatch][NBW],
+                                         const float (&pv)[SB][NBW],
                                          float (&v)[MW][4][NBW]) {
 #pragma unroll
-    for (int u = 0; u < kSlabBatch; ++u) {
+    for (int u = 0; u < SB; ++u) {
         const int t = t0 + u;
         if (t >= tot) break;
         const int32_t sl = slab_row<MW>(rb, len, tot, t);
@@ -428,7 +433,7 @@ __device__ __forceinline__ int centre_runs(int64_t row0, int g, int64_t n, int32
 }
 
 template <int NBW, int MW, bool OUT_F32, bool VEC, bool STREAM>
-__global__ __launch_bounds__(kGemmThreads, (STREAM && MW == 2) ? 1 : 2) void k_gemm_centre(
+__global__ __launch_bounds__(kGemmThreads, (STREAM && MW == 2) ? 1 : (STREAM ? 2 : 4)) void k_gemm_centre(
     const uint16_t* __restrict__ x, int c_in, int steps, const u32x4* __restrict__ wp, int n_wt,
     int c_out, int centre, const int32_t* __restrict__ rowbase, int64_t n,
     const float* __restrict__ part, void* __restrict__ yv, int relu) {
@@ -443,23 +448,39 @@ __global__ __launch_bounds__(kGemmThreads, (STREAM && MW == 2) ? 1 : 2) void k_g
     const int64_t rows_per_tile = 64 * MW;
     const int64_t n_rt = (n + rows_per_tile - 1) / rows_per_tile;
     const u32x4* src = wp + ((int64_t)centre * n_wt + wt_i) * n16;
+    if (!STREAM) {
+        constexpr int kPer = bg_per<NBW>();
+        u32x4 wv[kPer];
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int i = threadIdx.x + j * kGemmThreads;
+            wv[j] = src[i < n16 ? i : n16 - 1];
+        }
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int i = threadIdx.x + j * kGemmThreads;
+            if (i < n16) s_b[i] = wv[j];
+        }
+        __syncthreads();
+    }
     for (int64_t rt = blockIdx.x; rt < n_rt; rt += gridDim.x) {
         const int64_t row0 = rt * rows_per_tile + w * 16 * MW;
         const uint16_t* xrow[MW];
         u32x4 a[4][MW];
         int32_t rb[MW][4];
         int32_t rend[MW];
-        const bool resident = !STREAM && rt != blockIdx.x;    // the one-chunk slab stays in LDS
+        const bool resident = !STREAM;                        // loaded before the loop
         centre_tile_loads<MW, VEC>(x, c_in, steps, rowbase, n, row0, r, g, xrow, a, rb, rend);
-        u32x4 bw[bg_per<NBW>()];
-        if (STREAM || !resident) bg_fetch0<NBW>(src, steps, bw);
+        u32x4 bw[STREAM ? bg_per<NBW>() : 1];
+        if constexpr (STREAM) bg_fetch0<NBW>(src, steps, bw);
         int32_t re[MW], len[MW];
         const int tot = centre_runs<MW>(row0, g, n, rb, rend, re, len);
-        float pv[kSlabBatch][NBW];
-        load_slab<NBW, MW>(part, c_out, colc, vec_part, rb, len, tot, 0, pv);
+        constexpr int SB = slab_batch<STREAM>();
+        float pv[SB][NBW];
+        load_slab<NBW, MW, SB>(part, c_out, colc, vec_part, rb, len, tot, 0, pv);
         if (!resident) __syncthreads();            // the previous tile's reads of s_b are done
         f32x4 c[MW][NBW];
-        block_gemm<NBW, MW, VEC, STREAM>(xrow, c_in, steps, src, s_b, lane, g, a, bw, resident, c);
+        block_gemm<NBW, MW, VEC, STREAM, STREAM ? bg_per<NBW>() : 1>(xrow, c_in, steps, src, s_b, lane, g, a, bw, resident, c);
         float v[MW][4][NBW];
 #pragma unroll
         for (int m = 0; m < MW; ++m)
@@ -467,10 +488,10 @@ __global__ __launch_bounds__(kGemmThreads, (STREAM && MW == 2) ? 1 : 2) void k_g
             for (int j = 0; j < 4; ++j)
 #pragma unroll
                 for (int nb = 0; nb < NBW; ++nb) v[m][j][nb] = c[m][nb][j];
-        add_slab<NBW, MW>(rb, re, len, tot, 0, pv, v);
-        for (int t0 = kSlabBatch; t0 < tot; t0 += kSlabBatch) {
-            load_slab<NBW, MW>(part, c_out, colc, vec_part, rb, len, tot, t0, pv);
-            add_slab<NBW, MW>(rb, re, len, tot, t0, pv, v);
+        add_slab<NBW, MW, SB>(rb, re, len, tot, 0, pv, v);
+        for (int t0 = SB; t0 < tot; t0 += SB) {
+            load_slab<NBW, MW, SB>(part, c_out, colc, vec_part, rb, len, tot, t0, pv);
+            add_slab<NBW, MW, SB>(rb, re, len, tot, t0, pv, v);
         }
 #pragma unroll
         for (int m = 0; m < MW; ++m)
@@ -480,6 +501,218 @@ __global__ __launch_bounds__(kGemmThreads, (STREAM && MW == 2) ? 1 : 2) void k_g
                 if (row >= n || col0 >= c_out) continue;
                 store_row<NBW, OUT_F32>(yv, row, c_out, col0, v[m][j], relu);
             }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Wide inputs (C_in above 128, up to kBigMaxSteps k-steps): one (tap, column
+// tile) weight slab stays in LDS for the whole launch -- steps x NBW KiB, 128
+// KiB at C_in = 512 -- and eight waves stream 16-row fragments through it,
+// each fragment's rows loaded four k-steps at a time with the next four in
+// flight. No barrier in the loops. The chunked kernels above instead stream
+// the slab in 32 KiB chunks through two LDS buffers per 64-row tile, which
+// pays one L2 round trip per chunk per tile.
+constexpr int kBigThreads = 512;
+constexpr int kBigWaves = kBigThreads / 64;
+constexpr int kBigMaxSteps = 18;             // LDS: steps x NBW x 1 KiB <= 144 KiB
+
+inline bool big_ok(int steps, int nbw) {
+    return steps > kChunk && steps <= kBigMaxSteps && steps * nbw <= kBigMaxSteps * 8;
+}
+
+// k-steps s0 .. s0 + 3 of a fragment row (steps past the last re-read it).
+template <bool VEC>
+__device__ __forceinline__ void load_k4(const uint16_t* __restrict__ xrow, int c_in, int steps, int s0,
+                                        int g, u32x4 (&a)[kChunk]) {
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) a[i] = load_a4<VEC>(xrow, min(s0 + i, steps - 1) * 32 + g * 8, c_in);
+}
+
+template <int NBW>
+__device__ __forceinline__ void mma_k4(const u32x4 (&a)[kChunk], const u32x4* sb, int s0, int steps,
+                                       f32x4 (&c)[NBW]) {
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+        if (s0 + i < steps) {
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb)
+                c[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    as_bf16x8(a[i]), as_bf16x8(sb[((s0 + i) * NBW + nb) * 64]), c[nb], 0, 0, 0);
+        }
+    }
+}
+
+// The whole k loop of one 16-row fragment, four k-steps of rows at a time with
+// the next four in flight; a holds k-steps 0 .. 3 on entry (and is
+// overwritten). sb: this lane's word of the slab in LDS. (Loading every k-step
+// of the fragment at once, 16 per lane at C_in = 512, was slower: Deep centre
+// 22.3 -> 26.1 us, off-centre 25.5 -> 31.2 us.)
+template <int NBW, bool VEC>
+__device__ __forceinline__ void frag_gemm(const uint16_t* __restrict__ xrow, int c_in, int steps, int g,
+                                          const u32x4* sb, u32x4 (&a)[kChunk], f32x4 (&c)[NBW]) {
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) c[nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    u32x4 b[kChunk];
+    for (int s0 = 0; s0 < steps; s0 += 2 * kChunk) {
+        load_k4<VEC>(xrow, c_in, steps, s0 + kChunk, g, b);
+        mma_k4<NBW>(a, sb, s0, steps, c);
+        if (s0 + kChunk >= steps) break;
+        if (s0 + 2 * kChunk < steps) load_k4<VEC>(xrow, c_in, steps, s0 + 2 * kChunk, g, a);
+        mma_k4<NBW>(b, sb, s0 + kChunk, steps, c);
+    }
+}
+
+// The (tap, column tile) slab of n16 words into LDS, 8 loads per thread in
+// flight per round.
+__device__ __forceinline__ void stage_slab(const u32x4* __restrict__ src, int n16, u32x4* s_b) {
+    for (int base = 0; base < n16; base += 8 * kBigThreads) {
+        u32x4 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int i = base + (int)threadIdx.x + j * kBigThreads;
+            v[j] = src[i < n16 ? i : n16 - 1];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int i = base + (int)threadIdx.x + j * kBigThreads;
+            if (i < n16) s_b[i] = v[j];
+        }
+    }
+}
+
+// Off-centre taps, wide inputs: work items of kBigWaves x 16 pairs of one tap
+// (tap k's items from s_first[k]); block x takes the consecutive items
+// [x per, (x + 1) per), per = ceil(items / gridDim.x), so it reloads the slab
+// only when the tap changes. Each pair's product row goes to its slab row.
+template <int NBW>
+__global__ __launch_bounds__(kBigThreads, 2) void k_gemm_nc_big(
+    const uint16_t* __restrict__ x, int c_in, int steps, const u32x4* __restrict__ wp, int n_wt,
+    int c_out, int taps, const int32_t* __restrict__ pair_in,
+    const int32_t* __restrict__ pair_slot, const MapState* __restrict__ st, int64_t cap, int64_t n,
+    float* __restrict__ part) {
+    constexpr int kRows = kBigWaves * 16;          // pairs per item
+    extern __shared__ u32x4 s_b[];
+    __shared__ int32_t s_first[kMaxTaps + 1];
+    __shared__ int32_t s_cnt[kMaxTaps];
+    __shared__ int32_t s_wave0;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    nc_tap_table<kRows>(taps, st, s_first, s_cnt, &s_wave0);
+    const int n_items = s_first[taps];
+    const int per = (n_items + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int u0 = (int)blockIdx.x * per;
+    const int u1 = min(u0 + per, n_items);
+    const int wt_i = blockIdx.y;
+    const int col0 = wt_i * 16 * NBW + r * NBW;
+    const int n16 = steps * NBW * 64;
+    int tap = 0, slab_tap = -1;
+    for (int u = u0; u < u1; ++u) {
+        while (tap + 1 < taps && s_first[tap + 1] <= u) ++tap;
+        const int j0 = (u - s_first[tap]) * kRows + w * 16;     // this wave's first pair
+        const int cnt = s_cnt[tap];
+        const int64_t base = (int64_t)tap * cap + j0;
+        // the fragment's loads go out before any slab staging
+        const int pi = pair_in[base + r];
+        const int4 ps = *reinterpret_cast<const int4*>(pair_slot + base + 4 * g);
+        const bool ok = j0 + r < cnt && pi >= 0 && pi < n;
+        const uint16_t* xrow = x + (int64_t)(ok ? pi : 0) * c_in;
+        u32x4 a[kChunk];
+        load_k4<true>(xrow, c_in, steps, 0, g, a);
+        if (tap != slab_tap) {
+            __syncthreads();                       // earlier items' reads of s_b are done
+            stage_slab(wp + ((int64_t)tap * n_wt + wt_i) * n16, n16, s_b);
+            __syncthreads();
+            slab_tap = tap;
+        }
+        if (j0 >= cnt) continue;                   // a wave past the tap's pairs
+        f32x4 c[NBW];
+        frag_gemm<NBW, true>(xrow, c_in, steps, g, s_b + lane, a, c);
+        if (col0 >= c_out) continue;
+        const int slots[4] = {ps.x, ps.y, ps.z, ps.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (j0 + 4 * g + j >= cnt || slots[j] < 0) continue;
+            float v[NBW];
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb) v[nb] = c[nb][j];
+            store_f32<NBW>(part + (int64_t)slots[j] * c_out + col0, col0, c_out, v);
+        }
+    }
+}
+
+// Centre tap + output, wide inputs: the centre slab stays in LDS; wave
+// fragments of 16 consecutive rows (fragment = global wave index, stride =
+// all waves), the slab-run epilogue of the chunked kernel.
+template <int NBW, bool OUT_F32>
+__global__ __launch_bounds__(kBigThreads, 2) void k_gemm_centre_big(
+    const uint16_t* __restrict__ x, int c_in, int steps, const u32x4* __restrict__ wp, int n_wt,
+    int c_out, int centre, const int32_t* __restrict__ rowbase, int64_t n,
+    const float* __restrict__ part, void* __restrict__ yv, int relu) {
+    extern __shared__ u32x4 s_b[];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    const int wt_i = blockIdx.y;
+    const int col0 = wt_i * 16 * NBW + r * NBW;
+    const int colc = col0 < c_out ? col0 : 0;
+    const bool vec_part = col0 + NBW <= c_out && (c_out & 3) == 0 && NBW >= 4;
+    const int n16 = steps * NBW * 64;
+    const int64_t n_t = (n + 15) / 16;
+    const int64_t stride = (int64_t)gridDim.x * kBigWaves;
+    int64_t t = (int64_t)blockIdx.x * kBigWaves + w;
+    const bool live = t < n_t;
+    // a fragment's loads: its rows (k-steps 0 .. 3) and the run bounds of this lane's 4 rows
+    u32x4 a[kChunk];
+    const uint16_t* xr = x;
+    int32_t rb[1][4], rend[1];
+    auto frag_loads = [&](int64_t tt) {
+        const int64_t row0 = tt * 16;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t row = row0 + 4 * g + j;
+            rb[0][j] = rowbase[row < n ? row : n - 1];
+        }
+        const int64_t e = row0 + 4 * g + 4;
+        rend[0] = rowbase[e < n ? e : n];
+        const int64_t ir = row0 + r;
+        xr = x + (ir < n ? ir : 0) * c_in;
+        load_k4<true>(xr, c_in, steps, 0, g, a);
+    };
+    frag_loads(live ? t : 0);
+    stage_slab(wp + ((int64_t)centre * n_wt + wt_i) * n16, n16, s_b);
+    __syncthreads();
+    if (!live) return;
+    while (true) {
+        const int64_t row0 = t * 16;
+        int32_t re[1], len[1];
+        const int tot = centre_runs<1>(row0, g, n, rb, rend, re, len);
+        constexpr int SB = 4;
+        float pv[SB][NBW];
+        load_slab<NBW, 1, SB>(part, c_out, colc, vec_part, rb, len, tot, 0, pv);
+        f32x4 c[NBW];
+        frag_gemm<NBW, true>(xr, c_in, steps, g, s_b + lane, a, c);
+        const int64_t tn = t + stride;
+        int32_t rbc[1][4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rbc[0][j] = rb[0][j];
+        if (tn < n_t) frag_loads(tn);                  // next fragment's loads before the epilogue
+        float v[1][4][NBW];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb) v[0][j][nb] = c[nb][j];
+        add_slab<NBW, 1, SB>(rbc, re, len, tot, 0, pv, v);
+        for (int t0 = SB; t0 < tot; t0 += SB) {
+            load_slab<NBW, 1, SB>(part, c_out, colc, vec_part, rbc, len, tot, t0, pv);
+            add_slab<NBW, 1, SB>(rbc, re, len, tot, t0, pv, v);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t row = row0 + 4 * g + j;
+            if (row >= n || col0 >= c_out) continue;
+            store_row<NBW, OUT_F32>(yv, row, c_out, col0, v[0][j], relu);
+        }
+        if (tn >= n_t) break;
+        t = tn;
     }
 }
 
@@ -577,6 +810,33 @@ void launch_centre(dim3 grid, hipStream_t s, int mw, bool out_f32, const uint16_
         launch_centre_mw<NBW, 1, false, false>(grid, s, out_f32, x, c_in, steps, wp, n_wt, c_out, centre, rowbase, n, part, y, relu);
 }
 
+template <int NBW>
+void launch_nc_big(dim3 grid, size_t lds, hipStream_t s, const uint16_t* x, int c_in, int steps,
+                   const u32x4* wp, int n_wt, int c_out, int taps, const int32_t* pi,
+                   const int32_t* ps, const MapState* st, int64_t cap, int64_t n, float* part) {
+    static const bool ok = lds_ok(k_gemm_nc_big<NBW>, (size_t)kBigMaxSteps * 8 * 1024);
+    (void)ok;
+    launch(k_gemm_nc_big<NBW>, grid, kBigThreads, lds, s, x, c_in, steps, wp, n_wt, c_out, taps,
+           pi, ps, st, cap, n, part);
+}
+
+template <int NBW>
+void launch_centre_big(dim3 grid, size_t lds, hipStream_t s, bool out_f32, const uint16_t* x,
+                       int c_in, int steps, const u32x4* wp, int n_wt, int c_out, int centre,
+                       const int32_t* rowbase, int64_t n, const float* part, void* y, int relu) {
+    if (out_f32) {
+        static const bool ok = lds_ok(k_gemm_centre_big<NBW, true>, (size_t)kBigMaxSteps * 8 * 1024);
+        (void)ok;
+        launch(k_gemm_centre_big<NBW, true>, grid, kBigThreads, lds, s, x, c_in, steps, wp, n_wt,
+               c_out, centre, rowbase, n, part, y, relu);
+    } else {
+        static const bool ok = lds_ok(k_gemm_centre_big<NBW, false>, (size_t)kBigMaxSteps * 8 * 1024);
+        (void)ok;
+        launch(k_gemm_centre_big<NBW, false>, grid, kBigThreads, lds, s, x, c_in, steps, wp, n_wt,
+               c_out, centre, rowbase, n, part, y, relu);
+    }
+}
+
 }  // namespace
 
 size_t packed_weight_bytes(int taps, int c_in, int c_out) {
@@ -604,6 +864,20 @@ hipError_t launch_gemm_nc(const uint16_t* x, int c_in, const void* wpacked, int 
     const int steps = (c_in + 31) / 32;
     const int nbw = nbw_for(c_out);
     const int n_wt = (c_out + 16 * nbw - 1) / (16 * nbw);
+    if (big_ok(steps, nbw) && (c_in & 7) == 0) {
+        // one block per CU in all, column tiles of one item range on one die
+        const int64_t gx = xcd_round(std::max<int64_t>(1, n_cu / n_wt));
+        const dim3 grid((unsigned)gx, (unsigned)n_wt);
+        const size_t lds = (size_t)steps * nbw * 64 * 16;
+        const u32x4* wp = (const u32x4*)wpacked;
+        switch (nbw) {
+            case 1: launch_nc_big<1>(grid, lds, s, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part); break;
+            case 2: launch_nc_big<2>(grid, lds, s, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part); break;
+            case 4: launch_nc_big<4>(grid, lds, s, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part); break;
+            default: launch_nc_big<8>(grid, lds, s, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part); break;
+        }
+        return hipGetLastError();
+    }
     const int mw = mw_nc_for(c_in);
     int64_t gx = (taps - 1) * (cap / (64 * mw));  // tiles if every tap were full
     if (gx > (int64_t)n_cu * 2) gx = (int64_t)n_cu * 2;
@@ -628,9 +902,26 @@ hipError_t launch_gemm_centre(const uint16_t* x, int c_in, const void* wpacked, 
     const int steps = (c_in + 31) / 32;
     const int nbw = nbw_for(c_out);
     const int n_wt = (c_out + 16 * nbw - 1) / (16 * nbw);
+    if (big_ok(steps, nbw) && (c_in & 7) == 0) {
+        const int64_t frags = (n + 15) / 16;
+        const int64_t need = (frags + kBigWaves - 1) / kBigWaves;
+        const int64_t gx = xcd_round(std::min<int64_t>(need, std::max<int64_t>(1, n_cu / n_wt)));
+        const dim3 grid((unsigned)gx, (unsigned)n_wt);
+        const size_t lds = (size_t)steps * nbw * 64 * 16;
+        const u32x4* wp = (const u32x4*)wpacked;
+        const int rl = relu ? 1 : 0;
+        switch (nbw) {
+            case 1: launch_centre_big<1>(grid, lds, s, out_f32, x, c_in, steps, wp, n_wt, c_out, centre, rowbase, n, part, y, rl); break;
+            case 2: launch_centre_big<2>(grid, lds, s, out_f32, x, c_in, steps, wp, n_wt, c_out, centre, rowbase, n, part, y, rl); break;
+            case 4: launch_centre_big<4>(grid, lds, s, out_f32, x, c_in, steps, wp, n_wt, c_out, centre, rowbase, n, part, y, rl); break;
+            default: launch_centre_big<8>(grid, lds, s, out_f32, x, c_in, steps, wp, n_wt, c_out, centre, rowbase, n, part, y, rl); break;
+        }
+        return hipGetLastError();
+    }
     const int mw = mw_for(c_in);
     const int64_t row_tiles = (n + 64 * mw - 1) / (64 * mw);
-    const int64_t gx = xcd_round(row_tiles < (int64_t)n_cu * 2 ? row_tiles : (int64_t)n_cu * 2);
+    const int64_t cap_b = (int64_t)n_cu * (steps <= kChunk ? 4 : 2);
+    const int64_t gx = xcd_round(row_tiles < cap_b ? row_tiles : cap_b);
     dim3 grid((unsigned)gx, (unsigned)n_wt);
     const u32x4* wp = (const u32x4*)wpacked;
     const int rl = relu ? 1 : 0;

@@ -175,6 +175,7 @@ struct smc_map {
     DevBuf zrow;                      // zero row read for absent neighbours (mask-tile GEMM)
     bool has_pairs = false;
     bool has_sort = false;
+    bool has_table = false;           // nbr holds the last build's neighbour table
     int ksize = 3;                    // kernel size of the last build (taps = ksize^3)
     // strided builds: outputs differ from inputs (n = output rows, n_in = input rows)
     bool strided = false;
@@ -705,6 +706,9 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
         int32_t* nbr = m->nbr.as<int32_t>();
         uint32_t* mask = m->mask.as<uint32_t>();
         const bool fused = chosen == SMC_ROUTE_DENSE && want_pairs && kernel_size == 3;
+        // the fused kernel writes the table only when asked to or when the mask-tile
+        // path (which gathers through it) may run on this map
+        int32_t* nbr_out = fused && !want_sort && !(flags & SMC_BUILD_TABLE) ? nullptr : nbr;
         StageTimer t_nb(m, SMC_STAGE_NEIGHBOURS, s);
         if (chosen == SMC_ROUTE_DENSE) {
             const int gi = m->next_grid;
@@ -723,7 +727,7 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
             if (fused) {
                 t_nb.finish();
                 StageTimer t_cp(m, SMC_STAGE_COMPACT, s);
-                SMC_HIP(launch_lookup_compact(coords, n, g, grid, bits, nbr, mask, cap, kTileM, st,
+                SMC_HIP(launch_lookup_compact(coords, n, g, grid, bits, nbr_out, mask, cap, kTileM, st,
                                               m->pair_in.as<int32_t>(), m->pair_out.as<int32_t>(),
                                               m->pair_slot.as<int32_t>(),
                                               m->rowbase.as<int32_t>(), m->ws, status, s));
@@ -816,6 +820,8 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     }
     m->has_pairs = want_pairs;
     m->has_sort = want_sort;
+    m->has_table = !(chosen == SMC_ROUTE_DENSE && want_pairs && kernel_size == 3 && !want_sort &&
+                     !(flags & SMC_BUILD_TABLE)) || n == 0;
     m->sorted_order = ord;
     m->ksize = kernel_size;
     m->strided = strided;
@@ -936,7 +942,29 @@ int smc_map_export(smc_map* m, int32_t* nbr, uint32_t* mask, int32_t* perm, int3
     const int taps = m->ksize * m->ksize * m->ksize;
     const int mwords = m->ksize == 3 ? 1 : kMaxMaskWords;
     if (n > 0) {
-        if (nbr) SMC_HIP(hipMemcpy(nbr, m->nbr.p, (size_t)n * taps * 4, hipMemcpyDeviceToHost));
+        if (nbr && m->has_table)
+            SMC_HIP(hipMemcpy(nbr, m->nbr.p, (size_t)n * taps * 4, hipMemcpyDeviceToHost));
+        if (nbr && !m->has_table) {
+            // the table was not kept: every entry is a pair of the lists
+            std::vector<int32_t> pin, pout;
+            for (int64_t i = 0; i < n * taps; ++i) nbr[i] = -1;
+            for (int k = 0; k < taps; ++k) {
+                const int64_t c = hs.tap_count[k];
+                if (c > m->cap) return fail(SMC_ERR_STATE, "tap %d holds %lld pairs", k, (long long)c);
+                if (c == 0) continue;
+                pin.resize((size_t)c);
+                pout.resize((size_t)c);
+                SMC_HIP(hipMemcpy(pin.data(), m->pair_in.as<int32_t>() + (int64_t)k * m->cap,
+                                  (size_t)c * 4, hipMemcpyDeviceToHost));
+                SMC_HIP(hipMemcpy(pout.data(), m->pair_out.as<int32_t>() + (int64_t)k * m->cap,
+                                  (size_t)c * 4, hipMemcpyDeviceToHost));
+                for (int64_t j = 0; j < c; ++j) {
+                    if (pout[j] < 0 || pout[j] >= n)
+                        return fail(SMC_ERR_STATE, "pair output row %d out of range", pout[j]);
+                    nbr[(int64_t)pout[j] * taps + k] = pin[j];
+                }
+            }
+        }
         if (mask)
             SMC_HIP(hipMemcpy(mask, m->mask.p, (size_t)n * mwords * 4, hipMemcpyDeviceToHost));
         if (perm) {

@@ -174,3 +174,19 @@ def test_map_is_deterministic():
     a = gpu_map(coords, spatial_shape=(1440, 1440, 41))
     b = gpu_map(coords, spatial_shape=(1440, 1440, 41))
     assert_map_equal(a, b, "determinism")
+
+
+@pytest.mark.parametrize("name", ["tiny", "lidar", "stage"])
+@pytest.mark.parametrize("table", [False, True])
+def test_pair_only_build_with_and_without_the_table(name, table):
+    """The dense 3x3x3 build with pair lists and no mask order leaves the
+    neighbour table out of device memory unless asked (SMC_BUILD_TABLE): the
+    pair lists and masks are the same either way, and the exported table (from
+    the device, or filled on the host from the pair lists) equals the oracle's."""
+    w, coords = config(name)
+    m = smc.KernelMap().build(to_dev_i32(coords), spatial_shape=w.grid, sort=False, table=table)
+    got = m.export(perm=False)
+    m.close()
+    want = dict(oracle_map(name))
+    want.pop("perm")
+    assert_map_equal(got, want, f"{name} table={table}")
