@@ -413,6 +413,18 @@ int smc_probe_mfma_bf16(int64_t iters, float* out, size_t out_bytes, double* flo
                         void* stream);
 int smc_probe_copy(void* dst, const void* src, size_t bytes, void* stream);
 
+/*
+ * Test hook for the error path of the device-side waits. While on, the
+ * dense-route 3x3x3 compaction of this handle's builds waits for a look-back
+ * epoch that no block publishes, with a limit of 64 polls per thread instead
+ * of 2^22, so every wait runs out almost at once: the kernel still ends
+ * normally, its results are invalid (in bounds), and the build reports
+ * SMC_ERR_HIP ("a look-back wait ... ran out") like a real timeout. on = 0
+ * restores normal builds. For tests only; no result of a build made with it
+ * on is meaningful.
+ */
+int smc_test_force_lookback_timeout(smc_map* map, int on);
+
 /* Static text for a status code. */
 const char* smc_status_string(int status);
 

@@ -40,6 +40,7 @@ EXPORTED_SYMBOLS = [
     "smc_map_set_order", "smc_map_calibrate", "smc_map_build_strided",
     "smc_map_export_out_coords", "smc_set_allocator", "smc_probe_mfma_out_bytes",
     "smc_probe_mfma_bf16", "smc_probe_copy", "smc_conv_forward_noalloc",
+    "smc_test_force_lookback_timeout",
 ]
 STAGES = ["map", "neighbours", "mask_sort", "compact", "gemm", "centre"]
 
@@ -96,6 +97,7 @@ def lib():
     L.smc_weight_pack.argtypes = [vp, i32, i32, i32, vp, vp]
     L.smc_conv_forward.argtypes = [vp, vp, i32, vp, i32, vp, u32, vp]
     L.smc_conv_forward_noalloc.argtypes = [vp, vp, i32, vp, i32, vp, u32, vp]
+    L.smc_test_force_lookback_timeout.argtypes = [vp, i32]
     L.smc_status_string.argtypes = [i32]
     L.smc_status_string.restype = ctypes.c_char_p
     L.smc_last_error.argtypes = []
@@ -117,7 +119,7 @@ def lib():
                  "smc_timing_enable", "smc_timing_read", "smc_map_set_order",
                  "smc_map_calibrate", "smc_map_build_strided", "smc_map_export_out_coords",
                  "smc_set_allocator", "smc_probe_mfma_bf16", "smc_probe_copy",
-                 "smc_conv_forward_noalloc"):
+                 "smc_conv_forward_noalloc", "smc_test_force_lookback_timeout"):
         getattr(L, name).restype = i32
     _lib = L
     return L

@@ -83,16 +83,20 @@ __device__ inline uint32_t lookback(uint64_t* look, int stride, int d, int64_t p
 // column still open" flag alternate between two LDS slots by round parity,
 // so a slot is reset only after every thread has read it. Every thread of the
 // block must call this. The result is in s_sum[k] on return.
+// spin_limit bounds the waits of each thread; wait_xor (0 in every build but
+// the forced-timeout test, see smc_test_force_lookback_timeout) makes the
+// block wait for an epoch no block publishes, so that every wait runs out.
 template <int NC, int W, int kLanes>
 __device__ void block_lookback(uint64_t* look, int64_t pb, uint32_t epoch, uint32_t* status,
-                               uint32_t* s_sum, uint32_t* s_done) {
+                               uint32_t* s_sum, uint32_t* s_done, uint32_t spin_limit = kSpinLimit,
+                               uint32_t wait_xor = 0u) {
     static_assert(kLanes * NC <= 256, "one thread per (column, lane)");
     __shared__ uint32_t s_near[2][NC];
     __shared__ uint32_t s_open[2];
     const int tid = threadIdx.x;
     const int k = tid % NC, j0 = tid / NC;
     const bool active = tid < kLanes * NC;
-    const uint32_t ep = epoch & 0x3FFFFFFFu;
+    const uint32_t ep = (epoch ^ wait_xor) & 0x3FFFFFFFu;
     if (tid < NC) {
         s_sum[tid] = 0;
         s_done[tid] = pb < 0 ? 1u : 0u;
@@ -117,7 +121,7 @@ __device__ void block_lookback(uint64_t* look, int64_t pb, uint32_t epoch, uint3
             const int64_t idx = top - j0 - (int64_t)j * kLanes;
             if (!go || idx < 0) continue;
             while ((uint32_t)(e[j] >> 34) != ep) {
-                if (++spins > kSpinLimit) {
+                if (++spins > spin_limit) {
                     atomicOr(status, kStSortStall);
                     e[j] = 0;
                     break;
@@ -301,7 +305,9 @@ __device__ __forceinline__ void compact_chunk(CompactLds& L, uint32_t m, uint32_
                                               int32_t* __restrict__ pair_slot,
                                               int32_t* __restrict__ rowbase,
                                               uint64_t* __restrict__ look, uint32_t epoch,
-                                              uint32_t* status, int32_t* __restrict__ nbr_out) {
+                                              uint32_t* status, int32_t* __restrict__ nbr_out,
+                                              uint32_t spin_limit = kSpinLimit,
+                                              uint32_t wait_xor = 0u) {
     constexpr int kCols = kTaps + 1;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int64_t base0 = (int64_t)bid * kCChunk;
@@ -352,7 +358,8 @@ __device__ __forceinline__ void compact_chunk(CompactLds& L, uint32_t m, uint32_
             if (q < kCNbrVec && q < q_end) dst[q] = t4[j];
         }
     }
-    block_lookback<kCols, 16, 9>(look, (int64_t)bid - 1, epoch, status, L.pre, L.done);
+    block_lookback<kCols, 16, 9>(look, (int64_t)bid - 1, epoch, status, L.pre, L.done, spin_limit,
+                                 wait_xor);
     if (tid < kCols) {
         const int k = tid;
         const uint32_t run = L.tot[k];
@@ -475,7 +482,7 @@ __global__ __launch_bounds__(kCThreads) void k_lookup_compact(
     int64_t cap, int tile_m, MapState* st, int32_t* __restrict__ pair_in,
     int32_t* __restrict__ pair_out, int32_t* __restrict__ pair_slot, int32_t* __restrict__ rowbase,
     uint64_t* __restrict__ look, uint32_t* ticket, bool by_index, uint32_t epoch,
-    uint32_t* status) {
+    uint32_t* status, uint32_t spin_limit, uint32_t wait_xor) {
     __shared__ CompactLds L;
     const int tid = threadIdx.x;
     const uint32_t bid = chunk_of_block(by_index, ticket, &L.bid);
@@ -530,7 +537,7 @@ __global__ __launch_bounds__(kCThreads) void k_lookup_compact(
     if (row < n) mask[row] = m;
     __syncthreads();
     compact_chunk(L, m, bid, n, cap, tile_m, st, pair_in, pair_out, pair_slot, rowbase, look,
-                  epoch, status, nbr);
+                  epoch, status, nbr, spin_limit, wait_xor);
     if (!by_index && bid == gridDim.x - 1 && tid == 0) atomicExch(ticket, 0u);
 }
 
@@ -788,7 +795,7 @@ hipError_t launch_lookup_compact(const int32_t* coords, int64_t n, const Geom& g
     const bool by_index = fits_at_once((const void*)k_lookup_compact, 2, blocks);
     launch(k_lookup_compact, blocks, kCThreads, 0, s, coords, n, g, grid, bits, nbr, mask, cap,
            tile_m, st, pair_in, pair_out, pair_slot, rowbase, ws.look, ws.ticket, by_index, epoch,
-           status);
+           status, ws.force_timeout ? 64u : kSpinLimit, ws.force_timeout ? 0x15555555u : 0u);
     return hipGetLastError();
 }
 

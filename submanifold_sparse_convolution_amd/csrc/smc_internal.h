@@ -83,6 +83,9 @@ struct SortWork {
     // scan's per-segment sums, sized by sort_scan_ints(n) (nullptr: onesweep only)
     uint32_t* cnt = nullptr;
     int64_t cnt_ints = 0;
+    // test hook (smc_test_force_lookback_timeout): the dense route's fused
+    // compaction waits for an epoch no block publishes, 64 spins at most
+    bool force_timeout = false;
 };
 
 constexpr int kMaskBits = 27;

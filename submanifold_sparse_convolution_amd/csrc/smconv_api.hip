@@ -226,16 +226,20 @@ void* scratch_ptr(int dev) {
     return g_scratch_ptr[dev];
 }
 
+// First use of a handle: its device, event, pinned record and small buffers.
+// Every step can be repeated, and the handle counts as initialised (device
+// set) only once all of them succeeded, so a handle whose first build failed
+// to allocate is initialised again by its next build, never used half-made.
 int ensure_device(smc_map* m) {
     int dev = 0;
     SMC_HIP(hipGetDevice(&dev));
     if (m->device < 0) {
         lookup_scratch(dev);
-        m->device = dev;
         SMC_HIP(hipDeviceGetAttribute(&m->n_cu, hipDeviceAttributeMultiprocessorCount, dev));
-        SMC_HIP(hipEventCreateWithFlags(&m->done, hipEventDisableTiming));
-        if (hipHostMalloc((void**)&m->host_state, sizeof(MapState), hipHostMallocDefault) !=
-            hipSuccess) {
+        if (!m->done) SMC_HIP(hipEventCreateWithFlags(&m->done, hipEventDisableTiming));
+        if (!m->host_state &&
+            hipHostMalloc((void**)&m->host_state, sizeof(MapState), hipHostMallocDefault) !=
+                hipSuccess) {
             (void)hipGetLastError();
             m->host_state = nullptr;
             return fail(SMC_ERR_ALLOC, "hipHostMalloc of the readback record failed");
@@ -252,6 +256,7 @@ int ensure_device(smc_map* m) {
         SMC_HIP(launch_fill_i32(m->zrow.as<int32_t>(), kZeroRowBytes / 4, 0, nullptr));
         SMC_HIP(hipDeviceSynchronize());
         m->ws.ticket = m->ticket.as<uint32_t>();
+        m->device = dev;
     } else if (dev != m->device) {
         return fail(SMC_ERR_STATE, "map was created on device %d, current device is %d",
                     m->device, dev);
@@ -427,10 +432,12 @@ int smc_map_create(smc_map** out) {
 
 int smc_map_destroy(smc_map* m) {
     if (!m) return SMC_OK;
-    if (m->device >= 0) {
+    // (a handle whose first build failed part-way holds some buffers with no device set)
+    const bool touched = m->device >= 0 || m->done || m->host_state || m->state.p;
+    if (touched) {
         int cur = 0;
         (void)hipGetDevice(&cur);
-        (void)hipSetDevice(m->device);
+        if (m->device >= 0) (void)hipSetDevice(m->device);
         (void)hipDeviceSynchronize();
         DevBuf* bufs[] = {&m->state, &m->grid[0], &m->grid[1], &m->bits[0], &m->bits[1],
                           &m->cells[0], &m->cells[1], &m->keys0, &m->keys1, &m->keys2,
@@ -1289,6 +1296,12 @@ int smc_map_calibrate(smc_map* m, int n_groups, int32_t* bit_order, int32_t* gro
         for (int p = (26 * g) / n_groups; p < (26 * (g + 1)) / n_groups; ++p)
             group_of[chosen[p]] = g;
     group_of[kCentre] = n_groups - 1;
+    return SMC_OK;
+}
+
+int smc_test_force_lookback_timeout(smc_map* m, int on) {
+    if (!m) return fail(SMC_ERR_ARG, "map is NULL");
+    m->ws.force_timeout = on != 0;
     return SMC_OK;
 }
 

@@ -76,3 +76,32 @@ def test_allocator_switch_keeps_each_buffer_with_its_maker():
         assert torch.cuda.memory_allocated() == base
     finally:
         smc.use_torch_allocator(False)
+
+
+def test_allocator_returning_null_is_alloc_error():
+    """A caller's allocator that returns NULL makes the call fail with
+    SMC_ERR_ALLOC (a fresh handle at its first build, and an initialised
+    handle whose buffers must grow); NULL, NULL restores hipMalloc and the
+    same handles build again."""
+    import ctypes
+    L = smc.lib()
+    null_alloc = smc._ALLOC_T(lambda ctx, nbytes, stream: None)
+    no_free = smc._FREE_T(lambda ctx, ptr, stream: None)
+    small = synth.ground_box_coords(500, (40, 40, 10), seed=21, n_boxes=5)
+    big = synth.ground_box_coords(6000, (90, 90, 16), seed=22, n_boxes=30)
+    grown = smc.KernelMap().build(to_dev_i32(small), spatial_shape=(40, 40, 10))  # hipMalloc
+    fresh = smc.KernelMap()
+    assert L.smc_set_allocator(ctypes.cast(null_alloc, ctypes.c_void_p),
+                               ctypes.cast(no_free, ctypes.c_void_p), None) == 0
+    try:
+        for m, c, shape in ((fresh, small, (40, 40, 10)), (grown, big, (90, 90, 16))):
+            with pytest.raises(smc.SmconvError) as e:
+                m.build(to_dev_i32(c), spatial_shape=shape)
+            assert e.value.status == 5, str(e.value)
+            assert "NULL" in str(e.value)
+    finally:
+        assert L.smc_set_allocator(None, None, None) == 0
+    for m, c, shape in ((fresh, small, (40, 40, 10)), (grown, big, (90, 90, 16))):
+        m.build(to_dev_i32(c), spatial_shape=shape)
+        assert m.info()["pairs"] == len(oracle_map_of(c)["pair_in"])
+        m.close()

@@ -85,3 +85,28 @@ def test_forward_before_build():
                                     ctypes.c_void_p(y.data_ptr()), 0, None)
     assert rc == 7
     m.close()
+
+
+def test_forced_lookback_timeout_reports_hip_error():
+    """The device-side look-back wait running out (forced from the host: the
+    compaction waits for an epoch no block publishes, 64 polls at most) is
+    latched and reported as SMC_ERR_HIP by the build; the forward refuses the
+    map; with the hook off the same handle builds a correct map again."""
+    from _util import assert_map_equal, oracle_map_of
+    L = smc.lib()
+    w = synth.workload("lidar")
+    coords = synth.make_coords(w)
+    m = smc.KernelMap()
+    assert L.smc_test_force_lookback_timeout(m._h, 1) == 0
+    assert status_of(lambda: m.build(to_dev_i32(coords), spatial_shape=w.grid, sort=False)) == 6
+    assert b"ran out" in L.smc_last_error()
+    x = to_dev_bf16(synth.features(len(coords), 128, 2))
+    wp = smc.pack_weights(to_dev_bf16(synth.weights(128, 128, 2)))
+    assert status_of(lambda: m.forward(x, wp)) == 7
+    assert L.smc_test_force_lookback_timeout(m._h, 0) == 0
+    m.build(to_dev_i32(coords), spatial_shape=w.grid, sort=False)
+    got = m.export(perm=False)
+    want = dict(oracle_map_of(coords))
+    want.pop("perm")
+    assert_map_equal(got, want, "after the forced timeout")
+    m.close()

@@ -894,3 +894,46 @@ def test_planted_strided_unsorted_outputs(monkeypatch):
         return oc[::-1].copy(), osh, nbr[::-1].copy(), mask[::-1].copy()
     monkeypatch.setattr(so, "build_strided_map", broken)
     assert _fails(check_strided_map, synth.tiny_coords(seed=9, n=100, side=8), (8, 8, 8))
+
+
+CALIBRATION = os.path.join(os.path.dirname(__file__), "golden", "calibration.json")
+
+
+def check_calibration_fixture():
+    e = json.load(open(CALIBRATION))
+    mask = np.asarray([sum(1 << t for t in taps) for taps in e["rows_taps"]], np.uint32)
+    tile = e["tile"]
+    for G, key in ((1, None), (2, "group_of_2"), (3, "group_of_3")):
+        order, group_of = so.calibrate_order(mask, G, tile)
+        assert order == e["bit_order"], f"G={G}: bit order {order}"
+        if key:
+            for g, taps in e[key].items():
+                assert sorted(t for t in range(27) if group_of[t] == int(g)) == sorted(taps), \
+                    f"G={G}: group {g}"
+    cnt = [int(((mask >> np.uint32(t)) & 1).sum()) for t in range(27)]
+    start = sorted((t for t in range(27) if t != 13), key=lambda t: (cnt[t], t)) + [13]
+    o0, c0 = so.group_row_orders(mask, start)
+    o1, c1 = so.group_row_orders(mask, e["bit_order"])
+    assert so.tile_work(mask, o0[0], c0[0], None, tile) == e["work_start"]
+    assert so.tile_work(mask, o1[0], c1[0], None, tile) == e["work_chosen"]
+
+
+def test_calibration_hand_worked():
+    """calibrate_order on six hand-worked rows (tiles of 2): the exact greedy
+    choices, including ties kept for the earlier candidate, and its groups."""
+    check_calibration_fixture()
+
+
+def test_planted_calibration_ties_to_later_candidate(monkeypatch):
+    # every later evaluation looks a hair cheaper, so equal works go to the later candidate
+    orig_tw = so.tile_work
+    calls = [0]
+
+    def later_wins(*a, **k):
+        calls[0] += 1
+        return orig_tw(*a, **k) - 1e-6 * calls[0]
+    monkeypatch.setattr(so, "tile_work", later_wins)
+    e = json.load(open(CALIBRATION))
+    mask = np.asarray([sum(1 << t for t in taps) for taps in e["rows_taps"]], np.uint32)
+    order, _ = so.calibrate_order(mask, 1, e["tile"])
+    assert order != e["bit_order"]
