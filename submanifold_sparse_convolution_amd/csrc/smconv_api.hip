@@ -677,14 +677,19 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
         (rc = m->look.ensure(look_bytes, s)))
         return rc;
     if (!ord.plain && (rc = m->okeys.ensure((size_t)items * 4, s))) return rc;
+    // strided outputs: a small output grid goes through a bitmap (no candidate
+    // buffers); a larger one sorts 8 candidate keys per input
+    const bool cand_sort = strided && out_bitmap_words(sg, g.batch) > kOutBitmapWords;
     if (strided &&
+        ((rc = m->ocoords.ensure((size_t)n_cand * 16, s)) ||
+         (rc = m->qcoords.ensure((size_t)n_cand * 16, s))))
+        return rc;
+    if (cand_sort &&
         ((rc = m->ck0.ensure((size_t)n_cand * 8, s)) || (rc = m->ck1.ensure((size_t)n_cand * 8, s)) ||
          (rc = m->ck2.ensure((size_t)n_cand * 8, s)) || (rc = m->cv0.ensure((size_t)n_cand * 4, s)) ||
          (rc = m->cv1.ensure((size_t)n_cand * 4, s)) ||
          (rc = m->chist.ensure((size_t)kHistKeyInts * 4, s)) ||
-         (rc = m->ucounts.ensure((size_t)unique_blocks(n_cand) * 4, s)) ||
-         (rc = m->ocoords.ensure((size_t)n_cand * 16, s)) ||
-         (rc = m->qcoords.ensure((size_t)n_cand * 16, s))))
+         (rc = m->ucounts.ensure((size_t)unique_blocks(n_cand) * 4, s))))
         return rc;
     if (want_pairs &&
         ((rc = m->pair_in.ensure((size_t)taps * cap * 4, s)) ||
@@ -695,7 +700,7 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     {
         // the largest sort of the build: input keys, strided candidates or mask-sort items
         int64_t big = nn;
-        if (n_cand > big) big = n_cand;
+        if (cand_sort && n_cand > big) big = n_cand;
         if (items > big) big = items;
         const int64_t scan_ints = sort_scan_ints(big);
         if (scan_ints > 0 && (rc = m->scan.ensure((size_t)scan_ints * 4, s))) return rc;

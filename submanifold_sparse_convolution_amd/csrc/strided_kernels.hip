@@ -8,12 +8,20 @@
 // the 27 cells around the query point q = 2 o, numbered like the submanifold
 // taps. Output rows are ordered by (b, x, y, z).
 //
-// Steps: every input emits the (at most 8) output cells it feeds as packed
-// 64-bit keys; one radix sort orders them; a count / scan / write pass keeps
-// the first of each run and writes the output coordinates and query points.
-// The neighbour lookup around the query points then reuses the dense grid, or
-// searches the sorted input keys (k_query_lookup, one search per (dx, dy)
-// column as in the Z-Delta mapper).
+// Output cells, two routes chosen by the size of the output grid:
+//  * at most 2^27 cells (kOutBitmapWords words of one bit per cell, in
+//    (b, x, y, z) order): every input sets the bits of the (at most 8) output
+//    cells it feeds; per-block popcounts of the bitmap words are scanned once;
+//    each block writes its set bits' cells in bit order, so in (b, x, y, z)
+//    order, and clears its words again. The bitmap is zeroed when it is
+//    allocated and is all zero between builds;
+//  * larger grids: every input emits those cells as packed 64-bit keys; one
+//    radix sort orders them; a count / scan / write pass keeps the first of
+//    each run.
+// Both write the output coordinates and the query points. The neighbour
+// lookup around the query points then reuses the dense grid, or searches the
+// sorted input keys (k_query_lookup, one search per dx plane as in the Z-Delta
+// mapper).
 #include "smc_internal.h"
 
 namespace smc {

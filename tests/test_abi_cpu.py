@@ -89,3 +89,38 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(mod, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         mod.lib()
+
+
+def test_host_code_under_asan_and_ubsan(tmp_path):
+    """The library's host code (the C ABI source) built with AddressSanitizer
+    and UndefinedBehaviorSanitizer (host pass only; the kernels are the
+    regular objects) and driven by a C program through every argument-error
+    path of the header: no sanitizer report, every status as documented."""
+    build = os.path.join(ROOT, "_build")
+    objs = sorted(f for f in os.listdir(build) if f.endswith(".o")) if os.path.isdir(build) else []
+    if "smconv_api.o" not in objs:
+        pytest.fail("the library objects are not built (run __graft_entry__.build())")
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    clang = "/opt/rocm/llvm/bin/clang"
+    inc = ["-I", os.path.join(ROOT, "include")]
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=undefined"]
+    api_o = str(tmp_path / "smconv_api.o")
+    lib = str(tmp_path / "libsmconv_asan.so")
+    src = os.path.join(ROOT, "submanifold_sparse_convolution_amd", "csrc", "smconv_api.hip")
+    subprocess.run([hipcc, "-O1", "-g", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
+                    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", *san, *inc,
+                    "-c", src, "-o", api_o], check=True, capture_output=True)
+    others = [os.path.join(build, f) for f in objs if f != "smconv_api.o"]
+    subprocess.run([hipcc, "-shared", "-fPIC", "--offload-arch=gfx950", *san, api_o, *others,
+                    "-o", lib], check=True, capture_output=True)
+    exe = str(tmp_path / "abi_host_check")
+    subprocess.run([clang, "-O1", "-g", "-fsanitize=address,undefined",
+                    "-fno-sanitize-recover=undefined", *inc,
+                    os.path.join(ROOT, "tests", "abi_host_check.c"), lib,
+                    "-Wl,-rpath," + str(tmp_path), "-o", exe], check=True, capture_output=True)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:halt_on_error=1",
+               UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1", HIP_VISIBLE_DEVICES="")
+    r = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=300)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "abi host check ok" in r.stdout

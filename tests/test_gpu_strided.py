@@ -77,8 +77,11 @@ def test_strided_batches_derived_shape_ncols3(route):
               oracle_strided(a, (20, 20, 20)), "ncols=3")
 
 
-@pytest.mark.parametrize("name", ["lidar", "deep"])
+@pytest.mark.parametrize("name", ["lidar", "deep", "wide"])
 def test_strided_map_workloads(name):
+    """lidar and deep have output grids of at most 2^27 cells (their output
+    cells come from a bitmap); wide's (1048 x 1048 x 348) takes the candidate
+    sort over 760k keys (reduce-then-scan passes)."""
     w = synth.workload(name)
     coords = synth.make_coords(w)
     print(f"strided map {name} n={w.n}", flush=True)
