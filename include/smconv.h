@@ -177,9 +177,14 @@ int smc_map_destroy(smc_map* map);
  * route         SMC_ROUTE_*.
  * flags         SMC_BUILD_* bits or 0. Without SMC_BUILD_ASYNC the call waits for the
  *               device-side checks and returns SMC_ERR_DUPLICATE / SMC_ERR_RANGE
- *               when they fail. With it the call returns after enqueueing; the
- *               check result comes from smc_map_sync(). A map whose checks failed
- *               is in-bounds but meaningless and is refused by smc_conv_forward.
+ *               when they fail. With it the call returns after enqueueing, and
+ *               does not wait for an earlier asynchronous build either: the
+ *               checks of every build since the last wait are reported by the
+ *               next smc_map_sync(), synchronous build, smc_map_info or export
+ *               (a build that fails on the host before enqueueing, or an empty
+ *               one, discards the earlier map with its unread checks). A map
+ *               whose checks failed is in-bounds but meaningless and is refused
+ *               by smc_conv_forward once the failure has been read.
  * The dense route keeps its presence grid (4 bytes per padded cell) in the
  * handle between builds and leaves it cleared, so only the first build on
  * a handle pays for filling it.

@@ -39,21 +39,30 @@ __device__ inline int64_t dense_cell(const Geom& g, int b, int x, int y, int z) 
 
 // Puts a build record in its starting state (bounding box empty, everything
 // else zero) and clears its sort histograms; grid-strided over all threads.
-__device__ inline void clear_record(MapState* st, uint32_t* hist, int hist_ints) {
+// The status bits the record holds (an earlier build's device checks, maybe
+// never read by the host) are first ORed into *sticky, which the host reads
+// and clears when it next waits for the handle's builds.
+__device__ inline void clear_record(MapState* st, uint32_t* hist, int hist_ints, uint32_t* sticky) {
     const int64_t t0 = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
     const int64_t nt = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = t0; i < hist_ints; i += nt) hist[i] = 0;
     constexpr int kWords = (int)(sizeof(MapState) / 4);
     constexpr int kBox = (int)(offsetof(MapState, bbox) / 4);
+    static_assert(offsetof(MapState, status) == 0, "status is word 0");
     uint32_t* wv = reinterpret_cast<uint32_t*>(st);
+    if (t0 == 0 && sticky) {
+        const uint32_t old = wv[0];
+        if (old) atomicOr(sticky, old);
+    }
     for (int64_t i = t0; i < kWords; i += nt) {
         const int b = (int)i - kBox;
         wv[i] = (b >= 0 && b < 8) ? (uint32_t)((b < 3 || b == 6) ? INT_MAX : INT_MIN) : 0u;
     }
 }
 
-__global__ __launch_bounds__(kBlock) void k_state_init(MapState* st, uint32_t* hist, int hist_ints) {
-    clear_record(st, hist, hist_ints);
+__global__ __launch_bounds__(kBlock) void k_state_init(MapState* st, uint32_t* hist, int hist_ints,
+                                                       uint32_t* sticky) {
+    clear_record(st, hist, hist_ints, sticky);
 }
 
 __device__ inline int wave_min(int v) {
@@ -124,7 +133,7 @@ __global__ __launch_bounds__(kBlock) void k_dense_scatter(const int32_t* __restr
                                                           int32_t* __restrict__ cells,
                                                           MapState* st, NextRecord next,
                                                           PrevCells prev) {
-    if (next.st) clear_record(next.st, next.hist, next.hist_ints);
+    if (next.st) clear_record(next.st, next.hist, next.hist_ints, next.sticky);
     const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
     if (i < prev.n) {
         const int32_t c = prev.cells[i];
@@ -259,7 +268,7 @@ __global__ __launch_bounds__(kBlock) void k_make_keys(const int32_t* __restrict_
                                                       MapState* st, NextRecord next, int bits,
                                                       int passes, uint32_t* __restrict__ hist) {
     extern __shared__ uint32_t s_h[];             // passes << bits digit counters
-    if (next.st) clear_record(next.st, next.hist, next.hist_ints);
+    if (next.st) clear_record(next.st, next.hist, next.hist_ints, next.sticky);
     const int bins = 1 << bits;
     for (int i = threadIdx.x; i < passes * bins; i += kBlock) s_h[i] = 0;
     __syncthreads();
@@ -433,11 +442,12 @@ inline unsigned blocks_for(int64_t threads) {
 
 }  // namespace
 
-hipError_t launch_state_init(MapState* st, uint32_t* hist, int hist_ints, hipStream_t s) {
+hipError_t launch_state_init(MapState* st, uint32_t* hist, int hist_ints, uint32_t* sticky,
+                             hipStream_t s) {
     unsigned blocks = (unsigned)((hist_ints + kBlock - 1) / kBlock);
     if (blocks < 1) blocks = 1;
     if (blocks > 64) blocks = 64;
-    launch(k_state_init, blocks, kBlock, 0, s, st, hist, hist_ints);
+    launch(k_state_init, blocks, kBlock, 0, s, st, hist, hist_ints, sticky);
     return hipGetLastError();
 }
 

@@ -116,6 +116,7 @@ struct NextRecord {
     MapState* st = nullptr;
     uint32_t* hist = nullptr;
     int hist_ints = 0;
+    uint32_t* sticky = nullptr;   // the record's status bits are ORed in here before it is cleared
 };
 
 // Cells of the previous dense build, to put back to empty in the other grid
@@ -135,7 +136,9 @@ __device__ inline uint32_t cell_bits(const uint32_t* __restrict__ bits, int64_t 
 }
 
 // ---- map kernels (map_kernels.hip) ----
-hipError_t launch_state_init(MapState* st, uint32_t* hist, int hist_ints, hipStream_t s);
+// (sticky: as in NextRecord; nullptr for a record that holds no build yet)
+hipError_t launch_state_init(MapState* st, uint32_t* hist, int hist_ints, uint32_t* sticky,
+                             hipStream_t s);
 hipError_t launch_bbox(const int32_t* coords, int64_t n, int ncols, MapState* st, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 // Dense route: an int32 grid of row ids plus one occupancy bit per cell. A

@@ -132,7 +132,9 @@ int bit_len(int64_t v) {   // bits needed to hold 0..v
 struct smc_map {
     int device = -1;
     int n_cu = 0;
-    hipEvent_t done = nullptr;
+    hipEvent_t done = nullptr;        // end of a synchronous build (system-scope fence)
+    hipEvent_t done_nf = nullptr;     // end of an asynchronous build (no fence, see build_map)
+    hipEvent_t done_last = nullptr;   // the one the last build recorded
     MapState* host_state = nullptr;   // pinned
     bool built = false;
     bool pending = false;             // a build whose device checks are not read yet
@@ -161,6 +163,7 @@ struct smc_map {
     DevBuf vals0, vals1;              // u32
     DevBuf hist;                      // per record: digit histograms, mask sort then key sort
     DevBuf look, ticket;              // look-back table and block ticket (zeroed when allocated)
+    DevBuf sticky;                    // status bits of recycled records not read yet (one word)
     SortWork ws;
     bool state_copied = false;        // host_state already holds the last build's record
     DevBuf nbr, mask, mkey0, mkey1, mval0, mval1;
@@ -237,6 +240,9 @@ int ensure_device(smc_map* m) {
         lookup_scratch(dev);
         SMC_HIP(hipDeviceGetAttribute(&m->n_cu, hipDeviceAttributeMultiprocessorCount, dev));
         if (!m->done) SMC_HIP(hipEventCreateWithFlags(&m->done, hipEventDisableTiming));
+        if (!m->done_nf)
+            SMC_HIP(hipEventCreateWithFlags(&m->done_nf,
+                                            hipEventDisableTiming | hipEventDisableSystemFence));
         if (!m->host_state &&
             hipHostMalloc((void**)&m->host_state, sizeof(MapState), hipHostMallocDefault) !=
                 hipSuccess) {
@@ -247,12 +253,13 @@ int ensure_device(smc_map* m) {
         int rc = m->state.ensure(2 * sizeof(MapState));
         if (rc) return rc;
         if ((rc = m->ticket.ensure(256)) || (rc = m->hist.ensure((size_t)2 * kHistInts * 4)) ||
-            (rc = m->zrow.ensure(kZeroRowBytes)))
+            (rc = m->zrow.ensure(kZeroRowBytes)) || (rc = m->sticky.ensure(256)))
             return rc;
         SMC_HIP(launch_fill_i32(m->ticket.as<int32_t>(), 64, 0, nullptr));
+        SMC_HIP(launch_fill_i32(m->sticky.as<int32_t>(), 64, 0, nullptr));
         for (int k = 0; k < 2; ++k)
             SMC_HIP(launch_state_init(m->state.as<MapState>() + k, m->hist.as<uint32_t>() + k * kHistInts,
-                                      kHistInts, nullptr));
+                                      kHistInts, nullptr, nullptr));
         SMC_HIP(launch_fill_i32(m->zrow.as<int32_t>(), kZeroRowBytes / 4, 0, nullptr));
         SMC_HIP(hipDeviceSynchronize());
         m->ws.ticket = m->ticket.as<uint32_t>();
@@ -264,16 +271,26 @@ int ensure_device(smc_map* m) {
     return SMC_OK;
 }
 
+// Waits for the handle's last build and reads its record. Asynchronous builds
+// do not wait for each other: a build recycles the record of the build before
+// it, carrying that record's status bits into the sticky word first, so the
+// checks of every build since the last wait are reported here.
 int wait_build(smc_map* m) {
     if (!m->pending) return SMC_OK;
-    SMC_HIP(hipEventSynchronize(m->done));
+    SMC_HIP(hipEventSynchronize(m->done_last));
     if (!m->state_copied) {
         SMC_HIP(hipMemcpy(m->host_state, m->state.as<MapState>() + m->slot, sizeof(MapState),
                           hipMemcpyDeviceToHost));
         m->state_copied = true;
     }
     m->pending = false;
-    uint32_t st = m->host_state->status;
+    uint32_t sticky = 0;
+    SMC_HIP(hipMemcpy(&sticky, m->sticky.p, sizeof(sticky), hipMemcpyDeviceToHost));
+    if (sticky) {                                 // every build is done: nothing else writes it
+        const uint32_t zero = 0;
+        SMC_HIP(hipMemcpy(m->sticky.p, &zero, sizeof(zero), hipMemcpyHostToDevice));
+    }
+    uint32_t st = m->host_state->status | sticky;
     if (st & kStSortStall) {
         m->build_status = SMC_ERR_HIP;
         return fail(SMC_ERR_HIP, "a look-back wait of the map build ran out (results invalid)");
@@ -433,7 +450,7 @@ int smc_map_create(smc_map** out) {
 int smc_map_destroy(smc_map* m) {
     if (!m) return SMC_OK;
     // (a handle whose first build failed part-way holds some buffers with no device set)
-    const bool touched = m->device >= 0 || m->done || m->host_state || m->state.p;
+    const bool touched = m->device >= 0 || m->done || m->done_nf || m->host_state || m->state.p;
     if (touched) {
         int cur = 0;
         (void)hipGetDevice(&cur);
@@ -446,7 +463,7 @@ int smc_map_destroy(smc_map* m) {
                           &m->pair_in, &m->pair_out, &m->pair_slot, &m->rowbase, &m->part,
                           &m->zrow, &m->ck0, &m->ck1, &m->ck2, &m->cv0, &m->cv1, &m->chist,
                           &m->ucounts, &m->ocoords, &m->qcoords, &m->scan, &m->split,
-                          &m->obits};
+                          &m->obits, &m->sticky};
         for (DevBuf* b : bufs) b->release();
         for (auto& tk : m->seq) {
             if (tk.start) m->ev_pool.push_back(tk.start);
@@ -455,6 +472,7 @@ int smc_map_destroy(smc_map* m) {
         for (hipEvent_t e : m->ev_pool) (void)hipEventDestroy(e);
         if (m->host_state) (void)hipHostFree(m->host_state);
         if (m->done) (void)hipEventDestroy(m->done);
+        if (m->done_nf) (void)hipEventDestroy(m->done_nf);
         (void)hipSetDevice(cur);
     }
     delete m;
@@ -536,8 +554,12 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     int rc = ensure_device(m);
     if (rc) return rc;
     hipStream_t s = (hipStream_t)stream;
-    // a previous async build must not be overwritten while still unread
-    if (m->pending) SMC_HIP(hipEventSynchronize(m->done));
+    // an earlier build not waited for yet: its checks reach the sticky word when
+    // this build's first kernel recycles its record (stream order), and the next
+    // wait reports them (a build that fails before any kernel, or an empty one,
+    // drops them with the earlier map). A record already read is recycled
+    // without carrying anything.
+    const bool carry = m->pending;
     m->pending = false;
     m->built = false;
     m->perm = nullptr;
@@ -551,8 +573,9 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     next.st = m->state.as<MapState>() + (slot ^ 1);
     next.hist = m->hist.as<uint32_t>() + (slot ^ 1) * kHistInts;
     next.hist_ints = kHistInts;
+    next.sticky = carry ? m->sticky.as<uint32_t>() : nullptr;
     StageTimer t_map(m, SMC_STAGE_MAP, s, /*bracket=*/true);
-    if (!m->slot_clean[slot]) SMC_HIP(launch_state_init(st, hist_mask, kHistInts, s));
+    if (!m->slot_clean[slot]) SMC_HIP(launch_state_init(st, hist_mask, kHistInts, nullptr, s));
     if (n > 0) m->slot_clean[slot] = false;
 
     // ---- geometry: explicit shape, or the bounding box (one read) ----
@@ -845,7 +868,13 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     if (!async)
         SMC_HIP(hipMemcpyAsync(m->host_state, st, sizeof(MapState), hipMemcpyDeviceToHost, s));
     m->state_copied = !async;
-    SMC_HIP(hipEventRecord(m->done, s));
+    // A synchronous build has copied its record into pinned host memory before
+    // this event, so the event's system-scope fence makes that copy visible. An
+    // asynchronous build's record is read later by hipMemcpy, after the event:
+    // its fence (a write-back of the caches, about 4 us on MI355X between the
+    // build and the first GEMM) buys nothing there, and the event goes without.
+    m->done_last = async ? m->done_nf : m->done;
+    SMC_HIP(hipEventRecord(m->done_last, s));
     m->pending = true;
     m->built = true;
     m->build_status = SMC_OK;

@@ -110,3 +110,23 @@ def test_forced_lookback_timeout_reports_hip_error():
     want.pop("perm")
     assert_map_equal(got, want, "after the forced timeout")
     m.close()
+
+
+@pytest.mark.parametrize("route", ["dense", "sorted"])
+def test_async_builds_do_not_lose_checks(route):
+    """Asynchronous builds do not wait for each other: a failed check of an
+    earlier one (duplicates) reaches the next wait through the sticky status
+    word when the later build recycles its record; the wait after that is
+    clean again."""
+    bad = synth.tiny_coords(seed=1, n=400, side=10)
+    bad[10] = bad[20]
+    good = synth.tiny_coords(seed=2, n=400, side=10)
+    m = smc.KernelMap()
+    m.build(to_dev_i32(bad), route=route, sync=False)
+    m.build(to_dev_i32(good), route=route, sync=False)
+    m.build(to_dev_i32(good), route=route, sync=False)
+    assert status_of(m.sync) == 2
+    m.build(to_dev_i32(good), route=route, sync=False)
+    m.sync()
+    assert m.info()["status"] == 0
+    m.close()
