@@ -86,6 +86,8 @@ KERNEL_SOURCES = {
     "k_sorted_lookup": ("map_kernels.hip",),
     "k_gemm_nc": ("gemm_kernels.hip", "gemm_common.h"),
     "k_gemm_centre": ("gemm_kernels.hip", "gemm_common.h"),
+    "k_gemm_nc_big": ("gemm_kernels.hip", "gemm_common.h"),
+    "k_gemm_centre_big": ("gemm_kernels.hip", "gemm_common.h"),
     "k_conv_masktile": ("masktile_kernels.hip", "gemm_common.h"),
     "k_os_pass": ("radix_sort.hip",),
 }
@@ -107,9 +109,9 @@ def kernel_model(kernel, n, p, c_in, c_out, taps=27, table=False, n_out=None, gr
     m = n if n_out is None else n_out
     p_nc = p - n
     t4 = 4 * taps * m if table else 0
-    if kernel == "k_gemm_centre":
+    if kernel in ("k_gemm_centre", "k_gemm_centre_big"):
         return 2 * n * c_in + 2 * c_in * c_out + 2 * n * c_out, 2.0 * n * c_in * c_out
-    if kernel == "k_gemm_nc":
+    if kernel in ("k_gemm_nc", "k_gemm_nc_big"):
         return 2 * (taps - 1) * c_in * c_out + 8 * p_nc, 2.0 * p_nc * c_in * c_out
     if kernel == "k_conv_masktile":
         extra = 8 * m * c_out * (groups - 1)
@@ -196,12 +198,18 @@ def tile_work_ratio(mask, perm, group_rows, group_masks):
     return executed / useful if useful else 1.0
 
 
-def stage_kernels(stage, algo, route, kernel_size=3, strided=False):
+BIG_MIN_C, BIG_MAX_C = 129, 576     # C_in of the weight-resident wide GEMM kernels
+
+
+def stage_kernels(stage, algo, route, kernel_size=3, strided=False, c_in=128):
     """The kernels one execution of a stage launches (pair path unless stated)."""
+    big = BIG_MIN_C <= c_in <= BIG_MAX_C and c_in % 8 == 0
     if stage == "gemm":
-        return ("k_conv_masktile",) if algo == "mask_tiles" or strided else ("k_gemm_nc",)
+        if algo == "mask_tiles" or strided:
+            return ("k_conv_masktile",)
+        return ("k_gemm_nc_big",) if big else ("k_gemm_nc",)
     if stage == "centre":
-        return ("k_gemm_centre",)
+        return ("k_gemm_centre_big",) if big else ("k_gemm_centre",)
     if stage == "mask_sort":
         return ("k_mask_hist", "k_os_pass")
     fused = route == "dense" and algo == "pairs" and kernel_size == 3 and not strided
@@ -396,7 +404,7 @@ def stage_rows(r):
         us = r["stage_us"].get(st, 0.0)
         if us <= 0.0:
             continue
-        ks = stage_kernels(st, r["algo"], route, r["kernel_size"], r["strided"])
+        ks = stage_kernels(st, r["algo"], route, r["kernel_size"], r["strided"], c)
         row = dict(kernels=list(ks), us=us, per_step=r["stage_per_step"].get(st, 0.0))
         if len(ks) == 1:
             groups = info["n_groups"] if r["algo"] == "mask_tiles" else 1
@@ -628,6 +636,7 @@ def summarize_mfma(pmc_dir, workload, algo, bench_out):
     n, p, c = cfg["n"], cfg["pairs"], cfg["c_in"]
     useful = {"k_gemm_nc": 2.0 * (p - n) * c * c, "k_gemm_centre": 2.0 * n * c * c,
               "k_conv_masktile": 2.0 * p * c * c}
+    useful["k_gemm_nc_big"], useful["k_gemm_centre_big"] = useful["k_gemm_nc"], useful["k_gemm_centre"]
     files = glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True)
     if not files:
         raise SystemExit(f"no counter_collection.csv under {pmc_dir}")
@@ -663,6 +672,38 @@ def summarize_mfma(pmc_dir, workload, algo, bench_out):
         print(f"{k}: executed {v['mfma_flops_executed']:.4g} flop, useful {v['flops_useful']:.4g} "
               f"({v['useful_over_executed']:.3f}); MFMA busy {v['mfma_busy_frac']:.4f} of the "
               f"SIMD cycles over {v['profiled_ns'] / 1e3:.2f} us (profiled)")
+
+
+def summarize_trace(trace_dir, title, command, out_md):
+    """A rocprofv3 --kernel-trace run (run_kernel_trace.csv under trace_dir)
+    as a markdown table: per kernel and grid size, dispatches and durations
+    (us). The grid tells the voxel sets apart in a run that times several."""
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_trace.csv under {trace_dir}")
+    groups = {}
+    for fn in files:
+        with open(fn) as f:
+            for row in csv.DictReader(f):
+                k = _short(row["Kernel_Name"])
+                grid = row.get("Grid_Size_X") or row.get("Grid_Size") or ""
+                if row.get("Grid_Size_Y") not in (None, "", "1"):
+                    grid = f"{grid}x{row['Grid_Size_Y']}"
+                ns = float(row["End_Timestamp"]) - float(row["Start_Timestamp"])
+                groups.setdefault((k, grid), []).append(ns / 1e3)
+    total = sum(sum(v) for v in groups.values())
+    lines = [f"# Kernel trace: {title}", "",
+             "Command (from the repository root; rocprofv3 writes its CSV files under the "
+             "given directory):", "", "```", command, "```", "",
+             "Per kernel and grid size (work-items in x, x blocks in y), durations in microseconds:",
+             "", "| kernel | grid | calls | avg | min | max | share |",
+             "|---|---|---|---|---|---|---|"]
+    for (k, grid), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{k}` | {grid} | {len(v)} | {statistics.mean(v):.2f} | {min(v):.2f} | "
+                     f"{max(v):.2f} | {100 * sum(v) / total:.1f} % |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {out_md}")
 
 
 def summarize_pmc(fetch_dir, write_dir, workload, algo, copy_mb):
@@ -740,11 +781,16 @@ def main():
     ap.add_argument("--summarize-mfma", nargs=2, metavar=("PMC_DIR", "BENCH_OUT"),
                     help="summarise a rocprofv3 --pmc run of the MFMA counters and the "
                          "JSON line that run printed")
+    ap.add_argument("--summarize-trace", nargs=4, metavar=("TRACE_DIR", "TITLE", "COMMAND", "OUT_MD"),
+                    help="summarise a rocprofv3 --kernel-trace run into a markdown table")
     ap.add_argument("--report", default="",
                     help="also run the mask-tile orders, 5x5x5 kernels and batched frames of "
                          "every set and write their figures to this JSON file")
     args = ap.parse_args()
 
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
+        return
     if args.summarize_mfma:
         summarize_mfma(args.summarize_mfma[0], args.workload, args.algo, args.summarize_mfma[1])
         return
