@@ -25,9 +25,10 @@ region's wall clock per step.
 Prints ONE JSON line. --gpus above 1 exits: this build measures one GPU.
 
 Kernel durations come from a second pass with the library's stage timers:
-every kernel launched in a stage carries its own HIP start/stop events
-(stamped by the kernel's dispatch on the library's stream), so a
-single-kernel stage's average is that kernel's average duration.
+every kernel records one stop event (without the system fence) on the
+library's stream and is charged the interval from the previous kernel's stop
+to its own, so the kernels' times add up to the step and a single-kernel
+stage's average is that kernel's average interval.
 
 Algorithmic bytes of a launch are the compulsory ones only: every input
 that comes from outside the layer and every output it leaves, each once.
@@ -35,6 +36,8 @@ Intermediates of the method (the grid, keys, sort passes, the slab, row
 bases) count zero.
   k_gemm_centre     2 N C_in (x) + 2 C_in C_out (centre weights) + 2 N C_out (y)
   k_gemm_nc         2 (T-1) C_in C_out (off-centre weights) + 8 (P - N) (pair lists)
+  k_gemm_rows       2 N C_in + 2 T C_in C_out + 8 (P - N) + 2 N C_out (the two above in one)
+  (the *_big kernels of wide inputs: as k_gemm_nc / k_gemm_centre)
   k_dense_scatter / k_make_keys   16 N (coordinates)
   k_lookup_compact  16 N (coordinates) + 4 N (masks) + 8 P (pair lists) [+ 4 T N table]
   k_compact         4 N (masks) + 8 P (pair lists)
@@ -88,6 +91,7 @@ KERNEL_SOURCES = {
     "k_gemm_centre": ("gemm_kernels.hip", "gemm_common.h"),
     "k_gemm_nc_big": ("gemm_kernels.hip", "gemm_common.h"),
     "k_gemm_centre_big": ("gemm_kernels.hip", "gemm_common.h"),
+    "k_gemm_rows": ("rows_kernels.hip", "gemm_common.h"),
     "k_conv_masktile": ("masktile_kernels.hip", "gemm_common.h"),
     "k_os_pass": ("radix_sort.hip",),
 }
@@ -113,6 +117,9 @@ def kernel_model(kernel, n, p, c_in, c_out, taps=27, table=False, n_out=None, gr
         return 2 * n * c_in + 2 * c_in * c_out + 2 * n * c_out, 2.0 * n * c_in * c_out
     if kernel in ("k_gemm_nc", "k_gemm_nc_big"):
         return 2 * (taps - 1) * c_in * c_out + 8 * p_nc, 2.0 * p_nc * c_in * c_out
+    if kernel == "k_gemm_rows":
+        return (2 * n * c_in + 2 * taps * c_in * c_out + 8 * p_nc + 2 * n * c_out,
+                2.0 * p * c_in * c_out)
     if kernel == "k_conv_masktile":
         extra = 8 * m * c_out * (groups - 1)
         return (2 * n * c_in + 2 * taps * c_in * c_out + 2 * m * c_out + extra,
@@ -201,18 +208,26 @@ def tile_work_ratio(mask, perm, group_rows, group_masks):
 BIG_MIN_C, BIG_MAX_C = 129, 576     # C_in of the weight-resident wide GEMM kernels
 
 
+def rows_form(algo, kernel_size, c_in, c_out=None, strided=False):
+    """True where the pair-list forward runs as the one-kernel row-range GEMM."""
+    return (algo == "pairs" and kernel_size == 3 and c_in <= 64 and c_out <= 64 and c_in % 8 == 0
+            and not strided)
+
+
 def stage_kernels(stage, algo, route, kernel_size=3, strided=False, c_in=128):
     """The kernels one execution of a stage launches (pair path unless stated)."""
     big = BIG_MIN_C <= c_in <= BIG_MAX_C and c_in % 8 == 0
     if stage == "gemm":
         if algo == "mask_tiles" or strided:
             return ("k_conv_masktile",)
+        if rows_form(algo, kernel_size, c_in, c_in):
+            return ("k_gemm_rows",)
         return ("k_gemm_nc_big",) if big else ("k_gemm_nc",)
     if stage == "centre":
         return ("k_gemm_centre_big",) if big else ("k_gemm_centre",)
     if stage == "mask_sort":
         return ("k_mask_hist", "k_os_pass")
-    fused = route == "dense" and algo == "pairs" and kernel_size == 3 and not strided
+    fused = route == "dense" and algo != "mask_tiles" and kernel_size == 3 and not strided
     if stage == "neighbours":
         if strided:
             return ("k_stride_outputs", "k_dense_lookup" if route == "dense" else "k_query_lookup")
@@ -245,7 +260,7 @@ def run_workload(name, steps, warmup, sync_build=False, algo="pairs", copy_probe
     w_ds = [dev_bf16(synth.weights(c, c, w.seed, layer, taps)) for layer in range(w.layers)]
     cal = None
     cold_us = None
-    build_kw = dict(spatial_shape=w.grid, batch_size=frames, pairs=(algo == "pairs"),
+    build_kw = dict(spatial_shape=w.grid, batch_size=frames, pairs=(algo != "mask_tiles"),
                     sort=(algo == "mask_tiles"), kernel_size=kernel_size)
     if cold and not strided:
         # the first build on a fresh handle: its buffers are allocated, the
@@ -637,6 +652,7 @@ def summarize_mfma(pmc_dir, workload, algo, bench_out):
     useful = {"k_gemm_nc": 2.0 * (p - n) * c * c, "k_gemm_centre": 2.0 * n * c * c,
               "k_conv_masktile": 2.0 * p * c * c}
     useful["k_gemm_nc_big"], useful["k_gemm_centre_big"] = useful["k_gemm_nc"], useful["k_gemm_centre"]
+    useful["k_gemm_rows"] = 2.0 * p * c * c
     files = glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True)
     if not files:
         raise SystemExit(f"no counter_collection.csv under {pmc_dir}")
@@ -759,7 +775,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=HEADLINE, choices=list(CONFIG_NAMES))
-    ap.add_argument("--algo", default="pairs", choices=["pairs", "mask_tiles"],
+    ap.add_argument("--algo", default="pairs", choices=["pairs", "pairs_slab", "mask_tiles"],
                     help="forward algorithm of the headline line")
     ap.add_argument("--order", default="plain", choices=list(ORDERS),
                     help="mask-tile row order: plain mask value, calibrated bit order, or "

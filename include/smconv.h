@@ -90,7 +90,9 @@ enum {
 enum {
     SMC_FWD_RELU = 1,       /* apply max(y, 0) to the (rounded) output */
     SMC_FWD_OUT_F32 = 2,    /* write the float32 accumulator itself: y is float [n, c_out] */
-    SMC_FWD_MASK_TILES = 4  /* output-stationary mask-tile algorithm (see smc_conv_forward) */
+    SMC_FWD_MASK_TILES = 4, /* output-stationary mask-tile algorithm (see smc_conv_forward) */
+    SMC_FWD_SLAB_IN_MEMORY = 8 /* pair lists: always the two-kernel form with the slab in device
+                                  memory, also where the row-range kernel would run */
 };
 
 typedef struct smc_map_info_s {
@@ -289,7 +291,9 @@ int smc_map_set_order(smc_map* map, const int32_t* bit_order, const int32_t* gro
 int smc_map_calibrate(smc_map* map, int n_groups, int32_t* bit_order, int32_t* group_of);
 
 /* Bytes of the packed weight buffer for a K x K x K kernel (K = 3 or 5) and
- * c_in x c_out (both >= 1); 0 for an invalid request. */
+ * c_in x c_out (both >= 1); 0 for an invalid request. Where the one-kernel
+ * pair-list forward runs (K = 3, c_in and c_out <= 64, c_in a multiple of 8) the buffer
+ * also holds that kernel's column tiles, packed after the others. */
 size_t smc_weight_packed_bytes(int kernel_size, int c_in, int c_out);
 
 /*
@@ -310,11 +314,15 @@ int smc_weight_pack(const uint16_t* w, int kernel_size, int c_in, int c_out, voi
  *  - default, per-tap pair lists ("[Kernel] Add submanifold sparse 3D
  *    convolution", section "Design, and the measurements behind it" and
  *    commit d4161ef: gather -> mfma_f32_16x16x32_bf16 with float32
- *    accumulate -> scatter): the non-centre taps store each pair's
- *    float32 product row into a partial-product slab (one row per pair, a
- *    row's pairs consecutive), then the centre tap (every row with itself)
- *    runs as a dense GEMM whose epilogue adds the row's slab rows and writes
- *    the output. Needs a map built without SMC_BUILD_NO_PAIRS;
+ *    accumulate -> scatter): each non-centre pair's float32 product row goes
+ *    to a partial-product slab (one row per pair, a row's pairs
+ *    consecutive), the centre tap (every row with itself) runs as a dense
+ *    GEMM, and each output row is its centre product plus its slab rows in
+ *    order. On a 3 x 3 x 3 map with c_in, c_out <= 64 (c_in a multiple of 8), one
+ *    kernel does all of it over 256-row chunks with the chunk's slab rows in
+ *    LDS; otherwise (or with SMC_FWD_SLAB_IN_MEMORY) two kernels pass the
+ *    slab through device memory. Both forms give the same bits. Needs a map
+ *    built without SMC_BUILD_NO_PAIRS;
  *  - SMC_FWD_MASK_TILES ("Sparse convolution in FP32", "Neighbour masks and
  *    sorted rows"): tiles of mask-sorted rows run the union of their masks'
  *    taps and keep every tap's sum in registers; with one offset group, one
@@ -329,9 +337,10 @@ int smc_weight_pack(const uint16_t* w, int kernel_size, int c_in, int c_out, voi
  * wpacked device pointer from smc_weight_pack(map kernel size, c_in, c_out).
  * y       device pointer, 16-byte aligned, bf16 [n, c_out] (float [n, c_out] with
  *         SMC_FWD_OUT_F32); every row is written.
- * flags   SMC_FWD_RELU | SMC_FWD_OUT_F32, or 0. Without SMC_FWD_OUT_F32 the output
- *         is the float32 accumulator rounded to bf16 (to nearest, ties to even).
- * The pair-list algorithm's slab lives in the handle (grow-only, 4 c_out bytes
+ * flags   SMC_FWD_RELU | SMC_FWD_OUT_F32 | SMC_FWD_SLAB_IN_MEMORY, or 0. Without
+ *         SMC_FWD_OUT_F32 the output is the float32 accumulator rounded to bf16
+ *         (to nearest, ties to even).
+ * The two-kernel form's slab lives in the handle (grow-only, 4 c_out bytes
  * per off-centre pair). The host reads no pair count: the GEMM reads them on
  * the device, and the slab is sized for 26 pairs per row when the build's
  * counts have not been read (asynchronous builds) and that bound is under

@@ -28,10 +28,11 @@ SMC_BUILD_ASYNC = 1
 SMC_FWD_RELU = 1
 SMC_FWD_OUT_F32 = 2
 SMC_FWD_MASK_TILES = 4
+SMC_FWD_SLAB_IN_MEMORY = 8
 SMC_BUILD_NO_PAIRS = 2
 SMC_BUILD_NO_SORT = 4
 SMC_BUILD_TABLE = 8
-ALGOS = ("pairs", "mask_tiles")
+ALGOS = ("pairs", "pairs_slab", "mask_tiles")
 
 EXPORTED_SYMBOLS = [
     "smc_map_create", "smc_map_destroy", "smc_map_build", "smc_map_sync", "smc_map_info",
@@ -375,9 +376,11 @@ class KernelMap:
                 algo: str = "pairs", stream=None):
         """x: bf16 [N, C_in] CUDA tensor -> bf16 [N, C_out] (float32 with out_f32).
 
-        algo: "pairs" (per-tap pair lists, partial-product slab summed by the
-        centre-tap GEMM) or "mask_tiles" (output-stationary tiles of
-        mask-sorted rows)."""
+        algo: "pairs" (per-tap pair lists: each row is its centre product plus
+        its partial-product slab rows; one kernel with the slab in LDS for
+        3x3x3 maps and C_in, C_out <= 64 (C_in a multiple of 8), else two kernels with the
+        slab in device memory), "pairs_slab" (always the two-kernel form) or
+        "mask_tiles" (output-stationary tiles of mask-sorted rows)."""
         if algo not in ALGOS:
             raise ValueError(f"algo must be one of {ALGOS}")
         import torch
@@ -400,7 +403,8 @@ class KernelMap:
                                       ctypes.c_void_p(out.data_ptr()),
                                       (SMC_FWD_RELU if relu else 0)
                                       | (SMC_FWD_OUT_F32 if out_f32 else 0)
-                                      | (SMC_FWD_MASK_TILES if algo == "mask_tiles" else 0),
+                                      | (SMC_FWD_MASK_TILES if algo == "mask_tiles" else 0)
+                                      | (SMC_FWD_SLAB_IN_MEMORY if algo == "pairs_slab" else 0),
                                       _stream(stream)))
         return out
 

@@ -295,7 +295,8 @@ struct CompactLds {
 // L.nb filled): per-tap counts, look-back over earlier chunks, the chunk's
 // pairs listed in LDS as (row, tap) entries in output order, then written out
 // with consecutive threads on consecutive pair positions. The last chunk
-// publishes the totals. With nbr_out, the chunk's neighbour rows are stored
+// publishes the totals. chunk_pre[bid][k] receives the pairs of tap k (k <
+// kTaps) and the slab rows (k = kTaps) in earlier chunks. With nbr_out, the chunk's neighbour rows are stored
 // there (coalesced) between publishing the counts and the look-back, where
 // the block would otherwise wait. Starts and ends with all threads in step.
 __device__ __forceinline__ void compact_chunk(CompactLds& L, uint32_t m, uint32_t bid, int64_t n,
@@ -304,6 +305,7 @@ __device__ __forceinline__ void compact_chunk(CompactLds& L, uint32_t m, uint32_
                                               int32_t* __restrict__ pair_out,
                                               int32_t* __restrict__ pair_slot,
                                               int32_t* __restrict__ rowbase,
+                                              int32_t* __restrict__ chunk_pre,
                                               uint64_t* __restrict__ look, uint32_t epoch,
                                               uint32_t* status, int32_t* __restrict__ nbr_out,
                                               uint32_t spin_limit = kSpinLimit,
@@ -364,6 +366,10 @@ __device__ __forceinline__ void compact_chunk(CompactLds& L, uint32_t m, uint32_
         const int k = tid;
         const uint32_t run = L.tot[k];
         const uint32_t prefix = L.pre[k];
+        // per-chunk starts of every tap's pairs and of the slab rows (the last
+        // chunk also writes the totals as row gridDim.x), for row-range GEMMs
+        chunk_pre[(int64_t)bid * kCols + k] = (int32_t)prefix;
+        if (bid == gridDim.x - 1) chunk_pre[(int64_t)(bid + 1) * kCols + k] = (int32_t)(prefix + run);
         if (bid > 0)
             __hip_atomic_store(&look[(int64_t)bid * kCols + k], lb_pack(epoch, kIncl, prefix + run),
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -440,8 +446,8 @@ __device__ __forceinline__ void compact_chunk(CompactLds& L, uint32_t m, uint32_
 __global__ __launch_bounds__(kCThreads) void k_compact(
     const uint32_t* __restrict__ mask, const int32_t* __restrict__ nbr, int64_t n, int64_t cap,
     int tile_m, MapState* st, int32_t* __restrict__ pair_in, int32_t* __restrict__ pair_out,
-    int32_t* __restrict__ pair_slot, int32_t* __restrict__ rowbase, uint64_t* __restrict__ look,
-    uint32_t* ticket, bool by_index, uint32_t epoch, uint32_t* status) {
+    int32_t* __restrict__ pair_slot, int32_t* __restrict__ rowbase, int32_t* __restrict__ chunk_pre,
+    uint64_t* __restrict__ look, uint32_t* ticket, bool by_index, uint32_t epoch, uint32_t* status) {
     __shared__ CompactLds L;
     const int tid = threadIdx.x;
     const uint32_t bid = chunk_of_block(by_index, ticket, &L.bid);
@@ -467,7 +473,7 @@ __global__ __launch_bounds__(kCThreads) void k_compact(
         if (q < kCNbrVec) nb4[q] = nv4[j];
     }
     compact_chunk(L, row < n ? mv : 0u, bid, n, cap, tile_m, st, pair_in, pair_out, pair_slot,
-                  rowbase, look, epoch, status, nullptr);
+                  rowbase, chunk_pre, look, epoch, status, nullptr);
     if (!by_index && bid == gridDim.x - 1 && tid == 0) atomicExch(ticket, 0u);
 }
 
@@ -481,8 +487,8 @@ __global__ __launch_bounds__(kCThreads) void k_lookup_compact(
     const uint32_t* __restrict__ bits, int32_t* __restrict__ nbr, uint32_t* __restrict__ mask,
     int64_t cap, int tile_m, MapState* st, int32_t* __restrict__ pair_in,
     int32_t* __restrict__ pair_out, int32_t* __restrict__ pair_slot, int32_t* __restrict__ rowbase,
-    uint64_t* __restrict__ look, uint32_t* ticket, bool by_index, uint32_t epoch,
-    uint32_t* status, uint32_t spin_limit, uint32_t wait_xor) {
+    int32_t* __restrict__ chunk_pre, uint64_t* __restrict__ look, uint32_t* ticket, bool by_index,
+    uint32_t epoch, uint32_t* status, uint32_t spin_limit, uint32_t wait_xor) {
     __shared__ CompactLds L;
     const int tid = threadIdx.x;
     const uint32_t bid = chunk_of_block(by_index, ticket, &L.bid);
@@ -536,8 +542,8 @@ __global__ __launch_bounds__(kCThreads) void k_lookup_compact(
     }
     if (row < n) mask[row] = m;
     __syncthreads();
-    compact_chunk(L, m, bid, n, cap, tile_m, st, pair_in, pair_out, pair_slot, rowbase, look,
-                  epoch, status, nbr, spin_limit, wait_xor);
+    compact_chunk(L, m, bid, n, cap, tile_m, st, pair_in, pair_out, pair_slot, rowbase, chunk_pre,
+                  look, epoch, status, nbr, spin_limit, wait_xor);
     if (!by_index && bid == gridDim.x - 1 && tid == 0) atomicExch(ticket, 0u);
 }
 
@@ -768,8 +774,8 @@ static uint32_t next_epoch(SortWork& ws) {
 
 hipError_t launch_compact(const uint32_t* mask, const int32_t* nbr, int64_t n, int ksize,
                           int64_t cap, int tile_m, MapState* st, int32_t* pair_in,
-                          int32_t* pair_out, int32_t* pair_slot, int32_t* rowbase, SortWork& ws,
-                          uint32_t* status, hipStream_t s) {
+                          int32_t* pair_out, int32_t* pair_slot, int32_t* rowbase,
+                          int32_t* chunk_pre, SortWork& ws, uint32_t* status, hipStream_t s) {
     const uint32_t epoch = next_epoch(ws);
     const unsigned blocks = (unsigned)compact_chunks(n);
     if (ksize == 5) {
@@ -779,7 +785,7 @@ hipError_t launch_compact(const uint32_t* mask, const int32_t* nbr, int64_t n, i
     } else {
         const bool by_index = fits_at_once((const void*)k_compact, 1, blocks);
         launch(k_compact, blocks, kCThreads, 0, s, mask, nbr, n, cap, tile_m, st, pair_in,
-               pair_out, pair_slot, rowbase, ws.look, ws.ticket, by_index, epoch, status);
+               pair_out, pair_slot, rowbase, chunk_pre, ws.look, ws.ticket, by_index, epoch, status);
     }
     return hipGetLastError();
 }
@@ -788,14 +794,15 @@ hipError_t launch_lookup_compact(const int32_t* coords, int64_t n, const Geom& g
                                  const int32_t* grid, const uint32_t* bits, int32_t* nbr,
                                  uint32_t* mask, int64_t cap,
                                  int tile_m, MapState* st, int32_t* pair_in, int32_t* pair_out,
-                                 int32_t* pair_slot, int32_t* rowbase, SortWork& ws,
-                                 uint32_t* status, hipStream_t s) {
+                                 int32_t* pair_slot, int32_t* rowbase, int32_t* chunk_pre,
+                                 SortWork& ws, uint32_t* status, hipStream_t s) {
     const uint32_t epoch = next_epoch(ws);
     const unsigned blocks = (unsigned)compact_chunks(n);
     const bool by_index = fits_at_once((const void*)k_lookup_compact, 2, blocks);
     launch(k_lookup_compact, blocks, kCThreads, 0, s, coords, n, g, grid, bits, nbr, mask, cap,
-           tile_m, st, pair_in, pair_out, pair_slot, rowbase, ws.look, ws.ticket, by_index, epoch,
-           status, ws.force_timeout ? 64u : kSpinLimit, ws.force_timeout ? 0x15555555u : 0u);
+           tile_m, st, pair_in, pair_out, pair_slot, rowbase, chunk_pre, ws.look, ws.ticket,
+           by_index, epoch, status, ws.force_timeout ? 64u : kSpinLimit,
+           ws.force_timeout ? 0x15555555u : 0u);
     return hipGetLastError();
 }
 

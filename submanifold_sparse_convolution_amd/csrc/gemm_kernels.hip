@@ -843,9 +843,11 @@ size_t packed_weight_bytes(int taps, int c_in, int c_out) {
     int64_t steps = (c_in + 31) / 32;
     int nbw = nbw_for(c_out);
     int64_t n_wt = (c_out + 16 * nbw - 1) / (16 * nbw);
-    return (size_t)(taps * n_wt * steps * nbw * 64 * 16);
+    return (size_t)(taps * n_wt * steps * nbw * 64 * 16) + rows_weight_bytes(taps, c_in, c_out);
 }
 
+// The packing above, plus (where the row-range GEMM runs and needs other
+// column tiles) a second one after it with that kernel's tile width.
 hipError_t launch_weight_pack(const uint16_t* w, int taps, int c_in, int c_out, void* out,
                               hipStream_t s) {
     int steps = (c_in + 31) / 32;
@@ -855,6 +857,14 @@ hipError_t launch_weight_pack(const uint16_t* w, int taps, int c_in, int c_out, 
     unsigned blocks = (unsigned)((total + kBlock - 1) / kBlock);
     launch(k_weight_pack, blocks, kBlock, 0, s, w, taps, c_in, c_out, nbw, n_wt, steps,
            (uint4*)out);
+    if (rows_weight_bytes(taps, c_in, c_out) > 0) {
+        const int nb2 = rows_pack_nbw(c_out);
+        const int n_q = (c_out + 16 * nb2 - 1) / (16 * nb2);
+        const int64_t total2 = (int64_t)taps * n_q * steps * nb2 * 64;
+        launch(k_weight_pack, (unsigned)((total2 + kBlock - 1) / kBlock), kBlock, 0, s, w, taps,
+               c_in, c_out, nb2, n_q, steps,
+               (uint4*)((char*)out + rows_weight_offset(taps, c_in, c_out)));
+    }
     return hipGetLastError();
 }
 

@@ -253,19 +253,22 @@ size_t compact_look_bytes_k(int64_t n, int ksize);
 // Pairs of tap k go to [k cap, k cap + tap_count[k]) in ascending output row;
 // pair_slot numbers the off-centre pairs row by row (rowbase[i] = first slab
 // row of output row i; rowbase[n] = all off-centre pairs). ksize 3 or 5
-// (mask words and tap count follow it).
+// (mask words and tap count follow it). For ksize 3, chunk_pre ([chunks + 1]
+// x (kTaps + 1)) receives each 256-row chunk's starts: row c, column k < kTaps
+// = pairs of tap k in chunks before c, column kTaps = slab rows before c (row
+// c = chunks: the totals). ksize 5 leaves it alone.
 hipError_t launch_compact(const uint32_t* mask, const int32_t* nbr, int64_t n, int ksize,
                           int64_t cap, int tile_m, MapState* st, int32_t* pair_in,
-                          int32_t* pair_out, int32_t* pair_slot, int32_t* rowbase, SortWork& ws,
-                          uint32_t* status, hipStream_t s);
+                          int32_t* pair_out, int32_t* pair_slot, int32_t* rowbase,
+                          int32_t* chunk_pre, SortWork& ws, uint32_t* status, hipStream_t s);
 // Dense route: neighbour lookup and compaction in one kernel (also writes nbr
 // and mask).
 hipError_t launch_lookup_compact(const int32_t* coords, int64_t n, const Geom& g,
                                  const int32_t* grid, const uint32_t* bits, int32_t* nbr,
                                  uint32_t* mask, int64_t cap,
                                  int tile_m, MapState* st, int32_t* pair_in, int32_t* pair_out,
-                                 int32_t* pair_slot, int32_t* rowbase, SortWork& ws,
-                                 uint32_t* status, hipStream_t s);
+                                 int32_t* pair_slot, int32_t* rowbase, int32_t* chunk_pre,
+                                 SortWork& ws, uint32_t* status, hipStream_t s);
 
 // ---- GEMM (gemm_kernels.hip) ----
 // taps: 27 or 125 (the packed weights hold that many taps).
@@ -279,6 +282,27 @@ hipError_t launch_gemm_nc(const uint16_t* x, int c_in, const void* wpacked, int 
 hipError_t launch_gemm_centre(const uint16_t* x, int c_in, const void* wpacked, int c_out,
                               int taps, const int32_t* rowbase, int64_t n, const float* part,
                               void* y, bool out_f32, bool relu, int n_cu, hipStream_t s);
+// Row-range GEMM (rows_kernels.hip): the whole pair-list layer in one kernel
+// for 3 x 3 x 3 maps and c_in, c_out <= 64 (c_in a multiple of 8), the
+// partial-product slab kept in LDS. Its weights are a second packing after the
+// first (rows_weight_offset). Wider layers keep the two-kernel form: with a
+// wave's resident weights for 96 or 128 input channels a block walks its
+// chunks latency-bound (measured on the 91k-row set at 128 channels: 62 us
+// against 29 us for the two kernels with 16 waves of 128 registers, 66 us
+// with 8 waves of 256 and the next chunk's loads issued ahead; at 64
+// channels 19 us against 23 us).
+constexpr int kRowsMaxC = 64;
+inline bool rows_eligible(int taps, int c_in, int c_out) {
+    return taps == 27 && c_in <= kRowsMaxC && c_out <= kRowsMaxC && (c_in & 7) == 0;
+}
+size_t rows_weight_offset(int taps, int c_in, int c_out);   // 0: the first packing serves
+size_t rows_weight_bytes(int taps, int c_in, int c_out);    // bytes of the second packing (or 0)
+int rows_pack_nbw(int c_out);                               // its column blocks per tile
+hipError_t launch_gemm_rows(const uint16_t* x, int c_in, const void* wpacked, int c_out,
+                            const int32_t* pair_in, const int32_t* pair_slot,
+                            const int32_t* chunk_pre, const int32_t* rowbase, const MapState* st,
+                            int64_t cap, int64_t n, void* y, bool out_f32, bool relu, int n_cu,
+                            hipStream_t s);
 
 // ---- mask-tile GEMM (masktile_kernels.hip) ----
 // One pass over the rows of one offset group: taps gm of the rows listed at

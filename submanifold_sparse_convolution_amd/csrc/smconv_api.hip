@@ -172,6 +172,7 @@ struct smc_map {
     MaskOrder sorted_order;           // the order the last build's mask sort used
     DevBuf okeys;                     // per-group sort keys ([groups][n])
     DevBuf pair_in, pair_out, pair_slot, rowbase;
+    DevBuf chunk_pre;                 // per 256-row chunk: pairs of each tap and slab rows before it
     int64_t cap = 0;                  // pairs per tap the pair arrays hold (n rounded up to a tile)
     DevBuf part;                      // float32 partial-product slab of the pair-list forward
     DevBuf split;                     // splitter table of the sorted route's key sort
@@ -460,7 +461,8 @@ int smc_map_destroy(smc_map* m) {
                           &m->cells[0], &m->cells[1], &m->keys0, &m->keys1, &m->keys2,
                           &m->vals0, &m->vals1, &m->hist, &m->look, &m->ticket, &m->nbr,
                           &m->mask, &m->mkey0, &m->mkey1, &m->mval0, &m->mval1, &m->okeys,
-                          &m->pair_in, &m->pair_out, &m->pair_slot, &m->rowbase, &m->part,
+                          &m->pair_in, &m->pair_out, &m->pair_slot, &m->rowbase,
+                          &m->chunk_pre, &m->part,
                           &m->zrow, &m->ck0, &m->ck1, &m->ck2, &m->cv0, &m->cv1, &m->chist,
                           &m->ucounts, &m->ocoords, &m->qcoords, &m->scan, &m->split,
                           &m->obits, &m->sticky};
@@ -718,7 +720,8 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
         ((rc = m->pair_in.ensure((size_t)taps * cap * 4, s)) ||
          (rc = m->pair_out.ensure((size_t)taps * cap * 4, s)) ||
          (rc = m->pair_slot.ensure((size_t)taps * cap * 4, s)) ||
-         (rc = m->rowbase.ensure((size_t)(nn + 1) * 4, s))))
+         (rc = m->rowbase.ensure((size_t)(nn + 1) * 4, s)) ||
+         (rc = m->chunk_pre.ensure((size_t)(compact_chunks(nn) + 1) * (kTaps + 1) * 4, s))))
         return rc;
     {
         // the largest sort of the build: input keys, strided candidates or mask-sort items
@@ -765,7 +768,8 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
                 SMC_HIP(launch_lookup_compact(coords, n, g, grid, bits, nbr_out, mask, cap, kTileM, st,
                                               m->pair_in.as<int32_t>(), m->pair_out.as<int32_t>(),
                                               m->pair_slot.as<int32_t>(),
-                                              m->rowbase.as<int32_t>(), m->ws, status, s));
+                                              m->rowbase.as<int32_t>(),
+                                              m->chunk_pre.as<int32_t>(), m->ws, status, s));
                 t_cp.finish();
             } else if (strided) {
                 if ((rc = strided_outputs(m, coords, n, g, sg, st, status, s, &rows))) return rc;
@@ -849,7 +853,8 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
             SMC_HIP(launch_compact(mask, nbr, n, kernel_size, cap, kTileM, st,
                                    m->pair_in.as<int32_t>(),
                                    m->pair_out.as<int32_t>(), m->pair_slot.as<int32_t>(),
-                                   m->rowbase.as<int32_t>(), m->ws, status, s));
+                                   m->rowbase.as<int32_t>(), m->chunk_pre.as<int32_t>(), m->ws,
+                                   status, s));
             t_cp.finish();
         }
     }
@@ -1135,8 +1140,19 @@ static int conv_forward(smc_map* m, const uint16_t* x, int c_in, const void* wpa
         t_mt.finish();
         return SMC_OK;
     }
-    // slab: 4 c_out bytes per off-centre pair; without the build's counts, taps - 1 a row
     const int taps = m->ksize * m->ksize * m->ksize;
+    if (rows_eligible(taps, c_in, c_out) && !(flags & SMC_FWD_SLAB_IN_MEMORY)) {
+        // one kernel, the slab in LDS: nothing to allocate, no count to read
+        StageTimer t_r(m, SMC_STAGE_GEMM, s, false, fixed == nullptr);
+        SMC_HIP(launch_gemm_rows(x, c_in, wpacked, c_out, m->pair_in.as<int32_t>(),
+                                 m->pair_slot.as<int32_t>(), m->chunk_pre.as<int32_t>(),
+                                 m->rowbase.as<int32_t>(), m->state.as<MapState>() + m->slot,
+                                 m->cap, m->n, y, (flags & SMC_FWD_OUT_F32) != 0,
+                                 (flags & SMC_FWD_RELU) != 0, m->n_cu, s));
+        t_r.finish();
+        return SMC_OK;
+    }
+    // slab: 4 c_out bytes per off-centre pair; without the build's counts, taps - 1 a row
     double slab = (double)(taps - 1) * m->n * c_out * 4.0;
     if (m->pending && slab > (double)kSlabBoundBytes) {
         int rc = wait_build(m);

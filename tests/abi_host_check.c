@@ -38,6 +38,8 @@ int main(void) {
     EXPECT(strcmp(smc_status_string(SMC_OK), "ok"), 0);
     EXPECT(strcmp(smc_status_string(999), "unknown status"), 0);
     EXPECT(smc_weight_packed_bytes(3, 128, 128), 27 * 8 * 4 * 64 * 16);
+    EXPECT(smc_weight_packed_bytes(3, 64, 64), 2 * 27 * 4 * 2 * 64 * 16); /* two packings */
+    EXPECT(smc_weight_packed_bytes(3, 136, 128), 27 * 8 * 5 * 64 * 16);
     EXPECT(smc_weight_packed_bytes(3, 0, 5), 0);
     EXPECT(smc_weight_packed_bytes(4, 16, 16), 0);
     EXPECT(smc_map_create(NULL), SMC_ERR_ARG);

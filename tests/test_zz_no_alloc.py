@@ -1,11 +1,12 @@
 """smc_conv_forward_noalloc through the C ABI: the same results as
 smc_conv_forward on the same map (both run the same deterministic kernels, so
 the outputs are compared bit for bit), over two calls in a row with the
-second on a smaller voxel set, on the pair-list path and the grouped
-mask-tile path (whose partial sums also live in the fixed array); a slab
-above the fixed 32 MiB is refused before any work; and, with torch's caching
-allocator bound to the library, the call takes no device memory while the
-allocating forward does."""
+second on a smaller voxel set, on the pair-list path (the one-kernel form,
+which needs no scratch, and the two-kernel form, SMC_FWD_SLAB_IN_MEMORY,
+whose slab lives in the fixed array) and the grouped mask-tile path (whose
+partial sums also live there); a slab above the fixed 32 MiB is refused
+before any work; and, with torch's caching allocator bound to the library,
+the call takes no device memory while the allocating forward does."""
 import ctypes
 
 import numpy as np
@@ -21,6 +22,7 @@ torch = pytest.importorskip("torch")
 
 SMC_ERR_UNSUPPORTED = 8
 SCRATCH_BYTES = 32 << 20
+SLAB = 8                                                  # SMC_FWD_SLAB_IN_MEMORY
 
 
 def call(fn, m, x, wp, y, flags=0):
@@ -53,13 +55,15 @@ def inputs(n, grid, c, seed, n_boxes=40):
 @pytest.mark.parametrize("route", ["dense", "sorted"])
 def test_noalloc_equals_forward_on_two_calls_second_smaller(route):
     m = smc.KernelMap()
-    # the first build is asynchronous: 26 pairs per row would exceed the fixed
-    # array, so the call waits for the build's counts
+    # the first build is asynchronous: for the two-kernel form 26 pairs per row
+    # would exceed the fixed array, so the call waits for the build's counts
     for n, grid, c, seed, sync in ((20000, (400, 400, 24), 128, 31, False),
                                    (3001, (120, 120, 12), 64, 32, True)):
         coords_d, x_d, wp = inputs(n, grid, c, seed)
         m.build(coords_d, spatial_shape=grid, route=route, sync=sync)
-        for flags, f32 in ((0, False), (1, False), (2, True)):      # plain, ReLU, float32 out
+        # plain, ReLU, float32 out; one kernel, then two kernels with the slab
+        for flags, f32 in ((0, False), (1, False), (2, True), (SLAB, False), (SLAB | 1, False),
+                           (SLAB | 2, True)):
             a, b = both(m, x_d, wp, flags, f32)
             assert a.shape == (m.n, c)
             assert np.array_equal(a, b), (n, route, flags)
@@ -92,12 +96,17 @@ def test_noalloc_refuses_a_slab_above_the_fixed_array():
     wp = smc.pack_weights(to_dev_bf16(synth.weights(16, 16, 5)))
     y = torch.full((n, 16), 3.0, dtype=torch.bfloat16, device="cuda")
     L = smc.lib()
-    assert call(L.smc_conv_forward_noalloc, m, x, wp, y) == SMC_ERR_UNSUPPORTED
+    assert call(L.smc_conv_forward_noalloc, m, x, wp, y, SLAB) == SMC_ERR_UNSUPPORTED
     assert b"fixed scratch" in L.smc_last_error()
     torch.cuda.synchronize()
     assert bool((y == 3.0).all())                         # nothing ran
-    # the allocating forward still serves this map
-    assert call(L.smc_conv_forward, m, x, wp, y) == 0
+    # the allocating forward still serves this map, and the one-kernel form
+    # (slab rows in LDS) needs no scratch at all
+    assert call(L.smc_conv_forward, m, x, wp, y, SLAB) == 0
+    y2 = torch.full((n, 16), 3.0, dtype=torch.bfloat16, device="cuda")
+    assert call(L.smc_conv_forward_noalloc, m, x, wp, y2) == 0, L.smc_last_error()
+    torch.cuda.synchronize()
+    assert bool((y == y2).all())
     m.close()
 
 
@@ -111,10 +120,11 @@ def test_noalloc_takes_no_device_memory():
         y = torch.empty((m.n, 64), dtype=torch.bfloat16, device="cuda")
         torch.cuda.synchronize()
         before = torch.cuda.memory_allocated()
-        assert call(L.smc_conv_forward_noalloc, m, x_d, wp, y) == 0, L.smc_last_error()
+        for flags in (0, SLAB):
+            assert call(L.smc_conv_forward_noalloc, m, x_d, wp, y, flags) == 0, L.smc_last_error()
         torch.cuda.synchronize()
         assert torch.cuda.memory_allocated() == before
-        assert call(L.smc_conv_forward, m, x_d, wp, y) == 0     # allocates the handle's slab
+        assert call(L.smc_conv_forward, m, x_d, wp, y, SLAB) == 0   # allocates the handle's slab
         torch.cuda.synchronize()
         assert torch.cuda.memory_allocated() > before
         m.close()
