@@ -43,6 +43,8 @@ bases) count zero.
   k_compact         4 N (masks) + 8 P (pair lists)
   k_sorted_lookup / k_dense_lookup   4 N masks [+ 4 T N table]
   k_conv_masktile   2 N C_in + 2 T C_in C_out + 2 N C_out (+ 8 N C_out per extra group pass)
+  strided layers (M output rows): k_gemm_nc 2 N C_in + 2 T C_in C_out + 8 P (every tap),
+                    k_slab_sum 2 M C_out
   sort passes, k_weight_pack (outside the step), fills: 0
 
   --summarize-pmc FETCH_DIR WRITE_DIR   turn two `rocprofv3 --pmc FETCH_SIZE`
@@ -92,6 +94,7 @@ KERNEL_SOURCES = {
     "k_gemm_nc_big": ("gemm_kernels.hip", "gemm_common.h"),
     "k_gemm_centre_big": ("gemm_kernels.hip", "gemm_common.h"),
     "k_gemm_rows": ("rows_kernels.hip", "gemm_common.h"),
+    "k_slab_sum": ("gemm_kernels.hip", "gemm_common.h"),
     "k_conv_masktile": ("masktile_kernels.hip", "gemm_common.h"),
     "k_os_pass": ("radix_sort.hip",),
 }
@@ -109,8 +112,13 @@ def dev_bf16(bits):
 
 def kernel_model(kernel, n, p, c_in, c_out, taps=27, table=False, n_out=None, groups=1):
     """Compulsory bytes and useful flops of one launch of `kernel` (module
-    docstring). n input rows, p pairs, n_out output rows (strided layers)."""
+    docstring). n input rows, p pairs, n_out output rows (strided layers,
+    whose off-centre GEMM runs every tap and reads the inputs once)."""
     m = n if n_out is None else n_out
+    if n_out is not None and kernel in ("k_gemm_nc", "k_gemm_nc_big"):
+        return 2 * n * c_in + 2 * taps * c_in * c_out + 8 * p, 2.0 * p * c_in * c_out
+    if kernel == "k_slab_sum":
+        return 2 * m * c_out, 0.0
     p_nc = p - n
     t4 = 4 * taps * m if table else 0
     if kernel in ("k_gemm_centre", "k_gemm_centre_big"):
@@ -218,12 +226,14 @@ def stage_kernels(stage, algo, route, kernel_size=3, strided=False, c_in=128):
     """The kernels one execution of a stage launches (pair path unless stated)."""
     big = BIG_MIN_C <= c_in <= BIG_MAX_C and c_in % 8 == 0
     if stage == "gemm":
-        if algo == "mask_tiles" or strided:
+        if algo == "mask_tiles":
             return ("k_conv_masktile",)
         if rows_form(algo, kernel_size, c_in, c_in):
             return ("k_gemm_rows",)
         return ("k_gemm_nc_big",) if big else ("k_gemm_nc",)
     if stage == "centre":
+        if strided:
+            return ("k_slab_sum",)
         return ("k_gemm_centre_big",) if big else ("k_gemm_centre",)
     if stage == "mask_sort":
         return ("k_mask_hist", "k_os_pass")
@@ -304,15 +314,17 @@ def run_workload(name, steps, warmup, sync_build=False, algo="pairs", copy_probe
 
     if strided:
         # a downsampling layer: the output rows are new cells (one layer)
-        m.build_strided(coords_d, spatial_shape=w.grid, batch_size=frames)
+        m.build_strided(coords_d, spatial_shape=w.grid, batch_size=frames,
+                        pairs=algo != "mask_tiles", sort=algo == "mask_tiles")
         ys = [torch.empty((m.n, c), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
     else:
         ys = [torch.empty((n_rows, c), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
 
     def step():
         if strided:
-            m.build_strided(coords_d, spatial_shape=w.grid, batch_size=frames, sync=sync_build)
-            return m.forward(x_d, packed[0], out=ys[0], algo="mask_tiles")
+            m.build_strided(coords_d, spatial_shape=w.grid, batch_size=frames, sync=sync_build,
+                            pairs=algo != "mask_tiles", sort=algo == "mask_tiles")
+            return m.forward(x_d, packed[0], out=ys[0], algo=algo)
         m.build(coords_d, sync=sync_build, **build_kw)
         h = x_d
         for layer in range(w.layers):
@@ -890,7 +902,7 @@ def main():
         line["configs"] = entries
     if not args.no_strided:
         # downsampling layers (kernel 3, stride 2) on the same sets: new output cells,
-        # mask-tile forward; map built every step
+        # pair-list forward over them; map built every step
         line["strided"] = []
         for cname in ("lidar", "deep", "wide", "stage"):
             rr = run_workload(cname, max(10, args.steps // 2), args.warmup, strided=True)

@@ -206,10 +206,14 @@ int smc_map_build(smc_map* map, const int32_t* coords, int64_t n, int ncols,
  * [0, 3)^3, is active; its 27 taps are the cells 2 o + d' (d' in [-1, 1]^3,
  * the submanifold tap numbering), so nbr[o][k] is the input row at
  * 2 o + d_k or -1. Output rows are ordered by (b, x, y, z); their
- * coordinates come from smc_map_export_out_coords. The map then carries the
- * plain mask order over its output rows and no pair lists, and
- * smc_conv_forward runs the mask-tile algorithm on it (x: n_in input rows,
- * y: n output rows).
+ * coordinates come from smc_map_export_out_coords. Unless SMC_BUILD_NO_PAIRS,
+ * the map carries per-tap pair lists over its output rows in which the
+ * centre tap (the input at 2 o, present or not) is a tap like the others;
+ * unless SMC_BUILD_NO_SORT, the plain mask order of its output rows.
+ * smc_conv_forward (x: n_in input rows, y: n output rows) then runs the
+ * pair lists (every tap's products to the slab, each output row the sum of
+ * its slab rows in order) or, with SMC_FWD_MASK_TILES or without pair lists,
+ * the mask-tile algorithm.
  * Arguments as smc_map_build; coordinates count from 0: with spatial_shape
  * NULL the grid is [0, max + 1) per axis, and a negative coordinate is
  * SMC_ERR_RANGE. kernel_size must be 3 and stride 2 (else
@@ -234,6 +238,12 @@ int smc_map_sync(smc_map* map);
 
 /* Wait for the last build and describe the map. info: host pointer. */
 int smc_map_info(smc_map* map, smc_map_info_t* info);
+
+/* Output and input rows of the last build (host pointers, either may be
+ * NULL), without waiting for it: both are known on the host when a build
+ * returns (a strided build reads its output count during the call). For
+ * callers that size y right after an asynchronous build. */
+int smc_map_rows(smc_map* map, int64_t* n, int64_t* n_in);
 
 /*
  * Copy the map to host memory for inspection (parity tests). Each pointer is

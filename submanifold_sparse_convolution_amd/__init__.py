@@ -41,7 +41,7 @@ EXPORTED_SYMBOLS = [
     "smc_map_set_order", "smc_map_calibrate", "smc_map_build_strided",
     "smc_map_export_out_coords", "smc_set_allocator", "smc_probe_mfma_out_bytes",
     "smc_probe_mfma_bf16", "smc_probe_copy", "smc_conv_forward_noalloc",
-    "smc_test_force_lookback_timeout",
+    "smc_test_force_lookback_timeout", "smc_map_rows",
 ]
 STAGES = ["map", "neighbours", "mask_sort", "compact", "gemm", "centre"]
 
@@ -92,6 +92,7 @@ def lib():
     L.smc_map_build.argtypes = [vp, vp, i64, i32, vp, i32, i32, i32, u32, vp]
     L.smc_map_sync.argtypes = [vp]
     L.smc_map_info.argtypes = [vp, ctypes.POINTER(MapInfo)]
+    L.smc_map_rows.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i64)]
     L.smc_map_export.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     L.smc_weight_packed_bytes.argtypes = [i32, i32, i32]
     L.smc_weight_packed_bytes.restype = ctypes.c_size_t
@@ -120,7 +121,7 @@ def lib():
                  "smc_timing_enable", "smc_timing_read", "smc_map_set_order",
                  "smc_map_calibrate", "smc_map_build_strided", "smc_map_export_out_coords",
                  "smc_set_allocator", "smc_probe_mfma_bf16", "smc_probe_copy",
-                 "smc_conv_forward_noalloc", "smc_test_force_lookback_timeout"):
+                 "smc_conv_forward_noalloc", "smc_test_force_lookback_timeout", "smc_map_rows"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -276,9 +277,11 @@ class KernelMap:
 
     def build_strided(self, coords, spatial_shape=None, batch_size: int = 0, route: str = "auto",
                       sync: bool = True, kernel_size: int = 3, stride: int = 2,
-                      stream=None) -> "KernelMap":
+                      pairs: bool = True, sort: bool = True, stream=None) -> "KernelMap":
         """Downsampling map (kernel 3, stride 2, padding 1) of int32 [N, 4] / [N, 3]
-        CUDA coordinates; outputs are new cells (``out_coords()``), ``n`` of them."""
+        CUDA coordinates; outputs are new cells (``out_coords()``), ``n`` of them.
+        pairs: per-tap pair lists over the output rows (forward algo "pairs");
+        sort: the mask order of the output rows (forward algo "mask_tiles")."""
         import torch
         _need(coords, torch.int32, "coords", 2)
         n, ncols = int(coords.shape[0]), int(coords.shape[1])
@@ -290,9 +293,12 @@ class KernelMap:
         _check(lib().smc_map_build_strided(
             self._h, ctypes.c_void_p(coords.data_ptr() if n else 0), n, ncols, shape,
             int(batch_size), int(kernel_size), int(stride), ROUTES[route],
-            0 if sync else SMC_BUILD_ASYNC, _stream(stream)))
-        info = self.info()
-        self.n, self.n_in, self.kernel_size, self.strided = info["n"], n, int(kernel_size), True
+            (0 if sync else SMC_BUILD_ASYNC) | (0 if pairs else SMC_BUILD_NO_PAIRS)
+            | (0 if sort else SMC_BUILD_NO_SORT), _stream(stream)))
+        # the output count is on the host when the call returns: no wait here
+        rows = ctypes.c_int64()
+        _check(lib().smc_map_rows(self._h, ctypes.byref(rows), None))
+        self.n, self.n_in, self.kernel_size, self.strided = rows.value, n, int(kernel_size), True
         return self
 
     def out_coords(self):

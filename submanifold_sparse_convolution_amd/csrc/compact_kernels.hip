@@ -296,7 +296,9 @@ struct CompactLds {
 // pairs listed in LDS as (row, tap) entries in output order, then written out
 // with consecutive threads on consecutive pair positions. The last chunk
 // publishes the totals. chunk_pre[bid][k] receives the pairs of tap k (k <
-// kTaps) and the slab rows (k = kTaps) in earlier chunks. With nbr_out, the chunk's neighbour rows are stored
+// kTaps) and the slab rows (k = kTaps) in earlier chunks. dense_centre: the
+// centre tap pairs every row with itself and gets no slab rows (submanifold
+// maps); otherwise it is a tap like the others (strided maps). With nbr_out, the chunk's neighbour rows are stored
 // there (coalesced) between publishing the counts and the look-back, where
 // the block would otherwise wait. Starts and ends with all threads in step.
 __device__ __forceinline__ void compact_chunk(CompactLds& L, uint32_t m, uint32_t bid, int64_t n,
@@ -308,13 +310,17 @@ __device__ __forceinline__ void compact_chunk(CompactLds& L, uint32_t m, uint32_
                                               int32_t* __restrict__ chunk_pre,
                                               uint64_t* __restrict__ look, uint32_t epoch,
                                               uint32_t* status, int32_t* __restrict__ nbr_out,
+                                              bool dense_centre = true,
                                               uint32_t spin_limit = kSpinLimit,
                                               uint32_t wait_xor = 0u) {
     constexpr int kCols = kTaps + 1;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int64_t base0 = (int64_t)bid * kCChunk;
     const int64_t row = base0 + tid;
-    const uint32_t deg = m ? (uint32_t)__popc(m & ~(1u << kCentre)) : 0u;
+    // slab rows of the row: its off-centre pairs, or with a sparse centre (a
+    // strided map, whose output o need not be an input) every pair
+    const uint32_t slab_taps = dense_centre ? ~(1u << kCentre) : ~0u;
+    const uint32_t deg = (uint32_t)__popc(m & slab_taps);
     // per-wave count of each tap (lane k keeps tap k) and of slab rows (lane kTaps),
     // over the taps some row of the wave has (the wave's OR of masks)
     const uint32_t uni = wave_or(m);
@@ -431,11 +437,10 @@ __device__ __forceinline__ void compact_chunk(CompactLds& L, uint32_t m, uint32_
         const int64_t pos = (int64_t)k * cap + L.pre[k] + (p - (int)L.loc[k]);
         if (pos >= (int64_t)k * cap + cap) continue;          // only after a stalled wait
         const uint32_t mr = L.m[lr];
-        pair_in[pos] = k == kCentre ? (int32_t)(base0 + lr) : L.nb[lr * kTaps + k];
+        const bool self = dense_centre && k == kCentre;
+        pair_in[pos] = self ? (int32_t)(base0 + lr) : L.nb[lr * kTaps + k];
         pair_out[pos] = (int32_t)(base0 + lr);
-        pair_slot[pos] = k == kCentre
-                             ? -1
-                             : (int32_t)(L.rb[lr] + __popc(mr & ((1u << k) - 1u) & ~(1u << kCentre)));
+        pair_slot[pos] = self ? -1 : (int32_t)(L.rb[lr] + __popc(mr & ((1u << k) - 1u) & slab_taps));
     }
 }
 
@@ -447,7 +452,8 @@ __global__ __launch_bounds__(kCThreads) void k_compact(
     const uint32_t* __restrict__ mask, const int32_t* __restrict__ nbr, int64_t n, int64_t cap,
     int tile_m, MapState* st, int32_t* __restrict__ pair_in, int32_t* __restrict__ pair_out,
     int32_t* __restrict__ pair_slot, int32_t* __restrict__ rowbase, int32_t* __restrict__ chunk_pre,
-    uint64_t* __restrict__ look, uint32_t* ticket, bool by_index, uint32_t epoch, uint32_t* status) {
+    uint64_t* __restrict__ look, uint32_t* ticket, bool by_index, uint32_t epoch, uint32_t* status,
+    bool dense_centre) {
     __shared__ CompactLds L;
     const int tid = threadIdx.x;
     const uint32_t bid = chunk_of_block(by_index, ticket, &L.bid);
@@ -473,7 +479,7 @@ __global__ __launch_bounds__(kCThreads) void k_compact(
         if (q < kCNbrVec) nb4[q] = nv4[j];
     }
     compact_chunk(L, row < n ? mv : 0u, bid, n, cap, tile_m, st, pair_in, pair_out, pair_slot,
-                  rowbase, chunk_pre, look, epoch, status, nullptr);
+                  rowbase, chunk_pre, look, epoch, status, nullptr, dense_centre);
     if (!by_index && bid == gridDim.x - 1 && tid == 0) atomicExch(ticket, 0u);
 }
 
@@ -543,7 +549,7 @@ __global__ __launch_bounds__(kCThreads) void k_lookup_compact(
     if (row < n) mask[row] = m;
     __syncthreads();
     compact_chunk(L, m, bid, n, cap, tile_m, st, pair_in, pair_out, pair_slot, rowbase, chunk_pre,
-                  look, epoch, status, nbr, spin_limit, wait_xor);
+                  look, epoch, status, nbr, true, spin_limit, wait_xor);
     if (!by_index && bid == gridDim.x - 1 && tid == 0) atomicExch(ticket, 0u);
 }
 
@@ -775,7 +781,8 @@ static uint32_t next_epoch(SortWork& ws) {
 hipError_t launch_compact(const uint32_t* mask, const int32_t* nbr, int64_t n, int ksize,
                           int64_t cap, int tile_m, MapState* st, int32_t* pair_in,
                           int32_t* pair_out, int32_t* pair_slot, int32_t* rowbase,
-                          int32_t* chunk_pre, SortWork& ws, uint32_t* status, hipStream_t s) {
+                          int32_t* chunk_pre, SortWork& ws, uint32_t* status, hipStream_t s,
+                          bool dense_centre) {
     const uint32_t epoch = next_epoch(ws);
     const unsigned blocks = (unsigned)compact_chunks(n);
     if (ksize == 5) {
@@ -785,7 +792,8 @@ hipError_t launch_compact(const uint32_t* mask, const int32_t* nbr, int64_t n, i
     } else {
         const bool by_index = fits_at_once((const void*)k_compact, 1, blocks);
         launch(k_compact, blocks, kCThreads, 0, s, mask, nbr, n, cap, tile_m, st, pair_in,
-               pair_out, pair_slot, rowbase, chunk_pre, ws.look, ws.ticket, by_index, epoch, status);
+               pair_out, pair_slot, rowbase, chunk_pre, ws.look, ws.ticket, by_index, epoch, status,
+               dense_centre);
     }
     return hipGetLastError();
 }

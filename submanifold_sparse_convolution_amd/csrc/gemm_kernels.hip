@@ -206,21 +206,22 @@ __device__ __forceinline__ void store_f32(float* __restrict__ dst, int col0, int
     }
 }
 
-// Tile table of the non-centre taps, tiles of kRows pairs: on return
-// s_first[k] is tap k's first tile (s_first[taps]: the tile count) and
-// s_cnt[k] its pairs (the centre: none). Per-tap counts are read in parallel
-// (one thread per tap), tiles per tap scanned over the first two waves.
-// Every thread of the block calls this.
+// Tile table of the taps, tiles of kRows pairs: on return s_first[k] is tap
+// k's first tile (s_first[taps]: the tile count) and s_cnt[k] its pairs (the
+// centre: none when skip_centre, i.e. when the centre is a dense GEMM of its
+// own). Per-tap counts are read in parallel (one thread per tap), tiles per
+// tap scanned over the first two waves. Every thread of the block calls this.
 template <int kRows>
 __device__ __forceinline__ void nc_tap_table(int taps, const MapState* __restrict__ st,
-                                             int32_t* s_first, int32_t* s_cnt, int32_t* s_wave0) {
+                                             int32_t* s_first, int32_t* s_cnt, int32_t* s_wave0,
+                                             int skip_centre) {
     static_assert(kMaxTaps <= 128 && kGemmThreads >= 128, "two waves scan the taps");
     const int centre = taps / 2;
     const int lane = threadIdx.x & 63;
     const int k = threadIdx.x;
     int32_t tiles = 0;
     if (k < taps) {
-        const int32_t c = k == centre ? 0 : st->tap_count[k];
+        const int32_t c = skip_centre && k == centre ? 0 : st->tap_count[k];
         s_cnt[k] = c;
         tiles = (c + kRows - 1) / kRows;
     }
@@ -238,15 +239,16 @@ __device__ __forceinline__ void nc_tap_table(int taps, const MapState* __restric
     __syncthreads();
 }
 
-// Non-centre taps: blocks stride over tiles of 64 MW pairs of one tap (tap k
-// holds tap_count[k] pairs from k * cap on, cap a multiple of 256; the counts
-// are read on the device). Each pair's product row goes to its slab row.
+// Non-centre taps (every tap when skip_centre is 0): blocks stride over tiles
+// of 64 MW pairs of one tap (tap k holds tap_count[k] pairs from k * cap on,
+// cap a multiple of 256; the counts are read on the device). Each pair's
+// product row goes to its slab row. n: the input rows (bounds the gathers).
 template <int NBW, int MW, bool VEC, bool STREAM>
 __global__ __launch_bounds__(kGemmThreads, 2) void k_gemm_nc(
     const uint16_t* __restrict__ x, int c_in, int steps, const u32x4* __restrict__ wp, int n_wt,
     int c_out, int taps, const int32_t* __restrict__ pair_in,
     const int32_t* __restrict__ pair_slot, const MapState* __restrict__ st, int64_t cap, int64_t n,
-    float* __restrict__ part) {
+    float* __restrict__ part, int skip_centre) {
     constexpr int kRows = 64 * MW;                 // pairs per tile
     extern __shared__ u32x4 s_b[];
     __shared__ int32_t s_first[kMaxTaps + 1];     // first tile of each tap (centre: none)
@@ -254,7 +256,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_gemm_nc(
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
     __shared__ int32_t s_wave0;
-    nc_tap_table<kRows>(taps, st, s_first, s_cnt, &s_wave0);
+    nc_tap_table<kRows>(taps, st, s_first, s_cnt, &s_wave0, skip_centre);
     const int n_nc = s_first[taps];
     const int wt_i = blockIdx.y;
     const int col0 = wt_i * 16 * NBW + r * NBW;
@@ -504,6 +506,55 @@ __global__ __launch_bounds__(kGemmThreads, (STREAM && MW == 2) ? 1 : (STREAM ? 2
     }
 }
 
+// Output rows of a map whose centre tap is a tap like the others (strided
+// maps): row i is the sum of its slab rows rowbase[i] .. rowbase[i+1] - 1 in
+// order, rounded to bf16 (to nearest, ties to even) or kept in float, with the
+// optional ReLU. Thread t takes four columns (VEC4, c_out a multiple of 4) or
+// one column of one row; a row's threads read each slab row contiguously.
+template <bool VEC4, bool OUT_F32>
+__global__ __launch_bounds__(kBlock) void k_slab_sum(const float* __restrict__ part,
+                                                     const int32_t* __restrict__ rowbase, int64_t m,
+                                                     int c_out, void* __restrict__ yv, int relu) {
+    const int per = VEC4 ? c_out / 4 : c_out;      // threads per row
+    const int64_t total = m * per;
+    for (int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x; t < total;
+         t += (int64_t)gridDim.x * kBlock) {
+        const int64_t row = t / per;
+        const int col = (int)(t - row * per) * (VEC4 ? 4 : 1);
+        const int32_t e0 = rowbase[row], e1 = rowbase[row + 1];
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int32_t e = e0; e < e1; ++e) {
+            const float* p = part + (int64_t)e * c_out + col;
+            if (VEC4) {
+                const float4 q = *reinterpret_cast<const float4*>(p);
+                v[0] += q.x;
+                v[1] += q.y;
+                v[2] += q.z;
+                v[3] += q.w;
+            } else {
+                v[0] += p[0];
+            }
+        }
+        if (OUT_F32) {
+            float* y = static_cast<float*>(yv) + row * c_out + col;
+#pragma unroll
+            for (int j = 0; j < (VEC4 ? 4 : 1); ++j) y[j] = (relu && v[j] < 0.f) ? 0.f : v[j];
+        } else {
+            uint16_t* y = static_cast<uint16_t*>(yv) + row * c_out + col;
+            uint32_t b[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                b[j] = bf16_rne_bits(v[j]);
+                if (relu && (b[j] & 0x8000u)) b[j] = 0;
+            }
+            if (VEC4)
+                *reinterpret_cast<uint2*>(y) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+            else
+                y[0] = (uint16_t)b[0];
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Wide inputs (C_in above 128, up to kBigMaxSteps k-steps): one (tap, column
 // tile) weight slab stays in LDS for the whole launch -- steps x NBW KiB, 128
@@ -589,7 +640,7 @@ __global__ __launch_bounds__(kBigThreads, 2) void k_gemm_nc_big(
     const uint16_t* __restrict__ x, int c_in, int steps, const u32x4* __restrict__ wp, int n_wt,
     int c_out, int taps, const int32_t* __restrict__ pair_in,
     const int32_t* __restrict__ pair_slot, const MapState* __restrict__ st, int64_t cap, int64_t n,
-    float* __restrict__ part) {
+    float* __restrict__ part, int skip_centre) {
     constexpr int kRows = kBigWaves * 16;          // pairs per item
     extern __shared__ u32x4 s_b[];
     __shared__ int32_t s_first[kMaxTaps + 1];
@@ -597,7 +648,7 @@ __global__ __launch_bounds__(kBigThreads, 2) void k_gemm_nc_big(
     __shared__ int32_t s_wave0;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
-    nc_tap_table<kRows>(taps, st, s_first, s_cnt, &s_wave0);
+    nc_tap_table<kRows>(taps, st, s_first, s_cnt, &s_wave0, skip_centre);
     const int n_items = s_first[taps];
     const int per = (n_items + (int)gridDim.x - 1) / (int)gridDim.x;
     const int u0 = (int)blockIdx.x * per;
@@ -750,27 +801,27 @@ bool lds_ok(K kernel, size_t bytes) {
 template <int NBW, int MW, bool VEC, bool STREAM>
 void launch_nc_t(dim3 grid, hipStream_t s, const uint16_t* x, int c_in, int steps, const u32x4* wp,
                  int n_wt, int c_out, int taps, const int32_t* pi, const int32_t* ps,
-                 const MapState* st, int64_t cap, int64_t n, float* part) {
+                 const MapState* st, int64_t cap, int64_t n, float* part, int sc) {
     constexpr size_t lds = gemm_lds_bytes<NBW, STREAM>();
     static const bool ok = lds_ok(k_gemm_nc<NBW, MW, VEC, STREAM>, lds);
     (void)ok;
     launch(k_gemm_nc<NBW, MW, VEC, STREAM>, grid, kGemmThreads, lds, s, x, c_in, steps, wp, n_wt,
-           c_out, taps, pi, ps, st, cap, n, part);
+           c_out, taps, pi, ps, st, cap, n, part, sc);
 }
 
 template <int NBW>
 void launch_nc(dim3 grid, hipStream_t s, int mw, const uint16_t* x, int c_in, int steps,
                const u32x4* wp, int n_wt, int c_out, int taps, const int32_t* pi,
-               const int32_t* ps, const MapState* st, int64_t cap, int64_t n, float* part) {
+               const int32_t* ps, const MapState* st, int64_t cap, int64_t n, float* part, int sc) {
     const bool vec = (c_in & 7) == 0;
     if (mw == 2)                                   // mw_nc_for: streamed, 16-byte row loads
-        launch_nc_t<NBW, 2, true, true>(grid, s, x, c_in, steps, wp, n_wt, c_out, taps, pi, ps, st, cap, n, part);
+        launch_nc_t<NBW, 2, true, true>(grid, s, x, c_in, steps, wp, n_wt, c_out, taps, pi, ps, st, cap, n, part, sc);
     else if (steps > kChunk)
-        launch_nc_t<NBW, 1, false, true>(grid, s, x, c_in, steps, wp, n_wt, c_out, taps, pi, ps, st, cap, n, part);
+        launch_nc_t<NBW, 1, false, true>(grid, s, x, c_in, steps, wp, n_wt, c_out, taps, pi, ps, st, cap, n, part, sc);
     else if (vec)
-        launch_nc_t<NBW, 1, true, false>(grid, s, x, c_in, steps, wp, n_wt, c_out, taps, pi, ps, st, cap, n, part);
+        launch_nc_t<NBW, 1, true, false>(grid, s, x, c_in, steps, wp, n_wt, c_out, taps, pi, ps, st, cap, n, part, sc);
     else
-        launch_nc_t<NBW, 1, false, false>(grid, s, x, c_in, steps, wp, n_wt, c_out, taps, pi, ps, st, cap, n, part);
+        launch_nc_t<NBW, 1, false, false>(grid, s, x, c_in, steps, wp, n_wt, c_out, taps, pi, ps, st, cap, n, part, sc);
 }
 
 template <int NBW, int MW, bool OUT_F32, bool VEC, bool STREAM>
@@ -813,11 +864,12 @@ void launch_centre(dim3 grid, hipStream_t s, int mw, bool out_f32, const uint16_
 template <int NBW>
 void launch_nc_big(dim3 grid, size_t lds, hipStream_t s, const uint16_t* x, int c_in, int steps,
                    const u32x4* wp, int n_wt, int c_out, int taps, const int32_t* pi,
-                   const int32_t* ps, const MapState* st, int64_t cap, int64_t n, float* part) {
+                   const int32_t* ps, const MapState* st, int64_t cap, int64_t n, float* part,
+                   int sc) {
     static const bool ok = lds_ok(k_gemm_nc_big<NBW>, (size_t)kBigMaxSteps * 8 * 1024);
     (void)ok;
     launch(k_gemm_nc_big<NBW>, grid, kBigThreads, lds, s, x, c_in, steps, wp, n_wt, c_out, taps,
-           pi, ps, st, cap, n, part);
+           pi, ps, st, cap, n, part, sc);
 }
 
 template <int NBW>
@@ -870,7 +922,9 @@ hipError_t launch_weight_pack(const uint16_t* w, int taps, int c_in, int c_out, 
 
 hipError_t launch_gemm_nc(const uint16_t* x, int c_in, const void* wpacked, int c_out, int taps,
                           const int32_t* pair_in, const int32_t* pair_slot, const MapState* st,
-                          int64_t cap, int64_t n, int n_cu, float* part, hipStream_t s) {
+                          int64_t cap, int64_t n, int n_cu, float* part, hipStream_t s,
+                          bool skip_centre) {
+    const int sc = skip_centre ? 1 : 0;
     const int steps = (c_in + 31) / 32;
     const int nbw = nbw_for(c_out);
     const int n_wt = (c_out + 16 * nbw - 1) / (16 * nbw);
@@ -881,10 +935,10 @@ hipError_t launch_gemm_nc(const uint16_t* x, int c_in, const void* wpacked, int 
         const size_t lds = (size_t)steps * nbw * 64 * 16;
         const u32x4* wp = (const u32x4*)wpacked;
         switch (nbw) {
-            case 1: launch_nc_big<1>(grid, lds, s, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part); break;
-            case 2: launch_nc_big<2>(grid, lds, s, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part); break;
-            case 4: launch_nc_big<4>(grid, lds, s, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part); break;
-            default: launch_nc_big<8>(grid, lds, s, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part); break;
+            case 1: launch_nc_big<1>(grid, lds, s, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part, sc); break;
+            case 2: launch_nc_big<2>(grid, lds, s, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part, sc); break;
+            case 4: launch_nc_big<4>(grid, lds, s, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part, sc); break;
+            default: launch_nc_big<8>(grid, lds, s, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part, sc); break;
         }
         return hipGetLastError();
     }
@@ -896,10 +950,29 @@ hipError_t launch_gemm_nc(const uint16_t* x, int c_in, const void* wpacked, int 
     dim3 grid((unsigned)gx, (unsigned)n_wt);
     const u32x4* wp = (const u32x4*)wpacked;
     switch (nbw) {
-        case 1: launch_nc<1>(grid, s, mw, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part); break;
-        case 2: launch_nc<2>(grid, s, mw, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part); break;
-        case 4: launch_nc<4>(grid, s, mw, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part); break;
-        default: launch_nc<8>(grid, s, mw, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part); break;
+        case 1: launch_nc<1>(grid, s, mw, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part, sc); break;
+        case 2: launch_nc<2>(grid, s, mw, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part, sc); break;
+        case 4: launch_nc<4>(grid, s, mw, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part, sc); break;
+        default: launch_nc<8>(grid, s, mw, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part, sc); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_slab_sum(const float* part, const int32_t* rowbase, int64_t m, int c_out,
+                           void* y, bool out_f32, bool relu, int n_cu, hipStream_t s) {
+    if (m <= 0) return hipSuccess;
+    const bool vec4 = (c_out & 3) == 0;
+    const int64_t total = m * (vec4 ? c_out / 4 : c_out);
+    int64_t blocks = (total + kBlock - 1) / kBlock;
+    if (blocks > (int64_t)n_cu * 16) blocks = (int64_t)n_cu * 16;
+    const dim3 grid((unsigned)blocks);
+    const int rl = relu ? 1 : 0;
+    if (vec4) {
+        if (out_f32) launch(k_slab_sum<true, true>, grid, kBlock, 0, s, part, rowbase, m, c_out, y, rl);
+        else launch(k_slab_sum<true, false>, grid, kBlock, 0, s, part, rowbase, m, c_out, y, rl);
+    } else {
+        if (out_f32) launch(k_slab_sum<false, true>, grid, kBlock, 0, s, part, rowbase, m, c_out, y, rl);
+        else launch(k_slab_sum<false, false>, grid, kBlock, 0, s, part, rowbase, m, c_out, y, rl);
     }
     return hipGetLastError();
 }

@@ -257,10 +257,13 @@ size_t compact_look_bytes_k(int64_t n, int ksize);
 // x (kTaps + 1)) receives each 256-row chunk's starts: row c, column k < kTaps
 // = pairs of tap k in chunks before c, column kTaps = slab rows before c (row
 // c = chunks: the totals). ksize 5 leaves it alone.
+// dense_centre false (3 x 3 x 3 only): the centre tap is a tap like the others
+// (strided maps), with slab rows of its own and pair_in from the table.
 hipError_t launch_compact(const uint32_t* mask, const int32_t* nbr, int64_t n, int ksize,
                           int64_t cap, int tile_m, MapState* st, int32_t* pair_in,
                           int32_t* pair_out, int32_t* pair_slot, int32_t* rowbase,
-                          int32_t* chunk_pre, SortWork& ws, uint32_t* status, hipStream_t s);
+                          int32_t* chunk_pre, SortWork& ws, uint32_t* status, hipStream_t s,
+                          bool dense_centre = true);
 // Dense route: neighbour lookup and compaction in one kernel (also writes nbr
 // and mask).
 hipError_t launch_lookup_compact(const int32_t* coords, int64_t n, const Geom& g,
@@ -275,9 +278,17 @@ hipError_t launch_lookup_compact(const int32_t* coords, int64_t n, const Geom& g
 size_t packed_weight_bytes(int taps, int c_in, int c_out);
 hipError_t launch_weight_pack(const uint16_t* w, int taps, int c_in, int c_out, void* out,
                               hipStream_t s);
+// n: input rows (bounds the gathered rows). skip_centre: the centre tap runs
+// as a dense GEMM of its own (k_gemm_centre); false for strided maps, whose
+// centre tap is sparse like the others.
 hipError_t launch_gemm_nc(const uint16_t* x, int c_in, const void* wpacked, int c_out, int taps,
                           const int32_t* pair_in, const int32_t* pair_slot, const MapState* st,
-                          int64_t cap, int64_t n, int n_cu, float* part, hipStream_t s);
+                          int64_t cap, int64_t n, int n_cu, float* part, hipStream_t s,
+                          bool skip_centre = true);
+// Output rows of a strided map: y[i] = the sum of slab rows rowbase[i] ..
+// rowbase[i+1] - 1 in order (bf16 rounded or float, optional ReLU), m rows.
+hipError_t launch_slab_sum(const float* part, const int32_t* rowbase, int64_t m, int c_out,
+                           void* y, bool out_f32, bool relu, int n_cu, hipStream_t s);
 // rowbase: [n + 1], row i's slab rows are rowbase[i] .. rowbase[i+1] - 1.
 hipError_t launch_gemm_centre(const uint16_t* x, int c_in, const void* wpacked, int c_out,
                               int taps, const int32_t* rowbase, int64_t n, const float* part,

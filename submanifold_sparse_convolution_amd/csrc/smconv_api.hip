@@ -681,9 +681,10 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     m->n = n;
 
     // ---- buffers ----
-    // a strided map: no pair lists, the plain mask order over its output rows
-    const bool want_pairs = !(flags & SMC_BUILD_NO_PAIRS) && !strided;
-    const bool want_sort = (!(flags & SMC_BUILD_NO_SORT) && kernel_size == 3) || strided;
+    // a strided map: pair lists over its output rows (sized once the output
+    // count is known), the plain mask order
+    const bool want_pairs = !(flags & SMC_BUILD_NO_PAIRS);
+    const bool want_sort = !(flags & SMC_BUILD_NO_SORT) && kernel_size == 3;
     const int64_t nn = n > 0 ? n : 1;
     const int64_t n_cand = strided ? 8 * nn : 0;      // candidate output cells (8 per input)
     const int64_t rows_cap = strided ? n_cand : nn;   // rows of the map's tables
@@ -716,7 +717,7 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
          (rc = m->chist.ensure((size_t)kHistKeyInts * 4, s)) ||
          (rc = m->ucounts.ensure((size_t)unique_blocks(n_cand) * 4, s))))
         return rc;
-    if (want_pairs &&
+    if (want_pairs && !strided &&
         ((rc = m->pair_in.ensure((size_t)taps * cap * 4, s)) ||
          (rc = m->pair_out.ensure((size_t)taps * cap * 4, s)) ||
          (rc = m->pair_slot.ensure((size_t)taps * cap * 4, s)) ||
@@ -743,7 +744,7 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     if (n > 0) {
         int32_t* nbr = m->nbr.as<int32_t>();
         uint32_t* mask = m->mask.as<uint32_t>();
-        const bool fused = chosen == SMC_ROUTE_DENSE && want_pairs && kernel_size == 3;
+        const bool fused = chosen == SMC_ROUTE_DENSE && want_pairs && kernel_size == 3 && !strided;
         // the fused kernel writes the table only when asked to or when the mask-tile
         // path (which gathers through it) may run on this map
         int32_t* nbr_out = fused && !want_sort && !(flags & SMC_BUILD_TABLE) ? nullptr : nbr;
@@ -848,7 +849,26 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
             }
             t_ms.finish();
         }
-        if (want_pairs && !fused) {
+        if (want_pairs && !fused && strided) {
+            // the output rows' pair lists: every tap sparse, the centre too
+            const int64_t rr = rows > 0 ? rows : 1;
+            const int64_t cap_s = (rr + kCapAlign - 1) / kCapAlign * kCapAlign;
+            if ((rc = m->pair_in.ensure((size_t)taps * cap_s * 4, s)) ||
+                (rc = m->pair_out.ensure((size_t)taps * cap_s * 4, s)) ||
+                (rc = m->pair_slot.ensure((size_t)taps * cap_s * 4, s)) ||
+                (rc = m->rowbase.ensure((size_t)(rr + 1) * 4, s)) ||
+                (rc = m->chunk_pre.ensure((size_t)(compact_chunks(rr) + 1) * (kTaps + 1) * 4, s)))
+                return rc;
+            m->cap = cap_s;
+            if (rows > 0) {
+                StageTimer t_cp(m, SMC_STAGE_COMPACT, s);
+                SMC_HIP(launch_compact(mask, nbr, rows, kernel_size, cap_s, kTileM, st,
+                                       m->pair_in.as<int32_t>(), m->pair_out.as<int32_t>(),
+                                       m->pair_slot.as<int32_t>(), m->rowbase.as<int32_t>(),
+                                       m->chunk_pre.as<int32_t>(), m->ws, status, s, false));
+                t_cp.finish();
+            }
+        } else if (want_pairs && !fused) {
             StageTimer t_cp(m, SMC_STAGE_COMPACT, s);
             SMC_HIP(launch_compact(mask, nbr, n, kernel_size, cap, kTileM, st,
                                    m->pair_in.as<int32_t>(),
@@ -861,6 +881,7 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     m->has_pairs = want_pairs;
     m->has_sort = want_sort;
     m->has_table = !(chosen == SMC_ROUTE_DENSE && want_pairs && kernel_size == 3 && !want_sort &&
+                     !strided &&
                      !(flags & SMC_BUILD_TABLE)) || n == 0;
     m->sorted_order = ord;
     m->ksize = kernel_size;
@@ -903,8 +924,8 @@ int smc_map_build_strided(smc_map* m, const int32_t* coords, int64_t n, int ncol
                     kernel_size, stride);
     if (n > kMaxStridedRows)
         return fail(SMC_ERR_ARG, "n = %lld above 2^24 for a strided map", (long long)n);
-    return build_map(m, coords, n, ncols, spatial_shape, batch_size, kernel_size, route,
-                     flags & ~(unsigned)(SMC_BUILD_NO_PAIRS | SMC_BUILD_NO_SORT), stream, true);
+    return build_map(m, coords, n, ncols, spatial_shape, batch_size, kernel_size, route, flags,
+                     stream, true);
 }
 
 int smc_map_export_out_coords(smc_map* m, int32_t* out_coords) {
@@ -925,6 +946,14 @@ int smc_map_sync(smc_map* m) {
     int rc = wait_build(m);
     if (rc) return rc;
     return m->build_status;
+}
+
+int smc_map_rows(smc_map* m, int64_t* n, int64_t* n_in) {
+    if (!m) return fail(SMC_ERR_ARG, "map is NULL");
+    if (!m->built) return fail(SMC_ERR_STATE, "map was never built");
+    if (n) *n = m->n;
+    if (n_in) *n_in = m->n_in;
+    return SMC_OK;
 }
 
 int smc_map_info(smc_map* m, smc_map_info_t* info) {
@@ -1078,8 +1107,8 @@ static int conv_forward(smc_map* m, const uint16_t* x, int c_in, const void* wpa
     if (c_in < 1 || c_out < 1) return fail(SMC_ERR_ARG, "c_in = %d, c_out = %d", c_in, c_out);
     if (c_in > kMaxChannels || c_out > kMaxChannels)
         return fail(SMC_ERR_UNSUPPORTED, "channels above 4096");
-    // a strided map has mask tiles only (its outputs are not its inputs)
-    const bool mask_tiles = (flags & SMC_FWD_MASK_TILES) != 0 || m->strided;
+    // a strided map without pair lists has mask tiles only
+    const bool mask_tiles = (flags & SMC_FWD_MASK_TILES) != 0 || (m->strided && !m->has_pairs);
     if (!mask_tiles && !m->has_pairs)
         return fail(SMC_ERR_STATE, "map was built without pair lists (SMC_BUILD_NO_PAIRS)");
     if (mask_tiles && m->ksize != 3)
@@ -1141,7 +1170,7 @@ static int conv_forward(smc_map* m, const uint16_t* x, int c_in, const void* wpa
         return SMC_OK;
     }
     const int taps = m->ksize * m->ksize * m->ksize;
-    if (rows_eligible(taps, c_in, c_out) && !(flags & SMC_FWD_SLAB_IN_MEMORY)) {
+    if (rows_eligible(taps, c_in, c_out) && !m->strided && !(flags & SMC_FWD_SLAB_IN_MEMORY)) {
         // one kernel, the slab in LDS: nothing to allocate, no count to read
         StageTimer t_r(m, SMC_STAGE_GEMM, s, false, fixed == nullptr);
         SMC_HIP(launch_gemm_rows(x, c_in, wpacked, c_out, m->pair_in.as<int32_t>(),
@@ -1152,8 +1181,9 @@ static int conv_forward(smc_map* m, const uint16_t* x, int c_in, const void* wpa
         t_r.finish();
         return SMC_OK;
     }
-    // slab: 4 c_out bytes per off-centre pair; without the build's counts, taps - 1 a row
-    double slab = (double)(taps - 1) * m->n * c_out * 4.0;
+    // slab: 4 c_out bytes per off-centre pair (a strided map: per pair); without
+    // the build's counts, taps - 1 (taps) a row
+    double slab = (double)(m->strided ? taps : taps - 1) * m->n * c_out * 4.0;
     if (m->pending && slab > (double)kSlabBoundBytes) {
         int rc = wait_build(m);
         if (rc) return rc;
@@ -1178,14 +1208,21 @@ static int conv_forward(smc_map* m, const uint16_t* x, int c_in, const void* wpa
     }
     StageTimer t_g(m, SMC_STAGE_GEMM, s, false, fixed == nullptr);
     SMC_HIP(launch_gemm_nc(x, c_in, wpacked, c_out, taps, m->pair_in.as<int32_t>(),
-                           m->pair_slot.as<int32_t>(), m->state.as<MapState>() + m->slot, m->cap, m->n,
-                           m->n_cu, part, s));
+                           m->pair_slot.as<int32_t>(), m->state.as<MapState>() + m->slot, m->cap,
+                           m->n_in, m->n_cu, part, s, !m->strided));
     t_g.finish();
     StageTimer t_f(m, SMC_STAGE_CENTRE, s, false, fixed == nullptr);
-    SMC_HIP(launch_gemm_centre(x, c_in, wpacked, c_out, taps,
-                               m->rowbase.as<int32_t>(), m->n, part, y,
-                               (flags & SMC_FWD_OUT_F32) != 0, (flags & SMC_FWD_RELU) != 0,
-                               m->n_cu, s));
+    if (m->strided) {
+        // every tap went to the slab: each output row is its slab run's sum
+        SMC_HIP(launch_slab_sum(part, m->rowbase.as<int32_t>(), m->n, c_out, y,
+                                (flags & SMC_FWD_OUT_F32) != 0, (flags & SMC_FWD_RELU) != 0,
+                                m->n_cu, s));
+    } else {
+        SMC_HIP(launch_gemm_centre(x, c_in, wpacked, c_out, taps,
+                                   m->rowbase.as<int32_t>(), m->n, part, y,
+                                   (flags & SMC_FWD_OUT_F32) != 0, (flags & SMC_FWD_RELU) != 0,
+                                   m->n_cu, s));
+    }
     t_f.finish();
     return SMC_OK;
 }

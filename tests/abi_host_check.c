@@ -59,6 +59,8 @@ int main(void) {
     /* a handle never built */
     EXPECT(smc_map_info(h, &info), SMC_ERR_STATE);
     EXPECT(smc_map_info(h, NULL), SMC_ERR_ARG);
+    EXPECT(smc_map_rows(NULL, NULL, NULL), SMC_ERR_ARG);
+    EXPECT(smc_map_rows(h, NULL, NULL), SMC_ERR_STATE);
     EXPECT(smc_map_sync(h), SMC_ERR_STATE);
     EXPECT(smc_map_export(h, NULL, NULL, NULL, NULL, NULL, NULL), SMC_ERR_STATE);
     EXPECT(smc_map_export_out_coords(h, NULL), SMC_ERR_STATE);

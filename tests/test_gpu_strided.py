@@ -3,9 +3,11 @@
 "Sparse convolution in FP32" (DriveRT), section "Calibrated bit order": the
 strided layers change the coordinate set and run as mask-sorted tiles. The
 reading (kernel 3, stride 2, padding 1, outputs ordered by (b, x, y, z)) is
-the oracle's build_strided_map. Output coordinates, neighbour table, masks
-and mask order must match bit for bit on both routes; outputs exactly with
-integer inputs, within the bf16 / float32 tolerances otherwise.
+the oracle's build_strided_map. Output coordinates, neighbour table, masks,
+mask order and the output rows' pair lists (the centre a tap like the others)
+must match bit for bit on both routes; outputs of both forward algorithms
+(pair lists and mask tiles) exactly with integer inputs, within the bf16 /
+float32 tolerances otherwise.
 """
 import numpy as np
 import pytest
@@ -92,30 +94,34 @@ def test_strided_map_workloads(name):
     check_map(got2, want, name + " sorted")
 
 
-def strided_forward(coords, shape, xb, wb, relu=False, out_f32=False, route="auto"):
-    m = smc.KernelMap().build_strided(to_dev_i32(coords), spatial_shape=shape, route=route)
-    y = m.forward(to_dev_bf16(xb), smc.pack_weights(to_dev_bf16(wb)), relu=relu, out_f32=out_f32)
+def strided_forward(coords, shape, xb, wb, relu=False, out_f32=False, route="auto", algo="pairs"):
+    m = smc.KernelMap().build_strided(to_dev_i32(coords), spatial_shape=shape, route=route,
+                                      pairs=algo == "pairs", sort=algo == "mask_tiles")
+    y = m.forward(to_dev_bf16(xb), smc.pack_weights(to_dev_bf16(wb)), relu=relu, out_f32=out_f32,
+                  algo=algo)
     out = y.cpu().numpy() if out_f32 else bf16_bits_of(y)
     m.close()
     return out
 
 
+@pytest.mark.parametrize("algo", ["pairs", "mask_tiles"])
 @pytest.mark.parametrize("route", ["dense", "sorted"])
-@pytest.mark.parametrize("ci,co", [(16, 16), (64, 48), (200, 136), (1, 1), (128, 128)])
-def test_strided_layer_integer_exact(ci, co, route):
+@pytest.mark.parametrize("ci,co", [(16, 16), (64, 48), (200, 136), (1, 1), (128, 128), (520, 64)])
+def test_strided_layer_integer_exact(ci, co, route, algo):
     coords = random_cells((30, 30, 30), 4000, 11)
-    print(f"strided layer {ci}x{co} {route}", flush=True)
+    print(f"strided layer {ci}x{co} {route} {algo}", flush=True)
     xb = synth.int_features(4000, ci, 5)
     wb = synth.int_weights(ci, co, 5)
     r = so.strided_conv(coords, (30, 30, 30), xb, wb)
-    acc = strided_forward(coords, (30, 30, 30), xb, wb, out_f32=True, route=route)
+    acc = strided_forward(coords, (30, 30, 30), xb, wb, out_f32=True, route=route, algo=algo)
     assert np.array_equal(acc.astype(np.float64), r["acc"])
-    y = strided_forward(coords, (30, 30, 30), xb, wb, relu=True, route=route)
+    y = strided_forward(coords, (30, 30, 30), xb, wb, relu=True, route=route, algo=algo)
     assert np.array_equal(so.bf16_bits_to_f64(y), np.maximum(so.round_to_bf16(r["acc"]), 0.0))
 
 
+@pytest.mark.parametrize("algo", ["pairs", "mask_tiles"])
 @pytest.mark.parametrize("name", ["lidar", "deep"])
-def test_strided_layer_workloads(name):
+def test_strided_layer_workloads(name, algo):
     w = synth.workload(name)
     coords = synth.make_coords(w)
     c = w.channels
@@ -125,11 +131,58 @@ def test_strided_layer_workloads(name):
     x, wt = so.bf16_bits_to_f64(xb), so.bf16_bits_to_f64(wb)
     s_abs = so.conv_accumulate(np.abs(x), np.abs(wt), r["pair_in"], r["pair_out"], r["tap_off"],
                                len(r["out_coords"]))
-    print(f"strided layer {name}: {w.n} -> {len(r['out_coords'])} rows", flush=True)
-    y = strided_forward(coords, w.grid, xb, wb)
+    print(f"strided layer {name}: {w.n} -> {len(r['out_coords'])} rows, {algo}", flush=True)
+    y = strided_forward(coords, w.grid, xb, wb, algo=algo)
     check_bf16_output(y, r["acc"], name, abs_ref=s_abs, n_terms=27 * c)
-    acc = strided_forward(coords, w.grid, xb, wb, out_f32=True)
+    acc = strided_forward(coords, w.grid, xb, wb, out_f32=True, algo=algo)
     check_f32_acc(acc, r["acc"], name, abs_ref=s_abs, n_terms=27 * c)
+
+
+@pytest.mark.parametrize("route", ["dense", "sorted"])
+@pytest.mark.parametrize("case", ["small", "ragged", "lidar"])
+def test_strided_pair_lists(case, route):
+    """The output rows' pair lists, the centre tap (input at 2 o) a tap like
+    the others, bit for bit against the oracle's compaction of its table."""
+    if case == "lidar":
+        w = synth.workload("lidar")
+        coords, shape = synth.make_coords(w), w.grid
+    elif case == "ragged":
+        coords, shape = random_cells((31, 17, 40), 2500, 6), (31, 17, 40)
+    else:
+        coords, shape = random_cells((9, 7, 5), 120, 3), (9, 7, 5)
+    print(f"strided pair lists {case} {route}", flush=True)
+    want = oracle_strided(coords, shape)
+    pin, pout, toff = so.compact_pairs(want["nbr"], want["mask"])
+    m = smc.KernelMap().build_strided(to_dev_i32(coords), spatial_shape=shape, route=route,
+                                      sort=False)
+    ex = m.export(perm=False)
+    m.close()
+    assert np.array_equal(ex["tap_off"], toff)
+    assert np.array_equal(ex["pair_in"], pin) and np.array_equal(ex["pair_out"], pout)
+    assert np.array_equal(ex["nbr"], want["nbr"]) and np.array_equal(ex["mask"], want["mask"])
+
+
+def test_strided_build_without_pairs_or_sort():
+    """A pairs-only map refuses mask tiles; a sort-only map runs mask tiles
+    whatever the algorithm asked for (a strided map without pair lists has
+    only them); both give the same exact integers."""
+    coords = random_cells((20, 20, 20), 1500, 21)
+    xb, wb = synth.int_features(1500, 32, 2), synth.int_weights(32, 24, 3)
+    r = so.strided_conv(coords, (20, 20, 20), xb, wb)
+    x, wp = to_dev_bf16(xb), smc.pack_weights(to_dev_bf16(wb))
+    only_pairs = smc.KernelMap().build_strided(to_dev_i32(coords), spatial_shape=(20, 20, 20),
+                                               sort=False)
+    only_sort = smc.KernelMap().build_strided(to_dev_i32(coords), spatial_shape=(20, 20, 20),
+                                              pairs=False)
+    with pytest.raises(smc.SmconvError):
+        only_pairs.forward(x, wp, algo="mask_tiles")
+    a = only_pairs.forward(x, wp, out_f32=True).cpu().numpy()
+    b = only_sort.forward(x, wp, out_f32=True, algo="mask_tiles").cpu().numpy()
+    c = only_sort.forward(x, wp, out_f32=True, algo="pairs").cpu().numpy()
+    assert np.array_equal(a.astype(np.float64), r["acc"]) and np.array_equal(b, a)
+    assert np.array_equal(c, b)
+    only_pairs.close()
+    only_sort.close()
 
 
 def test_strided_errors_and_handle_reuse():
