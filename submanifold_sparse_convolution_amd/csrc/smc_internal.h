@@ -184,7 +184,7 @@ int64_t unique_blocks(int64_t n_c);
 // and left zero): coords -> output coords [M, 4] and query points [M, 4] in
 // (b, x, y, z) order, st->n_out = M; counts: out_bitmap_blocks(words) words of
 // scratch.
-constexpr int64_t kOutBitmapWords = (int64_t)1 << 22;   // 16 MiB: larger grids sort candidates
+constexpr int64_t kOutBitmapWords = (int64_t)1 << 25;   // 128 MiB: larger grids sort candidates
 int64_t out_bitmap_words(const StrideGeom& sg, int batch);
 int64_t out_bitmap_blocks(int64_t words);
 hipError_t launch_stride_bitmap(const int32_t* coords, int64_t n, const Geom& g,

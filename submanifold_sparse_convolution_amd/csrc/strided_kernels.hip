@@ -9,7 +9,7 @@
 // taps. Output rows are ordered by (b, x, y, z).
 //
 // Output cells, two routes chosen by the size of the output grid:
-//  * at most 2^27 cells (kOutBitmapWords words of one bit per cell, in
+//  * at most 2^30 cells (kOutBitmapWords words of one bit per cell, in
 //    (b, x, y, z) order): every input sets the bits of the (at most 8) output
 //    cells it feeds; per-block popcounts of the bitmap words are scanned once;
 //    each block writes its set bits' cells in bit order, so in (b, x, y, z)
@@ -287,18 +287,20 @@ __global__ __launch_bounds__(kUThreads) void k_bits_write(uint32_t* __restrict__
     uint32_t pos = offs[blockIdx.x] + inc - c;
     for (int q = 0; q < w; ++q) pos += s_w[q];
     const int r = (sg.ksize - 1) / 2;
+    // (the bitmap route covers fewer than 2^32 cells: 32-bit cell arithmetic)
+    const uint32_t ez = (uint32_t)sg.oext[2], ey = (uint32_t)sg.oext[1], ex = (uint32_t)sg.oext[0];
 #pragma unroll
     for (int j = 0; j < kBWords; ++j) {
         if (base + j >= words) break;
         if (v[j]) obits[base + j] = 0u;
         for (uint32_t bits = v[j]; bits; bits &= bits - 1) {
-            int64_t L = ((base + j) << 5) + __builtin_ctz(bits);
-            const int z = (int)(L % sg.oext[2]);
-            L /= sg.oext[2];
-            const int y = (int)(L % sg.oext[1]);
-            L /= sg.oext[1];
-            const int x = (int)(L % sg.oext[0]);
-            const int b = (int)(L / sg.oext[0]);
+            uint32_t L = ((uint32_t)(base + j) << 5) + (uint32_t)__builtin_ctz(bits);
+            const int z = (int)(L % ez);
+            L /= ez;
+            const int y = (int)(L % ey);
+            L /= ey;
+            const int x = (int)(L % ex);
+            const int b = (int)(L / ex);
             int32_t* oc = ocoords + (int64_t)pos * 4;
             oc[0] = b;
             oc[1] = x;

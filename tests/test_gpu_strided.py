@@ -81,9 +81,9 @@ def test_strided_batches_derived_shape_ncols3(route):
 
 @pytest.mark.parametrize("name", ["lidar", "deep", "wide"])
 def test_strided_map_workloads(name):
-    """lidar and deep have output grids of at most 2^27 cells (their output
-    cells come from a bitmap); wide's (1048 x 1048 x 348) takes the candidate
-    sort over 760k keys (reduce-then-scan passes)."""
+    """Output grids of at most 2^30 cells take the output bitmap: lidar and
+    deep (small), wide (1048 x 1048 x 348 = 382M cells, a 48 MB bitmap). The
+    candidate sort of larger grids is covered by the 64-bit-key test below."""
     w = synth.workload(name)
     coords = synth.make_coords(w)
     print(f"strided map {name} n={w.n}", flush=True)
@@ -222,6 +222,16 @@ def test_strided_errors_and_handle_reuse():
                             spatial_shape=(8, 8, 8))
     assert empty.n == 0
     m.close()
+
+
+def test_strided_candidate_sort_route():
+    """An output grid above 2^30 cells (1050 x 1050 x 1000): output cells from
+    the candidate sort (480k keys), on both routes."""
+    coords = synth.ground_box_coords(60000, (2100, 2100, 2000), seed=7, n_boxes=60)
+    print(f"strided candidate sort n={len(coords)}", flush=True)
+    want = oracle_strided(coords, (2100, 2100, 2000))
+    check_map(gpu_strided(coords, (2100, 2100, 2000)), want, "candidates")
+    check_map(gpu_strided(coords, (2100, 2100, 2000), route="sorted"), want, "candidates sorted")
 
 
 def test_strided_sorted_64bit_keys():
