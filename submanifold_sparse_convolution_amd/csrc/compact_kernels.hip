@@ -298,7 +298,9 @@ struct CompactLds {
 // publishes the totals. chunk_pre[bid][k] receives the pairs of tap k (k <
 // kTaps) and the slab rows (k = kTaps) in earlier chunks. dense_centre: the
 // centre tap pairs every row with itself and gets no slab rows (submanifold
-// maps); otherwise it is a tap like the others (strided maps). With nbr_out, the chunk's neighbour rows are stored
+// maps); otherwise it is a tap like the others (strided maps), and the only
+// pair of a row gets pair_slot -2 - row instead of a slab row: its product is
+// the row's output. With nbr_out, the chunk's neighbour rows are stored
 // there (coalesced) between publishing the counts and the look-back, where
 // the block would otherwise wait. Starts and ends with all threads in step.
 __device__ __forceinline__ void compact_chunk(CompactLds& L, uint32_t m, uint32_t bid, int64_t n,
@@ -318,9 +320,12 @@ __device__ __forceinline__ void compact_chunk(CompactLds& L, uint32_t m, uint32_
     const int64_t base0 = (int64_t)bid * kCChunk;
     const int64_t row = base0 + tid;
     // slab rows of the row: its off-centre pairs, or with a sparse centre (a
-    // strided map, whose output o need not be an input) every pair
+    // strided map, whose output o need not be an input) every pair of a row
+    // with two or more; a row with one pair has none (the GEMM writes its
+    // output directly)
     const uint32_t slab_taps = dense_centre ? ~(1u << kCentre) : ~0u;
-    const uint32_t deg = (uint32_t)__popc(m & slab_taps);
+    const uint32_t pop = (uint32_t)__popc(m & slab_taps);
+    const uint32_t deg = dense_centre || pop > 1u ? pop : 0u;
     // per-wave count of each tap (lane k keeps tap k) and of slab rows (lane kTaps),
     // over the taps some row of the wave has (the wave's OR of masks)
     const uint32_t uni = wave_or(m);
@@ -438,9 +443,12 @@ __device__ __forceinline__ void compact_chunk(CompactLds& L, uint32_t m, uint32_
         if (pos >= (int64_t)k * cap + cap) continue;          // only after a stalled wait
         const uint32_t mr = L.m[lr];
         const bool self = dense_centre && k == kCentre;
+        const bool direct = !dense_centre && __popc(mr) == 1;    // the row's only pair
         pair_in[pos] = self ? (int32_t)(base0 + lr) : L.nb[lr * kTaps + k];
         pair_out[pos] = (int32_t)(base0 + lr);
-        pair_slot[pos] = self ? -1 : (int32_t)(L.rb[lr] + __popc(mr & ((1u << k) - 1u) & slab_taps));
+        pair_slot[pos] = self     ? -1
+                         : direct ? -2 - (int32_t)(base0 + lr)
+                                  : (int32_t)(L.rb[lr] + __popc(mr & ((1u << k) - 1u) & slab_taps));
     }
 }
 

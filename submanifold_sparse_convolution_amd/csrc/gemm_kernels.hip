@@ -206,6 +206,29 @@ __device__ __forceinline__ void store_f32(float* __restrict__ dst, int col0, int
     }
 }
 
+// One pair's product row: to its slab row (slot >= 0); for the only pair of a
+// strided map's output row (slot = -2 - row) straight to that row's output,
+// as the sum the slab would have given (0 + product), rounded to bf16 or kept
+// in float (ymode bit 0), with the optional ReLU (bit 1); slot -1: none.
+template <int NBW>
+__device__ __forceinline__ void pair_row_out(float* __restrict__ part, void* __restrict__ yv,
+                                             int ymode, int32_t slot, int col0, int c_out,
+                                             const float (&v)[NBW]) {
+    if (slot >= 0) {
+        store_f32<NBW>(part + (int64_t)slot * c_out + col0, col0, c_out, v);
+        return;
+    }
+    if (slot == -1) return;
+    const int64_t row = -2 - (int64_t)slot;
+    float o[NBW];
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) o[nb] = 0.f + v[nb];
+    if (ymode & 1)
+        store_row<NBW, true>(yv, row, c_out, col0, o, ymode >> 1);
+    else
+        store_row<NBW, false>(yv, row, c_out, col0, o, ymode >> 1);
+}
+
 // Tile table of the taps, tiles of kRows pairs: on return s_first[k] is tap
 // k's first tile (s_first[taps]: the tile count) and s_cnt[k] its pairs (the
 // centre: none when skip_centre, i.e. when the centre is a dense GEMM of its
@@ -248,7 +271,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_gemm_nc(
     const uint16_t* __restrict__ x, int c_in, int steps, const u32x4* __restrict__ wp, int n_wt,
     int c_out, int taps, const int32_t* __restrict__ pair_in,
     const int32_t* __restrict__ pair_slot, const MapState* __restrict__ st, int64_t cap, int64_t n,
-    float* __restrict__ part, int skip_centre) {
+    float* __restrict__ part, int skip_centre, void* __restrict__ yv, int ymode) {
     constexpr int kRows = 64 * MW;                 // pairs per tile
     extern __shared__ u32x4 s_b[];
     __shared__ int32_t s_first[kMaxTaps + 1];     // first tile of each tap (centre: none)
@@ -293,11 +316,11 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_gemm_nc(
             const int slots[4] = {ps[m].x, ps[m].y, ps[m].z, ps[m].w};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                if (j0 + m * 16 + 4 * g + j >= cnt || slots[j] < 0) continue;
+                if (j0 + m * 16 + 4 * g + j >= cnt || slots[j] == -1) continue;
                 float v[NBW];
 #pragma unroll
                 for (int nb = 0; nb < NBW; ++nb) v[nb] = c[m][nb][j];
-                store_f32<NBW>(part + (int64_t)slots[j] * c_out + col0, col0, c_out, v);
+                pair_row_out<NBW>(part, yv, ymode, slots[j], col0, c_out, v);
             }
         }
     }
@@ -509,7 +532,8 @@ __global__ __launch_bounds__(kGemmThreads, (STREAM && MW == 2) ? 1 : (STREAM ? 2
 // Output rows of a map whose centre tap is a tap like the others (strided
 // maps): row i is the sum of its slab rows rowbase[i] .. rowbase[i+1] - 1 in
 // order, rounded to bf16 (to nearest, ties to even) or kept in float, with the
-// optional ReLU. Thread t takes four columns (VEC4, c_out a multiple of 4) or
+// optional ReLU. A row with no slab rows had a single pair, whose product the
+// off-centre GEMM already wrote as the row's output. Thread t takes four columns (VEC4, c_out a multiple of 4) or
 // one column of one row; a row's threads read each slab row contiguously.
 template <bool VEC4, bool OUT_F32>
 __global__ __launch_bounds__(kBlock) void k_slab_sum(const float* __restrict__ part,
@@ -522,6 +546,7 @@ __global__ __launch_bounds__(kBlock) void k_slab_sum(const float* __restrict__ p
         const int64_t row = t / per;
         const int col = (int)(t - row * per) * (VEC4 ? 4 : 1);
         const int32_t e0 = rowbase[row], e1 = rowbase[row + 1];
+        if (e1 <= e0) continue;                       // one pair: the GEMM wrote the row
         float v[4] = {0.f, 0.f, 0.f, 0.f};
         for (int32_t e = e0; e < e1; ++e) {
             const float* p = part + (int64_t)e * c_out + col;
@@ -640,7 +665,7 @@ __global__ __launch_bounds__(kBigThreads, 2) void k_gemm_nc_big(
     const uint16_t* __restrict__ x, int c_in, int steps, const u32x4* __restrict__ wp, int n_wt,
     int c_out, int taps, const int32_t* __restrict__ pair_in,
     const int32_t* __restrict__ pair_slot, const MapState* __restrict__ st, int64_t cap, int64_t n,
-    float* __restrict__ part, int skip_centre) {
+    float* __restrict__ part, int skip_centre, void* __restrict__ yv, int ymode) {
     constexpr int kRows = kBigWaves * 16;          // pairs per item
     extern __shared__ u32x4 s_b[];
     __shared__ int32_t s_first[kMaxTaps + 1];
@@ -682,11 +707,11 @@ __global__ __launch_bounds__(kBigThreads, 2) void k_gemm_nc_big(
         const int slots[4] = {ps.x, ps.y, ps.z, ps.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            if (j0 + 4 * g + j >= cnt || slots[j] < 0) continue;
+            if (j0 + 4 * g + j >= cnt || slots[j] == -1) continue;
             float v[NBW];
 #pragma unroll
             for (int nb = 0; nb < NBW; ++nb) v[nb] = c[nb][j];
-            store_f32<NBW>(part + (int64_t)slots[j] * c_out + col0, col0, c_out, v);
+            pair_row_out<NBW>(part, yv, ymode, slots[j], col0, c_out, v);
         }
     }
 }
@@ -801,27 +826,29 @@ bool lds_ok(K kernel, size_t bytes) {
 template <int NBW, int MW, bool VEC, bool STREAM>
 void launch_nc_t(dim3 grid, hipStream_t s, const uint16_t* x, int c_in, int steps, const u32x4* wp,
                  int n_wt, int c_out, int taps, const int32_t* pi, const int32_t* ps,
-                 const MapState* st, int64_t cap, int64_t n, float* part, int sc) {
+                 const MapState* st, int64_t cap, int64_t n, float* part, int sc, void* y,
+                 int ym) {
     constexpr size_t lds = gemm_lds_bytes<NBW, STREAM>();
     static const bool ok = lds_ok(k_gemm_nc<NBW, MW, VEC, STREAM>, lds);
     (void)ok;
     launch(k_gemm_nc<NBW, MW, VEC, STREAM>, grid, kGemmThreads, lds, s, x, c_in, steps, wp, n_wt,
-           c_out, taps, pi, ps, st, cap, n, part, sc);
+           c_out, taps, pi, ps, st, cap, n, part, sc, y, ym);
 }
 
 template <int NBW>
 void launch_nc(dim3 grid, hipStream_t s, int mw, const uint16_t* x, int c_in, int steps,
                const u32x4* wp, int n_wt, int c_out, int taps, const int32_t* pi,
-               const int32_t* ps, const MapState* st, int64_t cap, int64_t n, float* part, int sc) {
+               const int32_t* ps, const MapState* st, int64_t cap, int64_t n, float* part, int sc,
+               void* y, int ym) {
     const bool vec = (c_in & 7) == 0;
     if (mw == 2)                                   // mw_nc_for: streamed, 16-byte row loads
-        launch_nc_t<NBW, 2, true, true>(grid, s, x, c_in, steps, wp, n_wt, c_out, taps, pi, ps, st, cap, n, part, sc);
+        launch_nc_t<NBW, 2, true, true>(grid, s, x, c_in, steps, wp, n_wt, c_out, taps, pi, ps, st, cap, n, part, sc, y, ym);
     else if (steps > kChunk)
-        launch_nc_t<NBW, 1, false, true>(grid, s, x, c_in, steps, wp, n_wt, c_out, taps, pi, ps, st, cap, n, part, sc);
+        launch_nc_t<NBW, 1, false, true>(grid, s, x, c_in, steps, wp, n_wt, c_out, taps, pi, ps, st, cap, n, part, sc, y, ym);
     else if (vec)
-        launch_nc_t<NBW, 1, true, false>(grid, s, x, c_in, steps, wp, n_wt, c_out, taps, pi, ps, st, cap, n, part, sc);
+        launch_nc_t<NBW, 1, true, false>(grid, s, x, c_in, steps, wp, n_wt, c_out, taps, pi, ps, st, cap, n, part, sc, y, ym);
     else
-        launch_nc_t<NBW, 1, false, false>(grid, s, x, c_in, steps, wp, n_wt, c_out, taps, pi, ps, st, cap, n, part, sc);
+        launch_nc_t<NBW, 1, false, false>(grid, s, x, c_in, steps, wp, n_wt, c_out, taps, pi, ps, st, cap, n, part, sc, y, ym);
 }
 
 template <int NBW, int MW, bool OUT_F32, bool VEC, bool STREAM>
@@ -865,11 +892,11 @@ template <int NBW>
 void launch_nc_big(dim3 grid, size_t lds, hipStream_t s, const uint16_t* x, int c_in, int steps,
                    const u32x4* wp, int n_wt, int c_out, int taps, const int32_t* pi,
                    const int32_t* ps, const MapState* st, int64_t cap, int64_t n, float* part,
-                   int sc) {
+                   int sc, void* y, int ym) {
     static const bool ok = lds_ok(k_gemm_nc_big<NBW>, (size_t)kBigMaxSteps * 8 * 1024);
     (void)ok;
     launch(k_gemm_nc_big<NBW>, grid, kBigThreads, lds, s, x, c_in, steps, wp, n_wt, c_out, taps,
-           pi, ps, st, cap, n, part, sc);
+           pi, ps, st, cap, n, part, sc, y, ym);
 }
 
 template <int NBW>
@@ -923,8 +950,9 @@ hipError_t launch_weight_pack(const uint16_t* w, int taps, int c_in, int c_out, 
 hipError_t launch_gemm_nc(const uint16_t* x, int c_in, const void* wpacked, int c_out, int taps,
                           const int32_t* pair_in, const int32_t* pair_slot, const MapState* st,
                           int64_t cap, int64_t n, int n_cu, float* part, hipStream_t s,
-                          bool skip_centre) {
+                          bool skip_centre, void* y, bool out_f32, bool relu) {
     const int sc = skip_centre ? 1 : 0;
+    const int ym = (out_f32 ? 1 : 0) | (relu ? 2 : 0);
     const int steps = (c_in + 31) / 32;
     const int nbw = nbw_for(c_out);
     const int n_wt = (c_out + 16 * nbw - 1) / (16 * nbw);
@@ -935,10 +963,10 @@ hipError_t launch_gemm_nc(const uint16_t* x, int c_in, const void* wpacked, int 
         const size_t lds = (size_t)steps * nbw * 64 * 16;
         const u32x4* wp = (const u32x4*)wpacked;
         switch (nbw) {
-            case 1: launch_nc_big<1>(grid, lds, s, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part, sc); break;
-            case 2: launch_nc_big<2>(grid, lds, s, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part, sc); break;
-            case 4: launch_nc_big<4>(grid, lds, s, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part, sc); break;
-            default: launch_nc_big<8>(grid, lds, s, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part, sc); break;
+            case 1: launch_nc_big<1>(grid, lds, s, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part, sc, y, ym); break;
+            case 2: launch_nc_big<2>(grid, lds, s, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part, sc, y, ym); break;
+            case 4: launch_nc_big<4>(grid, lds, s, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part, sc, y, ym); break;
+            default: launch_nc_big<8>(grid, lds, s, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part, sc, y, ym); break;
         }
         return hipGetLastError();
     }
@@ -950,10 +978,10 @@ hipError_t launch_gemm_nc(const uint16_t* x, int c_in, const void* wpacked, int 
     dim3 grid((unsigned)gx, (unsigned)n_wt);
     const u32x4* wp = (const u32x4*)wpacked;
     switch (nbw) {
-        case 1: launch_nc<1>(grid, s, mw, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part, sc); break;
-        case 2: launch_nc<2>(grid, s, mw, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part, sc); break;
-        case 4: launch_nc<4>(grid, s, mw, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part, sc); break;
-        default: launch_nc<8>(grid, s, mw, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part, sc); break;
+        case 1: launch_nc<1>(grid, s, mw, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part, sc, y, ym); break;
+        case 2: launch_nc<2>(grid, s, mw, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part, sc, y, ym); break;
+        case 4: launch_nc<4>(grid, s, mw, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part, sc, y, ym); break;
+        default: launch_nc<8>(grid, s, mw, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part, sc, y, ym); break;
     }
     return hipGetLastError();
 }

@@ -281,12 +281,16 @@ hipError_t launch_weight_pack(const uint16_t* w, int taps, int c_in, int c_out, 
 // n: input rows (bounds the gathered rows). skip_centre: the centre tap runs
 // as a dense GEMM of its own (k_gemm_centre); false for strided maps, whose
 // centre tap is sparse like the others.
+// y, out_f32, relu: the output of pairs marked as their row's only one
+// (pair_slot -2 - row, strided maps), written here instead of a slab row.
 hipError_t launch_gemm_nc(const uint16_t* x, int c_in, const void* wpacked, int c_out, int taps,
                           const int32_t* pair_in, const int32_t* pair_slot, const MapState* st,
                           int64_t cap, int64_t n, int n_cu, float* part, hipStream_t s,
-                          bool skip_centre = true);
+                          bool skip_centre = true, void* y = nullptr, bool out_f32 = false,
+                          bool relu = false);
 // Output rows of a strided map: y[i] = the sum of slab rows rowbase[i] ..
-// rowbase[i+1] - 1 in order (bf16 rounded or float, optional ReLU), m rows.
+// rowbase[i+1] - 1 in order (bf16 rounded or float, optional ReLU), m rows;
+// rows without slab rows (one pair: written by the GEMM) are left alone.
 hipError_t launch_slab_sum(const float* part, const int32_t* rowbase, int64_t m, int c_out,
                            void* y, bool out_f32, bool relu, int n_cu, hipStream_t s);
 // rowbase: [n + 1], row i's slab rows are rowbase[i] .. rowbase[i+1] - 1.

@@ -1209,7 +1209,8 @@ static int conv_forward(smc_map* m, const uint16_t* x, int c_in, const void* wpa
     StageTimer t_g(m, SMC_STAGE_GEMM, s, false, fixed == nullptr);
     SMC_HIP(launch_gemm_nc(x, c_in, wpacked, c_out, taps, m->pair_in.as<int32_t>(),
                            m->pair_slot.as<int32_t>(), m->state.as<MapState>() + m->slot, m->cap,
-                           m->n_in, m->n_cu, part, s, !m->strided));
+                           m->n_in, m->n_cu, part, s, !m->strided, y,
+                           (flags & SMC_FWD_OUT_F32) != 0, (flags & SMC_FWD_RELU) != 0));
     t_g.finish();
     StageTimer t_f(m, SMC_STAGE_CENTRE, s, false, fixed == nullptr);
     if (m->strided) {
