@@ -46,6 +46,11 @@ bases) count zero.
   strided layers (M output rows): k_gemm_nc 2 N C_in + 2 T C_in C_out + 8 P (every tap),
                     k_slab_sum 2 M C_out
   sort passes, k_weight_pack (outside the step), fills: 0
+A stage of several kernels (a strided map's neighbour stage: the input grid or
+sorted keys, the output cells through a bitmap of the output grid or, above
+2^30 cells, a sort of candidate keys, then the lookup) is listed with its
+kernels and time but has no byte model and is never the roofline's kernel;
+"output_cells_route" says which output route a strided build took.
 
   --summarize-pmc FETCH_DIR WRITE_DIR   turn two `rocprofv3 --pmc FETCH_SIZE`
       / `--pmc WRITE_SIZE` runs of this script (with --copy-probe-mb) into
@@ -63,6 +68,7 @@ import csv
 import glob
 import hashlib
 import json
+import math
 import os
 import statistics
 import sys
@@ -222,8 +228,23 @@ def rows_form(algo, kernel_size, c_in, c_out=None, strided=False):
             and not strided)
 
 
-def stage_kernels(stage, algo, route, kernel_size=3, strided=False, c_in=128):
-    """The kernels one execution of a stage launches (pair path unless stated)."""
+OUT_BITMAP_CELLS = 1 << 30      # strided output grids up to this many cells use the bitmap
+
+
+def strided_output_kernels(out_cells):
+    """The kernels that find a strided map's output cells: a bitmap of the output
+    grid (mark, count per block, scan, write) or, for a larger grid, a radix sort
+    of 8 candidate keys per input (candidates, sort passes, unique count, scan,
+    unique write)."""
+    if out_cells <= OUT_BITMAP_CELLS:
+        return ("k_stride_mark", "k_bits_count", "k_scan_counts", "k_bits_write")
+    return ("k_stride_candidates", "k_os_pass", "k_unique_count", "k_scan_counts",
+            "k_unique_write")
+
+
+def stage_kernels(stage, algo, route, kernel_size=3, strided=False, c_in=128, out_cells=0):
+    """The kernels one execution of a stage launches (pair path unless stated);
+    out_cells: a strided map's output grid cells (batch x extents)."""
     big = BIG_MIN_C <= c_in <= BIG_MAX_C and c_in % 8 == 0
     if stage == "gemm":
         if algo == "mask_tiles":
@@ -240,7 +261,10 @@ def stage_kernels(stage, algo, route, kernel_size=3, strided=False, c_in=128):
     fused = route == "dense" and algo != "mask_tiles" and kernel_size == 3 and not strided
     if stage == "neighbours":
         if strided:
-            return ("k_stride_outputs", "k_dense_lookup" if route == "dense" else "k_query_lookup")
+            inputs = ("k_dense_scatter",) if route == "dense" else ("k_make_keys", "k_os_pass",
+                                                                    "k_key_dups")
+            return inputs + strided_output_kernels(out_cells) + (
+                "k_dense_lookup" if route == "dense" else "k_query_lookup",)
         if route == "sorted":
             return ("k_make_keys", "k_os_pass", "k_sorted_lookup")
         if fused:
@@ -431,7 +455,8 @@ def stage_rows(r):
         us = r["stage_us"].get(st, 0.0)
         if us <= 0.0:
             continue
-        ks = stage_kernels(st, r["algo"], route, r["kernel_size"], r["strided"], c)
+        ks = stage_kernels(st, r["algo"], route, r["kernel_size"], r["strided"], c,
+                           out_cells=r["frames"] * math.prod(info["out_extent"]))
         row = dict(kernels=list(ks), us=us, per_step=r["stage_per_step"].get(st, 0.0))
         if len(ks) == 1:
             groups = info["n_groups"] if r["algo"] == "mask_tiles" else 1
@@ -500,6 +525,8 @@ def summary(r):
         out["step_hbm_frac"] = round(step_bytes / (r["ms_per_step"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 5)
     else:
         out["n_out"] = r["n_out"]
+        cells = r["frames"] * math.prod(info["out_extent"])
+        out["output_cells_route"] = "bitmap" if cells <= OUT_BITMAP_CELLS else "candidate_sort"
     if r["map_cold_us"] is not None:
         out["map_cold_us"] = round(r["map_cold_us"], 1)
         out["map_cold_note"] = ("first build on a fresh handle, host clock around a synchronous "
@@ -908,8 +935,8 @@ def main():
             rr = run_workload(cname, max(10, args.steps // 2), args.warmup, strided=True)
             e = summary(rr)
             line["strided"].append({k: e[k] for k in ("workload", "n", "n_out", "pairs", "route",
-                                                      "us_per_layer", "tflops_effective",
-                                                      "stages", "roofline")})
+                                                      "output_cells_route", "us_per_layer",
+                                                      "tflops_effective", "stages", "roofline")})
     if args.other_algo:
         line["other_algo"] = []
         for order2 in ORDERS:
