@@ -217,12 +217,19 @@ int smc_map_build(smc_map* map, const int32_t* coords, int64_t n, int ncols,
  * Arguments as smc_map_build; coordinates count from 0: with spatial_shape
  * NULL the grid is [0, max + 1) per axis, and a negative coordinate is
  * SMC_ERR_RANGE. kernel_size must be 3 and stride 2 (else
- * SMC_ERR_UNSUPPORTED); n <= 2^24. The output count is read back to the host
- * once inside the call (the caller needs it to size y); with SMC_BUILD_ASYNC
- * the lookups and the mask sort that follow are still only enqueued.
- * Steps: the input grid or sorted input keys as for smc_map_build; every
- * input's (at most 8) output cells as packed keys; one radix sort; unique
- * (count, scan, write); the 27-tap lookup around each query point; mask sort.
+ * SMC_ERR_UNSUPPORTED); n <= 2^24. The output count n (the caller needs it to
+ * size y) reaches the host once: with the mask order (no SMC_BUILD_NO_SORT)
+ * it is read back inside the call; a pair-list build without it sizes the
+ * lookup and the compaction by the bound 8 n_in, which read the count on the
+ * device, and the count is read on first use (smc_map_rows, smc_map_info,
+ * the forward), so the call waits for nothing. With SMC_BUILD_ASYNC the
+ * kernels after the count are only enqueued in either case.
+ * Steps: the input grid or sorted input keys as for smc_map_build; the output
+ * cells, through a bitmap of the output grid (count per block, scan, write
+ * in (b, x, y, z) order) or, above 2^30 output cells, by sorting every
+ * input's (at most 8) candidate output keys and keeping the distinct ones;
+ * the 27-tap lookup around each query point; the pair lists and/or the mask
+ * sort.
  */
 int smc_map_build_strided(smc_map* map, const int32_t* coords, int64_t n, int ncols,
                           const int32_t* spatial_shape, int batch_size, int kernel_size,
@@ -240,9 +247,10 @@ int smc_map_sync(smc_map* map);
 int smc_map_info(smc_map* map, smc_map_info_t* info);
 
 /* Output and input rows of the last build (host pointers, either may be
- * NULL), without waiting for it: both are known on the host when a build
- * returns (a strided build reads its output count during the call). For
- * callers that size y right after an asynchronous build. */
+ * NULL), without waiting for the build: the only wait is, after a strided
+ * pair-list build, for its output count (an event right after the output
+ * cells; the lookup and compaction go on behind it). For callers that size y
+ * right after an asynchronous build. */
 int smc_map_rows(smc_map* map, int64_t* n, int64_t* n_in);
 
 /*

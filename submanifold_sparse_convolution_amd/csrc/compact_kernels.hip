@@ -303,7 +303,7 @@ struct CompactLds {
 // the row's output. With nbr_out, the chunk's neighbour rows are stored
 // there (coalesced) between publishing the counts and the look-back, where
 // the block would otherwise wait. Starts and ends with all threads in step.
-__device__ __forceinline__ void compact_chunk(CompactLds& L, uint32_t m, uint32_t bid, int64_t n,
+__device__ __forceinline__ void compact_chunk(CompactLds& L, uint32_t m, uint32_t bid, uint32_t last, int64_t n,
                                               int64_t cap, int tile_m, MapState* st,
                                               int32_t* __restrict__ pair_in,
                                               int32_t* __restrict__ pair_out,
@@ -378,13 +378,13 @@ __device__ __forceinline__ void compact_chunk(CompactLds& L, uint32_t m, uint32_
         const uint32_t run = L.tot[k];
         const uint32_t prefix = L.pre[k];
         // per-chunk starts of every tap's pairs and of the slab rows (the last
-        // chunk also writes the totals as row gridDim.x), for row-range GEMMs
+        // chunk also writes the totals as row last + 1), for row-range GEMMs
         chunk_pre[(int64_t)bid * kCols + k] = (int32_t)prefix;
-        if (bid == gridDim.x - 1) chunk_pre[(int64_t)(bid + 1) * kCols + k] = (int32_t)(prefix + run);
+        if (bid == last) chunk_pre[(int64_t)(bid + 1) * kCols + k] = (int32_t)(prefix + run);
         if (bid > 0)
             __hip_atomic_store(&look[(int64_t)bid * kCols + k], lb_pack(epoch, kIncl, prefix + run),
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (bid == gridDim.x - 1) {
+        if (bid == last) {
             // the last chunk: prefix + run is the total of column k
             const uint32_t tot = prefix + run;
             if (k < kTaps) {
@@ -404,7 +404,7 @@ __device__ __forceinline__ void compact_chunk(CompactLds& L, uint32_t m, uint32_
         uint32_t all;
         const uint32_t loc = wave_excl_scan<9>(t, &all);
         if (k <= kTaps) L.loc[k] = loc;                           // lane kTaps: the chunk's pairs
-        if (bid == gridDim.x - 1) {               // the last chunk: pairs and padded tiles
+        if (bid == last) {               // the last chunk: pairs and padded tiles
             int32_t c = k < kTaps ? (int32_t)(L.pre[k] + t) : 0;
             int32_t padded = (c + tile_m - 1) / tile_m * tile_m;
 #pragma unroll
@@ -456,24 +456,25 @@ __device__ __forceinline__ void compact_chunk(CompactLds& L, uint32_t m, uint32_
 // [bid*kCChunk, +kCChunk) in row order, one per thread. The chunk's
 // neighbour rows (contiguous in the table) are read once, coalesced, into
 // LDS.
-__global__ __launch_bounds__(kCThreads) void k_compact(
-    const uint32_t* __restrict__ mask, const int32_t* __restrict__ nbr, int64_t n, int64_t cap,
-    int tile_m, MapState* st, int32_t* __restrict__ pair_in, int32_t* __restrict__ pair_out,
-    int32_t* __restrict__ pair_slot, int32_t* __restrict__ rowbase, int32_t* __restrict__ chunk_pre,
-    uint64_t* __restrict__ look, uint32_t* ticket, bool by_index, uint32_t epoch, uint32_t* status,
-    bool dense_centre) {
-    __shared__ CompactLds L;
+// One chunk of k_compact: rows [bid kCChunk, +kCChunk) of n, last = the last
+// chunk's index.
+__device__ __forceinline__ void compact_table_chunk(
+    CompactLds& L, uint32_t bid, uint32_t last, const uint32_t* __restrict__ mask,
+    const int32_t* __restrict__ nbr, int64_t n, int64_t cap, int tile_m, MapState* st,
+    int32_t* __restrict__ pair_in, int32_t* __restrict__ pair_out, int32_t* __restrict__ pair_slot,
+    int32_t* __restrict__ rowbase, int32_t* __restrict__ chunk_pre, uint64_t* __restrict__ look,
+    uint32_t epoch, uint32_t* status, bool dense_centre) {
     const int tid = threadIdx.x;
-    const uint32_t bid = chunk_of_block(by_index, ticket, &L.bid);
     const int64_t base0 = (int64_t)bid * kCChunk;
     const int64_t row = base0 + tid;
     // mask, neighbour rows (whole 16-byte words; the table is padded so the last word
     // of the last row is readable)
-    const uint32_t mv = mask[row < n ? row : n - 1];
+    const uint32_t mv = n > 0 ? mask[row < n ? row : n - 1] : 0u;
     int4 nv4[kCNbrPer];
     {
         const int4* src = reinterpret_cast<const int4*>(nbr + base0 * kTaps);
-        const int64_t q_last = (n * kTaps + 3) / 4 - 1 - base0 * kTaps / 4;   // last readable word
+        int64_t q_last = (n * kTaps + 3) / 4 - 1 - base0 * kTaps / 4;         // last readable word
+        if (q_last < 0) q_last = 0;               // no rows: the table's first word (allocated)
 #pragma unroll
         for (int j = 0; j < kCNbrPer; ++j) {
             const int64_t q = tid + j * kCThreads;
@@ -486,9 +487,39 @@ __global__ __launch_bounds__(kCThreads) void k_compact(
         const int q = tid + j * kCThreads;
         if (q < kCNbrVec) nb4[q] = nv4[j];
     }
-    compact_chunk(L, row < n ? mv : 0u, bid, n, cap, tile_m, st, pair_in, pair_out, pair_slot,
+    compact_chunk(L, row < n ? mv : 0u, bid, last, n, cap, tile_m, st, pair_in, pair_out, pair_slot,
                   rowbase, chunk_pre, look, epoch, status, nullptr, dense_centre);
-    if (!by_index && bid == gridDim.x - 1 && tid == 0) atomicExch(ticket, 0u);
+}
+
+// Compaction of a neighbour table in memory: one chunk per block. With n_dev
+// (a device row count; n is then only its bound, 8 inputs a row for a strided
+// map) the grid is at most the resident blocks and block b takes chunks b,
+// b + gridDim.x, ... up to the count's last chunk. A chunk's look-back waits
+// only on lower chunks, each held by a resident block that waits only on
+// lower ones again, so every wait ends; no ticket is taken (a ticket per
+// block, 800 to 1000 atomics on one word, cost 10 us).
+__global__ __launch_bounds__(kCThreads) void k_compact(
+    const uint32_t* __restrict__ mask, const int32_t* __restrict__ nbr, int64_t n, int64_t cap,
+    int tile_m, MapState* st, int32_t* __restrict__ pair_in, int32_t* __restrict__ pair_out,
+    int32_t* __restrict__ pair_slot, int32_t* __restrict__ rowbase, int32_t* __restrict__ chunk_pre,
+    uint64_t* __restrict__ look, uint32_t* ticket, bool by_index, uint32_t epoch, uint32_t* status,
+    bool dense_centre, const int32_t* __restrict__ n_dev) {
+    __shared__ CompactLds L;
+    if (n_dev) {
+        const int64_t nd = *n_dev;
+        if (nd < n) n = nd > 0 ? nd : 0;
+        const uint32_t last = n > 0 ? (uint32_t)((n + kCChunk - 1) / kCChunk - 1) : 0u;
+        for (uint32_t bid = blockIdx.x; bid <= last; bid += gridDim.x) {
+            compact_table_chunk(L, bid, last, mask, nbr, n, cap, tile_m, st, pair_in, pair_out,
+                                pair_slot, rowbase, chunk_pre, look, epoch, status, dense_centre);
+            __syncthreads();                      // the chunk's LDS reads done before the next
+        }
+        return;
+    }
+    const uint32_t bid = chunk_of_block(by_index, ticket, &L.bid);
+    compact_table_chunk(L, bid, gridDim.x - 1, mask, nbr, n, cap, tile_m, st, pair_in, pair_out,
+                        pair_slot, rowbase, chunk_pre, look, epoch, status, dense_centre);
+    if (!by_index && bid == gridDim.x - 1 && threadIdx.x == 0) atomicExch(ticket, 0u);
 }
 
 // Dense route: lookup and compaction in one kernel. Each thread looks up its
@@ -556,7 +587,7 @@ __global__ __launch_bounds__(kCThreads) void k_lookup_compact(
     }
     if (row < n) mask[row] = m;
     __syncthreads();
-    compact_chunk(L, m, bid, n, cap, tile_m, st, pair_in, pair_out, pair_slot, rowbase, chunk_pre,
+    compact_chunk(L, m, bid, gridDim.x - 1, n, cap, tile_m, st, pair_in, pair_out, pair_slot, rowbase, chunk_pre,
                   look, epoch, status, nbr, true, spin_limit, wait_xor);
     if (!by_index && bid == gridDim.x - 1 && tid == 0) atomicExch(ticket, 0u);
 }
@@ -761,23 +792,30 @@ size_t compact_look_bytes_k(int64_t n, int ksize) {
     return (size_t)compact_chunks(n) * (ksize == 5 ? kK5Cols : kTaps + 1) * 8;
 }
 
-// Whether `blocks` blocks of 256 threads of `kern` fit on the current device at
-// once (occupancy per CU times CUs, queried once per kernel and device).
-static bool fits_at_once(const void* kern, int slot, unsigned blocks) {
+// Blocks of 256 threads of `kern` resident at once on the current device
+// (occupancy per CU times CUs, queried once per kernel and device; 0 if the
+// query failed).
+static int64_t resident_blocks(const void* kern, int slot) {
     constexpr int kDevs = 64;
     static std::atomic<int64_t> cache[kDevs][3];
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) return false;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) return 0;
     int64_t cap = cache[dev][slot].load(std::memory_order_relaxed);
     if (cap == 0) {
         int per_cu = 0, n_cu = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kCThreads, 0) != hipSuccess ||
             hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            return false;
+            return 0;
         cap = (int64_t)per_cu * n_cu;
         cache[dev][slot].store(cap > 0 ? cap : -1, std::memory_order_relaxed);
     }
-    return (int64_t)blocks <= cap;
+    return cap > 0 ? cap : 0;
+}
+
+// Whether `blocks` blocks of `kern` fit on the current device at once.
+static bool fits_at_once(const void* kern, int slot, unsigned blocks) {
+    const int64_t cap = resident_blocks(kern, slot);
+    return cap > 0 && (int64_t)blocks <= cap;
 }
 
 static uint32_t next_epoch(SortWork& ws) {
@@ -790,18 +828,26 @@ hipError_t launch_compact(const uint32_t* mask, const int32_t* nbr, int64_t n, i
                           int64_t cap, int tile_m, MapState* st, int32_t* pair_in,
                           int32_t* pair_out, int32_t* pair_slot, int32_t* rowbase,
                           int32_t* chunk_pre, SortWork& ws, uint32_t* status, hipStream_t s,
-                          bool dense_centre) {
+                          bool dense_centre, const int32_t* n_dev) {
     const uint32_t epoch = next_epoch(ws);
     const unsigned blocks = (unsigned)compact_chunks(n);
     if (ksize == 5) {
+        if (n_dev) return hipErrorInvalidValue;   // (a device count comes with 3 x 3 x 3 maps only)
         const bool by_index = fits_at_once((const void*)k_compact5, 0, blocks);
         launch(k_compact5, blocks, kCThreads, 0, s, mask, nbr, n, cap, tile_m, st, pair_in,
                pair_out, pair_slot, rowbase, ws.look, ws.ticket, by_index, epoch, status);
+    } else if (n_dev) {
+        // chunks up to the device count, strided over at most the resident blocks
+        const int64_t res = resident_blocks((const void*)k_compact, 1);
+        const unsigned grid = res > 0 && res < (int64_t)blocks ? (unsigned)res : blocks;
+        launch(k_compact, grid, kCThreads, 0, s, mask, nbr, n, cap, tile_m, st, pair_in,
+               pair_out, pair_slot, rowbase, chunk_pre, ws.look, ws.ticket, false, epoch, status,
+               dense_centre, n_dev);
     } else {
         const bool by_index = fits_at_once((const void*)k_compact, 1, blocks);
         launch(k_compact, blocks, kCThreads, 0, s, mask, nbr, n, cap, tile_m, st, pair_in,
                pair_out, pair_slot, rowbase, chunk_pre, ws.look, ws.ticket, by_index, epoch, status,
-               dense_centre);
+               dense_centre, n_dev);
     }
     return hipGetLastError();
 }

@@ -150,8 +150,11 @@ hipError_t launch_dense_scatter(const int32_t* coords, int64_t n, const Geom& g,
                                 const NextRecord& next, const PrevCells& prev, hipStream_t s);
 hipError_t launch_clear_cells(const PrevCells& prev, hipStream_t s);
 // nbr [n, K^3]; mask [n] (K = 3) or [n, 4] words (K = 5): g.ksize decides.
+// n_dev (optional): a device row count read by the kernel; the rows are then
+// min(n, *n_dev) (n the bound the grid was sized by).
 hipError_t launch_dense_lookup(const int32_t* coords, int64_t n, const Geom& g, const int32_t* grid,
-                               const uint32_t* bits, int32_t* nbr, uint32_t* mask, hipStream_t s);
+                               const uint32_t* bits, int32_t* nbr, uint32_t* mask, hipStream_t s,
+                               const int32_t* n_dev = nullptr);
 // Keys of the sorted route, and the digit histograms of every pass of `plan`
 // added into hist (which must start at zero).
 hipError_t launch_make_keys(const int32_t* coords, int64_t n, const Geom& g, bool wide, void* keys,
@@ -205,7 +208,7 @@ hipError_t launch_key_dups(const void* keys, bool wide, int64_t n, MapState* st,
 // sorted route: the 27 taps around each query point from the sorted input keys
 hipError_t launch_query_lookup(const void* keys, const uint32_t* vals, int64_t n_in, const Geom& g,
                                bool wide, const int32_t* qcoords, int64_t m, int32_t* nbr,
-                               uint32_t* mask, hipStream_t s);
+                               uint32_t* mask, hipStream_t s, const int32_t* m_dev = nullptr);
 
 // ---- radix sort (radix_sort.hip) ----
 // Stable LSD sort of (key, value) pairs on the low passes*bits key bits, one
@@ -263,7 +266,7 @@ hipError_t launch_compact(const uint32_t* mask, const int32_t* nbr, int64_t n, i
                           int64_t cap, int tile_m, MapState* st, int32_t* pair_in,
                           int32_t* pair_out, int32_t* pair_slot, int32_t* rowbase,
                           int32_t* chunk_pre, SortWork& ws, uint32_t* status, hipStream_t s,
-                          bool dense_centre = true);
+                          bool dense_centre = true, const int32_t* n_dev = nullptr);
 // Dense route: neighbour lookup and compaction in one kernel (also writes nbr
 // and mask).
 hipError_t launch_lookup_compact(const int32_t* coords, int64_t n, const Geom& g,

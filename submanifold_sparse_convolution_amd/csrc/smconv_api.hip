@@ -135,6 +135,8 @@ struct smc_map {
     hipEvent_t done = nullptr;        // end of a synchronous build (system-scope fence)
     hipEvent_t done_nf = nullptr;     // end of an asynchronous build (no fence, see build_map)
     hipEvent_t done_last = nullptr;   // the one the last build recorded
+    hipEvent_t rows_ev = nullptr;     // a strided build's output count copied to the host
+    bool rows_pending = false;        // n is that build's bound until rows_ev is read
     MapState* host_state = nullptr;   // pinned
     bool built = false;
     bool pending = false;             // a build whose device checks are not read yet
@@ -244,6 +246,7 @@ int ensure_device(smc_map* m) {
         if (!m->done_nf)
             SMC_HIP(hipEventCreateWithFlags(&m->done_nf,
                                             hipEventDisableTiming | hipEventDisableSystemFence));
+        if (!m->rows_ev) SMC_HIP(hipEventCreateWithFlags(&m->rows_ev, hipEventDisableTiming));
         if (!m->host_state &&
             hipHostMalloc((void**)&m->host_state, sizeof(MapState), hipHostMallocDefault) !=
                 hipSuccess) {
@@ -276,7 +279,25 @@ int ensure_device(smc_map* m) {
 // do not wait for each other: a build recycles the record of the build before
 // it, carrying that record's status bits into the sticky word first, so the
 // checks of every build since the last wait are reported here.
+// A strided pair-list build sizes its lookup and compaction by a bound (8
+// candidates per input) and leaves its output count on the device; the count
+// reaches the host with an event of its own, read here on first use.
+int resolve_rows(smc_map* m) {
+    if (!m->rows_pending) return SMC_OK;
+    SMC_HIP(hipEventSynchronize(m->rows_ev));
+    m->rows_pending = false;
+    const int64_t c = m->host_state->n_out;
+    if (c < 0 || c > m->n) {
+        m->n = 0;
+        m->build_status = SMC_ERR_STATE;
+        return fail(SMC_ERR_STATE, "output count %lld", (long long)c);
+    }
+    m->n = c;
+    return SMC_OK;
+}
+
 int wait_build(smc_map* m) {
+    if (int rc = resolve_rows(m)) return rc;
     if (!m->pending) return SMC_OK;
     SMC_HIP(hipEventSynchronize(m->done_last));
     if (!m->state_copied) {
@@ -451,7 +472,8 @@ int smc_map_create(smc_map** out) {
 int smc_map_destroy(smc_map* m) {
     if (!m) return SMC_OK;
     // (a handle whose first build failed part-way holds some buffers with no device set)
-    const bool touched = m->device >= 0 || m->done || m->done_nf || m->host_state || m->state.p;
+    const bool touched =
+        m->device >= 0 || m->done || m->done_nf || m->rows_ev || m->host_state || m->state.p;
     if (touched) {
         int cur = 0;
         (void)hipGetDevice(&cur);
@@ -475,19 +497,22 @@ int smc_map_destroy(smc_map* m) {
         if (m->host_state) (void)hipHostFree(m->host_state);
         if (m->done) (void)hipEventDestroy(m->done);
         if (m->done_nf) (void)hipEventDestroy(m->done_nf);
+        if (m->rows_ev) (void)hipEventDestroy(m->rows_ev);
         (void)hipSetDevice(cur);
     }
     delete m;
     return SMC_OK;
 }
 
-// Strided map, output side: candidate output keys of every input, one radix
-// sort, unique (output coords + query points), and one read of the output
-// count (*rows). The input-side structure (grid or sorted keys) is built by
-// the caller.
+// Strided map, output side: the output cells (a bitmap of the output grid, or
+// for a larger grid candidate output keys of every input, one radix sort and
+// unique), as output coords + query points. *rows: the output count, read
+// back at once, or with defer the bound 8 n (the count stays on the device in
+// st->n_out for the kernels after, and reaches the host through rows_ev). The
+// input-side structure (grid or sorted keys) is built by the caller.
 static int strided_outputs(smc_map* m, const int32_t* coords, int64_t n, const Geom& g,
                            const StrideGeom& sg, MapState* st, uint32_t* status, hipStream_t s,
-                           int64_t* rows) {
+                           int64_t* rows, bool defer) {
     const int64_t n_cand = 8 * n;
     // a small output grid: its cells through a bitmap, no candidate sort
     const int64_t words = out_bitmap_words(sg, g.batch);
@@ -529,6 +554,11 @@ static int strided_outputs(smc_map* m, const int32_t* coords, int64_t n, const G
     int32_t count = 0;
     SMC_HIP(hipMemcpyAsync(&m->host_state->n_out, &st->n_out, sizeof(int32_t),
                            hipMemcpyDeviceToHost, s));
+    if (defer) {                                  // the count is read on first use
+        SMC_HIP(hipEventRecord(m->rows_ev, s));
+        *rows = n_cand;
+        return SMC_OK;
+    }
     SMC_HIP(hipStreamSynchronize(s));
     count = m->host_state->n_out;
     if (count < 0 || count > n_cand) return fail(SMC_ERR_STATE, "output count %d", count);
@@ -692,7 +722,7 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     const MaskOrder ord = want_sort && !strided ? m->order : MaskOrder();
     const int64_t items = rows_cap * ord.n_groups;    // mask-sort items: one per (group, row)
     size_t look_bytes = sort_look_bytes(items > nn ? items : nn);
-    const size_t look_c = compact_look_bytes_k(nn, kernel_size);
+    const size_t look_c = compact_look_bytes_k(rows_cap, kernel_size);
     if (look_c > look_bytes) look_bytes = look_c;
     const size_t look_before = m->look.bytes;
     // (the neighbour table is read in whole 16-byte words: keep the last one readable)
@@ -741,6 +771,10 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     uint32_t* status = &st->status;
 
     int64_t rows = strided ? 0 : n;                  // rows of the map (strided: output cells)
+    // strided pair-list builds size everything after the output cells by the
+    // bound 8 n and read the count on the device: no wait inside the build
+    const bool defer_rows = strided && want_pairs && !want_sort && n > 0;
+    const int32_t* n_out_dev = defer_rows ? &st->n_out : nullptr;
     if (n > 0) {
         int32_t* nbr = m->nbr.as<int32_t>();
         uint32_t* mask = m->mask.as<uint32_t>();
@@ -773,11 +807,12 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
                                               m->chunk_pre.as<int32_t>(), m->ws, status, s));
                 t_cp.finish();
             } else if (strided) {
-                if ((rc = strided_outputs(m, coords, n, g, sg, st, status, s, &rows))) return rc;
+                if ((rc = strided_outputs(m, coords, n, g, sg, st, status, s, &rows, defer_rows)))
+                    return rc;
                 Geom gq = g;                          // query points: [M, 4] in input coordinates
                 gq.ncols = 4;
                 SMC_HIP(launch_dense_lookup(m->qcoords.as<int32_t>(), rows, gq, grid, bits, nbr,
-                                            mask, s));
+                                            mask, s, n_out_dev));
             } else {
                 SMC_HIP(launch_dense_lookup(coords, n, g, grid, bits, nbr, mask, s));
             }
@@ -816,9 +851,10 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
             }
             if (strided) {
                 SMC_HIP(launch_key_dups(skeys, m->wide, n, st, s));
-                if ((rc = strided_outputs(m, coords, n, g, sg, st, status, s, &rows))) return rc;
+                if ((rc = strided_outputs(m, coords, n, g, sg, st, status, s, &rows, defer_rows)))
+                    return rc;
                 SMC_HIP(launch_query_lookup(skeys, svals, n, g, m->wide, m->qcoords.as<int32_t>(),
-                                            rows, nbr, mask, s));
+                                            rows, nbr, mask, s, n_out_dev));
             } else {
                 SMC_HIP(launch_sorted_lookup(skeys, svals, n, g, m->wide, split, sh, nbr, mask, st,
                                              s));
@@ -865,7 +901,8 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
                 SMC_HIP(launch_compact(mask, nbr, rows, kernel_size, cap_s, kTileM, st,
                                        m->pair_in.as<int32_t>(), m->pair_out.as<int32_t>(),
                                        m->pair_slot.as<int32_t>(), m->rowbase.as<int32_t>(),
-                                       m->chunk_pre.as<int32_t>(), m->ws, status, s, false));
+                                       m->chunk_pre.as<int32_t>(), m->ws, status, s, false,
+                                       n_out_dev));
                 t_cp.finish();
             }
         } else if (want_pairs && !fused) {
@@ -888,6 +925,7 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     m->strided = strided;
     m->n_in = n;
     m->n = rows;
+    m->rows_pending = n_out_dev != nullptr;
     m->sgeom = sg;
     t_map.finish();
     const bool async = (flags & SMC_BUILD_ASYNC) != 0;
@@ -951,6 +989,7 @@ int smc_map_sync(smc_map* m) {
 int smc_map_rows(smc_map* m, int64_t* n, int64_t* n_in) {
     if (!m) return fail(SMC_ERR_ARG, "map is NULL");
     if (!m->built) return fail(SMC_ERR_STATE, "map was never built");
+    if (int rc = resolve_rows(m)) return rc;
     if (n) *n = m->n;
     if (n_in) *n_in = m->n_in;
     return SMC_OK;
@@ -1102,6 +1141,7 @@ static int conv_forward(smc_map* m, const uint16_t* x, int c_in, const void* wpa
                         void* y, unsigned flags, void* stream, float* fixed, size_t fixed_bytes) {
     if (!m) return fail(SMC_ERR_ARG, "map is NULL");
     if (!m->built) return fail(SMC_ERR_STATE, "map was never built");
+    if (int rc = resolve_rows(m)) return rc;
     if (!m->pending && m->build_status != SMC_OK)
         return fail(SMC_ERR_STATE, "map build failed: %s", smc_status_string(m->build_status));
     if (c_in < 1 || c_out < 1) return fail(SMC_ERR_ARG, "c_in = %d, c_out = %d", c_in, c_out);

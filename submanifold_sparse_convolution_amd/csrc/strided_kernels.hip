@@ -342,8 +342,10 @@ __global__ __launch_bounds__(kBlock) void k_query_lookup(const K* __restrict__ k
                                                          int64_t n_in, Geom g,
                                                          const int32_t* __restrict__ qcoords,
                                                          int64_t m, int32_t* __restrict__ nbr,
-                                                         uint32_t* __restrict__ mask) {
+                                                         uint32_t* __restrict__ mask,
+                                                         const int32_t* __restrict__ m_dev) {
     constexpr int kWalk = 12;
+    if (m_dev && *m_dev < m) m = *m_dev;          // rows counted on the device (grid: a bound)
     const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
     const int64_t o = t >> 2;
     const int c = (int)(t & 3);
@@ -455,14 +457,14 @@ hipError_t launch_stride_bitmap(const int32_t* coords, int64_t n, const Geom& g,
 
 hipError_t launch_query_lookup(const void* keys, const uint32_t* vals, int64_t n_in, const Geom& g,
                                bool wide, const int32_t* qcoords, int64_t m, int32_t* nbr,
-                               uint32_t* mask, hipStream_t s) {
+                               uint32_t* mask, hipStream_t s, const int32_t* m_dev) {
     if (m <= 0) return hipSuccess;
     if (wide)
         launch(k_query_lookup<uint64_t>, blocks_of(m * 4, kBlock), kBlock, 0, s,
-               (const uint64_t*)keys, vals, n_in, g, qcoords, m, nbr, mask);
+               (const uint64_t*)keys, vals, n_in, g, qcoords, m, nbr, mask, m_dev);
     else
         launch(k_query_lookup<uint32_t>, blocks_of(m * 4, kBlock), kBlock, 0, s,
-               (const uint32_t*)keys, vals, n_in, g, qcoords, m, nbr, mask);
+               (const uint32_t*)keys, vals, n_in, g, qcoords, m, nbr, mask, m_dev);
     return hipGetLastError();
 }
 
