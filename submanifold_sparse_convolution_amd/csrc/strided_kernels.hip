@@ -124,33 +124,49 @@ __global__ __launch_bounds__(kUThreads) void k_unique_count(const uint64_t* __re
 }
 
 // Exclusive scan of the per-block counts in place (one block); the total is the
-// number of output rows.
+// number of output rows. Thread t takes the contiguous segment
+// [t per, (t + 1) per), its loads 16 at a time in flight: its sum, one block
+// scan of the 1,024 sums, then the segment's prefixes. (A pass per 1,024
+// counts, three barriers each, took 14 us for 11,665 counts.)
 __global__ __launch_bounds__(1024) void k_scan_counts(uint32_t* __restrict__ counts, int64_t nb,
                                                       MapState* st) {
+    constexpr int kB = 16;
     __shared__ uint32_t s_w[16];
-    __shared__ uint32_t s_carry;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    if (threadIdx.x == 0) s_carry = 0;
-    __syncthreads();
-    for (int64_t c0 = 0; c0 < nb; c0 += 1024) {
-        const int64_t i = c0 + threadIdx.x;
-        const uint32_t v = i < nb ? counts[i] : 0u;
-        uint32_t inc = v;
+    const int64_t per = (nb + 1023) / 1024;
+    const int64_t i0 = (int64_t)threadIdx.x * per;
+    const int64_t i1 = i0 + per < nb ? i0 + per : nb;
+    uint32_t sum = 0;
+    for (int64_t b0 = i0; b0 < i1; b0 += kB) {
+        uint32_t v[kB];
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t t = __shfl_up(inc, o);
-            if (lane >= o) inc += t;
-        }
-        if (lane == 63) s_w[w] = inc;
-        __syncthreads();
-        uint32_t before = s_carry;
-        for (int q = 0; q < w; ++q) before += s_w[q];
-        if (i < nb) counts[i] = before + inc - v;
-        __syncthreads();
-        if (threadIdx.x == 1023) s_carry = before + inc;
-        __syncthreads();
+        for (int j = 0; j < kB; ++j) v[j] = b0 + j < i1 ? counts[b0 + j] : 0u;
+#pragma unroll
+        for (int j = 0; j < kB; ++j) sum += v[j];
     }
-    if (threadIdx.x == 0) st->n_out = (int32_t)s_carry;
+    uint32_t inc = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = __shfl_up(inc, o);
+        if (lane >= o) inc += t;
+    }
+    if (lane == 63) s_w[w] = inc;
+    __syncthreads();
+    uint32_t before = 0;
+    for (int q = 0; q < w; ++q) before += s_w[q];
+    uint32_t run = before + inc - sum;
+    for (int64_t b0 = i0; b0 < i1; b0 += kB) {
+        uint32_t v[kB];
+#pragma unroll
+        for (int j = 0; j < kB; ++j) v[j] = b0 + j < i1 ? counts[b0 + j] : 0u;
+#pragma unroll
+        for (int j = 0; j < kB; ++j)
+            if (b0 + j < i1) {
+                counts[b0 + j] = run;
+                run += v[j];
+            }
+    }
+    if (threadIdx.x == 1023) st->n_out = (int32_t)(before + inc);
 }
 
 // Each run head goes to output row offs[block] + (heads before it in the
