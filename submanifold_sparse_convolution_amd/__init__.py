@@ -295,7 +295,8 @@ class KernelMap:
             int(batch_size), int(kernel_size), int(stride), ROUTES[route],
             (0 if sync else SMC_BUILD_ASYNC) | (0 if pairs else SMC_BUILD_NO_PAIRS)
             | (0 if sort else SMC_BUILD_NO_SORT), _stream(stream)))
-        # the output count is on the host when the call returns: no wait here
+        # the output count: waits for its own event only (the lookup and
+        # compaction after it are still running)
         rows = ctypes.c_int64()
         _check(lib().smc_map_rows(self._h, ctypes.byref(rows), None))
         self.n, self.n_in, self.kernel_size, self.strided = rows.value, n, int(kernel_size), True

@@ -248,3 +248,49 @@ def test_strided_sorted_64bit_keys():
     got = gpu_strided(coords, shape)
     assert got["info"]["route"] == "sorted" and got["info"]["key_bits"] > 32
     check_map(got, oracle_strided(coords, shape), "64-bit keys")
+
+
+def test_deferred_output_count_readers():
+    """A strided pair-list build leaves its output count on the device (the
+    lookup and compaction after it are sized by the bound 8 n); every reader
+    of the count resolves it: the map info, the forward, the coordinate export,
+    also for a build nobody read before the next one started."""
+    import ctypes
+    import torch
+    L = smc.lib()
+    cases = [(random_cells((30, 30, 30), 3000, 31), (30, 30, 30)),
+             (random_cells((24, 24, 24), 1200, 32), (24, 24, 24))]
+    refs = [so.strided_conv(c, shp, synth.int_features(len(c), 16, 3),
+                            synth.int_weights(16, 24, 4)) for c, shp in cases]
+    m = smc.KernelMap()
+    keep = []
+
+    def build_async(k):
+        coords, shp = cases[k]
+        d = to_dev_i32(coords)
+        keep.append(d)
+        shape = (ctypes.c_int32 * 3)(*shp)
+        rc = L.smc_map_build_strided(m._h, ctypes.c_void_p(d.data_ptr()), len(coords), 4, shape,
+                                     0, 3, 2, 0, smc.SMC_BUILD_ASYNC | smc.SMC_BUILD_NO_SORT,
+                                     None)
+        assert rc == 0
+
+    # two builds back to back, the first count never read: the second's is reported
+    build_async(0)
+    build_async(1)
+    assert m.info()["n"] == len(refs[1]["out_coords"])
+    # the forward as the first reader, then the coordinate export
+    build_async(0)
+    n0 = len(refs[0]["out_coords"])
+    coords0, _ = cases[0]
+    x = to_dev_bf16(synth.int_features(len(coords0), 16, 3))
+    wp = smc.pack_weights(to_dev_bf16(synth.int_weights(16, 24, 4)))
+    y = torch.empty((n0, 24), dtype=torch.float32, device="cuda")
+    rc = L.smc_conv_forward(m._h, ctypes.c_void_p(x.data_ptr()), 16, ctypes.c_void_p(wp.buf.data_ptr()),
+                            24, ctypes.c_void_p(y.data_ptr()), smc.SMC_FWD_OUT_F32, None)
+    assert rc == 0
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), refs[0]["acc"])
+    m.n = n0
+    assert np.array_equal(m.out_coords(), refs[0]["out_coords"])
+    m.close()
