@@ -971,8 +971,11 @@ hipError_t launch_gemm_nc(const uint16_t* x, int c_in, const void* wpacked, int 
         return hipGetLastError();
     }
     const int mw = mw_nc_for(c_in);
-    int64_t gx = (taps - 1) * (cap / (64 * mw));  // tiles if every tap were full
-    if (gx > (int64_t)n_cu * 2) gx = (int64_t)n_cu * 2;
+    // tiles if every tap were full, at most four blocks per CU: a launch holds
+    // every tile of the sets here at once (measured against two per CU: 91k-row
+    // off-centre GEMM 14.1 -> 13.1 us, its strided layer's 48.5 -> 39.1 us)
+    int64_t gx = (taps - 1) * (cap / (64 * mw));
+    if (gx > (int64_t)n_cu * 4) gx = (int64_t)n_cu * 4;
     if (gx < 1) gx = 1;
     gx = xcd_round(gx);
     dim3 grid((unsigned)gx, (unsigned)n_wt);
