@@ -269,12 +269,15 @@ hipError_t launch_compact(const uint32_t* mask, const int32_t* nbr, int64_t n, i
                           bool dense_centre = true, const int32_t* n_dev = nullptr);
 // Dense route: neighbour lookup and compaction in one kernel (also writes nbr
 // and mask).
+// sparse_centre: coords are a strided map's query points (the centre a tap
+// like the others); n_dev: a device row count, n its bound (see launch_compact).
 hipError_t launch_lookup_compact(const int32_t* coords, int64_t n, const Geom& g,
                                  const int32_t* grid, const uint32_t* bits, int32_t* nbr,
                                  uint32_t* mask, int64_t cap,
                                  int tile_m, MapState* st, int32_t* pair_in, int32_t* pair_out,
                                  int32_t* pair_slot, int32_t* rowbase, int32_t* chunk_pre,
-                                 SortWork& ws, uint32_t* status, hipStream_t s);
+                                 SortWork& ws, uint32_t* status, hipStream_t s,
+                                 bool sparse_centre = false, const int32_t* n_dev = nullptr);
 
 // ---- GEMM (gemm_kernels.hip) ----
 // taps: 27 or 125 (the packed weights hold that many taps).

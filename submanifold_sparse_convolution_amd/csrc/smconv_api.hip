@@ -775,6 +775,20 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     // bound 8 n and read the count on the device: no wait inside the build
     const bool defer_rows = strided && want_pairs && !want_sort && n > 0;
     const int32_t* n_out_dev = defer_rows ? &st->n_out : nullptr;
+    // a strided map's pair lists over its (bound of) rows: every tap sparse
+    auto strided_pair_bufs = [&](int64_t rr) -> int {
+        const int64_t cap_s = (rr + kCapAlign - 1) / kCapAlign * kCapAlign;
+        int rc2;
+        if ((rc2 = m->pair_in.ensure((size_t)taps * cap_s * 4, s)) ||
+            (rc2 = m->pair_out.ensure((size_t)taps * cap_s * 4, s)) ||
+            (rc2 = m->pair_slot.ensure((size_t)taps * cap_s * 4, s)) ||
+            (rc2 = m->rowbase.ensure((size_t)(rr + 1) * 4, s)) ||
+            (rc2 = m->chunk_pre.ensure((size_t)(compact_chunks(rr) + 1) * (kTaps + 1) * 4, s)))
+            return rc2;
+        m->cap = cap_s;
+        return SMC_OK;
+    };
+    bool compacted = false;                          // the pair lists came with the lookup
     if (n > 0) {
         int32_t* nbr = m->nbr.as<int32_t>();
         uint32_t* mask = m->mask.as<uint32_t>();
@@ -811,8 +825,25 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
                     return rc;
                 Geom gq = g;                          // query points: [M, 4] in input coordinates
                 gq.ncols = 4;
-                SMC_HIP(launch_dense_lookup(m->qcoords.as<int32_t>(), rows, gq, grid, bits, nbr,
-                                            mask, s, n_out_dev));
+                if (want_pairs && !want_sort && kernel_size == 3 && rows > 0) {
+                    // lookup and compaction in one kernel (the centre a sparse tap)
+                    if ((rc = strided_pair_bufs(rows))) return rc;
+                    t_nb.finish();
+                    StageTimer t_cp(m, SMC_STAGE_COMPACT, s);
+                    SMC_HIP(launch_lookup_compact(m->qcoords.as<int32_t>(), rows, gq, grid, bits,
+                                                  nbr, mask, m->cap, kTileM, st,
+                                                  m->pair_in.as<int32_t>(),
+                                                  m->pair_out.as<int32_t>(),
+                                                  m->pair_slot.as<int32_t>(),
+                                                  m->rowbase.as<int32_t>(),
+                                                  m->chunk_pre.as<int32_t>(), m->ws, status, s,
+                                                  true, n_out_dev));
+                    t_cp.finish();
+                    compacted = true;
+                } else {
+                    SMC_HIP(launch_dense_lookup(m->qcoords.as<int32_t>(), rows, gq, grid, bits,
+                                                nbr, mask, s, n_out_dev));
+                }
             } else {
                 SMC_HIP(launch_dense_lookup(coords, n, g, grid, bits, nbr, mask, s));
             }
@@ -885,17 +916,10 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
             }
             t_ms.finish();
         }
-        if (want_pairs && !fused && strided) {
+        if (want_pairs && !fused && strided && !compacted) {
             // the output rows' pair lists: every tap sparse, the centre too
-            const int64_t rr = rows > 0 ? rows : 1;
-            const int64_t cap_s = (rr + kCapAlign - 1) / kCapAlign * kCapAlign;
-            if ((rc = m->pair_in.ensure((size_t)taps * cap_s * 4, s)) ||
-                (rc = m->pair_out.ensure((size_t)taps * cap_s * 4, s)) ||
-                (rc = m->pair_slot.ensure((size_t)taps * cap_s * 4, s)) ||
-                (rc = m->rowbase.ensure((size_t)(rr + 1) * 4, s)) ||
-                (rc = m->chunk_pre.ensure((size_t)(compact_chunks(rr) + 1) * (kTaps + 1) * 4, s)))
-                return rc;
-            m->cap = cap_s;
+            if ((rc = strided_pair_bufs(rows > 0 ? rows : 1))) return rc;
+            const int64_t cap_s = m->cap;
             if (rows > 0) {
                 StageTimer t_cp(m, SMC_STAGE_COMPACT, s);
                 SMC_HIP(launch_compact(mask, nbr, rows, kernel_size, cap_s, kTileM, st,
@@ -905,7 +929,7 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
                                        n_out_dev));
                 t_cp.finish();
             }
-        } else if (want_pairs && !fused) {
+        } else if (want_pairs && !fused && !strided) {
             StageTimer t_cp(m, SMC_STAGE_COMPACT, s);
             SMC_HIP(launch_compact(mask, nbr, n, kernel_size, cap, kTileM, st,
                                    m->pair_in.as<int32_t>(),
