@@ -275,10 +275,6 @@ int ensure_device(smc_map* m) {
     return SMC_OK;
 }
 
-// Waits for the handle's last build and reads its record. Asynchronous builds
-// do not wait for each other: a build recycles the record of the build before
-// it, carrying that record's status bits into the sticky word first, so the
-// checks of every build since the last wait are reported here.
 // A strided pair-list build sizes its lookup and compaction by a bound (8
 // candidates per input) and leaves its output count on the device; the count
 // reaches the host with an event of its own, read here on first use.
@@ -296,6 +292,10 @@ int resolve_rows(smc_map* m) {
     return SMC_OK;
 }
 
+// Waits for the handle's last build and reads its record. Asynchronous builds
+// do not wait for each other: a build recycles the record of the build before
+// it, carrying that record's status bits into the sticky word first, so the
+// checks of every build since the last wait are reported here.
 int wait_build(smc_map* m) {
     if (int rc = resolve_rows(m)) return rc;
     if (!m->pending) return SMC_OK;
@@ -594,6 +594,7 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     const bool carry = m->pending;
     m->pending = false;
     m->built = false;
+    m->rows_pending = false;                      // (a failed build leaves no count to read)
     m->perm = nullptr;
     // this build's record and histograms; the other slot is cleared by its first kernel
     const int slot = m->slot ^ 1;
