@@ -219,10 +219,10 @@ int smc_map_build(smc_map* map, const int32_t* coords, int64_t n, int ncols,
  * SMC_ERR_RANGE. kernel_size must be 3 and stride 2 (else
  * SMC_ERR_UNSUPPORTED); n <= 2^24. The output count n (the caller needs it to
  * size y) reaches the host once: with the mask order (no SMC_BUILD_NO_SORT)
- * it is read back inside the call; a pair-list build without it sizes the
- * lookup and the compaction by the bound 8 n_in, which read the count on the
- * device, and the count is read on first use (smc_map_rows, smc_map_info,
- * the forward), so the call waits for nothing. With SMC_BUILD_ASYNC the
+ * it is read back inside the call; a pair-list build without it (and with
+ * 8 n_in <= 2^23) sizes the lookup and the compaction by the bound 8 n_in,
+ * which read the count on the device, and the count is read on first use
+ * (smc_map_rows, smc_map_info, the forward), so the call waits for nothing. With SMC_BUILD_ASYNC the
  * kernels after the count are only enqueued in either case.
  * Steps: the input grid or sorted input keys as for smc_map_build; the output
  * cells, through a bitmap of the output grid (count per block, scan, write

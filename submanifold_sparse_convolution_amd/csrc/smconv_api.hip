@@ -773,8 +773,11 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
 
     int64_t rows = strided ? 0 : n;                  // rows of the map (strided: output cells)
     // strided pair-list builds size everything after the output cells by the
-    // bound 8 n and read the count on the device: no wait inside the build
-    const bool defer_rows = strided && want_pairs && !want_sort && n > 0;
+    // bound 8 n and read the count on the device: no wait inside the build (up
+    // to a bound of 2^23 rows, whose pair lists take 2.7 GB; larger builds read
+    // the count back and size by it)
+    constexpr int64_t kDeferMaxRows = (int64_t)1 << 23;
+    const bool defer_rows = strided && want_pairs && !want_sort && n > 0 && 8 * n <= kDeferMaxRows;
     const int32_t* n_out_dev = defer_rows ? &st->n_out : nullptr;
     // a strided map's pair lists over its (bound of) rows: every tap sparse
     auto strided_pair_bufs = [&](int64_t rr) -> int {

@@ -294,3 +294,32 @@ def test_deferred_output_count_readers():
     m.n = n0
     assert np.array_equal(m.out_coords(), refs[0]["out_coords"])
     m.close()
+
+
+def test_strided_above_the_deferred_bound():
+    """1.1M inputs: a bound of 8 n above 2^23 rows, so a pair-list build reads
+    its output count back and sizes by it (the fused lookup and compaction
+    without a device count). Its map and an integer-valued layer equal those
+    of a build that also sorts the masks (its own compaction, compared with
+    the oracle in the tests above) exactly."""
+    rng = np.random.default_rng(3)
+    shape = (120, 120, 100)
+    cells = rng.choice(int(np.prod(shape)), size=1_100_000, replace=False)
+    xyz = np.stack(np.unravel_index(cells, shape), axis=1)
+    coords = np.concatenate([np.zeros((len(xyz), 1)), xyz], axis=1).astype(np.int32)
+    print(f"strided above the bound: n={len(coords)}", flush=True)
+    d = to_dev_i32(coords)
+    xb = synth.int_features(len(coords), 16, 7)
+    wb = synth.int_weights(16, 16, 8)
+    out = []
+    for sort in (False, True):
+        m = smc.KernelMap().build_strided(d, spatial_shape=shape, sort=sort)
+        ex = m.export(perm=False)
+        y = m.forward(to_dev_bf16(xb), smc.pack_weights(to_dev_bf16(wb)), out_f32=True)
+        out.append((m.n, ex, y.cpu().numpy()))
+        m.close()
+    (na, ea, ya), (nb, eb, yb) = out
+    assert na == nb
+    for key in ("tap_off", "pair_in", "pair_out", "mask", "nbr"):
+        assert np.array_equal(np.asarray(ea[key]), np.asarray(eb[key])), key
+    assert np.array_equal(ya, yb)
