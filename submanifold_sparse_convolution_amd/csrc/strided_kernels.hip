@@ -249,16 +249,22 @@ __global__ __launch_bounds__(kBlock) void k_stride_mark(const int32_t* __restric
     const int nx = axis_cands(x, sg.oext[0], sg, x0, x1);
     const int ny = axis_cands(y, sg.oext[1], sg, y0, y1);
     const int nz = axis_cands(z, sg.oext[2], sg, z0, z1);
+    // the z candidates are neighbours (z0 = z1 + 1): their bits go out together,
+    // one atomic per (x, y) unless they straddle a word
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int e = 0; e < 2; ++e)
-#pragma unroll
-            for (int f = 0; f < 2; ++f)
-                if (a < nx && e < ny && f < nz) {
-                    const int64_t L = out_bit(sg, b, a ? x1 : x0, e ? y1 : y0, f ? z1 : z0);
-                    atomicOr(&obits[L >> 5], 1u << (L & 31));
+            if (a < nx && e < ny) {
+                const int64_t L = out_bit(sg, b, a ? x1 : x0, e ? y1 : y0, nz == 2 ? z1 : z0);
+                const int lo = (int)(L & 31);
+                uint32_t bits = 1u << lo;
+                if (nz == 2) {
+                    if (lo != 31) bits |= 2u << lo;
+                    else atomicOr(&obits[(L >> 5) + 1], 1u);
                 }
+                atomicOr(&obits[L >> 5], bits);
+            }
 }
 
 __global__ __launch_bounds__(kUThreads) void k_bits_count(const uint32_t* __restrict__ obits,
