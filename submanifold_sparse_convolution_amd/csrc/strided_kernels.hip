@@ -204,16 +204,11 @@ __global__ __launch_bounds__(kUThreads) void k_unique_write(
         const uint64_t k = keys[base + j];
         const int z = (int)(k & mz), y = (int)((k >> sg.wz) & my),
                   x = (int)((k >> (sg.wz + sg.wy)) & mx), b = (int)(k >> (sg.wz + sg.wy + sg.wx));
-        int32_t* oc = ocoords + (int64_t)pos * 4;
-        oc[0] = b;
-        oc[1] = x;
-        oc[2] = y;
-        oc[3] = z;
-        int32_t* qc = qcoords + (int64_t)pos * 4;
-        qc[0] = b;
-        qc[1] = sg.stride * x - sg.pad + r + sg.origin[0];
-        qc[2] = sg.stride * y - sg.pad + r + sg.origin[1];
-        qc[3] = sg.stride * z - sg.pad + r + sg.origin[2];
+        reinterpret_cast<int4*>(ocoords)[pos] = make_int4(b, x, y, z);
+        reinterpret_cast<int4*>(qcoords)[pos] =
+            make_int4(b, sg.stride * x - sg.pad + r + sg.origin[0],
+                      sg.stride * y - sg.pad + r + sg.origin[1],
+                      sg.stride * z - sg.pad + r + sg.origin[2]);
         ++pos;
     }
 }
@@ -323,16 +318,11 @@ __global__ __launch_bounds__(kUThreads) void k_bits_write(uint32_t* __restrict__
             L /= ey;
             const int x = (int)(L % ex);
             const int b = (int)(L / ex);
-            int32_t* oc = ocoords + (int64_t)pos * 4;
-            oc[0] = b;
-            oc[1] = x;
-            oc[2] = y;
-            oc[3] = z;
-            int32_t* qc = qcoords + (int64_t)pos * 4;
-            qc[0] = b;
-            qc[1] = sg.stride * x - sg.pad + r + sg.origin[0];
-            qc[2] = sg.stride * y - sg.pad + r + sg.origin[1];
-            qc[3] = sg.stride * z - sg.pad + r + sg.origin[2];
+            reinterpret_cast<int4*>(ocoords)[pos] = make_int4(b, x, y, z);
+            reinterpret_cast<int4*>(qcoords)[pos] =
+                make_int4(b, sg.stride * x - sg.pad + r + sg.origin[0],
+                          sg.stride * y - sg.pad + r + sg.origin[1],
+                          sg.stride * z - sg.pad + r + sg.origin[2]);
             ++pos;
         }
     }
