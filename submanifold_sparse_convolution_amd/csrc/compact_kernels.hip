@@ -522,89 +522,102 @@ __global__ __launch_bounds__(kCThreads) void k_compact(
     if (!by_index && bid == gridDim.x - 1 && threadIdx.x == 0) atomicExch(ticket, 0u);
 }
 
-// Dense route: lookup and compaction in one kernel. Each thread looks up its
-// row's 27 cells as 9 (dx, dy) columns of 3 consecutive cells (z fastest):
-// first their occupancy bits, then the row ids of the occupied ones;
-// writes the neighbour row to LDS and its mask, then the chunk is compacted
-// (which also stores the chunk's neighbour rows to the table, coalesced).
-// One chunk: rows [bid kCChunk, +kCChunk) of n, last = the last chunk's index.
-// SPARSE: the rows are a strided map's query points (input coordinates of
-// 2 o), whose centre cell is looked up like the other taps (the input at 2 o
-// may be absent) and is a tap like the others in the compaction.
+// Lookup and compaction in one kernel: each thread looks up its row's 27
+// neighbour rows (the lookup policy), writes them to LDS and its mask,
+// then the chunk is compacted (which also stores the chunk's neighbour rows to
+// the table, coalesced).
+//
+// Dense route: each row's 27 cells as 9 (dx, dy) columns of 3 consecutive
+// cells (z fastest): first their occupancy bits, then the row ids of the
+// occupied ones. SPARSE: the rows are a strided map's query points (input
+// coordinates of 2 o), whose centre cell is looked up like the other taps (the
+// input at 2 o may be absent).
 template <bool SPARSE>
+struct DenseLookup {
+    static constexpr bool kDenseCentre = !SPARSE;
+    const int32_t* coords;
+    Geom g;
+    const int32_t* grid;
+    const uint32_t* bits;
+    __device__ __forceinline__ void operator()(int64_t row, int64_t n, int32_t (&v)[kTaps]) const {
+        const int64_t rc = row < n ? row : (n > 0 ? n - 1 : 0);
+        const int32_t* c = coords + rc * g.ncols;
+        const int b = g.ncols == 4 ? c[0] : 0;
+        const int32_t* q = c + (g.ncols == 4 ? 1 : 0);
+        const int x = q[0] - g.origin[0], y = q[1] - g.origin[1], z = q[2] - g.origin[2];
+        const bool ok = row < n && (unsigned)b < (unsigned)g.batch &&
+                        (unsigned)x < (unsigned)g.ext[0] && (unsigned)y < (unsigned)g.ext[1] &&
+                        (unsigned)z < (unsigned)g.ext[2];
+        // cell (x, y, z - 1) of the padded grid (g.pad cells of padding a side),
+        // whose 3x3x3 neighbourhood starts at c0 - sz_x - sz_y. Rows out of range
+        // (and rows past n) read the neighbourhood of padded cell (1, 1, 0)
+        // instead, which lies inside the grid; their values are unused.
+        const int64_t c0 = ok ? b * g.sz_b + (int64_t)(x + g.pad) * g.sz_x +
+                                    (int64_t)(y + g.pad) * g.sz_y + (z + g.pad - 1)
+                              : g.sz_x + g.sz_y;
+        // occupancy of the 9 (dx, dy) columns (3 bits each, two words per column) ...
+        uint32_t cb[9];
+#pragma unroll
+        for (int dx = 0; dx < 3; ++dx)
+#pragma unroll
+            for (int dy = 0; dy < 3; ++dy)
+                cb[3 * dx + dy] =
+                    cell_bits(bits, c0 + (int64_t)(dx - 1) * g.sz_x + (int64_t)(dy - 1) * g.sz_y, 3);
+        // ... then row ids of the occupied cells only. Every tap issues its load; an
+        // empty one reads cell 0 (one line, cached for the whole launch), so no load
+        // is conditional.
+#pragma unroll
+        for (int dx = 0; dx < 3; ++dx)
+#pragma unroll
+            for (int dy = 0; dy < 3; ++dy)
+#pragma unroll
+                for (int dz = 0; dz < 3; ++dz) {
+                    const int k = 9 * dx + 3 * dy + dz;
+                    if (!SPARSE && k == kCentre) continue;
+                    const bool on = (cb[3 * dx + dy] >> dz) & 1u;
+                    const int64_t cc =
+                        c0 + (int64_t)(dx - 1) * g.sz_x + (int64_t)(dy - 1) * g.sz_y + dz;
+                    v[k] = grid[on ? cc : 0];
+                    v[k] = on ? v[k] : -1;
+                }
+        if (!SPARSE) v[kCentre] = (int32_t)row;
+#pragma unroll
+        for (int k = 0; k < kTaps; ++k) v[k] = ok ? v[k] : -1;
+    }
+};
+
+// One chunk: rows [bid kCChunk, +kCChunk) of n, last = the last chunk's index.
+template <class LOOKUP>
 __device__ __forceinline__ void lookup_compact_chunk(
-    CompactLds& L, uint32_t bid, uint32_t last, const int32_t* __restrict__ coords, int64_t n,
-    const Geom& g, const int32_t* __restrict__ grid, const uint32_t* __restrict__ bits,
+    CompactLds& L, uint32_t bid, uint32_t last, const LOOKUP& lk, int64_t n,
     int32_t* __restrict__ nbr, uint32_t* __restrict__ mask, int64_t cap, int tile_m, MapState* st,
     int32_t* __restrict__ pair_in, int32_t* __restrict__ pair_out, int32_t* __restrict__ pair_slot,
     int32_t* __restrict__ rowbase, int32_t* __restrict__ chunk_pre, uint64_t* __restrict__ look,
     uint32_t epoch, uint32_t* status, uint32_t spin_limit, uint32_t wait_xor) {
     const int tid = threadIdx.x;
-    const int64_t base0 = (int64_t)bid * kCChunk;
-    const int64_t row = base0 + tid;
-    const int64_t rc = row < n ? row : (n > 0 ? n - 1 : 0);
-    const int32_t* c = coords + rc * g.ncols;
-    const int b = g.ncols == 4 ? c[0] : 0;
-    const int32_t* q = c + (g.ncols == 4 ? 1 : 0);
-    const int x = q[0] - g.origin[0], y = q[1] - g.origin[1], z = q[2] - g.origin[2];
-    const bool ok = row < n && (unsigned)b < (unsigned)g.batch && (unsigned)x < (unsigned)g.ext[0] &&
-                    (unsigned)y < (unsigned)g.ext[1] && (unsigned)z < (unsigned)g.ext[2];
-    // cell (x, y, z - 1) of the padded grid (g.pad cells of padding a side), whose
-    // 3x3x3 neighbourhood starts at c0 - sz_x - sz_y. Rows out of range (and rows
-    // past n) read the neighbourhood of padded cell (1, 1, 0) instead, which lies
-    // inside the grid; their values are unused.
-    const int64_t c0 = ok ? b * g.sz_b + (int64_t)(x + g.pad) * g.sz_x +
-                                (int64_t)(y + g.pad) * g.sz_y + (z + g.pad - 1)
-                          : g.sz_x + g.sz_y;
-    // occupancy of the 9 (dx, dy) columns (3 bits each, two words per column) ...
-    uint32_t cb[9];
-#pragma unroll
-    for (int dx = 0; dx < 3; ++dx)
-#pragma unroll
-        for (int dy = 0; dy < 3; ++dy)
-            cb[3 * dx + dy] =
-                cell_bits(bits, c0 + (int64_t)(dx - 1) * g.sz_x + (int64_t)(dy - 1) * g.sz_y, 3);
-    // ... then row ids of the occupied cells only. Every tap issues its load; an
-    // empty one reads cell 0 (one line, cached for the whole launch), so no load
-    // is conditional.
-    const int64_t c_self = 0;
+    const int64_t row = (int64_t)bid * kCChunk + tid;
     int32_t v[kTaps];
-#pragma unroll
-    for (int dx = 0; dx < 3; ++dx)
-#pragma unroll
-        for (int dy = 0; dy < 3; ++dy)
-#pragma unroll
-            for (int dz = 0; dz < 3; ++dz) {
-                const int k = 9 * dx + 3 * dy + dz;
-                if (!SPARSE && k == kCentre) continue;
-                const bool on = (cb[3 * dx + dy] >> dz) & 1u;
-                const int64_t cc = c0 + (int64_t)(dx - 1) * g.sz_x + (int64_t)(dy - 1) * g.sz_y + dz;
-                v[k] = grid[on ? cc : c_self];
-                v[k] = on ? v[k] : -1;
-            }
-    if (!SPARSE) v[kCentre] = (int32_t)row;
+    lk(row, n, v);
     uint32_t m = 0;
 #pragma unroll
     for (int k = 0; k < kTaps; ++k) {
-        v[k] = ok ? v[k] : -1;
         m |= (v[k] >= 0 ? 1u : 0u) << k;
         L.nb[tid * kTaps + k] = v[k];
     }
     if (row < n) mask[row] = m;
     __syncthreads();
     compact_chunk(L, m, bid, last, n, cap, tile_m, st, pair_in, pair_out, pair_slot, rowbase,
-                  chunk_pre, look, epoch, status, nbr, !SPARSE, spin_limit, wait_xor);
+                  chunk_pre, look, epoch, status, nbr, LOOKUP::kDenseCentre, spin_limit, wait_xor);
 }
 
 // One chunk per block; with n_dev (a device row count, n only its bound) the
 // grid is at most the resident blocks, each taking chunks blockIdx.x,
 // + gridDim.x, ... up to the count's last chunk (as k_compact).
-template <bool SPARSE>
+template <class LOOKUP>
 __global__ __launch_bounds__(kCThreads) void k_lookup_compact(
-    const int32_t* __restrict__ coords, int64_t n, Geom g, const int32_t* __restrict__ grid,
-    const uint32_t* __restrict__ bits, int32_t* __restrict__ nbr, uint32_t* __restrict__ mask,
-    int64_t cap, int tile_m, MapState* st, int32_t* __restrict__ pair_in,
-    int32_t* __restrict__ pair_out, int32_t* __restrict__ pair_slot, int32_t* __restrict__ rowbase,
+    LOOKUP lk, int64_t n, int32_t* __restrict__ nbr, uint32_t* __restrict__ mask, int64_t cap,
+    int tile_m, MapState* st, int32_t* __restrict__ pair_in, int32_t* __restrict__ pair_out,
+    int32_t* __restrict__ pair_slot, int32_t* __restrict__ rowbase,
     int32_t* __restrict__ chunk_pre, uint64_t* __restrict__ look, uint32_t* ticket, bool by_index,
     uint32_t epoch, uint32_t* status, uint32_t spin_limit, uint32_t wait_xor,
     const int32_t* __restrict__ n_dev) {
@@ -614,17 +627,17 @@ __global__ __launch_bounds__(kCThreads) void k_lookup_compact(
         if (nd < n) n = nd > 0 ? nd : 0;
         const uint32_t last = n > 0 ? (uint32_t)((n + kCChunk - 1) / kCChunk - 1) : 0u;
         for (uint32_t bid = blockIdx.x; bid <= last; bid += gridDim.x) {
-            lookup_compact_chunk<SPARSE>(L, bid, last, coords, n, g, grid, bits, nbr, mask, cap,
-                                         tile_m, st, pair_in, pair_out, pair_slot, rowbase,
-                                         chunk_pre, look, epoch, status, spin_limit, wait_xor);
+            lookup_compact_chunk(L, bid, last, lk, n, nbr, mask, cap, tile_m, st, pair_in,
+                                 pair_out, pair_slot, rowbase, chunk_pre, look, epoch, status,
+                                 spin_limit, wait_xor);
             __syncthreads();                      // the chunk's LDS reads done before the next
         }
         return;
     }
     const uint32_t bid = chunk_of_block(by_index, ticket, &L.bid);
-    lookup_compact_chunk<SPARSE>(L, bid, gridDim.x - 1, coords, n, g, grid, bits, nbr, mask, cap,
-                                 tile_m, st, pair_in, pair_out, pair_slot, rowbase, chunk_pre, look,
-                                 epoch, status, spin_limit, wait_xor);
+    lookup_compact_chunk(L, bid, gridDim.x - 1, lk, n, nbr, mask, cap, tile_m, st, pair_in,
+                         pair_out, pair_slot, rowbase, chunk_pre, look, epoch, status, spin_limit,
+                         wait_xor);
     if (!by_index && bid == gridDim.x - 1 && threadIdx.x == 0) atomicExch(ticket, 0u);
 }
 
@@ -888,6 +901,34 @@ hipError_t launch_compact(const uint32_t* mask, const int32_t* nbr, int64_t n, i
     return hipGetLastError();
 }
 
+// One launch of k_lookup_compact with lookup lk: by block index when every
+// block fits at once (else by ticket), or under a device row count over at most
+// the resident blocks.
+template <class LOOKUP>
+static hipError_t launch_lookup_compact_t(const LOOKUP& lk, int slot, int64_t n, int32_t* nbr,
+                                          uint32_t* mask, int64_t cap, int tile_m, MapState* st,
+                                          int32_t* pair_in, int32_t* pair_out, int32_t* pair_slot,
+                                          int32_t* rowbase, int32_t* chunk_pre, SortWork& ws,
+                                          uint32_t* status, hipStream_t s, const int32_t* n_dev) {
+    const uint32_t epoch = next_epoch(ws);
+    const unsigned blocks = (unsigned)compact_chunks(n);
+    const uint32_t spin = ws.force_timeout ? 64u : kSpinLimit;
+    const uint32_t wx = ws.force_timeout ? 0x15555555u : 0u;
+    const void* kern = (const void*)k_lookup_compact<LOOKUP>;
+    unsigned grid_x = blocks;
+    bool by_index = false;
+    if (n_dev) {
+        const int64_t res = resident_blocks(kern, slot);
+        if (res > 0 && res < (int64_t)blocks) grid_x = (unsigned)res;
+    } else {
+        by_index = fits_at_once(kern, slot, blocks);
+    }
+    launch(k_lookup_compact<LOOKUP>, grid_x, kCThreads, 0, s, lk, n, nbr, mask, cap, tile_m, st,
+           pair_in, pair_out, pair_slot, rowbase, chunk_pre, ws.look, ws.ticket, by_index, epoch,
+           status, spin, wx, n_dev);
+    return hipGetLastError();
+}
+
 hipError_t launch_lookup_compact(const int32_t* coords, int64_t n, const Geom& g,
                                  const int32_t* grid, const uint32_t* bits, int32_t* nbr,
                                  uint32_t* mask, int64_t cap,
@@ -895,28 +936,13 @@ hipError_t launch_lookup_compact(const int32_t* coords, int64_t n, const Geom& g
                                  int32_t* pair_slot, int32_t* rowbase, int32_t* chunk_pre,
                                  SortWork& ws, uint32_t* status, hipStream_t s, bool sparse_centre,
                                  const int32_t* n_dev) {
-    const uint32_t epoch = next_epoch(ws);
-    const unsigned blocks = (unsigned)compact_chunks(n);
-    const uint32_t spin = ws.force_timeout ? 64u : kSpinLimit;
-    const uint32_t wx = ws.force_timeout ? 0x15555555u : 0u;
-    auto go = [&](auto kern, int slot) {
-        unsigned grid_x = blocks;
-        bool by_index = false;
-        if (n_dev) {                              // chunks up to the device count
-            const int64_t res = resident_blocks((const void*)kern, slot);
-            if (res > 0 && res < (int64_t)blocks) grid_x = (unsigned)res;
-        } else {
-            by_index = fits_at_once((const void*)kern, slot, blocks);
-        }
-        launch(kern, grid_x, kCThreads, 0, s, coords, n, g, grid, bits, nbr, mask, cap, tile_m, st,
-               pair_in, pair_out, pair_slot, rowbase, chunk_pre, ws.look, ws.ticket, by_index, epoch,
-               status, spin, wx, n_dev);
-    };
     if (sparse_centre)
-        go(k_lookup_compact<true>, 3);
-    else
-        go(k_lookup_compact<false>, 2);
-    return hipGetLastError();
+        return launch_lookup_compact_t(DenseLookup<true>{coords, g, grid, bits}, 3, n, nbr, mask,
+                                       cap, tile_m, st, pair_in, pair_out, pair_slot, rowbase,
+                                       chunk_pre, ws, status, s, n_dev);
+    return launch_lookup_compact_t(DenseLookup<false>{coords, g, grid, bits}, 2, n, nbr, mask, cap,
+                                   tile_m, st, pair_in, pair_out, pair_slot, rowbase, chunk_pre,
+                                   ws, status, s, n_dev);
 }
 
 }  // namespace smc
