@@ -174,10 +174,8 @@ __global__ __launch_bounds__(kBlock) void k_dense_lookup(const int32_t* __restri
                                                          const int32_t* __restrict__ grid,
                                                          const uint32_t* __restrict__ bits,
                                                          int32_t* __restrict__ nbr,
-                                                         uint32_t* __restrict__ mask,
-                                                         const int32_t* __restrict__ n_dev) {
+                                                         uint32_t* __restrict__ mask) {
     constexpr int kCols = 9;
-    if (n_dev && *n_dev < n) n = *n_dev;          // rows counted on the device (grid: a bound)
     const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
     const int64_t row = t >> 4;
     const int c = (int)(t & 15);
@@ -484,16 +482,13 @@ hipError_t launch_clear_cells(const PrevCells& prev, hipStream_t s) {
 }
 
 hipError_t launch_dense_lookup(const int32_t* coords, int64_t n, const Geom& g, const int32_t* grid,
-                               const uint32_t* bits, int32_t* nbr, uint32_t* mask, hipStream_t s,
-                               const int32_t* n_dev) {
-    if (g.ksize == 5) {
-        if (n_dev) return hipErrorInvalidValue;   // (strided maps are 3 x 3 x 3)
+                               const uint32_t* bits, int32_t* nbr, uint32_t* mask, hipStream_t s) {
+    if (g.ksize == 5)
         launch(k_dense_lookup5, blocks_for(n * 32), kBlock, 0, s, coords, n, g, grid, bits, nbr,
                mask);
-    } else {
+    else
         launch(k_dense_lookup, blocks_for(n * 16), kBlock, 0, s, coords, n, g, grid, bits, nbr,
-               mask, n_dev);
-    }
+               mask);
     return hipGetLastError();
 }
 

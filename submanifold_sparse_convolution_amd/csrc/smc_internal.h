@@ -150,11 +150,8 @@ hipError_t launch_dense_scatter(const int32_t* coords, int64_t n, const Geom& g,
                                 const NextRecord& next, const PrevCells& prev, hipStream_t s);
 hipError_t launch_clear_cells(const PrevCells& prev, hipStream_t s);
 // nbr [n, K^3]; mask [n] (K = 3) or [n, 4] words (K = 5): g.ksize decides.
-// n_dev (optional): a device row count read by the kernel; the rows are then
-// min(n, *n_dev) (n the bound the grid was sized by).
 hipError_t launch_dense_lookup(const int32_t* coords, int64_t n, const Geom& g, const int32_t* grid,
-                               const uint32_t* bits, int32_t* nbr, uint32_t* mask, hipStream_t s,
-                               const int32_t* n_dev = nullptr);
+                               const uint32_t* bits, int32_t* nbr, uint32_t* mask, hipStream_t s);
 // Keys of the sorted route, and the digit histograms of every pass of `plan`
 // added into hist (which must start at zero).
 hipError_t launch_make_keys(const int32_t* coords, int64_t n, const Geom& g, bool wide, void* keys,
@@ -206,6 +203,8 @@ hipError_t launch_unique(const uint64_t* keys, int64_t n_c, const StrideGeom& sg
 // sorted keys with an equal neighbour: the duplicate-coordinate status bit
 hipError_t launch_key_dups(const void* keys, bool wide, int64_t n, MapState* st, hipStream_t s);
 // sorted route: the 27 taps around each query point from the sorted input keys
+// m_dev (optional): a device row count read by the kernel; the rows are then
+// min(m, *m_dev) (m the bound the grid was sized by).
 hipError_t launch_query_lookup(const void* keys, const uint32_t* vals, int64_t n_in, const Geom& g,
                                bool wide, const int32_t* qcoords, int64_t m, int32_t* nbr,
                                uint32_t* mask, hipStream_t s, const int32_t* m_dev = nullptr);

@@ -844,9 +844,9 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
                                                   true, n_out_dev));
                     t_cp.finish();
                     compacted = true;
-                } else {
+                } else {                              // (rows exact: no device count)
                     SMC_HIP(launch_dense_lookup(m->qcoords.as<int32_t>(), rows, gq, grid, bits,
-                                                nbr, mask, s, n_out_dev));
+                                                nbr, mask, s));
                 }
             } else {
                 SMC_HIP(launch_dense_lookup(coords, n, g, grid, bits, nbr, mask, s));
