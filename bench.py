@@ -16,7 +16,9 @@ step, ReLU between layers; value = (map + 6 layers) / 6 microseconds per
 layer. Beside it, "configs" holds every set (tiny, lidar, deep, wide,
 stage) with its own timing, roofline, cold and warm map builds and the CPU
 oracle timed on the host cores (map and compute apart). "strided" holds the
-downsampling layers, "peaks_measured" an MFMA-only loop and a device copy.
+downsampling layers, "peaks_measured" an MFMA-only loop and a device copy,
+"wide_sorted_route" the Wide set with the sorted mapper forced (the auto route
+maps its 3.06e9-cell grid densely when 13 GB fit the dense-grid budget).
 
 Timing: W warm-up steps, then a timed region of exactly K steps between
 device synchronisations, repeated three times; ms_per_step is the median
@@ -278,7 +280,8 @@ def stage_kernels(stage, algo, route, kernel_size=3, strided=False, c_in=128, ou
 
 
 def run_workload(name, steps, warmup, sync_build=False, algo="pairs", copy_probe_mb=0,
-                 order="plain", kernel_size=3, frames=1, strided=False, cold=False):
+                 order="plain", kernel_size=3, frames=1, strided=False, cold=False,
+                 route="auto"):
     import torch
 
     import submanifold_sparse_convolution_amd as smc
@@ -295,7 +298,7 @@ def run_workload(name, steps, warmup, sync_build=False, algo="pairs", copy_probe
     cal = None
     cold_us = None
     build_kw = dict(spatial_shape=w.grid, batch_size=frames, pairs=(algo != "mask_tiles"),
-                    sort=(algo == "mask_tiles"), kernel_size=kernel_size)
+                    sort=(algo == "mask_tiles"), kernel_size=kernel_size, route=route)
     if cold and not strided:
         # the first build on a fresh handle: its buffers are allocated, the
         # dense route's occupancy bitmap zero-filled once (host clock around
@@ -338,7 +341,7 @@ def run_workload(name, steps, warmup, sync_build=False, algo="pairs", copy_probe
 
     if strided:
         # a downsampling layer: the output rows are new cells (one layer)
-        m.build_strided(coords_d, spatial_shape=w.grid, batch_size=frames,
+        m.build_strided(coords_d, spatial_shape=w.grid, batch_size=frames, route=route,
                         pairs=algo != "mask_tiles", sort=algo == "mask_tiles")
         ys = [torch.empty((m.n, c), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
     else:
@@ -347,7 +350,8 @@ def run_workload(name, steps, warmup, sync_build=False, algo="pairs", copy_probe
     def step():
         if strided:
             m.build_strided(coords_d, spatial_shape=w.grid, batch_size=frames, sync=sync_build,
-                            pairs=algo != "mask_tiles", sort=algo == "mask_tiles")
+                            route=route, pairs=algo != "mask_tiles",
+                            sort=algo == "mask_tiles")
             return m.forward(x_d, packed[0], out=ys[0], algo=algo)
         m.build(coords_d, sync=sync_build, **build_kw)
         h = x_d
@@ -927,6 +931,13 @@ def main():
                                      else cpu_baseline(cname, args.cpu_budget))
             entries.append(e)
         line["configs"] = entries
+        if "wide" in configs:
+            # the sorted mapper (packed keys, radix sort, plane searches) on the Wide
+            # scene, which the auto route now maps densely where memory allows
+            rr = run_workload("wide", args.steps, args.warmup, args.sync_build, route="sorted")
+            e = summary(rr)
+            line["wide_sorted_route"] = {k: e[k] for k in ("route", "key_bits", "us_per_layer",
+                                                           "map_us_events", "stages")}
     if not args.no_strided:
         # downsampling layers (kernel 3, stride 2) on the same sets: new output cells,
         # pair-list forward over them; map built every step

@@ -59,15 +59,16 @@ typedef enum smc_status {
     SMC_ERR_HIP = 6,          /* a HIP runtime call or a kernel launch failed */
     SMC_ERR_STATE = 7,        /* the map is not built, or was built with an error */
     SMC_ERR_UNSUPPORTED = 8,  /* a valid request this version does not implement (kernel_size != 3) */
-    SMC_ERR_GRID = 9          /* the dense route was forced on a grid of 2^31 cells or more */
+    SMC_ERR_GRID = 9          /* the dense route was forced on a grid of 2^36 cells or more */
 } smc_status;
 
 /* Map routes ("[Kernel] Add submanifold sparse 3D convolution", section
  * "Design, and the measurements behind it": two mappers chosen by
  * bounding-box volume). */
 enum {
-    SMC_ROUTE_AUTO = 0,   /* dense presence grid when it has < 2^31 cells and fits the
-                             dense-grid budget, sorted packed keys otherwise */
+    SMC_ROUTE_AUTO = 0,   /* dense presence grid when its 4.25 bytes a cell (int32 ids,
+                             two occupancy bitmaps) fit 1/16 of the device's memory
+                             and at most 16 GiB, sorted packed keys otherwise */
     SMC_ROUTE_DENSE = 1,  /* force the dense presence grid */
     SMC_ROUTE_SORTED = 2  /* force the sorted packed-key mapper */
 };

@@ -119,11 +119,11 @@ struct NextRecord {
     uint32_t* sticky = nullptr;   // the record's status bits are ORed in here before it is cleared
 };
 
-// Cells of the previous dense build, to put back to empty in the other grid
-// (dense grids are double-buffered: a build writes one grid while its first
-// kernel clears the cells the previous build set in the other one).
+// Cells of the previous dense build, to put back to empty in the other bitmap
+// (occupancy bitmaps are double-buffered: a build sets bits in one while its
+// first kernel clears the words the previous build set in the other one).
 struct PrevCells {
-    const int32_t* cells = nullptr;   // grid cell of each row of that build (-1: none)
+    const int32_t* cells = nullptr;   // bitmap word of each row's cell in that build (-1: none)
     int64_t n = 0;
     uint32_t* bits = nullptr;         // occupancy bits of that build's grid
 };

@@ -115,7 +115,10 @@ constexpr int64_t kMaxRows = (int64_t)1 << 26;
 constexpr int64_t kMaxStridedRows = (int64_t)1 << 24;            // 8 candidates per input
 constexpr int kMaxChannels = 4096;
 constexpr int kZeroRowBytes = kMaxChannels * 2;                 // keeps 27 n + pads < 2^31
-constexpr int64_t kDenseBudgetBytes = (int64_t)4 << 30;        // auto route: grid <= 4 GiB
+// auto route: the dense grid (4 bytes a cell, two bitmaps of 1 bit) takes at most
+// 1/16 of the device's memory and at most 16 GiB
+constexpr int64_t kDenseBudgetMaxBytes = (int64_t)16 << 30;
+constexpr double kDenseMaxCells = 68719476736.0;                 // 2^36: bitmap words fit int32
 constexpr int64_t kSlabBoundBytes = (int64_t)4 << 30;          // unread counts: bound the slab
 
 int bit_len(int64_t v) {   // bits needed to hold 0..v
@@ -132,6 +135,7 @@ int bit_len(int64_t v) {   // bits needed to hold 0..v
 struct smc_map {
     int device = -1;
     int n_cu = 0;
+    int64_t dense_budget = 0;         // bytes the auto route may spend on a dense grid
     hipEvent_t done = nullptr;        // end of a synchronous build (system-scope fence)
     hipEvent_t done_nf = nullptr;     // end of an asynchronous build (no fence, see build_map)
     hipEvent_t done_last = nullptr;   // the one the last build recorded
@@ -151,15 +155,17 @@ struct smc_map {
     DevBuf state;                     // two MapState records: builds alternate between them
     int slot = 1;                     // record of the last build
     bool slot_clean[2] = {true, true};  // record in its starting state
-    // Dense route: two int32 presence grids, used by alternate dense builds and kept
-    // all -1 between them. cells[i] records the cell of every row of the last build
-    // on grid i; the next dense build (on the other grid) or, before a sorted build,
-    // a small kernel puts those cells back to -1.
-    DevBuf grid[2];                          // int32 row ids (read only where a bit is set)
+    // Dense route: one int32 id grid and two occupancy bitmaps, used by alternate
+    // dense builds and kept all zero between them. A build writes the ids of its
+    // own cells only and reads ids only under its own bits, so the id grid is
+    // never cleared. cells[i] records the bitmap word of every row of the last
+    // build on bitmap i; the next dense build (on the other bitmap) or, before a
+    // sorted build, a small kernel clears those words.
+    DevBuf grid;                             // int32 row ids (read only where a bit is set)
     DevBuf bits[2];                          // one occupancy bit per cell (+2 words)
     int64_t bits_clean_words[2] = {0, 0};    // prefix of each bitmap known to be zero
     DevBuf cells[2];
-    int next_grid = 0;                       // grid of the next dense build
+    int next_grid = 0;                       // bitmap of the next dense build
     PrevCells stale;                         // cells not yet put back (stale.n = 0: none)
     DevBuf keys0, keys1, keys2;       // packed keys (u32 or u64)
     DevBuf vals0, vals1;              // u32
@@ -242,6 +248,9 @@ int ensure_device(smc_map* m) {
     if (m->device < 0) {
         lookup_scratch(dev);
         SMC_HIP(hipDeviceGetAttribute(&m->n_cu, hipDeviceAttributeMultiprocessorCount, dev));
+        size_t total = 0;
+        SMC_HIP(hipDeviceTotalMem(&total, dev));
+        m->dense_budget = std::min<int64_t>(kDenseBudgetMaxBytes, (int64_t)(total / 16));
         if (!m->done) SMC_HIP(hipEventCreateWithFlags(&m->done, hipEventDisableTiming));
         if (!m->done_nf)
             SMC_HIP(hipEventCreateWithFlags(&m->done_nf,
@@ -331,7 +340,7 @@ int wait_build(smc_map* m) {
 
 int ensure_grid(smc_map* m, int gi, int64_t cells, hipStream_t s) {
     const int64_t words = cells / 32 + 2;
-    DevBuf& grid = m->grid[gi];
+    DevBuf& grid = m->grid;
     DevBuf& bits = m->bits[gi];
     int rc = grid.ensure((size_t)cells * 4, s);       // never filled: read only under a set bit
     if (rc) return rc;
@@ -479,7 +488,7 @@ int smc_map_destroy(smc_map* m) {
         (void)hipGetDevice(&cur);
         if (m->device >= 0) (void)hipSetDevice(m->device);
         (void)hipDeviceSynchronize();
-        DevBuf* bufs[] = {&m->state, &m->grid[0], &m->grid[1], &m->bits[0], &m->bits[1],
+        DevBuf* bufs[] = {&m->state, &m->grid, &m->bits[0], &m->bits[1],
                           &m->cells[0], &m->cells[1], &m->keys0, &m->keys1, &m->keys2,
                           &m->vals0, &m->vals1, &m->hist, &m->look, &m->ticket, &m->nbr,
                           &m->mask, &m->mkey0, &m->mkey1, &m->mval0, &m->mval1, &m->okeys,
@@ -665,16 +674,17 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     const double pad2 = 2.0 * g.pad;
     const double cells_d =
         (double)g.batch * (g.ext[0] + pad2) * (g.ext[1] + pad2) * (g.ext[2] + pad2);
-    const bool dense_addressable = cells_d < 2147483648.0;
+    const bool dense_addressable = cells_d < kDenseMaxCells;
     int chosen;
     if (route == SMC_ROUTE_DENSE) {
         if (!dense_addressable)
-            return fail(SMC_ERR_GRID, "dense grid of %.3g cells exceeds 2^31", cells_d);
+            return fail(SMC_ERR_GRID, "dense grid of %.3g cells exceeds 2^36", cells_d);
         chosen = SMC_ROUTE_DENSE;
     } else if (route == SMC_ROUTE_SORTED) {
         chosen = SMC_ROUTE_SORTED;
     } else {
-        chosen = (dense_addressable && cells_d * 4.0 <= (double)kDenseBudgetBytes)
+        // ids (4 bytes a cell) and the two bitmaps
+        chosen = (dense_addressable && cells_d * 4.25 <= (double)m->dense_budget)
                      ? SMC_ROUTE_DENSE : SMC_ROUTE_SORTED;
     }
     g.sz_y = g.ext[2] + 2 * g.pad;
@@ -806,7 +816,7 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
             if ((rc = ensure_grid(m, gi, m->grid_cells, s)) ||
                 (rc = m->cells[gi].ensure((size_t)nn * 4, s)))
                 return rc;
-            int32_t* grid = m->grid[gi].as<int32_t>();
+            int32_t* grid = m->grid.as<int32_t>();
             uint32_t* bits = m->bits[gi].as<uint32_t>();
             SMC_HIP(launch_dense_scatter(coords, n, g, grid, bits, m->cells[gi].as<int32_t>(), st,
                                          next, m->stale, s));

@@ -58,7 +58,9 @@ def test_async_build_reports_on_sync():
 
 
 def test_dense_forced_on_huge_grid():
-    coords = np.array([[0, 0, 0, 0], [0, 2094, 2094, 694]], np.int32)
+    # 8194 x 8194 x 1026 padded cells: past 2^36, where a bitmap word index
+    # would no longer fit an int32
+    coords = np.array([[0, 0, 0, 0], [0, 8191, 8191, 1023]], np.int32)
     m = smc.KernelMap()
     assert status_of(lambda: m.build(to_dev_i32(coords), route="dense")) == 9
     m.build(to_dev_i32(coords))                          # auto picks the sorted route

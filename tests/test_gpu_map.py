@@ -11,6 +11,16 @@ pytestmark = pytest.mark.gpu
 smc = pytest.importorskip("submanifold_sparse_convolution_amd")
 
 
+def auto_route(grid, pad=1):
+    """The route the library picks: dense when the padded grid's int32 ids and
+    two occupancy bitmaps (4.25 bytes a cell) fit 1/16 of the device's memory,
+    at most 16 GiB."""
+    import torch
+    cells = float(np.prod([g + 2 * pad for g in grid]))
+    budget = min(16 << 30, torch.cuda.get_device_properties(0).total_memory // 16)
+    return "dense" if cells * 4.25 <= budget and cells < 2.0 ** 36 else "sorted"
+
+
 def gpu_map(coords, route="auto", spatial_shape=None, batch_size=0, ncols=4):
     c = coords if ncols == 4 else coords[:, 1:]
     m = smc.KernelMap().build(to_dev_i32(c), spatial_shape=spatial_shape, batch_size=batch_size,
@@ -29,11 +39,11 @@ def test_workload_map_bit_exact(name):
     assert_map_equal(got, oracle_map(name), name)
     info = got["info"]
     assert info["pairs"] == len(oracle_map(name)["pair_in"])
-    assert info["route"] == ("sorted" if name == "wide" else "dense")
+    assert info["route"] == auto_route(w.grid)
     assert info["pairs_padded"] % info["tile_m"] == 0
 
 
-@pytest.mark.parametrize("name", ["tiny", "lidar", "deep"])
+@pytest.mark.parametrize("name", ["tiny", "lidar", "deep", "wide"])
 def test_dense_equals_sorted(name):
     w, coords = config(name)
     a = gpu_map(coords, route="dense", spatial_shape=w.grid)
@@ -47,7 +57,7 @@ def test_sorted_derived_shape_32bit_keys():
     """Keys are cells of the padded grid: the wide set's box (2095 x 2095 x 695 at
     most, 2 cells of padding per axis) needs 32 bits, not the 34 of bit fields."""
     _, coords = config("wide")
-    got = gpu_map(coords)                      # bounding box derived on the device
+    got = gpu_map(coords, route="sorted")      # bounding box derived on the device
     ext = coords[:, 1:].max(0) - coords[:, 1:].min(0) + 1
     cells = int(np.prod(ext.astype(np.int64) + 2))
     assert got["info"]["route"] == "sorted"
@@ -166,6 +176,24 @@ def test_route_switches_and_sizes_on_one_handle():
                     sort=sort)
             assert_map_equal(m.export(pairs=pairs, perm=sort), oracle_map_of(coords),
                              f"{route} n={n} pairs={pairs} sort={sort}")
+    m.close()
+
+
+def test_dense_rebuilds_beyond_2_31_cells():
+    """Dense builds on a 2095 x 2095 x 695 grid (3.06e9 padded cells): cell
+    indices past 2^31, bitmap words past 2^26. Sets near the far corner and near
+    the origin alternate on one handle, so each build's first kernel clears the
+    previous build's words in the other bitmap."""
+    grid = (2095, 2095, 695)
+    m = smc.KernelMap()
+    for seed, far in ((1, True), (2, False), (3, True), (4, True)):
+        coords = synth.ground_box_coords(2000, (60, 60, 20), seed=seed, n_boxes=6)
+        if far:
+            coords[:, 1:] += np.array([2095 - 60, 2095 - 60, 695 - 20], np.int32)
+        print(f"huge dense seed {seed} far={far}", flush=True)
+        m.build(to_dev_i32(coords), spatial_shape=grid, route="dense")
+        assert m.info()["route"] == "dense" and m.info()["grid_cells"] > 2 ** 31
+        assert_map_equal(m.export(), oracle_map_of(coords), f"seed {seed}")
     m.close()
 
 
