@@ -233,13 +233,14 @@ def rows_form(algo, kernel_size, c_in, c_out=None, strided=False):
 OUT_BITMAP_CELLS = 1 << 30      # strided output grids up to this many cells use the bitmap
 
 
-def strided_output_kernels(out_cells):
+def strided_output_kernels(out_cells, route="sorted"):
     """The kernels that find a strided map's output cells: a bitmap of the output
-    grid (mark, count per block, scan, write) or, for a larger grid, a radix sort
-    of 8 candidate keys per input (candidates, sort passes, unique count, scan,
-    unique write)."""
+    grid (mark, count per block, scan, write; on the dense route the input
+    scatter marks the bits) or, for a larger grid, a radix sort of 8 candidate
+    keys per input (candidates, sort passes, unique count, scan, unique write)."""
     if out_cells <= OUT_BITMAP_CELLS:
-        return ("k_stride_mark", "k_bits_count", "k_scan_counts", "k_bits_write")
+        mark = () if route == "dense" else ("k_stride_mark",)
+        return mark + ("k_bits_count", "k_scan_counts", "k_bits_write")
     return ("k_stride_candidates", "k_os_pass", "k_unique_count", "k_scan_counts",
             "k_unique_write")
 
@@ -265,7 +266,7 @@ def stage_kernels(stage, algo, route, kernel_size=3, strided=False, c_in=128, ou
         if strided:
             inputs = ("k_dense_scatter",) if route == "dense" else ("k_make_keys", "k_os_pass",
                                                                     "k_key_dups")
-            return inputs + strided_output_kernels(out_cells) + (
+            return inputs + strided_output_kernels(out_cells, route) + (
                 "k_dense_lookup" if route == "dense" else "k_query_lookup",)
         if route == "sorted":
             return ("k_make_keys", "k_os_pass", "k_sorted_lookup")

@@ -67,8 +67,10 @@ typedef enum smc_status {
  * bounding-box volume). */
 enum {
     SMC_ROUTE_AUTO = 0,   /* dense presence grid when its 4.25 bytes a cell (int32 ids,
-                             two occupancy bitmaps) fit 1/16 of the device's memory
-                             and at most 16 GiB, sorted packed keys otherwise */
+                             two occupancy bitmaps) fit 1/16 of the device's memory,
+                             at most 16 GiB, and (if the handle must allocate it)
+                             half the memory free at the build; sorted packed keys
+                             otherwise */
     SMC_ROUTE_DENSE = 1,  /* force the dense presence grid */
     SMC_ROUTE_SORTED = 2  /* force the sorted packed-key mapper */
 };

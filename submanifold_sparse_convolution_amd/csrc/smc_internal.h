@@ -145,9 +145,14 @@ hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 // cell's row id is only read when its bit is set, so the int32 grid needs no
 // initial fill and no reset; the bits of a build are cleared (whole words)
 // by the next build that uses the other grid. bits has 2 words of padding.
+// obits, sg (strided builds whose output cells go through a bitmap): each row
+// also sets the bits of the output cells it feeds (stride_mark), in the same
+// pass.
+struct StrideGeom;
 hipError_t launch_dense_scatter(const int32_t* coords, int64_t n, const Geom& g, int32_t* grid,
                                 uint32_t* bits, int32_t* cells, MapState* st,
-                                const NextRecord& next, const PrevCells& prev, hipStream_t s);
+                                const NextRecord& next, const PrevCells& prev, hipStream_t s,
+                                uint32_t* obits = nullptr, const StrideGeom* sg = nullptr);
 hipError_t launch_clear_cells(const PrevCells& prev, hipStream_t s);
 // nbr [n, K^3]; mask [n] (K = 3) or [n, 4] words (K = 5): g.ksize decides.
 hipError_t launch_dense_lookup(const int32_t* coords, int64_t n, const Geom& g, const int32_t* grid,
@@ -180,6 +185,54 @@ struct StrideGeom {
     uint64_t sentinel;
 };
 int64_t unique_blocks(int64_t n_c);
+
+// Output cells along one axis fed by input coordinate v: o = (v + pad - d) / s
+// for taps d with the division exact and o inside [0, oext).
+__device__ inline int axis_cands(int v, int oext, const StrideGeom& sg, int& o0, int& o1) {
+    int cnt = 0;
+#pragma unroll
+    for (int d = 0; d < 3; ++d) {
+        const int t = v + sg.pad - d;
+        const bool ok = t >= 0 && t % sg.stride == 0 && t / sg.stride < oext;
+        if (ok) {
+            if (cnt == 0) o0 = t / sg.stride;
+            else o1 = t / sg.stride;
+            ++cnt;
+        }
+    }
+    return cnt;                                   // at most 2 for K = 3, stride 2
+}
+
+// Bit of output cell (b, x, y, z) in the output-grid bitmap ((b, x, y, z) order).
+__device__ inline int64_t out_bit(const StrideGeom& sg, int b, int x, int y, int z) {
+    return (((int64_t)b * sg.oext[0] + x) * sg.oext[1] + y) * sg.oext[2] + z;
+}
+
+// Set the bits of the (at most 8) output cells that input cell (b, x, y, z),
+// relative to the grid origin and inside it, feeds. The z candidates are
+// neighbours (z0 = z1 + 1): their bits go out together, one atomic per
+// (x, y) unless they straddle a word.
+__device__ inline void stride_mark(const StrideGeom& sg, int b, int x, int y, int z,
+                                   uint32_t* __restrict__ obits) {
+    int x0 = 0, x1 = 0, y0 = 0, y1 = 0, z0 = 0, z1 = 0;
+    const int nx = axis_cands(x, sg.oext[0], sg, x0, x1);
+    const int ny = axis_cands(y, sg.oext[1], sg, y0, y1);
+    const int nz = axis_cands(z, sg.oext[2], sg, z0, z1);
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+            if (a < nx && e < ny) {
+                const int64_t L = out_bit(sg, b, a ? x1 : x0, e ? y1 : y0, nz == 2 ? z1 : z0);
+                const int lo = (int)(L & 31);
+                uint32_t bits = 1u << lo;
+                if (nz == 2) {
+                    if (lo != 31) bits |= 2u << lo;
+                    else atomicOr(&obits[(L >> 5) + 1], 1u);
+                }
+                atomicOr(&obits[L >> 5], bits);
+            }
+}
 // Output cells through a bitmap of the output grid (words of it, zero on entry
 // and left zero): coords -> output coords [M, 4] and query points [M, 4] in
 // (b, x, y, z) order, st->n_out = M; counts: out_bitmap_blocks(words) words of
@@ -187,10 +240,11 @@ int64_t unique_blocks(int64_t n_c);
 constexpr int64_t kOutBitmapWords = (int64_t)1 << 25;   // 128 MiB: larger grids sort candidates
 int64_t out_bitmap_words(const StrideGeom& sg, int batch);
 int64_t out_bitmap_blocks(int64_t words);
+// marked: the bits are set already (by the dense scatter of the same rows).
 hipError_t launch_stride_bitmap(const int32_t* coords, int64_t n, const Geom& g,
                                 const StrideGeom& sg, uint32_t* obits, int64_t words,
                                 uint32_t* counts, int32_t* ocoords, int32_t* qcoords,
-                                MapState* st, hipStream_t s);
+                                MapState* st, hipStream_t s, bool marked = false);
 // coords [n, ncols] -> 8 candidate output keys per row (sentinels where fewer)
 hipError_t launch_stride_candidates(const int32_t* coords, int64_t n, const Geom& g,
                                     const StrideGeom& sg, uint64_t* keys, MapState* st,

@@ -519,27 +519,33 @@ int smc_map_destroy(smc_map* m) {
 // back at once, or with defer the bound 8 n (the count stays on the device in
 // st->n_out for the kernels after, and reaches the host through rows_ev). The
 // input-side structure (grid or sorted keys) is built by the caller.
+// The output-grid bitmap (zero when allocated and between builds) and the
+// per-block counts of its bitmap route.
+static int prepare_obits(smc_map* m, int64_t words, hipStream_t s) {
+    const size_t want = (size_t)words * 4 + 4;
+    int rc;
+    if (want > m->obits.bytes) {
+        if ((rc = m->obits.ensure(want, s))) return rc;
+        SMC_HIP(launch_fill_i32(m->obits.as<int32_t>(), (int64_t)(m->obits.bytes / 4), 0, s));
+    }
+    const int64_t nb = out_bitmap_blocks(words);
+    if ((size_t)nb * 4 > m->ucounts.bytes && (rc = m->ucounts.ensure((size_t)nb * 4, s))) return rc;
+    return SMC_OK;
+}
+
+// marked: the dense scatter has set the output bits already (bitmap route).
 static int strided_outputs(smc_map* m, const int32_t* coords, int64_t n, const Geom& g,
                            const StrideGeom& sg, MapState* st, uint32_t* status, hipStream_t s,
-                           int64_t* rows, bool defer) {
+                           int64_t* rows, bool defer, bool marked) {
     const int64_t n_cand = 8 * n;
     // a small output grid: its cells through a bitmap, no candidate sort
     const int64_t words = out_bitmap_words(sg, g.batch);
     if (words <= kOutBitmapWords) {
-        const size_t want = (size_t)words * 4 + 4;
-        if (want > m->obits.bytes) {
-            int rc;
-            if ((rc = m->obits.ensure(want, s))) return rc;
-            SMC_HIP(launch_fill_i32(m->obits.as<int32_t>(), (int64_t)(m->obits.bytes / 4), 0, s));
-        }
-        const int64_t nb = out_bitmap_blocks(words);
-        if ((size_t)nb * 4 > m->ucounts.bytes) {
-            int rc;
-            if ((rc = m->ucounts.ensure((size_t)nb * 4, s))) return rc;
-        }
+        int rc;
+        if ((rc = prepare_obits(m, words, s))) return rc;
         SMC_HIP(launch_stride_bitmap(coords, n, g, sg, m->obits.as<uint32_t>(), words,
                                      m->ucounts.as<uint32_t>(), m->ocoords.as<int32_t>(),
-                                     m->qcoords.as<int32_t>(), st, s));
+                                     m->qcoords.as<int32_t>(), st, s, marked));
     } else {
         SMC_HIP(launch_stride_candidates(coords, n, g, sg, m->ck0.as<uint64_t>(), st, s));
         int bits = 1;
@@ -683,9 +689,20 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     } else if (route == SMC_ROUTE_SORTED) {
         chosen = SMC_ROUTE_SORTED;
     } else {
-        // ids (4 bytes a cell) and the two bitmaps
-        chosen = (dense_addressable && cells_d * 4.25 <= (double)m->dense_budget)
-                     ? SMC_ROUTE_DENSE : SMC_ROUTE_SORTED;
+        // ids (4 bytes a cell) and the two bitmaps; a grid this handle has not
+        // allocated yet must also fit half the device memory free now
+        const double need = cells_d * 4.25;
+        bool fits = dense_addressable && need <= (double)m->dense_budget;
+        if (fits && (double)m->grid.bytes < cells_d * 4.0) {
+            size_t free_b = 0, total_b = 0;
+            if (hipMemGetInfo(&free_b, &total_b) != hipSuccess) {
+                (void)hipGetLastError();
+                fits = false;
+            } else if (need > (double)free_b / 2) {
+                fits = false;
+            }
+        }
+        chosen = fits ? SMC_ROUTE_DENSE : SMC_ROUTE_SORTED;
     }
     g.sz_y = g.ext[2] + 2 * g.pad;
     g.sz_x = (int64_t)(g.ext[1] + 2 * g.pad) * g.sz_y;
@@ -818,8 +835,13 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
                 return rc;
             int32_t* grid = m->grid.as<int32_t>();
             uint32_t* bits = m->bits[gi].as<uint32_t>();
+            // a strided build on the output bitmap's route marks its output cells
+            // in the same pass
+            const bool mark = strided && out_bitmap_words(sg, g.batch) <= kOutBitmapWords;
+            if (mark && (rc = prepare_obits(m, out_bitmap_words(sg, g.batch), s))) return rc;
             SMC_HIP(launch_dense_scatter(coords, n, g, grid, bits, m->cells[gi].as<int32_t>(), st,
-                                         next, m->stale, s));
+                                         next, m->stale, s, mark ? m->obits.as<uint32_t>() : nullptr,
+                                         &sg));
             m->slot_clean[slot ^ 1] = true;
             m->stale.cells = m->cells[gi].as<int32_t>();
             m->stale.n = n;
@@ -835,7 +857,8 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
                                               m->chunk_pre.as<int32_t>(), m->ws, status, s));
                 t_cp.finish();
             } else if (strided) {
-                if ((rc = strided_outputs(m, coords, n, g, sg, st, status, s, &rows, defer_rows)))
+                if ((rc = strided_outputs(m, coords, n, g, sg, st, status, s, &rows, defer_rows,
+                                          mark)))
                     return rc;
                 Geom gq = g;                          // query points: [M, 4] in input coordinates
                 gq.ncols = 4;
@@ -896,7 +919,8 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
             }
             if (strided) {
                 SMC_HIP(launch_key_dups(skeys, m->wide, n, st, s));
-                if ((rc = strided_outputs(m, coords, n, g, sg, st, status, s, &rows, defer_rows)))
+                if ((rc = strided_outputs(m, coords, n, g, sg, st, status, s, &rows, defer_rows,
+                                          false)))
                     return rc;
                 SMC_HIP(launch_query_lookup(skeys, svals, n, g, m->wide, m->qcoords.as<int32_t>(),
                                             rows, nbr, mask, s, n_out_dev));

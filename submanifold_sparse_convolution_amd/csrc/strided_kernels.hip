@@ -39,23 +39,6 @@ __device__ inline uint64_t pack_out(const StrideGeom& sg, int b, int x, int y, i
     return k;
 }
 
-// Output cells along one axis fed by input coordinate v: o = (v + pad - d) / s
-// for taps d with the division exact and o inside [0, oext).
-__device__ inline int axis_cands(int v, int oext, const StrideGeom& sg, int& o0, int& o1) {
-    int cnt = 0;
-#pragma unroll
-    for (int d = 0; d < 3; ++d) {
-        const int t = v + sg.pad - d;
-        const bool ok = t >= 0 && t % sg.stride == 0 && t / sg.stride < oext;
-        if (ok) {
-            if (cnt == 0) o0 = t / sg.stride;
-            else o1 = t / sg.stride;
-            ++cnt;
-        }
-    }
-    return cnt;                                   // at most 2 for K = 3, stride 2
-}
-
 // Eight key slots per input row: the output cells it feeds, then the sentinel
 // (above every key: it sorts last and is dropped).
 __global__ __launch_bounds__(kBlock) void k_stride_candidates(const int32_t* __restrict__ coords,
@@ -220,10 +203,6 @@ __global__ __launch_bounds__(kUThreads) void k_unique_write(
 constexpr int kBWords = 4;                        // bitmap words per thread
 constexpr int kBTile = kUThreads * kBWords;       // words per count / write block
 
-__device__ inline int64_t out_bit(const StrideGeom& sg, int b, int x, int y, int z) {
-    return (((int64_t)b * sg.oext[0] + x) * sg.oext[1] + y) * sg.oext[2] + z;
-}
-
 __global__ __launch_bounds__(kBlock) void k_stride_mark(const int32_t* __restrict__ coords,
                                                         int64_t n, Geom g, StrideGeom sg,
                                                         uint32_t* __restrict__ obits,
@@ -240,26 +219,7 @@ __global__ __launch_bounds__(kBlock) void k_stride_mark(const int32_t* __restric
         atomicOr(&st->status, kStRange);
         return;
     }
-    int x0 = 0, x1 = 0, y0 = 0, y1 = 0, z0 = 0, z1 = 0;
-    const int nx = axis_cands(x, sg.oext[0], sg, x0, x1);
-    const int ny = axis_cands(y, sg.oext[1], sg, y0, y1);
-    const int nz = axis_cands(z, sg.oext[2], sg, z0, z1);
-    // the z candidates are neighbours (z0 = z1 + 1): their bits go out together,
-    // one atomic per (x, y) unless they straddle a word
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int e = 0; e < 2; ++e)
-            if (a < nx && e < ny) {
-                const int64_t L = out_bit(sg, b, a ? x1 : x0, e ? y1 : y0, nz == 2 ? z1 : z0);
-                const int lo = (int)(L & 31);
-                uint32_t bits = 1u << lo;
-                if (nz == 2) {
-                    if (lo != 31) bits |= 2u << lo;
-                    else atomicOr(&obits[(L >> 5) + 1], 1u);
-                }
-                atomicOr(&obits[L >> 5], bits);
-            }
+    stride_mark(sg, b, x, y, z, obits);
 }
 
 __global__ __launch_bounds__(kUThreads) void k_bits_count(const uint32_t* __restrict__ obits,
@@ -456,10 +416,11 @@ int64_t out_bitmap_blocks(int64_t words) { return (words + kBTile - 1) / kBTile;
 hipError_t launch_stride_bitmap(const int32_t* coords, int64_t n, const Geom& g,
                                 const StrideGeom& sg, uint32_t* obits, int64_t words,
                                 uint32_t* counts, int32_t* ocoords, int32_t* qcoords,
-                                MapState* st, hipStream_t s) {
+                                MapState* st, hipStream_t s, bool marked) {
     if (n <= 0 || words <= 0) return hipSuccess;
     const int64_t nb = out_bitmap_blocks(words);
-    launch(k_stride_mark, blocks_of(n, kBlock), kBlock, 0, s, coords, n, g, sg, obits, st);
+    if (!marked)
+        launch(k_stride_mark, blocks_of(n, kBlock), kBlock, 0, s, coords, n, g, sg, obits, st);
     launch(k_bits_count, (unsigned)nb, kUThreads, 0, s, (const uint32_t*)obits, words, counts);
     launch(k_scan_counts, 1u, 1024, 0, s, counts, nb, st);
     launch(k_bits_write, (unsigned)nb, kUThreads, 0, s, obits, words, sg, (const uint32_t*)counts,

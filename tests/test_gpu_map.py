@@ -12,12 +12,13 @@ smc = pytest.importorskip("submanifold_sparse_convolution_amd")
 
 
 def auto_route(grid, pad=1):
-    """The route the library picks: dense when the padded grid's int32 ids and
-    two occupancy bitmaps (4.25 bytes a cell) fit 1/16 of the device's memory,
-    at most 16 GiB."""
+    """The route the library picks for a fresh handle: dense when the padded
+    grid's int32 ids and two occupancy bitmaps (4.25 bytes a cell) fit 1/16 of
+    the device's memory, at most 16 GiB, and half the memory free now."""
     import torch
     cells = float(np.prod([g + 2 * pad for g in grid]))
     budget = min(16 << 30, torch.cuda.get_device_properties(0).total_memory // 16)
+    budget = min(budget, torch.cuda.mem_get_info()[0] / 2)
     return "dense" if cells * 4.25 <= budget and cells < 2.0 ** 36 else "sorted"
 
 
