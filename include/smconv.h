@@ -314,7 +314,8 @@ int smc_map_calibrate(smc_map* map, int n_groups, int32_t* bit_order, int32_t* g
 /* Bytes of the packed weight buffer for a K x K x K kernel (K = 3 or 5) and
  * c_in x c_out (both >= 1); 0 for an invalid request. Where the one-kernel
  * pair-list forward runs (K = 3, c_in and c_out <= 64, c_in a multiple of 8) the buffer
- * also holds that kernel's column tiles, packed after the others. */
+ * also holds that kernel's column tiles, packed after the others; for c_in <= 128
+ * and c_out > 64, the off-centre GEMM's 64-column tiles likewise. */
 size_t smc_weight_packed_bytes(int kernel_size, int c_in, int c_out);
 
 /*

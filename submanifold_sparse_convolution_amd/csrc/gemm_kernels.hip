@@ -916,17 +916,43 @@ void launch_centre_big(dim3 grid, size_t lds, hipStream_t s, bool out_f32, const
     }
 }
 
-}  // namespace
-
-size_t packed_weight_bytes(int taps, int c_in, int c_out) {
-    int64_t steps = (c_in + 31) / 32;
-    int nbw = nbw_for(c_out);
-    int64_t n_wt = (c_out + 16 * nbw - 1) / (16 * nbw);
-    return (size_t)(taps * n_wt * steps * nbw * 64 * 16) + rows_weight_bytes(taps, c_in, c_out);
+// Column blocks per wave tile of the off-centre GEMM's own packing, or 0 when it
+// reads the first packing. Where one chunk of weights is resident (C_in <= 128)
+// and the first packing has 8 blocks (128 columns), the off-centre kernel takes
+// tiles of 64 columns: twice the blocks, each staging half the weights, and its
+// gathered rows read once more from L2 (measured on the 91k-row set: 13.1 ->
+// 11.8 us; the centre GEMM stays at 128 columns: 64 made it slower, 17.7 ->
+// 18.1 us there and 15.8 -> 18.8 us on the 95k-row set).
+int nc_pack_nbw(int c_in, int c_out) {
+    return (c_in + 31) / 32 <= kChunk && nbw_for(c_out) == 8 ? 4 : 0;
 }
 
-// The packing above, plus (where the row-range GEMM runs and needs other
-// column tiles) a second one after it with that kernel's tile width.
+size_t first_pack_bytes(int taps, int c_in, int c_out) {
+    const int64_t steps = (c_in + 31) / 32;
+    const int nbw = nbw_for(c_out);
+    const int64_t n_wt = (c_out + 16 * nbw - 1) / (16 * nbw);
+    return (size_t)(taps * n_wt * steps * nbw * 64 * 16);
+}
+
+size_t nc_pack_bytes(int taps, int c_in, int c_out) {
+    const int nb = nc_pack_nbw(c_in, c_out);
+    if (nb == 0) return 0;
+    const int64_t steps = (c_in + 31) / 32;
+    const int64_t n_wt = (c_out + 16 * nb - 1) / (16 * nb);
+    return (size_t)(taps * n_wt * steps * nb * 64 * 16);
+}
+
+}  // namespace
+
+// The first packing, then (where the row-range GEMM runs and needs other
+// column tiles) that kernel's packing, or (nc_pack_nbw) the off-centre
+// kernel's; the two never occur together (C_out <= 64 against > 64).
+size_t packed_weight_bytes(int taps, int c_in, int c_out) {
+    return first_pack_bytes(taps, c_in, c_out) + rows_weight_bytes(taps, c_in, c_out) +
+           nc_pack_bytes(taps, c_in, c_out);
+}
+
+// The packings above, each with its own tile width.
 hipError_t launch_weight_pack(const uint16_t* w, int taps, int c_in, int c_out, void* out,
                               hipStream_t s) {
     int steps = (c_in + 31) / 32;
@@ -943,6 +969,14 @@ hipError_t launch_weight_pack(const uint16_t* w, int taps, int c_in, int c_out, 
         launch(k_weight_pack, (unsigned)((total2 + kBlock - 1) / kBlock), kBlock, 0, s, w, taps,
                c_in, c_out, nb2, n_q, steps,
                (uint4*)((char*)out + rows_weight_offset(taps, c_in, c_out)));
+    }
+    if (nc_pack_bytes(taps, c_in, c_out) > 0) {
+        const int nb3 = nc_pack_nbw(c_in, c_out);
+        const int n_q = (c_out + 16 * nb3 - 1) / (16 * nb3);
+        const int64_t total3 = (int64_t)taps * n_q * steps * nb3 * 64;
+        launch(k_weight_pack, (unsigned)((total3 + kBlock - 1) / kBlock), kBlock, 0, s, w, taps,
+               c_in, c_out, nb3, n_q, steps,
+               (uint4*)((char*)out + first_pack_bytes(taps, c_in, c_out)));
     }
     return hipGetLastError();
 }
@@ -978,13 +1012,20 @@ hipError_t launch_gemm_nc(const uint16_t* x, int c_in, const void* wpacked, int 
     if (gx > (int64_t)n_cu * 4) gx = (int64_t)n_cu * 4;
     if (gx < 1) gx = 1;
     gx = xcd_round(gx);
-    dim3 grid((unsigned)gx, (unsigned)n_wt);
-    const u32x4* wp = (const u32x4*)wpacked;
-    switch (nbw) {
-        case 1: launch_nc<1>(grid, s, mw, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part, sc, y, ym); break;
-        case 2: launch_nc<2>(grid, s, mw, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part, sc, y, ym); break;
-        case 4: launch_nc<4>(grid, s, mw, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part, sc, y, ym); break;
-        default: launch_nc<8>(grid, s, mw, x, c_in, steps, wp, n_wt, c_out, taps, pair_in, pair_slot, st, cap, n, part, sc, y, ym); break;
+    // its own packing where it has one (nc_pack_nbw), on submanifold maps: a
+    // strided map's 27 taps of pair lists were slower in 64-column tiles
+    // (91k-input layer 39.4 -> 51.9 us, 32k-input 20.3 -> 24.7 us)
+    const int nb_own = skip_centre ? nc_pack_nbw(c_in, c_out) : 0;
+    const int nbw_nc = nb_own ? nb_own : nbw;
+    const int n_wt_nc = nb_own ? (c_out + 16 * nb_own - 1) / (16 * nb_own) : n_wt;
+    const u32x4* wp = (const u32x4*)((const char*)wpacked +
+                                     (nb_own ? first_pack_bytes(taps, c_in, c_out) : 0));
+    dim3 grid((unsigned)gx, (unsigned)n_wt_nc);
+    switch (nbw_nc) {
+        case 1: launch_nc<1>(grid, s, mw, x, c_in, steps, wp, n_wt_nc, c_out, taps, pair_in, pair_slot, st, cap, n, part, sc, y, ym); break;
+        case 2: launch_nc<2>(grid, s, mw, x, c_in, steps, wp, n_wt_nc, c_out, taps, pair_in, pair_slot, st, cap, n, part, sc, y, ym); break;
+        case 4: launch_nc<4>(grid, s, mw, x, c_in, steps, wp, n_wt_nc, c_out, taps, pair_in, pair_slot, st, cap, n, part, sc, y, ym); break;
+        default: launch_nc<8>(grid, s, mw, x, c_in, steps, wp, n_wt_nc, c_out, taps, pair_in, pair_slot, st, cap, n, part, sc, y, ym); break;
     }
     return hipGetLastError();
 }

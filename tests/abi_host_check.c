@@ -37,7 +37,7 @@ int main(void) {
     EXPECT(smc_version() >= 100, 1);
     EXPECT(strcmp(smc_status_string(SMC_OK), "ok"), 0);
     EXPECT(strcmp(smc_status_string(999), "unknown status"), 0);
-    EXPECT(smc_weight_packed_bytes(3, 128, 128), 27 * 8 * 4 * 64 * 16);
+    EXPECT(smc_weight_packed_bytes(3, 128, 128), 2 * 27 * 8 * 4 * 64 * 16); /* + 64-column tiles */
     EXPECT(smc_weight_packed_bytes(3, 64, 64), 2 * 27 * 4 * 2 * 64 * 16); /* two packings */
     EXPECT(smc_weight_packed_bytes(3, 136, 128), 27 * 8 * 5 * 64 * 16);
     EXPECT(smc_weight_packed_bytes(3, 0, 5), 0);

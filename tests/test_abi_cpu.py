@@ -50,10 +50,14 @@ def test_static_calls(L):
     # packed weights: K^3 taps x ceil(co/16) x ceil(ci/32) x 64 lanes x 16 bytes
     # (column blocks padded to the wave tile), and for K = 3 with c_in, c_out
     # <= 64 (c_in a multiple of 8) a second copy in 32-column tiles for the
-    # one-kernel forward, unless the first already has 2 column blocks per tile
-    assert L.smc_weight_packed_bytes(3, 128, 128) == 27 * 8 * 4 * 64 * 16
+    # one-kernel forward, unless the first already has 2 column blocks per tile;
+    # for c_in <= 128 and c_out > 64 a second copy in 64-column tiles for the
+    # off-centre kernel
+    assert L.smc_weight_packed_bytes(3, 128, 128) == 2 * 27 * 8 * 4 * 64 * 16
     assert L.smc_weight_packed_bytes(3, 64, 64) == 2 * 27 * 4 * 2 * 64 * 16
-    assert L.smc_weight_packed_bytes(3, 64, 128) == 27 * 8 * 2 * 64 * 16
+    assert L.smc_weight_packed_bytes(3, 64, 128) == 2 * 27 * 8 * 2 * 64 * 16
+    assert L.smc_weight_packed_bytes(3, 32, 96) == 27 * 8 * 64 * 16 + 27 * 2 * 4 * 64 * 16
+    assert L.smc_weight_packed_bytes(3, 40, 72) == 27 * 8 * 2 * 64 * 16 + 27 * 2 * 2 * 4 * 64 * 16
     assert L.smc_weight_packed_bytes(3, 16, 32) == 27 * 2 * 1 * 64 * 16
     assert L.smc_weight_packed_bytes(3, 136, 128) == 27 * 8 * 5 * 64 * 16
     assert L.smc_weight_packed_bytes(3, 1, 1) == 27 * 1 * 1 * 64 * 16
