@@ -106,7 +106,8 @@ typedef struct smc_map_info_s {
     int32_t extent[3];      /* grid extent (X, Y, Z) */
     int32_t batch;          /* number of batches B */
     int32_t tile_m;         /* pairs per GEMM tile */
-    int64_t grid_cells;     /* dense route: cells of the padded presence grid; sorted: 0 */
+    int64_t grid_cells;     /* dense route: cells of the padded presence grid (in whole
+                               8 x 8 x 16 bricks when Z + 2 r >= 256); sorted: 0 */
     int64_t pairs;          /* P: valid (input, output) pairs including the centre tap */
     int64_t pairs_padded;   /* sum over taps of tap_count rounded up to tile_m (0 without pairs) */
     int64_t n_tiles;        /* pairs_padded / tile_m: GEMM tiles of all taps (0 without pairs) */

@@ -532,7 +532,7 @@ __global__ __launch_bounds__(kCThreads) void k_compact(
 // occupied ones. SPARSE: the rows are a strided map's query points (input
 // coordinates of 2 o), whose centre cell is looked up like the other taps (the
 // input at 2 o may be absent).
-template <bool SPARSE>
+template <bool SPARSE, bool BRICK>
 struct DenseLookup {
     static constexpr bool kDenseCentre = !SPARSE;
     const int32_t* coords;
@@ -548,21 +548,21 @@ struct DenseLookup {
         const bool ok = row < n && (unsigned)b < (unsigned)g.batch &&
                         (unsigned)x < (unsigned)g.ext[0] && (unsigned)y < (unsigned)g.ext[1] &&
                         (unsigned)z < (unsigned)g.ext[2];
-        // cell (x, y, z - 1) of the padded grid (g.pad cells of padding a side),
-        // whose 3x3x3 neighbourhood starts at c0 - sz_x - sz_y. Rows out of range
-        // (and rows past n) read the neighbourhood of padded cell (1, 1, 0)
-        // instead, which lies inside the grid; their values are unused.
-        const int64_t c0 = ok ? b * g.sz_b + (int64_t)(x + g.pad) * g.sz_x +
-                                    (int64_t)(y + g.pad) * g.sz_y + (z + g.pad - 1)
-                              : g.sz_x + g.sz_y;
-        // occupancy of the 9 (dx, dy) columns (3 bits each, two words per column) ...
+        // the row's cell in the padded grid (g.pad cells of padding a side), z
+        // one lower: its 3x3x3 neighbourhood is (xp - 1 .. xp + 1, yp - 1 ..
+        // yp + 1, zp .. zp + 2). Rows out of range (and rows past n) read the
+        // neighbourhood of padded cell (1, 1, 1) of batch 0 instead, which lies
+        // inside the grid; their values are unused.
+        const int bb = ok ? b : 0;
+        const int64_t xp = ok ? x + g.pad : 1, yp = ok ? y + g.pad : 1;
+        const int64_t zp = ok ? z + g.pad - 1 : 0;
+        // occupancy of the 9 (dx, dy) columns (3 bits each) ...
         uint32_t cb[9];
 #pragma unroll
         for (int dx = 0; dx < 3; ++dx)
 #pragma unroll
             for (int dy = 0; dy < 3; ++dy)
-                cb[3 * dx + dy] =
-                    cell_bits(bits, c0 + (int64_t)(dx - 1) * g.sz_x + (int64_t)(dy - 1) * g.sz_y, 3);
+                cb[3 * dx + dy] = column_bits<BRICK>(bits, g, bb, xp + dx - 1, yp + dy - 1, zp, 3);
         // ... then row ids of the occupied cells only. Every tap issues its load; an
         // empty one reads cell 0 (one line, cached for the whole launch), so no load
         // is conditional.
@@ -575,8 +575,7 @@ struct DenseLookup {
                     const int k = 9 * dx + 3 * dy + dz;
                     if (!SPARSE && k == kCentre) continue;
                     const bool on = (cb[3 * dx + dy] >> dz) & 1u;
-                    const int64_t cc =
-                        c0 + (int64_t)(dx - 1) * g.sz_x + (int64_t)(dy - 1) * g.sz_y + dz;
+                    const int64_t cc = grid_cell<BRICK>(g, bb, xp + dx - 1, yp + dy - 1, zp + dz);
                     v[k] = grid[on ? cc : 0];
                     v[k] = on ? v[k] : -1;
                 }
@@ -846,7 +845,7 @@ size_t compact_look_bytes_k(int64_t n, int ksize) {
 // query failed).
 static int64_t resident_blocks(const void* kern, int slot) {
     constexpr int kDevs = 64;
-    static std::atomic<int64_t> cache[kDevs][4];
+    static std::atomic<int64_t> cache[kDevs][6];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) return 0;
     int64_t cap = cache[dev][slot].load(std::memory_order_relaxed);
@@ -936,12 +935,21 @@ hipError_t launch_lookup_compact(const int32_t* coords, int64_t n, const Geom& g
                                  int32_t* pair_slot, int32_t* rowbase, int32_t* chunk_pre,
                                  SortWork& ws, uint32_t* status, hipStream_t s, bool sparse_centre,
                                  const int32_t* n_dev) {
-    if (sparse_centre)
-        return launch_lookup_compact_t(DenseLookup<true>{coords, g, grid, bits}, 3, n, nbr, mask,
-                                       cap, tile_m, st, pair_in, pair_out, pair_slot, rowbase,
+    // (resident-block cache slots 2 .. 5, one per instance)
+    if (sparse_centre && g.brick)
+        return launch_lookup_compact_t(DenseLookup<true, true>{coords, g, grid, bits}, 5, n, nbr,
+                                       mask, cap, tile_m, st, pair_in, pair_out, pair_slot, rowbase,
                                        chunk_pre, ws, status, s, n_dev);
-    return launch_lookup_compact_t(DenseLookup<false>{coords, g, grid, bits}, 2, n, nbr, mask, cap,
-                                   tile_m, st, pair_in, pair_out, pair_slot, rowbase, chunk_pre,
+    if (sparse_centre)
+        return launch_lookup_compact_t(DenseLookup<true, false>{coords, g, grid, bits}, 3, n, nbr,
+                                       mask, cap, tile_m, st, pair_in, pair_out, pair_slot, rowbase,
+                                       chunk_pre, ws, status, s, n_dev);
+    if (g.brick)
+        return launch_lookup_compact_t(DenseLookup<false, true>{coords, g, grid, bits}, 4, n, nbr,
+                                       mask, cap, tile_m, st, pair_in, pair_out, pair_slot, rowbase,
+                                       chunk_pre, ws, status, s, n_dev);
+    return launch_lookup_compact_t(DenseLookup<false, false>{coords, g, grid, bits}, 2, n, nbr, mask,
+                                   cap, tile_m, st, pair_in, pair_out, pair_slot, rowbase, chunk_pre,
                                    ws, status, s, n_dev);
 }
 

@@ -31,8 +31,8 @@ __device__ inline bool load_rel(const int32_t* __restrict__ coords, int64_t i, c
            (unsigned)y < (unsigned)g.ext[1] && (unsigned)z < (unsigned)g.ext[2];
 }
 
-// cell of a voxel in the grid padded by r cells on every side (also the
-// sorted route's key)
+// linear cell of a voxel in the grid padded by r cells on every side: the
+// sorted route's key
 __device__ inline int64_t dense_cell(const Geom& g, int b, int x, int y, int z) {
     return b * g.sz_b + (int64_t)(x + g.pad) * g.sz_x + (int64_t)(y + g.pad) * g.sz_y + (z + g.pad);
 }
@@ -150,7 +150,8 @@ __global__ __launch_bounds__(kBlock) void k_dense_scatter(const int32_t* __restr
         cells[i] = -1;
         return;
     }
-    const int64_t cell = dense_cell(g, b, x, y, z);
+    const int64_t cell = g.brick ? grid_cell<true>(g, b, x + g.pad, y + g.pad, z + g.pad)
+                                 : grid_cell<false>(g, b, x + g.pad, y + g.pad, z + g.pad);
     cells[i] = (int32_t)(cell >> 5);             // its bitmap word (grids below 2^36 cells)
     const uint32_t bit = 1u << (cell & 31);
     const uint32_t old = atomicOr(&bits[cell >> 5], bit);
@@ -169,11 +170,11 @@ __global__ __launch_bounds__(kBlock) void k_clear_cells(PrevCells prev) {
 }
 
 // 16 lanes per row (9 active), lane c for the (dx, dy) column c = 3 (dx + 1) +
-// (dy + 1). The column's cells z - 1 .. z + 1 are consecutive in the grid, so
-// one 64-bit window of occupancy bits (two words) gives its 3 taps 3c .. 3c +
-// 2, and only occupied cells read the grid. The lane writes those 3
+// (dy + 1). The column's occupancy bits of z - 1 .. z + 1 give its 3 taps
+// 3c .. 3c + 2, and only occupied cells read the grid. The lane writes those 3
 // neighbour entries (a row's 27 are contiguous); the row's mask is ORed
 // together from the lanes' 3-bit patterns.
+template <bool BRICK>
 __global__ __launch_bounds__(kBlock) void k_dense_lookup(const int32_t* __restrict__ coords,
                                                          int64_t n, Geom g,
                                                          const int32_t* __restrict__ grid,
@@ -189,14 +190,12 @@ __global__ __launch_bounds__(kBlock) void k_dense_lookup(const int32_t* __restri
         int v[3] = {-1, -1, -1};
         int b, x, y, z;
         if (load_rel(coords, row, g, b, x, y, z)) {
-            const int dx = c / 3 - 1, dy = c % 3 - 1;
-            const int64_t c0 = dense_cell(g, b, x, y, z) + dx * g.sz_x + dy * g.sz_y - 1;
-            // (the bit array has a word of slack past the last cell's)
-            const uint64_t win = ((uint64_t)bits[(c0 >> 5) + 1] << 32) | bits[c0 >> 5];
-            pat = (uint32_t)(win >> (c0 & 31)) & 7u;
+            const int64_t xp = x + g.pad + c / 3 - 1, yp = y + g.pad + c % 3 - 1;
+            const int64_t zp = z + g.pad - 1;
+            pat = column_bits<BRICK>(bits, g, b, xp, yp, zp, 3);
 #pragma unroll
             for (int j = 0; j < 3; ++j)
-                if ((pat >> j) & 1u) v[j] = grid[c0 + j];
+                if ((pat >> j) & 1u) v[j] = grid[grid_cell<BRICK>(g, b, xp, yp, zp + j)];
         }
         int32_t* dst = nbr + row * kTaps + 3 * c;
 #pragma unroll
@@ -209,12 +208,12 @@ __global__ __launch_bounds__(kBlock) void k_dense_lookup(const int32_t* __restri
 }
 
 // 5 x 5 x 5 kernel: 32 lanes per row (25 active), lane c for the (dx, dy)
-// column c = 5 (dx + 2) + (dy + 2). The column's cells z - 2 .. z + 2 are
-// consecutive in the grid, so one 64-bit window of occupancy bits (two
-// words) gives its 5 taps 5c .. 5c + 4, and only occupied cells read the
+// column c = 5 (dx + 2) + (dy + 2). The column's occupancy bits of z - 2 ..
+// z + 2 give its 5 taps 5c .. 5c + 4, and only occupied cells read the
 // grid. The lane writes those 5 neighbour entries (a row's 125 are
 // contiguous); the row's 4 mask words are ORed together from the lanes'
 // 5-bit patterns.
+template <bool BRICK>
 __global__ __launch_bounds__(kBlock) void k_dense_lookup5(const int32_t* __restrict__ coords,
                                                           int64_t n, Geom g,
                                                           const int32_t* __restrict__ grid,
@@ -230,14 +229,12 @@ __global__ __launch_bounds__(kBlock) void k_dense_lookup5(const int32_t* __restr
         int v[5] = {-1, -1, -1, -1, -1};
         int b, x, y, z;
         if (load_rel(coords, row, g, b, x, y, z)) {
-            const int dx = c / 5 - 2, dy = c % 5 - 2;
-            const int64_t c0 = dense_cell(g, b, x, y, z) + dx * g.sz_x + dy * g.sz_y - 2;
-            // (the bit array has a word of slack past the last cell's)
-            const uint64_t win = ((uint64_t)bits[(c0 >> 5) + 1] << 32) | bits[c0 >> 5];
-            pat = (uint32_t)(win >> (c0 & 31)) & 31u;
+            const int64_t xp = x + g.pad + c / 5 - 2, yp = y + g.pad + c % 5 - 2;
+            const int64_t zp = z + g.pad - 2;
+            pat = column_bits<BRICK>(bits, g, b, xp, yp, zp, 5);
 #pragma unroll
             for (int j = 0; j < 5; ++j)
-                if ((pat >> j) & 1u) v[j] = grid[c0 + j];
+                if ((pat >> j) & 1u) v[j] = grid[grid_cell<BRICK>(g, b, xp, yp, zp + j)];
         }
         int32_t* dst = nbr + row * kT + 5 * c;
 #pragma unroll
@@ -490,12 +487,20 @@ hipError_t launch_clear_cells(const PrevCells& prev, hipStream_t s) {
 
 hipError_t launch_dense_lookup(const int32_t* coords, int64_t n, const Geom& g, const int32_t* grid,
                                const uint32_t* bits, int32_t* nbr, uint32_t* mask, hipStream_t s) {
-    if (g.ksize == 5)
-        launch(k_dense_lookup5, blocks_for(n * 32), kBlock, 0, s, coords, n, g, grid, bits, nbr,
-               mask);
-    else
-        launch(k_dense_lookup, blocks_for(n * 16), kBlock, 0, s, coords, n, g, grid, bits, nbr,
-               mask);
+    if (g.ksize == 5) {
+        if (g.brick)
+            launch(k_dense_lookup5<true>, blocks_for(n * 32), kBlock, 0, s, coords, n, g, grid,
+                   bits, nbr, mask);
+        else
+            launch(k_dense_lookup5<false>, blocks_for(n * 32), kBlock, 0, s, coords, n, g, grid,
+                   bits, nbr, mask);
+    } else if (g.brick) {
+        launch(k_dense_lookup<true>, blocks_for(n * 16), kBlock, 0, s, coords, n, g, grid, bits,
+               nbr, mask);
+    } else {
+        launch(k_dense_lookup<false>, blocks_for(n * 16), kBlock, 0, s, coords, n, g, grid, bits,
+               nbr, mask);
+    }
     return hipGetLastError();
 }
 

@@ -6,6 +6,7 @@
 #include <mutex>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -680,20 +681,26 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     const double pad2 = 2.0 * g.pad;
     const double cells_d =
         (double)g.batch * (g.ext[0] + pad2) * (g.ext[1] + pad2) * (g.ext[2] + pad2);
-    const bool dense_addressable = cells_d < kDenseMaxCells;
+    // the dense route's cells: tall grids in whole bricks of 8 x 8 x 16 (brick_cell)
+    const bool brick = g.ext[2] + 2 * g.pad >= kBrickMinZ;
+    const double grid_cells_d = brick ? (double)g.batch * std::ceil((g.ext[0] + pad2) / 8.0) *
+                                            std::ceil((g.ext[1] + pad2) / 8.0) *
+                                            std::ceil((g.ext[2] + pad2) / 16.0) * 1024.0
+                                      : cells_d;
+    const bool dense_addressable = grid_cells_d < kDenseMaxCells;
     int chosen;
     if (route == SMC_ROUTE_DENSE) {
         if (!dense_addressable)
-            return fail(SMC_ERR_GRID, "dense grid of %.3g cells exceeds 2^36", cells_d);
+            return fail(SMC_ERR_GRID, "dense grid of %.3g cells exceeds 2^36", grid_cells_d);
         chosen = SMC_ROUTE_DENSE;
     } else if (route == SMC_ROUTE_SORTED) {
         chosen = SMC_ROUTE_SORTED;
     } else {
         // ids (4 bytes a cell) and the two bitmaps; a grid this handle has not
         // allocated yet must also fit half the device memory free now
-        const double need = cells_d * 4.25;
+        const double need = grid_cells_d * 4.25;
         bool fits = dense_addressable && need <= (double)m->dense_budget;
-        if (fits && (double)m->grid.bytes < cells_d * 4.0) {
+        if (fits && (double)m->grid.bytes < grid_cells_d * 4.0) {
             size_t free_b = 0, total_b = 0;
             if (hipMemGetInfo(&free_b, &total_b) != hipSuccess) {
                 (void)hipGetLastError();
@@ -707,6 +714,10 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     g.sz_y = g.ext[2] + 2 * g.pad;
     g.sz_x = (int64_t)(g.ext[1] + 2 * g.pad) * g.sz_y;
     g.sz_b = (int64_t)(g.ext[0] + 2 * g.pad) * g.sz_x;
+    g.bs_y = (g.ext[2] + 2 * g.pad + 15) / 16;
+    g.bs_x = (int64_t)((g.ext[1] + 2 * g.pad + 7) / 8) * g.bs_y;
+    g.bs_b = (int64_t)((g.ext[0] + 2 * g.pad + 7) / 8) * g.bs_x;
+    g.brick = chosen == SMC_ROUTE_DENSE && brick ? 1 : 0;
     int key_bits = 0;
     if (chosen == SMC_ROUTE_SORTED) {
         // keys are cells of the padded grid: 0 .. cells - 1
@@ -735,7 +746,8 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     m->route = chosen;
     m->key_bits = key_bits;
     m->wide = key_bits > 32;
-    m->grid_cells = chosen == SMC_ROUTE_DENSE ? (int64_t)cells_d : 0;
+    m->grid_cells = chosen != SMC_ROUTE_DENSE ? 0
+                    : g.brick ? (int64_t)g.batch * g.bs_b * 1024 : (int64_t)g.batch * g.sz_b;
     m->n = n;
 
     // ---- buffers ----

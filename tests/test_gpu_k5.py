@@ -81,6 +81,18 @@ def test_k5_dense_equals_sorted_and_ncols3():
     assert_map_equal(a, oracle_map5(coords), "k5 vs oracle")
 
 
+def test_k5_bricked_dense_grid():
+    """5 x 5 x 5 taps on a tall grid (bricked dense layout): each column's
+    5-cell run crosses a 16-cell brick face for a quarter of the rows."""
+    rng = np.random.default_rng(9)
+    a = synth.box_coords(10, 9, 44, origin=(2, 6, 7), batch=0)
+    coords = a[rng.random(len(a)) < 0.5]
+    coords = coords[rng.permutation(len(coords))].astype(np.int32)
+    got = gpu_map5(coords, route="dense", spatial_shape=(24, 24, 260))
+    assert got["info"]["route"] == "dense"
+    assert_map_equal(got, oracle_map5(coords), "k5 bricked")
+
+
 def test_k5_wide_grid_64bit_keys():
     """A grid too large for the dense route: 64-bit packed keys with two cells of
     padding per field."""

@@ -16,7 +16,11 @@ def auto_route(grid, pad=1):
     grid's int32 ids and two occupancy bitmaps (4.25 bytes a cell) fit 1/16 of
     the device's memory, at most 16 GiB, and half the memory free now."""
     import torch
-    cells = float(np.prod([g + 2 * pad for g in grid]))
+    # tall grids (Z + 2 pad >= 256) in whole bricks of 8 x 8 x 16 cells
+    if grid[2] + 2 * pad >= 256:
+        cells = float(np.prod([-(-(g + 2 * pad) // d) * d for g, d in zip(grid, (8, 8, 16))]))
+    else:
+        cells = float(np.prod([g + 2 * pad for g in grid]))
     budget = min(16 << 30, torch.cuda.get_device_properties(0).total_memory // 16)
     budget = min(budget, torch.cuda.mem_get_info()[0] / 2)
     return "dense" if cells * 4.25 <= budget and cells < 2.0 ** 36 else "sorted"
@@ -196,6 +200,37 @@ def test_dense_rebuilds_beyond_2_31_cells():
         assert m.info()["route"] == "dense" and m.info()["grid_cells"] > 2 ** 31
         assert_map_equal(m.export(), oracle_map_of(coords), f"seed {seed}")
     m.close()
+
+
+def tall_grid_coords(seed, batch=1):
+    """Two boxes in a 40 x 40 x 300 grid (302 padded cells along z: the dense
+    route's bricked layout), spanning several 16-cell bricks along z and 8-cell
+    bricks along x and y, sparsified so masks vary."""
+    rng = np.random.default_rng(seed)
+    a = synth.box_coords(9, 10, 40, origin=(3, 5, 10), batch=0)
+    b = synth.box_coords(12, 7, 25, origin=(20, 14, 270), batch=batch - 1)
+    c = np.concatenate([a, b])
+    c = c[rng.random(len(c)) < 0.6]
+    return c[rng.permutation(len(c))].astype(np.int32)
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_bricked_dense_grid(seed):
+    """A tall grid maps through bricks of 8 x 8 x 16 cells; rows next to brick
+    faces read their column bits from two bricks. Bit-exact against the oracle
+    and the sorted route, with a rebuild on the same handle in between."""
+    coords = tall_grid_coords(seed)
+    want = oracle_map_of(coords)
+    m = smc.KernelMap()
+    for rep in range(2):
+        m.build(to_dev_i32(coords), spatial_shape=(40, 40, 300), route="dense")
+        info = m.info()
+        assert info["route"] == "dense"
+        assert info["grid_cells"] == 48 * 48 * 304      # 6 x 6 x 19 bricks of 1,024 cells
+        assert_map_equal(m.export(), want, f"bricked seed {seed} build {rep}")
+    m.close()
+    assert_map_equal(gpu_map(coords, route="sorted", spatial_shape=(40, 40, 300)), want,
+                     f"sorted seed {seed}")
 
 
 def test_map_is_deterministic():
