@@ -235,11 +235,14 @@ OUT_BITMAP_CELLS = 1 << 30      # strided output grids up to this many cells use
 
 def strided_output_kernels(out_cells, route="sorted"):
     """The kernels that find a strided map's output cells: a bitmap of the output
-    grid (mark, count per block, scan, write; on the dense route the input
-    scatter marks the bits) or, for a larger grid, a radix sort of 8 candidate
-    keys per input (candidates, sort passes, unique count, scan, unique write)."""
+    grid (mark, then count, scan and write; on the dense route the input scatter
+    marks the bits; a bitmap of at most 2 chunks of 1,024 words per CU in one
+    look-back pass) or, for a larger grid, a radix sort of 8 candidate keys per
+    input (candidates, sort passes, unique count, scan, unique write)."""
     if out_cells <= OUT_BITMAP_CELLS:
         mark = () if route == "dense" else ("k_stride_mark",)
+        if (out_cells + 31) // 32 <= 2 * 256 * 1024:
+            return mark + ("k_bits_emit",)
         return mark + ("k_bits_count", "k_scan_counts", "k_bits_write")
     return ("k_stride_candidates", "k_os_pass", "k_unique_count", "k_scan_counts",
             "k_unique_write")

@@ -18,6 +18,7 @@
 // atomics and no accumulator to clear.
 #include <atomic>
 
+#include "lookback.h"
 #include "smc_internal.h"
 
 namespace smc {
@@ -31,131 +32,6 @@ constexpr int kCWaves = kCThreads / 64;
 constexpr int kCChunk = kCThreads;                // rows per compaction block (one per thread)
 constexpr int kCNbrVec = kCChunk * kTaps / 4;     // 16-byte words of the chunk's neighbour rows
 constexpr int kCNbrPer = (kCNbrVec + kCThreads - 1) / kCThreads;
-constexpr uint32_t kSpinLimit = 1u << 22;
-constexpr uint64_t kAgg = 1, kIncl = 2;
-
-__device__ inline uint64_t lb_pack(uint32_t epoch, uint64_t state, uint32_t count) {
-    return ((uint64_t)epoch << 34) | (state << 32) | count;
-}
-
-// Sum of column d of the look-back table over blocks pb, pb-1, ... back to
-// the first inclusive entry (W loads per round trip).
-template <int W>
-__device__ inline uint32_t lookback(uint64_t* look, int stride, int d, int64_t pb, uint32_t epoch,
-                                    uint32_t* status) {
-    const uint32_t ep = epoch & 0x3FFFFFFFu;
-    uint32_t prefix = 0;
-    uint32_t spins = 0;
-    while (pb >= 0) {
-        uint64_t e[W];
-#pragma unroll
-        for (int j = 0; j < W; ++j)
-            e[j] = pb - j >= 0 ? __hip_atomic_load(&look[(pb - j) * stride + d], __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT)
-                               : 0;
-#pragma unroll
-        for (int j = 0; j < W; ++j) {
-            if (pb - j < 0) return prefix;
-            while ((uint32_t)(e[j] >> 34) != ep) {
-                if (++spins > kSpinLimit) {
-                    atomicOr(status, kStSortStall);
-                    return prefix;
-                }
-                __builtin_amdgcn_s_sleep(1);
-                e[j] = __hip_atomic_load(&look[(pb - j) * stride + d], __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-            }
-            prefix += (uint32_t)e[j];
-            if (((e[j] >> 32) & 3u) == kIncl) return prefix;
-        }
-        pb -= W;
-    }
-    return prefix;
-}
-
-// Prefix of column k (k < NC) over blocks pb, pb-1, ..., read by the whole
-// block: thread t < kLanes NC covers column t % NC and every kLanes-th
-// predecessor starting at pb - t / NC, W of them per round trip (kLanes W
-// predecessors per column per round). A round finds, per column, the nearest
-// entry that holds an inclusive prefix (LDS minimum of the distance), and
-// sums the entries up to and including it; columns without one go on to the
-// next round. Two barriers per round: the distance minima and the "some
-// column still open" flag alternate between two LDS slots by round parity,
-// so a slot is reset only after every thread has read it. Every thread of the
-// block must call this. The result is in s_sum[k] on return.
-// spin_limit bounds the waits of each thread; wait_xor (0 in every build but
-// the forced-timeout test, see smc_test_force_lookback_timeout) makes the
-// block wait for an epoch no block publishes, so that every wait runs out.
-template <int NC, int W, int kLanes>
-__device__ void block_lookback(uint64_t* look, int64_t pb, uint32_t epoch, uint32_t* status,
-                               uint32_t* s_sum, uint32_t* s_done, uint32_t spin_limit = kSpinLimit,
-                               uint32_t wait_xor = 0u) {
-    static_assert(kLanes * NC <= 256, "one thread per (column, lane)");
-    __shared__ uint32_t s_near[2][NC];
-    __shared__ uint32_t s_open[2];
-    const int tid = threadIdx.x;
-    const int k = tid % NC, j0 = tid / NC;
-    const bool active = tid < kLanes * NC;
-    const uint32_t ep = (epoch ^ wait_xor) & 0x3FFFFFFFu;
-    if (tid < NC) {
-        s_sum[tid] = 0;
-        s_done[tid] = pb < 0 ? 1u : 0u;
-        s_near[0][tid] = 0xFFFFFFFFu;
-    }
-    __syncthreads();
-    uint32_t spins = 0;
-    int r = 0;
-    for (int64_t top = pb; top >= 0; top -= kLanes * W, r ^= 1) {
-        const bool go = active && !s_done[k];
-        uint64_t e[W];
-        uint32_t near = 0xFFFFFFFFu;
-#pragma unroll
-        for (int j = 0; j < W; ++j) {
-            const int64_t idx = top - j0 - (int64_t)j * kLanes;
-            e[j] = 0;
-            if (go && idx >= 0)
-                e[j] = __hip_atomic_load(&look[idx * NC + k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-#pragma unroll
-        for (int j = 0; j < W; ++j) {
-            const int64_t idx = top - j0 - (int64_t)j * kLanes;
-            if (!go || idx < 0) continue;
-            while ((uint32_t)(e[j] >> 34) != ep) {
-                if (++spins > spin_limit) {
-                    atomicOr(status, kStSortStall);
-                    e[j] = 0;
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
-                e[j] = __hip_atomic_load(&look[idx * NC + k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-            if (((e[j] >> 32) & 3u) == kIncl) near = min(near, (uint32_t)(top - idx));
-        }
-        if (go && near != 0xFFFFFFFFu) atomicMin(&s_near[r][k], near);
-        if (tid == 0) s_open[r] = 0u;
-        __syncthreads();
-        const uint32_t lim = go ? s_near[r][k] : 0u;
-        uint32_t part = 0;
-#pragma unroll
-        for (int j = 0; j < W; ++j) {
-            const int64_t idx = top - j0 - (int64_t)j * kLanes;
-            if (go && idx >= 0 && (uint32_t)(top - idx) <= lim) part += (uint32_t)e[j];
-        }
-        if (part) atomicAdd(&s_sum[k], part);
-        if (tid < NC) {
-            if (!s_done[tid]) {
-                if (s_near[r][tid] != 0xFFFFFFFFu || top - kLanes * W < 0)
-                    s_done[tid] = 1u;
-                else
-                    s_open[r] = 1u;
-            }
-            s_near[r ^ 1][tid] = 0xFFFFFFFFu;     // the next round's slot
-        }
-        __syncthreads();
-        if (!s_open[r]) break;
-    }
-}
-
 // Exclusive prefix over the wave's lanes of a value below 2^B, from one
 // ballot per bit plane: the count of lower lanes with bit b set, times 2^b.
 // The wave total comes back in *total.
@@ -871,6 +747,8 @@ static uint32_t next_epoch(SortWork& ws) {
     if (epoch == 0) epoch = ++ws.epoch & 0x3FFFFFFFu;
     return epoch;
 }
+
+uint32_t take_epoch(SortWork& ws) { return next_epoch(ws); }
 
 hipError_t launch_compact(const uint32_t* mask, const int32_t* nbr, int64_t n, int ksize,
                           int64_t cap, int tile_m, MapState* st, int32_t* pair_in,

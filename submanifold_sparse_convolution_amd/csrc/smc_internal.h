@@ -280,7 +280,8 @@ __device__ inline void stride_mark(const StrideGeom& sg, int b, int x, int y, in
 // Output cells through a bitmap of the output grid (words of it, zero on entry
 // and left zero): coords -> output coords [M, 4] and query points [M, 4] in
 // (b, x, y, z) order, st->n_out = M; counts: out_bitmap_blocks(words) words of
-// scratch.
+// scratch; bitmaps of at most 2 n_cu chunks go through one look-back pass over
+// ws.look (at least out_bitmap_blocks(words) entries).
 constexpr int64_t kOutBitmapWords = (int64_t)1 << 25;   // 128 MiB: larger grids sort candidates
 int64_t out_bitmap_words(const StrideGeom& sg, int batch);
 int64_t out_bitmap_blocks(int64_t words);
@@ -288,7 +289,10 @@ int64_t out_bitmap_blocks(int64_t words);
 hipError_t launch_stride_bitmap(const int32_t* coords, int64_t n, const Geom& g,
                                 const StrideGeom& sg, uint32_t* obits, int64_t words,
                                 uint32_t* counts, int32_t* ocoords, int32_t* qcoords,
-                                MapState* st, hipStream_t s, bool marked = false);
+                                MapState* st, SortWork& ws, int n_cu, hipStream_t s,
+                                bool marked = false);
+// The next look-back epoch of ws (never 0), for a kernel that tags entries with it.
+uint32_t take_epoch(SortWork& ws);
 // coords [n, ncols] -> 8 candidate output keys per row (sentinels where fewer)
 hipError_t launch_stride_candidates(const int32_t* coords, int64_t n, const Geom& g,
                                     const StrideGeom& sg, uint64_t* keys, MapState* st,

@@ -546,7 +546,7 @@ static int strided_outputs(smc_map* m, const int32_t* coords, int64_t n, const G
         if ((rc = prepare_obits(m, words, s))) return rc;
         SMC_HIP(launch_stride_bitmap(coords, n, g, sg, m->obits.as<uint32_t>(), words,
                                      m->ucounts.as<uint32_t>(), m->ocoords.as<int32_t>(),
-                                     m->qcoords.as<int32_t>(), st, s, marked));
+                                     m->qcoords.as<int32_t>(), st, m->ws, m->n_cu, s, marked));
     } else {
         SMC_HIP(launch_stride_candidates(coords, n, g, sg, m->ck0.as<uint64_t>(), st, s));
         int bits = 1;
@@ -764,6 +764,10 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     size_t look_bytes = sort_look_bytes(items > nn ? items : nn);
     const size_t look_c = compact_look_bytes_k(rows_cap, kernel_size);
     if (look_c > look_bytes) look_bytes = look_c;
+    if (strided && out_bitmap_words(sg, g.batch) <= kOutBitmapWords) {   // the bitmap's chunks
+        const size_t look_o = (size_t)out_bitmap_blocks(out_bitmap_words(sg, g.batch)) * 8;
+        if (look_o > look_bytes) look_bytes = look_o;
+    }
     const size_t look_before = m->look.bytes;
     // (the neighbour table is read in whole 16-byte words: keep the last one readable)
     if ((rc = m->nbr.ensure((size_t)rows_cap * taps * 4 + 16, s)) ||

@@ -22,6 +22,7 @@
 // lookup around the query points then reuses the dense grid, or searches the
 // sorted input keys (k_query_lookup, one search per dx plane as in the Z-Delta
 // mapper).
+#include "lookback.h"
 #include "smc_internal.h"
 
 namespace smc {
@@ -288,6 +289,85 @@ __global__ __launch_bounds__(kUThreads) void k_bits_write(uint32_t* __restrict__
     }
 }
 
+// The same in one pass, for bitmaps of at most 2 chunks per CU (512 on this
+// GPU): block b takes chunk b (far fewer blocks than the device holds at once,
+// so every block is resident and a block only waits for running blocks),
+// counts its set bits, publishes the count, adds the counts of every earlier
+// chunk by decoupled look-back (the whole block reads 1,024 predecessors per
+// round trip), then writes its set bits as above. The last block stores the
+// total as the output count. One launch instead of three (strided layers: 6
+// chunks 118.6 -> 115.2 us, 333 chunks 134.3 -> 133.2 and 74.9 -> 74.3 us).
+// Larger bitmaps keep the three passes: a block per chunk with tickets from
+// one counter serialised on its atomics (60 -> 180 us for 11,665 chunks).
+__global__ __launch_bounds__(kUThreads) void k_bits_emit(uint32_t* __restrict__ obits,
+                                                         int64_t words, StrideGeom sg,
+                                                         uint64_t* __restrict__ look,
+                                                         uint32_t epoch,
+                                                         int32_t* __restrict__ ocoords,
+                                                         int32_t* __restrict__ qcoords,
+                                                         MapState* __restrict__ st) {
+    __shared__ uint32_t s_w[kUThreads / 64];
+    __shared__ uint32_t s_tot, s_pre[1], s_done[1];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t bid = blockIdx.x;
+    const int64_t base = bid * kBTile + (int64_t)threadIdx.x * kBWords;
+    uint32_t v[kBWords];
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < kBWords; ++j) {
+        v[j] = base + j < words ? obits[base + j] : 0u;
+        c += (uint32_t)__popc(v[j]);
+    }
+    uint32_t inc = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = __shfl_up(inc, o);
+        if (lane >= o) inc += t;
+    }
+    if (lane == 63) s_w[w] = inc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t tot = 0;
+        for (int q = 0; q < kUThreads / 64; ++q) tot += s_w[q];
+        s_tot = tot;
+        __hip_atomic_store(&look[bid], lb_pack(epoch & 0x3FFFFFFFu, bid == 0 ? kIncl : kAgg, tot),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    block_lookback<1, 4, kUThreads>(look, bid - 1, epoch, &st->status, s_pre, s_done);
+    const uint32_t pre = s_pre[0];
+    if (threadIdx.x == 0) {
+        if (bid > 0)
+            __hip_atomic_store(&look[bid], lb_pack(epoch & 0x3FFFFFFFu, kIncl, pre + s_tot),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (bid == (int64_t)gridDim.x - 1) st->n_out = (int32_t)(pre + s_tot);
+    }
+    uint32_t pos = pre + inc - c;
+    for (int q = 0; q < w; ++q) pos += s_w[q];
+    const int r = (sg.ksize - 1) / 2;
+    // (the bitmap route covers fewer than 2^32 cells: 32-bit cell arithmetic)
+    const uint32_t ez = (uint32_t)sg.oext[2], ey = (uint32_t)sg.oext[1], ex = (uint32_t)sg.oext[0];
+#pragma unroll
+    for (int j = 0; j < kBWords; ++j) {
+        if (base + j >= words) break;
+        if (v[j]) obits[base + j] = 0u;
+        for (uint32_t bits = v[j]; bits; bits &= bits - 1) {
+            uint32_t L = ((uint32_t)(base + j) << 5) + (uint32_t)__builtin_ctz(bits);
+            const int z = (int)(L % ez);
+            L /= ez;
+            const int y = (int)(L % ey);
+            L /= ey;
+            const int x = (int)(L % ex);
+            const int b = (int)(L / ex);
+            reinterpret_cast<int4*>(ocoords)[pos] = make_int4(b, x, y, z);
+            reinterpret_cast<int4*>(qcoords)[pos] =
+                make_int4(b, sg.stride * x - sg.pad + r + sg.origin[0],
+                          sg.stride * y - sg.pad + r + sg.origin[1],
+                          sg.stride * z - sg.pad + r + sg.origin[2]);
+            ++pos;
+        }
+    }
+}
+
 template <typename K>
 __device__ inline int64_t lower_bound_k(const K* __restrict__ keys, int64_t n, K t) {
     int64_t lo = 0, len = n;
@@ -416,11 +496,16 @@ int64_t out_bitmap_blocks(int64_t words) { return (words + kBTile - 1) / kBTile;
 hipError_t launch_stride_bitmap(const int32_t* coords, int64_t n, const Geom& g,
                                 const StrideGeom& sg, uint32_t* obits, int64_t words,
                                 uint32_t* counts, int32_t* ocoords, int32_t* qcoords,
-                                MapState* st, hipStream_t s, bool marked) {
+                                MapState* st, SortWork& ws, int n_cu, hipStream_t s, bool marked) {
     if (n <= 0 || words <= 0) return hipSuccess;
     const int64_t nb = out_bitmap_blocks(words);
     if (!marked)
         launch(k_stride_mark, blocks_of(n, kBlock), kBlock, 0, s, coords, n, g, sg, obits, st);
+    if (nb <= 2 * (int64_t)n_cu) {
+        launch(k_bits_emit, (unsigned)nb, kUThreads, 0, s, obits, words, sg, ws.look,
+               take_epoch(ws), ocoords, qcoords, st);
+        return hipGetLastError();
+    }
     launch(k_bits_count, (unsigned)nb, kUThreads, 0, s, (const uint32_t*)obits, words, counts);
     launch(k_scan_counts, 1u, 1024, 0, s, counts, nb, st);
     launch(k_bits_write, (unsigned)nb, kUThreads, 0, s, obits, words, sg, (const uint32_t*)counts,
