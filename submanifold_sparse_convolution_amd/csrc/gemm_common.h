@@ -65,7 +65,10 @@ __device__ inline uint32_t bf16_rne_bits(float f) {
 
 // Write NBW consecutive output values of one row (columns col0 ..), as bf16
 // (rounded to nearest, ties to even) or float, with optional ReLU. Full
-// 8-column bf16 rows go out as one streaming (non-temporal) 16-byte store.
+// 8-column bf16 rows go out as one 16-byte store, a plain (cached) one: the
+// next layer reads the output at once, and the lines kept in the caches make
+// that read cheaper (six 91k-row layers on one map: 34.1 -> 32.5 us per layer
+// against streaming stores).
 template <int NBW, bool OUT_F32>
 __device__ __forceinline__ void store_row(void* __restrict__ yv, int64_t row, int c_out, int col0,
                                           const float (&v)[NBW], int relu) {
@@ -85,9 +88,8 @@ __device__ __forceinline__ void store_row(void* __restrict__ yv, int64_t row, in
         if (relu && (bb[nb] & 0x8000u)) bb[nb] = 0;
     }
     if (NBW == 8 && full && (c_out & 7) == 0) {
-        __builtin_nontemporal_store((u32x4){bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16),
-                                            bb[4] | (bb[5] << 16), bb[6] | (bb[7] << 16)},
-                                    reinterpret_cast<u32x4*>(y));
+        *reinterpret_cast<u32x4*>(y) = (u32x4){bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16),
+                                               bb[4] | (bb[5] << 16), bb[6] | (bb[7] << 16)};
     } else if (NBW == 4 && full && (c_out & 3) == 0) {
         *reinterpret_cast<uint2*>(y) = make_uint2(bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16));
     } else {
