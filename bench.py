@@ -24,7 +24,7 @@ Timing: W warm-up steps, then a timed region of exactly K steps between
 device synchronisations, repeated three times; ms_per_step is the median
 region's wall clock per step.
 
-Prints ONE JSON line. --gpus above 1 exits: this build measures one GPU.
+Prints ONE JSON line. --gpus above 1 exits: the library runs on one GPU.
 
 Kernel durations come from a second pass with the library's stage timers:
 every kernel records one stop event (without the system fence) on the
@@ -863,8 +863,8 @@ def main():
         return
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
-              "(no multi-GPU path: every box here has one GPU)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the library "
+              "has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
 
     import torch

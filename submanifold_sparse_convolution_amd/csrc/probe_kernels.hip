@@ -1,5 +1,5 @@
 // Attainable-peak probes: a bf16 MFMA loop and a plain device copy. They
-// compute nothing of the convolution; the benchmark times them on the box to
+// compute nothing of the convolution; the benchmark times them on the same GPU to
 // put the spec peaks (2.5 PFLOP/s dense bf16, 8 TB/s HBM) next to what this
 // part reaches under its power and clock limits.
 #include "smconv.h"
