@@ -46,18 +46,22 @@ bases) count zero.
   k_sorted_lookup / k_dense_lookup   4 N masks [+ 4 T N table]
   k_conv_masktile   2 N C_in + 2 T C_in C_out + 2 N C_out (+ 8 N C_out per extra group pass)
   strided layers (M output rows): k_gemm_nc 2 N C_in + 2 T C_in C_out + 8 P (every tap),
-                    k_slab_sum 2 M C_out
+                    k_slab_sum 2 M C_out, k_lookup_compact (dense route: the M query
+                    points' lookup inside the compaction) 16 M + 4 M + 8 P
   sort passes, k_weight_pack (outside the step), fills: 0
 A stage of several kernels (a strided map's neighbour stage: the input grid or
 sorted keys, the output cells through a bitmap of the output grid or, above
-2^30 cells, a sort of candidate keys, then the lookup) is listed with its
+2^30 cells, a sort of candidate keys, and on the sorted route the query
+lookup) is listed with its
 kernels and time but has no byte model and is never the roofline's kernel;
 "output_cells_route" says which output route a strided build took.
 
   --summarize-pmc FETCH_DIR WRITE_DIR   turn two `rocprofv3 --pmc FETCH_SIZE`
       / `--pmc WRITE_SIZE` runs of this script (with --copy-probe-mb) into
-      profiles/traffic_<workload>_<algo>.json, which later runs read for the
-      roofline's "traffic" (null when a kernel source changed since).
+      profiles/traffic_<workload>_<algo>.json (with --strided-layer:
+      traffic_<workload>_strided.json, runs that time the stride-2 layer), which
+      later runs read for the roofline's "traffic" (null when a kernel source
+      changed since).
   --summarize-mfma PMC_DIR BENCH_OUT   turn one `rocprofv3 --pmc
       SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES` run of this script
       (its stdout saved in BENCH_OUT) into profiles/mfma_<workload>_<algo>.json:
@@ -143,7 +147,7 @@ def kernel_model(kernel, n, p, c_in, c_out, taps=27, table=False, n_out=None, gr
     if kernel in ("k_dense_scatter", "k_make_keys"):
         return 16 * n, 0.0
     if kernel == "k_lookup_compact":
-        return 16 * n + 4 * n + 8 * p + t4, 0.0
+        return 16 * m + 4 * m + 8 * p + t4, 0.0
     if kernel in ("k_compact", "k_compact5"):
         return (4 if taps == 27 else 16) * n + 8 * p, 0.0
     if kernel in ("k_sorted_lookup", "k_dense_lookup", "k_dense_lookup5", "k_query_lookup"):
@@ -264,13 +268,15 @@ def stage_kernels(stage, algo, route, kernel_size=3, strided=False, c_in=128, ou
         return ("k_gemm_centre_big",) if big else ("k_gemm_centre",)
     if stage == "mask_sort":
         return ("k_mask_hist", "k_os_pass")
-    fused = route == "dense" and algo != "mask_tiles" and kernel_size == 3 and not strided
+    # dense route, pair lists: the lookup runs inside the compaction (for a strided
+    # map, of its query points)
+    fused = route == "dense" and algo != "mask_tiles" and kernel_size == 3
     if stage == "neighbours":
         if strided:
             inputs = ("k_dense_scatter",) if route == "dense" else ("k_make_keys", "k_os_pass",
                                                                     "k_key_dups")
-            return inputs + strided_output_kernels(out_cells, route) + (
-                "k_dense_lookup" if route == "dense" else "k_query_lookup",)
+            look = () if fused else ("k_dense_lookup" if route == "dense" else "k_query_lookup",)
+            return inputs + strided_output_kernels(out_cells, route) + look
         if route == "sorted":
             return ("k_make_keys", "k_os_pass", "k_sorted_lookup")
         if fused:
@@ -468,8 +474,11 @@ def stage_rows(r):
         row = dict(kernels=list(ks), us=us, per_step=r["stage_per_step"].get(st, 0.0))
         if len(ks) == 1:
             groups = info["n_groups"] if r["algo"] == "mask_tiles" else 1
+            # the neighbour table is written for mask tiles and by a strided map's
+            # sorted-route query lookup; fused dense builds keep none
             by, fl = kernel_model(ks[0], r["n"], r["pairs"], c, c, taps,
-                                  table=r["algo"] == "mask_tiles" or r["strided"],
+                                  table=r["algo"] == "mask_tiles"
+                                  or (r["strided"] and route != "dense"),
                                   n_out=r["n_out"] if r["strided"] else None, groups=groups)
             row.update(bytes=by, flops=fl)
         out[st] = row
@@ -495,8 +504,10 @@ def roofline(r):
            "peak": PEAK_BF16_TFLOPS if mfma else PEAK_HBM_GBS,
            "unit": "TFLOP/s" if mfma else "GB/s"}
     out["frac"] = round(out["achieved"] / out["peak"], 5)
-    plain = r["kernel_size"] == 3 and r["frames"] == 1 and r["order"] == "plain" and not r["strided"]
-    out["traffic"] = traffic_for(r["workload"].name, r["algo"], kernel) if plain else None
+    plain = r["kernel_size"] == 3 and r["frames"] == 1 and r["order"] == "plain"
+    rec = "strided" if r["strided"] else r["algo"]    # counter records: pair path, stride-2 layer
+    out["traffic"] = (traffic_for(r["workload"].name, rec, kernel)
+                      if plain and (r["algo"] == "pairs" or not r["strided"]) else None)
     out["avg_us"] = round(us, 3)
     out["launches_per_step"] = round(mo["per_step"], 3)
     out["algorithmic_bytes"] = mo["bytes"]
@@ -835,6 +846,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=6.0,
                     help="seconds per oracle part (map, compute) and set")
     ap.add_argument("--no-strided", action="store_true")
+    ap.add_argument("--strided-layer", action="store_true",
+                    help="time the set's stride-2 layer as the main line (profiling runs; "
+                         "its counter summaries go to profiles/traffic_<set>_strided.json)")
     ap.add_argument("--no-peaks", action="store_true")
     ap.add_argument("--other-algo", action="store_true",
                     help="also time the mask-tile forward (three row orders) on the headline set")
@@ -858,7 +872,8 @@ def main():
         summarize_mfma(args.summarize_mfma[0], args.workload, args.algo, args.summarize_mfma[1])
         return
     if args.summarize_pmc:
-        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.algo,
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload,
+                      "strided" if args.strided_layer else args.algo,
                       args.copy_probe_mb or 256)
         return
 
@@ -878,7 +893,8 @@ def main():
             raise SystemExit(f"unknown set {cname}")
 
     r = run_workload(args.workload, args.steps, args.warmup, args.sync_build, args.algo,
-                     args.copy_probe_mb, args.order, cold=True)
+                     args.copy_probe_mb, args.order, cold=not args.strided_layer,
+                     strided=args.strided_layer)
     w, info = r["workload"], r["info"]
     c = w.channels
     s = summary(r)
@@ -898,9 +914,11 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"{w.name}: {w.n} voxels, grid {w.grid[0]}x{w.grid[1]}x{w.grid[2]}, "
-                        f"C_in=C_out={c}, {w.layers} layer(s) sharing one map, seed {w.seed}",
+                        f"C_in=C_out={c}, "
+                        + ("one stride-2 layer" if args.strided_layer
+                           else f"{w.layers} layer(s) sharing one map") + f", seed {w.seed}",
             "n": w.n, "pairs": r["pairs"], "pairs_per_voxel": round(r["pairs"] / w.n, 4),
-            "route": info["route"], "c_in": c, "c_out": c, "layers": w.layers,
+            "route": info["route"], "c_in": c, "c_out": c, "layers": r["layers"],
             "map_built_every_step": True, "build_mode": "sync" if args.sync_build else "async",
             "algo": args.algo, "value_is": "(map + all layers) / layers, microseconds",
             **({"order": args.order} if args.algo == "mask_tiles" else {}),
