@@ -879,12 +879,14 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
                 Geom gq = g;                          // query points: [M, 4] in input coordinates
                 gq.ncols = 4;
                 if (want_pairs && !want_sort && kernel_size == 3 && rows > 0) {
-                    // lookup and compaction in one kernel (the centre a sparse tap)
+                    // lookup and compaction in one kernel (the centre a sparse tap); the
+                    // table only when asked for: nothing after the pair lists reads it
                     if ((rc = strided_pair_bufs(rows))) return rc;
                     t_nb.finish();
                     StageTimer t_cp(m, SMC_STAGE_COMPACT, s);
                     SMC_HIP(launch_lookup_compact(m->qcoords.as<int32_t>(), rows, gq, grid, bits,
-                                                  nbr, mask, m->cap, kTileM, st,
+                                                  (flags & SMC_BUILD_TABLE) ? nbr : nullptr,
+                                                  mask, m->cap, kTileM, st,
                                                   m->pair_in.as<int32_t>(),
                                                   m->pair_out.as<int32_t>(),
                                                   m->pair_slot.as<int32_t>(),
@@ -996,7 +998,6 @@ static int build_map(smc_map* m, const int32_t* coords, int64_t n, int ncols,
     m->has_pairs = want_pairs;
     m->has_sort = want_sort;
     m->has_table = !(chosen == SMC_ROUTE_DENSE && want_pairs && kernel_size == 3 && !want_sort &&
-                     !strided &&
                      !(flags & SMC_BUILD_TABLE)) || n == 0;
     m->sorted_order = ord;
     m->ksize = kernel_size;
